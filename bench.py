@@ -1,0 +1,196 @@
+"""Benchmark of the MI355X chunkwise gated delta rule: one step = rewy_fwd +
+rewy_bwd (complete backward) on the KDA workload B=1, T=8192, H=32,
+K=V=128, bf16 features, fp32 gates, synthetic seeded inputs resident in HBM.
+
+Prints ONE JSON line: whole-job fwd+bwd tokens/s, algorithmic TFLOPS and the
+fraction of the bf16 MFMA peak, a roofline entry for the dominant kernel
+(per-kernel HIP-event durations from the library's trace hook, measured on the
+launch stream) and the FP64 oracle timed on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd tokens/s and MFMA TFLOPS (% bf16 peak), KDA H=32 d=128 T=8192"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq):
+    """Algorithmic HBM bytes one launch of `kernel` must move in this design:
+    its compulsory inputs and outputs, each counted once (chunk-level tiles per
+    chunk-head, token-level rows per valid token)."""
+    n = sum(chunk_lens)                 # valid tokens per head
+    nc = len(chunk_lens)                # chunks per head
+    gb = {0: 0, 1: 4, 2: 4 * K}[gate]   # gate bytes per token
+    tok_k, tok_v = K * esz, V * esz
+    st = K * V * esz                    # one stored state tile
+    cq = 64 * 64 * esz                  # one 64x64 coefficient tile
+    per_head = {
+        "k_fwd_prep": n * (2 * tok_k + tok_v + gb + besz) + n * (3 * tok_k + tok_v) + nc * (cq + 4 * K),
+        "k_fwd_scan": n * (2 * tok_k + tok_v) + nc * 4 * K + nc * st + n * tok_v,
+        "k_fwd_out": n * (tok_k + 2 * tok_v) + nc * (st + cq),
+        "k_bwd_scan": n * (3 * tok_k + tok_v) + nc * (cq + 4 * K) + nc * st + n * tok_v,
+        "k_bwd_prod": n * (tok_k + gb + besz + 4 * tok_v) + n * (2 * tok_v + 4) + nc * 2 * cq,
+        "k_bwd_cons": nc * 2 * cq + n * 3 * tok_v + nc * 2 * st + n * (2 * tok_k + gb + besz + 4)
+                      + n * (2 * tok_k + gb + besz),
+    }
+    for name, b in per_head.items():
+        if f"rewy::{name}<" in kernel:
+            extra = 0
+            if name in ("k_fwd_scan", "k_bwd_scan"):
+                extra = nseq * 2 * 4 * K * V  # initial / final state (fp32) per sequence
+            return b * H + extra * H
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="kda_t8192_h32_d128")
+    ap.add_argument("--policy", default="recompute", choices=["recompute", "save"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="heads of the workload the oracle baseline runs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(heads shard across GPUs with no communication, so per-GPU throughput is the "
+              "N=1 figure)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from chunkwise_delta_rule_chunk_amd import binding, flops, ops
+
+    dev = torch.device("cuda:0")
+    inp = workloads.workload(args.workload)  # CPU generator, then resident in HBM
+    x = inp.to(dev)
+    B, T, H, K, V = inp.shape
+    seq_lens = ([T] * B) if inp.cu_seqlens is None else \
+        [int(b - a) for a, b in zip(inp.cu_seqlens[:-1], inp.cu_seqlens[1:])]
+    prob = ops.make_problem(x.q, x.v, x.g, x.beta, scale=inp.scale, cu_seqlens=inp.cu_seqlens,
+                            policy=args.policy)
+    ws0, ws1 = ops.workspace(prob, 0), ops.workspace(prob, 1)
+    torch.cuda.synchronize()
+
+    def step():
+        o, ht, ctx = ops.forward(x.q, x.k, x.v, x.g, x.beta, scale=inp.scale, h0=x.h0,
+                                 cu_seqlens=inp.cu_seqlens, policy=args.policy, ws=ws0)
+        return ops.backward(ctx, x.dO, x.dht, ws=ws1)
+
+    t_w = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_w < 2.0:
+        step()
+        done += 1
+        if done % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {done} steps", file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # per-kernel durations: K forward calls, then K backward calls, with the
+    # event-pair trace on (same stream, same buffers)
+    def traced(fn):
+        binding.rewy_trace_begin()
+        for _ in range(args.steps):
+            fn()
+        tr = binding.rewy_trace_end()
+        torch.cuda.synchronize()
+        return {name: (tot / cnt, cnt / args.steps) for name, tot, cnt in tr}
+
+    holder = {}
+
+    def fwd_only():
+        holder["ctx"] = ops.forward(x.q, x.k, x.v, x.g, x.beta, scale=inp.scale, h0=x.h0,
+                                    cu_seqlens=inp.cu_seqlens, policy=args.policy, ws=ws0)[2]
+
+    k_fwd = traced(fwd_only)
+    k_bwd = traced(lambda: ops.backward(holder["ctx"], x.dO, x.dht, ws=ws1))
+    fwd_ms = sum(a * p for a, p in k_fwd.values())
+    bwd_ms = sum(a * p for a, p in k_bwd.values())
+    kern = {}
+    for d in (k_fwd, k_bwd):
+        for name, (a, p) in d.items():
+            if name in kern:  # same kernel in both passes (recompute): pool the launches
+                a0, p0 = kern[name]
+                kern[name] = ((a0 * p0 + a * p) / (p0 + p), p0 + p)
+            else:
+                kern[name] = (a, p)
+    f_fwd, f_bwd, f_rc = flops.workload_flops(seq_lens, H, K, V)
+    tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
+    # dominant kernel: largest share of the step
+    dom, (dom_avg, dom_per) = max(kern.items(), key=lambda kv: kv[1][0] * kv[1][1])
+    chunk_lens = flops.chunk_lengths(seq_lens)
+    esz = 2 if inp.q.dtype == torch.bfloat16 else 4
+    besz = 2 if inp.beta.dtype == torch.bfloat16 else 4
+    gate = {"none": 0, "scalar": 1, "vector": 2}[inp.gate]
+    dbytes = kernel_bytes(dom, chunk_lens, H, K, V, esz, besz, gate, len(seq_lens))
+    achieved = dbytes / (dom_avg * 1e-3) / 1e9 if dbytes else None
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": None if achieved is None else achieved / PEAK_HBM_GBS,
+                "traffic": None, "avg_ms": dom_avg, "launches_per_step": dom_per,
+                "algorithmic_bytes_per_launch": dbytes}
+    result = {
+        "metric": METRIC, "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": done, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if esz == 2 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
+                   "gate": inp.gate, "policy": args.policy, "global_batch": B, "seq_len": T,
+                   "parallelism": "single-gpu"},
+        "tflops": tflops, "pct_bf16_peak": 100 * tflops / PEAK_BF16_TFLOPS,
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
+        "bwd_pct_bf16_peak": 100 * f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "flops_per_step": {"forward": f_fwd, "backward": f_bwd, "recompute_executed": f_rc},
+        "kernels_ms": {name: {"avg_ms": a, "launches_per_step": p} for name, (a, p) in kern.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        hs = list(range(min(args.cpu_heads, H)))
+        sel = lambda t: None if t is None else t[:, :, hs]
+        threads = oracle.default_threads()
+        cu = None if inp.cu_seqlens is None else inp.cu_seqlens.tolist()
+        tc = time.perf_counter()
+        oracle.forward(sel(inp.q), sel(inp.k), sel(inp.v), sel(inp.g), sel(inp.beta),
+                       scale=inp.scale, h0=None if inp.h0 is None else inp.h0[:, hs],
+                       cu_seqlens=cu, threads=threads)
+        oracle.backward(sel(inp.q), sel(inp.k), sel(inp.v), sel(inp.g), sel(inp.beta),
+                        sel(inp.dO), scale=inp.scale,
+                        h0=None if inp.h0 is None else inp.h0[:, hs], cu_seqlens=cu,
+                        threads=threads)
+        tcpu = time.perf_counter() - tc
+        frac = len(hs) / H
+        result["cpu_baseline"] = {
+            "value": B * T * frac / tcpu, "unit": "tokens/s", "cores": min(threads, len(hs) * len(seq_lens)),
+            "kind": "oracle",
+            "sample": f"FP64 token-recurrence oracle, forward+backward of heads 0..{len(hs) - 1} "
+                      f"of {H} of {args.workload} ({tcpu:.1f} s); tokens/s scaled by the head "
+                      f"fraction {frac:g}",
+            "host_cpus": os.cpu_count(),
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,392 @@
+// Host side of the C ABI declared in include/rewy.h: argument validation,
+// workspace planning and the launch sequence of each pass.  Nothing here
+// allocates device memory or waits for the device.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "kernels.hpp"
+#include "rewy.h"
+
+#define REWY_API extern "C" __attribute__((visibility("default")))
+
+namespace rewy {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Plan {
+  int B, T, H, K, V, N, nc_max;
+  int64_t BT;  // packed tokens
+  bool f32, beta_f32;
+  int gate, policy;
+  size_t esz;
+};
+
+int kv_supported(int K, int V, bool f32) {
+  auto ok = [](int x) { return x == 32 || x == 64 || x == 128; };
+  if (!ok(K) || !ok(V)) return 0;
+  if (f32 && (K > 64 || V > 64)) return 0;
+  return 1;
+}
+
+int make_plan(const rewy_desc* d, Plan& p) {
+  if (!d) return fail(REWY_EINVAL, "desc is NULL");
+  if (d->B <= 0 || d->T < 0 || d->H <= 0 || d->K <= 0 || d->V <= 0)
+    return fail(REWY_EINVAL, "bad shape B=%d T=%d H=%d K=%d V=%d", d->B, d->T, d->H, d->K, d->V);
+  if (d->dtype != REWY_BF16 && d->dtype != REWY_F32) return fail(REWY_EINVAL, "bad dtype %d", d->dtype);
+  if (d->beta_dtype != REWY_BF16 && d->beta_dtype != REWY_F32)
+    return fail(REWY_EINVAL, "bad beta_dtype %d", d->beta_dtype);
+  if (d->gate < REWY_GATE_NONE || d->gate > REWY_GATE_VECTOR) return fail(REWY_EINVAL, "bad gate %d", d->gate);
+  if (d->policy != REWY_RECOMPUTE && d->policy != REWY_SAVE) return fail(REWY_EINVAL, "bad policy %d", d->policy);
+  if (d->K > 256) return fail(REWY_EINVAL, "K=%d exceeds 256", d->K);
+  const bool f32 = d->dtype == REWY_F32;
+  if (!kv_supported(d->K, d->V, f32))
+    return fail(REWY_EUNSUPPORTED, "K=%d V=%d not supported for %s (K, V in {32,64,128}; fp32 <= 64)",
+                d->K, d->V, f32 ? "fp32" : "bf16");
+  p.B = d->B; p.T = d->T; p.H = d->H; p.K = d->K; p.V = d->V;
+  p.f32 = f32; p.beta_f32 = d->beta_dtype == REWY_F32; p.gate = d->gate; p.policy = d->policy;
+  p.esz = f32 ? 4 : 2;
+  p.BT = (int64_t)d->B * d->T;
+  if (p.BT >= (int64_t)1 << 31) return fail(REWY_EINVAL, "B*T=%lld exceeds int32", (long long)p.BT);
+  if (d->cu_seqlens) {
+    if (d->B != 1) return fail(REWY_EINVAL, "cu_seqlens requires B == 1 (got B=%d)", d->B);
+    if (d->N <= 0) return fail(REWY_EINVAL, "cu_seqlens requires N >= 1 (got N=%d)", d->N);
+    p.N = d->N;
+    if (d->cu_seqlens_host) {
+      const int32_t* cu = d->cu_seqlens_host;
+      if (cu[0] != 0 || cu[p.N] != d->T)
+        return fail(REWY_EINVAL, "cu_seqlens must start at 0 and end at T=%d", d->T);
+      int64_t nc = 0;
+      for (int i = 0; i < p.N; ++i) {
+        if (cu[i + 1] < cu[i]) return fail(REWY_EINVAL, "cu_seqlens not ascending at %d", i);
+        nc += (cu[i + 1] - cu[i] + CH - 1) / CH;
+      }
+      p.nc_max = (int)nc;
+    } else {
+      p.nc_max = (d->T + CH - 1) / CH + p.N;
+    }
+  } else {
+    if (d->N != 0 && d->N != d->B) return fail(REWY_EINVAL, "N=%d must equal B=%d without cu_seqlens", d->N, d->B);
+    p.N = d->B;
+    p.nc_max = d->B * ((d->T + CH - 1) / CH);
+  }
+  return REWY_OK;
+}
+
+// Buffer layout.  `saved` holds what the backward reads from the forward under
+// the save-all policy; everything else is scratch in the workspace.
+struct Layout {
+  size_t chunks, seqoff, W, U, F, Qg, Cq, glast, hbuf, R;   // forward set
+  size_t Rb, dhbuf, P, D, Hq, dbw;                           // backward set
+  size_t ws_fwd, ws_bwd, saved;
+};
+
+Layout layout(const Plan& p) {
+  Layout L{};
+  const size_t nc = p.nc_max, H = p.H, K = p.K, V = p.V, BT = p.BT, e = p.esz;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
+  // workspace always starts with the chunk index
+  L.chunks = take(nc * sizeof(ChunkInfo));
+  L.seqoff = take((size_t)(p.N + 1) * 4);
+  L.U = take(BT * H * V * e);
+  const size_t ws_head = off;
+  // forward set: in the workspace (recompute) or in `saved` (save-all)
+  size_t s = (p.policy == REWY_SAVE) ? 0 : off;
+  auto takef = [&](size_t bytes) { size_t o = s; s += up(bytes); return o; };
+  L.W = takef(BT * H * K * e);
+  L.F = takef(BT * H * K * e);
+  L.Qg = takef(BT * H * K * e);
+  L.Cq = takef(nc * H * CH * CH * e);
+  L.glast = takef(nc * H * K * 4);
+  L.hbuf = takef(nc * H * K * V * e);
+  L.R = takef(BT * H * V * e);
+  if (p.policy == REWY_SAVE) {
+    L.saved = s;
+    off = ws_head;
+  } else {
+    L.saved = 0;
+    off = s;
+  }
+  L.ws_fwd = off;
+  L.Rb = take(BT * H * V * e);
+  L.dhbuf = take(nc * H * K * V * e);
+  L.P = take(BT * H * V * e);
+  L.D = take(nc * H * CH * CH * e);
+  L.Hq = take(nc * H * CH * CH * e);
+  L.dbw = take(BT * H * 4);
+  L.ws_bwd = off;
+  return L;
+}
+
+__global__ void k_copy_or_zero(float* dst, const float* src, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src ? src[i] : 0.f;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(REWY_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return REWY_OK;
+}
+
+int copy_state(float* dst, const float* src, int64_t n, hipStream_t s) {
+  if (!dst || n == 0) return REWY_OK;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_copy_or_zero, dim3(blocks), dim3(256), 0, s, dst, src, n);
+  return hip_check(hipGetLastError(), "state copy");
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+void fill_common(Args& a, const Plan& p, const rewy_desc* d, char* ws, char* fs,
+                 const Layout& L) {
+  memset(&a, 0, sizeof(a));
+  a.B = p.B; a.T = p.T; a.H = p.H; a.K = p.K; a.V = p.V; a.N = p.N; a.nc_max = p.nc_max;
+  a.gate = p.gate; a.beta_f32 = p.beta_f32; a.scale = d->scale; a.cu = d->cu_seqlens;
+  a.chunks = reinterpret_cast<ChunkInfo*>(ws + L.chunks);
+  a.seqoff = reinterpret_cast<int*>(ws + L.seqoff);
+  a.U = ws + L.U;
+  a.W = fs + L.W; a.F = fs + L.F; a.Qg = fs + L.Qg; a.Cq = fs + L.Cq;
+  a.glast = reinterpret_cast<float*>(fs + L.glast);
+  a.hbuf = fs + L.hbuf; a.R = fs + L.R;
+  a.Rb = ws + L.Rb; a.dhbuf = ws + L.dhbuf; a.P = ws + L.P; a.D = ws + L.D; a.Hq = ws + L.Hq;
+  a.dbw = reinterpret_cast<float*>(ws + L.dbw);
+}
+
+int check_tensor_ptrs(const void* const* ps, const char* const* names, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (!ps[i]) return fail(REWY_EINVAL, "%s is NULL", names[i]);
+    if (!aligned(ps[i], 16)) return fail(REWY_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  return REWY_OK;
+}
+
+// ---- tracing: event pairs around every launch, per thread ------------------
+struct TraceRec {
+  const char* stage;  // kernel template name
+  int variant;        // instantiation key (dtype, K, V)
+  hipEvent_t e0, e1;
+};
+struct Tracer {
+  bool on = false;
+  std::vector<TraceRec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  hipEvent_t ev() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+thread_local Tracer g_tr;
+
+template <typename F>
+hipError_t traced(const char* stage, int variant, hipStream_t s, F&& launch) {
+  if (!g_tr.on) return launch();
+  TraceRec r{stage, variant, g_tr.ev(), g_tr.ev()};
+  if (r.e0) hipEventRecord(r.e0, s);
+  const hipError_t e = launch();
+  if (r.e1) hipEventRecord(r.e1, s);
+  if (r.e0 && r.e1) g_tr.recs.push_back(r);
+  return e;
+}
+
+int variant_of(const Args& a, bool f32) { return (f32 ? 1000000 : 0) + a.K * 1000 + a.V; }
+
+// Forward chunk stages shared by rewy_fwd and the recompute in rewy_bwd.
+int run_forward_stages(const Args& a, bool f32, bool with_output, hipStream_t s) {
+  int rc;
+  const int vr = variant_of(a, f32);
+  if ((rc = hip_check(traced("k_chunk_table", -1, s, [&] { return launch_chunk_table(a, s); }),
+                      "chunk table")))
+    return rc;
+  if ((rc = hip_check(traced("k_fwd_prep", vr, s, [&] { return launch_fwd_prep(a, f32, s); }),
+                      "forward prep")))
+    return rc;
+  if ((rc = hip_check(traced("k_fwd_scan", vr, s, [&] { return launch_fwd_scan(a, f32, s); }),
+                      "forward scan")))
+    return rc;
+  if (with_output &&
+      (rc = hip_check(traced("k_fwd_out", vr, s, [&] { return launch_fwd_out(a, f32, s); }),
+                      "forward output")))
+    return rc;
+  return REWY_OK;
+}
+
+}  // namespace
+}  // namespace rewy
+
+using namespace rewy;
+
+REWY_API size_t rewy_workspace_bytes(const rewy_desc* d, int phase) {
+  Plan p;
+  if (make_plan(d, p) != REWY_OK) return 0;
+  const Layout L = layout(p);
+  return phase == 0 ? L.ws_fwd : L.ws_bwd;
+}
+
+REWY_API size_t rewy_saved_bytes(const rewy_desc* d) {
+  Plan p;
+  if (make_plan(d, p) != REWY_OK) return 0;
+  return layout(p).saved;
+}
+
+REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const void* v,
+                      const float* g, const void* beta, const float* h0, void* o, float* ht,
+                      void* saved, void* workspace, size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(d, p);
+  if (rc) return rc;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t state_n = (int64_t)p.N * p.H * p.K * p.V;
+  if (p.BT == 0) return copy_state(ht, h0, state_n, s);
+  {
+    const void* ps[] = {q, k, v, beta, o};
+    const char* nm[] = {"q", "k", "v", "beta", "o"};
+    if ((rc = check_tensor_ptrs(ps, nm, 5))) return rc;
+  }
+  if ((p.gate != REWY_GATE_NONE) != (g != nullptr))
+    return fail(REWY_EINVAL, "g must be given exactly when gate != NONE");
+  if (g && !aligned(g, 16)) return fail(REWY_EINVAL, "g is not 16-byte aligned");
+  const Layout L = layout(p);
+  if (!workspace || !aligned(workspace, ALIGN) || ws_bytes < L.ws_fwd)
+    return fail(REWY_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.ws_fwd,
+                ws_bytes);
+  if (p.policy == REWY_SAVE && (!saved || !aligned(saved, ALIGN)))
+    return fail(REWY_EWORKSPACE, "policy SAVE needs a 256-byte aligned saved buffer of %zu bytes",
+                L.saved);
+  Args a;
+  char* ws = static_cast<char*>(workspace);
+  fill_common(a, p, d, ws, p.policy == REWY_SAVE ? static_cast<char*>(saved) : ws, L);
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+  return run_forward_stages(a, p.f32, true, s);
+}
+
+REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const void* v,
+                      const float* g, const void* beta, const float* h0, const void* dO,
+                      const float* dht, const void* saved, void* dq, void* dk, void* dv,
+                      float* dg, void* dbeta, float* dh0, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  Plan p;
+  int rc = make_plan(d, p);
+  if (rc) return rc;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (h0 && !dh0) return fail(REWY_EINVAL, "dh0 must be given when h0 is given");
+  const int64_t state_n = (int64_t)p.N * p.H * p.K * p.V;
+  if (p.BT == 0) return copy_state(dh0, dht, state_n, s);
+  {
+    const void* ps[] = {q, k, v, beta, dO, dq, dk, dv, dbeta};
+    const char* nm[] = {"q", "k", "v", "beta", "dO", "dq", "dk", "dv", "dbeta"};
+    if ((rc = check_tensor_ptrs(ps, nm, 9))) return rc;
+  }
+  if ((p.gate != REWY_GATE_NONE) != (g != nullptr))
+    return fail(REWY_EINVAL, "g must be given exactly when gate != NONE");
+  if ((p.gate != REWY_GATE_NONE) != (dg != nullptr))
+    return fail(REWY_EINVAL, "dg must be given exactly when gate != NONE");
+  if ((g && !aligned(g, 16)) || (dg && !aligned(dg, 16)))
+    return fail(REWY_EINVAL, "g / dg must be 16-byte aligned");
+  const Layout L = layout(p);
+  if (!workspace || !aligned(workspace, ALIGN) || ws_bytes < L.ws_bwd)
+    return fail(REWY_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.ws_bwd,
+                ws_bytes);
+  if (p.policy == REWY_SAVE && (!saved || !aligned(saved, ALIGN)))
+    return fail(REWY_EWORKSPACE, "policy SAVE needs the saved buffer written by rewy_fwd");
+  Args a;
+  char* ws = static_cast<char*>(workspace);
+  char* fs = p.policy == REWY_SAVE ? const_cast<char*>(static_cast<const char*>(saved)) : ws;
+  fill_common(a, p, d, ws, fs, L);
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = dO; a.dht = dht;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+  const bool f32 = p.f32;
+  const int vr = variant_of(a, f32);
+  if (p.policy == REWY_RECOMPUTE) {
+    if ((rc = run_forward_stages(a, f32, false, s))) return rc;
+  } else if ((rc = hip_check(traced("k_chunk_table", -1, s,
+                                    [&] { return launch_chunk_table(a, s); }),
+                             "chunk table"))) {
+    return rc;
+  }
+  if ((rc = hip_check(traced("k_bwd_scan", vr, s, [&] { return launch_bwd_scan(a, f32, s); }),
+                      "reverse scan")))
+    return rc;
+  if ((rc = hip_check(traced("k_bwd_prod", vr, s, [&] { return launch_bwd_prod(a, f32, s); }),
+                      "ReWY producer")))
+    return rc;
+  if ((rc = hip_check(traced("k_bwd_cons", vr, s, [&] { return launch_bwd_cons(a, f32, s); }),
+                      "gradient consumer")))
+    return rc;
+  return REWY_OK;
+}
+
+REWY_API int rewy_trace_begin(void) {
+  g_tr.recs.clear();
+  g_tr.used = 0;
+  g_tr.on = true;
+  return REWY_OK;
+}
+
+REWY_API int rewy_trace_end(rewy_trace_entry* out, int cap) {
+  g_tr.on = false;
+  if (!out && cap > 0) return fail(REWY_EINVAL, "trace output is NULL");
+  std::vector<rewy_trace_entry> agg;
+  for (const TraceRec& r : g_tr.recs) {
+    if (hipEventSynchronize(r.e1) != hipSuccess) return fail(REWY_EHIP, "trace synchronise");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) return fail(REWY_EHIP, "trace elapsed");
+    char name[96];
+    if (r.variant < 0) {
+      snprintf(name, sizeof(name), "rewy::%s(rewy::Args)", r.stage);
+    } else {
+      const bool f32 = r.variant >= 1000000;
+      const int kv = r.variant % 1000000;
+      snprintf(name, sizeof(name), "void rewy::%s<%s, %d, %d>(rewy::Args)", r.stage,
+               f32 ? "float" : "__bf16", kv / 1000, kv % 1000);
+    }
+    size_t i = 0;
+    while (i < agg.size() && strcmp(agg[i].kernel, name) != 0) ++i;
+    if (i == agg.size()) {
+      rewy_trace_entry e{};
+      snprintf(e.kernel, sizeof(e.kernel), "%s", name);
+      agg.push_back(e);
+    }
+    agg[i].total_ms += ms;
+    agg[i].launches += 1;
+  }
+  g_tr.recs.clear();
+  g_tr.used = 0;
+  const int n = (int)std::min<size_t>(agg.size(), (size_t)std::max(cap, 0));
+  for (int i = 0; i < n; ++i) out[i] = agg[i];
+  return (int)agg.size();
+}
+
+REWY_API const char* rewy_status_string(int status) {
+  switch (status) {
+    case REWY_OK: return "REWY_OK";
+    case REWY_EINVAL: return "REWY_EINVAL";
+    case REWY_EUNSUPPORTED: return "REWY_EUNSUPPORTED";
+    case REWY_EWORKSPACE: return "REWY_EWORKSPACE";
+    case REWY_EHIP: return "REWY_EHIP";
+    default: return "REWY_UNKNOWN";
+  }
+}
+
+REWY_API const char* rewy_last_error(void) { return g_err; }

@@ -1,0 +1,212 @@
+// Device-side building blocks shared by the gfx950 kernels of the chunkwise
+// gated delta rule: element types, MFMA fragment loads, LDS tile movers and
+// the per-chunk index record.
+//
+// MFMA tiles are 16x16.  bf16 operands use v_mfma_f32_16x16x32_bf16 (32-long
+// contraction per instruction); fp32 operands use v_mfma_f32_16x16x4_f32.
+// For both, lane l of a wave holds row (l & 15) of an A fragment / column
+// (l & 15) of a B fragment, and contraction slots
+//   bf16: k0 + 8*(l >> 4) + e, e = 0..7        fp32: k0 + (l >> 4)
+// The result lives as acc[i] = C[4*(l >> 4) + i][l & 15], i = 0..3.
+// A and B fragments use the same slot convention, so any consistent slot
+// assignment gives the exact product.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace rewy {
+
+using bf16 = __bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 64;          // chunk length (tokens)
+constexpr int SUB = 16;         // sub-chunk = MFMA tile edge
+constexpr int NSUB = CH / SUB;  // sub-chunks per chunk
+constexpr float LOG2E = 1.4426950408889634f;
+// Largest in-block gate range (log2 units) for which midpoint-centred factors
+// exp2(+-(G - mid)) stay inside 2^64; wider diagonal blocks take the pairwise path.
+constexpr float CENTRE_MAX_RANGE = 128.f;
+
+// One chunk of one sequence: tokens [bos, bos + len) of the packed token axis.
+struct ChunkInfo {
+  int seq;  // sequence index
+  int bos;  // first token (row of the [B*T] token axis)
+  int len;  // valid tokens, 0 for an unused slot
+  int pos;  // chunk index within its sequence
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+template <typename T>
+__device__ __forceinline__ float tof(T x) { return (float)x; }
+template <typename T>
+__device__ __forceinline__ T fromf(float x) { return (T)x; }
+
+template <typename T>
+struct MM;
+template <>
+struct MM<bf16> {
+  static constexpr int KS = 32;
+  using frag = bf16x8;
+};
+template <>
+struct MM<float> {
+  static constexpr int KS = 4;
+  using frag = float;
+};
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Operand fragment of a k-step starting at k0.  Element (r, k) of the operand
+// is p[r * rs + k * ks] with r = lane & 15 (row of A / column of B).  KC means
+// ks == 1 and rows are 16-byte aligned, so one vector read serves the lane.
+template <typename T, bool KC>
+__device__ __forceinline__ typename MM<T>::frag ldfrag(const T* p, int rs, int ks, int k0) {
+  const int l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  if constexpr (std::is_same_v<T, bf16>) {
+    const int kb = k0 + g * 8;
+    if constexpr (KC) {
+      return *reinterpret_cast<const bf16x8*>(p + r * rs + kb);
+    } else {
+      bf16x8 f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = p[r * rs + (kb + e) * ks];
+      return f;
+    }
+  } else {
+    return p[r * rs + (k0 + g) * ks];
+  }
+}
+
+// acc += A[16 x kd] * B[kd x 16]; A(m,k) = a[m*a_rs + k*a_ks], B(k,n) = b[n*b_rs + k*b_ks].
+template <typename T, bool AKC, bool BKC>
+__device__ __forceinline__ void mma_tile(f32x4& acc, const T* a, int a_rs, int a_ks, const T* b,
+                                         int b_rs, int b_ks, int kd) {
+  for (int k0 = 0; k0 < kd; k0 += MM<T>::KS)
+    acc = mma(ldfrag<T, AKC>(a, a_rs, a_ks, k0), ldfrag<T, BKC>(b, b_rs, b_ks, k0), acc);
+}
+
+// acc += A[16 x 16] * B[16 x 16] (a 16-long contraction, e.g. one sub-chunk of
+// tokens).  bf16 uses v_mfma_f32_16x16x16_bf16 with slots 4*(l >> 4) + e.
+template <typename T, bool AKC, bool BKC>
+__device__ __forceinline__ void mma_k16(f32x4& acc, const T* a, int a_rs, int a_ks, const T* b,
+                                        int b_rs, int b_ks) {
+  if constexpr (std::is_same_v<T, bf16>) {
+    const int l = lane_id();
+    const int r = l & 15, kb = (l >> 4) * 4;
+    bf16x4 fa, fb;
+    if constexpr (AKC) {
+      fa = *reinterpret_cast<const bf16x4*>(a + r * a_rs + kb);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fa[e] = a[r * a_rs + (kb + e) * a_ks];
+    }
+    if constexpr (BKC) {
+      fb = *reinterpret_cast<const bf16x4*>(b + r * b_rs + kb);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fb[e] = b[r * b_rs + (kb + e) * b_ks];
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, fb, acc, 0, 0, 0);
+  } else {
+    mma_tile<float, false, false>(acc, a, a_rs, a_ks, b, b_rs, b_ks, 16);
+  }
+}
+
+// Row/column of the C fragment held by this lane.
+__device__ __forceinline__ int crow(int i) { return ((lane_id() >> 4) << 2) + i; }
+__device__ __forceinline__ int ccol() { return lane_id() & 15; }
+
+// Store a C tile: dst(m, n) = dst[m * rs + n * cs], rows m < mmax only.
+template <typename U>
+__device__ __forceinline__ void st_tile(const f32x4& acc, U* dst, int rs, int cs, int mmax = 16) {
+  const int n = ccol();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = crow(i);
+    if (m < mmax) dst[m * rs + n * cs] = fromf<U>(acc[i]);
+  }
+}
+
+// Copy rows [0, nvalid) of a [nrows x C] tile from global (row stride gs
+// elements) into LDS (row stride ls), zero-filling rows [nvalid, nrows).
+// 16-byte vectors; C * sizeof(T) must be a multiple of 16, as must gs and ls.
+template <typename T, int C>
+__device__ __forceinline__ void g2s(T* s, int ls, const T* g, int64_t gs, int nvalid, int nrows,
+                                    int tid, int nthr) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int PER = C / VEC;
+  for (int idx = tid; idx < nrows * PER; idx += nthr) {
+    const int r = idx / PER, c = (idx - r * PER) * VEC;
+    uint4 val = {0u, 0u, 0u, 0u};
+    if (r < nvalid) val = *reinterpret_cast<const uint4*>(g + (int64_t)r * gs + c);
+    *reinterpret_cast<uint4*>(s + r * ls + c) = val;
+  }
+}
+
+// Transposing copy: s[c * ls + r] = g[r * gs + c] for rows r < nvalid, zero for
+// r in [nvalid, nrows).
+template <typename T, int C>
+__device__ __forceinline__ void g2s_T(T* s, int ls, const T* g, int64_t gs, int nvalid, int nrows,
+                                      int tid, int nthr) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int PER = C / VEC;
+  for (int idx = tid; idx < nrows * PER; idx += nthr) {
+    const int r = idx / PER, c = (idx - r * PER) * VEC;
+    union {
+      uint4 u;
+      T e[VEC];
+    } val;
+    val.u = uint4{0u, 0u, 0u, 0u};
+    if (r < nvalid) val.u = *reinterpret_cast<const uint4*>(g + (int64_t)r * gs + c);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s[(c + e) * ls + r] = val.e[e];
+  }
+}
+
+// Copy rows [0, nvalid) of an LDS tile back to global with 16-byte vectors.
+template <typename T, int C>
+__device__ __forceinline__ void s2g(T* g, int64_t gs, const T* s, int ls, int nvalid, int tid,
+                                    int nthr) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int PER = C / VEC;
+  for (int idx = tid; idx < nvalid * PER; idx += nthr) {
+    const int r = idx / PER, c = (idx - r * PER) * VEC;
+    *reinterpret_cast<uint4*>(g + (int64_t)r * gs + c) =
+        *reinterpret_cast<const uint4*>(s + r * ls + c);
+  }
+}
+
+// beta may be stored as bf16 or fp32 independently of the feature dtype.
+__device__ __forceinline__ float ld_beta(const void* p, int is_f32, int64_t idx) {
+  return is_f32 ? reinterpret_cast<const float*>(p)[idx]
+                : (float)reinterpret_cast<const bf16*>(p)[idx];
+}
+__device__ __forceinline__ void st_beta(void* p, int is_f32, int64_t idx, float v) {
+  if (is_f32)
+    reinterpret_cast<float*>(p)[idx] = v;
+  else
+    reinterpret_cast<bf16*>(p)[idx] = (bf16)v;
+}
+
+// LDS row pitch (elements) for a row of C elements of type T: +16 bytes of
+// padding keeps 16-byte alignment and spreads rows over the banks.
+template <typename T>
+constexpr int pitch(int C) {
+  return C + 16 / (int)sizeof(T);
+}
+
+}  // namespace rewy

@@ -1,0 +1,53 @@
+// Chunk-parallel output (ReWY paper, "The chunk system": O = Qg S + Cq R;
+// KDA blog section 6.5: read the decayed incoming state, then add the causal
+// in-chunk writes).  One workgroup per (chunk, head).
+#include "chunk_common.hpp"
+
+namespace rewy {
+
+template <typename T, int K, int V>
+__global__ __launch_bounds__(256) void k_fwd_out(Args a) {
+  constexpr int PK = pitch<T>(K), PA = pitch<T>(CH);
+  __shared__ __align__(16) T sQg[CH * PK];
+  __shared__ __align__(16) T sHt[V * PK];  // state S_c as operand, [v][k]
+  __shared__ __align__(16) T sCq[CH * PA];
+  __shared__ __align__(16) T sRt[V * PA];  // R as operand, [v][i]
+
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const ChunkInfo ci = a.chunks[c];
+  const int len = ci.len;
+  if (len == 0) return;
+  const int H = a.H;
+  const int64_t t0 = ci.bos;
+  const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
+  g2s<T, K>(sQg, PK, reinterpret_cast<const T*>(a.Qg) + (t0 * H + h) * K, gsK, len, CH, tid, 256);
+  g2s_T<T, V>(sHt, PK, reinterpret_cast<const T*>(a.hbuf) + ((int64_t)c * H + h) * K * V, V, K, K,
+              tid, 256);
+  g2s<T, CH>(sCq, PA, reinterpret_cast<const T*>(a.Cq) + ((int64_t)c * H + h) * CH * CH, CH, CH,
+             CH, tid, 256);
+  g2s_T<T, V>(sRt, PA, reinterpret_cast<const T*>(a.R) + (t0 * H + h) * V, gsV, len, CH, tid, 256);
+  __syncthreads();
+  T* og = reinterpret_cast<T*>(a.o) + (t0 * H + h) * V;
+  const int w = wave_id();
+  for (int cb = w; cb < V / SUB; cb += 4) {
+    for (int I = 0; I < NSUB && I * SUB < len; ++I) {
+      f32x4 acc = zero4();
+      mma_tile<T, true, true>(acc, sQg + I * SUB * PK, PK, 1, sHt + cb * SUB * PK, PK, 1, K);
+      const int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
+      mma_tile<T, true, true>(acc, sCq + I * SUB * PA, PA, 1, sRt + cb * SUB * PA, PA, 1, kd);
+      st_tile<T>(acc, og + (I * SUB) * gsV + cb * SUB, (int)gsV, 1, len - I * SUB);
+    }
+  }
+}
+
+template <typename T>
+static hipError_t out_t(const Args& a, hipStream_t s) {
+  const dim3 grid(a.nc_max, a.H), block(256);
+  REWY_KV_SWITCH(k_fwd_out)
+}
+
+hipError_t launch_fwd_out(const Args& a, int f32, hipStream_t s) {
+  return f32 ? out_t<float>(a, s) : out_t<bf16>(a, s);
+}
+
+}  // namespace rewy

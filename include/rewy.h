@@ -1,0 +1,139 @@
+/*
+ * rewy.h -- C ABI of the MI355X (gfx950) chunkwise gated delta-rule operator
+ * with the ReWY backward.  librewy.so exports exactly the functions below.
+ *
+ * What the operator computes (ReWY paper, "Background / Delta-rule operators",
+ * Table 1; KDA blog, section 4 boxed equations).  For every sequence n and head
+ * h, with the state S in [K,V] layout (fp32), tokens t in order:
+ *     S~  = diag(exp g_t) S                 decay (g_t natural log, <= 0 expected)
+ *     r_t = beta_t (v_t - S~^T k_t)         predict from the decayed state, correct
+ *     S   = S~ + k_t r_t^T                  rank-one write
+ *     o_t = S^T (scale * q_t)               read after the write
+ * Gate kinds (Table 1): NONE = DeltaNet (g = 0), SCALAR = Gated DeltaNet (one g
+ * per token and head), VECTOR = KDA (one g per token, head and key channel).
+ * rewy_fwd returns o and the final states; rewy_bwd returns the gradients of
+ * l = <dO, o> + <dht, ht> with respect to q, k, v, g, beta and h0, computed in
+ * the chunkwise WY form (Appendix A) with the ReWY local pullback (Algorithm 1:
+ * P = A^T Rbar, D = -tril_strict(P R^T)), matrix-intra contractions for the
+ * vector gate (section 3.3) and the Gram-free reduction for the scalar gate
+ * (section 3.4), in the complete reverse order of Appendix 10.
+ *
+ * Layouts (all row-major, contiguous, token-major as in the pages' code):
+ *   q, k            [B, T, H, K]   dtype
+ *   v, o, dO        [B, T, H, V]   dtype
+ *   g               NULL (NONE) | [B, T, H] fp32 (SCALAR) | [B, T, H, K] fp32 (VECTOR)
+ *   beta, dbeta     [B, T, H]      beta_dtype
+ *   h0, ht, dht, dh0 [N, H, K, V]  fp32
+ *   dq, dk [B,T,H,K] dtype; dv [B,T,H,V] dtype; dg same shape as g, fp32.
+ * With cu_seqlens (device int32, N+1 ascending offsets, [0] = 0, [N] = T) the
+ * batch must be B = 1 and the N sequences are packed along T; chunks of 64
+ * tokens restart at every sequence start and the last chunk of a sequence may
+ * be partial.  Without it, N = B and every batch row is one sequence.
+ *
+ * Ownership and execution.  Every pointer except desc and cu_seqlens_host is a
+ * device pointer owned by the caller.  The library never allocates device
+ * memory and keeps no state between calls: scratch comes from the caller's
+ * workspace (size from rewy_workspace_bytes) and, for the save-all policy,
+ * forward intermediates go to the caller's `saved` buffer (size from
+ * rewy_saved_bytes), which must stay unchanged, together with the inputs,
+ * between rewy_fwd and rewy_bwd.  All work is enqueued on `stream` (a
+ * hipStream_t; NULL = the null stream) and the call returns without waiting.
+ * Outputs are overwritten, never accumulated into.  Calls on distinct streams
+ * with distinct buffers may run concurrently.  No atomics: results are
+ * bitwise reproducible for a given shape.
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued; a
+ * failed check returns a negative rewy_status and has no side effect.
+ * rewy_last_error() gives a thread-local text for the last failure.  Faults
+ * inside kernels surface asynchronously at the caller's next synchronisation.
+ */
+#ifndef REWY_H
+#define REWY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    REWY_OK = 0,
+    REWY_EINVAL = -1,       /* malformed argument (null pointer, bad shape, bad cu_seqlens) */
+    REWY_EUNSUPPORTED = -2, /* valid request this build does not implement (K, V not in {32,64,128}) */
+    REWY_EWORKSPACE = -3,   /* workspace or saved buffer too small or misaligned */
+    REWY_EHIP = -4          /* a HIP launch or copy reported an error */
+} rewy_status;
+
+typedef enum { REWY_GATE_NONE = 0, REWY_GATE_SCALAR = 1, REWY_GATE_VECTOR = 2 } rewy_gate;
+typedef enum { REWY_BF16 = 0, REWY_F32 = 1 } rewy_dtype;
+/* Saving policies of the ReWY paper (section 4.1): RECOMPUTE re-runs the forward
+ * chunk stages inside rewy_bwd; SAVE keeps them from rewy_fwd in `saved`. */
+typedef enum { REWY_RECOMPUTE = 0, REWY_SAVE = 1 } rewy_policy;
+
+typedef struct {
+    int32_t B, T, H, K, V;          /* K, V in {32, 64, 128} */
+    int32_t N;                      /* sequences: B without cu_seqlens, else len(cu_seqlens)-1 */
+    const int32_t *cu_seqlens;      /* device [N+1] or NULL */
+    const int32_t *cu_seqlens_host; /* optional host copy of cu_seqlens, validated if given */
+    int32_t dtype;                  /* rewy_dtype of q, k, v, o, dO, dq, dk, dv */
+    int32_t beta_dtype;             /* rewy_dtype of beta and dbeta */
+    int32_t gate;                   /* rewy_gate */
+    int32_t policy;                 /* rewy_policy */
+    float scale;                    /* query scale, usually K^-1/2 */
+} rewy_desc;
+
+/* Bytes of device workspace a call needs: phase 0 = rewy_fwd, 1 = rewy_bwd.
+ * Returns 0 for an invalid descriptor (see rewy_last_error). */
+size_t rewy_workspace_bytes(const rewy_desc *d, int phase);
+
+/* Bytes of the `saved` buffer for policy SAVE (0 for RECOMPUTE). */
+size_t rewy_saved_bytes(const rewy_desc *d);
+
+/* Forward.  h0 may be NULL (zero initial state); ht may be NULL (final state
+ * not returned); saved must be non-NULL for policy SAVE.  workspace must be
+ * 256-byte aligned and at least rewy_workspace_bytes(d, 0) long. */
+int rewy_fwd(const rewy_desc *d, const void *q, const void *k, const void *v,
+             const float *g, const void *beta, const float *h0,
+             void *o, float *ht, void *saved,
+             void *workspace, size_t ws_bytes, void *stream);
+
+/* Backward.  dht may be NULL (zero terminal adjoint).  dg must be NULL exactly
+ * when gate == NONE.  dh0 must be non-NULL when h0 is non-NULL and may be
+ * non-NULL otherwise (then it is the gradient for a zero initial state).
+ * For policy SAVE, `saved` must hold what rewy_fwd wrote for the same inputs;
+ * for RECOMPUTE it is ignored. */
+int rewy_bwd(const rewy_desc *d, const void *q, const void *k, const void *v,
+             const float *g, const void *beta, const float *h0,
+             const void *dO, const float *dht, const void *saved,
+             void *dq, void *dk, void *dv, float *dg, void *dbeta, float *dh0,
+             void *workspace, size_t ws_bytes, void *stream);
+
+/* Per-kernel timing (a tracing aid: device events, as in the ReWY paper's timing
+ * protocol).  After rewy_trace_begin(), calls made by this thread
+ * record a HIP event pair on the call's stream around every kernel they
+ * enqueue.  rewy_trace_end() waits for the recorded events, stops recording and
+ * fills at most `cap` entries, one per kernel name (the name rocprofv3 shows),
+ * with the summed elapsed milliseconds and the launch count; it returns the
+ * number of entries, or a negative rewy_status.  Not for use under graph
+ * capture.  Events are created once per thread and reused. */
+typedef struct {
+    char kernel[96];
+    double total_ms;
+    int launches;
+} rewy_trace_entry;
+
+int rewy_trace_begin(void);
+int rewy_trace_end(rewy_trace_entry *out, int cap);
+
+/* Name of a rewy_status value. */
+const char *rewy_status_string(int status);
+
+/* Thread-local description of the last failed call on this thread. */
+const char *rewy_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REWY_H */

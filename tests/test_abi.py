@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/rewy.h declares, and rejects malformed descriptors on the host before
+anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunkwise_delta_rule_chunk_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "rewy.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rewy_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("librewy.so is not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = _declared()
+    assert decl == sorted(B.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {B.LIB_PATH}").read()
+    exported = sorted(set(re.findall(r"\bT (rewy_[a-z_]+)\b", out)))
+    assert exported == decl  # nothing else of ours is exported
+
+
+def _desc(**kw):
+    d = dict(B=1, T=256, H=2, K=128, V=128, N=0, cu_seqlens=None, cu_seqlens_host=None,
+             dtype=B.REWY_BF16, beta_dtype=B.REWY_BF16, gate=B.REWY_GATE_VECTOR,
+             policy=B.REWY_RECOMPUTE, scale=128 ** -0.5)
+    d.update(kw)
+    return B.RewyDesc(**d)
+
+
+def test_status_strings(lib):
+    assert B.rewy_status_string(0) == "REWY_OK"
+    assert B.rewy_status_string(-1) == "REWY_EINVAL"
+    assert B.rewy_status_string(-2) == "REWY_EUNSUPPORTED"
+    assert B.rewy_status_string(-3) == "REWY_EWORKSPACE"
+    assert B.rewy_status_string(-4) == "REWY_EHIP"
+    assert B.rewy_status_string(99) == "REWY_UNKNOWN"
+
+
+@pytest.mark.parametrize("bad,msg", [
+    (dict(K=48), "not supported"), (dict(V=256), "not supported"), (dict(K=300), "exceeds 256"),
+    (dict(B=0), "bad shape"), (dict(H=-1), "bad shape"), (dict(dtype=7), "bad dtype"),
+    (dict(gate=3), "bad gate"), (dict(policy=5), "bad policy"),
+    (dict(dtype=B.REWY_F32, K=128), "not supported"), (dict(N=3), "must equal B"),
+])
+def test_invalid_descriptor_rejected(lib, bad, msg):
+    assert B.rewy_workspace_bytes(_desc(**bad), 0) == 0
+    assert msg in B.rewy_last_error()
+
+
+def test_cu_seqlens_validation(lib):
+    cu = (ctypes.c_int32 * 4)(0, 10, 5, 256)  # not ascending
+    d = _desc(N=3, cu_seqlens=8, cu_seqlens_host=ctypes.addressof(cu))
+    assert B.rewy_workspace_bytes(d, 0) == 0 and "not ascending" in B.rewy_last_error()
+    cu2 = (ctypes.c_int32 * 3)(0, 100, 200)  # does not end at T
+    d = _desc(N=2, cu_seqlens=8, cu_seqlens_host=ctypes.addressof(cu2))
+    assert B.rewy_workspace_bytes(d, 0) == 0 and "end at T" in B.rewy_last_error()
+    d = _desc(B=2, N=2, cu_seqlens=8)
+    assert B.rewy_workspace_bytes(d, 0) == 0 and "B == 1" in B.rewy_last_error()
+
+
+def test_workspace_sizes_follow_the_layout(lib):
+    d = _desc()
+    nc = 4  # 256 tokens / 64
+    e, H, K, V, BT = 2, 2, 128, 128, 256
+    up = lambda x: (x + 255) // 256 * 256
+    head = up(nc * 16) + up(2 * 4) + up(BT * H * V * e)
+    fwd_set = 3 * up(BT * H * K * e) + up(nc * H * 64 * 64 * e) + up(nc * H * K * 4) + \
+        up(nc * H * K * V * e) + up(BT * H * V * e)
+    bwd_set = up(BT * H * V * e) * 2 + up(nc * H * K * V * e) + 2 * up(nc * H * 64 * 64 * e) + \
+        up(BT * H * 4)
+    assert B.rewy_workspace_bytes(d, 0) == head + fwd_set
+    assert B.rewy_workspace_bytes(d, 1) == head + fwd_set + bwd_set
+    assert B.rewy_saved_bytes(d) == 0
+    ds = _desc(policy=B.REWY_SAVE)
+    assert B.rewy_saved_bytes(ds) == fwd_set
+    assert B.rewy_workspace_bytes(ds, 0) == head
+    assert B.rewy_workspace_bytes(ds, 1) == head + bwd_set
+
+
+def test_calls_reject_bad_pointers_without_launching(lib):
+    d = _desc()
+    ws = ctypes.create_string_buffer(1024)
+    P = ctypes.c_void_p
+    # q is NULL: host-side rejection, nothing enqueued
+    rc = B.rewy_fwd(d, None, P(256), P(256), P(256), P(256), None, P(256), None, None,
+                    P(256), 1 << 40, None)
+    assert rc == B.REWY_EINVAL and "q is NULL" in B.rewy_last_error()
+    # missing gate for a gated descriptor
+    rc = B.rewy_fwd(d, P(256), P(256), P(256), None, P(256), None, P(256), None, None,
+                    P(256), 1 << 40, None)
+    assert rc == B.REWY_EINVAL and "g must be given" in B.rewy_last_error()
+    # workspace too small
+    rc = B.rewy_fwd(d, P(256), P(256), P(256), P(256), P(256), None, P(256), None, None,
+                    P(256), 16, None)
+    assert rc == B.REWY_EWORKSPACE
+    # misaligned tensor
+    rc = B.rewy_fwd(d, P(258), P(256), P(256), P(256), P(256), None, P(256), None, None,
+                    P(256), 1 << 40, None)
+    assert rc == B.REWY_EINVAL and "aligned" in B.rewy_last_error()
+    # h0 without dh0 in the backward
+    rc = B.rewy_bwd(d, P(256), P(256), P(256), P(256), P(256), P(256), P(256), None, None,
+                    P(256), P(256), P(256), P(256), P(256), None, P(256), 1 << 40, None)
+    assert rc == B.REWY_EINVAL and "dh0" in B.rewy_last_error()
+    # dg missing for a gated backward
+    rc = B.rewy_bwd(d, P(256), P(256), P(256), P(256), P(256), None, P(256), None, None,
+                    P(256), P(256), P(256), None, P(256), None, P(256), 1 << 40, None)
+    assert rc == B.REWY_EINVAL and "dg" in B.rewy_last_error()
+    # save-all policy without the saved buffer
+    dsv = _desc(policy=B.REWY_SAVE)
+    rc = B.rewy_fwd(dsv, P(256), P(256), P(256), P(256), P(256), None, P(256), None, None,
+                    P(256), 1 << 40, None)
+    assert rc == B.REWY_EWORKSPACE
+    del ws
+
+
+def test_product_path_has_no_fallback():
+    """The package never imports the oracle and raises when the library is missing."""
+    import chunkwise_delta_rule_chunk_amd as pkg
+    pkg_dir = os.path.dirname(pkg.__file__)
+    for name in os.listdir(pkg_dir):
+        if name.endswith(".py"):
+            src = open(os.path.join(pkg_dir, name)).read()
+            assert "import oracle" not in src and "from oracle" not in src, name
+    saved, B._lib, path = B._lib, None, B.LIB_PATH
+    try:
+        B.LIB_PATH = path + ".missing"
+        with pytest.raises(RuntimeError, match="missing"):
+            B.load()
+    finally:
+        B.LIB_PATH, B._lib = path, saved
