@@ -43,7 +43,7 @@ def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq):
                       + n * (2 * tok_k + gb + besz),
     }
     for name, b in per_head.items():
-        if f"rewy::{name}<" in kernel:
+        if f"{len(name)}{name}I" in kernel:
             extra = 0
             if name in ("k_fwd_scan", "k_bwd_scan"):
                 extra = nseq * 2 * 4 * K * V  # initial / final state (fp32) per sequence

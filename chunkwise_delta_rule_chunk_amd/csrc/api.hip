@@ -352,14 +352,15 @@ REWY_API int rewy_trace_end(rewy_trace_entry* out, int cap) {
     if (hipEventSynchronize(r.e1) != hipSuccess) return fail(REWY_EHIP, "trace synchronise");
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) return fail(REWY_EHIP, "trace elapsed");
+    // the names rocprofv3 reports: the plain kernel demangled, the templates mangled
     char name[96];
     if (r.variant < 0) {
       snprintf(name, sizeof(name), "rewy::%s(rewy::Args)", r.stage);
     } else {
       const bool f32 = r.variant >= 1000000;
       const int kv = r.variant % 1000000;
-      snprintf(name, sizeof(name), "void rewy::%s<%s, %d, %d>(rewy::Args)", r.stage,
-               f32 ? "float" : "__bf16", kv / 1000, kv % 1000);
+      snprintf(name, sizeof(name), "_ZN4rewy%zu%sI%sLi%dELi%dEEEvNS_4ArgsE", strlen(r.stage),
+               r.stage, f32 ? "f" : "DF16b", kv / 1000, kv % 1000);
     }
     size_t i = 0;
     while (i < agg.size() && strcmp(agg[i].kernel, name) != 0) ++i;

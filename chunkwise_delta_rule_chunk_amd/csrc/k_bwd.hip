@@ -179,21 +179,20 @@ __global__ __launch_bounds__(256) void k_bwd_cons(Args a) {
 
   __shared__ __align__(16) T sD[CH * PA];
   __shared__ __align__(16) T sHq[CH * PA];
-  __shared__ __align__(16) T sDT[BF ? CH * PA : 8];   // D^T, [j][i]
-  __shared__ __align__(16) T sHqT[BF ? CH * PA : 8];  // Hq^T
   __shared__ __align__(16) T sdO[CH * PV];
   __shared__ __align__(16) T sP[CH * PV];
   __shared__ __align__(16) T sR[CH * PV];
   __shared__ __align__(16) float sG[CH * PGT];
   __shared__ __align__(16) T sK[CH * PKT];
   __shared__ __align__(16) T sQ[CH * PKT];
-  // scaled sending operands, [feature][token]
-  __shared__ __align__(16) T sKcE[KT * PA];  // k exp2(Gl_J - G)
-  __shared__ __align__(16) T sKcM[KT * PA];  // k exp2(mid_J - G)
-  __shared__ __align__(16) T sKaF[KT * PA];  // beta k exp2(G - Gf_I)
-  __shared__ __align__(16) T sKaM[KT * PA];  // beta k exp2(G - mid_I)
-  __shared__ __align__(16) T sQaF[KT * PA];  // s q exp2(G - Gf_I)
-  __shared__ __align__(16) T sQaM[KT * PA];  // s q exp2(G - mid_I)
+  // scaled sending operands, [feature][token]; for bf16 each is held as a
+  // high part and a low part (x ~ hi + lo) so that the matrix-intra products
+  // keep about 16 mantissa bits of the sending side: the log-gate gradient is a
+  // difference of nearly equal receiving and sending sums, which amplifies the
+  // rounding of these operands.
+  constexpr int NPART = BF ? 2 : 1;
+  __shared__ __align__(16) T sSc[6 * NPART][KT * PA];
+  enum { KC_E = 0, KC_M = 1, KA_F = 2, KA_M = 3, QA_F = 4, QA_M = 5 };
   __shared__ __align__(16) float sGb[CH * PGT];
   __shared__ float sBeta[CH], sDbe[CH], sGs[CH];
   __shared__ float sGf[NSUB * KT], sGl[NSUB * KT], sMid[NSUB * KT];
@@ -215,10 +214,6 @@ __global__ __launch_bounds__(256) void k_bwd_cons(Args a) {
     const T* Hg = reinterpret_cast<const T*>(a.Hq) + ((int64_t)c * H + h) * CH * CH;
     g2s<T, CH>(sD, PA, Dg, CH, CH, CH, tid, NTH);
     g2s<T, CH>(sHq, PA, Hg, CH, CH, CH, tid, NTH);
-    if constexpr (BF) {
-      g2s_T<T, CH>(sDT, PA, Dg, CH, CH, CH, tid, NTH);
-      g2s_T<T, CH>(sHqT, PA, Hg, CH, CH, CH, tid, NTH);
-    }
   }
   g2s<T, V>(sdO, PV, reinterpret_cast<const T*>(a.dO) + (t0 * H + h) * V, gsV, n, CH, tid, NTH);
   g2s<T, V>(sP, PV, reinterpret_cast<const T*>(a.P) + (t0 * H + h) * V, gsV, n, CH, tid, NTH);
@@ -265,14 +260,16 @@ __global__ __launch_bounds__(256) void k_bwd_cons(Args a) {
       const float G = sG[j * PGT + kk];
       const float kv = tof(sK[j * PKT + kk]), qv = tof(sQ[j * PKT + kk]), b = sBeta[j];
       const float gl = sGl[J * KT + kk], gf = sGf[J * KT + kk], md = sMid[J * KT + kk];
-      sKcE[kk * PA + j] = fromf<T>(kv * exp2f(gl - G));
-      sKaF[kk * PA + j] = fromf<T>(b * kv * exp2f(G - gf));
-      sQaF[kk * PA + j] = fromf<T>(scale * qv * exp2f(G - gf));
       const bool cen = !sFlag[J];
       const float em = cen ? exp2f(md - G) : 0.f, ep = cen ? exp2f(G - md) : 0.f;
-      sKcM[kk * PA + j] = fromf<T>(kv * em);
-      sKaM[kk * PA + j] = fromf<T>(b * kv * ep);
-      sQaM[kk * PA + j] = fromf<T>(scale * qv * ep);
+      const float val[6] = {kv * exp2f(gl - G), kv * em, b * kv * exp2f(G - gf), b * kv * ep,
+                            scale * qv * exp2f(G - gf), scale * qv * ep};
+#pragma unroll
+      for (int o = 0; o < 6; ++o) {
+        const T hi = fromf<T>(val[o]);
+        sSc[o * NPART][kk * PA + j] = hi;
+        if constexpr (BF) sSc[o * NPART + 1][kk * PA + j] = fromf<T>(val[o] - tof(hi));
+      }
     }
     __syncthreads();
 
@@ -290,28 +287,27 @@ __global__ __launch_bounds__(256) void k_bwd_cons(Args a) {
         // -- matrix intra, receiving block I ----------------------------------
         f32x4 XHY = zero4(), XDY = zero4(), XDE = zero4(), XHQ = zero4();
         const float gfI = sGf[I * KT + kc], glI = sGl[I * KT + kc], mdI = sMid[I * KT + kc];
+        // acc += M-block (rows of this wave's block) x sending operand op (all parts)
+        auto mm = [&](f32x4& acc, const T* m, int m_rs, int m_ks, int op, int src) {
+#pragma unroll
+          for (int pt = 0; pt < NPART; ++pt) {
+            const T* B = sSc[op * NPART + pt] + kl * PA + src * SUB;
+            if (m_ks == 1) mma_k16<T, true, true>(acc, m, m_rs, 1, B, PA, 1);
+            else mma_k16<T, false, true>(acc, m, 1, m_ks, B, PA, 1);
+          }
+        };
         for (int J = 0; J < I; ++J) {  // sources before I: gamma (H Y), gamma (D Y)
           f32x4 tH = zero4(), tD = zero4();
-          const T* B = sKcE + kl * PA + J * SUB;
-          mma_k16<T, true, true>(tH, sHq + I * SUB * PA + J * SUB, PA, 1, B, PA, 1);
-          mma_k16<T, true, true>(tD, sD + I * SUB * PA + J * SUB, PA, 1, B, PA, 1);
+          mm(tH, sHq + I * SUB * PA + J * SUB, PA, 1, KC_E, J);
+          mm(tD, sD + I * SUB * PA + J * SUB, PA, 1, KC_E, J);
           const float cf = exp2f(gfI - sGl[J * KT + kc]);
           XHY += cf * tH;
           XDY += cf * tD;
         }
         for (int J2 = I + 1; J2 < NSUB && J2 * SUB < n; ++J2) {  // sources after I: transposed
           f32x4 tE = zero4(), tQ = zero4();
-          if constexpr (BF) {
-            mma_k16<T, true, true>(tE, sDT + I * SUB * PA + J2 * SUB, PA, 1,
-                                   sKaF + kl * PA + J2 * SUB, PA, 1);
-            mma_k16<T, true, true>(tQ, sHqT + I * SUB * PA + J2 * SUB, PA, 1,
-                                   sQaF + kl * PA + J2 * SUB, PA, 1);
-          } else {
-            mma_k16<T, false, true>(tE, sD + J2 * SUB * PA + I * SUB, 1, PA,
-                                    sKaF + kl * PA + J2 * SUB, PA, 1);
-            mma_k16<T, false, true>(tQ, sHq + J2 * SUB * PA + I * SUB, 1, PA,
-                                    sQaF + kl * PA + J2 * SUB, PA, 1);
-          }
+          mm(tE, sD + J2 * SUB * PA + I * SUB, 1, PA, KA_F, J2);   // D^T block, read strided
+          mm(tQ, sHq + J2 * SUB * PA + I * SUB, 1, PA, QA_F, J2);
           const float cf = exp2f(sGf[J2 * KT + kc] - glI);
           XDE += cf * tE;
           XHQ += cf * tQ;
@@ -330,21 +326,10 @@ __global__ __launch_bounds__(256) void k_bwd_cons(Args a) {
         // diagonal block I
         if (!sFlag[I]) {
           f32x4 tH = zero4(), tD = zero4(), tE = zero4(), tQ = zero4();
-          mma_k16<T, true, true>(tH, sHq + I * SUB * PA + I * SUB, PA, 1, sKcM + kl * PA + I * SUB,
-                                 PA, 1);
-          mma_k16<T, true, true>(tD, sD + I * SUB * PA + I * SUB, PA, 1, sKcM + kl * PA + I * SUB,
-                                 PA, 1);
-          if constexpr (BF) {
-            mma_k16<T, true, true>(tE, sDT + I * SUB * PA + I * SUB, PA, 1,
-                                   sKaM + kl * PA + I * SUB, PA, 1);
-            mma_k16<T, true, true>(tQ, sHqT + I * SUB * PA + I * SUB, PA, 1,
-                                   sQaM + kl * PA + I * SUB, PA, 1);
-          } else {
-            mma_k16<T, false, true>(tE, sD + I * SUB * PA + I * SUB, 1, PA,
-                                    sKaM + kl * PA + I * SUB, PA, 1);
-            mma_k16<T, false, true>(tQ, sHq + I * SUB * PA + I * SUB, 1, PA,
-                                    sQaM + kl * PA + I * SUB, PA, 1);
-          }
+          mm(tH, sHq + I * SUB * PA + I * SUB, PA, 1, KC_M, I);
+          mm(tD, sD + I * SUB * PA + I * SUB, PA, 1, KC_M, I);
+          mm(tE, sD + I * SUB * PA + I * SUB, 1, PA, KA_M, I);
+          mm(tQ, sHq + I * SUB * PA + I * SUB, 1, PA, QA_M, I);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float fr = exp2f(Gv[i] - mdI), fc = exp2f(mdI - Gv[i]);
@@ -421,7 +406,7 @@ __global__ __launch_bounds__(256) void k_bwd_cons(Args a) {
         float run = 0.f;
         for (int i = n - 1; i >= 0; --i) {
           run += sGb[i * PGT + kk];
-          a.dg[(t0 + i) * gsK + kf0 + kk] = run;
+          a.dg[((t0 + i) * H + h) * K + kf0 + kk] = run;
         }
       }
     } else if (a.gate == 1) {
