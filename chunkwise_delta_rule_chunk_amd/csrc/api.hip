@@ -90,46 +90,68 @@ int make_plan(const rewy_desc* d, Plan& p) {
 
 // Buffer layout.  `saved` holds what the backward reads from the forward under
 // the save-all policy; everything else is scratch in the workspace.
+//   recompute: ws = [index | glast hbuf R | W Ft U | (fwd) Qg Cq  / (bwd) F Wt Qgt Cqt | bwd set]
+//   save-all:  saved = [glast hbuf R F Wt Qgt Cqt]
+//              ws (fwd) = [index | W Ft U Qg Cq],  ws (bwd) = [index | bwd set]
 struct Layout {
-  size_t chunks, seqoff, W, U, F, Qg, Cq, glast, hbuf, R;   // forward set
-  size_t Rb, dhbuf, P, D, Hq, dbw;                           // backward set
+  size_t chunks, seqoff;
+  size_t glast, hbuf, R;             // read by output and backward
+  size_t W, Ft, U;                   // forward scan operands
+  size_t Qg, Cq;                     // output operands
+  size_t F, Wt, Qgt, Cqt;            // reverse scan operands
+  size_t Rb, dhbuf, P, D, Hq, dbw;   // backward set
   size_t ws_fwd, ws_bwd, saved;
 };
 
 Layout layout(const Plan& p) {
   Layout L{};
   const size_t nc = p.nc_max, H = p.H, K = p.K, V = p.V, BT = p.BT, e = p.esz;
+  const size_t tokK = BT * H * K * e, tokV = BT * H * V * e;
+  const size_t tileK = nc * H * K * CH * e, tile64 = nc * H * CH * CH * e;
   size_t off = 0;
-  auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
-  // workspace always starts with the chunk index
-  L.chunks = take(nc * sizeof(ChunkInfo));
-  L.seqoff = take((size_t)(p.N + 1) * 4);
-  L.U = take(BT * H * V * e);
-  const size_t ws_head = off;
-  // forward set: in the workspace (recompute) or in `saved` (save-all)
-  size_t s = (p.policy == REWY_SAVE) ? 0 : off;
-  auto takef = [&](size_t bytes) { size_t o = s; s += up(bytes); return o; };
-  L.W = takef(BT * H * K * e);
-  L.F = takef(BT * H * K * e);
-  L.Qg = takef(BT * H * K * e);
-  L.Cq = takef(nc * H * CH * CH * e);
-  L.glast = takef(nc * H * K * 4);
-  L.hbuf = takef(nc * H * K * V * e);
-  L.R = takef(BT * H * V * e);
-  if (p.policy == REWY_SAVE) {
-    L.saved = s;
-    off = ws_head;
+  auto take = [&](size_t& o, size_t bytes) { const size_t r = o; o += up(bytes); return r; };
+  L.chunks = take(off, nc * sizeof(ChunkInfo));
+  L.seqoff = take(off, (size_t)(p.N + 1) * 4);
+  const size_t head = off;
+  const bool save = p.policy == REWY_SAVE;
+  size_t s = save ? 0 : off;
+  L.glast = take(s, nc * H * K * 4);
+  L.hbuf = take(s, nc * H * K * V * e);
+  L.R = take(s, tokV);
+  size_t bs = save ? s : 0;  // reverse-scan set: in `saved` for save-all
+  if (save) {
+    L.F = take(bs, tokK);
+    L.Wt = take(bs, tileK);
+    L.Qgt = take(bs, tileK);
+    L.Cqt = take(bs, tile64);
+    L.saved = bs;
+    off = head;
   } else {
-    L.saved = 0;
     off = s;
   }
+  L.W = take(off, tokK);
+  L.Ft = take(off, tileK);
+  L.U = take(off, tokV);
+  const size_t after_scan = off;
+  L.Qg = take(off, tokK);
+  L.Cq = take(off, tile64);
   L.ws_fwd = off;
-  L.Rb = take(BT * H * V * e);
-  L.dhbuf = take(nc * H * K * V * e);
-  L.P = take(BT * H * V * e);
-  L.D = take(nc * H * CH * CH * e);
-  L.Hq = take(nc * H * CH * CH * e);
-  L.dbw = take(BT * H * 4);
+  if (save) {
+    off = head;
+  } else {
+    size_t u = after_scan;  // reverse-scan set shares the output operands' space
+    L.F = take(u, tokK);
+    L.Wt = take(u, tileK);
+    L.Qgt = take(u, tileK);
+    L.Cqt = take(u, tile64);
+    off = u;
+  }
+  L.Rb = take(off, tokV);
+  L.dhbuf = take(off, nc * H * K * V * e);
+  L.P = take(off, tokV);
+  L.D = take(off, tile64);
+  L.Hq = take(off, tile64);
+  L.dbw = take(off, BT * H * 4);
   L.ws_bwd = off;
   return L;
 }
@@ -154,17 +176,18 @@ int copy_state(float* dst, const float* src, int64_t n, hipStream_t s) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-void fill_common(Args& a, const Plan& p, const rewy_desc* d, char* ws, char* fs,
+void fill_common(Args& a, const Plan& p, const rewy_desc* d, char* ws, char* sv,
                  const Layout& L) {
   memset(&a, 0, sizeof(a));
   a.B = p.B; a.T = p.T; a.H = p.H; a.K = p.K; a.V = p.V; a.N = p.N; a.nc_max = p.nc_max;
   a.gate = p.gate; a.beta_f32 = p.beta_f32; a.scale = d->scale; a.cu = d->cu_seqlens;
   a.chunks = reinterpret_cast<ChunkInfo*>(ws + L.chunks);
   a.seqoff = reinterpret_cast<int*>(ws + L.seqoff);
-  a.U = ws + L.U;
-  a.W = fs + L.W; a.F = fs + L.F; a.Qg = fs + L.Qg; a.Cq = fs + L.Cq;
+  char* fs = p.policy == REWY_SAVE ? sv : ws;  // where the saved set lives
   a.glast = reinterpret_cast<float*>(fs + L.glast);
   a.hbuf = fs + L.hbuf; a.R = fs + L.R;
+  a.F = fs + L.F; a.Wt = fs + L.Wt; a.Qgt = fs + L.Qgt; a.Cqt = fs + L.Cqt;
+  a.W = ws + L.W; a.Ft = ws + L.Ft; a.U = ws + L.U; a.Qg = ws + L.Qg; a.Cq = ws + L.Cq;
   a.Rb = ws + L.Rb; a.dhbuf = ws + L.dhbuf; a.P = ws + L.P; a.D = ws + L.D; a.Hq = ws + L.Hq;
   a.dbw = reinterpret_cast<float*>(ws + L.dbw);
 }
@@ -275,9 +298,9 @@ REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const vo
     return fail(REWY_EWORKSPACE, "policy SAVE needs a 256-byte aligned saved buffer of %zu bytes",
                 L.saved);
   Args a;
-  char* ws = static_cast<char*>(workspace);
-  fill_common(a, p, d, ws, p.policy == REWY_SAVE ? static_cast<char*>(saved) : ws, L);
+  fill_common(a, p, d, static_cast<char*>(workspace), static_cast<char*>(saved), L);
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+  a.prep_mode = PREP_FWD_SCAN | PREP_FWD_OUT | (p.policy == REWY_SAVE ? PREP_BWD_SCAN : 0);
   return run_forward_stages(a, p.f32, true, s);
 }
 
@@ -311,9 +334,9 @@ REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const vo
   if (p.policy == REWY_SAVE && (!saved || !aligned(saved, ALIGN)))
     return fail(REWY_EWORKSPACE, "policy SAVE needs the saved buffer written by rewy_fwd");
   Args a;
-  char* ws = static_cast<char*>(workspace);
-  char* fs = p.policy == REWY_SAVE ? const_cast<char*>(static_cast<const char*>(saved)) : ws;
-  fill_common(a, p, d, ws, fs, L);
+  fill_common(a, p, d, static_cast<char*>(workspace),
+              const_cast<char*>(static_cast<const char*>(saved)), L);
+  a.prep_mode = PREP_FWD_SCAN | PREP_BWD_SCAN;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = dO; a.dht = dht;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
   const bool f32 = p.f32;

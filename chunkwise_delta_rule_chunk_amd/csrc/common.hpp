@@ -141,6 +141,20 @@ __device__ __forceinline__ void st_tile(const f32x4& acc, U* dst, int rs, int cs
   }
 }
 
+// Store a C tile transposed: dst[n * rs + m] for m = 4*(l>>4) .. +3 as one vector.
+template <typename U>
+__device__ __forceinline__ void st_tile_T(const f32x4& acc, U* dst, int rs) {
+  const int n = ccol(), m0 = crow(0);
+  if constexpr (std::is_same_v<U, bf16>) {
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)acc[i];
+    *reinterpret_cast<bf16x4*>(dst + n * rs + m0) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(dst + n * rs + m0) = acc;
+  }
+}
+
 // Copy rows [0, nvalid) of a [nrows x C] tile from global (row stride gs
 // elements) into LDS (row stride ls), zero-filling rows [nvalid, nrows).
 // 16-byte vectors; C * sizeof(T) must be a multiple of 16, as must gs and ls.
@@ -189,6 +203,53 @@ __device__ __forceinline__ void s2g(T* g, int64_t gs, const T* s, int ls, int nv
         *reinterpret_cast<const uint4*>(s + r * ls + c);
   }
 }
+
+// Register staging of a [ROWS x COLS] tile for software prefetch: load() issues
+// the global reads (rows >= nvalid read as zero), store() writes the tile into
+// LDS later, so the load latency overlaps whatever runs in between.
+template <typename T, int ROWS, int COLS, int NTH>
+struct Staged {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int PER = COLS / VEC;
+  static constexpr int TOTAL = ROWS * PER;
+  static constexpr int N = (TOTAL + NTH - 1) / NTH;
+  static_assert(COLS % VEC == 0, "row length must be a multiple of 16 bytes");
+  uint4 r[N];
+  __device__ __forceinline__ void load(const T* g, int64_t gs, int nvalid, int tid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = tid + j * NTH;
+      const int row = idx / PER, c = (idx - row * PER) * VEC;
+      r[j] = uint4{0u, 0u, 0u, 0u};
+      if (idx < TOTAL && row < nvalid) r[j] = *reinterpret_cast<const uint4*>(g + (int64_t)row * gs + c);
+    }
+  }
+  __device__ __forceinline__ void store(T* s, int ls, int tid) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = tid + j * NTH;
+      const int row = idx / PER, c = (idx - row * PER) * VEC;
+      if (idx < TOTAL) *reinterpret_cast<uint4*>(s + row * ls + c) = r[j];
+    }
+  }
+  // transposed store: s[c * ls + row] = tile[row][c]
+  __device__ __forceinline__ void store_T(T* s, int ls, int tid) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = tid + j * NTH;
+      const int row = idx / PER, c = (idx - row * PER) * VEC;
+      if (idx < TOTAL) {
+        union {
+          uint4 u;
+          T e[VEC];
+        } v;
+        v.u = r[j];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[(c + e) * ls + row] = v.e[e];
+      }
+    }
+  }
+};
 
 // beta may be stored as bf16 or fp32 independently of the feature dtype.
 __device__ __forceinline__ float ld_beta(const void* p, int is_f32, int64_t idx) {

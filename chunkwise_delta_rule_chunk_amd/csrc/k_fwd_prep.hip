@@ -113,19 +113,39 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Args a) {
   for (int idx = tid; idx < CH * PA; idx += NTH) sCq[idx] = fromf<T>(0.f);
   load_gate_cumsum<K>(sG, PG, a, t0, h, n, K, 0, tid, NTH);
 
-  // ---- 2. sub-chunk statistics; Qg, F and G2_last outputs ------------------
+  // ---- 2. sub-chunk statistics; element-wise outputs ----------------------
   subchunk_stats<K>(sG, PG, n, nullptr, sGl, sMid, sFlag, tid, NTH);
+  const int mode = a.prep_mode;
+  const int64_t cbase = (int64_t)c * H + h;  // chunk-tile index
   {
-    T* Qgo = reinterpret_cast<T*>(a.Qg) + (t0 * H + h) * K;
-    T* Fo = reinterpret_cast<T*>(a.F) + (t0 * H + h) * K;
     const float* Gn = sG + (n - 1) * PG;
-    for (int idx = tid; idx < n * K; idx += NTH) {
-      const int i = idx / K, kk = idx - i * K;
-      const float G = sG[i * PG + kk];
-      Qgo[i * gsK + kk] = fromf<T>(a.scale * tof(sQ[i * PK + kk]) * exp2f(G));
-      Fo[i * gsK + kk] = fromf<T>(tof(sK[i * PK + kk]) * exp2f(Gn[kk] - G));
+    if (mode & (PREP_FWD_OUT | PREP_BWD_SCAN)) {
+      T* Qgo = reinterpret_cast<T*>(a.Qg) + (t0 * H + h) * K;
+      T* Fo = reinterpret_cast<T*>(a.F) + (t0 * H + h) * K;
+      for (int idx = tid; idx < n * K; idx += NTH) {
+        const int i = idx / K, kk = idx - i * K;
+        const float G = sG[i * PG + kk];
+        if (mode & PREP_FWD_OUT) Qgo[i * gsK + kk] = fromf<T>(a.scale * tof(sQ[i * PK + kk]) * exp2f(G));
+        if (mode & PREP_BWD_SCAN) Fo[i * gsK + kk] = fromf<T>(tof(sK[i * PK + kk]) * exp2f(Gn[kk] - G));
+      }
     }
-    for (int kk = tid; kk < K; kk += NTH) a.glast[((int64_t)c * H + h) * K + kk] = Gn[kk];
+    if (mode & (PREP_FWD_SCAN | PREP_BWD_SCAN))
+      for (int kk = tid; kk < K; kk += NTH) a.glast[cbase * K + kk] = Gn[kk];
+    // token-contiguous tiles [K][64] (zeros past the chunk end: sK, sQ rows are zero there)
+    if (mode & PREP_FWD_SCAN) {
+      T* Fto = reinterpret_cast<T*>(a.Ft) + cbase * K * CH;
+      for (int idx = tid; idx < K * CH; idx += NTH) {
+        const int kk = idx / CH, i = idx - kk * CH;
+        Fto[idx] = fromf<T>(tof(sK[i * PK + kk]) * exp2f(Gn[kk] - sG[i * PG + kk]));
+      }
+    }
+    if (mode & PREP_BWD_SCAN) {
+      T* Qgto = reinterpret_cast<T*>(a.Qgt) + cbase * K * CH;
+      for (int idx = tid; idx < K * CH; idx += NTH) {
+        const int kk = idx / CH, i = idx - kk * CH;
+        Qgto[idx] = fromf<T>(a.scale * tof(sQ[i * PK + kk]) * exp2f(sG[i * PG + kk]));
+      }
+    }
   }
   __syncthreads();
 
@@ -133,8 +153,15 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Args a) {
   score_tiles<T, K, true>(sG, PG, sK, sQ, PK, sBeta, sMid, sGl, sFlag, n, a.scale, sL, PL, sCq,
                           PA);
   __syncthreads();
-  s2g<T, CH>(reinterpret_cast<T*>(a.Cq) + ((int64_t)c * H + h) * CH * CH, CH, sCq, PA, CH, tid,
-             NTH);
+  if (mode & PREP_FWD_OUT)
+    s2g<T, CH>(reinterpret_cast<T*>(a.Cq) + cbase * CH * CH, CH, sCq, PA, CH, tid, NTH);
+  if (mode & PREP_BWD_SCAN) {
+    T* Cqto = reinterpret_cast<T*>(a.Cqt) + cbase * CH * CH;
+    for (int idx = tid; idx < CH * CH; idx += NTH) {
+      const int i = idx / CH, j = idx - i * CH;
+      Cqto[idx] = sCq[j * PA + i];
+    }
+  }
   __syncthreads();  // sCq becomes solve scratch
 
   // ---- 4. A = (I + L)^-1 in fp32 --------------------------------------------
@@ -155,57 +182,71 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Args a) {
   const int w = wave_id();
   T* Wo = reinterpret_cast<T*>(a.W) + (t0 * H + h) * K;
   T* Uo = reinterpret_cast<T*>(a.U) + (t0 * H + h) * V;
+  T* Wto = reinterpret_cast<T*>(a.Wt) + cbase * K * CH;
+  const bool wantW = mode & PREP_FWD_SCAN, wantWt = mode & PREP_BWD_SCAN, wantU = wantW;
+  // W^T needs every row block (rows past the chunk end are exact zeros)
+  const int nblk = wantWt ? NSUB : (n + SUB - 1) / SUB;
+  auto put_w = [&](const f32x4& acc, int I, int col) {
+    if (wantW) st_tile<T>(acc, Wo + (I * SUB) * gsK + col, (int)gsK, 1, n - I * SUB);
+    if (wantWt) st_tile_T<T>(acc, Wto + (int64_t)col * CH + I * SUB, CH);
+  };
   if constexpr (BF) {
     constexpr int VEC = 8, PER = V / VEC;
-    for (int idx = tid; idx < CH * PER; idx += NTH) {
-      const int r = idx / PER, c0 = (idx - r * PER) * VEC;
-      union {
-        uint4 u;
-        T e[VEC];
-      } val;
-      val.u = uint4{0u, 0u, 0u, 0u};
-      if (r < n) val.u = *reinterpret_cast<const uint4*>(vg + (int64_t)r * gsV + c0);
-      const float b = sBeta[r];
+    if (wantU) {
+      for (int idx = tid; idx < CH * PER; idx += NTH) {
+        const int r = idx / PER, c0 = (idx - r * PER) * VEC;
+        union {
+          uint4 u;
+          T e[VEC];
+        } val;
+        val.u = uint4{0u, 0u, 0u, 0u};
+        if (r < n) val.u = *reinterpret_cast<const uint4*>(vg + (int64_t)r * gsV + c0);
+        const float b = sBeta[r];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) sZt[(c0 + e) * PA + r] = fromf<T>(b * tof(val.e[e]));
+        for (int e = 0; e < VEC; ++e) sZt[(c0 + e) * PA + r] = fromf<T>(b * tof(val.e[e]));
+      }
     }
     __syncthreads();
     // ---- 6. W = A E, U = A Z ------------------------------------------------
-    constexpr int NCB = (K + V) / SUB;
+    const int NCB = (K + (wantU ? V : 0)) / SUB;
     for (int cb = w; cb < NCB; cb += 4) {
       const bool isW = cb < K / SUB;
+      if (isW && !wantW && !wantWt) continue;
       const int col = isW ? cb * SUB : (cb - K / SUB) * SUB;
       const T* Bop = (isW ? sEt : sZt) + col * PA;
-      for (int I = 0; I < NSUB && I * SUB < n; ++I) {
+      for (int I = 0; I < (isW ? nblk : (n + SUB - 1) / SUB); ++I) {
         f32x4 acc = zero4();
         const int kd = ((SUB * (I + 1) + 31) / 32) * 32;
         mma_tile<T, true, true>(acc, sAb + (I * SUB) * PA, PA, 1, Bop, PA, 1, kd);
-        if (isW) st_tile<T>(acc, Wo + (I * SUB) * gsK + col, (int)gsK, 1, n - I * SUB);
+        if (isW) put_w(acc, I, col);
         else st_tile<T>(acc, Uo + (I * SUB) * gsV + col, (int)gsV, 1, n - I * SUB);
       }
     }
   } else {
     __syncthreads();
-    for (int cb = w; cb < K / SUB; cb += 4)
-      for (int I = 0; I < NSUB && I * SUB < n; ++I) {
-        f32x4 acc = zero4();
-        mma_tile<float, false, false>(acc, sA + (I * SUB) * PL, PL, 1, sEt + cb * SUB * PA, PA,
-                                      1, SUB * (I + 1));
-        st_tile<T>(acc, Wo + (I * SUB) * gsK + cb * SUB, (int)gsK, 1, n - I * SUB);
-      }
+    if (wantW || wantWt)
+      for (int cb = w; cb < K / SUB; cb += 4)
+        for (int I = 0; I < nblk; ++I) {
+          f32x4 acc = zero4();
+          mma_tile<float, false, false>(acc, sA + (I * SUB) * PL, PL, 1, sEt + cb * SUB * PA, PA,
+                                        1, SUB * (I + 1));
+          put_w(acc, I, cb * SUB);
+        }
     __syncthreads();
-    for (int idx = tid; idx < V * CH; idx += NTH) {
-      const int vv = idx / CH, j = idx - vv * CH;
-      sZt[vv * PA + j] = fromf<T>(j < n ? sBeta[j] * tof(vg[(int64_t)j * gsV + vv]) : 0.f);
+    if (wantU) {
+      for (int idx = tid; idx < V * CH; idx += NTH) {
+        const int vv = idx / CH, j = idx - vv * CH;
+        sZt[vv * PA + j] = fromf<T>(j < n ? sBeta[j] * tof(vg[(int64_t)j * gsV + vv]) : 0.f);
+      }
+      __syncthreads();
+      for (int cb = w; cb < V / SUB; cb += 4)
+        for (int I = 0; I < NSUB && I * SUB < n; ++I) {
+          f32x4 acc = zero4();
+          mma_tile<float, false, false>(acc, sA + (I * SUB) * PL, PL, 1, sZt + cb * SUB * PA, PA,
+                                        1, SUB * (I + 1));
+          st_tile<T>(acc, Uo + (I * SUB) * gsV + cb * SUB, (int)gsV, 1, n - I * SUB);
+        }
     }
-    __syncthreads();
-    for (int cb = w; cb < V / SUB; cb += 4)
-      for (int I = 0; I < NSUB && I * SUB < n; ++I) {
-        f32x4 acc = zero4();
-        mma_tile<float, false, false>(acc, sA + (I * SUB) * PL, PL, 1, sZt + cb * SUB * PA, PA,
-                                      1, SUB * (I + 1));
-        st_tile<T>(acc, Uo + (I * SUB) * gsV + cb * SUB, (int)gsV, 1, n - I * SUB);
-      }
   }
 }
 

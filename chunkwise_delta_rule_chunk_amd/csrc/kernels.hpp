@@ -39,13 +39,22 @@ struct Args {
   float* dg;
   void* dbeta;
   float* dh0;
-  // forward intermediates (token-major [BT,H,*] or chunk-major [nc_max,H,*,*])
-  void* W;       // A E              [BT,H,K]   dtype
-  void* U;       // A Z              [BT,H,V]   dtype
-  void* F;       // K exp2(Gn - G)   [BT,H,K]   dtype
-  void* Qg;      // s Q exp2(G)      [BT,H,K]   dtype
-  void* Cq;      // tril_incl(Qg Y^T) [nc,H,64,64] dtype
-  float* glast;  // G2 at the last row [nc,H,K] fp32
+  // Forward intermediates.  Token-major tensors are [BT,H,*]; chunk tiles are
+  // [nc_max,H,rows,64] with all 64 token columns written (zeros past the
+  // chunk's end).  Each product reads its operands with the contraction index
+  // contiguous, so tiles that are contracted over tokens are stored with the
+  // token index last (the "t" tiles).
+  int prep_mode;  // PREP_* bits: which of the sets below k_fwd_prep writes
+  void* W;       // A E                 [BT,H,K]     forward scan (R = U - W S)
+  void* Ft;      // F^T, F = K exp2(Gn - G)  [nc,H,K,64]  forward scan (S += F^T R)
+  void* U;       // A Z                 [BT,H,V]     forward scan
+  float* glast;  // G2 at the last row  [nc,H,K]     both scans
+  void* Qg;      // s Q exp2(G)         [BT,H,K]     output
+  void* Cq;      // tril_incl(Qg Y^T)   [nc,H,64,64] output
+  void* F;       // F                   [BT,H,K]     reverse scan (Rbar = F dS+)
+  void* Wt;      // W^T                 [nc,H,K,64]  reverse scan (dS -= W^T Rbar)
+  void* Qgt;     // Qg^T                [nc,H,K,64]  reverse scan (dS += Qg^T dO)
+  void* Cqt;     // Cq^T                [nc,H,64,64] reverse scan (Rbar += Cq^T dO)
   void* hbuf;    // state entering each chunk [nc,H,K,V] dtype
   void* R;       // corrections U - W S [BT,H,V] dtype
   // backward intermediates
@@ -57,13 +66,16 @@ struct Args {
   float* dbw;    // write part of dbeta, <V_i, P_i>  [BT,H] fp32
 };
 
-// Scan tile width over the value axis (one workgroup per sequence, head and
-// value tile).
-constexpr int SCAN_BV = 32;
+constexpr int PREP_FWD_SCAN = 1;  // W, Ft, U, glast
+constexpr int PREP_FWD_OUT = 2;   // Qg, Cq
+constexpr int PREP_BWD_SCAN = 4;  // F, Wt, Qgt, Cqt, glast
 
 // Launchers: enqueue on `stream`; return the hipError_t of the launch.
 hipError_t launch_chunk_table(const Args& a, hipStream_t s);
 hipError_t launch_fwd_prep(const Args& a, int dtype_f32, hipStream_t s);
+// Value-tile width of the scans: 16 or 32 columns per workgroup, chosen so
+// that the number of workgroups covers the chip.
+int scan_bv(const Args& a, int dtype_f32);
 hipError_t launch_fwd_scan(const Args& a, int dtype_f32, hipStream_t s);
 hipError_t launch_fwd_out(const Args& a, int dtype_f32, hipStream_t s);
 hipError_t launch_bwd_scan(const Args& a, int dtype_f32, hipStream_t s);

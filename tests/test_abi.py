@@ -79,18 +79,22 @@ def test_workspace_sizes_follow_the_layout(lib):
     nc = 4  # 256 tokens / 64
     e, H, K, V, BT = 2, 2, 128, 128, 256
     up = lambda x: (x + 255) // 256 * 256
-    head = up(nc * 16) + up(2 * 4) + up(BT * H * V * e)
-    fwd_set = 3 * up(BT * H * K * e) + up(nc * H * 64 * 64 * e) + up(nc * H * K * 4) + \
-        up(nc * H * K * V * e) + up(BT * H * V * e)
-    bwd_set = up(BT * H * V * e) * 2 + up(nc * H * K * V * e) + 2 * up(nc * H * 64 * 64 * e) + \
-        up(BT * H * 4)
-    assert B.rewy_workspace_bytes(d, 0) == head + fwd_set
-    assert B.rewy_workspace_bytes(d, 1) == head + fwd_set + bwd_set
+    tokK, tokV = up(BT * H * K * e), up(BT * H * V * e)
+    tileK, tile64 = up(nc * H * K * 64 * e), up(nc * H * 64 * 64 * e)
+    head = up(nc * 16) + up(2 * 4)
+    shared = up(nc * H * K * 4) + up(nc * H * K * V * e) + tokV        # glast, hbuf, R
+    scan = tokK + tileK + tokV                                          # W, Ft, U
+    out = tokK + tile64                                                 # Qg, Cq
+    rscan = tokK + 2 * tileK + tile64                                   # F, Wt, Qgt, Cqt
+    bwd = 2 * tokV + up(nc * H * K * V * e) + 2 * tile64 + up(BT * H * 4)
+    assert B.rewy_workspace_bytes(d, 0) == head + shared + scan + out
+    # the reverse-scan set of the backward reuses the output operands' space
+    assert B.rewy_workspace_bytes(d, 1) == head + shared + scan + rscan + bwd
     assert B.rewy_saved_bytes(d) == 0
     ds = _desc(policy=B.REWY_SAVE)
-    assert B.rewy_saved_bytes(ds) == fwd_set
-    assert B.rewy_workspace_bytes(ds, 0) == head
-    assert B.rewy_workspace_bytes(ds, 1) == head + bwd_set
+    assert B.rewy_saved_bytes(ds) == shared + rscan
+    assert B.rewy_workspace_bytes(ds, 0) == head + scan + out
+    assert B.rewy_workspace_bytes(ds, 1) == head + bwd
 
 
 def test_calls_reject_bad_pointers_without_launching(lib):
