@@ -8,6 +8,8 @@
 //   L  = tril_strict(E Y^T),  Cq = tril_incl(Qg Y^T),  A = (I + L)^-1
 // with E = beta exp2(G2) K, Y = K exp2(-G2), Qg = s Q exp2(G2).
 #pragma once
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace rewy {
@@ -198,6 +200,21 @@ __device__ __forceinline__ void solve_unit_lower(const float* sL, float* sA, int
 }
 
 constexpr int cmax(int x, int y) { return x > y ? x : y; }
+
+// Workgroups of a persistent chunk kernel: one per compute unit of the
+// current device (queried once per device).
+inline int persistent_grid() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+      cu = 256;
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
 
 // Launch helper: the (T, K, V) instantiations this build provides.  fp32 keeps
 // K, V <= 64 so that every kernel's LDS stays within one CU's 160 KB.

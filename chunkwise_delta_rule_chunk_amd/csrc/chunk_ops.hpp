@@ -1,0 +1,245 @@
+// Register-resident gate prefix sums and centred chunk operands shared by the
+// chunk-parallel kernels.
+//
+// Gate prefix (KDA blog 6.6; base 2 as in the pages' pipeline): thread t of an
+// NTH-thread workgroup owns feature column c = t % KC of a [64 x KC] gate tile
+// and the rows [seg*RS, seg*RS + RS), seg = t / KC.  The in-chunk inclusive sum
+// G2 = log2(e) * cumsum(g) is formed in registers; one LDS exchange of segment
+// totals joins the segments.
+//
+// Centring (ReWY paper section 3.3, "Centered factors", and Appendix 8): every
+// sub-chunk J of 16 rows gets, per feature, a receiving reference rA_J and a
+// sending reference rB_J: both its gate midpoint (max + min) / 2, or, when the
+// sub-chunk's gate range exceeds CENTRE_MAX_RANGE, its first row (rA) and its
+// last valid row (rB).  Operands are stored pre-scaled,
+//   Ka[i] = beta_i k_i exp2(G_i - rA),  Qa[i] = s q_i exp2(G_i - rA),
+//   Kc[j] = k_j exp2(rB - G_j),
+// and a pair of sub-chunks I > J contributes through the per-feature factor
+//   f_IJ = exp2(rA_I - rB_J) <= 1   (rA_I <= G at the first row of I <= G at the
+//                                    last row of J <= rB_J for a decaying gate),
+// so exp2(G_i - G_j) = exp2(G_i - rA_I) f_IJ exp2(rB_J - G_j) is never formed as
+// a product of unbounded factors.  Midpoint-centred factors are bounded by
+// 2^(range/2) <= 2^64.  A diagonal pair of a wide sub-chunk is summed pairwise.
+#pragma once
+#include "chunk_common.hpp"
+
+namespace rewy {
+
+// Thread t < 4*KC owns feature column c = t % KC and sub-chunk seg = t / KC,
+// i.e. the 16 rows [16 seg, 16 seg + 16); threads t >= 4*KC take no part.
+template <int KC>
+struct GateCols {
+  static constexpr int NG = NSUB * KC;  // participating threads
+  static constexpr int RS = SUB;        // rows per thread
+  float G[RS];
+  int c, seg;
+  bool on;
+
+  __device__ __forceinline__ void init(int tid) {
+    on = tid < NG;
+    c = tid % KC;
+    seg = (tid / KC) % NSUB;
+  }
+  // raw natural-log gates of rows < n (zero beyond); features [k0, k0 + KC)
+  __device__ __forceinline__ void load(const Args& a, int64_t t0, int h, int n, int K, int k0) {
+    const int H = a.H;
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const int row = seg * RS + r;
+      float x = 0.f;
+      if (on && row < n) {
+        if (a.gate == 2) x = a.g[((t0 + row) * H + h) * K + k0 + c];
+        else if (a.gate == 1) x = a.g[(t0 + row) * H + h];
+      }
+      G[r] = x;
+    }
+  }
+  // G2 = log2(e) * inclusive prefix over the chunk's rows, in two halves around
+  // a barrier the caller places: prefix_local() publishes the segment totals in
+  // sTot [NSUB][KC], prefix_finish() adds the totals of earlier segments.
+  __device__ __forceinline__ void prefix_local(float* sTot) {
+#pragma unroll
+    for (int r = 1; r < RS; ++r) G[r] += G[r - 1];
+    if (on) sTot[seg * KC + c] = G[RS - 1];
+  }
+  __device__ __forceinline__ void prefix_finish(const float* sTot) {
+    float off = 0.f;
+    if (on)
+      for (int s = 0; s < seg; ++s) off += sTot[s * KC + c];
+#pragma unroll
+    for (int r = 0; r < RS; ++r) G[r] = (G[r] + off) * LOG2E;
+  }
+};
+
+// Sub-chunk statistics from the register-resident prefix sums: midpoint, first
+// row and last valid row per (J, feature) into sMid/sGf/sGl [NSUB][KC], G2 at
+// the chunk's last valid row into sGn [KC], and sFlag[J] set when a feature's
+// range exceeds CENTRE_MAX_RANGE (sFlag zero on entry).  No barrier inside.
+template <int KC>
+__device__ __forceinline__ void subchunk_stats_regs(const GateCols<KC>& gc, int n, float* sMid,
+                                                    float* sGf, float* sGl, float* sGn,
+                                                    int* sFlag) {
+  if (!gc.on) return;
+  const int J = gc.seg, r0 = J * SUB;
+  if (r0 >= n) return;
+  const int last = min(r0 + SUB, n) - 1;
+  float mx = -INFINITY, mn = INFINITY, gl = 0.f;
+#pragma unroll
+  for (int r = 0; r < SUB; ++r) {
+    const int row = r0 + r;
+    const float x = gc.G[r];
+    if (row < n) {
+      mx = fmaxf(mx, x);
+      mn = fminf(mn, x);
+    }
+    if (row == last) gl = x;
+  }
+  const int idx = J * KC + gc.c;
+  sMid[idx] = 0.5f * (mx + mn);
+  sGf[idx] = gc.G[0];
+  sGl[idx] = gl;
+  if (last == n - 1) sGn[gc.c] = gl;
+  if (mx - mn > CENTRE_MAX_RANGE) sFlag[J] = 1;  // benign race: same value
+}
+
+// References of sub-chunk J for feature k (after the statistics are visible).
+__device__ __forceinline__ float ref_recv(const float* sMid, const float* sGf, const int* sFlag,
+                                          int J, int KC, int k) {
+  return sFlag[J] ? sGf[J * KC + k] : sMid[J * KC + k];
+}
+__device__ __forceinline__ float ref_send(const float* sMid, const float* sGl, const int* sFlag,
+                                          int J, int KC, int k) {
+  return sFlag[J] ? sGl[J * KC + k] : sMid[J * KC + k];
+}
+
+// Pair factors fac[p][KC] = exp2(rA_I - rB_J) for the 10 pairs I >= J (pair_ij
+// order); 1 on a centred diagonal, and unused on a wide diagonal.
+template <int KC>
+__device__ __forceinline__ void pair_factors(const float* sMid, const float* sGf,
+                                             const float* sGl, const int* sFlag, float* fac,
+                                             int n, int tid, int nthr) {
+  for (int idx = tid; idx < 10 * KC; idx += nthr) {
+    const int p = idx / KC, k = idx - p * KC;
+    int I, J;
+    pair_ij(p, I, J);
+    float f = 0.f;
+    if (I * SUB < n)
+      f = (I == J) ? 1.f
+                   : exp2f(ref_recv(sMid, sGf, sFlag, I, KC, k) -
+                           ref_send(sMid, sGl, sFlag, J, KC, k));
+    fac[idx] = f;
+  }
+}
+
+// Score tiles from pre-scaled operands (natural [token][feature] layout, pitch
+// PK, bf16 or fp32): L_IJ = (Ka_I * f_IJ) Kc_J^T (strict), and with WITH_CQ
+// Cq_IJ = (Qa_I * f_IJ) Kc_J^T (inclusive), for the pairs I >= J with rows < n.
+// Flagged diagonal pairs are skipped here (see pairwise_diag).  The callback
+// st(I, J, accL, accC) receives each finished tile.  Called by all NW waves.
+template <typename T, int K, bool WITH_CQ, int NW, typename Store>
+__device__ __forceinline__ void score_tiles_pre(const T* sKa, const T* sQa, const T* sKc, int PK,
+                                                const float* fac, const int* sFlag, int n,
+                                                Store&& st) {
+  constexpr bool BF = std::is_same_v<T, bf16>;
+  const int w = wave_id(), l = lane_id();
+  for (int p = w; p < 10; p += NW) {
+    int I, J;
+    pair_ij(p, I, J);
+    if (I * SUB >= n || (I == J && sFlag[J])) continue;
+    const int ri = I * SUB + (l & 15), rj = J * SUB + (l & 15);
+    const float* f = fac + p * K;
+    f32x4 accL = zero4(), accC = zero4();
+    for (int k0 = 0; k0 < K; k0 += MM<T>::KS) {
+      typename MM<T>::frag ak, aq, bk;
+      if constexpr (BF) {
+        const int kb = k0 + (l >> 4) * 8;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sKa + ri * PK + kb);
+        bk = *reinterpret_cast<const bf16x8*>(sKc + rj * PK + kb);
+        bf16x8 qa;
+        if constexpr (WITH_CQ) qa = *reinterpret_cast<const bf16x8*>(sQa + ri * PK + kb);
+        if (I == J) {
+          ak = ka;
+          if constexpr (WITH_CQ) aq = qa;
+        } else {
+          const f32x4 f0 = *reinterpret_cast<const f32x4*>(f + kb);
+          const f32x4 f1 = *reinterpret_cast<const f32x4*>(f + kb + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float fe = e < 4 ? f0[e] : f1[e - 4];
+            ak[e] = (bf16)((float)ka[e] * fe);
+            if constexpr (WITH_CQ) aq[e] = (bf16)((float)qa[e] * fe);
+          }
+        }
+      } else {
+        const int kk = k0 + (l >> 4);
+        const float fe = (I == J) ? 1.f : f[kk];
+        ak = tof(sKa[ri * PK + kk]) * fe;
+        if constexpr (WITH_CQ) aq = tof(sQa[ri * PK + kk]) * fe;
+        bk = sKc[rj * PK + kk];
+      }
+      accL = mma(ak, bk, accL);
+      if constexpr (WITH_CQ) accC = mma(aq, bk, accC);
+    }
+    st(I, J, accL, accC);
+  }
+}
+
+// Pairwise diagonal tile of a wide sub-chunk I (one wave): entries
+//   L[i][j]  = beta_i sum_k k_ik k_jk exp2(G_ik - G_jk)      (j < i)
+//   Cq[i][j] = s sum_k q_ik k_jk exp2(G_ik - G_jk)            (j <= i)
+// with G_i - G_j summed from the raw gates between the two rows, so no factor
+// exceeds 1.  Reads q, k, g from global.  Lane l takes column j = l & 15 and
+// the feature quarter l >> 4; results come back in the C-fragment layout.
+template <typename T, int K, bool WITH_CQ>
+__device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, int n, int I,
+                                              const float* sBeta, f32x4& accL, f32x4& accC) {
+  const int l = lane_id(), j = l & 15, qk = l >> 4, H = a.H;
+  const T* kg = reinterpret_cast<const T*>(a.k);
+  const T* qg = reinterpret_cast<const T*>(a.q);
+  float pL[SUB], pC[SUB];
+#pragma unroll
+  for (int i = 0; i < SUB; ++i) pL[i] = pC[i] = 0.f;
+  const int rj = I * SUB + j;
+  if (rj < n) {
+    for (int k = qk * (K / 4); k < (qk + 1) * (K / 4); ++k) {
+      const float kj = tof(kg[((t0 + rj) * H + h) * K + k]);
+      float run = 0.f;
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) {
+        const int ri = I * SUB + i;
+        if (i >= j && ri < n) {
+          if (i > j) {
+            float gi = 0.f;
+            if (a.gate == 2) gi = a.g[((t0 + ri) * H + h) * K + k];
+            else if (a.gate == 1) gi = a.g[(t0 + ri) * H + h];
+            run += gi * LOG2E;
+          }
+          const float f = exp2f(run) * kj;
+          pL[i] += tof(kg[((t0 + ri) * H + h) * K + k]) * f;
+          if constexpr (WITH_CQ) pC[i] += tof(qg[((t0 + ri) * H + h) * K + k]) * f;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SUB; ++i) {
+    pL[i] += __shfl_xor(pL[i], 16);
+    pL[i] += __shfl_xor(pL[i], 32);
+    if constexpr (WITH_CQ) {
+      pC[i] += __shfl_xor(pC[i], 16);
+      pC[i] += __shfl_xor(pC[i], 32);
+    }
+  }
+  accL = zero4();
+  accC = zero4();
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4)
+    if (qk == g4)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        accL[r] = sBeta[I * SUB + 4 * g4 + r] * pL[4 * g4 + r];
+        accC[r] = a.scale * pC[4 * g4 + r];
+      }
+}
+
+}  // namespace rewy

@@ -39,8 +39,35 @@ struct ChunkInfo {
   int pos;  // chunk index within its sequence
 };
 
+// Lane and wave index.  A translation unit whose kernels loop over many work
+// items in one workgroup defines REWY_OPAQUE_IDS before its first include: the
+// indices are then opaque at every use, so the compiler cannot hoist address
+// arithmetic derived from them out of the item loop (hoisted values stay live
+// across items and spill).  Elsewhere they are plain, so the usual common
+// subexpressions are shared.
+#ifdef REWY_OPAQUE_IDS
+__device__ __forceinline__ int lane_id() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
+__device__ __forceinline__ int wave_id() {
+  int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  asm volatile("" : "+s"(w));
+  return w;
+}
+#else
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+#endif
+// Thread index made opaque to the optimiser.  Persistent item loops take it
+// once per item: otherwise the compiler hoists address arithmetic derived from
+// it out of the loop, and the hoisted values stay live (and spill) across items.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 template <typename T>
 __device__ __forceinline__ float tof(T x) { return (float)x; }

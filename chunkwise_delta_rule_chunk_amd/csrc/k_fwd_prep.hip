@@ -10,7 +10,8 @@
 //   Cq = tril_incl(Qg Y^T), A = (I + L)^-1 (fp32), W = A E, U = A Z (Z = beta V),
 //   F = K exp2(G2_last - G2) (keys decayed to the chunk end), Qg = s Q exp2(G2),
 //   and G2_last.  Score tiles are centred (see chunk_common.hpp).
-#include "chunk_common.hpp"
+#define REWY_OPAQUE_IDS
+#include "chunk_ops.hpp"
 
 namespace rewy {
 
@@ -56,203 +57,276 @@ hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// One persistent workgroup processes chunk-heads item = blockIdx.x + i*gridDim.x
+// (item = chunk * H + head).  The next item's k, q, v, g and beta are read into
+// registers while the current item computes, so HBM latency overlaps compute.
 template <typename T, int K, int V>
-__global__ __launch_bounds__(256) void k_fwd_prep(Args a) {
-  constexpr int NTH = 256;
+__global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
+  constexpr int NTH = 512, NW = NTH / 64;
   constexpr bool BF = std::is_same_v<T, bf16>;
   constexpr int PK = pitch<T>(K);   // T rows of K
-  constexpr int PG = K + 4;         // fp32 rows of K
   constexpr int PL = CH + 4;        // fp32 rows of 64
   constexpr int PA = pitch<T>(CH);  // T rows of 64
-  constexpr int SZ_Q = CH * PK * (int)sizeof(T);
-  constexpr int SZ_L = CH * PL * 4;
-  constexpr int SZ_ET = K * PA * (int)sizeof(T);
-  constexpr int SZ_ZT = V * PA * (int)sizeof(T);
-  // phase 1: [sQ | sL | sA]; phase 2 (bf16): [E^T | Z^T] over the same bytes.
-  // fp32 keeps sA alive during the WY products, so E^T / Z^T stay below sL.
-  constexpr int OFF_L = BF ? SZ_Q : cmax(SZ_Q, cmax(SZ_ET, SZ_ZT));
-  constexpr int REG = BF ? cmax(SZ_Q + 2 * SZ_L, SZ_ET + SZ_ZT) : OFF_L + 2 * SZ_L;
+  using GC = GateCols<K>;
+  constexpr int RS = GC::RS;
 
-  __shared__ __align__(16) float sG[CH * PG];
-  __shared__ __align__(16) T sK[CH * PK];
-  __shared__ __align__(16) char sReg[REG];
-  __shared__ __align__(16) T sCq[CH * PA];  // later: solve scratch
+  __shared__ __align__(16) T sK[CH * PK];   // raw k, then Kc in place
+  __shared__ __align__(16) T sQ[CH * PK];   // raw q, then Qa in place
+  __shared__ __align__(16) T sKa[CH * PK];
+  __shared__ __align__(16) float sL[CH * PL];
+  __shared__ __align__(16) float sA[CH * PL];
   __shared__ __align__(16) T sAb[BF ? CH * PA : 8];
+  __shared__ __align__(16) T sEt[K * PA];   // E^T, [k][j]
+  __shared__ __align__(16) T sZt[V * PA];   // Z^T, [v][j]
+  __shared__ __align__(16) float sFac[10 * K];
+  __shared__ float sTot[NSUB * K];
+  __shared__ float sMid[NSUB * K], sGf[NSUB * K], sGl[NSUB * K], sGn[K];
   __shared__ float sBeta[CH];
-  __shared__ float sMid[NSUB * K], sGl[NSUB * K];
+  __shared__ float sT[4 * SUB * 20];
   __shared__ int sFlag[NSUB];
-  static_assert(CH * PA * sizeof(T) >= 4 * SUB * 20 * 4, "solve scratch");
 
-  T* sQ = reinterpret_cast<T*>(sReg);
-  float* sL = reinterpret_cast<float*>(sReg + OFF_L);
-  float* sA = reinterpret_cast<float*>(sReg + OFF_L + SZ_L);
-  T* sEt = reinterpret_cast<T*>(sReg);
-  T* sZt = reinterpret_cast<T*>(sReg + (BF ? SZ_ET : 0));
-  float* sT = reinterpret_cast<float*>(sCq);
-
-  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const ChunkInfo ci = a.chunks[c];
-  const int n = ci.len;
-  if (n == 0) return;
-  const int H = a.H;
-  const int64_t t0 = ci.bos;
+  const int H = a.H, mode = a.prep_mode;
+  const int total = a.nc_max * H;
   const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
-  const T* qg = reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K;
-  const T* kg = reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K;
-  const T* vg = reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V;
 
-  // ---- 1. keys, queries, beta; zeroed score buffers; gate prefix sum -------
-  g2s<T, K>(sK, PK, kg, gsK, n, CH, tid, NTH);
-  g2s<T, K>(sQ, PK, qg, gsK, n, CH, tid, NTH);
-  if (tid < CH) sBeta[tid] = tid < n ? ld_beta(a.beta, a.beta_f32, (t0 + tid) * H + h) : 0.f;
-  if (tid < NSUB) sFlag[tid] = 0;
-  for (int idx = tid; idx < CH * PL; idx += NTH) {
-    sL[idx] = 0.f;
-    sA[idx] = 0.f;
-  }
-  for (int idx = tid; idx < CH * PA; idx += NTH) sCq[idx] = fromf<T>(0.f);
-  load_gate_cumsum<K>(sG, PG, a, t0, h, n, K, 0, tid, NTH);
-
-  // ---- 2. sub-chunk statistics; element-wise outputs ----------------------
-  subchunk_stats<K>(sG, PG, n, nullptr, sGl, sMid, sFlag, tid, NTH);
-  const int mode = a.prep_mode;
-  const int64_t cbase = (int64_t)c * H + h;  // chunk-tile index
-  {
-    const float* Gn = sG + (n - 1) * PG;
-    if (mode & (PREP_FWD_OUT | PREP_BWD_SCAN)) {
-      T* Qgo = reinterpret_cast<T*>(a.Qg) + (t0 * H + h) * K;
-      T* Fo = reinterpret_cast<T*>(a.F) + (t0 * H + h) * K;
-      for (int idx = tid; idx < n * K; idx += NTH) {
-        const int i = idx / K, kk = idx - i * K;
-        const float G = sG[i * PG + kk];
-        if (mode & PREP_FWD_OUT) Qgo[i * gsK + kk] = fromf<T>(a.scale * tof(sQ[i * PK + kk]) * exp2f(G));
-        if (mode & PREP_BWD_SCAN) Fo[i * gsK + kk] = fromf<T>(tof(sK[i * PK + kk]) * exp2f(Gn[kk] - G));
-      }
-    }
-    if (mode & (PREP_FWD_SCAN | PREP_BWD_SCAN))
-      for (int kk = tid; kk < K; kk += NTH) a.glast[cbase * K + kk] = Gn[kk];
-    // token-contiguous tiles [K][64] (zeros past the chunk end: sK, sQ rows are zero there)
-    if (mode & PREP_FWD_SCAN) {
-      T* Fto = reinterpret_cast<T*>(a.Ft) + cbase * K * CH;
-      for (int idx = tid; idx < K * CH; idx += NTH) {
-        const int kk = idx / CH, i = idx - kk * CH;
-        Fto[idx] = fromf<T>(tof(sK[i * PK + kk]) * exp2f(Gn[kk] - sG[i * PG + kk]));
-      }
-    }
-    if (mode & PREP_BWD_SCAN) {
-      T* Qgto = reinterpret_cast<T*>(a.Qgt) + cbase * K * CH;
-      for (int idx = tid; idx < K * CH; idx += NTH) {
-        const int kk = idx / CH, i = idx - kk * CH;
-        Qgto[idx] = fromf<T>(a.scale * tof(sQ[i * PK + kk]) * exp2f(sG[i * PG + kk]));
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- 3. centred score tiles: L (strict) and Cq (inclusive) ---------------
-  score_tiles<T, K, true>(sG, PG, sK, sQ, PK, sBeta, sMid, sGl, sFlag, n, a.scale, sL, PL, sCq,
-                          PA);
-  __syncthreads();
-  if (mode & PREP_FWD_OUT)
-    s2g<T, CH>(reinterpret_cast<T*>(a.Cq) + cbase * CH * CH, CH, sCq, PA, CH, tid, NTH);
-  if (mode & PREP_BWD_SCAN) {
-    T* Cqto = reinterpret_cast<T*>(a.Cqt) + cbase * CH * CH;
-    for (int idx = tid; idx < CH * CH; idx += NTH) {
-      const int i = idx / CH, j = idx - i * CH;
-      Cqto[idx] = sCq[j * PA + i];
-    }
-  }
-  __syncthreads();  // sCq becomes solve scratch
-
-  // ---- 4. A = (I + L)^-1 in fp32 --------------------------------------------
-  solve_unit_lower(sL, sA, PL, sT, n);
-
-  // ---- 5. operands of the WY products --------------------------------------
-  if constexpr (BF) {
-    for (int idx = tid; idx < CH * CH; idx += NTH) {
-      const int i = idx / CH, j = idx - i * CH;
-      sAb[i * PA + j] = (bf16)sA[i * PL + j];
-    }
-    __syncthreads();  // sA is overwritten by E^T / Z^T below
-  }
-  for (int idx = tid; idx < K * CH; idx += NTH) {
-    const int kk = idx / CH, j = idx - kk * CH;
-    sEt[kk * PA + j] = fromf<T>(sBeta[j] * tof(sK[j * PK + kk]) * exp2f(sG[j * PG + kk]));
-  }
-  const int w = wave_id();
-  T* Wo = reinterpret_cast<T*>(a.W) + (t0 * H + h) * K;
-  T* Uo = reinterpret_cast<T*>(a.U) + (t0 * H + h) * V;
-  T* Wto = reinterpret_cast<T*>(a.Wt) + cbase * K * CH;
-  const bool wantW = mode & PREP_FWD_SCAN, wantWt = mode & PREP_BWD_SCAN, wantU = wantW;
-  // W^T needs every row block (rows past the chunk end are exact zeros)
-  const int nblk = wantWt ? NSUB : (n + SUB - 1) / SUB;
-  auto put_w = [&](const f32x4& acc, int I, int col) {
-    if (wantW) st_tile<T>(acc, Wo + (I * SUB) * gsK + col, (int)gsK, 1, n - I * SUB);
-    if (wantWt) st_tile_T<T>(acc, Wto + (int64_t)col * CH + I * SUB, CH);
+  GC gc, gnx;
+  gc.init(threadIdx.x);
+  gnx.init(threadIdx.x);
+  Staged<T, CH, K, NTH> pk, pq;
+  Staged<T, CH, V, NTH> pv;
+  float pbeta = 0.f;
+  // the next item's inputs: k, q, v and beta as soon as the current ones are in
+  // LDS, the gates once the current gates are consumed
+  auto fetch_kqv = [&](int item, int tid) {
+    const int c = item / H, h = item - c * H;
+    const ChunkInfo ci = a.chunks[c];
+    if (ci.len == 0) return;
+    const int64_t t0 = ci.bos;
+    pk.load(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, gsK, ci.len, tid);
+    pq.load(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, gsK, ci.len, tid);
+    pv.load(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, gsV, ci.len, tid);
+    pbeta = tid < ci.len ? ld_beta(a.beta, a.beta_f32, (t0 + tid) * H + h) : 0.f;
   };
-  if constexpr (BF) {
-    constexpr int VEC = 8, PER = V / VEC;
-    if (wantU) {
-      for (int idx = tid; idx < CH * PER; idx += NTH) {
+  auto fetch_g = [&](int item) {
+    const int c = item / H, h = item - c * H;
+    const ChunkInfo ci = a.chunks[c];
+    if (ci.len == 0) return;
+    gnx.load(a, (int64_t)ci.bos, h, ci.len, K, 0);
+  };
+
+  if (blockIdx.x < total) {
+    fetch_kqv(blockIdx.x, threadIdx.x);
+    fetch_g(blockIdx.x);
+  }
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int tid = opaque_tid(), w = wave_id();
+    const int c = item / H, h = item - c * H;
+    const ChunkInfo ci = a.chunks[c];
+    const int n = ci.len;
+    if (n == 0) {  // uniform: nothing was fetched for this slot
+      if (item + (int)gridDim.x < total) {
+        fetch_kqv(item + gridDim.x, tid);
+        fetch_g(item + gridDim.x);
+      }
+      continue;
+    }
+    const int64_t t0 = ci.bos, cb = (int64_t)c * H + h;
+
+    // ---- S0: staged inputs into LDS, local gate prefix ----------------------
+    pk.store(sK, PK, tid);
+    pq.store(sQ, PK, tid);
+    if (tid < CH) sBeta[tid] = pbeta;
+    if (tid < NSUB) sFlag[tid] = 0;
+    for (int idx = tid; idx < CH * PL / 4; idx += NTH) {
+      reinterpret_cast<f32x4*>(sL)[idx] = zero4();
+      reinterpret_cast<f32x4*>(sA)[idx] = zero4();
+    }
+#pragma unroll
+    for (int r = 0; r < RS; ++r) gc.G[r] = gnx.G[r];
+    gc.prefix_local(sTot);
+    __syncthreads();
+
+    // ---- S1: finish the prefix, Z^T from the staged v, statistics ------------
+    gc.prefix_finish(sTot);
+    if constexpr (BF) {
+      constexpr int VEC = 8, PER = V / VEC;
+#pragma unroll
+      for (int j = 0; j < decltype(pv)::N; ++j) {
+        const int idx = tid + j * NTH;
         const int r = idx / PER, c0 = (idx - r * PER) * VEC;
+        if (idx < CH * PER) {
+          union {
+            uint4 u;
+            T e[VEC];
+          } val;
+          val.u = pv.r[j];
+          const float b = sBeta[r];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) sZt[(c0 + e) * PA + r] = fromf<T>(b * tof(val.e[e]));
+        }
+      }
+    } else {
+      constexpr int VEC = 4, PER = V / VEC;
+#pragma unroll
+      for (int j = 0; j < decltype(pv)::N; ++j) {
+        const int idx = tid + j * NTH;
+        const int r = idx / PER, c0 = (idx - r * PER) * VEC;
+        if (idx < CH * PER) {
+          union {
+            uint4 u;
+            T e[VEC];
+          } val;
+          val.u = pv.r[j];
+          const float b = sBeta[r];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) sZt[(c0 + e) * PA + r] = fromf<T>(b * tof(val.e[e]));
+        }
+      }
+    }
+    // the staged registers are free: read the next item while this one computes
+    const bool more = item + (int)gridDim.x < total;
+    if (more) fetch_kqv(item + gridDim.x, tid);
+    subchunk_stats_regs(gc, n, sMid, sGf, sGl, sGn, sFlag);
+    __syncthreads();
+
+    // ---- S2: pair factors; element-wise outputs and centred operands --------
+    pair_factors<K>(sMid, sGf, sGl, sFlag, sFac, n, tid, NTH);
+    if (gc.on) {
+      // opaque per item: keeps the compiler from hoisting these addresses out of
+      // the item loop (they would have to stay live, and spill, across items)
+      int col = gc.c, r0 = gc.seg * RS;
+      asm volatile("" : "+v"(col), "+v"(r0));
+      const float gn = sGn[col];
+      constexpr int VE = 16 / (int)sizeof(T);
+      T* Ftd = reinterpret_cast<T*>(a.Ft) + (cb * K + col) * CH + r0;
+      T* Qgtd = reinterpret_cast<T*>(a.Qgt) + (cb * K + col) * CH + r0;
+#pragma unroll
+      for (int r8 = 0; r8 < RS; r8 += VE) {
         union {
           uint4 u;
-          T e[VEC];
-        } val;
-        val.u = uint4{0u, 0u, 0u, 0u};
-        if (r < n) val.u = *reinterpret_cast<const uint4*>(vg + (int64_t)r * gsV + c0);
-        const float b = sBeta[r];
+          T e[VE];
+        } ft, qt;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) sZt[(c0 + e) * PA + r] = fromf<T>(b * tof(val.e[e]));
-      }
-    }
-    __syncthreads();
-    // ---- 6. W = A E, U = A Z ------------------------------------------------
-    const int NCB = (K + (wantU ? V : 0)) / SUB;
-    for (int cb = w; cb < NCB; cb += 4) {
-      const bool isW = cb < K / SUB;
-      if (isW && !wantW && !wantWt) continue;
-      const int col = isW ? cb * SUB : (cb - K / SUB) * SUB;
-      const T* Bop = (isW ? sEt : sZt) + col * PA;
-      for (int I = 0; I < (isW ? nblk : (n + SUB - 1) / SUB); ++I) {
-        f32x4 acc = zero4();
-        const int kd = ((SUB * (I + 1) + 31) / 32) * 32;
-        mma_tile<T, true, true>(acc, sAb + (I * SUB) * PA, PA, 1, Bop, PA, 1, kd);
-        if (isW) put_w(acc, I, col);
-        else st_tile<T>(acc, Uo + (I * SUB) * gsV + col, (int)gsV, 1, n - I * SUB);
-      }
-    }
-  } else {
-    __syncthreads();
-    if (wantW || wantWt)
-      for (int cb = w; cb < K / SUB; cb += 4)
-        for (int I = 0; I < nblk; ++I) {
-          f32x4 acc = zero4();
-          mma_tile<float, false, false>(acc, sA + (I * SUB) * PL, PL, 1, sEt + cb * SUB * PA, PA,
-                                        1, SUB * (I + 1));
-          put_w(acc, I, cb * SUB);
+        for (int e = 0; e < VE; ++e) {
+          const int r = r8 + e, row = r0 + r;
+          float vKa = 0.f, vQa = 0.f, vKc = 0.f, vE = 0.f, vF = 0.f, vQg = 0.f;
+          if (row < n) {
+            const int J = row / SUB;
+            const float G = gc.G[r];
+            const float kr = tof(sK[row * PK + col]), qr = tof(sQ[row * PK + col]);
+            const float b = sBeta[row];
+            const float gam = exp2f(G);
+            const float ea = exp2f(G - ref_recv(sMid, sGf, sFlag, J, K, col));
+            vKa = b * kr * ea;
+            vQa = a.scale * qr * ea;
+            vKc = kr * exp2f(ref_send(sMid, sGl, sFlag, J, K, col) - G);
+            vE = b * kr * gam;
+            vF = kr * exp2f(gn - G);
+            vQg = a.scale * qr * gam;
+            if (mode & PREP_FWD_OUT)
+              reinterpret_cast<T*>(a.Qg)[(t0 + row) * gsK + h * K + col] = fromf<T>(vQg);
+            if (mode & PREP_BWD_SCAN)
+              reinterpret_cast<T*>(a.F)[(t0 + row) * gsK + h * K + col] = fromf<T>(vF);
+          }
+          sKa[row * PK + col] = fromf<T>(vKa);
+          sQ[row * PK + col] = fromf<T>(vQa);
+          sK[row * PK + col] = fromf<T>(vKc);
+          sEt[col * PA + row] = fromf<T>(vE);
+          ft.e[e] = fromf<T>(vF);
+          qt.e[e] = fromf<T>(vQg);
         }
+        // token-contiguous tiles: this thread holds consecutive tokens of column col
+        if (mode & PREP_FWD_SCAN) *reinterpret_cast<uint4*>(Ftd + r8) = ft.u;
+        if (mode & PREP_BWD_SCAN) *reinterpret_cast<uint4*>(Qgtd + r8) = qt.u;
+      }
+      if ((mode & (PREP_FWD_SCAN | PREP_BWD_SCAN)) && gc.seg == 0) a.glast[cb * K + col] = gn;
+    }
+    // the gate registers are free: read the next item's gates
+    if (more) fetch_g(item + gridDim.x);
     __syncthreads();
-    if (wantU) {
-      for (int idx = tid; idx < V * CH; idx += NTH) {
-        const int vv = idx / CH, j = idx - vv * CH;
-        sZt[vv * PA + j] = fromf<T>(j < n ? sBeta[j] * tof(vg[(int64_t)j * gsV + vv]) : 0.f);
+
+    // ---- S3: score tiles L (strict, fp32 in LDS) and Cq (inclusive, global) --
+    {
+      T* Cqo = reinterpret_cast<T*>(a.Cq) + cb * CH * CH;
+      T* Cqto = reinterpret_cast<T*>(a.Cqt) + cb * CH * CH;
+      auto store = [&](int I, int J, const f32x4& accL, const f32x4& accC) {
+        f32x4 cq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = I * SUB + crow(i), col = J * SUB + ccol();
+          if (row > col) sL[row * PL + col] = accL[i];
+          cq[i] = row >= col ? accC[i] : 0.f;
+        }
+        if (mode & PREP_FWD_OUT) st_tile<T>(cq, Cqo + (I * SUB) * CH + J * SUB, CH, 1);
+        if (mode & PREP_BWD_SCAN) st_tile_T<T>(cq, Cqto + (J * SUB) * CH + I * SUB, CH);
+      };
+      score_tiles_pre<T, K, true, NW>(sKa, sQ, sK, PK, sFac, sFlag, n, store);
+      // wide diagonal sub-chunks: pairwise, one wave each
+      for (int J = w; J < NSUB; J += NW)
+        if (J * SUB < n && sFlag[J]) {
+          f32x4 accL, accC;
+          pairwise_diag<T, K, true>(a, t0, h, n, J, sBeta, accL, accC);
+          store(J, J, accL, accC);
+        }
+      // tiles nobody computed: zeros (the upper triangle and rows past the end)
+      for (int t = w; t < NSUB * NSUB; t += NW) {
+        const int I = t / NSUB, J = t - I * NSUB;
+        if (J <= I && I * SUB < n) continue;
+        if (mode & PREP_FWD_OUT) st_tile<T>(zero4(), Cqo + (I * SUB) * CH + J * SUB, CH, 1);
+        if (mode & PREP_BWD_SCAN) st_tile_T<T>(zero4(), Cqto + (J * SUB) * CH + I * SUB, CH);
+      }
+    }
+    __syncthreads();
+
+    // ---- S4: A = (I + L)^-1 in fp32 ------------------------------------------
+    solve_unit_lower(sL, sA, PL, sT, n);
+
+    // ---- S5: W = A E, U = A Z --------------------------------------------------
+    T* Wo = reinterpret_cast<T*>(a.W) + (t0 * H + h) * K;
+    T* Uo = reinterpret_cast<T*>(a.U) + (t0 * H + h) * V;
+    T* Wto = reinterpret_cast<T*>(a.Wt) + cb * K * CH;
+    const bool wantW = mode & PREP_FWD_SCAN, wantWt = mode & PREP_BWD_SCAN, wantU = wantW;
+    const int nblk = (n + SUB - 1) / SUB;
+    const int nblkW = wantWt ? NSUB : nblk;  // W^T needs every row block (exact zeros past n)
+    if constexpr (BF) {
+      for (int idx = tid; idx < CH * CH / 4; idx += NTH) {
+        const int i = idx / (CH / 4), j = (idx - i * (CH / 4)) * 4;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sA + i * PL + j);
+        bf16x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (bf16)x[e];
+        *reinterpret_cast<bf16x4*>(sAb + i * PA + j) = y;
       }
       __syncthreads();
-      for (int cb = w; cb < V / SUB; cb += 4)
-        for (int I = 0; I < NSUB && I * SUB < n; ++I) {
-          f32x4 acc = zero4();
-          mma_tile<float, false, false>(acc, sA + (I * SUB) * PL, PL, 1, sZt + cb * SUB * PA, PA,
-                                        1, SUB * (I + 1));
-          st_tile<T>(acc, Uo + (I * SUB) * gsV + cb * SUB, (int)gsV, 1, n - I * SUB);
-        }
     }
+    const T* Aop = BF ? (const T*)sAb : (const T*)sA;
+    constexpr int PAo = BF ? PA : PL;
+    const int NCB = (K + (wantU ? V : 0)) / SUB;
+    for (int cbk = w; cbk < NCB; cbk += NW) {
+      const bool isW = cbk < K / SUB;
+      if (isW && !wantW && !wantWt) continue;
+      const int col = isW ? cbk * SUB : (cbk - K / SUB) * SUB;
+      const T* Bop = (isW ? sEt : sZt) + col * PA;
+      for (int I = 0; I < (isW ? nblkW : nblk); ++I) {
+        f32x4 acc = zero4();
+        const int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
+        mma_tile<T, true, true>(acc, Aop + (I * SUB) * PAo, PAo, 1, Bop, PA, 1, kd);
+        if (isW) {
+          if (wantW) st_tile<T>(acc, Wo + (I * SUB) * gsK + col, (int)gsK, 1, n - I * SUB);
+          if (wantWt) st_tile_T<T>(acc, Wto + (int64_t)col * CH + I * SUB, CH);
+        } else {
+          st_tile<T>(acc, Uo + (I * SUB) * gsV + col, (int)gsV, 1, n - I * SUB);
+        }
+      }
+    }
+    __syncthreads();  // LDS is rewritten by the next item
   }
 }
 
 template <typename T>
 static hipError_t prep_t(const Args& a, hipStream_t s) {
-  const dim3 grid(a.nc_max, a.H), block(256);
+  const int items = a.nc_max * a.H;
+  const dim3 grid(std::min(items, persistent_grid()), 1), block(512);
   REWY_KV_SWITCH(k_fwd_prep)
 }
 
