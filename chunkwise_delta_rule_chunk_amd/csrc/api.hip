@@ -89,17 +89,20 @@ int make_plan(const rewy_desc* d, Plan& p) {
 }
 
 // Buffer layout.  `saved` holds what the backward reads from the forward under
-// the save-all policy; everything else is scratch in the workspace.
-//   recompute: ws = [index | glast hbuf R | W Ft U | (fwd) Qg Cq  / (bwd) F Wt Qgt Cqt | bwd set]
-//   save-all:  saved = [glast hbuf R F Wt Qgt Cqt]
-//              ws (fwd) = [index | W Ft U Qg Cq],  ws (bwd) = [index | bwd set]
+// the save-all policy; everything else is scratch in the workspace.  The
+// reverse set is what the reverse scan and the chunk backward read:
+// F Wt Qgt Cqt (reverse scan) and At Kt Qt G2t (chunk backward).
+//   recompute: ws = [index | glast hbuf R | W Ft U | (fwd) Qg Cq  / (bwd) reverse set | Rbt dhbuf]
+//   save-all:  saved = [glast hbuf R | reverse set]
+//              ws (fwd) = [index | W Ft U Qg Cq],  ws (bwd) = [index | Rbt dhbuf]
 struct Layout {
   size_t chunks, seqoff;
   size_t glast, hbuf, R;             // read by output and backward
   size_t W, Ft, U;                   // forward scan operands
   size_t Qg, Cq;                     // output operands
   size_t F, Wt, Qgt, Cqt;            // reverse scan operands
-  size_t Rb, dhbuf, P, D, Hq, dbw;   // backward set
+  size_t At, Kt, Qt, G2t;            // chunk backward operands
+  size_t Rbt, dhbuf;                 // written by the reverse scan
   size_t ws_fwd, ws_bwd, saved;
 };
 
@@ -107,9 +110,22 @@ Layout layout(const Plan& p) {
   Layout L{};
   const size_t nc = p.nc_max, H = p.H, K = p.K, V = p.V, BT = p.BT, e = p.esz;
   const size_t tokK = BT * H * K * e, tokV = BT * H * V * e;
-  const size_t tileK = nc * H * K * CH * e, tile64 = nc * H * CH * CH * e;
+  const size_t tileK = nc * H * K * CH * e, tileV = nc * H * V * CH * e;
+  const size_t tile64 = nc * H * CH * CH * e;
+  const size_t g2 = p.gate == REWY_GATE_VECTOR ? nc * H * K * CH * 4
+                    : p.gate == REWY_GATE_SCALAR ? nc * H * CH * 4 : 0;
   size_t off = 0;
   auto take = [&](size_t& o, size_t bytes) { const size_t r = o; o += up(bytes); return r; };
+  auto take_reverse = [&](size_t& o) {
+    L.F = take(o, tokK);
+    L.Wt = take(o, tileK);
+    L.Qgt = take(o, tileK);
+    L.Cqt = take(o, tile64);
+    L.At = take(o, tile64);
+    L.Kt = take(o, tileK);
+    L.Qt = take(o, tileK);
+    L.G2t = take(o, g2);
+  };
   L.chunks = take(off, nc * sizeof(ChunkInfo));
   L.seqoff = take(off, (size_t)(p.N + 1) * 4);
   const size_t head = off;
@@ -118,13 +134,9 @@ Layout layout(const Plan& p) {
   L.glast = take(s, nc * H * K * 4);
   L.hbuf = take(s, nc * H * K * V * e);
   L.R = take(s, tokV);
-  size_t bs = save ? s : 0;  // reverse-scan set: in `saved` for save-all
   if (save) {
-    L.F = take(bs, tokK);
-    L.Wt = take(bs, tileK);
-    L.Qgt = take(bs, tileK);
-    L.Cqt = take(bs, tile64);
-    L.saved = bs;
+    take_reverse(s);
+    L.saved = s;
     off = head;
   } else {
     off = s;
@@ -139,19 +151,11 @@ Layout layout(const Plan& p) {
   if (save) {
     off = head;
   } else {
-    size_t u = after_scan;  // reverse-scan set shares the output operands' space
-    L.F = take(u, tokK);
-    L.Wt = take(u, tileK);
-    L.Qgt = take(u, tileK);
-    L.Cqt = take(u, tile64);
-    off = u;
+    off = after_scan;  // the reverse set shares the output operands' space
+    take_reverse(off);
   }
-  L.Rb = take(off, tokV);
+  L.Rbt = take(off, tileV);
   L.dhbuf = take(off, nc * H * K * V * e);
-  L.P = take(off, tokV);
-  L.D = take(off, tile64);
-  L.Hq = take(off, tile64);
-  L.dbw = take(off, BT * H * 4);
   L.ws_bwd = off;
   return L;
 }
@@ -188,8 +192,9 @@ void fill_common(Args& a, const Plan& p, const rewy_desc* d, char* ws, char* sv,
   a.hbuf = fs + L.hbuf; a.R = fs + L.R;
   a.F = fs + L.F; a.Wt = fs + L.Wt; a.Qgt = fs + L.Qgt; a.Cqt = fs + L.Cqt;
   a.W = ws + L.W; a.Ft = ws + L.Ft; a.U = ws + L.U; a.Qg = ws + L.Qg; a.Cq = ws + L.Cq;
-  a.Rb = ws + L.Rb; a.dhbuf = ws + L.dhbuf; a.P = ws + L.P; a.D = ws + L.D; a.Hq = ws + L.Hq;
-  a.dbw = reinterpret_cast<float*>(ws + L.dbw);
+  a.At = fs + L.At; a.Kt = fs + L.Kt; a.Qt = fs + L.Qt;
+  a.G2t = reinterpret_cast<float*>(fs + L.G2t);
+  a.Rbt = ws + L.Rbt; a.dhbuf = ws + L.dhbuf;
 }
 
 int check_tensor_ptrs(const void* const* ps, const char* const* names, int n) {
@@ -300,7 +305,8 @@ REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const vo
   Args a;
   fill_common(a, p, d, static_cast<char*>(workspace), static_cast<char*>(saved), L);
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
-  a.prep_mode = PREP_FWD_SCAN | PREP_FWD_OUT | (p.policy == REWY_SAVE ? PREP_BWD_SCAN : 0);
+  a.prep_mode = PREP_FWD_SCAN | PREP_FWD_OUT |
+                (p.policy == REWY_SAVE ? PREP_BWD_SCAN | PREP_BWD_CHUNK : 0);
   return run_forward_stages(a, p.f32, true, s);
 }
 
@@ -336,7 +342,7 @@ REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const vo
   Args a;
   fill_common(a, p, d, static_cast<char*>(workspace),
               const_cast<char*>(static_cast<const char*>(saved)), L);
-  a.prep_mode = PREP_FWD_SCAN | PREP_BWD_SCAN;
+  a.prep_mode = PREP_FWD_SCAN | PREP_BWD_SCAN | PREP_BWD_CHUNK;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = dO; a.dht = dht;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
   const bool f32 = p.f32;
@@ -351,11 +357,8 @@ REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const vo
   if ((rc = hip_check(traced("k_bwd_scan", vr, s, [&] { return launch_bwd_scan(a, f32, s); }),
                       "reverse scan")))
     return rc;
-  if ((rc = hip_check(traced("k_bwd_prod", vr, s, [&] { return launch_bwd_prod(a, f32, s); }),
-                      "ReWY producer")))
-    return rc;
-  if ((rc = hip_check(traced("k_bwd_cons", vr, s, [&] { return launch_bwd_cons(a, f32, s); }),
-                      "gradient consumer")))
+  if ((rc = hip_check(traced("k_bwd_chunk", vr, s, [&] { return launch_bwd_chunk(a, f32, s); }),
+                      "chunk backward")))
     return rc;
   return REWY_OK;
 }

@@ -1,0 +1,561 @@
+// Chunk-parallel backward after the reverse scan: the ReWY shared-sensitivity
+// producer, the gradient consumers and the gate reverse sum, fused into one
+// workgroup per (chunk, head).  ReWY paper Algorithm 1 steps 1-4 and
+// Appendices 7 and 10; KDA blog sections 6.3-6.5 for the gated operands.
+//
+//   P  = A^T Rbar                       shared sensitivity (no adjoint of A)
+//   dv = beta * P,  dbeta_write_i = <V_i, P_i>
+//   D  = -tril_strict(P R^T),  Hq = tril_incl(dO R^T)
+//   Qgbar = dO S^T + Hq Y,  Ebar = -P S^T + D Y,  Ybar = D^T E + Hq^T Qg + Fbar Lambda,
+//   Fbar = R dS+^T        (S = state entering the chunk, dS+ = adjoint of the state leaving it)
+//   dq = s gamma Qgbar,  dk = beta gamma Ebar + Ybar / gamma,  dbeta_erase = <gamma K, Ebar>
+//   Gbar = Qg Qgbar + E Ebar - Y Ybar,  plus at the last row
+//          lambda = gamma_last * (rowsum(S * dS+) + colsum(Y * Fbar))
+//   dg = reverse in-chunk cumulative sum of Gbar (summed over features for a scalar gate)
+//
+// Work split.  Wave I (of four) owns the token rows [16 I, 16 I + 16) of every
+// output.  Its left operands D[I, :], Hq[I, :] and the transposed D[:, I]^T,
+// Hq[:, I]^T are computed straight into MFMA operand registers: the C tile of
+// M^T holds, lane by lane, exactly the A-operand fragment of M (lane l gets row
+// l & 15 and four consecutive columns), so none of them goes through LDS.  The
+// gated right operands (keys and queries times exp2 factors) are formed in
+// registers from token-contiguous tiles, one 16-feature block at a time; a lane
+// holds four consecutive tokens of one feature, which is the B-operand fragment
+// of a 16-token contraction.
+//
+// Gate factors (ReWY paper section 3.3 and Appendix 8).  For receiving block I
+// and an earlier sending block J the sending operand is K exp2(Gl_J - G), the
+// column factor exp2(Gf_I - Gl_J) and the receiving factor exp2(G - Gf_I), where
+// Gf and Gl are G2 at the block's first and last valid row: every factor is at
+// most 1.  The transposed products mirror this with I and J exchanged.  A
+// diagonal block is centred on its midpoint (max + min) / 2, and when some
+// feature of the 16-feature block spans more than CENTRE_MAX_RANGE it is summed
+// pairwise instead.  Sending operands are split into a high and a low bf16 part
+// (x ~ hi + lo): the log-gate gradient is a difference of nearly equal
+// receiving and sending sums, which amplifies operand rounding.
+#include "chunk_common.hpp"
+
+namespace rewy {
+
+// Four values along a 16-token contraction held by one lane: the A-operand
+// fragment of row (l & 15) or the B-operand fragment of column (l & 15).
+template <typename T>
+struct Frag4;
+template <>
+struct Frag4<bf16> {
+  using type = bf16x4;
+};
+template <>
+struct Frag4<float> {
+  using type = f32x4;
+};
+
+// acc += A[16 x 16] B[16 x 16] with both operands given as lane fragments: lane
+// l supplies A(l & 15, 4 (l >> 4) + e) and B(4 (l >> 4) + e, l & 15), e = 0..3.
+// fp32 runs four 16x16x4 steps, step e taking contraction slot 4 (l >> 4) + e.
+__device__ __forceinline__ void mm16(f32x4& acc, bf16x4 a, bf16x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mm16(f32x4& acc, f32x4 a, f32x4 b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Frag4<T>::type to_frag(const f32x4& x) {
+  if constexpr (std::is_same_v<T, bf16>) {
+    bf16x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (bf16)x[e];
+    return r;
+  } else {
+    return x;
+  }
+}
+
+// acc += M x (hi + lo) for a sending operand x given in fp32 (bf16: two MFMAs).
+template <typename T>
+__device__ __forceinline__ void mm16_split(f32x4& acc, typename Frag4<T>::type m, const f32x4& x) {
+  if constexpr (std::is_same_v<T, bf16>) {
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = (bf16)x[e];
+      lo[e] = (bf16)(x[e] - (float)hi[e]);
+    }
+    mm16(acc, m, hi);
+    mm16(acc, m, lo);
+  } else {
+    mm16(acc, m, x);
+  }
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).  Every
+// register array below is indexed by such constants only (an index the
+// compiler cannot resolve would move the array to scratch memory).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// arr[I] for a wave-uniform I, by selects
+template <typename X>
+__device__ __forceinline__ X pick(const X (&arr)[NSUB], int I) {
+  X r = arr[0];
+  static_for<1, NSUB>([&](auto J) {
+    if (I == J) r = arr[J];
+  });
+  return r;
+}
+__device__ __forceinline__ float comp(const f32x4& x, int e) {
+  return e == 0 ? x[0] : e == 1 ? x[1] : e == 2 ? x[2] : x[3];
+}
+
+template <typename T, int K, int V>
+__global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
+  constexpr int NTH = 256;
+  constexpr int PV = pitch<T>(V), PA = pitch<T>(CH);
+  constexpr int NFB = K / SUB, NVB = V / SUB;
+  constexpr int KS = MM<T>::KS;
+  constexpr int PD = SUB + 1;  // fp32 diagonal blocks for the pairwise path
+  constexpr int SZ_AT = CH * PA * (int)sizeof(T), SZ_DG = NSUB * 2 * SUB * PD * 4;
+  using FR = typename Frag4<T>::type;
+
+  __shared__ __align__(16) T sO[CH * PV];  // dO
+  __shared__ __align__(16) T sP[CH * PV];  // P
+  __shared__ __align__(16) T sR[CH * PV];  // R
+  __shared__ __align__(16) char sX[cmax(SZ_AT, SZ_DG)];  // A^T, then the diagonal blocks
+  __shared__ __align__(16) float sBeta[CH];
+  __shared__ float sDbw[CH];
+  __shared__ float sTot[2][NSUB * SUB], sLam[2][NSUB * SUB];  // per feature block, two buffers
+
+  const int H = a.H;
+  const int c = blockIdx.x / H, h = blockIdx.x - c * H;
+  const ChunkInfo ci = a.chunks[c];
+  const int n = ci.len;
+  if (n == 0) return;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int q4 = l >> 4, f = l & 15;
+  const int I = w;  // row block of this wave
+  const bool live = I * SUB < n;
+  const int64_t t0 = ci.bos, cb = (int64_t)c * H + h;
+  const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
+  const float scale = a.scale;
+  T* sAt = reinterpret_cast<T*>(sX);
+  float* sDiag = reinterpret_cast<float*>(sX) + w * 2 * SUB * PD;  // [D_II | Hq_II], this wave
+
+  // ---- loads ---------------------------------------------------------------
+  g2s<T, V>(sO, PV, reinterpret_cast<const T*>(a.dO) + (t0 * H + h) * V, gsV, n, CH, tid, NTH);
+  g2s<T, V>(sR, PV, reinterpret_cast<const T*>(a.R) + (t0 * H + h) * V, gsV, n, CH, tid, NTH);
+  g2s<T, CH>(sAt, PA, reinterpret_cast<const T*>(a.At) + cb * CH * CH, CH, CH, CH, tid, NTH);
+  if (tid < CH) sBeta[tid] = tid < n ? ld_beta(a.beta, a.beta_f32, (t0 + tid) * H + h) : 0.f;
+  __syncthreads();
+
+  // ---- P = A^T Rbar, rows of block I; dv and the write part of dbeta --------
+  // The tile computed is P^T (rows v, columns i): its C fragment gives lane l
+  // row i = 16 I + (l & 15) and the four columns v0 .. v0 + 3, v0 = 16 vb + 4 (l >> 4).
+  {
+    const T* Rbt = reinterpret_cast<const T*>(a.Rbt) + cb * V * CH;
+    const T* vg = reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V;
+    T* dvg = reinterpret_cast<T*>(a.dv) + (t0 * H + h) * V;
+    const int k0 = (I * SUB / KS) * KS;  // A^T is upper triangular: tokens j >= 16 I
+    const int i = I * SUB + f;
+    const float b = sBeta[i];
+    float dbw = 0.f;
+    for (int vb = 0; vb < NVB; ++vb) {
+      f32x4 acc = zero4();
+      if (live)
+        mma_tile<T, true, true>(acc, Rbt + vb * SUB * CH + k0, CH, 1, sAt + I * SUB * PA + k0, PA,
+                                1, CH - k0);
+      const int v0 = vb * SUB + 4 * q4;
+      if (i < n) {
+        f32x4 vv;
+        if constexpr (std::is_same_v<T, bf16>) {
+          const bf16x4 x = *reinterpret_cast<const bf16x4*>(vg + i * gsV + v0);
+          bf16x4 y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vv[e] = (float)x[e];
+            y[e] = (bf16)(b * acc[e]);
+          }
+          *reinterpret_cast<bf16x4*>(dvg + i * gsV + v0) = y;
+        } else {
+          vv = *reinterpret_cast<const f32x4*>(vg + i * gsV + v0);
+          *reinterpret_cast<f32x4*>(dvg + i * gsV + v0) = b * acc;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dbw += vv[e] * acc[e];
+      }
+      *reinterpret_cast<FR*>(sP + i * PV + v0) = to_frag<T>(acc);
+    }
+    dbw += __shfl_xor(dbw, 16);
+    dbw += __shfl_xor(dbw, 32);
+    if (q4 == 0) sDbw[i] = dbw;
+  }
+  __syncthreads();  // P complete; A^T is dead
+
+  // ---- left operands of block I, straight into fragments ---------------------
+  //   Dm[J]  = D[I, J]      (J <= I)    Hm[J]  = Hq[I, J]      (J <= I)
+  //   Dtm[J] = D[J, I]^T    (J >= I)    Htm[J] = Hq[J, I]^T    (J >= I)
+  // The fragment of M is the C tile of M^T; lane l holds M(l & 15, 4 (l >> 4) + e).
+  FR Dm[NSUB], Hm[NSUB], Dtm[NSUB], Htm[NSUB];
+  static_for<0, NSUB>([&](auto J) {
+    Dm[J] = Hm[J] = Dtm[J] = Htm[J] = to_frag<T>(zero4());
+    if (!live || J * SUB >= n) return;
+    if (J <= I) {
+      f32x4 yd = zero4(), yh = zero4();
+      mma_tile<T, true, true>(yd, sR + J * SUB * PV, PV, 1, sP + I * SUB * PV, PV, 1, V);
+      mma_tile<T, true, true>(yh, sR + J * SUB * PV, PV, 1, sO + I * SUB * PV, PV, 1, V);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jj = 4 * q4 + e;  // column of M inside block J; row is f
+        yd[e] = (J < I || jj < f) ? -yd[e] : 0.f;
+        yh[e] = (J < I || jj <= f) ? yh[e] : 0.f;
+        if (J == I) {
+          sDiag[f * PD + jj] = yd[e];
+          sDiag[SUB * PD + f * PD + jj] = yh[e];
+        }
+      }
+      Dm[J] = to_frag<T>(yd);
+      Hm[J] = to_frag<T>(yh);
+    }
+    if (J >= I) {
+      f32x4 yd = zero4(), yh = zero4();
+      mma_tile<T, true, true>(yd, sP + J * SUB * PV, PV, 1, sR + I * SUB * PV, PV, 1, V);
+      mma_tile<T, true, true>(yh, sO + J * SUB * PV, PV, 1, sR + I * SUB * PV, PV, 1, V);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jj = 4 * q4 + e;
+        yd[e] = (J > I || jj > f) ? -yd[e] : 0.f;
+        yh[e] = (J > I || jj >= f) ? yh[e] : 0.f;
+      }
+      Dtm[J] = to_frag<T>(yd);
+      Htm[J] = to_frag<T>(yh);
+    }
+  });
+  __syncthreads();  // diagonal blocks in sDiag visible to every lane of the wave
+
+  // ---- per 16-feature block: state products, matrix intra, chain rules -------
+  // The gate reverse sum needs the block totals of the later row blocks: they
+  // are exchanged through LDS once per feature block (all waves take part).
+  const T* hb = reinterpret_cast<const T*>(a.hbuf) + cb * K * V;
+  const T* dhb = reinterpret_cast<const T*>(a.dhbuf) + cb * K * V;
+  const T* Ktg = reinterpret_cast<const T*>(a.Kt) + cb * K * CH;
+  const T* Qtg = reinterpret_cast<const T*>(a.Qt) + cb * K * CH;
+  T* dqg = reinterpret_cast<T*>(a.dq) + (t0 * H + h) * K;
+  T* dkg = reinterpret_cast<T*>(a.dk) + (t0 * H + h) * K;
+  const int jl = n - 1;  // last valid row
+  const FR DmI = pick(Dm, I), HmI = pick(Hm, I), DtmI = pick(Dtm, I), HtmI = pick(Htm, I);
+  f32x4 beta_r[NSUB];
+  static_for<0, NSUB>([&](auto J) {
+    beta_r[J] = *reinterpret_cast<const f32x4*>(sBeta + J * SUB + 4 * q4);
+  });
+  const f32x4 bI = pick(beta_r, I);
+  f32x4 sufs = zero4();  // scalar gate: Gbar summed over features, this lane's rows
+  float dbe[4] = {0.f, 0.f, 0.f, 0.f};
+  float lam0s = 0.f, lamws = 0.f;
+
+#pragma unroll 1
+  for (int fb = 0; fb < NFB; ++fb) {
+    const int kc = fb * SUB + f;  // this lane's feature
+    const int buf = fb & 1;
+    f32x4 gbar = zero4();
+    float lamw = 0.f, l0 = 0.f;
+    if (live) {
+      // gated operands of all four blocks at this lane's rows 16 J + 4 q4 + e
+      f32x4 G[NSUB], kx[NSUB], qx[NSUB];
+      static_for<0, NSUB>([&](auto J) {
+        const int r0 = J * SUB + 4 * q4;
+        if (a.gate == 2)
+          G[J] = *reinterpret_cast<const f32x4*>(a.G2t + (cb * K + kc) * CH + r0);
+        else if (a.gate == 1)
+          G[J] = *reinterpret_cast<const f32x4*>(a.G2t + cb * CH + r0);
+        else
+          G[J] = zero4();
+        const FR kf = *reinterpret_cast<const FR*>(Ktg + (int64_t)kc * CH + r0);
+        const FR qf = *reinterpret_cast<const FR*>(Qtg + (int64_t)kc * CH + r0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kx[J][e] = tof(kf[e]);
+          qx[J][e] = tof(qf[e]);
+        }
+      });
+      // block statistics over valid rows: first / last valid row, midpoint, range
+      float Gf[NSUB], Gl[NSUB], Md[NSUB];
+      bool wide[NSUB];
+      static_for<0, NSUB>([&](auto J) {
+        float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (J * SUB + 4 * q4 + e < n) {
+            mx = fmaxf(mx, G[J][e]);
+            mn = fminf(mn, G[J][e]);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mn = fminf(mn, __shfl_xor(mn, 16));
+        mn = fminf(mn, __shfl_xor(mn, 32));
+        const int last = min(J * SUB + SUB - 1, jl);
+        Gf[J] = __shfl(G[J][0], f);
+        Gl[J] = __shfl(comp(G[J], last & 3), (((last & 15) >> 2) << 4) | f);
+        const bool valid = J * SUB < n;
+        Md[J] = valid ? 0.5f * (mx + mn) : 0.f;
+        wide[J] = valid && __any(mx - mn > CENTRE_MAX_RANGE);
+      });
+      float GlN = Gl[0];
+      static_for<1, NSUB>([&](auto J) {
+        if (J * SUB <= jl) GlN = Gl[J];
+      });
+      const float Gn = GlN;
+      const f32x4 GI = pick(G, I), kI = pick(kx, I), qI = pick(qx, I);
+      const float GfI = pick(Gf, I), GlI = pick(Gl, I), MdI = pick(Md, I);
+      const bool wideI = pick(wide, I);
+      // state products (contraction over V) and rowsum(S * dS+) for this feature
+      f32x4 SQ = zero4(), SE = zero4(), SF = zero4();
+      {
+        const T* hr = hb + (int64_t)(fb * SUB) * V;
+        const T* dr = dhb + (int64_t)(fb * SUB) * V;
+#pragma unroll
+        for (int k0 = 0; k0 < V; k0 += KS) {
+          const auto sf = ldfrag<T, true>(hr, V, 1, k0);
+          const auto df = ldfrag<T, true>(dr, V, 1, k0);
+          if constexpr (std::is_same_v<T, bf16>) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) l0 += (float)sf[e] * (float)df[e];
+          } else {
+            l0 += sf * df;
+          }
+          SQ = mma(ldfrag<T, true>(sO + I * SUB * PV, PV, 1, k0), sf, SQ);
+          SE = mma(ldfrag<T, true>(sP + I * SUB * PV, PV, 1, k0), sf, SE);
+          SF = mma(ldfrag<T, true>(sR + I * SUB * PV, PV, 1, k0), df, SF);
+        }
+        l0 += __shfl_xor(l0, 16);
+        l0 += __shfl_xor(l0, 32);
+        l0 *= exp2f(Gn);
+      }
+      // -- sources before I: gamma (Hq Y), gamma (D Y) ----------------------------
+      f32x4 XHY = zero4(), XDY = zero4(), XDE = zero4(), XHQ = zero4();
+      static_for<0, NSUB - 1>([&](auto J) {
+        if (J >= I) return;
+        f32x4 ks;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ks[e] = kx[J][e] * exp2f(Gl[J] - G[J][e]);
+        f32x4 tH = zero4(), tD = zero4();
+        mm16_split<T>(tH, Hm[J], ks);
+        mm16_split<T>(tD, Dm[J], ks);
+        const float cf = exp2f(GfI - Gl[J]);
+        XHY += cf * tH;
+        XDY += cf * tD;
+      });
+      // -- sources after I: (D^T E) / gamma, (Hq^T Qg) / gamma -------------------
+      static_for<1, NSUB>([&](auto J) {
+        if (J <= I || J * SUB >= n) return;
+        f32x4 es, qs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = exp2f(G[J][e] - Gf[J]);
+          es[e] = beta_r[J][e] * kx[J][e] * x;
+          qs[e] = scale * qx[J][e] * x;
+        }
+        f32x4 tE = zero4(), tQ = zero4();
+        mm16_split<T>(tE, Dtm[J], es);
+        mm16_split<T>(tQ, Htm[J], qs);
+        const float cf = exp2f(Gf[J] - GlI);
+        XDE += cf * tE;
+        XHQ += cf * tQ;
+      });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fr = exp2f(GI[e] - GfI), fc = exp2f(GlI - GI[e]);
+        XHY[e] *= fr;
+        XDY[e] *= fr;
+        XDE[e] *= fc;
+        XHQ[e] *= fc;
+      }
+      // -- diagonal block ------------------------------------------------------------
+      if (!wideI) {
+        f32x4 ks, es, qs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xm = exp2f(MdI - GI[e]), xp = exp2f(GI[e] - MdI);
+          ks[e] = kI[e] * xm;
+          es[e] = bI[e] * kI[e] * xp;
+          qs[e] = scale * qI[e] * xp;
+        }
+        f32x4 tH = zero4(), tD = zero4(), tE = zero4(), tQ = zero4();
+        mm16_split<T>(tH, HmI, ks);
+        mm16_split<T>(tD, DmI, ks);
+        mm16_split<T>(tE, DtmI, es);
+        mm16_split<T>(tQ, HtmI, qs);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float fr = exp2f(GI[e] - MdI), fc = exp2f(MdI - GI[e]);
+          XHY[e] += fr * tH[e];
+          XDY[e] += fr * tD[e];
+          XDE[e] += fc * tE[e];
+          XHQ[e] += fc * tQ[e];
+        }
+      } else {
+        // pairwise inside the block: exp2(G_r - G_j) formed per pair, never above 1
+        const float* Dd = sDiag;
+        const float* Hd = sDiag + SUB * PD;
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+          const int src = ((j >> 2) << 4) | f;
+          const float Gj = __shfl(GI[j & 3], src);
+          const float kj = __shfl(kI[j & 3], src);
+          const float qj = __shfl(qI[j & 3], src);
+          const float bj = sBeta[I * SUB + j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            if (j <= r) {
+              const float x = exp2f(GI[e] - Gj) * kj;
+              XHY[e] += Hd[r * PD + j] * x;
+              XDY[e] += Dd[r * PD + j] * x;
+            }
+            if (j >= r) {
+              const float x = exp2f(Gj - GI[e]);
+              XDE[e] += Dd[j * PD + r] * bj * kj * x;
+              XHQ[e] += Hd[j * PD + r] * scale * qj * x;
+            }
+          }
+        }
+      }
+      // -- chain rules ---------------------------------------------------------------
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = I * SUB + 4 * q4 + e;
+        if (row < n) {
+          const float gam = exp2f(GI[e]), tail = exp2f(Gn - GI[e]);
+          const float XQ = gam * SQ[e] + XHY[e];
+          const float XE = -gam * SE[e] + XDY[e];
+          const float XY = XDE[e] + XHQ[e] + SF[e] * tail;
+          const float kv = kI[e], qv = qI[e], b = bI[e];
+          dqg[row * gsK + kc] = fromf<T>(scale * XQ);
+          dkg[row * gsK + kc] = fromf<T>(b * XE + XY);
+          gbar[e] = scale * qv * XQ + b * kv * XE - kv * XY;
+          dbe[e] += kv * XE;
+          lamw += kv * SF[e] * tail;
+        }
+      }
+      lamw += __shfl_xor(lamw, 16);
+      lamw += __shfl_xor(lamw, 32);
+    }
+    if (a.gate == 2) {
+      // in-block reverse sum: own rows, then the lane groups after this one
+      const float s = gbar[0] + gbar[1] + gbar[2] + gbar[3];
+      float x = s;
+      float y = __shfl_down(x, 16);
+      x += q4 < 3 ? y : 0.f;
+      y = __shfl_down(x, 32);
+      x += q4 < 2 ? y : 0.f;  // sum over lane groups >= q4
+      float run = x - s;
+      f32x4 suf;
+      suf[3] = run += gbar[3];
+      suf[2] = run += gbar[2];
+      suf[1] = run += gbar[1];
+      suf[0] = run + gbar[0];
+      if (q4 == 0) {
+        sTot[buf][I * SUB + f] = x;
+        sLam[buf][I * SUB + f] = lamw;
+      }
+      __syncthreads();
+      if (live) {
+        float add = l0;  // endpoint term, added to every row
+#pragma unroll
+        for (int J = 0; J < NSUB; ++J) {
+          add += sLam[buf][J * SUB + f];
+          if (J > I) add += sTot[buf][J * SUB + f];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = I * SUB + 4 * q4 + e;
+          if (row < n) a.dg[((t0 + row) * H + h) * K + kc] = suf[e] + add;
+        }
+      }
+    } else if (a.gate == 1 && live) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = gbar[e];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        sufs[e] += x;
+      }
+      float x = lamw, y = l0;
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 8);
+      y += __shfl_xor(y, 1);
+      y += __shfl_xor(y, 2);
+      y += __shfl_xor(y, 4);
+      y += __shfl_xor(y, 8);
+      lamws += x;
+      lam0s += y;
+    }
+  }
+
+  // ---- dbeta = write part + erase part (rows of block I) ---------------------
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float x = dbe[e];
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    const int row = I * SUB + 4 * q4 + e;
+    if (f == 0 && row < n)
+      st_beta(a.dbeta, a.beta_f32, (t0 + row) * H + h, sDbw[row] + x);
+  }
+
+  // ---- scalar gate: reverse sum over the chunk's rows ---------------------------
+  if (a.gate == 1) {
+    const float s = sufs[0] + sufs[1] + sufs[2] + sufs[3];
+    float x = s;
+    float y = __shfl_down(x, 16);
+    x += q4 < 3 ? y : 0.f;
+    y = __shfl_down(x, 32);
+    x += q4 < 2 ? y : 0.f;
+    float run = x - s;
+    sufs[3] = run += sufs[3];
+    sufs[2] = run += sufs[2];
+    sufs[1] = run += sufs[1];
+    sufs[0] = run + sufs[0];
+    const int buf = NFB & 1;  // not used by the last feature block
+    if (l == 0) {
+      sTot[buf][I] = live ? x : 0.f;
+      sLam[buf][I] = live ? lamws : 0.f;
+    }
+    __syncthreads();
+    if (live) {
+      float add = lam0s;
+      for (int J = 0; J < NSUB; ++J) {
+        add += sLam[buf][J];
+        if (J > I) add += sTot[buf][J];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = I * SUB + 4 * q4 + e;
+        if (f == 0 && row < n) a.dg[(t0 + row) * H + h] = sufs[e] + add;
+      }
+    }
+  }
+}
+
+template <typename T>
+static hipError_t bwd_chunk_t(const Args& a, hipStream_t s) {
+  const dim3 grid(a.nc_max * a.H), block(256);
+  REWY_KV_SWITCH(k_bwd_chunk)
+}
+
+hipError_t launch_bwd_chunk(const Args& a, int f32, hipStream_t s) {
+  return f32 ? bwd_chunk_t<float>(a, s) : bwd_chunk_t<bf16>(a, s);
+}
+
+}  // namespace rewy

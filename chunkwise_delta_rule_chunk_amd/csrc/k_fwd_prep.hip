@@ -200,16 +200,20 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       constexpr int VE = 16 / (int)sizeof(T);
       T* Ftd = reinterpret_cast<T*>(a.Ft) + (cb * K + col) * CH + r0;
       T* Qgtd = reinterpret_cast<T*>(a.Qgt) + (cb * K + col) * CH + r0;
+      T* Ktd = reinterpret_cast<T*>(a.Kt) + (cb * K + col) * CH + r0;
+      T* Qtd = reinterpret_cast<T*>(a.Qt) + (cb * K + col) * CH + r0;
 #pragma unroll
       for (int r8 = 0; r8 < RS; r8 += VE) {
         union {
           uint4 u;
           T e[VE];
-        } ft, qt;
+        } ft, qt, kt, qq;
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
           const int r = r8 + e, row = r0 + r;
           float vKa = 0.f, vQa = 0.f, vKc = 0.f, vE = 0.f, vF = 0.f, vQg = 0.f;
+          kt.e[e] = sK[row * PK + col];  // raw k and q (zero past the chunk's end)
+          qq.e[e] = sQ[row * PK + col];
           if (row < n) {
             const int J = row / SUB;
             const float G = gc.G[r];
@@ -238,6 +242,20 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         // token-contiguous tiles: this thread holds consecutive tokens of column col
         if (mode & PREP_FWD_SCAN) *reinterpret_cast<uint4*>(Ftd + r8) = ft.u;
         if (mode & PREP_BWD_SCAN) *reinterpret_cast<uint4*>(Qgtd + r8) = qt.u;
+        if (mode & PREP_BWD_CHUNK) {
+          *reinterpret_cast<uint4*>(Ktd + r8) = kt.u;
+          *reinterpret_cast<uint4*>(Qtd + r8) = qq.u;
+        }
+      }
+      // G2 token-contiguous (rows past the end hold G2 of the last row)
+      if (mode & PREP_BWD_CHUNK) {
+        float* G2d = a.gate == 2 ? a.G2t + (cb * K + col) * CH + r0
+                                 : (a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr);
+        if (G2d)
+#pragma unroll
+          for (int r4 = 0; r4 < RS; r4 += 4)
+            *reinterpret_cast<f32x4*>(G2d + r4) =
+                f32x4{gc.G[r4], gc.G[r4 + 1], gc.G[r4 + 2], gc.G[r4 + 3]};
       }
       if ((mode & (PREP_FWD_SCAN | PREP_BWD_SCAN)) && gc.seg == 0) a.glast[cb * K + col] = gn;
     }
@@ -280,6 +298,20 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
 
     // ---- S4: A = (I + L)^-1 in fp32 ------------------------------------------
     solve_unit_lower(sL, sA, PL, sT, n);
+    if (mode & PREP_BWD_CHUNK) {  // A^T for the chunk backward, 16-byte rows
+      constexpr int VA = 16 / (int)sizeof(T), PER = CH / VA;
+      T* Ato = reinterpret_cast<T*>(a.At) + cb * CH * CH;
+      for (int idx = tid; idx < CH * PER; idx += NTH) {
+        const int i = idx / PER, j0 = (idx - i * PER) * VA;
+        union {
+          uint4 u;
+          T e[VA];
+        } v;
+#pragma unroll
+        for (int e = 0; e < VA; ++e) v.e[e] = fromf<T>(sA[(j0 + e) * PL + i]);
+        *reinterpret_cast<uint4*>(Ato + i * CH + j0) = v.u;
+      }
+    }
 
     // ---- S5: W = A E, U = A Z --------------------------------------------------
     T* Wo = reinterpret_cast<T*>(a.W) + (t0 * H + h) * K;

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
     }
     __syncthreads();
     // Rbar = F dS+ + Cq^T dO
-    T* Rbg = reinterpret_cast<T*>(a.Rb) + (t0 * H + h) * V + vt * BV;
+    T* Rbt = reinterpret_cast<T*>(a.Rbt) + ((int64_t)c * H + h) * V * CH + vt * BV * CH;
 #pragma unroll
     for (int r = 0; r < S::RPW; ++r) {
       const int t = w + 4 * r, ti = t / CT, tv = t - ti * CT;
@@ -230,10 +230,11 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
       mma_tile<T, true, true>(acc, sF[b] + ti * SUB * PK, PK, 1, sDt + tv * SUB * PK, PK, 1, K);
       mma_tile<T, true, true>(acc, sCqt[b] + ti * SUB * PA, PA, 1, sdOt[b] + tv * SUB * PA, PA, 1,
                               CH);
+      // rows past the chunk's end are exact zeros (F and Cq vanish there)
+      st_tile_T<T>(acc, Rbt + (tv * SUB) * CH + ti * SUB, CH);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = ti * SUB + crow(i), col = tv * SUB + ccol();
-        if (row < len) Rbg[row * gsV + col] = fromf<T>(acc[i]);
         sRbt[col * PA + row] = fromf<T>(-acc[i]);
       }
     }

@@ -57,18 +57,19 @@ struct Args {
   void* Cqt;     // Cq^T                [nc,H,64,64] reverse scan (Rbar += Cq^T dO)
   void* hbuf;    // state entering each chunk [nc,H,K,V] dtype
   void* R;       // corrections U - W S [BT,H,V] dtype
+  void* At;      // A^T                 [nc,H,64,64] chunk backward (P = A^T Rbar)
+  void* Kt;      // K^T                 [nc,H,K,64]  chunk backward
+  void* Qt;      // Q^T                 [nc,H,K,64]  chunk backward
+  float* G2t;    // G2^T  [nc,H,K,64] (vector gate) or [nc,H,64] (scalar gate)
   // backward intermediates
-  void* Rb;      // accumulated correction adjoint [BT,H,V] dtype
+  void* Rbt;     // correction adjoint Rbar^T [nc,H,V,64] dtype
   void* dhbuf;   // adjoint of the state leaving each chunk [nc,H,K,V] dtype
-  void* P;       // shared sensitivity A^T Rbar [BT,H,V] dtype
-  void* D;       // -tril_strict(P R^T) [nc,H,64,64] dtype
-  void* Hq;      // tril_incl(dO R^T)   [nc,H,64,64] dtype
-  float* dbw;    // write part of dbeta, <V_i, P_i>  [BT,H] fp32
 };
 
 constexpr int PREP_FWD_SCAN = 1;  // W, Ft, U, glast
 constexpr int PREP_FWD_OUT = 2;   // Qg, Cq
 constexpr int PREP_BWD_SCAN = 4;  // F, Wt, Qgt, Cqt, glast
+constexpr int PREP_BWD_CHUNK = 8; // At, Kt, Qt, G2t
 
 // Launchers: enqueue on `stream`; return the hipError_t of the launch.
 hipError_t launch_chunk_table(const Args& a, hipStream_t s);
@@ -79,7 +80,6 @@ int scan_bv(const Args& a, int dtype_f32);
 hipError_t launch_fwd_scan(const Args& a, int dtype_f32, hipStream_t s);
 hipError_t launch_fwd_out(const Args& a, int dtype_f32, hipStream_t s);
 hipError_t launch_bwd_scan(const Args& a, int dtype_f32, hipStream_t s);
-hipError_t launch_bwd_prod(const Args& a, int dtype_f32, hipStream_t s);
-hipError_t launch_bwd_cons(const Args& a, int dtype_f32, hipStream_t s);
+hipError_t launch_bwd_chunk(const Args& a, int dtype_f32, hipStream_t s);
 
 }  // namespace rewy

@@ -86,7 +86,8 @@ def test_workspace_sizes_follow_the_layout(lib):
     scan = tokK + tileK + tokV                                          # W, Ft, U
     out = tokK + tile64                                                 # Qg, Cq
     rscan = tokK + 2 * tileK + tile64                                   # F, Wt, Qgt, Cqt
-    bwd = 2 * tokV + up(nc * H * K * V * e) + 2 * tile64 + up(BT * H * 4)
+    rscan += tile64 + 2 * tileK + up(nc * H * K * 64 * 4)               # At, Kt, Qt, G2t
+    bwd = up(nc * H * V * 64 * e) + up(nc * H * K * V * e)              # Rbt, dhbuf
     assert B.rewy_workspace_bytes(d, 0) == head + shared + scan + out
     # the reverse-scan set of the backward reuses the output operands' space
     assert B.rewy_workspace_bytes(d, 1) == head + shared + scan + rscan + bwd
