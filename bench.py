@@ -23,24 +23,38 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq):
-    """Algorithmic HBM bytes one launch of `kernel` must move in this design:
-    its compulsory inputs and outputs, each counted once (chunk-level tiles per
-    chunk-head, token-level rows per valid token)."""
+def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy):
+    """Algorithmic HBM bytes of one launch of `kernel` in this design: its
+    compulsory reads and writes, each counted once.  Token-level rows count per
+    valid token; chunk tiles count their full 64 rows per chunk-head.  The
+    forward prep runs in two modes under the recompute policy (forward pass,
+    and the recompute in the backward pass that also writes the reverse-scan
+    and chunk-backward operands); its figure is the mean of the launches of
+    one step, matching the pooled average duration."""
     n = sum(chunk_lens)                 # valid tokens per head
     nc = len(chunk_lens)                # chunks per head
     gb = {0: 0, 1: 4, 2: 4 * K}[gate]   # gate bytes per token
-    tok_k, tok_v = K * esz, V * esz
-    st = K * V * esz                    # one stored state tile
-    cq = 64 * 64 * esz                  # one 64x64 coefficient tile
+    tk, tv = K * esz, V * esz           # one token row of q/k, of v
+    tileK, tileV, tile64 = nc * 64 * K * esz, nc * 64 * V * esz, nc * 64 * 64 * esz
+    st = nc * K * V * esz               # stored per-chunk states
+    glast = nc * K * 4
+    g2t = {0: 0, 1: nc * 64 * 4, 2: nc * 64 * K * 4}[gate]
+    prep_in = n * (2 * tk + tv + gb + besz)
+    w_fscan = n * (tk + tv) + tileK + glast              # W, U, Ft, glast
+    w_fout = n * tk + tile64                              # Qg, Cq
+    w_bscan = n * tk + 2 * tileK + tile64                 # F, Wt, Qgt, Cqt
+    w_bchunk = tile64 + 2 * tileK + g2t                   # At, Kt, Qt, G2t
+    if policy == "save":
+        prep = prep_in + w_fscan + w_fout + w_bscan + w_bchunk
+    else:
+        prep = prep_in + (w_fscan + w_fout + (w_fscan + w_bscan + w_bchunk)) / 2
     per_head = {
-        "k_fwd_prep": n * (2 * tok_k + tok_v + gb + besz) + n * (3 * tok_k + tok_v) + nc * (cq + 4 * K),
-        "k_fwd_scan": n * (2 * tok_k + tok_v) + nc * 4 * K + nc * st + n * tok_v,
-        "k_fwd_out": n * (tok_k + 2 * tok_v) + nc * (st + cq),
-        "k_bwd_scan": n * (3 * tok_k + tok_v) + nc * (cq + 4 * K) + nc * st + n * tok_v,
-        "k_bwd_prod": n * (tok_k + gb + besz + 4 * tok_v) + n * (2 * tok_v + 4) + nc * 2 * cq,
-        "k_bwd_cons": nc * 2 * cq + n * 3 * tok_v + nc * 2 * st + n * (2 * tok_k + gb + besz + 4)
-                      + n * (2 * tok_k + gb + besz),
+        "k_fwd_prep": prep,
+        "k_fwd_scan": n * (tk + tv) + tileK + glast + st + n * tv,
+        "k_fwd_out": n * (tk + tv) + st + tile64 + n * tv,
+        "k_bwd_scan": n * (tk + tv) + 2 * tileK + tile64 + glast + st + tileV,
+        "k_bwd_chunk": n * 3 * tv + tile64 + tileV + 2 * st + 2 * tileK + g2t + n * besz
+                       + n * (2 * tk + tv + gb + besz),
     }
     for name, b in per_head.items():
         if f"{len(name)}{name}I" in kernel:
@@ -61,6 +75,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the oracle baseline runs")
+    ap.add_argument("--min-warmup-s", type=float, default=2.0,
+                    help="warm-up lasts at least this long (profiler runs pass 0)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before the steps, copy a buffer of this many MiB once (a plain "
+                         "copy kernel of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -81,6 +100,13 @@ def main():
     prob = ops.make_problem(x.q, x.v, x.g, x.beta, scale=inp.scale, cu_seqlens=inp.cu_seqlens,
                             policy=args.policy)
     ws0, ws1 = ops.workspace(prob, 0), ops.workspace(prob, 1)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
 
     def step():
@@ -90,7 +116,7 @@ def main():
 
     t_w = time.perf_counter()
     done = 0
-    while done < args.warmup or time.perf_counter() - t_w < 2.0:
+    while done < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         step()
         done += 1
         if done % 10 == 0:
@@ -98,24 +124,29 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup {done} steps", file=sys.stderr, flush=True)
 
+    # Timed region: K steps with the library's event-pair trace on, so every
+    # kernel's duration comes from HIP events recorded on its launch stream
+    # around exactly the launches that are timed.
     torch.cuda.synchronize()
+    binding.rewy_trace_begin()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    tr = binding.rewy_trace_end()
     ms = elapsed * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
-
-    # per-kernel durations: K forward calls, then K backward calls, with the
-    # event-pair trace on (same stream, same buffers)
+    # per kernel: (average ms per launch, launches per step)
+    kern = {name: (tot / cnt, cnt / args.steps) for name, tot, cnt in tr}
+    # forward / backward split from a second, separately traced pass
     def traced(fn):
         binding.rewy_trace_begin()
         for _ in range(args.steps):
             fn()
-        tr = binding.rewy_trace_end()
+        t = binding.rewy_trace_end()
         torch.cuda.synchronize()
-        return {name: (tot / cnt, cnt / args.steps) for name, tot, cnt in tr}
+        return {name: (tot / cnt, cnt / args.steps) for name, tot, cnt in t}
 
     holder = {}
 
@@ -127,14 +158,6 @@ def main():
     k_bwd = traced(lambda: ops.backward(holder["ctx"], x.dO, x.dht, ws=ws1))
     fwd_ms = sum(a * p for a, p in k_fwd.values())
     bwd_ms = sum(a * p for a, p in k_bwd.values())
-    kern = {}
-    for d in (k_fwd, k_bwd):
-        for name, (a, p) in d.items():
-            if name in kern:  # same kernel in both passes (recompute): pool the launches
-                a0, p0 = kern[name]
-                kern[name] = ((a0 * p0 + a * p) / (p0 + p), p0 + p)
-            else:
-                kern[name] = (a, p)
     f_fwd, f_bwd, f_rc = flops.workload_flops(seq_lens, H, K, V)
     tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
     # dominant kernel: largest share of the step
@@ -143,7 +166,7 @@ def main():
     esz = 2 if inp.q.dtype == torch.bfloat16 else 4
     besz = 2 if inp.beta.dtype == torch.bfloat16 else 4
     gate = {"none": 0, "scalar": 1, "vector": 2}[inp.gate]
-    dbytes = kernel_bytes(dom, chunk_lens, H, K, V, esz, besz, gate, len(seq_lens))
+    dbytes = kernel_bytes(dom, chunk_lens, H, K, V, esz, besz, gate, len(seq_lens), args.policy)
     achieved = dbytes / (dom_avg * 1e-3) / 1e9 if dbytes else None
     roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": None if achieved is None else achieved / PEAK_HBM_GBS,
@@ -162,7 +185,11 @@ def main():
         "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
         "bwd_pct_bf16_peak": 100 * f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "flops_per_step": {"forward": f_fwd, "backward": f_bwd, "recompute_executed": f_rc},
-        "kernels_ms": {name: {"avg_ms": a, "launches_per_step": p} for name, (a, p) in kern.items()},
+        "kernels_ms": {name: {"avg_ms": a, "launches_per_step": p,
+                              "algorithmic_GBps": (lambda b: None if b is None else b / (a * 1e-3) / 1e9)(
+                                  kernel_bytes(name, chunk_lens, H, K, V, esz, besz, gate,
+                                               len(seq_lens), args.policy))}
+                       for name, (a, p) in kern.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
