@@ -46,7 +46,7 @@ __device__ __forceinline__ void solve_unit_lower(const float* sL, float* sA, int
 #pragma unroll
     for (int i = 0; i < SUB; ++i) Ab[i * PL + cc] = x[i];
   }
-  __syncthreads();
+  lds_barrier();
   for (int d = 1; d < NSUB; ++d) {
     const int I = w + d, J = w;
     const bool act = (w < NSUB - d) && (I * SUB < n);
@@ -57,13 +57,13 @@ __device__ __forceinline__ void solve_unit_lower(const float* sL, float* sA, int
                                     sA + (J * SUB) * PL + J * SUB, 1, PL, SUB * d);
       st_tile<float>(t, Ts, 20, 1);
     }
-    __syncthreads();
+    lds_barrier();
     if (act) {
       f32x4 t = zero4();
       mma_tile<float, false, false>(t, sA + (I * SUB) * PL + I * SUB, PL, 1, Ts, 1, 20, SUB);
       st_tile<float>(-t, sA + (I * SUB) * PL + J * SUB, PL, 1);
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 

@@ -74,11 +74,13 @@ struct GateCols {
 // Sub-chunk statistics from the register-resident prefix sums: midpoint, first
 // row and last valid row per (J, feature) into sMid/sGf/sGl [NSUB][KC], G2 at
 // the chunk's last valid row into sGn [KC], and sFlag[J] set when a feature's
-// range exceeds CENTRE_MAX_RANGE (sFlag zero on entry).  No barrier inside.
+// range exceeds CENTRE_MAX_RANGE (sFlag zero on entry).  With gst non-null the
+// record {first, last, midpoint, range} of every non-empty (J, feature) is also
+// written to gst[J * KC + feature].  No barrier inside.
 template <int KC>
 __device__ __forceinline__ void subchunk_stats_regs(const GateCols<KC>& gc, int n, float* sMid,
                                                     float* sGf, float* sGl, float* sGn,
-                                                    int* sFlag) {
+                                                    int* sFlag, f32x4* gst) {
   if (!gc.on) return;
   const int J = gc.seg, r0 = J * SUB;
   if (r0 >= n) return;
@@ -100,6 +102,7 @@ __device__ __forceinline__ void subchunk_stats_regs(const GateCols<KC>& gc, int 
   sGl[idx] = gl;
   if (last == n - 1) sGn[gc.c] = gl;
   if (mx - mn > CENTRE_MAX_RANGE) sFlag[J] = 1;  // benign race: same value
+  if (gst) gst[idx] = f32x4{gc.G[0], gl, 0.5f * (mx + mn), mx - mn};
 }
 
 // References of sub-chunk J for feature k (after the statistics are visible).
@@ -125,7 +128,7 @@ __device__ __forceinline__ void pair_factors(const float* sMid, const float* sGf
     float f = 0.f;
     if (I * SUB < n)
       f = (I == J) ? 1.f
-                   : exp2f(ref_recv(sMid, sGf, sFlag, I, KC, k) -
+                   : fexp2(ref_recv(sMid, sGf, sFlag, I, KC, k) -
                            ref_send(sMid, sGl, sFlag, J, KC, k));
     fac[idx] = f;
   }
@@ -214,7 +217,7 @@ __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, 
             else if (a.gate == 1) gi = a.g[(t0 + ri) * H + h];
             run += gi * LOG2E;
           }
-          const float f = exp2f(run) * kj;
+          const float f = fexp2(run) * kj;
           pL[i] += tof(kg[((t0 + ri) * H + h) * K + k]) * f;
           if constexpr (WITH_CQ) pC[i] += tof(qg[((t0 + ri) * H + h) * K + k]) * f;
         }

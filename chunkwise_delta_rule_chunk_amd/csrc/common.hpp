@@ -69,6 +69,20 @@ __device__ __forceinline__ int opaque_tid() {
   return t;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// and meets the other waves, but leaves global loads and stores in flight (a
+// full __syncthreads() fence also drains them, which would stall every barrier
+// on outstanding prefetches and output stores).  Global memory is never used
+// to communicate between the threads of one workgroup in these kernels.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 2^x with the hardware instruction (v_exp_f32): about 1 ulp, results below
+// the normal range flush to zero.  Every use is a gate factor or decay whose
+// values that small are negligible against the terms they scale.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <typename T>
 __device__ __forceinline__ float tof(T x) { return (float)x; }
 template <typename T>

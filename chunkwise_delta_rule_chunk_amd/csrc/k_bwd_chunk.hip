@@ -119,6 +119,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   constexpr int NTH = 256;
   constexpr int PV = pitch<T>(V), PA = pitch<T>(CH);
   constexpr int NFB = K / SUB, NVB = V / SUB;
+  static_assert(NFB % 2 == 0, "feature blocks are written in pairs");
   constexpr int KS = MM<T>::KS;
   constexpr int PD = SUB + 1;  // fp32 diagonal blocks for the pairwise path
   constexpr int SZ_AT = CH * PA * (int)sizeof(T), SZ_DG = NSUB * 2 * SUB * PD * 4;
@@ -152,50 +153,71 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   g2s<T, V>(sR, PV, reinterpret_cast<const T*>(a.R) + (t0 * H + h) * V, gsV, n, CH, tid, NTH);
   g2s<T, CH>(sAt, PA, reinterpret_cast<const T*>(a.At) + cb * CH * CH, CH, CH, CH, tid, NTH);
   if (tid < CH) sBeta[tid] = tid < n ? ld_beta(a.beta, a.beta_f32, (t0 + tid) * H + h) : 0.f;
-  __syncthreads();
+  lds_barrier();
 
   // ---- P = A^T Rbar, rows of block I; dv and the write part of dbeta --------
   // The tile computed is P^T (rows v, columns i): its C fragment gives lane l
   // row i = 16 I + (l & 15) and the four columns v0 .. v0 + 3, v0 = 16 vb + 4 (l >> 4).
+  // All value blocks are computed first, then each row of dv is written in one
+  // sweep (whole rows reach the cache together and leave it as full lines).
   {
     const T* Rbt = reinterpret_cast<const T*>(a.Rbt) + cb * V * CH;
     const T* vg = reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V;
     T* dvg = reinterpret_cast<T*>(a.dv) + (t0 * H + h) * V;
     const int k0 = (I * SUB / KS) * KS;  // A^T is upper triangular: tokens j >= 16 I
     const int i = I * SUB + f;
+    f32x4 acc[NVB];
+    if constexpr (std::is_same_v<T, bf16>) {
+      // bf16: at most two 32-token steps; every Rbar fragment is requested up front
+      bf16x8 rb[NVB][2];
+      static_for<0, NVB>([&](auto vb) {
+        static_for<0, 2>([&](auto st) {
+          rb[vb][st] = bf16x8{};
+          if (live && st * 32 >= k0)
+            rb[vb][st] = ldfrag<T, true>(Rbt + vb * SUB * CH, CH, 1, st * 32);
+        });
+      });
+      const bf16x8 at0 = ldfrag<T, true>(sAt + I * SUB * PA, PA, 1, 0);
+      const bf16x8 at1 = ldfrag<T, true>(sAt + I * SUB * PA, PA, 1, 32);
+      static_for<0, NVB>([&](auto vb) {
+        acc[vb] = mma(rb[vb][1], at1, zero4());
+        if (k0 == 0) acc[vb] = mma(rb[vb][0], at0, acc[vb]);
+      });
+    } else {
+      static_for<0, NVB>([&](auto vb) {
+        acc[vb] = zero4();
+        if (live)
+          mma_tile<T, true, true>(acc[vb], Rbt + vb * SUB * CH + k0, CH, 1,
+                                  sAt + I * SUB * PA + k0, PA, 1, CH - k0);
+      });
+    }
     const float b = sBeta[i];
     float dbw = 0.f;
-    for (int vb = 0; vb < NVB; ++vb) {
-      f32x4 acc = zero4();
-      if (live)
-        mma_tile<T, true, true>(acc, Rbt + vb * SUB * CH + k0, CH, 1, sAt + I * SUB * PA + k0, PA,
-                                1, CH - k0);
+    static_for<0, NVB>([&](auto vb) {
       const int v0 = vb * SUB + 4 * q4;
+      *reinterpret_cast<FR*>(sP + i * PV + v0) = to_frag<T>(acc[vb]);
       if (i < n) {
-        f32x4 vv;
         if constexpr (std::is_same_v<T, bf16>) {
           const bf16x4 x = *reinterpret_cast<const bf16x4*>(vg + i * gsV + v0);
-          bf16x4 y;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vv[e] = (float)x[e];
-            y[e] = (bf16)(b * acc[e]);
-          }
-          *reinterpret_cast<bf16x4*>(dvg + i * gsV + v0) = y;
+          for (int e = 0; e < 4; ++e) dbw += (float)x[e] * acc[vb][e];
         } else {
-          vv = *reinterpret_cast<const f32x4*>(vg + i * gsV + v0);
-          *reinterpret_cast<f32x4*>(dvg + i * gsV + v0) = b * acc;
-        }
+          const f32x4 x = *reinterpret_cast<const f32x4*>(vg + i * gsV + v0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dbw += vv[e] * acc[e];
+          for (int e = 0; e < 4; ++e) dbw += x[e] * acc[vb][e];
+        }
       }
-      *reinterpret_cast<FR*>(sP + i * PV + v0) = to_frag<T>(acc);
-    }
+    });
+    if (i < n)
+      static_for<0, NVB>([&](auto vb) {
+        const int v0 = vb * SUB + 4 * q4;
+        *reinterpret_cast<FR*>(dvg + i * gsV + v0) = to_frag<T>(b * acc[vb]);
+      });
     dbw += __shfl_xor(dbw, 16);
     dbw += __shfl_xor(dbw, 32);
     if (q4 == 0) sDbw[i] = dbw;
   }
-  __syncthreads();  // P complete; A^T is dead
+  lds_barrier();  // P complete; A^T is dead
 
   // ---- left operands of block I, straight into fragments ---------------------
   //   Dm[J]  = D[I, J]      (J <= I)    Hm[J]  = Hq[I, J]      (J <= I)
@@ -236,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       Htm[J] = to_frag<T>(yh);
     }
   });
-  __syncthreads();  // diagonal blocks in sDiag visible to every lane of the wave
+  lds_barrier();  // diagonal blocks in sDiag visible to every lane of the wave
 
   // ---- per 16-feature block: state products, matrix intra, chain rules -------
   // The gate reverse sum needs the block totals of the later row blocks: they
@@ -245,6 +267,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   const T* dhb = reinterpret_cast<const T*>(a.dhbuf) + cb * K * V;
   const T* Ktg = reinterpret_cast<const T*>(a.Kt) + cb * K * CH;
   const T* Qtg = reinterpret_cast<const T*>(a.Qt) + cb * K * CH;
+  const float* Gstg = a.Gst + cb * NSUB * K * 4;  // float4 records, [J][K]
   T* dqg = reinterpret_cast<T*>(a.dq) + (t0 * H + h) * K;
   T* dkg = reinterpret_cast<T*>(a.dk) + (t0 * H + h) * K;
   const int jl = n - 1;  // last valid row
@@ -256,6 +279,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   const f32x4 bI = pick(beta_r, I);
   f32x4 sufs = zero4();  // scalar gate: Gbar summed over features, this lane's rows
   float dbe[4] = {0.f, 0.f, 0.f, 0.f};
+  float pdq[4] = {0.f, 0.f, 0.f, 0.f}, pdk[4] = {0.f, 0.f, 0.f, 0.f};
   float lam0s = 0.f, lamws = 0.f;
 
 #pragma unroll 1
@@ -283,38 +307,50 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
           qx[J][e] = tof(qf[e]);
         }
       });
-      // block statistics over valid rows: first / last valid row, midpoint, range
+      // sub-chunk statistics of this feature (written by the forward prep):
+      // G2 at the first and last valid row, midpoint, range; only blocks with
+      // valid rows are read
       float Gf[NSUB], Gl[NSUB], Md[NSUB];
       bool wide[NSUB];
       static_for<0, NSUB>([&](auto J) {
-        float mx = -INFINITY, mn = INFINITY;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (J * SUB + 4 * q4 + e < n) {
-            mx = fmaxf(mx, G[J][e]);
-            mn = fminf(mn, G[J][e]);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        mn = fminf(mn, __shfl_xor(mn, 16));
-        mn = fminf(mn, __shfl_xor(mn, 32));
-        const int last = min(J * SUB + SUB - 1, jl);
-        Gf[J] = __shfl(G[J][0], f);
-        Gl[J] = __shfl(comp(G[J], last & 3), (((last & 15) >> 2) << 4) | f);
-        const bool valid = J * SUB < n;
-        Md[J] = valid ? 0.5f * (mx + mn) : 0.f;
-        wide[J] = valid && __any(mx - mn > CENTRE_MAX_RANGE);
+        f32x4 st = zero4();
+        if (J * SUB < n) st = reinterpret_cast<const f32x4*>(Gstg)[J * K + kc];
+        Gf[J] = st[0];
+        Gl[J] = st[1];
+        Md[J] = st[2];
+        wide[J] = __any(st[3] > CENTRE_MAX_RANGE);
       });
-      float GlN = Gl[0];
-      static_for<1, NSUB>([&](auto J) {
-        if (J * SUB <= jl) GlN = Gl[J];
-      });
-      const float Gn = GlN;
+      const float Gn = a.glast[cb * K + kc];
       const f32x4 GI = pick(G, I), kI = pick(kx, I), qI = pick(qx, I);
       const float GfI = pick(Gf, I), GlI = pick(Gl, I), MdI = pick(Md, I);
       const bool wideI = pick(wide, I);
-      // state products (contraction over V) and rowsum(S * dS+) for this feature
-      f32x4 SQ = zero4(), SE = zero4(), SF = zero4();
+      // Row factors of block I.  Centred block: xp = exp2(G - Md), xm = exp2(Md - G)
+      // (each at most 2^(range/2)), and the receiving factors follow by per-lane
+      // constants, fr = exp2(G - Gf) = xp exp2(Md - Gf), fc = exp2(Gl - G) =
+      // xm exp2(Gl - Md), tail = exp2(Gn - G) = xm exp2(Gn - Md).  A wide block
+      // forms fr, fc and tail directly (xp and xm are not used there).
+      f32x4 xp, xm, fr, fc, tail;
+      if (!wideI) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xp[e] = fexp2(GI[e] - MdI);
+          xm[e] = fexp2(MdI - GI[e]);
+        }
+        fr = xp * fexp2(MdI - GfI);
+        fc = xm * fexp2(GlI - MdI);
+        tail = xm * fexp2(Gn - MdI);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xp[e] = xm[e] = 0.f;
+          fr[e] = fexp2(GI[e] - GfI);
+          fc[e] = fexp2(GlI - GI[e]);
+          tail[e] = fexp2(Gn - GI[e]);
+        }
+      }
+      // state products (contraction over V); rowsum(S * dS+) for this feature is
+      // the diagonal of S_fb dS+_fb^T, one more MFMA on the same fragments
+      f32x4 SQ = zero4(), SE = zero4(), SF = zero4(), SS = zero4();
       {
         const T* hr = hb + (int64_t)(fb * SUB) * V;
         const T* dr = dhb + (int64_t)(fb * SUB) * V;
@@ -322,19 +358,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         for (int k0 = 0; k0 < V; k0 += KS) {
           const auto sf = ldfrag<T, true>(hr, V, 1, k0);
           const auto df = ldfrag<T, true>(dr, V, 1, k0);
-          if constexpr (std::is_same_v<T, bf16>) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) l0 += (float)sf[e] * (float)df[e];
-          } else {
-            l0 += sf * df;
-          }
+          SS = mma(sf, df, SS);
           SQ = mma(ldfrag<T, true>(sO + I * SUB * PV, PV, 1, k0), sf, SQ);
           SE = mma(ldfrag<T, true>(sP + I * SUB * PV, PV, 1, k0), sf, SE);
           SF = mma(ldfrag<T, true>(sR + I * SUB * PV, PV, 1, k0), df, SF);
         }
-        l0 += __shfl_xor(l0, 16);
-        l0 += __shfl_xor(l0, 32);
-        l0 *= exp2f(Gn);
+        // diagonal element (f, f) sits in lane 16 (f >> 2) + f, component f & 3
+        l0 = __shfl(comp(SS, f & 3), ((f >> 2) << 4) | f) * fexp2(Gn);
       }
       // -- sources before I: gamma (Hq Y), gamma (D Y) ----------------------------
       f32x4 XHY = zero4(), XDY = zero4(), XDE = zero4(), XHQ = zero4();
@@ -342,11 +372,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         if (J >= I) return;
         f32x4 ks;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ks[e] = kx[J][e] * exp2f(Gl[J] - G[J][e]);
+        for (int e = 0; e < 4; ++e) ks[e] = kx[J][e] * fexp2(Gl[J] - G[J][e]);
         f32x4 tH = zero4(), tD = zero4();
         mm16_split<T>(tH, Hm[J], ks);
         mm16_split<T>(tD, Dm[J], ks);
-        const float cf = exp2f(GfI - Gl[J]);
+        const float cf = fexp2(GfI - Gl[J]);
         XHY += cf * tH;
         XDY += cf * tD;
       });
@@ -356,48 +386,33 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         f32x4 es, qs;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x = exp2f(G[J][e] - Gf[J]);
+          const float x = fexp2(G[J][e] - Gf[J]);
           es[e] = beta_r[J][e] * kx[J][e] * x;
           qs[e] = scale * qx[J][e] * x;
         }
         f32x4 tE = zero4(), tQ = zero4();
         mm16_split<T>(tE, Dtm[J], es);
         mm16_split<T>(tQ, Htm[J], qs);
-        const float cf = exp2f(Gf[J] - GlI);
+        const float cf = fexp2(Gf[J] - GlI);
         XDE += cf * tE;
         XHQ += cf * tQ;
       });
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float fr = exp2f(GI[e] - GfI), fc = exp2f(GlI - GI[e]);
-        XHY[e] *= fr;
-        XDY[e] *= fr;
-        XDE[e] *= fc;
-        XHQ[e] *= fc;
-      }
+      XHY *= fr;
+      XDY *= fr;
+      XDE *= fc;
+      XHQ *= fc;
       // -- diagonal block ------------------------------------------------------------
       if (!wideI) {
-        f32x4 ks, es, qs;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float xm = exp2f(MdI - GI[e]), xp = exp2f(GI[e] - MdI);
-          ks[e] = kI[e] * xm;
-          es[e] = bI[e] * kI[e] * xp;
-          qs[e] = scale * qI[e] * xp;
-        }
+        const f32x4 ks = kI * xm, es = bI * kI * xp, qs = scale * qI * xp;
         f32x4 tH = zero4(), tD = zero4(), tE = zero4(), tQ = zero4();
         mm16_split<T>(tH, HmI, ks);
         mm16_split<T>(tD, DmI, ks);
         mm16_split<T>(tE, DtmI, es);
         mm16_split<T>(tQ, HtmI, qs);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float fr = exp2f(GI[e] - MdI), fc = exp2f(MdI - GI[e]);
-          XHY[e] += fr * tH[e];
-          XDY[e] += fr * tD[e];
-          XDE[e] += fc * tE[e];
-          XHQ[e] += fc * tQ[e];
-        }
+        XHY += xp * tH;
+        XDY += xp * tD;
+        XDE += xm * tE;
+        XHQ += xm * tQ;
       } else {
         // pairwise inside the block: exp2(G_r - G_j) formed per pair, never above 1
         const float* Dd = sDiag;
@@ -413,12 +428,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * q4 + e;
             if (j <= r) {
-              const float x = exp2f(GI[e] - Gj) * kj;
+              const float x = fexp2(GI[e] - Gj) * kj;
               XHY[e] += Hd[r * PD + j] * x;
               XDY[e] += Dd[r * PD + j] * x;
             }
             if (j >= r) {
-              const float x = exp2f(Gj - GI[e]);
+              const float x = fexp2(Gj - GI[e]);
               XDE[e] += Dd[j * PD + r] * bj * kj * x;
               XHQ[e] += Hd[j * PD + r] * scale * qj * x;
             }
@@ -430,16 +445,25 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       for (int e = 0; e < 4; ++e) {
         const int row = I * SUB + 4 * q4 + e;
         if (row < n) {
-          const float gam = exp2f(GI[e]), tail = exp2f(Gn - GI[e]);
+          const float gam = fexp2(GI[e]);
           const float XQ = gam * SQ[e] + XHY[e];
           const float XE = -gam * SE[e] + XDY[e];
-          const float XY = XDE[e] + XHQ[e] + SF[e] * tail;
+          const float XY = XDE[e] + XHQ[e] + SF[e] * tail[e];
           const float kv = kI[e], qv = qI[e], b = bI[e];
-          dqg[row * gsK + kc] = fromf<T>(scale * XQ);
-          dkg[row * gsK + kc] = fromf<T>(b * XE + XY);
+          // dq, dk of an even feature block wait for the next block, so that
+          // both halves of each 64-byte row segment are written together
+          if ((fb & 1) == 0) {
+            pdq[e] = scale * XQ;
+            pdk[e] = b * XE + XY;
+          } else {
+            dqg[row * gsK + kc - SUB] = fromf<T>(pdq[e]);
+            dqg[row * gsK + kc] = fromf<T>(scale * XQ);
+            dkg[row * gsK + kc - SUB] = fromf<T>(pdk[e]);
+            dkg[row * gsK + kc] = fromf<T>(b * XE + XY);
+          }
           gbar[e] = scale * qv * XQ + b * kv * XE - kv * XY;
           dbe[e] += kv * XE;
-          lamw += kv * SF[e] * tail;
+          lamw += kv * SF[e] * tail[e];
         }
       }
       lamw += __shfl_xor(lamw, 16);
@@ -463,7 +487,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         sTot[buf][I * SUB + f] = x;
         sLam[buf][I * SUB + f] = lamw;
       }
-      __syncthreads();
+      lds_barrier();
       if (live) {
         float add = l0;  // endpoint term, added to every row
 #pragma unroll
@@ -532,7 +556,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       sTot[buf][I] = live ? x : 0.f;
       sLam[buf][I] = live ? lamws : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     if (live) {
       float add = lam0s;
       for (int J = 0; J < NSUB; ++J) {

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void k_fwd_out(Args a) {
   g2s<T, CH>(sCq, PA, reinterpret_cast<const T*>(a.Cq) + ((int64_t)c * H + h) * CH * CH, CH, CH,
              CH, tid, 256);
   g2s_T<T, V>(sRt, PA, reinterpret_cast<const T*>(a.R) + (t0 * H + h) * V, gsV, len, CH, tid, 256);
-  __syncthreads();
+  lds_barrier();
   T* og = reinterpret_cast<T*>(a.o) + (t0 * H + h) * V;
   const int w = wave_id();
   for (int cb = w; cb < V / SUB; cb += 4) {

@@ -28,7 +28,7 @@ __global__ void k_chunk_table(Args a) {
     a.seqoff[a.N] = off;
     s_total = min(off, a.nc_max);
   }
-  __syncthreads();
+  __syncthreads();  // full fence: the other threads read seqoff from global memory
   const int total = s_total;
   for (int c = threadIdx.x; c < a.nc_max; c += blockDim.x) {
     ChunkInfo ci = {0, 0, 0, 0};
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
 #pragma unroll
     for (int r = 0; r < RS; ++r) gc.G[r] = gnx.G[r];
     gc.prefix_local(sTot);
-    __syncthreads();
+    lds_barrier();
 
     // ---- S1: finish the prefix, Z^T from the staged v, statistics ------------
     gc.prefix_finish(sTot);
@@ -186,8 +186,10 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     // the staged registers are free: read the next item while this one computes
     const bool more = item + (int)gridDim.x < total;
     if (more) fetch_kqv(item + gridDim.x, tid);
-    subchunk_stats_regs(gc, n, sMid, sGf, sGl, sGn, sFlag);
-    __syncthreads();
+    subchunk_stats_regs(gc, n, sMid, sGf, sGl, sGn, sFlag,
+                        (mode & PREP_BWD_CHUNK) ? reinterpret_cast<f32x4*>(a.Gst) + cb * NSUB * K
+                                                : nullptr);
+    lds_barrier();
 
     // ---- S2: pair factors; element-wise outputs and centred operands --------
     pair_factors<K>(sMid, sGf, sGl, sFlag, sFac, n, tid, NTH);
@@ -219,13 +221,13 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
             const float G = gc.G[r];
             const float kr = tof(sK[row * PK + col]), qr = tof(sQ[row * PK + col]);
             const float b = sBeta[row];
-            const float gam = exp2f(G);
-            const float ea = exp2f(G - ref_recv(sMid, sGf, sFlag, J, K, col));
+            const float gam = fexp2(G);
+            const float ea = fexp2(G - ref_recv(sMid, sGf, sFlag, J, K, col));
             vKa = b * kr * ea;
             vQa = a.scale * qr * ea;
-            vKc = kr * exp2f(ref_send(sMid, sGl, sFlag, J, K, col) - G);
+            vKc = kr * fexp2(ref_send(sMid, sGl, sFlag, J, K, col) - G);
             vE = b * kr * gam;
-            vF = kr * exp2f(gn - G);
+            vF = kr * fexp2(gn - G);
             vQg = a.scale * qr * gam;
             if (mode & PREP_FWD_OUT)
               reinterpret_cast<T*>(a.Qg)[(t0 + row) * gsK + h * K + col] = fromf<T>(vQg);
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     }
     // the gate registers are free: read the next item's gates
     if (more) fetch_g(item + gridDim.x);
-    __syncthreads();
+    lds_barrier();
 
     // ---- S3: score tiles L (strict, fp32 in LDS) and Cq (inclusive, global) --
     {
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         if (mode & PREP_BWD_SCAN) st_tile_T<T>(zero4(), Cqto + (J * SUB) * CH + I * SUB, CH);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- S4: A = (I + L)^-1 in fp32 ------------------------------------------
     solve_unit_lower(sL, sA, PL, sT, n);
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         for (int e = 0; e < 4; ++e) y[e] = (bf16)x[e];
         *reinterpret_cast<bf16x4*>(sAb + i * PA + j) = y;
       }
-      __syncthreads();
+      lds_barrier();
     }
     const T* Aop = BF ? (const T*)sAb : (const T*)sA;
     constexpr int PAo = BF ? PA : PL;
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         }
       }
     }
-    __syncthreads();  // LDS is rewritten by the next item
+    lds_barrier();  // LDS is rewritten by the next item
   }
 }
 

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
         sHt[vv * PK + kk] = x;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // R = U - W S
     T* Rg = reinterpret_cast<T*>(a.R) + (t0 * H + h) * V + vt * BV;
 #pragma unroll
@@ -118,13 +118,13 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
         sRt[col * PA + row] = rv;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // S = diag(exp2 G2_last) S + F^T R
 #pragma unroll
     for (int s = 0; s < S::TPW; ++s) {
       const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[s][i] *= exp2f(sGl[b][tk * SUB + crow(i)]);
+      for (int i = 0; i < 4; ++i) st[s][i] *= fexp2(sGl[b][tk * SUB + crow(i)]);
       mma_tile<T, true, true>(st[s], sFt[b] + tk * SUB * PA, PA, 1, sRt + tv * SUB * PA, PA, 1, CH);
     }
     if (c + 1 < c1) put(b ^ 1);
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
         sDt[vv * PK + kk] = x;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // Rbar = F dS+ + Cq^T dO
     T* Rbt = reinterpret_cast<T*>(a.Rbt) + ((int64_t)c * H + h) * V * CH + vt * BV * CH;
 #pragma unroll
@@ -238,13 +238,13 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
         sRbt[col * PA + row] = fromf<T>(-acc[i]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     // dS = diag(exp2 G2_last) dS+ + Qg^T dO - W^T Rbar
 #pragma unroll
     for (int s = 0; s < S::TPW; ++s) {
       const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[s][i] *= exp2f(sGl[b][tk * SUB + crow(i)]);
+      for (int i = 0; i < 4; ++i) st[s][i] *= fexp2(sGl[b][tk * SUB + crow(i)]);
       mma_tile<T, true, true>(st[s], sQgt[b] + tk * SUB * PA, PA, 1, sdOt[b] + tv * SUB * PA, PA,
                               1, CH);
       mma_tile<T, true, true>(st[s], sWt[b] + tk * SUB * PA, PA, 1, sRbt + tv * SUB * PA, PA, 1,

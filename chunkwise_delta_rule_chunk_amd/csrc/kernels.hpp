@@ -61,6 +61,8 @@ struct Args {
   void* Kt;      // K^T                 [nc,H,K,64]  chunk backward
   void* Qt;      // Q^T                 [nc,H,K,64]  chunk backward
   float* G2t;    // G2^T  [nc,H,K,64] (vector gate) or [nc,H,64] (scalar gate)
+  float* Gst;    // sub-chunk gate statistics [nc,H,4,K] of float4 {G2 at the first row,
+                 // G2 at the last valid row, midpoint (max+min)/2, range max-min}
   // backward intermediates
   void* Rbt;     // correction adjoint Rbar^T [nc,H,V,64] dtype
   void* dhbuf;   // adjoint of the state leaving each chunk [nc,H,K,V] dtype
@@ -69,7 +71,7 @@ struct Args {
 constexpr int PREP_FWD_SCAN = 1;  // W, Ft, U, glast
 constexpr int PREP_FWD_OUT = 2;   // Qg, Cq
 constexpr int PREP_BWD_SCAN = 4;  // F, Wt, Qgt, Cqt, glast
-constexpr int PREP_BWD_CHUNK = 8; // At, Kt, Qt, G2t
+constexpr int PREP_BWD_CHUNK = 8; // At, Kt, Qt, G2t, Gst
 
 // Launchers: enqueue on `stream`; return the hipError_t of the launch.
 hipError_t launch_chunk_table(const Args& a, hipStream_t s);
