@@ -39,11 +39,12 @@ def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy
     st = nc * K * V * esz               # stored per-chunk states
     glast = nc * K * 4
     g2t = {0: 0, 1: nc * 64 * 4, 2: nc * 64 * K * 4}[gate]
+    gst = nc * 4 * K * 16               # sub-chunk gate statistics, float4 per (block, feature)
     prep_in = n * (2 * tk + tv + gb + besz)
     w_fscan = n * (tk + tv) + tileK + glast              # W, U, Ft, glast
     w_fout = n * tk + tile64                              # Qg, Cq
     w_bscan = n * tk + 2 * tileK + tile64                 # F, Wt, Qgt, Cqt
-    w_bchunk = tile64 + 2 * tileK + g2t                   # At, Kt, Qt, G2t
+    w_bchunk = tile64 + 2 * tileK + g2t + gst             # At, Kt, Qt, G2t, Gst
     if policy == "save":
         prep = prep_in + w_fscan + w_fout + w_bscan + w_bchunk
     else:
@@ -53,7 +54,7 @@ def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy
         "k_fwd_scan": n * (tk + tv) + tileK + glast + st + n * tv,
         "k_fwd_out": n * (tk + tv) + st + tile64 + n * tv,
         "k_bwd_scan": n * (tk + tv) + 2 * tileK + tile64 + glast + st + tileV,
-        "k_bwd_chunk": n * 3 * tv + tile64 + tileV + 2 * st + 2 * tileK + g2t + n * besz
+        "k_bwd_chunk": n * 3 * tv + tile64 + tileV + 2 * st + 2 * tileK + g2t + gst + n * besz
                        + n * (2 * tk + tv + gb + besz),
     }
     for name, b in per_head.items():
@@ -62,6 +63,27 @@ def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy
             if name in ("k_fwd_scan", "k_bwd_scan"):
                 extra = nseq * 2 * 4 * K * V  # initial / final state (fp32) per sequence
             return b * H + extra * H
+    return None
+
+
+def measured_traffic(kernel: str, workload: str, policy: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, calibrated on a plain copy), or None
+    when there is no summary for this workload or the library sources changed
+    since the counters were taken."""
+    import re
+    from chunkwise_delta_rule_chunk_amd import build
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_{policy}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"Library source digest: `([0-9a-f]+)`", text)
+    if not m or m.group(1) != build.source_digest():
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 4 and cells[0] == f"`{kernel}`":
+            return float(cells[3])
     return None
 
 
@@ -168,9 +190,12 @@ def main():
     gate = {"none": 0, "scalar": 1, "vector": 2}[inp.gate]
     dbytes = kernel_bytes(dom, chunk_lens, H, K, V, esz, besz, gate, len(seq_lens), args.policy)
     achieved = dbytes / (dom_avg * 1e-3) / 1e9 if dbytes else None
+    short = next((k for k in ("k_fwd_prep", "k_fwd_scan", "k_fwd_out", "k_bwd_scan", "k_bwd_chunk")
+                  if f"{len(k)}{k}I" in dom), dom)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": None if achieved is None else achieved / PEAK_HBM_GBS,
-                "traffic": None, "avg_ms": dom_avg, "launches_per_step": dom_per,
+                "traffic": measured_traffic(short, args.workload, args.policy),
+                "avg_ms": dom_avg, "launches_per_step": dom_per,
                 "algorithmic_bytes_per_launch": dbytes}
     result = {
         "metric": METRIC, "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,

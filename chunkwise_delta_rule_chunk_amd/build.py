@@ -42,6 +42,18 @@ def _digest(src: str) -> str:
     return h.hexdigest()[:16]
 
 
+def source_digest() -> str:
+    """Digest of every library source (kernels, headers, the C header): names
+    the exact code a measurement was taken on."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    h.update(open(os.path.join(INCLUDE, "rewy.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def _compile(name: str, force: bool) -> str:
     src = os.path.join(CSRC, name)
     obj = os.path.join(OBJDIR, f"{name}.{_digest(src)}.o")
