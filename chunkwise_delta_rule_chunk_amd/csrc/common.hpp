@@ -304,6 +304,84 @@ __device__ __forceinline__ void st_beta(void* p, int is_f32, int64_t idx, float 
     reinterpret_cast<bf16*>(p)[idx] = (bf16)v;
 }
 
+// ---- register-fragment products -------------------------------------------
+// Four values along a 16-long contraction held by one lane: the A-operand
+// fragment of row (l & 15) or the B-operand fragment of column (l & 15).
+template <typename T>
+struct Frag4;
+template <>
+struct Frag4<bf16> {
+  using type = bf16x4;
+};
+template <>
+struct Frag4<float> {
+  using type = f32x4;
+};
+
+// acc += A[16 x 16] B[16 x 16] with both operands given as lane fragments: lane
+// l supplies A(l & 15, 4 (l >> 4) + e) and B(4 (l >> 4) + e, l & 15), e = 0..3.
+// fp32 runs four 16x16x4 steps, step e taking contraction slot 4 (l >> 4) + e.
+__device__ __forceinline__ void mm16(f32x4& acc, bf16x4 a, bf16x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mm16(f32x4& acc, f32x4 a, f32x4 b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Frag4<T>::type to_frag(const f32x4& x) {
+  if constexpr (std::is_same_v<T, bf16>) {
+    bf16x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (bf16)x[e];
+    return r;
+  } else {
+    return x;
+  }
+}
+
+// acc += M x (hi + lo) for a sending operand x given in fp32 (bf16: two MFMAs).
+template <typename T>
+__device__ __forceinline__ void mm16_split(f32x4& acc, typename Frag4<T>::type m, const f32x4& x) {
+  if constexpr (std::is_same_v<T, bf16>) {
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = (bf16)x[e];
+      lo[e] = (bf16)(x[e] - (float)hi[e]);
+    }
+    mm16(acc, m, hi);
+    mm16(acc, m, lo);
+  } else {
+    mm16(acc, m, x);
+  }
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).  Every
+// register array below is indexed by such constants only (an index the
+// compiler cannot resolve would move the array to scratch memory).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// arr[I] for a wave-uniform I, by selects
+template <typename X>
+__device__ __forceinline__ X pick(const X (&arr)[NSUB], int I) {
+  X r = arr[0];
+  static_for<1, NSUB>([&](auto J) {
+    if (I == J) r = arr[J];
+  });
+  return r;
+}
+__device__ __forceinline__ float comp(const f32x4& x, int e) {
+  return e == 0 ? x[0] : e == 1 ? x[1] : e == 2 ? x[2] : x[3];
+}
+
 // LDS row pitch (elements) for a row of C elements of type T: +16 bytes of
 // padding keeps 16-byte alignment and spreads rows over the banks.
 template <typename T>

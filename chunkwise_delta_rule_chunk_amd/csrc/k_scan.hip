@@ -29,6 +29,27 @@ struct ScanShape {
   static_assert(TPW >= 1 && RPW >= 1, "tile split");
 };
 
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// exp2 of G2 at the chunk's last row, per key row: the chunk decay Lambda.
+template <int K>
+struct StagedDecay {
+  f32x4 r;
+  __device__ __forceinline__ void load(const float* g, int tid) {
+    r = zero4();
+    if (tid < K / 4) r = reinterpret_cast<const f32x4*>(g)[tid];
+  }
+  __device__ __forceinline__ void store(float* s, int tid) const {
+    if (tid < K / 4) {
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = fexp2(r[e]);
+      reinterpret_cast<f32x4*>(s)[tid] = x;
+    }
+  }
+};
+
 template <typename T, int K, int V, int BV>
 __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
   using S = ScanShape<K, BV>;
@@ -37,9 +58,15 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
   __shared__ __align__(16) T sW[2][CH * PK];
   __shared__ __align__(16) T sFt[2][K * PA];
   __shared__ __align__(16) T sU[2][CH * PU];
-  __shared__ __align__(16) float sGl[2][K];
-  __shared__ __align__(16) T sHt[BV * PK];  // state as operand, [v][k]
-  __shared__ __align__(16) T sRt[BV * PA];  // R as operand, [v][i]
+  __shared__ __align__(16) float sLam[2][K];  // exp2(G2_last)
+  __shared__ __align__(16) T sHt[BV * PK];    // state as operand, [v][k]
+  __shared__ __align__(16) T sRt[BV * PA];    // R as operand, [v][i]
+  // S_c and R_c in natural layout, written to global memory with 16-byte
+  // stores during the next step (few memory instructions per step)
+  __shared__ __align__(16) T sS[2][K * PU];
+  __shared__ __align__(16) T sR[2][CH * PU];
+  __shared__ int sLen[2];
+  __shared__ int64_t sT0[2];
 
   const int H = a.H;
   const int u = blockIdx.x, vt = blockIdx.y;
@@ -51,23 +78,42 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
   const T* Ftg = reinterpret_cast<const T*>(a.Ft);
   const T* Ug = reinterpret_cast<const T*>(a.U);
 
-  Staged<T, CH, K, NTH> pW;
-  Staged<T, K, CH, NTH> pF;
-  Staged<T, CH, BV, NTH> pU;
-  Staged<float, 1, K, NTH> pL;
-  auto fetch = [&](int c) {
+  // two register sets: chunk c + 2 is read while chunk c is processed
+  Staged<T, CH, K, NTH> pW[2];
+  Staged<T, K, CH, NTH> pF[2];
+  Staged<T, CH, BV, NTH> pU[2];
+  StagedDecay<K> pL[2];
+  auto fetch = [&](auto set, int c) {
     const ChunkInfo ci = a.chunks[c];
     const int64_t t0 = ci.bos, cb = (int64_t)c * H + h;
-    pW.load(Wg + (t0 * H + h) * K, gsK, ci.len, tid);
-    pF.load(Ftg + cb * K * CH, CH, K, tid);
-    pU.load(Ug + (t0 * H + h) * V + vt * BV, gsV, ci.len, tid);
-    pL.load(a.glast + cb * K, K, 1, tid);
+    pW[set].load(Wg + (t0 * H + h) * K, gsK, ci.len, tid);
+    pF[set].load(Ftg + cb * K * CH, CH, K, tid);
+    pU[set].load(Ug + (t0 * H + h) * V + vt * BV, gsV, ci.len, tid);
+    pL[set].load(a.glast + cb * K, tid);
   };
-  auto put = [&](int b) {
-    pW.store(sW[b], PK, tid);
-    pF.store(sFt[b], PA, tid);
-    pU.store(sU[b], PU, tid);
-    pL.store(sGl[b], K, tid);
+  auto put = [&](auto set) {
+    pW[set].store(sW[set], PK, tid);
+    pF[set].store(sFt[set], PA, tid);
+    pU[set].store(sU[set], PU, tid);
+    pL[set].store(sLam[set], tid);
+  };
+  // S and R staged in buffer b, to global memory (R rows past the end skipped)
+  auto flush = [&](auto b, int c) {
+    constexpr int VE = 16 / (int)sizeof(T), PER = BV / VE;
+    T* hb = reinterpret_cast<T*>(a.hbuf) + ((int64_t)c * H + h) * K * V + vt * BV;
+    for (int idx = tid; idx < K * PER; idx += NTH) {
+      const int r = idx / PER, c8 = (idx - r * PER) * VE;
+      *reinterpret_cast<uint4*>(hb + (int64_t)r * V + c8) =
+          *reinterpret_cast<const uint4*>(sS[b] + r * PU + c8);
+    }
+    const int len = sLen[b];
+    T* Rg = reinterpret_cast<T*>(a.R) + (sT0[b] * H + h) * V + vt * BV;
+    for (int idx = tid; idx < CH * PER; idx += NTH) {
+      const int r = idx / PER, c8 = (idx - r * PER) * VE;
+      if (r < len)
+        *reinterpret_cast<uint4*>(Rg + (int64_t)r * gsV + c8) =
+            *reinterpret_cast<const uint4*>(sR[b] + r * PU + c8);
+    }
   };
 
   f32x4 st[S::TPW];
@@ -81,42 +127,49 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
     }
   }
   if (c0 < c1) {
-    fetch(c0);
-    put(0);
+    fetch(ic<0>{}, c0);
+    if (c0 + 1 < c1) fetch(ic<1>{}, c0 + 1);
+    put(ic<0>{});
   }
-  for (int c = c0; c < c1; ++c) {
-    const int b = (c - c0) & 1;
-    const ChunkInfo ci = a.chunks[c];
-    const int len = ci.len;
-    const int64_t t0 = ci.bos;
-    if (c + 1 < c1) fetch(c + 1);
-    T* hb = reinterpret_cast<T*>(a.hbuf) + ((int64_t)c * H + h) * K * V + vt * BV;
+  lds_barrier();
+
+  auto step = [&](auto buf, int c) {
+    constexpr int B = decltype(buf)::value;
+    if (c + 2 < c1) fetch(ic<B>{}, c + 2);
+    if (c > c0) flush(ic<B ^ 1>{}, c - 1);
+    // S_c: staged for global memory, and as the operand of W S
 #pragma unroll
     for (int s = 0; s < S::TPW; ++s) {
       const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
+      f32x4 x;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kk = tk * SUB + crow(i), vv = tv * SUB + ccol();
-        const T x = fromf<T>(st[s][i]);
-        hb[(int64_t)kk * V + vv] = x;
-        sHt[vv * PK + kk] = x;
+        x[i] = tof(fromf<T>(st[s][i]));
+        sS[B][(tk * SUB + crow(i)) * PU + tv * SUB + ccol()] = fromf<T>(st[s][i]);
       }
+      st_tile_T<T>(x, sHt + (tv * SUB) * PK + tk * SUB, PK);
+    }
+    if (tid == 0) {
+      const ChunkInfo ci = a.chunks[c];
+      sLen[B] = ci.len;
+      sT0[B] = ci.bos;
     }
     lds_barrier();
     // R = U - W S
-    T* Rg = reinterpret_cast<T*>(a.R) + (t0 * H + h) * V + vt * BV;
 #pragma unroll
     for (int r = 0; r < S::RPW; ++r) {
       const int t = w + 4 * r, ti = t / CT, tv = t - ti * CT;
       f32x4 p = zero4();
-      mma_tile<T, true, true>(p, sW[b] + ti * SUB * PK, PK, 1, sHt + tv * SUB * PK, PK, 1, K);
+      mma_tile<T, true, true>(p, sW[B] + ti * SUB * PK, PK, 1, sHt + tv * SUB * PK, PK, 1, K);
+      f32x4 rv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = ti * SUB + crow(i), col = tv * SUB + ccol();
-        const T rv = fromf<T>(tof(sU[b][row * PU + col]) - p[i]);
-        if (row < len) Rg[row * gsV + col] = rv;
-        sRt[col * PA + row] = rv;
+        const T x = fromf<T>(tof(sU[B][row * PU + col]) - p[i]);
+        sR[B][row * PU + col] = x;
+        rv[i] = tof(x);
       }
+      st_tile_T<T>(rv, sRt + (tv * SUB) * PA + ti * SUB, PA);
     }
     lds_barrier();
     // S = diag(exp2 G2_last) S + F^T R
@@ -124,10 +177,19 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
     for (int s = 0; s < S::TPW; ++s) {
       const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[s][i] *= fexp2(sGl[b][tk * SUB + crow(i)]);
-      mma_tile<T, true, true>(st[s], sFt[b] + tk * SUB * PA, PA, 1, sRt + tv * SUB * PA, PA, 1, CH);
+      for (int i = 0; i < 4; ++i) st[s][i] *= sLam[B][tk * SUB + crow(i)];
+      mma_tile<T, true, true>(st[s], sFt[B] + tk * SUB * PA, PA, 1, sRt + tv * SUB * PA, PA, 1, CH);
     }
-    if (c + 1 < c1) put(b ^ 1);
+    if (c + 1 < c1) put(ic<B ^ 1>{});  // chunk c + 1; its buffer was last read a step ago
+  };
+  for (int c = c0; c < c1; c += 2) {
+    step(ic<0>{}, c);
+    if (c + 1 < c1) step(ic<1>{}, c + 1);
+  }
+  lds_barrier();
+  if (c1 > c0) {  // the last chunk's S and R
+    if ((c1 - 1 - c0) & 1) flush(ic<1>{}, c1 - 1);
+    else flush(ic<0>{}, c1 - 1);
   }
   if (a.ht) {
 #pragma unroll
@@ -146,15 +208,18 @@ template <typename T, int K, int V, int BV>
 __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
   using S = ScanShape<K, BV>;
   constexpr int CT = S::CT, NTH = 256;
-  constexpr int PK = pitch<T>(K), PA = pitch<T>(CH);
-  __shared__ __align__(16) T sF[2][CH * PK];
-  __shared__ __align__(16) T sWt[2][K * PA];
-  __shared__ __align__(16) T sQgt[2][K * PA];
-  __shared__ __align__(16) T sCqt[2][CH * PA];
-  __shared__ __align__(16) T sdOt[2][BV * PA];  // dO as operand, [v][j]
-  __shared__ __align__(16) float sGl[2][K];
-  __shared__ __align__(16) T sDt[BV * PK];      // dS_{c+1} as operand, [v][k]
-  __shared__ __align__(16) T sRbt[BV * PA];     // -Rbar as operand, [v][i]
+  constexpr int PK = pitch<T>(K), PA = pitch<T>(CH), PS = pitch<T>(BV);
+  // one buffer of chunk operands, refilled between two barriers
+  __shared__ __align__(16) T sF[CH * PK];
+  __shared__ __align__(16) T sWt[K * PA];
+  __shared__ __align__(16) T sQgt[K * PA];
+  __shared__ __align__(16) T sCqt[CH * PA];
+  __shared__ __align__(16) T sdOt[BV * PA];   // dO as operand, [v][j]
+  __shared__ __align__(16) float sLam[K];     // exp2(G2_last)
+  __shared__ __align__(16) T sDt[BV * PK];    // dS_{c+1} as operand, [v][k]
+  __shared__ __align__(16) T sRbt[BV * PA];   // -Rbar as operand, [v][i]
+  // dS_{c+1} in natural layout, written to global memory during the next step
+  __shared__ __align__(16) T sD[2][K * PS];
 
   const int H = a.H;
   const int u = blockIdx.x, vt = blockIdx.y;
@@ -163,29 +228,39 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
   const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
   const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
 
-  Staged<T, CH, K, NTH> pF;
-  Staged<T, K, CH, NTH> pW;
-  Staged<T, K, CH, NTH> pQ;
-  Staged<T, CH, CH, NTH> pC;
-  Staged<T, CH, BV, NTH> pO;
-  Staged<float, 1, K, NTH> pL;
-  auto fetch = [&](int c) {
+  // two register sets: chunk c - 2 is read while chunk c is processed
+  Staged<T, CH, K, NTH> pF[2];
+  Staged<T, K, CH, NTH> pW[2];
+  Staged<T, K, CH, NTH> pQ[2];
+  Staged<T, CH, CH, NTH> pC[2];
+  Staged<T, CH, BV, NTH> pO[2];
+  StagedDecay<K> pL[2];
+  auto fetch = [&](auto set, int c) {
     const ChunkInfo ci = a.chunks[c];
     const int64_t t0 = ci.bos, cb = (int64_t)c * H + h;
-    pF.load(reinterpret_cast<const T*>(a.F) + (t0 * H + h) * K, gsK, ci.len, tid);
-    pW.load(reinterpret_cast<const T*>(a.Wt) + cb * K * CH, CH, K, tid);
-    pQ.load(reinterpret_cast<const T*>(a.Qgt) + cb * K * CH, CH, K, tid);
-    pC.load(reinterpret_cast<const T*>(a.Cqt) + cb * CH * CH, CH, CH, tid);
-    pO.load(reinterpret_cast<const T*>(a.dO) + (t0 * H + h) * V + vt * BV, gsV, ci.len, tid);
-    pL.load(a.glast + cb * K, K, 1, tid);
+    pF[set].load(reinterpret_cast<const T*>(a.F) + (t0 * H + h) * K, gsK, ci.len, tid);
+    pW[set].load(reinterpret_cast<const T*>(a.Wt) + cb * K * CH, CH, K, tid);
+    pQ[set].load(reinterpret_cast<const T*>(a.Qgt) + cb * K * CH, CH, K, tid);
+    pC[set].load(reinterpret_cast<const T*>(a.Cqt) + cb * CH * CH, CH, CH, tid);
+    pO[set].load(reinterpret_cast<const T*>(a.dO) + (t0 * H + h) * V + vt * BV, gsV, ci.len, tid);
+    pL[set].load(a.glast + cb * K, tid);
   };
-  auto put = [&](int b) {
-    pF.store(sF[b], PK, tid);
-    pW.store(sWt[b], PA, tid);
-    pQ.store(sQgt[b], PA, tid);
-    pC.store(sCqt[b], PA, tid);
-    pO.store_T(sdOt[b], PA, tid);
-    pL.store(sGl[b], K, tid);
+  auto put = [&](auto set) {
+    pF[set].store(sF, PK, tid);
+    pW[set].store(sWt, PA, tid);
+    pQ[set].store(sQgt, PA, tid);
+    pC[set].store(sCqt, PA, tid);
+    pO[set].store_T(sdOt, PA, tid);
+    pL[set].store(sLam, tid);
+  };
+  auto flush = [&](auto b, int c) {
+    constexpr int VE = 16 / (int)sizeof(T), PER = BV / VE;
+    T* db = reinterpret_cast<T*>(a.dhbuf) + ((int64_t)c * H + h) * K * V + vt * BV;
+    for (int idx = tid; idx < K * PER; idx += NTH) {
+      const int r = idx / PER, c8 = (idx - r * PER) * VE;
+      *reinterpret_cast<uint4*>(db + (int64_t)r * V + c8) =
+          *reinterpret_cast<const uint4*>(sD[b] + r * PS + c8);
+    }
   };
 
   f32x4 st[S::TPW];
@@ -199,44 +274,41 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
     }
   }
   if (c0 < c1) {
-    fetch(c1 - 1);
-    put(0);
+    fetch(ic<0>{}, c1 - 1);
+    if (c1 - 2 >= c0) fetch(ic<1>{}, c1 - 2);
+    put(ic<0>{});
   }
-  for (int c = c1 - 1; c >= c0; --c) {
-    const int b = (c1 - 1 - c) & 1;
+
+  auto step = [&](auto buf, int c) {
+    constexpr int B = decltype(buf)::value;
+    if (c - 2 >= c0) fetch(ic<B>{}, c - 2);
+    if (c < c1 - 1) flush(ic<B ^ 1>{}, c + 1);  // dS_{c+2}, staged last step
     const ChunkInfo ci = a.chunks[c];
-    const int len = ci.len;
     const int64_t t0 = ci.bos;
-    if (c - 1 >= c0) fetch(c - 1);
-    T* db = reinterpret_cast<T*>(a.dhbuf) + ((int64_t)c * H + h) * K * V + vt * BV;
+    // dS_{c+1}: staged for global memory, and as the operand of F dS+
 #pragma unroll
     for (int s = 0; s < S::TPW; ++s) {
       const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
+      f32x4 x;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kk = tk * SUB + crow(i), vv = tv * SUB + ccol();
-        const T x = fromf<T>(st[s][i]);
-        db[(int64_t)kk * V + vv] = x;
-        sDt[vv * PK + kk] = x;
+        x[i] = tof(fromf<T>(st[s][i]));
+        sD[B][(tk * SUB + crow(i)) * PS + tv * SUB + ccol()] = fromf<T>(st[s][i]);
       }
+      st_tile_T<T>(x, sDt + (tv * SUB) * PK + tk * SUB, PK);
     }
-    lds_barrier();
-    // Rbar = F dS+ + Cq^T dO
+    lds_barrier();  // operands of chunk c and dS_{c+1} visible
+    // Rbar = F dS+ + Cq^T dO, stored token-contiguous
     T* Rbt = reinterpret_cast<T*>(a.Rbt) + ((int64_t)c * H + h) * V * CH + vt * BV * CH;
 #pragma unroll
     for (int r = 0; r < S::RPW; ++r) {
       const int t = w + 4 * r, ti = t / CT, tv = t - ti * CT;
       f32x4 acc = zero4();
-      mma_tile<T, true, true>(acc, sF[b] + ti * SUB * PK, PK, 1, sDt + tv * SUB * PK, PK, 1, K);
-      mma_tile<T, true, true>(acc, sCqt[b] + ti * SUB * PA, PA, 1, sdOt[b] + tv * SUB * PA, PA, 1,
-                              CH);
+      mma_tile<T, true, true>(acc, sF + ti * SUB * PK, PK, 1, sDt + tv * SUB * PK, PK, 1, K);
+      mma_tile<T, true, true>(acc, sCqt + ti * SUB * PA, PA, 1, sdOt + tv * SUB * PA, PA, 1, CH);
       // rows past the chunk's end are exact zeros (F and Cq vanish there)
       st_tile_T<T>(acc, Rbt + (tv * SUB) * CH + ti * SUB, CH);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = ti * SUB + crow(i), col = tv * SUB + ccol();
-        sRbt[col * PA + row] = fromf<T>(-acc[i]);
-      }
+      st_tile_T<T>(-acc, sRbt + (tv * SUB) * PA + ti * SUB, PA);
     }
     lds_barrier();
     // dS = diag(exp2 G2_last) dS+ + Qg^T dO - W^T Rbar
@@ -244,13 +316,24 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
     for (int s = 0; s < S::TPW; ++s) {
       const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[s][i] *= fexp2(sGl[b][tk * SUB + crow(i)]);
-      mma_tile<T, true, true>(st[s], sQgt[b] + tk * SUB * PA, PA, 1, sdOt[b] + tv * SUB * PA, PA,
-                              1, CH);
-      mma_tile<T, true, true>(st[s], sWt[b] + tk * SUB * PA, PA, 1, sRbt + tv * SUB * PA, PA, 1,
-                              CH);
+      for (int i = 0; i < 4; ++i) st[s][i] *= sLam[tk * SUB + crow(i)];
+      mma_tile<T, true, true>(st[s], sQgt + tk * SUB * PA, PA, 1, sdOt + tv * SUB * PA, PA, 1, CH);
+      mma_tile<T, true, true>(st[s], sWt + tk * SUB * PA, PA, 1, sRbt + tv * SUB * PA, PA, 1, CH);
     }
-    if (c - 1 >= c0) put(b ^ 1);
+    (void)t0;
+    if (c - 1 >= c0) {
+      lds_barrier();  // every wave is done with chunk c's operands
+      put(ic<B ^ 1>{});
+    }
+  };
+  for (int c = c1 - 1; c >= c0; c -= 2) {
+    step(ic<0>{}, c);
+    if (c - 1 >= c0) step(ic<1>{}, c - 1);
+  }
+  lds_barrier();
+  if (c1 > c0) {  // dS_{c0+1}, staged by the last step
+    if ((c1 - 1 - c0) & 1) flush(ic<1>{}, c0);
+    else flush(ic<0>{}, c0);
   }
   if (a.dh0) {
 #pragma unroll
