@@ -25,9 +25,9 @@ __device__ __forceinline__ void pair_ij(int p, int& I, int& J) {
 // forward substitution (one lane per column), then the off-diagonal blocks are
 // merged in order of distance from the diagonal,
 //   A_IJ = -A_II * sum_{m=J}^{I-1} L_Im A_mJ,
-// with fp32 MFMA.  sT: 4 x 16 x 20 fp32 scratch.  Called by all four waves.
-__device__ __forceinline__ void solve_unit_lower(const float* sL, float* sA, int PL, float* sT,
-                                                 int n) {
+// with fp32 MFMA.  Called by every wave of the workgroup (waves 0 .. 2 do the
+// merges).
+__device__ __forceinline__ void solve_unit_lower(const float* sL, float* sA, int PL, int n) {
   const int w = wave_id(), l = lane_id();
   if (w == 0) {
     const int b = l >> 4, cc = l & 15;
@@ -35,36 +35,37 @@ __device__ __forceinline__ void solve_unit_lower(const float* sL, float* sA, int
     float x[SUB];
 #pragma unroll
     for (int i = 0; i < SUB; ++i) x[i] = (i == cc) ? 1.f : 0.f;
+    // column-oriented substitution: once x[m] is final, its term leaves every
+    // later row at once (15 dependent steps instead of a chain per row)
 #pragma unroll
-    for (int i = 1; i < SUB; ++i) {
-      float s = 0.f;
+    for (int m = 0; m < SUB - 1; ++m)
 #pragma unroll
-      for (int m = 0; m < i; ++m) s += Lb[i * PL + m] * x[m];
-      if (i > cc) x[i] = -s;
-    }
+      for (int i = m + 1; i < SUB; ++i) x[i] -= Lb[i * PL + m] * x[m];
     float* Ab = sA + (b * SUB) * PL + b * SUB;
 #pragma unroll
     for (int i = 0; i < SUB; ++i) Ab[i * PL + cc] = x[i];
   }
   lds_barrier();
-  for (int d = 1; d < NSUB; ++d) {
+  // distance d is a compile-time constant, so each product's operand reads
+  // are issued together ahead of its MFMA chain.  The inner sum stays in
+  // registers: its C fragment (lane l: rows 4 (l >> 4) .. +3 of column l & 15)
+  // is the B operand of the outer product with A_II.
+  static_for<1, NSUB>([&](auto dd) {
+    constexpr int d = decltype(dd)::value;
     const int I = w + d, J = w;
-    const bool act = (w < NSUB - d) && (I * SUB < n);
-    float* Ts = sT + w * SUB * 20;
-    if (act) {
+    if ((w < NSUB - d) && (I * SUB < n)) {
       f32x4 t = zero4();
       mma_tile<float, false, false>(t, sL + (I * SUB) * PL + J * SUB, PL, 1,
                                     sA + (J * SUB) * PL + J * SUB, 1, PL, SUB * d);
-      st_tile<float>(t, Ts, 20, 1);
+      const int l = lane_id();
+      const f32x4 aII =
+          *reinterpret_cast<const f32x4*>(sA + (I * SUB + (l & 15)) * PL + I * SUB + 4 * (l >> 4));
+      f32x4 r = zero4();
+      mm16(r, aII, t);
+      st_tile<float>(-r, sA + (I * SUB) * PL + J * SUB, PL, 1);
     }
     lds_barrier();
-    if (act) {
-      f32x4 t = zero4();
-      mma_tile<float, false, false>(t, sA + (I * SUB) * PL + I * SUB, PL, 1, Ts, 1, 20, SUB);
-      st_tile<float>(-t, sA + (I * SUB) * PL + J * SUB, PL, 1);
-    }
-    lds_barrier();
-  }
+  });
 }
 
 constexpr int cmax(int x, int y) { return x > y ? x : y; }

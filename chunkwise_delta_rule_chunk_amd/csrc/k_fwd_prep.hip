@@ -82,7 +82,6 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
   __shared__ float sTot[NSUB * K];
   __shared__ float sMid[NSUB * K], sGf[NSUB * K], sGl[NSUB * K], sGn[K];
   __shared__ float sBeta[CH];
-  __shared__ float sT[4 * SUB * 20];
   __shared__ int sFlag[NSUB];
 
   const int H = a.H, mode = a.prep_mode;
@@ -199,6 +198,9 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       int col = gc.c, r0 = gc.seg * RS;
       asm volatile("" : "+v"(col), "+v"(r0));
       const float gn = sGn[col];
+      // the thread's 16 rows lie in sub-chunk seg: its references are per thread
+      const float rA = ref_recv(sMid, sGf, sFlag, gc.seg, K, col);
+      const float rB = ref_send(sMid, sGl, sFlag, gc.seg, K, col);
       constexpr int VE = 16 / (int)sizeof(T);
       T* Ftd = reinterpret_cast<T*>(a.Ft) + (cb * K + col) * CH + r0;
       T* Qgtd = reinterpret_cast<T*>(a.Qgt) + (cb * K + col) * CH + r0;
@@ -217,15 +219,14 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
           kt.e[e] = sK[row * PK + col];  // raw k and q (zero past the chunk's end)
           qq.e[e] = sQ[row * PK + col];
           if (row < n) {
-            const int J = row / SUB;
             const float G = gc.G[r];
             const float kr = tof(sK[row * PK + col]), qr = tof(sQ[row * PK + col]);
             const float b = sBeta[row];
             const float gam = fexp2(G);
-            const float ea = fexp2(G - ref_recv(sMid, sGf, sFlag, J, K, col));
+            const float ea = fexp2(G - rA);
             vKa = b * kr * ea;
             vQa = a.scale * qr * ea;
-            vKc = kr * fexp2(ref_send(sMid, sGl, sFlag, J, K, col) - G);
+            vKc = kr * fexp2(rB - G);
             vE = b * kr * gam;
             vF = kr * fexp2(gn - G);
             vQg = a.scale * qr * gam;
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     lds_barrier();
 
     // ---- S4: A = (I + L)^-1 in fp32 ------------------------------------------
-    solve_unit_lower(sL, sA, PL, sT, n);
+    solve_unit_lower(sL, sA, PL, n);
     if (mode & PREP_BWD_CHUNK) {  // A^T for the chunk backward, 16-byte rows
       constexpr int VA = 16 / (int)sizeof(T), PER = CH / VA;
       T* Ato = reinterpret_cast<T*>(a.At) + cb * CH * CH;
@@ -333,6 +334,12 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       }
       lds_barrier();
     }
+    // staging of W and U: the score operands in sKa and the fp32 L in sL are
+    // dead once A is formed (64 x pitch(V) elements of T fit in sL's bytes)
+    T* sWs = sKa;
+    T* sUs = reinterpret_cast<T*>(sL);
+    constexpr int PUs = pitch<T>(V);
+    static_assert(CH * PUs * sizeof(T) <= CH * PL * sizeof(float), "U staging fits in sL");
     const T* Aop = BF ? (const T*)sAb : (const T*)sA;
     constexpr int PAo = BF ? PA : PL;
     const int NCB = (K + (wantU ? V : 0)) / SUB;
@@ -341,16 +348,35 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       if (isW && !wantW && !wantWt) continue;
       const int col = isW ? cbk * SUB : (cbk - K / SUB) * SUB;
       const T* Bop = (isW ? sEt : sZt) + col * PA;
-      for (int I = 0; I < (isW ? nblkW : nblk); ++I) {
+      const int nI = isW ? nblkW : nblk;
+      static_for<0, NSUB>([&](auto II) {
+        constexpr int I = decltype(II)::value;
+        if (I >= nI) return;
         f32x4 acc = zero4();
-        const int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
+        // A is lower triangular: row block I needs tokens < 16 (I + 1) only
+        constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
         mma_tile<T, true, true>(acc, Aop + (I * SUB) * PAo, PAo, 1, Bop, PA, 1, kd);
         if (isW) {
-          if (wantW) st_tile<T>(acc, Wo + (I * SUB) * gsK + col, (int)gsK, 1, n - I * SUB);
+          if (wantW) st_tile<T>(acc, sWs + (I * SUB) * PK + col, PK, 1);
           if (wantWt) st_tile_T<T>(acc, Wto + (int64_t)col * CH + I * SUB, CH);
         } else {
-          st_tile<T>(acc, Uo + (I * SUB) * gsV + col, (int)gsV, 1, n - I * SUB);
+          st_tile<T>(acc, sUs + (I * SUB) * PUs + col, PUs, 1);
         }
+      });
+    }
+    // W and U leave through LDS as whole 16-byte row pieces: rows written from
+    // sixteen-column tiles by different waves would otherwise reach memory as
+    // partial lines
+    if (wantW) {
+      lds_barrier();
+      constexpr int VE = 16 / (int)sizeof(T);
+      for (int idx = tid; idx < n * (K / VE); idx += NTH) {
+        const int r = idx / (K / VE), c8 = (idx - r * (K / VE)) * VE;
+        *reinterpret_cast<uint4*>(Wo + r * gsK + c8) = *reinterpret_cast<const uint4*>(sWs + r * PK + c8);
+      }
+      for (int idx = tid; idx < n * (V / VE); idx += NTH) {
+        const int r = idx / (V / VE), c8 = (idx - r * (V / VE)) * VE;
+        *reinterpret_cast<uint4*>(Uo + r * gsV + c8) = *reinterpret_cast<const uint4*>(sUs + r * PUs + c8);
       }
     }
     lds_barrier();  // LDS is rewritten by the next item
