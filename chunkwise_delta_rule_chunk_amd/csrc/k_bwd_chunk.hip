@@ -55,6 +55,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   __shared__ __align__(16) float sBeta[CH];
   __shared__ float sDbw[CH];
   __shared__ float sTot[2][NSUB * SUB], sLam[2][NSUB * SUB];  // per feature block, two buffers
+  // One 16-feature block of per-feature operands, loaded once per workgroup
+  // (every wave needs all of it): G2 [feature][token] (row 0 for a scalar
+  // gate), K^T and Q^T [feature][token], the sub-chunk statistics [J][feature],
+  // the state and state-adjoint rows [feature][v], and G2 at the last row.
+  constexpr int PGS = CH + 4, PKS = pitch<T>(CH), PSS = pitch<T>(V);
+  __shared__ __align__(16) float sG2[SUB * PGS];
+  __shared__ __align__(16) T sKs[SUB * PKS];
+  __shared__ __align__(16) T sQs[SUB * PKS];
+  __shared__ __align__(16) float sSt[NSUB * SUB * 4];
+  __shared__ __align__(16) T sSs[SUB * PSS];
+  __shared__ __align__(16) T sDs[SUB * PSS];
+  __shared__ __align__(16) float sGn[SUB];
 
   const int H = a.H;
   const int c = blockIdx.x / H, h = blockIdx.x - c * H;
@@ -195,56 +207,89 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   T* dkg = reinterpret_cast<T*>(a.dk) + (t0 * H + h) * K;
   const int jl = n - 1;  // last valid row
   const FR DmI = pick(Dm, I), HmI = pick(Hm, I), DtmI = pick(Dtm, I), HtmI = pick(Htm, I);
-  f32x4 beta_r[NSUB];
-  static_for<0, NSUB>([&](auto J) {
-    beta_r[J] = *reinterpret_cast<const f32x4*>(sBeta + J * SUB + 4 * q4);
-  });
-  const f32x4 bI = pick(beta_r, I);
+  const f32x4 bI = *reinterpret_cast<const f32x4*>(sBeta + I * SUB + 4 * q4);
   f32x4 sufs = zero4();  // scalar gate: Gbar summed over features, this lane's rows
   float dbe[4] = {0.f, 0.f, 0.f, 0.f};
   float pdq[4] = {0.f, 0.f, 0.f, 0.f}, pdk[4] = {0.f, 0.f, 0.f, 0.f};
   float lam0s = 0.f, lamws = 0.f;
 
+  // registers of the next block's operands (loaded during this block's products)
+  Staged<float, SUB, CH, NTH> pG;
+  Staged<T, SUB, CH, NTH> pK, pQ;
+  Staged<float, NSUB, SUB * 4, NTH> pX;
+  Staged<T, SUB, V, NTH> pS, pD;
+  Staged<float, 1, SUB, NTH> pN;
+  auto fetch_fb = [&](int fb) {
+    if (a.gate == 2) pG.load(a.G2t + (cb * K + fb * SUB) * CH, CH, SUB, tid);
+    else if (a.gate == 1) pG.load(a.G2t + cb * CH, CH, 1, tid);
+    pK.load(Ktg + (int64_t)fb * SUB * CH, CH, SUB, tid);
+    pQ.load(Qtg + (int64_t)fb * SUB * CH, CH, SUB, tid);
+    pX.load(Gstg + fb * SUB * 4, K * 4, NSUB, tid);
+    pS.load(hb + (int64_t)fb * SUB * V, V, SUB, tid);
+    pD.load(dhb + (int64_t)fb * SUB * V, V, SUB, tid);
+    pN.load(a.glast + cb * K + fb * SUB, SUB, 1, tid);
+  };
+  auto put_fb = [&]() {
+    if (a.gate != 0) pG.store(sG2, PGS, tid);
+    pK.store(sKs, PKS, tid);
+    pQ.store(sQs, PKS, tid);
+    pX.store(sSt, SUB * 4, tid);
+    pS.store(sSs, PSS, tid);
+    pD.store(sDs, PSS, tid);
+    pN.store(sGn, SUB, tid);
+  };
+  fetch_fb(0);
+  put_fb();
+  lds_barrier();
+
 #pragma unroll 1
   for (int fb = 0; fb < NFB; ++fb) {
     const int kc = fb * SUB + f;  // this lane's feature
     const int buf = fb & 1;
+    if (fb + 1 < NFB) fetch_fb(fb + 1);
+    // first row of this lane, opaque per iteration: the output addresses derived
+    // from it are recomputed rather than kept live (and spilled) across blocks
+    int lrow = I * SUB + 4 * q4;
+    asm volatile("" : "+v"(lrow));
     f32x4 gbar = zero4();
     float lamw = 0.f, l0 = 0.f;
     if (live) {
       // gated operands of all four blocks at this lane's rows 16 J + 4 q4 + e
-      f32x4 G[NSUB], kx[NSUB], qx[NSUB];
+      // (k and q stay packed in their storage type until used)
+      f32x4 G[NSUB];
+      FR kp[NSUB], qp[NSUB];
       static_for<0, NSUB>([&](auto J) {
         const int r0 = J * SUB + 4 * q4;
         if (a.gate == 2)
-          G[J] = *reinterpret_cast<const f32x4*>(a.G2t + (cb * K + kc) * CH + r0);
+          G[J] = *reinterpret_cast<const f32x4*>(sG2 + f * PGS + r0);
         else if (a.gate == 1)
-          G[J] = *reinterpret_cast<const f32x4*>(a.G2t + cb * CH + r0);
+          G[J] = *reinterpret_cast<const f32x4*>(sG2 + r0);
         else
           G[J] = zero4();
-        const FR kf = *reinterpret_cast<const FR*>(Ktg + (int64_t)kc * CH + r0);
-        const FR qf = *reinterpret_cast<const FR*>(Qtg + (int64_t)kc * CH + r0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kx[J][e] = tof(kf[e]);
-          qx[J][e] = tof(qf[e]);
-        }
+        kp[J] = *reinterpret_cast<const FR*>(sKs + f * PKS + r0);
+        qp[J] = *reinterpret_cast<const FR*>(sQs + f * PKS + r0);
       });
+      auto unpack = [](const FR& x) {
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = tof(x[e]);
+        return r;
+      };
       // sub-chunk statistics of this feature (written by the forward prep):
       // G2 at the first and last valid row, midpoint, range; only blocks with
-      // valid rows are read
+      // valid rows are used
       float Gf[NSUB], Gl[NSUB], Md[NSUB];
       bool wide[NSUB];
       static_for<0, NSUB>([&](auto J) {
         f32x4 st = zero4();
-        if (J * SUB < n) st = reinterpret_cast<const f32x4*>(Gstg)[J * K + kc];
+        if (J * SUB < n) st = *reinterpret_cast<const f32x4*>(sSt + (J * SUB + f) * 4);
         Gf[J] = st[0];
         Gl[J] = st[1];
         Md[J] = st[2];
         wide[J] = __any(st[3] > CENTRE_MAX_RANGE);
       });
-      const float Gn = a.glast[cb * K + kc];
-      const f32x4 GI = pick(G, I), kI = pick(kx, I), qI = pick(qx, I);
+      const float Gn = sGn[f];
+      const f32x4 GI = pick(G, I), kI = unpack(pick(kp, I)), qI = unpack(pick(qp, I));
       const float GfI = pick(Gf, I), GlI = pick(Gl, I), MdI = pick(Md, I);
       const bool wideI = pick(wide, I);
       // Row factors of block I.  Centred block: xp = exp2(G - Md), xm = exp2(Md - G)
@@ -275,12 +320,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       // the diagonal of S_fb dS+_fb^T, one more MFMA on the same fragments
       f32x4 SQ = zero4(), SE = zero4(), SF = zero4(), SS = zero4();
       {
-        const T* hr = hb + (int64_t)(fb * SUB) * V;
-        const T* dr = dhb + (int64_t)(fb * SUB) * V;
 #pragma unroll
         for (int k0 = 0; k0 < V; k0 += KS) {
-          const auto sf = ldfrag<T, true>(hr, V, 1, k0);
-          const auto df = ldfrag<T, true>(dr, V, 1, k0);
+          const auto sf = ldfrag<T, true>(sSs, PSS, 1, k0);
+          const auto df = ldfrag<T, true>(sDs, PSS, 1, k0);
           SS = mma(sf, df, SS);
           SQ = mma(ldfrag<T, true>(sO + I * SUB * PV, PV, 1, k0), sf, SQ);
           SE = mma(ldfrag<T, true>(sP + I * SUB * PV, PV, 1, k0), sf, SE);
@@ -294,8 +337,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       static_for<0, NSUB - 1>([&](auto J) {
         if (J >= I) return;
         f32x4 ks;
+        const f32x4 kJ = unpack(kp[J]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ks[e] = kx[J][e] * fexp2(Gl[J] - G[J][e]);
+        for (int e = 0; e < 4; ++e) ks[e] = kJ[e] * fexp2(Gl[J] - G[J][e]);
         f32x4 tH = zero4(), tD = zero4();
         mm16_split<T>(tH, Hm[J], ks);
         mm16_split<T>(tD, Dm[J], ks);
@@ -307,11 +351,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       static_for<1, NSUB>([&](auto J) {
         if (J <= I || J * SUB >= n) return;
         f32x4 es, qs;
+        const f32x4 kJ = unpack(kp[J]), qJ = unpack(qp[J]);
+        const f32x4 bJ = *reinterpret_cast<const f32x4*>(sBeta + J * SUB + 4 * q4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = fexp2(G[J][e] - Gf[J]);
-          es[e] = beta_r[J][e] * kx[J][e] * x;
-          qs[e] = scale * qx[J][e] * x;
+          es[e] = bJ[e] * kJ[e] * x;
+          qs[e] = scale * qJ[e] * x;
         }
         f32x4 tE = zero4(), tQ = zero4();
         mm16_split<T>(tE, Dtm[J], es);
@@ -366,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       // -- chain rules ---------------------------------------------------------------
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = I * SUB + 4 * q4 + e;
+        const int row = lrow + e;
         if (row < n) {
           const float gam = fexp2(GI[e]);
           const float XQ = gam * SQ[e] + XHY[e];
@@ -410,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         sTot[buf][I * SUB + f] = x;
         sLam[buf][I * SUB + f] = lamw;
       }
-      lds_barrier();
+      lds_barrier();  // block totals visible; this block's operands are no longer read
       if (live) {
         float add = l0;  // endpoint term, added to every row
 #pragma unroll
@@ -420,7 +466,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = I * SUB + 4 * q4 + e;
+          const int row = lrow + e;
           if (row < n) a.dg[((t0 + row) * H + h) * K + kc] = suf[e] + add;
         }
       }
@@ -446,6 +492,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       lamws += x;
       lam0s += y;
     }
+    if (a.gate != 2) lds_barrier();  // this block's operands are no longer read
+    if (fb + 1 < NFB) put_fb();
+    lds_barrier();                   // the next block's operands are visible
   }
 
   // ---- dbeta = write part + erase part (rows of block I) ---------------------
