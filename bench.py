@@ -217,6 +217,33 @@ def main():
                        for name, (a, p) in kern.items()},
         "roofline": roofline,
     }
+    # The other saving policy, timed the same way after the headline run: under
+    # "save" the forward writes the backward's operands and the backward runs no
+    # recompute ("A" in the pages' R/A pairs); under "recompute" the backward
+    # re-runs the forward prep and scan ("R").
+    other = "save" if args.policy == "recompute" else "recompute"
+    prob2 = ops.make_problem(x.q, x.v, x.g, x.beta, scale=inp.scale, cu_seqlens=inp.cu_seqlens,
+                             policy=other)
+    w20, w21 = ops.workspace(prob2, 0), ops.workspace(prob2, 1)
+
+    def step2():
+        o, ht, ctx = ops.forward(x.q, x.k, x.v, x.g, x.beta, scale=inp.scale, h0=x.h0,
+                                 cu_seqlens=inp.cu_seqlens, policy=other, ws=w20)
+        return ops.backward(ctx, x.dO, x.dht, ws=w21)
+
+    for _ in range(max(3, args.warmup // 4)):
+        step2()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step2()
+    torch.cuda.synchronize()
+    ms2 = (time.perf_counter() - t2) * 1e3 / args.steps
+    result["other_policy"] = {"policy": other, "ms_per_step": ms2, "value": B * T / (ms2 * 1e-3),
+                              "unit": "tokens/s"}
+    del w20, w21, prob2
+    print(f"[bench] {other} policy: {ms2:.3f} ms/step", file=sys.stderr, flush=True)
+
     if not args.no_cpu_baseline:
         import oracle
         hs = list(range(min(args.cpu_heads, H)))

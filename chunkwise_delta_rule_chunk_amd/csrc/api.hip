@@ -92,14 +92,14 @@ int make_plan(const rewy_desc* d, Plan& p) {
 // the save-all policy; everything else is scratch in the workspace.  The
 // reverse set is what the reverse scan and the chunk backward read:
 // F Wt Qgt Cqt (reverse scan) and At Kt Qt G2t Gst (chunk backward).
-//   recompute: ws = [index | glast hbuf R | W Ft U | (fwd) Qg Cq  / (bwd) reverse set | Rbt dhbuf]
+//   recompute: ws = [index | glast hbuf R | W Ft U | (fwd) Qg Cq hbufT RT / (bwd) reverse set | Rbt dhbuf]
 //   save-all:  saved = [glast hbuf R | reverse set]
-//              ws (fwd) = [index | W Ft U Qg Cq],  ws (bwd) = [index | Rbt dhbuf]
+//              ws (fwd) = [index | W Ft U Qg Cq hbufT RT],  ws (bwd) = [index | Rbt dhbuf]
 struct Layout {
   size_t chunks, seqoff;
   size_t glast, hbuf, R;             // read by output and backward
   size_t W, Ft, U;                   // forward scan operands
-  size_t Qg, Cq;                     // output operands
+  size_t Qg, Cq, hbufT, RT;          // output operands
   size_t F, Wt, Qgt, Cqt;            // reverse scan operands
   size_t At, Kt, Qt, G2t, Gst;       // chunk backward operands
   size_t Rbt, dhbuf;                 // written by the reverse scan
@@ -148,6 +148,8 @@ Layout layout(const Plan& p) {
   const size_t after_scan = off;
   L.Qg = take(off, tokK);
   L.Cq = take(off, tile64);
+  L.hbufT = take(off, nc * H * K * V * e);
+  L.RT = take(off, tileV);
   L.ws_fwd = off;
   if (save) {
     off = head;
@@ -193,6 +195,7 @@ void fill_common(Args& a, const Plan& p, const rewy_desc* d, char* ws, char* sv,
   a.hbuf = fs + L.hbuf; a.R = fs + L.R;
   a.F = fs + L.F; a.Wt = fs + L.Wt; a.Qgt = fs + L.Qgt; a.Cqt = fs + L.Cqt;
   a.W = ws + L.W; a.Ft = ws + L.Ft; a.U = ws + L.U; a.Qg = ws + L.Qg; a.Cq = ws + L.Cq;
+  a.hbufT = ws + L.hbufT; a.RT = ws + L.RT;
   a.At = fs + L.At; a.Kt = fs + L.Kt; a.Qt = fs + L.Qt;
   a.G2t = reinterpret_cast<float*>(fs + L.G2t);
   a.Gst = reinterpret_cast<float*>(fs + L.Gst);
@@ -309,6 +312,7 @@ REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const vo
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
   a.prep_mode = PREP_FWD_SCAN | PREP_FWD_OUT |
                 (p.policy == REWY_SAVE ? PREP_BWD_SCAN | PREP_BWD_CHUNK : 0);
+  a.scan_out = SCAN_TRANSPOSED | (p.policy == REWY_SAVE ? SCAN_NATURAL : 0);
   return run_forward_stages(a, p.f32, true, s);
 }
 
@@ -345,6 +349,7 @@ REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const vo
   fill_common(a, p, d, static_cast<char*>(workspace),
               const_cast<char*>(static_cast<const char*>(saved)), L);
   a.prep_mode = PREP_FWD_SCAN | PREP_BWD_SCAN | PREP_BWD_CHUNK;
+  a.scan_out = SCAN_NATURAL;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = dO; a.dht = dht;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
   const bool f32 = p.f32;

@@ -21,22 +21,27 @@ __global__ __launch_bounds__(256) void k_fwd_out(Args a) {
   const int64_t t0 = ci.bos;
   const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
   g2s<T, K>(sQg, PK, reinterpret_cast<const T*>(a.Qg) + (t0 * H + h) * K, gsK, len, CH, tid, 256);
-  g2s_T<T, V>(sHt, PK, reinterpret_cast<const T*>(a.hbuf) + ((int64_t)c * H + h) * K * V, V, K, K,
-              tid, 256);
+  // S_c^T and R^T tiles, written transposed by the forward scan
+  g2s<T, K>(sHt, PK, reinterpret_cast<const T*>(a.hbufT) + ((int64_t)c * H + h) * V * K, K, V, V,
+            tid, 256);
   g2s<T, CH>(sCq, PA, reinterpret_cast<const T*>(a.Cq) + ((int64_t)c * H + h) * CH * CH, CH, CH,
              CH, tid, 256);
-  g2s_T<T, V>(sRt, PA, reinterpret_cast<const T*>(a.R) + (t0 * H + h) * V, gsV, len, CH, tid, 256);
+  g2s<T, CH>(sRt, PA, reinterpret_cast<const T*>(a.RT) + ((int64_t)c * H + h) * V * CH, CH, V, V,
+             tid, 256);
   lds_barrier();
   T* og = reinterpret_cast<T*>(a.o) + (t0 * H + h) * V;
   const int w = wave_id();
   for (int cb = w; cb < V / SUB; cb += 4) {
-    for (int I = 0; I < NSUB && I * SUB < len; ++I) {
+    static_for<0, NSUB>([&](auto II) {
+      constexpr int I = decltype(II)::value;
+      if (I * SUB >= len) return;
       f32x4 acc = zero4();
       mma_tile<T, true, true>(acc, sQg + I * SUB * PK, PK, 1, sHt + cb * SUB * PK, PK, 1, K);
-      const int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
+      // Cq is lower triangular: row block I needs tokens < 16 (I + 1) only
+      constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
       mma_tile<T, true, true>(acc, sCq + I * SUB * PA, PA, 1, sRt + cb * SUB * PA, PA, 1, kd);
       st_tile<T>(acc, og + (I * SUB) * gsV + cb * SUB, (int)gsV, 1, len - I * SUB);
-    }
+    });
   }
 }
 

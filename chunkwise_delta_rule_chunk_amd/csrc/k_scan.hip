@@ -59,8 +59,10 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
   __shared__ __align__(16) T sFt[2][K * PA];
   __shared__ __align__(16) T sU[2][CH * PU];
   __shared__ __align__(16) float sLam[2][K];  // exp2(G2_last)
-  __shared__ __align__(16) T sHt[BV * PK];    // state as operand, [v][k]
-  __shared__ __align__(16) T sRt[BV * PA];    // R as operand, [v][i]
+  // S_c and R_c as MFMA operands, [v][k] and [v][i]; two buffers, since the
+  // transposed outputs are written from them during the next step
+  __shared__ __align__(16) T sHt[2][BV * PK];
+  __shared__ __align__(16) T sRt[2][BV * PA];
   // S_c and R_c in natural layout, written to global memory with 16-byte
   // stores during the next step (few memory instructions per step)
   __shared__ __align__(16) T sS[2][K * PU];
@@ -97,9 +99,26 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
     pU[set].store(sU[set], PU, tid);
     pL[set].store(sLam[set], tid);
   };
-  // S and R staged in buffer b, to global memory (R rows past the end skipped)
+  // S and R staged in buffer b, to global memory (R rows past the end skipped):
+  // natural layouts for the chunk backward, transposed ones for the output
+  const bool natural = a.scan_out & SCAN_NATURAL, transposed = a.scan_out & SCAN_TRANSPOSED;
   auto flush = [&](auto b, int c) {
     constexpr int VE = 16 / (int)sizeof(T), PER = BV / VE;
+    if (transposed) {
+      T* ht = reinterpret_cast<T*>(a.hbufT) + (((int64_t)c * H + h) * V + vt * BV) * K;
+      for (int idx = tid; idx < BV * (K / VE); idx += NTH) {
+        const int r = idx / (K / VE), c8 = (idx - r * (K / VE)) * VE;
+        *reinterpret_cast<uint4*>(ht + (int64_t)r * K + c8) =
+            *reinterpret_cast<const uint4*>(sHt[b] + r * PK + c8);
+      }
+      T* rt = reinterpret_cast<T*>(a.RT) + (((int64_t)c * H + h) * V + vt * BV) * CH;
+      for (int idx = tid; idx < BV * (CH / VE); idx += NTH) {
+        const int r = idx / (CH / VE), c8 = (idx - r * (CH / VE)) * VE;
+        *reinterpret_cast<uint4*>(rt + r * CH + c8) =
+            *reinterpret_cast<const uint4*>(sRt[b] + r * PA + c8);
+      }
+    }
+    if (!natural) return;
     T* hb = reinterpret_cast<T*>(a.hbuf) + ((int64_t)c * H + h) * K * V + vt * BV;
     for (int idx = tid; idx < K * PER; idx += NTH) {
       const int r = idx / PER, c8 = (idx - r * PER) * VE;
@@ -145,9 +164,9 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         x[i] = tof(fromf<T>(st[s][i]));
-        sS[B][(tk * SUB + crow(i)) * PU + tv * SUB + ccol()] = fromf<T>(st[s][i]);
+        if (natural) sS[B][(tk * SUB + crow(i)) * PU + tv * SUB + ccol()] = fromf<T>(st[s][i]);
       }
-      st_tile_T<T>(x, sHt + (tv * SUB) * PK + tk * SUB, PK);
+      st_tile_T<T>(x, sHt[B] + (tv * SUB) * PK + tk * SUB, PK);
     }
     if (tid == 0) {
       const ChunkInfo ci = a.chunks[c];
@@ -160,16 +179,16 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
     for (int r = 0; r < S::RPW; ++r) {
       const int t = w + 4 * r, ti = t / CT, tv = t - ti * CT;
       f32x4 p = zero4();
-      mma_tile<T, true, true>(p, sW[B] + ti * SUB * PK, PK, 1, sHt + tv * SUB * PK, PK, 1, K);
+      mma_tile<T, true, true>(p, sW[B] + ti * SUB * PK, PK, 1, sHt[B] + tv * SUB * PK, PK, 1, K);
       f32x4 rv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = ti * SUB + crow(i), col = tv * SUB + ccol();
         const T x = fromf<T>(tof(sU[B][row * PU + col]) - p[i]);
-        sR[B][row * PU + col] = x;
+        if (natural) sR[B][row * PU + col] = x;
         rv[i] = tof(x);
       }
-      st_tile_T<T>(rv, sRt + (tv * SUB) * PA + ti * SUB, PA);
+      st_tile_T<T>(rv, sRt[B] + (tv * SUB) * PA + ti * SUB, PA);
     }
     lds_barrier();
     // S = diag(exp2 G2_last) S + F^T R
@@ -178,7 +197,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
       const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
 #pragma unroll
       for (int i = 0; i < 4; ++i) st[s][i] *= sLam[B][tk * SUB + crow(i)];
-      mma_tile<T, true, true>(st[s], sFt[B] + tk * SUB * PA, PA, 1, sRt + tv * SUB * PA, PA, 1, CH);
+      mma_tile<T, true, true>(st[s], sFt[B] + tk * SUB * PA, PA, 1, sRt[B] + tv * SUB * PA, PA, 1, CH);
     }
     if (c + 1 < c1) put(ic<B ^ 1>{});  // chunk c + 1; its buffer was last read a step ago
   };

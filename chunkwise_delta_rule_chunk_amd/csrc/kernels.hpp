@@ -57,6 +57,9 @@ struct Args {
   void* Cqt;     // Cq^T                [nc,H,64,64] reverse scan (Rbar += Cq^T dO)
   void* hbuf;    // state entering each chunk [nc,H,K,V] dtype
   void* R;       // corrections U - W S [BT,H,V] dtype
+  void* hbufT;   // the same states transposed [nc,H,V,K] (output kernel)
+  void* RT;      // R^T tiles [nc,H,V,64] (output kernel)
+  int scan_out;  // SCAN_* bits: which of hbuf/R and hbufT/RT the forward scan writes
   void* At;      // A^T                 [nc,H,64,64] chunk backward (P = A^T Rbar)
   void* Kt;      // K^T                 [nc,H,K,64]  chunk backward
   void* Qt;      // Q^T                 [nc,H,K,64]  chunk backward
@@ -67,6 +70,9 @@ struct Args {
   void* Rbt;     // correction adjoint Rbar^T [nc,H,V,64] dtype
   void* dhbuf;   // adjoint of the state leaving each chunk [nc,H,K,V] dtype
 };
+
+constexpr int SCAN_NATURAL = 1;     // hbuf, R (read by the chunk backward)
+constexpr int SCAN_TRANSPOSED = 2;  // hbufT, RT (read by the output kernel)
 
 constexpr int PREP_FWD_SCAN = 1;  // W, Ft, U, glast
 constexpr int PREP_FWD_OUT = 2;   // Qg, Cq
