@@ -201,6 +201,11 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       // the thread's 16 rows lie in sub-chunk seg: its references are per thread
       const float rA = ref_recv(sMid, sGf, sFlag, gc.seg, K, col);
       const float rB = ref_send(sMid, sGl, sFlag, gc.seg, K, col);
+      // two exponentials per row: ea = exp2(G - rA), eb = exp2(rB - G); then
+      // gamma = exp2(G) = ea exp2(rA) and exp2(gn - G) = eb exp2(gn - rB).  Values
+      // that flush to zero this way are below 2^-62 and multiply O(1) terms.
+      const float cA = fexp2(rA), cB = fexp2(gn - rB);
+      const float bs = a.scale;
       constexpr int VE = 16 / (int)sizeof(T);
       T* Ftd = reinterpret_cast<T*>(a.Ft) + (cb * K + col) * CH + r0;
       T* Qgtd = reinterpret_cast<T*>(a.Qgt) + (cb * K + col) * CH + r0;
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         union {
           uint4 u;
           T e[VE];
-        } ft, qt, kt, qq;
+        } ft, qt, kt, qq, et;
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
           const int r = r8 + e, row = r0 + r;
@@ -222,14 +227,14 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
             const float G = gc.G[r];
             const float kr = tof(sK[row * PK + col]), qr = tof(sQ[row * PK + col]);
             const float b = sBeta[row];
-            const float gam = fexp2(G);
-            const float ea = fexp2(G - rA);
+            const float ea = fexp2(G - rA), eb = fexp2(rB - G);
+            const float gam = ea * cA;
             vKa = b * kr * ea;
-            vQa = a.scale * qr * ea;
-            vKc = kr * fexp2(rB - G);
+            vQa = bs * qr * ea;
+            vKc = kr * eb;
             vE = b * kr * gam;
-            vF = kr * fexp2(gn - G);
-            vQg = a.scale * qr * gam;
+            vF = kr * (eb * cB);
+            vQg = bs * qr * gam;
             if (mode & PREP_FWD_OUT)
               reinterpret_cast<T*>(a.Qg)[(t0 + row) * gsK + h * K + col] = fromf<T>(vQg);
             if (mode & PREP_BWD_SCAN)
@@ -238,11 +243,12 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
           sKa[row * PK + col] = fromf<T>(vKa);
           sQ[row * PK + col] = fromf<T>(vQa);
           sK[row * PK + col] = fromf<T>(vKc);
-          sEt[col * PA + row] = fromf<T>(vE);
+          et.e[e] = fromf<T>(vE);
           ft.e[e] = fromf<T>(vF);
           qt.e[e] = fromf<T>(vQg);
         }
         // token-contiguous tiles: this thread holds consecutive tokens of column col
+        *reinterpret_cast<uint4*>(sEt + col * PA + r0 + r8) = et.u;
         if (mode & PREP_FWD_SCAN) *reinterpret_cast<uint4*>(Ftd + r8) = ft.u;
         if (mode & PREP_BWD_SCAN) *reinterpret_cast<uint4*>(Qgtd + r8) = qt.u;
         if (mode & PREP_BWD_CHUNK) {
