@@ -87,6 +87,28 @@ def measured_traffic(kernel: str, workload: str, policy: str):
     return None
 
 
+def _time_other(result, other, prob2, x, inp, B, T, args, ops, torch):
+    """Time K steps under the other saving policy and record them in result."""
+    w20, w21 = ops.workspace(prob2, 0), ops.workspace(prob2, 1)
+
+    def step2():
+        o, ht, ctx = ops.forward(x.q, x.k, x.v, x.g, x.beta, scale=inp.scale, h0=x.h0,
+                                 cu_seqlens=inp.cu_seqlens, policy=other, ws=w20)
+        return ops.backward(ctx, x.dO, x.dht, ws=w21)
+
+    for _ in range(max(3, args.warmup // 4)):
+        step2()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step2()
+    torch.cuda.synchronize()
+    ms2 = (time.perf_counter() - t2) * 1e3 / args.steps
+    result["other_policy"] = {"policy": other, "ms_per_step": ms2, "value": B * T / (ms2 * 1e-3),
+                              "unit": "tokens/s"}
+    print(f"[bench] {other} policy: {ms2:.3f} ms/step", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,10 +117,12 @@ def main():
     ap.add_argument("--workload", default="kda_t8192_h32_d128")
     ap.add_argument("--policy", default="recompute", choices=["recompute", "save"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16,
+    ap.add_argument("--cpu-heads", type=int, default=32,
                     help="heads of the workload the oracle baseline runs")
     ap.add_argument("--min-warmup-s", type=float, default=2.0,
                     help="warm-up lasts at least this long (profiler runs pass 0)")
+    ap.add_argument("--no-other-policy", action="store_true",
+                    help="skip timing the other saving policy (profiler runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB once (a plain "
                          "copy kernel of known size, to calibrate HBM byte counters)")
@@ -222,27 +246,12 @@ def main():
     # recompute ("A" in the pages' R/A pairs); under "recompute" the backward
     # re-runs the forward prep and scan ("R").
     other = "save" if args.policy == "recompute" else "recompute"
-    prob2 = ops.make_problem(x.q, x.v, x.g, x.beta, scale=inp.scale, cu_seqlens=inp.cu_seqlens,
-                             policy=other)
-    w20, w21 = ops.workspace(prob2, 0), ops.workspace(prob2, 1)
-
-    def step2():
-        o, ht, ctx = ops.forward(x.q, x.k, x.v, x.g, x.beta, scale=inp.scale, h0=x.h0,
-                                 cu_seqlens=inp.cu_seqlens, policy=other, ws=w20)
-        return ops.backward(ctx, x.dO, x.dht, ws=w21)
-
-    for _ in range(max(3, args.warmup // 4)):
-        step2()
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        step2()
-    torch.cuda.synchronize()
-    ms2 = (time.perf_counter() - t2) * 1e3 / args.steps
-    result["other_policy"] = {"policy": other, "ms_per_step": ms2, "value": B * T / (ms2 * 1e-3),
-                              "unit": "tokens/s"}
-    del w20, w21, prob2
-    print(f"[bench] {other} policy: {ms2:.3f} ms/step", file=sys.stderr, flush=True)
+    if args.no_other_policy:
+        other = None
+    prob2 = None if other is None else ops.make_problem(x.q, x.v, x.g, x.beta, scale=inp.scale,
+                                                         cu_seqlens=inp.cu_seqlens, policy=other)
+    if other is not None:
+        _time_other(result, other, prob2, x, inp, B, T, args, ops, torch)
 
     if not args.no_cpu_baseline:
         import oracle
