@@ -1,13 +1,19 @@
-// The two serial inter-chunk scans.  One workgroup per (sequence, head, value
-// tile of BV columns) walks the sequence's chunks in order; the fp32 state
-// tile [K x BV] stays in MFMA accumulator registers for the whole walk.
-// Grid = (N*H, V/BV): consecutive workgroup ids, which the dispatcher spreads
-// round-robin over the 8 XCDs, give the value tiles of one (sequence, head)
-// the same XCD and L2 whenever N*H is a multiple of 8.
+// The two serial inter-chunk scans.  One workgroup of four waves per
+// (sequence, head, value tile of BV columns) walks the sequence's chunks in
+// order; the fp32 state tile [K x BV] stays in MFMA accumulator registers for
+// the whole walk.  Grid = (N*H, V/BV): consecutive workgroup ids, which the
+// dispatcher spreads round-robin over the 8 XCDs, give the value tiles of one
+// (sequence, head) the same XCD and L2 whenever N*H is a multiple of 8.
 //
-// Each step's operand tiles are prefetched one chunk ahead: the global reads
-// for chunk c+1 are issued before chunk c's products and land in the other LDS
-// buffer after them, so a step waits only on its two barriers.
+// Wave w owns token tile w of the per-chunk product (R or Rbar) and a set of
+// key tiles of the state.  The chunk operands it contracts (rows of W, F^T,
+// F, Cq^T, Qg^T, W^T) go straight from global memory into MFMA operand
+// registers, 16 bytes per lane, two chunks ahead; only the state and the
+// per-chunk product pass through LDS, with two barriers per step.  Every
+// global load and store inside the chunk loop is unconditional (clamped
+// indices, rows past a chunk's end masked where they are used), so the
+// compiler's memory counters let each use wait for exactly its own load and
+// the prefetches stay in flight across steps.
 //
 // Forward (ReWY paper, "The chunk system": R = U - W S, S' = Lambda S + F^T R;
 // KDA blog section 6.4 state fast-forward):
@@ -21,350 +27,443 @@
 
 namespace rewy {
 
-template <int K, int BV>
-struct ScanShape {
-  static constexpr int CT = BV / SUB;             // column tiles of the state
-  static constexpr int TPW = (K / SUB) * CT / 4;  // state tiles per wave
-  static constexpr int RPW = (CH / SUB) * CT / 4; // R tiles per wave
-  static_assert(TPW >= 1 && RPW >= 1, "tile split");
-};
-
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-// exp2 of G2 at the chunk's last row, per key row: the chunk decay Lambda.
-template <int K>
-struct StagedDecay {
-  f32x4 r;
-  __device__ __forceinline__ void load(const float* g, int tid) {
-    r = zero4();
-    if (tid < K / 4) r = reinterpret_cast<const f32x4*>(g)[tid];
-  }
-  __device__ __forceinline__ void store(float* s, int tid) const {
-    if (tid < K / 4) {
-      f32x4 x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = fexp2(r[e]);
-      reinterpret_cast<f32x4*>(s)[tid] = x;
-    }
-  }
-};
-
-template <typename T, int K, int V, int BV>
-__global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
-  using S = ScanShape<K, BV>;
-  constexpr int CT = S::CT, NTH = 256;
-  constexpr int PK = pitch<T>(K), PU = pitch<T>(BV), PA = pitch<T>(CH);
-  __shared__ __align__(16) T sW[2][CH * PK];
-  __shared__ __align__(16) T sFt[2][K * PA];
-  __shared__ __align__(16) T sU[2][CH * PU];
-  __shared__ __align__(16) float sLam[2][K];  // exp2(G2_last)
-  // S_c and R_c as MFMA operands, [v][k] and [v][i]; two buffers, since the
-  // transposed outputs are written from them during the next step
-  __shared__ __align__(16) T sHt[2][BV * PK];
-  __shared__ __align__(16) T sRt[2][BV * PA];
-  // S_c and R_c in natural layout, written to global memory with 16-byte
-  // stores during the next step (few memory instructions per step)
-  __shared__ __align__(16) T sS[2][K * PU];
-  __shared__ __align__(16) T sR[2][CH * PU];
-  __shared__ int sLen[2];
-  __shared__ int64_t sT0[2];
-
-  const int H = a.H;
-  const int u = blockIdx.x, vt = blockIdx.y;
-  const int n = u / H, h = u - n * H;
-  const int w = wave_id(), tid = threadIdx.x;
-  const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
-  const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
-  const T* Wg = reinterpret_cast<const T*>(a.W);
-  const T* Ftg = reinterpret_cast<const T*>(a.Ft);
-  const T* Ug = reinterpret_cast<const T*>(a.U);
-
-  // two register sets: chunk c + 2 is read while chunk c is processed
-  Staged<T, CH, K, NTH> pW[2];
-  Staged<T, K, CH, NTH> pF[2];
-  Staged<T, CH, BV, NTH> pU[2];
-  StagedDecay<K> pL[2];
-  auto fetch = [&](auto set, int c) {
-    const ChunkInfo ci = a.chunks[c];
-    const int64_t t0 = ci.bos, cb = (int64_t)c * H + h;
-    pW[set].load(Wg + (t0 * H + h) * K, gsK, ci.len, tid);
-    pF[set].load(Ftg + cb * K * CH, CH, K, tid);
-    pU[set].load(Ug + (t0 * H + h) * V + vt * BV, gsV, ci.len, tid);
-    pL[set].load(a.glast + cb * K, tid);
-  };
-  auto put = [&](auto set) {
-    pW[set].store(sW[set], PK, tid);
-    pF[set].store(sFt[set], PA, tid);
-    pU[set].store(sU[set], PU, tid);
-    pL[set].store(sLam[set], tid);
-  };
-  // S and R staged in buffer b, to global memory (R rows past the end skipped):
-  // natural layouts for the chunk backward, transposed ones for the output
-  const bool natural = a.scan_out & SCAN_NATURAL, transposed = a.scan_out & SCAN_TRANSPOSED;
-  auto flush = [&](auto b, int c) {
-    constexpr int VE = 16 / (int)sizeof(T), PER = BV / VE;
-    if (transposed) {
-      T* ht = reinterpret_cast<T*>(a.hbufT) + (((int64_t)c * H + h) * V + vt * BV) * K;
-      for (int idx = tid; idx < BV * (K / VE); idx += NTH) {
-        const int r = idx / (K / VE), c8 = (idx - r * (K / VE)) * VE;
-        *reinterpret_cast<uint4*>(ht + (int64_t)r * K + c8) =
-            *reinterpret_cast<const uint4*>(sHt[b] + r * PK + c8);
-      }
-      T* rt = reinterpret_cast<T*>(a.RT) + (((int64_t)c * H + h) * V + vt * BV) * CH;
-      for (int idx = tid; idx < BV * (CH / VE); idx += NTH) {
-        const int r = idx / (CH / VE), c8 = (idx - r * (CH / VE)) * VE;
-        *reinterpret_cast<uint4*>(rt + r * CH + c8) =
-            *reinterpret_cast<const uint4*>(sRt[b] + r * PA + c8);
-      }
-    }
-    if (!natural) return;
-    T* hb = reinterpret_cast<T*>(a.hbuf) + ((int64_t)c * H + h) * K * V + vt * BV;
-    for (int idx = tid; idx < K * PER; idx += NTH) {
-      const int r = idx / PER, c8 = (idx - r * PER) * VE;
-      *reinterpret_cast<uint4*>(hb + (int64_t)r * V + c8) =
-          *reinterpret_cast<const uint4*>(sS[b] + r * PU + c8);
-    }
-    const int len = sLen[b];
-    T* Rg = reinterpret_cast<T*>(a.R) + (sT0[b] * H + h) * V + vt * BV;
-    for (int idx = tid; idx < CH * PER; idx += NTH) {
-      const int r = idx / PER, c8 = (idx - r * PER) * VE;
-      if (r < len)
-        *reinterpret_cast<uint4*>(Rg + (int64_t)r * gsV + c8) =
-            *reinterpret_cast<const uint4*>(sR[b] + r * PU + c8);
-    }
-  };
-
-  f32x4 st[S::TPW];
-#pragma unroll
-  for (int s = 0; s < S::TPW; ++s) {
-    const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kk = tk * SUB + crow(i), vv = vt * BV + tv * SUB + ccol();
-      st[s][i] = a.h0 ? a.h0[(((int64_t)n * H + h) * K + kk) * V + vv] : 0.f;
-    }
-  }
-  if (c0 < c1) {
-    fetch(ic<0>{}, c0);
-    if (c0 + 1 < c1) fetch(ic<1>{}, c0 + 1);
-    put(ic<0>{});
-  }
-  lds_barrier();
-
-  auto step = [&](auto buf, int c) {
-    constexpr int B = decltype(buf)::value;
-    if (c + 2 < c1) fetch(ic<B>{}, c + 2);
-    if (c > c0) flush(ic<B ^ 1>{}, c - 1);
-    // S_c: staged for global memory, and as the operand of W S
-#pragma unroll
-    for (int s = 0; s < S::TPW; ++s) {
-      const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
-      f32x4 x;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = tof(fromf<T>(st[s][i]));
-        if (natural) sS[B][(tk * SUB + crow(i)) * PU + tv * SUB + ccol()] = fromf<T>(st[s][i]);
-      }
-      st_tile_T<T>(x, sHt[B] + (tv * SUB) * PK + tk * SUB, PK);
-    }
-    if (tid == 0) {
-      const ChunkInfo ci = a.chunks[c];
-      sLen[B] = ci.len;
-      sT0[B] = ci.bos;
-    }
-    lds_barrier();
-    // R = U - W S
-#pragma unroll
-    for (int r = 0; r < S::RPW; ++r) {
-      const int t = w + 4 * r, ti = t / CT, tv = t - ti * CT;
-      f32x4 p = zero4();
-      mma_tile<T, true, true>(p, sW[B] + ti * SUB * PK, PK, 1, sHt[B] + tv * SUB * PK, PK, 1, K);
-      f32x4 rv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = ti * SUB + crow(i), col = tv * SUB + ccol();
-        const T x = fromf<T>(tof(sU[B][row * PU + col]) - p[i]);
-        if (natural) sR[B][row * PU + col] = x;
-        rv[i] = tof(x);
-      }
-      st_tile_T<T>(rv, sRt[B] + (tv * SUB) * PA + ti * SUB, PA);
-    }
-    lds_barrier();
-    // S = diag(exp2 G2_last) S + F^T R
-#pragma unroll
-    for (int s = 0; s < S::TPW; ++s) {
-      const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[s][i] *= sLam[B][tk * SUB + crow(i)];
-      mma_tile<T, true, true>(st[s], sFt[B] + tk * SUB * PA, PA, 1, sRt[B] + tv * SUB * PA, PA, 1, CH);
-    }
-    if (c + 1 < c1) put(ic<B ^ 1>{});  // chunk c + 1; its buffer was last read a step ago
-  };
-  for (int c = c0; c < c1; c += 2) {
-    step(ic<0>{}, c);
-    if (c + 1 < c1) step(ic<1>{}, c + 1);
-  }
-  lds_barrier();
-  if (c1 > c0) {  // the last chunk's S and R
-    if ((c1 - 1 - c0) & 1) flush(ic<1>{}, c1 - 1);
-    else flush(ic<0>{}, c1 - 1);
-  }
-  if (a.ht) {
-#pragma unroll
-    for (int s = 0; s < S::TPW; ++s) {
-      const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = tk * SUB + crow(i), vv = vt * BV + tv * SUB + ccol();
-        a.ht[(((int64_t)n * H + h) * K + kk) * V + vv] = st[s][i];
-      }
-    }
+// acc += A B over one 16-byte lane group: lane l supplies 16 bytes of row
+// (l & 15) of A and of column (l & 15) of B, at contraction slots
+// VE (l >> 4) + e of the group (VE = 16 / sizeof(T)).  bf16: one 16x16x32
+// MFMA; fp32: four 16x16x4 MFMAs, step e taking element e of every lane.
+template <typename T>
+__device__ __forceinline__ void mma16B(f32x4& acc, uint4 a, uint4 b) {
+  if constexpr (std::is_same_v<T, bf16>) {
+    union {
+      uint4 u;
+      bf16x8 v;
+    } x, y;
+    x.u = a;
+    y.u = b;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.v, y.v, acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
   }
 }
 
-template <typename T, int K, int V, int BV>
-__global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
-  using S = ScanShape<K, BV>;
-  constexpr int CT = S::CT, NTH = 256;
-  constexpr int PK = pitch<T>(K), PA = pitch<T>(CH), PS = pitch<T>(BV);
-  // one buffer of chunk operands, refilled between two barriers
-  __shared__ __align__(16) T sF[CH * PK];
-  __shared__ __align__(16) T sWt[K * PA];
-  __shared__ __align__(16) T sQgt[K * PA];
-  __shared__ __align__(16) T sCqt[CH * PA];
-  __shared__ __align__(16) T sdOt[BV * PA];   // dO as operand, [v][j]
-  __shared__ __align__(16) float sLam[K];     // exp2(G2_last)
-  __shared__ __align__(16) T sDt[BV * PK];    // dS_{c+1} as operand, [v][k]
-  __shared__ __align__(16) T sRbt[BV * PA];   // -Rbar as operand, [v][i]
-  // dS_{c+1} in natural layout, written to global memory during the next step
-  __shared__ __align__(16) T sD[2][K * PS];
+// Copy a [ROWS x COLS] tile from LDS (pitch lp) to global memory (row stride
+// gs elements) with every thread storing the same number of equal pieces, so
+// the store count per thread is a compile-time constant.  Rows >= nvalid are
+// redirected to row nvalid - 1 (the same bytes written twice), which keeps
+// the stores unconditional.
+template <typename T, int ROWS, int COLS, int NTH>
+__device__ __forceinline__ void tile_out(T* g, int64_t gs, const T* s, int lp, int nvalid, int tid) {
+  constexpr int BYTES = ROWS * COLS * (int)sizeof(T);
+  constexpr int PB = BYTES / NTH >= 16 ? 16 : BYTES / NTH;  // bytes per piece
+  static_assert(PB == 16 || PB == 8, "piece size");
+  constexpr int E = PB / (int)sizeof(T), PER = COLS / E, NP = BYTES / (PB * NTH);
+  static_assert(COLS % E == 0 && BYTES % (PB * NTH) == 0, "tile split");
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int idx = tid + j * NTH;
+    const int r = min(idx / PER, nvalid - 1), c = (idx % PER) * E;
+    if constexpr (PB == 16)
+      *reinterpret_cast<uint4*>(g + (int64_t)r * gs + c) = *reinterpret_cast<const uint4*>(s + r * lp + c);
+    else
+      *reinterpret_cast<uint2*>(g + (int64_t)r * gs + c) = *reinterpret_cast<const uint2*>(s + r * lp + c);
+  }
+}
+
+// Forward scan.  Wave w owns token tile w of R (all value columns of the
+// workgroup) and a set of key tiles of the state; it reads the W rows and F^T
+// rows it contracts straight from global memory into MFMA operand registers
+// (16 bytes per lane, DEPTH chunks ahead), so only S_c and R_c pass through
+// LDS.  Every global load and store in the chunk loop is unconditional
+// (clamped indices, selects): the compiler then counts exactly which loads a
+// use has to wait for, and the prefetches stay in flight across steps.
+template <typename T, int K, int V, int BV, int OUT>
+__global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
+  constexpr int NTH = 256, DEPTH = 2;
+  constexpr bool NAT = OUT & SCAN_NATURAL, TRN = OUT & SCAN_TRANSPOSED;
+  constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE;  // elements per lane piece, per group
+  constexpr int CT = BV / SUB, NKT = K / SUB;
+  constexpr int NGK = K / KG, NGT = CH / KG;
+  // state tiles: wave w takes key tiles w, w + 4, ... with all CT column tiles,
+  // or, for K = 32, key tile w % 2 and column tile w / 2
+  constexpr bool WIDE = NKT >= 4;
+  constexpr int KW = WIDE ? NKT / 4 : 1, CW = WIDE ? CT : CT * NKT / 4;
+  static_assert(WIDE || (NKT == 2 && CT == 2), "state tile split");
+  constexpr int PK = pitch<T>(K), PA = pitch<T>(CH), PU = pitch<T>(BV);
+  __shared__ __align__(16) T sHt[BV * PK];        // S_c as operand, [v][k]
+  __shared__ __align__(16) T sRt[BV * PA];        // R_c as operand, [v][i]
+  __shared__ __align__(16) T sS[NAT ? K * PU : 8];   // S_c, natural layout
+  __shared__ __align__(16) T sR[NAT ? CH * PU : 8];  // R_c, natural layout
 
   const int H = a.H;
   const int u = blockIdx.x, vt = blockIdx.y;
   const int n = u / H, h = u - n * H;
-  const int w = wave_id(), tid = threadIdx.x;
+  const int w = wave_id(), tid = threadIdx.x, l = lane_id();
+  const int r16 = l & 15, g = l >> 4;
   const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
   const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
+  const int seq_bos = a.cu ? a.cu[n] : n * a.T, seq_eos = a.cu ? a.cu[n + 1] : (n + 1) * a.T;
+  const T* Wg = reinterpret_cast<const T*>(a.W);
+  const T* Ftg = reinterpret_cast<const T*>(a.Ft);
+  const T* Ug = reinterpret_cast<const T*>(a.U);
+  auto ktile = [&](int j) { return WIDE ? w + 4 * j : w % NKT; };
+  auto vtile = [&](int m) { return WIDE ? m : (w / NKT) * CW + m; };
 
-  // two register sets: chunk c - 2 is read while chunk c is processed
-  Staged<T, CH, K, NTH> pF[2];
-  Staged<T, K, CH, NTH> pW[2];
-  Staged<T, K, CH, NTH> pQ[2];
-  Staged<T, CH, CH, NTH> pC[2];
-  Staged<T, CH, BV, NTH> pO[2];
-  StagedDecay<K> pL[2];
-  auto fetch = [&](auto set, int c) {
-    const ChunkInfo ci = a.chunks[c];
-    const int64_t t0 = ci.bos, cb = (int64_t)c * H + h;
-    pF[set].load(reinterpret_cast<const T*>(a.F) + (t0 * H + h) * K, gsK, ci.len, tid);
-    pW[set].load(reinterpret_cast<const T*>(a.Wt) + cb * K * CH, CH, K, tid);
-    pQ[set].load(reinterpret_cast<const T*>(a.Qgt) + cb * K * CH, CH, K, tid);
-    pC[set].load(reinterpret_cast<const T*>(a.Cqt) + cb * CH * CH, CH, CH, tid);
-    pO[set].load(reinterpret_cast<const T*>(a.dO) + (t0 * H + h) * V + vt * BV, gsV, ci.len, tid);
-    pL[set].load(a.glast + cb * K, tid);
+  // DEPTH register sets: chunk c + DEPTH is read while chunk c is processed
+  uint4 wf[DEPTH][NGK];      // W row 16 w + r16, lane piece of every key group
+  T uf[DEPTH][CT][4];        // U in the C layout of R's tiles
+  uint4 ff[DEPTH][KW][NGT];  // F^T row 16 ktile + r16, lane piece of every token group
+  f32x4 lam[DEPTH][KW];      // G2_last of the state rows this lane holds
+  // chunk c of this sequence from the sequence bounds; past the last chunk the
+  // last one is read again (valid memory, never used)
+  auto chunk_bos = [&](int c) { return seq_bos + (min(c, c1 - 1) - c0) * CH; };
+  auto fetch_wu = [&](auto set, int c) {
+    constexpr int B = decltype(set)::value;
+    const int bos = chunk_bos(c), len = min(CH, seq_eos - bos);
+    const int row = SUB * w + r16;
+    const T* wp = Wg + ((int64_t)bos * H + h) * K + (int64_t)min(row, len - 1) * gsK + VE * g;
+    // rows past the chunk's end read row len - 1; they are zeroed where used
+#pragma unroll
+    for (int q = 0; q < NGK; ++q) wf[B][q] = *reinterpret_cast<const uint4*>(wp + KG * q);
+#pragma unroll
+    for (int m = 0; m < CT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = SUB * w + 4 * g + i;
+        uf[B][m][i] = Ug[((int64_t)bos + min(rr, len - 1)) * gsV + (int64_t)h * V + vt * BV + SUB * m + r16];
+      }
   };
-  auto put = [&](auto set) {
-    pF[set].store(sF, PK, tid);
-    pW[set].store(sWt, PA, tid);
-    pQ[set].store(sQgt, PA, tid);
-    pC[set].store(sCqt, PA, tid);
-    pO[set].store_T(sdOt, PA, tid);
-    pL[set].store(sLam, tid);
-  };
-  auto flush = [&](auto b, int c) {
-    constexpr int VE = 16 / (int)sizeof(T), PER = BV / VE;
-    T* db = reinterpret_cast<T*>(a.dhbuf) + ((int64_t)c * H + h) * K * V + vt * BV;
-    for (int idx = tid; idx < K * PER; idx += NTH) {
-      const int r = idx / PER, c8 = (idx - r * PER) * VE;
-      *reinterpret_cast<uint4*>(db + (int64_t)r * V + c8) =
-          *reinterpret_cast<const uint4*>(sD[b] + r * PS + c8);
+  auto fetch_fl = [&](auto set, int c) {
+    constexpr int B = decltype(set)::value;
+    const int64_t cb = (int64_t)min(c, c1 - 1) * H + h;
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      const int kr = SUB * ktile(j);
+      const T* fp = Ftg + (cb * K + kr + r16) * CH + VE * g;
+#pragma unroll
+      for (int q = 0; q < NGT; ++q) ff[B][j][q] = *reinterpret_cast<const uint4*>(fp + KG * q);
+      lam[B][j] = *reinterpret_cast<const f32x4*>(a.glast + cb * K + kr + 4 * g);
     }
   };
 
-  f32x4 st[S::TPW];
+  f32x4 st[KW][CW];
 #pragma unroll
-  for (int s = 0; s < S::TPW; ++s) {
-    const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
+  for (int j = 0; j < KW; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kk = tk * SUB + crow(i), vv = vt * BV + tv * SUB + ccol();
-      st[s][i] = a.dht ? a.dht[(((int64_t)n * H + h) * K + kk) * V + vv] : 0.f;
-    }
+    for (int m = 0; m < CW; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = SUB * ktile(j) + 4 * g + i, vv = vt * BV + SUB * vtile(m) + r16;
+        st[j][m][i] = a.h0 ? a.h0[(((int64_t)n * H + h) * K + kk) * V + vv] : 0.f;
+      }
+  if (c0 >= c1) {  // empty sequence: the final state is the initial one
+    if (a.ht)
+#pragma unroll
+      for (int j = 0; j < KW; ++j)
+#pragma unroll
+        for (int m = 0; m < CW; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kk = SUB * ktile(j) + 4 * g + i, vv = vt * BV + SUB * vtile(m) + r16;
+            a.ht[(((int64_t)n * H + h) * K + kk) * V + vv] = st[j][m][i];
+          }
+    return;
   }
-  if (c0 < c1) {
-    fetch(ic<0>{}, c1 - 1);
-    if (c1 - 2 >= c0) fetch(ic<1>{}, c1 - 2);
-    put(ic<0>{});
-  }
+  static_for<0, DEPTH>([&](auto B) {
+    fetch_wu(B, c0 + B);
+    fetch_fl(B, c0 + B);
+  });
 
   auto step = [&](auto buf, int c) {
     constexpr int B = decltype(buf)::value;
-    if (c - 2 >= c0) fetch(ic<B>{}, c - 2);
-    if (c < c1 - 1) flush(ic<B ^ 1>{}, c + 1);  // dS_{c+2}, staged last step
-    const ChunkInfo ci = a.chunks[c];
-    const int64_t t0 = ci.bos;
-    // dS_{c+1}: staged for global memory, and as the operand of F dS+
+    const int bos = chunk_bos(c), len = min(CH, seq_eos - bos);
+    // S_c: operand [v][k] and, for global memory, natural [k][v]
 #pragma unroll
-    for (int s = 0; s < S::TPW; ++s) {
-      const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
-      f32x4 x;
+    for (int j = 0; j < KW; ++j)
+#pragma unroll
+      for (int m = 0; m < CW; ++m) {
+        const int kr = SUB * ktile(j), vc = SUB * vtile(m);
+        f32x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const T y = fromf<T>(st[j][m][i]);
+          x[i] = tof(y);
+          if constexpr (NAT) sS[(kr + 4 * g + i) * PU + vc + r16] = y;
+        }
+        st_tile_T<T>(x, sHt + vc * PK + kr, PK);
+      }
+    lds_barrier();
+    const int64_t cb = (int64_t)c * H + h;
+    if constexpr (TRN)
+      tile_out<T, BV, K, NTH>(reinterpret_cast<T*>(a.hbufT) + (cb * V + vt * BV) * K, K, sHt, PK, BV, tid);
+    if constexpr (NAT)
+      tile_out<T, K, BV, NTH>(reinterpret_cast<T*>(a.hbuf) + cb * K * V + vt * BV, V, sS, PU, K, tid);
+    // R = U - W S for token tile w (rows past the chunk's end are zero)
+    const bool wok = SUB * w + r16 < len;
+    uint4 wv[NGK];
+#pragma unroll
+    for (int q = 0; q < NGK; ++q) {
+      const uint4 x = wf[B][q];
+      wv[q] = uint4{wok ? x.x : 0u, wok ? x.y : 0u, wok ? x.z : 0u, wok ? x.w : 0u};
+    }
+#pragma unroll
+    for (int m = 0; m < CT; ++m) {
+      f32x4 p = zero4();
+      const T* hb = sHt + (SUB * m + r16) * PK + VE * g;
+#pragma unroll
+      for (int q = 0; q < NGK; ++q) mma16B<T>(p, wv[q], *reinterpret_cast<const uint4*>(hb + KG * q));
+      f32x4 rv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = tof(fromf<T>(st[s][i]));
-        sD[B][(tk * SUB + crow(i)) * PS + tv * SUB + ccol()] = fromf<T>(st[s][i]);
+        const float uu = SUB * w + 4 * g + i < len ? tof(uf[B][m][i]) : 0.f;
+        const T x = fromf<T>(uu - p[i]);
+        if constexpr (NAT) sR[(SUB * w + 4 * g + i) * PU + SUB * m + r16] = x;
+        rv[i] = tof(x);
       }
-      st_tile_T<T>(x, sDt + (tv * SUB) * PK + tk * SUB, PK);
+      st_tile_T<T>(rv, sRt + (SUB * m) * PA + SUB * w, PA);
     }
-    lds_barrier();  // operands of chunk c and dS_{c+1} visible
-    // Rbar = F dS+ + Cq^T dO, stored token-contiguous
-    T* Rbt = reinterpret_cast<T*>(a.Rbt) + ((int64_t)c * H + h) * V * CH + vt * BV * CH;
-#pragma unroll
-    for (int r = 0; r < S::RPW; ++r) {
-      const int t = w + 4 * r, ti = t / CT, tv = t - ti * CT;
-      f32x4 acc = zero4();
-      mma_tile<T, true, true>(acc, sF + ti * SUB * PK, PK, 1, sDt + tv * SUB * PK, PK, 1, K);
-      mma_tile<T, true, true>(acc, sCqt + ti * SUB * PA, PA, 1, sdOt + tv * SUB * PA, PA, 1, CH);
-      // rows past the chunk's end are exact zeros (F and Cq vanish there)
-      st_tile_T<T>(acc, Rbt + (tv * SUB) * CH + ti * SUB, CH);
-      st_tile_T<T>(-acc, sRbt + (tv * SUB) * PA + ti * SUB, PA);
-    }
+    fetch_wu(ic<B>{}, c + DEPTH);
     lds_barrier();
-    // dS = diag(exp2 G2_last) dS+ + Qg^T dO - W^T Rbar
+    if constexpr (TRN)
+      tile_out<T, BV, CH, NTH>(reinterpret_cast<T*>(a.RT) + (cb * V + vt * BV) * CH, CH, sRt, PA, BV, tid);
+    if constexpr (NAT)
+      tile_out<T, CH, BV, NTH>(reinterpret_cast<T*>(a.R) + ((int64_t)bos * H + h) * V + vt * BV, gsV, sR,
+                               PU, len, tid);
+    // S = diag(exp2 G2_last) S + F^T R
 #pragma unroll
-    for (int s = 0; s < S::TPW; ++s) {
-      const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
+    for (int j = 0; j < KW; ++j) {
+      f32x4 d;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[s][i] *= sLam[tk * SUB + crow(i)];
-      mma_tile<T, true, true>(st[s], sQgt + tk * SUB * PA, PA, 1, sdOt + tv * SUB * PA, PA, 1, CH);
-      mma_tile<T, true, true>(st[s], sWt + tk * SUB * PA, PA, 1, sRbt + tv * SUB * PA, PA, 1, CH);
+      for (int i = 0; i < 4; ++i) d[i] = fexp2(lam[B][j][i]);
+#pragma unroll
+      for (int m = 0; m < CW; ++m) {
+        const T* rb = sRt + (SUB * vtile(m) + r16) * PA + VE * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[j][m][i] *= d[i];
+#pragma unroll
+        for (int q = 0; q < NGT; ++q) mma16B<T>(st[j][m], ff[B][j][q], *reinterpret_cast<const uint4*>(rb + KG * q));
+      }
     }
-    (void)t0;
-    if (c - 1 >= c0) {
-      lds_barrier();  // every wave is done with chunk c's operands
-      put(ic<B ^ 1>{});
+    fetch_fl(ic<B>{}, c + DEPTH);
+  };
+  // the back edge always follows both steps, so the loop body's memory
+  // operations are the same on every path
+  for (int c = c0;;) {
+    step(ic<0>{}, c);
+    if (++c >= c1) break;
+    step(ic<1>{}, c);
+    if (++c >= c1) break;
+  }
+  if (a.ht) {
+#pragma unroll
+    for (int j = 0; j < KW; ++j)
+#pragma unroll
+      for (int m = 0; m < CW; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = SUB * ktile(j) + 4 * g + i, vv = vt * BV + SUB * vtile(m) + r16;
+          a.ht[(((int64_t)n * H + h) * K + kk) * V + vv] = st[j][m][i];
+        }
+  }
+}
+
+// Reverse scan, organised like the forward one: wave w owns token tile w of
+// Rbar and a set of key tiles of dS; F rows, Cq^T rows, Qg^T rows and W^T rows
+// go straight from global memory into operand registers; dS_{c+1}, dO_c
+// (transposed) and Rbar_c pass through LDS.
+template <typename T, int K, int V, int BV>
+__global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
+  constexpr int NTH = 256, DEPTH = 2;
+  constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE;
+  constexpr int CT = BV / SUB, NKT = K / SUB;
+  constexpr int NGK = K / KG, NGT = CH / KG;
+  constexpr bool WIDE = NKT >= 4;
+  constexpr int KW = WIDE ? NKT / 4 : 1, CW = WIDE ? CT : CT * NKT / 4;
+  static_assert(WIDE || (NKT == 2 && CT == 2), "state tile split");
+  constexpr int PK = pitch<T>(K), PA = pitch<T>(CH), PS = pitch<T>(BV);
+  // dO rows as staged by the threads: 8-byte pieces (4 elements)
+  constexpr int OE = 8 / (int)sizeof(T), OPER = BV / OE;
+  constexpr int ON = CH * BV * (int)sizeof(T) / (NTH * 8);  // dO pieces per thread
+  static_assert(ON >= 1 && CH * BV * (int)sizeof(T) == NTH * 8 * ON, "dO staging split");
+  __shared__ __align__(16) T sDt[BV * PK];      // dS_{c+1} as operand, [v][k]
+  __shared__ __align__(16) T sD[K * PS];        // dS_{c+1}, natural layout
+  __shared__ __align__(16) T sOt[2][BV * PA];   // dO_c as operand, [v][j]
+  __shared__ __align__(16) T sRbt[BV * PA];     // Rbar_c as operand, [v][i]
+
+  const int H = a.H;
+  const int u = blockIdx.x, vt = blockIdx.y;
+  const int n = u / H, h = u - n * H;
+  const int w = wave_id(), tid = threadIdx.x, l = lane_id();
+  const int r16 = l & 15, g = l >> 4;
+  const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
+  const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
+  const int seq_bos = a.cu ? a.cu[n] : n * a.T, seq_eos = a.cu ? a.cu[n + 1] : (n + 1) * a.T;
+  auto ktile = [&](int j) { return WIDE ? w + 4 * j : w % NKT; };
+  auto vtile = [&](int m) { return WIDE ? m : (w / NKT) * CW + m; };
+
+  uint4 ff[DEPTH][NGK];      // F row 16 w + r16 (keys)
+  uint4 cf[DEPTH][NGT];      // Cq^T row 16 w + r16 (tokens j)
+  uint4 qf[DEPTH][KW][NGT];  // Qg^T row 16 ktile + r16 (tokens)
+  uint4 wf[DEPTH][KW][NGT];  // W^T row 16 ktile + r16 (tokens)
+  f32x4 lam[DEPTH][KW];
+  uint2 of[DEPTH][ON];       // dO pieces
+  // chunks are walked from the last; before the first one the first is read
+  // again (valid memory, never used)
+  auto chunk_of = [&](int c) { return max(c, c0); };
+  auto fetch = [&](auto set, int c) {
+    constexpr int B = decltype(set)::value;
+    const int cc = chunk_of(c);
+    const int bos = seq_bos + (cc - c0) * CH, len = min(CH, seq_eos - bos);
+    const int64_t cb = (int64_t)cc * H + h;
+    const int row = SUB * w + r16;
+    const T* fp = reinterpret_cast<const T*>(a.F) + ((int64_t)bos * H + h) * K +
+                  (int64_t)min(row, len - 1) * gsK + VE * g;
+#pragma unroll
+    for (int q = 0; q < NGK; ++q) ff[B][q] = *reinterpret_cast<const uint4*>(fp + KG * q);
+    const T* cp = reinterpret_cast<const T*>(a.Cqt) + (cb * CH + row) * CH + VE * g;
+#pragma unroll
+    for (int q = 0; q < NGT; ++q) cf[B][q] = *reinterpret_cast<const uint4*>(cp + KG * q);
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      const int kr = SUB * ktile(j);
+      const T* qp = reinterpret_cast<const T*>(a.Qgt) + (cb * K + kr + r16) * CH + VE * g;
+      const T* wp = reinterpret_cast<const T*>(a.Wt) + (cb * K + kr + r16) * CH + VE * g;
+#pragma unroll
+      for (int q = 0; q < NGT; ++q) {
+        qf[B][j][q] = *reinterpret_cast<const uint4*>(qp + KG * q);
+        wf[B][j][q] = *reinterpret_cast<const uint4*>(wp + KG * q);
+      }
+      lam[B][j] = *reinterpret_cast<const f32x4*>(a.glast + cb * K + kr + 4 * g);
+    }
+    const T* op = reinterpret_cast<const T*>(a.dO) + ((int64_t)bos * H + h) * V + vt * BV;
+#pragma unroll
+    for (int e = 0; e < ON; ++e) {
+      const int idx = tid + e * NTH, r = idx / OPER, c8 = (idx % OPER) * OE;
+      of[B][e] = *reinterpret_cast<const uint2*>(op + (int64_t)min(r, len - 1) * gsV + c8);
     }
   };
-  for (int c = c1 - 1; c >= c0; c -= 2) {
-    step(ic<0>{}, c);
-    if (c - 1 >= c0) step(ic<1>{}, c - 1);
-  }
-  lds_barrier();
-  if (c1 > c0) {  // dS_{c0+1}, staged by the last step
-    if ((c1 - 1 - c0) & 1) flush(ic<1>{}, c0);
-    else flush(ic<0>{}, c0);
-  }
-  if (a.dh0) {
+
+  f32x4 st[KW][CW];
 #pragma unroll
-    for (int s = 0; s < S::TPW; ++s) {
-      const int t = w + 4 * s, tk = t / CT, tv = t - tk * CT;
+  for (int j = 0; j < KW; ++j)
+#pragma unroll
+    for (int m = 0; m < CW; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kk = tk * SUB + crow(i), vv = vt * BV + tv * SUB + ccol();
-        a.dh0[(((int64_t)n * H + h) * K + kk) * V + vv] = st[s][i];
+        const int kk = SUB * ktile(j) + 4 * g + i, vv = vt * BV + SUB * vtile(m) + r16;
+        st[j][m][i] = a.dht ? a.dht[(((int64_t)n * H + h) * K + kk) * V + vv] : 0.f;
+      }
+  auto final_out = [&]() {
+    if (a.dh0)
+#pragma unroll
+      for (int j = 0; j < KW; ++j)
+#pragma unroll
+        for (int m = 0; m < CW; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kk = SUB * ktile(j) + 4 * g + i, vv = vt * BV + SUB * vtile(m) + r16;
+            a.dh0[(((int64_t)n * H + h) * K + kk) * V + vv] = st[j][m][i];
+          }
+  };
+  if (c0 >= c1) {
+    final_out();
+    return;
+  }
+  static_for<0, DEPTH>([&](auto B) { fetch(B, c1 - 1 - B); });
+
+  auto step = [&](auto buf, int c) {
+    constexpr int B = decltype(buf)::value;
+    const int bos = seq_bos + (c - c0) * CH, len = min(CH, seq_eos - bos);
+    const int64_t cb = (int64_t)c * H + h;
+    // dS_{c+1}: operand [v][k] and natural [k][v]; dO_c transposed (rows past
+    // the chunk's end zero)
+#pragma unroll
+    for (int j = 0; j < KW; ++j)
+#pragma unroll
+      for (int m = 0; m < CW; ++m) {
+        const int kr = SUB * ktile(j), vc = SUB * vtile(m);
+        f32x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const T y = fromf<T>(st[j][m][i]);
+          x[i] = tof(y);
+          sD[(kr + 4 * g + i) * PS + vc + r16] = y;
+        }
+        st_tile_T<T>(x, sDt + vc * PK + kr, PK);
+      }
+#pragma unroll
+    for (int e = 0; e < ON; ++e) {
+      const int idx = tid + e * NTH, r = idx / OPER, c8 = (idx % OPER) * OE;
+      union {
+        uint2 u;
+        T v[OE];
+      } x;
+      x.u = of[B][e];
+#pragma unroll
+      for (int k = 0; k < OE; ++k) sOt[B][(c8 + k) * PA + r] = r < len ? x.v[k] : fromf<T>(0.f);
+    }
+    lds_barrier();
+    tile_out<T, K, BV, NTH>(reinterpret_cast<T*>(a.dhbuf) + cb * K * V + vt * BV, V, sD, PS, K, tid);
+    // Rbar = F dS+ + Cq^T dO for token tile w (F rows past the end are zero)
+    const bool fok = SUB * w + r16 < len;
+    uint4 fv[NGK];
+#pragma unroll
+    for (int q = 0; q < NGK; ++q) {
+      const uint4 x = ff[B][q];
+      fv[q] = uint4{fok ? x.x : 0u, fok ? x.y : 0u, fok ? x.z : 0u, fok ? x.w : 0u};
+    }
+#pragma unroll
+    for (int m = 0; m < CT; ++m) {
+      f32x4 acc = zero4();
+      const T* db = sDt + (SUB * m + r16) * PK + VE * g;
+      const T* ob = sOt[B] + (SUB * m + r16) * PA + VE * g;
+#pragma unroll
+      for (int q = 0; q < NGK; ++q) mma16B<T>(acc, fv[q], *reinterpret_cast<const uint4*>(db + KG * q));
+#pragma unroll
+      for (int q = 0; q < NGT; ++q) mma16B<T>(acc, cf[B][q], *reinterpret_cast<const uint4*>(ob + KG * q));
+      st_tile_T<T>(acc, sRbt + (SUB * m) * PA + SUB * w, PA);
+    }
+    lds_barrier();
+    tile_out<T, BV, CH, NTH>(reinterpret_cast<T*>(a.Rbt) + (cb * V + vt * BV) * CH, CH, sRbt, PA, BV, tid);
+    // dS = diag(exp2 G2_last) dS+ + Qg^T dO - W^T Rbar (W^T negated by its sign bits)
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      f32x4 d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = fexp2(lam[B][j][i]);
+      uint4 wn[NGT];
+      constexpr unsigned SGN = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
+#pragma unroll
+      for (int q = 0; q < NGT; ++q) {
+        const uint4 x = wf[B][j][q];
+        wn[q] = uint4{x.x ^ SGN, x.y ^ SGN, x.z ^ SGN, x.w ^ SGN};
+      }
+#pragma unroll
+      for (int m = 0; m < CW; ++m) {
+        const T* ob = sOt[B] + (SUB * vtile(m) + r16) * PA + VE * g;
+        const T* rb = sRbt + (SUB * vtile(m) + r16) * PA + VE * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[j][m][i] *= d[i];
+#pragma unroll
+        for (int q = 0; q < NGT; ++q) mma16B<T>(st[j][m], qf[B][j][q], *reinterpret_cast<const uint4*>(ob + KG * q));
+#pragma unroll
+        for (int q = 0; q < NGT; ++q) mma16B<T>(st[j][m], wn[q], *reinterpret_cast<const uint4*>(rb + KG * q));
       }
     }
+    fetch(ic<B>{}, c - DEPTH);
+  };
+  for (int c = c1 - 1;;) {
+    step(ic<0>{}, c);
+    if (--c < c0) break;
+    step(ic<1>{}, c);
+    if (--c < c0) break;
   }
+  final_out();
 }
 
 int scan_bv(const Args& a, int f32) {
@@ -381,7 +480,12 @@ static hipError_t fwd_scan_bv(const Args& a, hipStream_t s) {
   case K_ * 1000 + V_:                                                          \
     if constexpr (kv_ok<T, K_, V_>() && V_ >= BV && K_ * BV >= 1024 && \
                   (sizeof(T) == 2 || K_ == 32 || BV == 16)) {                             \
-      hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV>), grid, block, 0, s, a);    \
+      if (a.scan_out == SCAN_NATURAL)                                           \
+        hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV, SCAN_NATURAL>), grid, block, 0, s, a); \
+      else if (a.scan_out == SCAN_TRANSPOSED)                                   \
+        hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV, SCAN_TRANSPOSED>), grid, block, 0, s, a); \
+      else                                                                      \
+        hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV, SCAN_NATURAL | SCAN_TRANSPOSED>), grid, block, 0, s, a); \
       return hipGetLastError();                                                 \
     } else {                                                                    \
       return hipErrorInvalidValue;                                              \
