@@ -40,24 +40,31 @@ struct GateCols {
     c = tid % KC;
     seg = (tid / KC) % NSUB;
   }
-  // raw natural-log gates of rows < n (zero beyond); features [k0, k0 + KC)
+  // raw natural-log gates, features [k0, k0 + KC), of the chunk's n >= 1 rows.
+  // Every load is unconditional: rows past the end read row n - 1 and are
+  // zeroed by prefix_local(), so the loads' wait falls at that first use.
   __device__ __forceinline__ void load(const Args& a, int64_t t0, int h, int n, int K, int k0) {
-    const int H = a.H;
+    const int H = a.H, r0 = seg * RS;
+    if (a.gate == 2) {
+      const float* gp = a.g + (t0 * H + h) * K + k0 + c;
 #pragma unroll
-    for (int r = 0; r < RS; ++r) {
-      const int row = seg * RS + r;
-      float x = 0.f;
-      if (on && row < n) {
-        if (a.gate == 2) x = a.g[((t0 + row) * H + h) * K + k0 + c];
-        else if (a.gate == 1) x = a.g[(t0 + row) * H + h];
-      }
-      G[r] = x;
+      for (int r = 0; r < RS; ++r) G[r] = gp[(int64_t)min(r0 + r, n - 1) * H * K];
+    } else if (a.gate == 1) {
+      const float* gp = a.g + t0 * H + h;
+#pragma unroll
+      for (int r = 0; r < RS; ++r) G[r] = gp[(int64_t)min(r0 + r, n - 1) * H];
+    } else {
+#pragma unroll
+      for (int r = 0; r < RS; ++r) G[r] = 0.f;
     }
   }
-  // G2 = log2(e) * inclusive prefix over the chunk's rows, in two halves around
-  // a barrier the caller places: prefix_local() publishes the segment totals in
-  // sTot [NSUB][KC], prefix_finish() adds the totals of earlier segments.
-  __device__ __forceinline__ void prefix_local(float* sTot) {
+  // G2 = log2(e) * inclusive prefix over the chunk's n rows (rows past the end
+  // add zero), in two halves around a barrier the caller places:
+  // prefix_local() publishes the segment totals in sTot [NSUB][KC],
+  // prefix_finish() adds the totals of earlier segments.
+  __device__ __forceinline__ void prefix_local(float* sTot, int n) {
+#pragma unroll
+    for (int r = 0; r < RS; ++r) G[r] = seg * RS + r < n ? G[r] : 0.f;
 #pragma unroll
     for (int r = 1; r < RS; ++r) G[r] += G[r - 1];
     if (on) sTot[seg * KC + c] = G[RS - 1];

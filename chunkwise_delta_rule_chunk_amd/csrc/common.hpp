@@ -292,7 +292,34 @@ struct Staged {
   }
 };
 
+// The chunk record c read through the scalar data cache (c uniform over the
+// wave).  Records are written by an earlier kernel, and the scalar cache is
+// invalidated at every dispatch.  A scalar load is counted apart from the
+// vector memory counter, so waiting for it does not also wait for every
+// global load and store the wave still has in flight, as waiting for a
+// vector load of the record would.
+__device__ __forceinline__ ChunkInfo load_chunk(const ChunkInfo* p, int c) {
+  static_assert(sizeof(ChunkInfo) == 4 * sizeof(int), "record layout");
+  const auto* q = (const __attribute__((address_space(4))) int*)p + 4 * c;
+  ChunkInfo r;
+  r.seq = q[0];
+  r.bos = q[1];
+  r.len = q[2];
+  r.pos = q[3];
+  return r;
+}
+
 // beta may be stored as bf16 or fp32 independently of the feature dtype.
+// ld_beta_raw() issues the load and returns the element's raw bits; the value
+// is decoded by beta_val() where it is used, so the wait for the load falls
+// there and not at the load.
+__device__ __forceinline__ uint32_t ld_beta_raw(const void* p, int is_f32, int64_t idx) {
+  if (is_f32) return reinterpret_cast<const uint32_t*>(p)[idx];
+  return reinterpret_cast<const uint16_t*>(p)[idx];
+}
+__device__ __forceinline__ float beta_val(uint32_t raw, int is_f32) {
+  return __uint_as_float(is_f32 ? raw : raw << 16);
+}
 __device__ __forceinline__ float ld_beta(const void* p, int is_f32, int64_t idx) {
   return is_f32 ? reinterpret_cast<const float*>(p)[idx]
                 : (float)reinterpret_cast<const bf16*>(p)[idx];

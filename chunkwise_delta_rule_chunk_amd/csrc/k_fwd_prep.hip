@@ -93,22 +93,22 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
   gnx.init(threadIdx.x);
   Staged<T, CH, K, NTH> pk, pq;
   Staged<T, CH, V, NTH> pv;
-  float pbeta = 0.f;
+  uint32_t pbeta = 0u;  // raw bits of the next item's beta for row tid
   // the next item's inputs: k, q, v and beta as soon as the current ones are in
   // LDS, the gates once the current gates are consumed
   auto fetch_kqv = [&](int item, int tid) {
     const int c = item / H, h = item - c * H;
-    const ChunkInfo ci = a.chunks[c];
+    const ChunkInfo ci = load_chunk(a.chunks, c);
     if (ci.len == 0) return;
     const int64_t t0 = ci.bos;
     pk.load(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, gsK, ci.len, tid);
     pq.load(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, gsK, ci.len, tid);
     pv.load(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, gsV, ci.len, tid);
-    pbeta = tid < ci.len ? ld_beta(a.beta, a.beta_f32, (t0 + tid) * H + h) : 0.f;
+    pbeta = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, ci.len - 1)) * H + h);
   };
   auto fetch_g = [&](int item) {
     const int c = item / H, h = item - c * H;
-    const ChunkInfo ci = a.chunks[c];
+    const ChunkInfo ci = load_chunk(a.chunks, c);
     if (ci.len == 0) return;
     gnx.load(a, (int64_t)ci.bos, h, ci.len, K, 0);
   };
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int tid = opaque_tid(), w = wave_id();
     const int c = item / H, h = item - c * H;
-    const ChunkInfo ci = a.chunks[c];
+    const ChunkInfo ci = load_chunk(a.chunks, c);
     const int n = ci.len;
     if (n == 0) {  // uniform: nothing was fetched for this slot
       if (item + (int)gridDim.x < total) {
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     // ---- S0: staged inputs into LDS, local gate prefix ----------------------
     pk.store(sK, PK, tid);
     pq.store(sQ, PK, tid);
-    if (tid < CH) sBeta[tid] = pbeta;
+    if (tid < CH) sBeta[tid] = tid < n ? beta_val(pbeta, a.beta_f32) : 0.f;
     if (tid < NSUB) sFlag[tid] = 0;
     for (int idx = tid; idx < CH * PL / 4; idx += NTH) {
       reinterpret_cast<f32x4*>(sL)[idx] = zero4();
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     }
 #pragma unroll
     for (int r = 0; r < RS; ++r) gc.G[r] = gnx.G[r];
-    gc.prefix_local(sTot);
+    gc.prefix_local(sTot, n);
     lds_barrier();
 
     // ---- S1: finish the prefix, Z^T from the staged v, statistics ------------
