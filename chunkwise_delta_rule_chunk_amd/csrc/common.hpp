@@ -309,6 +309,86 @@ __device__ __forceinline__ ChunkInfo load_chunk(const ChunkInfo* p, int c) {
   return r;
 }
 
+// ---- bounds-checked global access ------------------------------------------
+// A buffer resource over [base, base + bytes): the hardware range check makes
+// an access at an offset >= bytes read zeros and drops a store there, so an
+// access guarded per lane (rows past a chunk's end) is one unconditional
+// instruction.  Unconditional memory instructions keep the compiler's count
+// of outstanding vector memory operations exact, so a use waits for its own
+// load only and not for every load and store still in flight.
+constexpr uint32_t OOB = 0x80000000u;  // an offset beyond every range used here
+struct GBuf {
+  __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ GBuf gbuf(const void* base, uint32_t bytes) {
+  // 0x00020000: raw (unswizzled, unformatted) 32-bit-element buffer on gfx9
+  return GBuf{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000)};
+}
+// Bytes spanned by nrows rows (stride rs elements) whose first cols elements
+// are in range.
+template <typename T>
+__device__ __forceinline__ uint32_t tile_bytes(int nrows, int64_t rs, int cols) {
+  return nrows <= 0 ? 0u : (uint32_t)(((int64_t)(nrows - 1) * rs + cols) * (int64_t)sizeof(T));
+}
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 gld16(const GBuf& b, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b.r, off, 0, 0);
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ uint2 gld8(const GBuf& b, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(b.r, off, 0, 0);
+  return uint2{v[0], v[1]};
+}
+__device__ __forceinline__ uint32_t gld4(const GBuf& b, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(b.r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t gld2(const GBuf& b, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(b.r, off, 0, 0);
+}
+__device__ __forceinline__ void gst16(const GBuf& b, uint32_t off, uint4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, b.r, off, 0, 0);
+}
+__device__ __forceinline__ void gst8(const GBuf& b, uint32_t off, uint2 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{x.x, x.y}, b.r, off, 0, 0);
+}
+__device__ __forceinline__ void gst4(const GBuf& b, uint32_t off, uint32_t x) {
+  __builtin_amdgcn_raw_buffer_store_b32(x, b.r, off, 0, 0);
+}
+__device__ __forceinline__ void gst2(const GBuf& b, uint32_t off, uint32_t x) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)x, b.r, off, 0, 0);
+}
+
+// A [ROWS x COLS] tile read into registers with one unconditional 16-byte load
+// per piece (rows out of the buffer's range read as zero), then written to
+// LDS: every load of the tile is issued before the first LDS write waits.
+template <typename T, int ROWS, int COLS, int NTH>
+struct TileRegs {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int PER = COLS / VEC;
+  static constexpr int TOTAL = ROWS * PER;
+  static constexpr int N = (TOTAL + NTH - 1) / NTH;
+  static_assert(COLS % VEC == 0, "row length must be a multiple of 16 bytes");
+  uint4 r[N];
+  // tile rows at stride gs elements from the buffer's base
+  __device__ __forceinline__ void load(const GBuf& b, int64_t gs, int tid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = tid + j * NTH;
+      const int row = idx / PER, c = (idx - row * PER) * VEC;
+      r[j] = gld16(b, idx < TOTAL ? (uint32_t)(((int64_t)row * gs + c) * (int64_t)sizeof(T)) : OOB);
+    }
+  }
+  __device__ __forceinline__ void store(T* s, int ls, int tid) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = tid + j * NTH;
+      const int row = idx / PER, c = (idx - row * PER) * VEC;
+      if (idx < TOTAL) *reinterpret_cast<uint4*>(s + row * ls + c) = r[j];
+    }
+  }
+};
+
 // beta may be stored as bf16 or fp32 independently of the feature dtype.
 // ld_beta_raw() issues the load and returns the element's raw bits; the value
 // is decoded by beta_val() where it is used, so the wait for the load falls

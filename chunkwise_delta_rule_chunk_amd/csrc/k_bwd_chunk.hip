@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
 
   const int H = a.H;
   const int c = blockIdx.x / H, h = blockIdx.x - c * H;
-  const ChunkInfo ci = a.chunks[c];
+  const ChunkInfo ci = load_chunk(a.chunks, c);
   const int n = ci.len;
   if (n == 0) return;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
@@ -83,12 +83,22 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   T* sAt = reinterpret_cast<T*>(sX);
   float* sDiag = reinterpret_cast<float*>(sX) + w * 2 * SUB * PD;  // [D_II | Hq_II], this wave
 
-  // ---- loads ---------------------------------------------------------------
-  g2s<T, V>(sO, PV, reinterpret_cast<const T*>(a.dO) + (t0 * H + h) * V, gsV, n, CH, tid, NTH);
-  g2s<T, V>(sR, PV, reinterpret_cast<const T*>(a.R) + (t0 * H + h) * V, gsV, n, CH, tid, NTH);
-  g2s<T, CH>(sAt, PA, reinterpret_cast<const T*>(a.At) + cb * CH * CH, CH, CH, CH, tid, NTH);
-  if (tid < CH) sBeta[tid] = tid < n ? ld_beta(a.beta, a.beta_f32, (t0 + tid) * H + h) : 0.f;
-  lds_barrier();
+  // ---- loads: every read of the first phase is issued before the first wait.
+  // Rows past the chunk's end read as zero (bounds-checked buffer loads).
+  const GBuf bv = gbuf(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, tile_bytes<T>(n, gsV, V));
+  const int k0a = (I * SUB / KS) * KS;  // A^T is upper triangular: tokens j >= 16 I
+  {
+    TileRegs<T, CH, V, NTH> pO, pR;
+    TileRegs<T, CH, CH, NTH> pA;
+    pO.load(gbuf(reinterpret_cast<const T*>(a.dO) + (t0 * H + h) * V, tile_bytes<T>(n, gsV, V)), gsV, tid);
+    pR.load(gbuf(reinterpret_cast<const T*>(a.R) + (t0 * H + h) * V, tile_bytes<T>(n, gsV, V)), gsV, tid);
+    pA.load(gbuf(reinterpret_cast<const T*>(a.At) + cb * CH * CH, CH * CH * sizeof(T)), CH, tid);
+    const uint32_t braw = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, n - 1)) * H + h);
+    pO.store(sO, PV, tid);
+    pR.store(sR, PV, tid);
+    pA.store(sAt, PA, tid);
+    if (tid < CH) sBeta[tid] = tid < n ? beta_val(braw, a.beta_f32) : 0.f;
+  }
 
   // ---- P = A^T Rbar, rows of block I; dv and the write part of dbeta --------
   // The tile computed is P^T (rows v, columns i): its C fragment gives lane l
@@ -97,21 +107,33 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   // sweep (whole rows reach the cache together and leave it as full lines).
   {
     const T* Rbt = reinterpret_cast<const T*>(a.Rbt) + cb * V * CH;
-    const T* vg = reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V;
-    T* dvg = reinterpret_cast<T*>(a.dv) + (t0 * H + h) * V;
-    const int k0 = (I * SUB / KS) * KS;  // A^T is upper triangular: tokens j >= 16 I
+    const GBuf bdv = gbuf(reinterpret_cast<T*>(a.dv) + (t0 * H + h) * V, tile_bytes<T>(n, gsV, V));
+    const int k0 = k0a;
     const int i = I * SUB + f;
+    // this lane's four values of v in each value block (zero past the end)
+    using VR = std::conditional_t<std::is_same_v<T, bf16>, uint2, uint4>;
+    VR vr[NVB];
+    static_for<0, NVB>([&](auto vb) {
+      const uint32_t off = (uint32_t)(((int64_t)i * gsV + vb * SUB + 4 * q4) * (int64_t)sizeof(T));
+      if constexpr (std::is_same_v<T, bf16>) vr[vb] = gld8(bv, off);
+      else vr[vb] = gld16(bv, off);
+    });
     f32x4 acc[NVB];
     if constexpr (std::is_same_v<T, bf16>) {
-      // bf16: at most two 32-token steps; every Rbar fragment is requested up front
+      // bf16: at most two 32-token steps; every Rbar fragment is requested up
+      // front (unused steps read as zero)
+      const GBuf brb = gbuf(Rbt, V * CH * sizeof(T));
       bf16x8 rb[NVB][2];
       static_for<0, NVB>([&](auto vb) {
         static_for<0, 2>([&](auto st) {
-          rb[vb][st] = bf16x8{};
-          if (live && st * 32 >= k0)
-            rb[vb][st] = ldfrag<T, true>(Rbt + vb * SUB * CH, CH, 1, st * 32);
+          const uint32_t off = (live && st * 32 >= k0)
+                                   ? (uint32_t)(((vb * SUB + f) * CH + st * 32 + 8 * q4) * sizeof(T))
+                                   : OOB;
+          const uint4 x = gld16(brb, off);
+          rb[vb][st] = __builtin_bit_cast(bf16x8, x);
         });
       });
+      lds_barrier();
       const bf16x8 at0 = ldfrag<T, true>(sAt + I * SUB * PA, PA, 1, 0);
       const bf16x8 at1 = ldfrag<T, true>(sAt + I * SUB * PA, PA, 1, 32);
       static_for<0, NVB>([&](auto vb) {
@@ -119,6 +141,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         if (k0 == 0) acc[vb] = mma(rb[vb][0], at0, acc[vb]);
       });
     } else {
+      lds_barrier();
       static_for<0, NVB>([&](auto vb) {
         acc[vb] = zero4();
         if (live)
@@ -131,23 +154,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
     static_for<0, NVB>([&](auto vb) {
       const int v0 = vb * SUB + 4 * q4;
       *reinterpret_cast<FR*>(sP + i * PV + v0) = to_frag<T>(acc[vb]);
-      if (i < n) {
-        if constexpr (std::is_same_v<T, bf16>) {
-          const bf16x4 x = *reinterpret_cast<const bf16x4*>(vg + i * gsV + v0);
+      const FR x = __builtin_bit_cast(FR, vr[vb]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dbw += (float)x[e] * acc[vb][e];
-        } else {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(vg + i * gsV + v0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dbw += x[e] * acc[vb][e];
-        }
-      }
+      for (int e = 0; e < 4; ++e) dbw += tof(x[e]) * acc[vb][e];
     });
-    if (i < n)
-      static_for<0, NVB>([&](auto vb) {
-        const int v0 = vb * SUB + 4 * q4;
-        *reinterpret_cast<FR*>(dvg + i * gsV + v0) = to_frag<T>(b * acc[vb]);
-      });
+    // rows past the chunk's end fall outside the buffer and are dropped
+    static_for<0, NVB>([&](auto vb) {
+      const uint32_t off = (uint32_t)(((int64_t)i * gsV + vb * SUB + 4 * q4) * (int64_t)sizeof(T));
+      const FR y = to_frag<T>(b * acc[vb]);
+      if constexpr (std::is_same_v<T, bf16>) gst8(bdv, off, __builtin_bit_cast(uint2, y));
+      else gst16(bdv, off, __builtin_bit_cast(uint4, y));
+    });
     dbw += __shfl_xor(dbw, 16);
     dbw += __shfl_xor(dbw, 32);
     if (q4 == 0) sDbw[i] = dbw;
@@ -203,8 +220,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   const T* Ktg = reinterpret_cast<const T*>(a.Kt) + cb * K * CH;
   const T* Qtg = reinterpret_cast<const T*>(a.Qt) + cb * K * CH;
   const float* Gstg = a.Gst + cb * NSUB * K * 4;  // float4 records, [J][K]
-  T* dqg = reinterpret_cast<T*>(a.dq) + (t0 * H + h) * K;
-  T* dkg = reinterpret_cast<T*>(a.dk) + (t0 * H + h) * K;
+  // outputs through bounds-checked buffers: rows past the chunk's end are dropped
+  const GBuf bdq = gbuf(reinterpret_cast<T*>(a.dq) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
+  const GBuf bdk = gbuf(reinterpret_cast<T*>(a.dk) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
+  const GBuf bdg = gbuf(a.dg + (t0 * H + h) * K, a.gate == 2 ? tile_bytes<float>(n, gsK, K) : 0u);
   const int jl = n - 1;  // last valid row
   const FR DmI = pick(Dm, I), HmI = pick(Hm, I), DtmI = pick(Dtm, I), HtmI = pick(Htm, I);
   const f32x4 bI = *reinterpret_cast<const f32x4*>(sBeta + I * SUB + 4 * q4);
@@ -213,21 +232,24 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   float pdq[4] = {0.f, 0.f, 0.f, 0.f}, pdk[4] = {0.f, 0.f, 0.f, 0.f};
   float lam0s = 0.f, lamws = 0.f;
 
-  // registers of the next block's operands (loaded during this block's products)
-  Staged<float, SUB, CH, NTH> pG;
-  Staged<T, SUB, CH, NTH> pK, pQ;
-  Staged<float, NSUB, SUB * 4, NTH> pX;
-  Staged<T, SUB, V, NTH> pS, pD;
-  Staged<float, 1, SUB, NTH> pN;
+  // registers of the next block's operands (loaded during this block's
+  // products).  Every load is unconditional: a scalar gate has one G2 row
+  // (the others read as zero) and no gate reads none.
+  TileRegs<float, SUB, CH, NTH> pG;
+  TileRegs<T, SUB, CH, NTH> pK, pQ;
+  TileRegs<float, NSUB, SUB * 4, NTH> pX;
+  TileRegs<T, SUB, V, NTH> pS, pD;
+  TileRegs<float, 1, SUB, NTH> pN;
   auto fetch_fb = [&](int fb) {
-    if (a.gate == 2) pG.load(a.G2t + (cb * K + fb * SUB) * CH, CH, SUB, tid);
-    else if (a.gate == 1) pG.load(a.G2t + cb * CH, CH, 1, tid);
-    pK.load(Ktg + (int64_t)fb * SUB * CH, CH, SUB, tid);
-    pQ.load(Qtg + (int64_t)fb * SUB * CH, CH, SUB, tid);
-    pX.load(Gstg + fb * SUB * 4, K * 4, NSUB, tid);
-    pS.load(hb + (int64_t)fb * SUB * V, V, SUB, tid);
-    pD.load(dhb + (int64_t)fb * SUB * V, V, SUB, tid);
-    pN.load(a.glast + cb * K + fb * SUB, SUB, 1, tid);
+    const float* gp = a.gate == 2 ? a.G2t + (cb * K + fb * SUB) * CH : a.G2t + cb * CH;
+    const int grows = a.gate == 2 ? SUB : a.gate == 1 ? 1 : 0;
+    pG.load(gbuf(gp, tile_bytes<float>(grows, CH, CH)), CH, tid);
+    pK.load(gbuf(Ktg + (int64_t)fb * SUB * CH, SUB * CH * sizeof(T)), CH, tid);
+    pQ.load(gbuf(Qtg + (int64_t)fb * SUB * CH, SUB * CH * sizeof(T)), CH, tid);
+    pX.load(gbuf(Gstg + fb * SUB * 4, tile_bytes<float>(NSUB, K * 4, SUB * 4)), K * 4, tid);
+    pS.load(gbuf(hb + (int64_t)fb * SUB * V, SUB * V * sizeof(T)), V, tid);
+    pD.load(gbuf(dhb + (int64_t)fb * SUB * V, SUB * V * sizeof(T)), V, tid);
+    pN.load(gbuf(a.glast + cb * K + fb * SUB, SUB * sizeof(float)), SUB, tid);
   };
   auto put_fb = [&]() {
     if (a.gate != 0) pG.store(sG2, PGS, tid);
@@ -246,13 +268,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   for (int fb = 0; fb < NFB; ++fb) {
     const int kc = fb * SUB + f;  // this lane's feature
     const int buf = fb & 1;
-    if (fb + 1 < NFB) fetch_fb(fb + 1);
+    fetch_fb(min(fb + 1, NFB - 1));  // the last block reads itself again, unused
     // first row of this lane, opaque per iteration: the output addresses derived
     // from it are recomputed rather than kept live (and spilled) across blocks
     int lrow = I * SUB + 4 * q4;
     asm volatile("" : "+v"(lrow));
     f32x4 gbar = zero4();
     float lamw = 0.f, l0 = 0.f;
+    float oq[4] = {0.f, 0.f, 0.f, 0.f}, ok_[4] = {0.f, 0.f, 0.f, 0.f};  // dq, dk of this block
     if (live) {
       // gated operands of all four blocks at this lane's rows 16 J + 4 q4 + e
       // (k and q stay packed in their storage type until used)
@@ -419,17 +442,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
           const float XE = -gam * SE[e] + XDY[e];
           const float XY = XDE[e] + XHQ[e] + SF[e] * tail[e];
           const float kv = kI[e], qv = qI[e], b = bI[e];
-          // dq, dk of an even feature block wait for the next block, so that
-          // both halves of each 64-byte row segment are written together
-          if ((fb & 1) == 0) {
-            pdq[e] = scale * XQ;
-            pdk[e] = b * XE + XY;
-          } else {
-            dqg[row * gsK + kc - SUB] = fromf<T>(pdq[e]);
-            dqg[row * gsK + kc] = fromf<T>(scale * XQ);
-            dkg[row * gsK + kc - SUB] = fromf<T>(pdk[e]);
-            dkg[row * gsK + kc] = fromf<T>(b * XE + XY);
-          }
+          oq[e] = scale * XQ;
+          ok_[e] = b * XE + XY;
           gbar[e] = scale * qv * XQ + b * kv * XE - kv * XY;
           dbe[e] += kv * XE;
           lamw += kv * SF[e] * tail[e];
@@ -437,6 +451,31 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       }
       lamw += __shfl_xor(lamw, 16);
       lamw += __shfl_xor(lamw, 32);
+    }
+    // dq, dk of an even feature block wait for the next block, so that both
+    // halves of each 64-byte row segment are written together; the stores are
+    // issued in every block (even blocks and rows past the end fall outside
+    // the buffers and are dropped), which keeps the loop's memory operations
+    // the same on every path
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = lrow + e;
+      const bool odd = fb & 1;
+      const uint32_t o1 = odd ? (uint32_t)(((int64_t)row * gsK + kc - SUB) * (int64_t)sizeof(T)) : OOB;
+      const uint32_t o2 = odd ? (uint32_t)(((int64_t)row * gsK + kc) * (int64_t)sizeof(T)) : OOB;
+      if constexpr (std::is_same_v<T, bf16>) {
+        gst2(bdq, o1, __builtin_bit_cast(uint16_t, fromf<T>(pdq[e])));
+        gst2(bdq, o2, __builtin_bit_cast(uint16_t, fromf<T>(oq[e])));
+        gst2(bdk, o1, __builtin_bit_cast(uint16_t, fromf<T>(pdk[e])));
+        gst2(bdk, o2, __builtin_bit_cast(uint16_t, fromf<T>(ok_[e])));
+      } else {
+        gst4(bdq, o1, __float_as_uint(pdq[e]));
+        gst4(bdq, o2, __float_as_uint(oq[e]));
+        gst4(bdk, o1, __float_as_uint(pdk[e]));
+        gst4(bdk, o2, __float_as_uint(ok_[e]));
+      }
+      pdq[e] = oq[e];
+      pdk[e] = ok_[e];
     }
     if (a.gate == 2) {
       // in-block reverse sum: own rows, then the lane groups after this one
@@ -457,19 +496,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         sLam[buf][I * SUB + f] = lamw;
       }
       lds_barrier();  // block totals visible; this block's operands are no longer read
-      if (live) {
-        float add = l0;  // endpoint term, added to every row
+      float add = l0;  // endpoint term, added to every row
 #pragma unroll
-        for (int J = 0; J < NSUB; ++J) {
-          add += sLam[buf][J * SUB + f];
-          if (J > I) add += sTot[buf][J * SUB + f];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = lrow + e;
-          if (row < n) a.dg[((t0 + row) * H + h) * K + kc] = suf[e] + add;
-        }
+      for (int J = 0; J < NSUB; ++J) {
+        add += sLam[buf][J * SUB + f];
+        if (J > I) add += sTot[buf][J * SUB + f];
       }
+      // rows past the end (all rows of a wave past the end) are dropped
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        gst4(bdg, (uint32_t)(((int64_t)(lrow + e) * gsK + kc) * 4), __float_as_uint(suf[e] + add));
     } else if (a.gate == 1 && live) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -493,7 +529,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       lam0s += y;
     }
     if (a.gate != 2) lds_barrier();  // this block's operands are no longer read
-    if (fb + 1 < NFB) put_fb();
+    put_fb();                        // after the last block: unused
     lds_barrier();                   // the next block's operands are visible
   }
 

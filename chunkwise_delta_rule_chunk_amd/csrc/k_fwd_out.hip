@@ -14,33 +14,40 @@ __global__ __launch_bounds__(256) void k_fwd_out(Args a) {
   __shared__ __align__(16) T sRt[V * PA];  // R as operand, [v][i]
 
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const ChunkInfo ci = a.chunks[c];
+  const ChunkInfo ci = load_chunk(a.chunks, c);
   const int len = ci.len;
   if (len == 0) return;
   const int H = a.H;
-  const int64_t t0 = ci.bos;
+  const int64_t t0 = ci.bos, cb = (int64_t)c * H + h;
   const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
-  g2s<T, K>(sQg, PK, reinterpret_cast<const T*>(a.Qg) + (t0 * H + h) * K, gsK, len, CH, tid, 256);
-  // S_c^T and R^T tiles, written transposed by the forward scan
-  g2s<T, K>(sHt, PK, reinterpret_cast<const T*>(a.hbufT) + ((int64_t)c * H + h) * V * K, K, V, V,
-            tid, 256);
-  g2s<T, CH>(sCq, PA, reinterpret_cast<const T*>(a.Cq) + ((int64_t)c * H + h) * CH * CH, CH, CH,
-             CH, tid, 256);
-  g2s<T, CH>(sRt, PA, reinterpret_cast<const T*>(a.RT) + ((int64_t)c * H + h) * V * CH, CH, V, V,
-             tid, 256);
+  // all four tiles are read before the first LDS write waits; Qg rows past
+  // the chunk's end read as zero.  S_c^T and R^T were written transposed by
+  // the forward scan.
+  TileRegs<T, CH, K, 256> pq;
+  TileRegs<T, V, K, 256> ph;
+  TileRegs<T, CH, CH, 256> pc;
+  TileRegs<T, V, CH, 256> pr;
+  pq.load(gbuf(reinterpret_cast<const T*>(a.Qg) + (t0 * H + h) * K, tile_bytes<T>(len, gsK, K)), gsK, tid);
+  ph.load(gbuf(reinterpret_cast<const T*>(a.hbufT) + cb * V * K, V * K * sizeof(T)), K, tid);
+  pc.load(gbuf(reinterpret_cast<const T*>(a.Cq) + cb * CH * CH, CH * CH * sizeof(T)), CH, tid);
+  pr.load(gbuf(reinterpret_cast<const T*>(a.RT) + cb * V * CH, V * CH * sizeof(T)), CH, tid);
+  pq.store(sQg, PK, tid);
+  ph.store(sHt, PK, tid);
+  pc.store(sCq, PA, tid);
+  pr.store(sRt, PA, tid);
   lds_barrier();
   T* og = reinterpret_cast<T*>(a.o) + (t0 * H + h) * V;
   const int w = wave_id();
-  for (int cb = w; cb < V / SUB; cb += 4) {
+  for (int vb = w; vb < V / SUB; vb += 4) {
     static_for<0, NSUB>([&](auto II) {
       constexpr int I = decltype(II)::value;
       if (I * SUB >= len) return;
       f32x4 acc = zero4();
-      mma_tile<T, true, true>(acc, sQg + I * SUB * PK, PK, 1, sHt + cb * SUB * PK, PK, 1, K);
+      mma_tile<T, true, true>(acc, sQg + I * SUB * PK, PK, 1, sHt + vb * SUB * PK, PK, 1, K);
       // Cq is lower triangular: row block I needs tokens < 16 (I + 1) only
       constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
-      mma_tile<T, true, true>(acc, sCq + I * SUB * PA, PA, 1, sRt + cb * SUB * PA, PA, 1, kd);
-      st_tile<T>(acc, og + (I * SUB) * gsV + cb * SUB, (int)gsV, 1, len - I * SUB);
+      mma_tile<T, true, true>(acc, sCq + I * SUB * PA, PA, 1, sRt + vb * SUB * PA, PA, 1, kd);
+      st_tile<T>(acc, og + (I * SUB) * gsV + vb * SUB, (int)gsV, 1, len - I * SUB);
     });
   }
 }
