@@ -101,6 +101,31 @@ constexpr bool kv_ok() {
       return hipErrorInvalidValue;                                                \
     }
 
+// The same with one more template argument after (T, K, V).
+#define REWY_KV_CASE_X(KERNEL, X, K_, V_)                                         \
+  case K_ * 1000 + V_:                                                            \
+    if constexpr (kv_ok<T, K_, V_>()) {                                           \
+      hipLaunchKernelGGL((KERNEL<T, K_, V_, X>), grid, block, 0, s, a);           \
+      return hipGetLastError();                                                   \
+    } else {                                                                      \
+      return hipErrorInvalidValue;                                                \
+    }
+
+#define REWY_KV_SWITCH_X(KERNEL, X)                                               \
+  switch (a.K * 1000 + a.V) {                                                     \
+    REWY_KV_CASE_X(KERNEL, X, 32, 32)                                             \
+    REWY_KV_CASE_X(KERNEL, X, 32, 64)                                             \
+    REWY_KV_CASE_X(KERNEL, X, 32, 128)                                            \
+    REWY_KV_CASE_X(KERNEL, X, 64, 32)                                             \
+    REWY_KV_CASE_X(KERNEL, X, 64, 64)                                             \
+    REWY_KV_CASE_X(KERNEL, X, 64, 128)                                            \
+    REWY_KV_CASE_X(KERNEL, X, 128, 32)                                            \
+    REWY_KV_CASE_X(KERNEL, X, 128, 64)                                            \
+    REWY_KV_CASE_X(KERNEL, X, 128, 128)                                           \
+    default:                                                                      \
+      return hipErrorInvalidValue;                                                \
+  }
+
 #define REWY_KV_SWITCH(KERNEL)                                                    \
   switch (a.K * 1000 + a.V) {                                                     \
     REWY_KV_CASE(KERNEL, 32, 32)                                                  \

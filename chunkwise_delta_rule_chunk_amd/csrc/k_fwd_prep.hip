@@ -60,7 +60,9 @@ hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
 // One persistent workgroup processes chunk-heads item = blockIdx.x + i*gridDim.x
 // (item = chunk * H + head).  The next item's k, q, v, g and beta are read into
 // registers while the current item computes, so HBM latency overlaps compute.
-template <typename T, int K, int V>
+// MODE: the PREP_* sets this launch writes (a compile-time constant, so the
+// loop body holds no flag tests and no pointers of unused outputs).
+template <typename T, int K, int V, int MODE>
 __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
   constexpr int NTH = 512, NW = NTH / 64;
   constexpr bool BF = std::is_same_v<T, bf16>;
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
   __shared__ float sBeta[CH];
   __shared__ int sFlag[NSUB];
 
-  const int H = a.H, mode = a.prep_mode;
+  const int H = a.H;
   const int total = a.nc_max * H;
   const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
 
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     const bool more = item + (int)gridDim.x < total;
     if (more) fetch_kqv(item + gridDim.x, tid);
     subchunk_stats_regs(gc, n, sMid, sGf, sGl, sGn, sFlag,
-                        (mode & PREP_BWD_CHUNK) ? reinterpret_cast<f32x4*>(a.Gst) + cb * NSUB * K
+                        (MODE & PREP_BWD_CHUNK) ? reinterpret_cast<f32x4*>(a.Gst) + cb * NSUB * K
                                                 : nullptr);
     lds_barrier();
 
@@ -195,15 +197,23 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     if (gc.on) {
       // opaque per item: keeps the compiler from hoisting these addresses out of
       // the item loop (they would have to stay live, and spill, across items)
-      int col = gc.c, r0 = gc.seg * RS;
-      asm volatile("" : "+v"(col), "+v"(r0));
+      int col = gc.c;
+      asm volatile("" : "+v"(col));
+      // the thread's 16 rows lie in sub-chunk seg, the same for the whole wave
+      // when a wave spans one segment (K >= 64)
+      const int r0 = K >= 64 ? __builtin_amdgcn_readfirstlane(gc.seg * RS) : gc.seg * RS;
       const float gn = sGn[col];
-      // the thread's 16 rows lie in sub-chunk seg: its references are per thread
-      const float rA = ref_recv(sMid, sGf, sFlag, gc.seg, K, col);
-      const float rB = ref_send(sMid, sGl, sFlag, gc.seg, K, col);
+      // a segment wholly past the chunk's end has no statistics; its rows hold
+      // G2 = gn exactly (the prefix adds zeros there), so gn as both references
+      // makes both factors 1
+      const bool seg_live = r0 < n;
+      const float rA = seg_live ? ref_recv(sMid, sGf, sFlag, gc.seg, K, col) : gn;
+      const float rB = seg_live ? ref_send(sMid, sGl, sFlag, gc.seg, K, col) : gn;
       // two exponentials per row: ea = exp2(G - rA), eb = exp2(rB - G); then
-      // gamma = exp2(G) = ea exp2(rA) and exp2(gn - G) = eb exp2(gn - rB).  Values
-      // that flush to zero this way are below 2^-62 and multiply O(1) terms.
+      // gamma = exp2(G) = ea exp2(rA) and exp2(gn - G) = eb exp2(gn - rB), with
+      // exp2(rA) <= 1 and exp2(gn - rB) <= 1.  Values that flush to zero this
+      // way are below 2^-62 and multiply O(1) terms.  Rows past the chunk's end
+      // hold k = q = beta = 0 and come out as zeros.
       const float cA = fexp2(rA), cB = fexp2(gn - rB);
       const float bs = a.scale;
       constexpr int VE = 16 / (int)sizeof(T);
@@ -211,6 +221,12 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       T* Qgtd = reinterpret_cast<T*>(a.Qgt) + (cb * K + col) * CH + r0;
       T* Ktd = reinterpret_cast<T*>(a.Kt) + (cb * K + col) * CH + r0;
       T* Qtd = reinterpret_cast<T*>(a.Qt) + (cb * K + col) * CH + r0;
+      // natural-layout rows (Qg forward, F reverse) through bounds-checked
+      // buffers: rows past the chunk's end are dropped by the range check
+      const uint32_t natb = tile_bytes<T>(n, gsK, K);
+      const GBuf bQg = gbuf(reinterpret_cast<T*>(a.Qg) + (t0 * H + h) * K, (MODE & PREP_FWD_OUT) ? natb : 0u);
+      const GBuf bF = gbuf(reinterpret_cast<T*>(a.F) + (t0 * H + h) * K, (MODE & PREP_BWD_SCAN) ? natb : 0u);
+      const uint32_t rowb = (uint32_t)(gsK * (int64_t)sizeof(T)), colb = col * (int)sizeof(T);
 #pragma unroll
       for (int r8 = 0; r8 < RS; r8 += VE) {
         union {
@@ -220,25 +236,22 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
           const int r = r8 + e, row = r0 + r;
-          float vKa = 0.f, vQa = 0.f, vKc = 0.f, vE = 0.f, vF = 0.f, vQg = 0.f;
-          kt.e[e] = sK[row * PK + col];  // raw k and q (zero past the chunk's end)
-          qq.e[e] = sQ[row * PK + col];
-          if (row < n) {
-            const float G = gc.G[r];
-            const float kr = tof(sK[row * PK + col]), qr = tof(sQ[row * PK + col]);
-            const float b = sBeta[row];
-            const float ea = fexp2(G - rA), eb = fexp2(rB - G);
-            const float gam = ea * cA;
-            vKa = b * kr * ea;
-            vQa = bs * qr * ea;
-            vKc = kr * eb;
-            vE = b * kr * gam;
-            vF = kr * (eb * cB);
-            vQg = bs * qr * gam;
-            if (mode & PREP_FWD_OUT)
-              reinterpret_cast<T*>(a.Qg)[(t0 + row) * gsK + h * K + col] = fromf<T>(vQg);
-            if (mode & PREP_BWD_SCAN)
-              reinterpret_cast<T*>(a.F)[(t0 + row) * gsK + h * K + col] = fromf<T>(vF);
+          const T kraw = sK[row * PK + col], qraw = sQ[row * PK + col];
+          kt.e[e] = kraw;  // raw k and q (zero past the chunk's end)
+          qq.e[e] = qraw;
+          const float G = gc.G[r];
+          const float kr = tof(kraw), qr = tof(qraw);
+          const float ea = fexp2(G - rA), eb = fexp2(rB - G);
+          const float vKa = sBeta[row] * kr * ea, vQa = bs * qr * ea, vKc = kr * eb;
+          const float vE = vKa * cA, vQg = vQa * cA, vF = vKc * cB;
+          const uint32_t off = colb + (uint32_t)row * rowb;
+          if constexpr (MODE & PREP_FWD_OUT) {
+            if constexpr (sizeof(T) == 2) gst2(bQg, off, __builtin_bit_cast(uint16_t, fromf<T>(vQg)));
+            else gst4(bQg, off, __float_as_uint(vQg));
+          }
+          if constexpr (MODE & PREP_BWD_SCAN) {
+            if constexpr (sizeof(T) == 2) gst2(bF, off, __builtin_bit_cast(uint16_t, fromf<T>(vF)));
+            else gst4(bF, off, __float_as_uint(vF));
           }
           sKa[row * PK + col] = fromf<T>(vKa);
           sQ[row * PK + col] = fromf<T>(vQa);
@@ -249,15 +262,15 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         }
         // token-contiguous tiles: this thread holds consecutive tokens of column col
         *reinterpret_cast<uint4*>(sEt + col * PA + r0 + r8) = et.u;
-        if (mode & PREP_FWD_SCAN) *reinterpret_cast<uint4*>(Ftd + r8) = ft.u;
-        if (mode & PREP_BWD_SCAN) *reinterpret_cast<uint4*>(Qgtd + r8) = qt.u;
-        if (mode & PREP_BWD_CHUNK) {
+        if constexpr (MODE & PREP_FWD_SCAN) *reinterpret_cast<uint4*>(Ftd + r8) = ft.u;
+        if constexpr (MODE & PREP_BWD_SCAN) *reinterpret_cast<uint4*>(Qgtd + r8) = qt.u;
+        if constexpr (MODE & PREP_BWD_CHUNK) {
           *reinterpret_cast<uint4*>(Ktd + r8) = kt.u;
           *reinterpret_cast<uint4*>(Qtd + r8) = qq.u;
         }
       }
       // G2 token-contiguous (rows past the end hold G2 of the last row)
-      if (mode & PREP_BWD_CHUNK) {
+      if constexpr (MODE & PREP_BWD_CHUNK) {
         float* G2d = a.gate == 2 ? a.G2t + (cb * K + col) * CH + r0
                                  : (a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr);
         if (G2d)
@@ -266,7 +279,8 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
             *reinterpret_cast<f32x4*>(G2d + r4) =
                 f32x4{gc.G[r4], gc.G[r4 + 1], gc.G[r4 + 2], gc.G[r4 + 3]};
       }
-      if ((mode & (PREP_FWD_SCAN | PREP_BWD_SCAN)) && gc.seg == 0) a.glast[cb * K + col] = gn;
+      if constexpr ((MODE & (PREP_FWD_SCAN | PREP_BWD_SCAN)) != 0)
+        if (gc.seg == 0) a.glast[cb * K + col] = gn;
     }
     // the gate registers are free: read the next item's gates
     if (more) fetch_g(item + gridDim.x);
@@ -284,8 +298,8 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
           if (row > col) sL[row * PL + col] = accL[i];
           cq[i] = row >= col ? accC[i] : 0.f;
         }
-        if (mode & PREP_FWD_OUT) st_tile<T>(cq, Cqo + (I * SUB) * CH + J * SUB, CH, 1);
-        if (mode & PREP_BWD_SCAN) st_tile_T<T>(cq, Cqto + (J * SUB) * CH + I * SUB, CH);
+        if constexpr (MODE & PREP_FWD_OUT) st_tile<T>(cq, Cqo + (I * SUB) * CH + J * SUB, CH, 1);
+        if constexpr (MODE & PREP_BWD_SCAN) st_tile_T<T>(cq, Cqto + (J * SUB) * CH + I * SUB, CH);
       };
       score_tiles_pre<T, K, true, NW>(sKa, sQ, sK, PK, sFac, sFlag, n, store);
       // wide diagonal sub-chunks: pairwise, one wave each
@@ -299,15 +313,15 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       for (int t = w; t < NSUB * NSUB; t += NW) {
         const int I = t / NSUB, J = t - I * NSUB;
         if (J <= I && I * SUB < n) continue;
-        if (mode & PREP_FWD_OUT) st_tile<T>(zero4(), Cqo + (I * SUB) * CH + J * SUB, CH, 1);
-        if (mode & PREP_BWD_SCAN) st_tile_T<T>(zero4(), Cqto + (J * SUB) * CH + I * SUB, CH);
+        if constexpr (MODE & PREP_FWD_OUT) st_tile<T>(zero4(), Cqo + (I * SUB) * CH + J * SUB, CH, 1);
+        if constexpr (MODE & PREP_BWD_SCAN) st_tile_T<T>(zero4(), Cqto + (J * SUB) * CH + I * SUB, CH);
       }
     }
     lds_barrier();
 
     // ---- S4: A = (I + L)^-1 in fp32 ------------------------------------------
     solve_unit_lower(sL, sA, PL, n);
-    if (mode & PREP_BWD_CHUNK) {  // A^T for the chunk backward, 16-byte rows
+    if constexpr (MODE & PREP_BWD_CHUNK) {  // A^T for the chunk backward, 16-byte rows
       constexpr int VA = 16 / (int)sizeof(T), PER = CH / VA;
       T* Ato = reinterpret_cast<T*>(a.At) + cb * CH * CH;
       for (int idx = tid; idx < CH * PER; idx += NTH) {
@@ -326,7 +340,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     T* Wo = reinterpret_cast<T*>(a.W) + (t0 * H + h) * K;
     T* Uo = reinterpret_cast<T*>(a.U) + (t0 * H + h) * V;
     T* Wto = reinterpret_cast<T*>(a.Wt) + cb * K * CH;
-    const bool wantW = mode & PREP_FWD_SCAN, wantWt = mode & PREP_BWD_SCAN, wantU = wantW;
+    constexpr bool wantW = MODE & PREP_FWD_SCAN, wantWt = MODE & PREP_BWD_SCAN, wantU = wantW;
     const int nblk = (n + SUB - 1) / SUB;
     const int nblkW = wantWt ? NSUB : nblk;  // W^T needs every row block (exact zeros past n)
     if constexpr (BF) {
@@ -389,11 +403,26 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
   }
 }
 
-template <typename T>
-static hipError_t prep_t(const Args& a, hipStream_t s) {
+template <typename T, int MODE>
+static hipError_t prep_m(const Args& a, hipStream_t s) {
   const int items = a.nc_max * a.H;
   const dim3 grid(std::min(items, persistent_grid()), 1), block(512);
-  REWY_KV_SWITCH(k_fwd_prep)
+  REWY_KV_SWITCH_X(k_fwd_prep, MODE)
+}
+
+// The three output sets in use: the forward (recompute policy), the forward
+// that also saves the backward's operands, and the recomputation in the backward.
+template <typename T>
+static hipError_t prep_t(const Args& a, hipStream_t s) {
+  constexpr int FWD = PREP_FWD_SCAN | PREP_FWD_OUT;
+  constexpr int ALL = FWD | PREP_BWD_SCAN | PREP_BWD_CHUNK;
+  constexpr int BWD = PREP_FWD_SCAN | PREP_BWD_SCAN | PREP_BWD_CHUNK;
+  switch (a.prep_mode) {
+    case FWD: return prep_m<T, FWD>(a, s);
+    case ALL: return prep_m<T, ALL>(a, s);
+    case BWD: return prep_m<T, BWD>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_fwd_prep(const Args& a, int f32, hipStream_t s) {
