@@ -142,9 +142,9 @@ Layout layout(const Plan& p) {
   } else {
     off = s;
   }
-  L.W = take(off, tokK);
+  L.W = take(off, tileK);
   L.Ft = take(off, tileK);
-  L.U = take(off, tokV);
+  L.U = take(off, tileV);
   const size_t after_scan = off;
   L.Qg = take(off, tokK);
   L.Cq = take(off, tile64);

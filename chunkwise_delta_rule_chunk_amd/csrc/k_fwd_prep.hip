@@ -94,7 +94,13 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
   gc.init(threadIdx.x);
   gnx.init(threadIdx.x);
   Staged<T, CH, K, NTH> pk, pq;
+  // v for Z^T: bf16 threads take rows (2p, 2p + 1), p = tid % 32, and the
+  // eight columns from 8 (tid / 32), so each Z^T write is one 4-byte pair of
+  // tokens (conflict-free across the wave); fp32 keeps the row-piece mapping
+  static constexpr int VSL = (CH / 2) * (V / 8);         // (row pair, column piece) slots
+  static constexpr int VPT = BF ? (VSL + NTH - 1) / NTH : 1;  // slots per thread
   Staged<T, CH, V, NTH> pv;
+  uint4 pv2[2 * VPT];
   uint32_t pbeta = 0u;  // raw bits of the next item's beta for row tid
   // the next item's inputs: k, q, v and beta as soon as the current ones are in
   // LDS, the gates once the current gates are consumed
@@ -105,7 +111,19 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     const int64_t t0 = ci.bos;
     pk.load(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, gsK, ci.len, tid);
     pq.load(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, gsK, ci.len, tid);
-    pv.load(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, gsV, ci.len, tid);
+    if constexpr (BF) {
+      // pair slot s = tid + j NTH: p = s % 32, column piece s / 32
+      const GBuf bv = gbuf(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, tile_bytes<T>(ci.len, gsV, V));
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int sl = tid + j * NTH, p = sl % 32, c0 = (sl / 32) * 8;
+        const bool ok = sl < VSL;
+        pv2[2 * j] = gld16(bv, ok ? (uint32_t)(((int64_t)(2 * p) * gsV + c0) * 2) : OOB);
+        pv2[2 * j + 1] = gld16(bv, ok ? (uint32_t)(((int64_t)(2 * p + 1) * gsV + c0) * 2) : OOB);
+      }
+    } else {
+      pv.load(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, gsV, ci.len, tid);
+    }
     pbeta = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, ci.len - 1)) * H + h);
   };
   auto fetch_g = [&](int item) {
@@ -150,20 +168,27 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     // ---- S1: finish the prefix, Z^T from the staged v, statistics ------------
     gc.prefix_finish(sTot);
     if constexpr (BF) {
-      constexpr int VEC = 8, PER = V / VEC;
+      // Z^T[v][j] = beta_j v[j][v], two tokens per 4-byte write
 #pragma unroll
-      for (int j = 0; j < decltype(pv)::N; ++j) {
-        const int idx = tid + j * NTH;
-        const int r = idx / PER, c0 = (idx - r * PER) * VEC;
-        if (idx < CH * PER) {
+      for (int j = 0; j < VPT; ++j) {
+        const int sl = tid + j * NTH, p = sl % 32, c0 = (sl / 32) * 8;
+        if (sl >= VSL) continue;
+        union {
+          uint4 u;
+          T e[8];
+        } v0, v1;
+        v0.u = pv2[2 * j];
+        v1.u = pv2[2 * j + 1];
+        const float b0 = sBeta[2 * p], b1 = sBeta[2 * p + 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
           union {
-            uint4 u;
-            T e[VEC];
-          } val;
-          val.u = pv.r[j];
-          const float b = sBeta[r];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) sZt[(c0 + e) * PA + r] = fromf<T>(b * tof(val.e[e]));
+            uint32_t u;
+            T h[2];
+          } z;
+          z.h[0] = fromf<T>(b0 * tof(v0.e[e]));
+          z.h[1] = fromf<T>(b1 * tof(v1.e[e]));
+          *reinterpret_cast<uint32_t*>(sZt + (c0 + e) * PA + 2 * p) = z.u;
         }
       }
     } else {
@@ -217,7 +242,10 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       const float cA = fexp2(rA), cB = fexp2(gn - rB);
       const float bs = a.scale;
       constexpr int VE = 16 / (int)sizeof(T);
-      T* Ftd = reinterpret_cast<T*>(a.Ft) + (cb * K + col) * CH + r0;
+      // F^T in operand-fragment order (see kernels.hpp): 16 k rows x KG tokens
+      // per fragment, this thread's VE-token groups are single 16-byte pieces
+      constexpr int KGF = 4 * (16 / (int)sizeof(T)), NGTF = CH / KGF;
+      T* Ftd = reinterpret_cast<T*>(a.Ft) + cb * K * CH;
       T* Qgtd = reinterpret_cast<T*>(a.Qgt) + (cb * K + col) * CH + r0;
       T* Ktd = reinterpret_cast<T*>(a.Kt) + (cb * K + col) * CH + r0;
       T* Qtd = reinterpret_cast<T*>(a.Qt) + (cb * K + col) * CH + r0;
@@ -262,7 +290,10 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         }
         // token-contiguous tiles: this thread holds consecutive tokens of column col
         *reinterpret_cast<uint4*>(sEt + col * PA + r0 + r8) = et.u;
-        if constexpr (MODE & PREP_FWD_SCAN) *reinterpret_cast<uint4*>(Ftd + r8) = ft.u;
+        if constexpr (MODE & PREP_FWD_SCAN) {
+          const int tk = r0 + r8, q = tk / KGF, g = (tk % KGF) / VE;
+          *reinterpret_cast<uint4*>(Ftd + (((col / SUB) * NGTF + q) * 64 + g * 16 + col % SUB) * VE) = ft.u;
+        }
         if constexpr (MODE & PREP_BWD_SCAN) *reinterpret_cast<uint4*>(Qgtd + r8) = qt.u;
         if constexpr (MODE & PREP_BWD_CHUNK) {
           *reinterpret_cast<uint4*>(Ktd + r8) = kt.u;
@@ -337,12 +368,12 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     }
 
     // ---- S5: W = A E, U = A Z --------------------------------------------------
-    T* Wo = reinterpret_cast<T*>(a.W) + (t0 * H + h) * K;
-    T* Uo = reinterpret_cast<T*>(a.U) + (t0 * H + h) * V;
+    // W and U in operand-fragment order (see kernels.hpp), all 64 rows (rows
+    // past the chunk's end are exact zeros)
+    T* Wfo = reinterpret_cast<T*>(a.W) + cb * CH * K;
+    T* Ufo = reinterpret_cast<T*>(a.U) + cb * CH * V;
     T* Wto = reinterpret_cast<T*>(a.Wt) + cb * K * CH;
     constexpr bool wantW = MODE & PREP_FWD_SCAN, wantWt = MODE & PREP_BWD_SCAN, wantU = wantW;
-    const int nblk = (n + SUB - 1) / SUB;
-    const int nblkW = wantWt ? NSUB : nblk;  // W^T needs every row block (exact zeros past n)
     if constexpr (BF) {
       for (int idx = tid; idx < CH * CH / 4; idx += NTH) {
         const int i = idx / (CH / 4), j = (idx - i * (CH / 4)) * 4;
@@ -354,12 +385,8 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       }
       lds_barrier();
     }
-    // staging of W and U: the score operands in sKa and the fp32 L in sL are
-    // dead once A is formed (64 x pitch(V) elements of T fit in sL's bytes)
+    // staging of W: the score operands in sKa are dead once A is formed
     T* sWs = sKa;
-    T* sUs = reinterpret_cast<T*>(sL);
-    constexpr int PUs = pitch<T>(V);
-    static_assert(CH * PUs * sizeof(T) <= CH * PL * sizeof(float), "U staging fits in sL");
     const T* Aop = BF ? (const T*)sAb : (const T*)sA;
     constexpr int PAo = BF ? PA : PL;
     const int NCB = (K + (wantU ? V : 0)) / SUB;
@@ -368,10 +395,8 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       if (isW && !wantW && !wantWt) continue;
       const int col = isW ? cbk * SUB : (cbk - K / SUB) * SUB;
       const T* Bop = (isW ? sEt : sZt) + col * PA;
-      const int nI = isW ? nblkW : nblk;
       static_for<0, NSUB>([&](auto II) {
         constexpr int I = decltype(II)::value;
-        if (I >= nI) return;
         f32x4 acc = zero4();
         // A is lower triangular: row block I needs tokens < 16 (I + 1) only
         constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
@@ -380,23 +405,22 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
           if (wantW) st_tile<T>(acc, sWs + (I * SUB) * PK + col, PK, 1);
           if (wantWt) st_tile_T<T>(acc, Wto + (int64_t)col * CH + I * SUB, CH);
         } else {
-          st_tile<T>(acc, sUs + (I * SUB) * PUs + col, PUs, 1);
+          // the C tile is the fragment piece: lane l holds rows 16 I + 4 (l >> 4) + i
+          // of column col + (l & 15)
+          using FR = typename Frag4<T>::type;
+          *reinterpret_cast<FR*>(Ufo + (((col / SUB) * NSUB + I) * 64 + lane_id()) * 4) = to_frag<T>(acc);
         }
       });
     }
-    // W and U leave through LDS as whole 16-byte row pieces: rows written from
-    // sixteen-column tiles by different waves would otherwise reach memory as
-    // partial lines
-    if (wantW) {
+    // W leaves through LDS: fragment piece p = (16-row block, key group, lane)
+    // is row 16 tw + (lane & 15), keys KG q + VE (lane >> 4) .. + VE - 1
+    if constexpr (wantW) {
       lds_barrier();
-      constexpr int VE = 16 / (int)sizeof(T);
-      for (int idx = tid; idx < n * (K / VE); idx += NTH) {
-        const int r = idx / (K / VE), c8 = (idx - r * (K / VE)) * VE;
-        *reinterpret_cast<uint4*>(Wo + r * gsK + c8) = *reinterpret_cast<const uint4*>(sWs + r * PK + c8);
-      }
-      for (int idx = tid; idx < n * (V / VE); idx += NTH) {
-        const int r = idx / (V / VE), c8 = (idx - r * (V / VE)) * VE;
-        *reinterpret_cast<uint4*>(Uo + r * gsV + c8) = *reinterpret_cast<const uint4*>(sUs + r * PUs + c8);
+      constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE, NGK = K / KG;
+      for (int idx = tid; idx < CH * K / VE; idx += NTH) {
+        const int ln = idx % 64, blk = idx / 64, tw = blk / NGK, q = blk - tw * NGK;
+        const int row = SUB * tw + (ln & 15), k0 = KG * q + VE * (ln >> 4);
+        *reinterpret_cast<uint4*>(Wfo + idx * VE) = *reinterpret_cast<const uint4*>(sWs + row * PK + k0);
       }
     }
     lds_barrier();  // LDS is rewritten by the next item

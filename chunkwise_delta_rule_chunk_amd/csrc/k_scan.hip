@@ -114,29 +114,25 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
   auto ktile = [&](int j) { return WIDE ? w + 4 * j : w % NKT; };
   auto vtile = [&](int m) { return WIDE ? m : (w / NKT) * CW + m; };
 
-  // DEPTH register sets: chunk c + DEPTH is read while chunk c is processed
-  uint4 wf[DEPTH][NGK];      // W row 16 w + r16, lane piece of every key group
-  T uf[DEPTH][CT][4];        // U in the C layout of R's tiles
-  uint4 ff[DEPTH][KW][NGT];  // F^T row 16 ktile + r16, lane piece of every token group
+  // DEPTH register sets: chunk c + DEPTH is read while chunk c is processed.
+  // W, F^T and U are stored in operand-fragment order (kernels.hpp), rows past
+  // a chunk's end as exact zeros: every read below is one contiguous piece.
+  using FR = typename Frag4<T>::type;
+  uint4 wf[DEPTH][NGK];      // W rows 16 w + r16, lane piece of every key group
+  FR uf[DEPTH][CT];          // U in the C layout of R's tiles
+  uint4 ff[DEPTH][KW][NGT];  // F^T rows 16 ktile + r16, lane piece of every token group
   f32x4 lam[DEPTH][KW];      // G2_last of the state rows this lane holds
-  // chunk c of this sequence from the sequence bounds; past the last chunk the
-  // last one is read again (valid memory, never used)
+  // past the last chunk the last one is read again (valid memory, never used)
   auto chunk_bos = [&](int c) { return seq_bos + (min(c, c1 - 1) - c0) * CH; };
   auto fetch_wu = [&](auto set, int c) {
     constexpr int B = decltype(set)::value;
-    const int bos = chunk_bos(c), len = min(CH, seq_eos - bos);
-    const int row = SUB * w + r16;
-    const T* wp = Wg + ((int64_t)bos * H + h) * K + (int64_t)min(row, len - 1) * gsK + VE * g;
-    // rows past the chunk's end read row len - 1; they are zeroed where used
+    const int64_t cb = (int64_t)min(c, c1 - 1) * H + h;
+    const T* wp = Wg + cb * CH * K + (int64_t)(w * NGK * 64 + l) * VE;
 #pragma unroll
-    for (int q = 0; q < NGK; ++q) wf[B][q] = *reinterpret_cast<const uint4*>(wp + KG * q);
+    for (int q = 0; q < NGK; ++q) wf[B][q] = *reinterpret_cast<const uint4*>(wp + q * 64 * VE);
+    const T* up = Ug + cb * CH * V + (int64_t)((vt * CT * NSUB + w) * 64 + l) * 4;
 #pragma unroll
-    for (int m = 0; m < CT; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = SUB * w + 4 * g + i;
-        uf[B][m][i] = Ug[((int64_t)bos + min(rr, len - 1)) * gsV + (int64_t)h * V + vt * BV + SUB * m + r16];
-      }
+    for (int m = 0; m < CT; ++m) uf[B][m] = *reinterpret_cast<const FR*>(up + m * NSUB * 64 * 4);
   };
   auto fetch_fl = [&](auto set, int c) {
     constexpr int B = decltype(set)::value;
@@ -144,9 +140,9 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
 #pragma unroll
     for (int j = 0; j < KW; ++j) {
       const int kr = SUB * ktile(j);
-      const T* fp = Ftg + (cb * K + kr + r16) * CH + VE * g;
+      const T* fp = Ftg + cb * K * CH + (int64_t)(ktile(j) * NGT * 64 + l) * VE;
 #pragma unroll
-      for (int q = 0; q < NGT; ++q) ff[B][j][q] = *reinterpret_cast<const uint4*>(fp + KG * q);
+      for (int q = 0; q < NGT; ++q) ff[B][j][q] = *reinterpret_cast<const uint4*>(fp + q * 64 * VE);
       lam[B][j] = *reinterpret_cast<const f32x4*>(a.glast + cb * K + kr + 4 * g);
     }
   };
@@ -203,25 +199,18 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
       tile_out<T, BV, K, NTH>(reinterpret_cast<T*>(a.hbufT) + (cb * V + vt * BV) * K, K, sHt, PK, BV, tid);
     if constexpr (NAT)
       tile_out<T, K, BV, NTH>(reinterpret_cast<T*>(a.hbuf) + cb * K * V + vt * BV, V, sS, PU, K, tid);
-    // R = U - W S for token tile w (rows past the chunk's end are zero)
-    const bool wok = SUB * w + r16 < len;
-    uint4 wv[NGK];
-#pragma unroll
-    for (int q = 0; q < NGK; ++q) {
-      const uint4 x = wf[B][q];
-      wv[q] = uint4{wok ? x.x : 0u, wok ? x.y : 0u, wok ? x.z : 0u, wok ? x.w : 0u};
-    }
+    // R = U - W S for token tile w (rows past the chunk's end are zero: W and
+    // U are zero there)
 #pragma unroll
     for (int m = 0; m < CT; ++m) {
       f32x4 p = zero4();
       const T* hb = sHt + (SUB * m + r16) * PK + VE * g;
 #pragma unroll
-      for (int q = 0; q < NGK; ++q) mma16B<T>(p, wv[q], *reinterpret_cast<const uint4*>(hb + KG * q));
+      for (int q = 0; q < NGK; ++q) mma16B<T>(p, wf[B][q], *reinterpret_cast<const uint4*>(hb + KG * q));
       f32x4 rv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float uu = SUB * w + 4 * g + i < len ? tof(uf[B][m][i]) : 0.f;
-        const T x = fromf<T>(uu - p[i]);
+        const T x = fromf<T>(tof(uf[B][m][i]) - p[i]);
         if constexpr (NAT) sR[(SUB * w + 4 * g + i) * PU + SUB * m + r16] = x;
         rv[i] = tof(x);
       }

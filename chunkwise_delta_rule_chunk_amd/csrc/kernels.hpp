@@ -44,10 +44,19 @@ struct Args {
   // chunk's end).  Each product reads its operands with the contraction index
   // contiguous, so tiles that are contracted over tokens are stored with the
   // token index last (the "t" tiles).
+  //
+  // The forward scan's operands are stored in operand-fragment order, one
+  // [64 x K] or [64 x V] tile per (chunk, head), so that each MFMA operand a
+  // wave needs is one contiguous load of 16 bytes per lane (VE = 16 / sizeof
+  // element, KG = 4 VE contraction slots per fragment, lane l, e < VE):
+  //   W  piece ((tw * K/KG + q) * 64 + l) holds W[16 tw + (l & 15)][KG q + VE (l >> 4) + e]
+  //   Ft piece ((tk * 64/KG + q) * 64 + l) holds F[KG q + VE (l >> 4) + e][16 tk + (l & 15)]
+  //   U  piece ((tv * 4 + tw) * 64 + l) holds U[16 tw + 4 (l >> 4) + i][16 tv + (l & 15)], i < 4
+  // (U in the C-fragment layout of the R tile it is subtracted from).
   int prep_mode;  // PREP_* bits: which of the sets below k_fwd_prep writes
-  void* W;       // A E                 [BT,H,K]     forward scan (R = U - W S)
-  void* Ft;      // F^T, F = K exp2(Gn - G)  [nc,H,K,64]  forward scan (S += F^T R)
-  void* U;       // A Z                 [BT,H,V]     forward scan
+  void* W;       // A E                 [nc,H,64,K] fragment order   forward scan (R = U - W S)
+  void* Ft;      // F^T, F = K exp2(Gn - G) [nc,H,K,64] fragment order   forward scan (S += F^T R)
+  void* U;       // A Z                 [nc,H,64,V] fragment order   forward scan
   float* glast;  // G2 at the last row  [nc,H,K]     both scans
   void* Qg;      // s Q exp2(G)         [BT,H,K]     output
   void* Cq;      // tril_incl(Qg Y^T)   [nc,H,64,64] output
