@@ -117,7 +117,7 @@ Layout layout(const Plan& p) {
   size_t off = 0;
   auto take = [&](size_t& o, size_t bytes) { const size_t r = o; o += up(bytes); return r; };
   auto take_reverse = [&](size_t& o) {
-    L.F = take(o, tokK);
+    L.F = take(o, tileK);
     L.Wt = take(o, tileK);
     L.Qgt = take(o, tileK);
     L.Cqt = take(o, tile64);

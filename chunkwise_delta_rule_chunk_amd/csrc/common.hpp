@@ -309,6 +309,29 @@ __device__ __forceinline__ ChunkInfo load_chunk(const ChunkInfo* p, int c) {
   return r;
 }
 
+// ---- operand-fragment order ---------------------------------------------------
+// A tile with 64-long rows stored so that the MFMA operand fragments of a row
+// block are contiguous: with VE = 16 / sizeof(T) and KG = 4 VE, piece
+// ((rb * 64/KG + q) * 64 + l) holds row 16 rb + (l & 15), columns
+// KG q + VE (l >> 4) + e, e < VE (one 16-byte load per lane per fragment).
+// Store of the transposed C tile of a 16 x 16 product X (rows 16 I + 4 (l >> 4)
+// + i, column 16 J + (l & 15) of X) into such a tile of X^T: row 16 J + (l & 15),
+// columns 16 I + 4 (l >> 4) .. + 3, four consecutive elements of one piece.
+template <typename T>
+__device__ __forceinline__ void st_frag_T(const f32x4& acc, T* tile, int I, int J) {
+  constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE, NG = CH / KG;
+  const int l = lane_id(), c0 = SUB * I + 4 * (l >> 4);
+  T* p = tile + ((J * NG + c0 / KG) * 64 + ((c0 % KG) / VE) * 16 + (l & 15)) * VE + c0 % VE;
+  if constexpr (std::is_same_v<T, bf16>) {
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)acc[i];
+    *reinterpret_cast<bf16x4*>(p) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = acc;
+  }
+}
+
 // ---- bounds-checked global access ------------------------------------------
 // A buffer resource over [base, base + bytes): the hardware range check makes
 // an access at an offset >= bytes read zeros and drops a store there, so an

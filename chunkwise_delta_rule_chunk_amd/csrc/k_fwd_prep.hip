@@ -246,14 +246,18 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       // per fragment, this thread's VE-token groups are single 16-byte pieces
       constexpr int KGF = 4 * (16 / (int)sizeof(T)), NGTF = CH / KGF;
       T* Ftd = reinterpret_cast<T*>(a.Ft) + cb * K * CH;
-      T* Qgtd = reinterpret_cast<T*>(a.Qgt) + (cb * K + col) * CH + r0;
+      T* Qgtd = reinterpret_cast<T*>(a.Qgt) + cb * K * CH;
       T* Ktd = reinterpret_cast<T*>(a.Kt) + (cb * K + col) * CH + r0;
       T* Qtd = reinterpret_cast<T*>(a.Qt) + (cb * K + col) * CH + r0;
-      // natural-layout rows (Qg forward, F reverse) through bounds-checked
-      // buffers: rows past the chunk's end are dropped by the range check
+      // natural-layout rows of Qg through a bounds-checked buffer: rows past
+      // the chunk's end are dropped by the range check
       const uint32_t natb = tile_bytes<T>(n, gsK, K);
       const GBuf bQg = gbuf(reinterpret_cast<T*>(a.Qg) + (t0 * H + h) * K, (MODE & PREP_FWD_OUT) ? natb : 0u);
-      const GBuf bF = gbuf(reinterpret_cast<T*>(a.F) + (t0 * H + h) * K, (MODE & PREP_BWD_SCAN) ? natb : 0u);
+      // F in operand-fragment order (row block seg, key group col / KGF): this
+      // thread's 16 rows are elements VE apart in one column of pieces
+      constexpr int NGKF = K / KGF;
+      T* Fd = reinterpret_cast<T*>(a.F) + cb * CH * K +
+              ((gc.seg * NGKF + col / KGF) * 64 + ((col % KGF) / VE) * 16) * VE + col % VE;
       const uint32_t rowb = (uint32_t)(gsK * (int64_t)sizeof(T)), colb = col * (int)sizeof(T);
 #pragma unroll
       for (int r8 = 0; r8 < RS; r8 += VE) {
@@ -277,10 +281,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
             if constexpr (sizeof(T) == 2) gst2(bQg, off, __builtin_bit_cast(uint16_t, fromf<T>(vQg)));
             else gst4(bQg, off, __float_as_uint(vQg));
           }
-          if constexpr (MODE & PREP_BWD_SCAN) {
-            if constexpr (sizeof(T) == 2) gst2(bF, off, __builtin_bit_cast(uint16_t, fromf<T>(vF)));
-            else gst4(bF, off, __float_as_uint(vF));
-          }
+          if constexpr (MODE & PREP_BWD_SCAN) Fd[r * VE] = fromf<T>(vF);
           sKa[row * PK + col] = fromf<T>(vKa);
           sQ[row * PK + col] = fromf<T>(vQa);
           sK[row * PK + col] = fromf<T>(vKc);
@@ -294,7 +295,10 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
           const int tk = r0 + r8, q = tk / KGF, g = (tk % KGF) / VE;
           *reinterpret_cast<uint4*>(Ftd + (((col / SUB) * NGTF + q) * 64 + g * 16 + col % SUB) * VE) = ft.u;
         }
-        if constexpr (MODE & PREP_BWD_SCAN) *reinterpret_cast<uint4*>(Qgtd + r8) = qt.u;
+        if constexpr (MODE & PREP_BWD_SCAN) {
+          const int tk = r0 + r8, q = tk / KGF, g = (tk % KGF) / VE;
+          *reinterpret_cast<uint4*>(Qgtd + (((col / SUB) * NGTF + q) * 64 + g * 16 + col % SUB) * VE) = qt.u;
+        }
         if constexpr (MODE & PREP_BWD_CHUNK) {
           *reinterpret_cast<uint4*>(Ktd + r8) = kt.u;
           *reinterpret_cast<uint4*>(Qtd + r8) = qq.u;
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
           cq[i] = row >= col ? accC[i] : 0.f;
         }
         if constexpr (MODE & PREP_FWD_OUT) st_tile<T>(cq, Cqo + (I * SUB) * CH + J * SUB, CH, 1);
-        if constexpr (MODE & PREP_BWD_SCAN) st_tile_T<T>(cq, Cqto + (J * SUB) * CH + I * SUB, CH);
+        if constexpr (MODE & PREP_BWD_SCAN) st_frag_T<T>(cq, Cqto, I, J);
       };
       score_tiles_pre<T, K, true, NW>(sKa, sQ, sK, PK, sFac, sFlag, n, store);
       // wide diagonal sub-chunks: pairwise, one wave each
@@ -345,7 +349,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         const int I = t / NSUB, J = t - I * NSUB;
         if (J <= I && I * SUB < n) continue;
         if constexpr (MODE & PREP_FWD_OUT) st_tile<T>(zero4(), Cqo + (I * SUB) * CH + J * SUB, CH, 1);
-        if constexpr (MODE & PREP_BWD_SCAN) st_tile_T<T>(zero4(), Cqto + (J * SUB) * CH + I * SUB, CH);
+        if constexpr (MODE & PREP_BWD_SCAN) st_frag_T<T>(zero4(), Cqto, I, J);
       }
     }
     lds_barrier();
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         mma_tile<T, true, true>(acc, Aop + (I * SUB) * PAo, PAo, 1, Bop, PA, 1, kd);
         if (isW) {
           if (wantW) st_tile<T>(acc, sWs + (I * SUB) * PK + col, PK, 1);
-          if (wantWt) st_tile_T<T>(acc, Wto + (int64_t)col * CH + I * SUB, CH);
+          if (wantWt) st_frag_T<T>(acc, Wto, I, col / SUB);
         } else {
           // the C tile is the fragment piece: lane l holds rows 16 I + 4 (l >> 4) + i
           // of column col + (l & 15)

@@ -304,28 +304,29 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
   // chunks are walked from the last; before the first one the first is read
   // again (valid memory, never used)
   auto chunk_of = [&](int c) { return max(c, c0); };
+  // F, Cq^T, Qg^T and W^T are stored in operand-fragment order (kernels.hpp),
+  // rows past a chunk's end as exact zeros: each read is one contiguous piece
   auto fetch = [&](auto set, int c) {
     constexpr int B = decltype(set)::value;
     const int cc = chunk_of(c);
     const int bos = seq_bos + (cc - c0) * CH, len = min(CH, seq_eos - bos);
     const int64_t cb = (int64_t)cc * H + h;
-    const int row = SUB * w + r16;
-    const T* fp = reinterpret_cast<const T*>(a.F) + ((int64_t)bos * H + h) * K +
-                  (int64_t)min(row, len - 1) * gsK + VE * g;
+    const T* fp = reinterpret_cast<const T*>(a.F) + cb * CH * K + (int64_t)(w * NGK * 64 + l) * VE;
 #pragma unroll
-    for (int q = 0; q < NGK; ++q) ff[B][q] = *reinterpret_cast<const uint4*>(fp + KG * q);
-    const T* cp = reinterpret_cast<const T*>(a.Cqt) + (cb * CH + row) * CH + VE * g;
+    for (int q = 0; q < NGK; ++q) ff[B][q] = *reinterpret_cast<const uint4*>(fp + q * 64 * VE);
+    const T* cp = reinterpret_cast<const T*>(a.Cqt) + cb * CH * CH + (int64_t)(w * NGT * 64 + l) * VE;
 #pragma unroll
-    for (int q = 0; q < NGT; ++q) cf[B][q] = *reinterpret_cast<const uint4*>(cp + KG * q);
+    for (int q = 0; q < NGT; ++q) cf[B][q] = *reinterpret_cast<const uint4*>(cp + q * 64 * VE);
 #pragma unroll
     for (int j = 0; j < KW; ++j) {
       const int kr = SUB * ktile(j);
-      const T* qp = reinterpret_cast<const T*>(a.Qgt) + (cb * K + kr + r16) * CH + VE * g;
-      const T* wp = reinterpret_cast<const T*>(a.Wt) + (cb * K + kr + r16) * CH + VE * g;
+      const int64_t po = (int64_t)(ktile(j) * NGT * 64 + l) * VE;
+      const T* qp = reinterpret_cast<const T*>(a.Qgt) + cb * K * CH + po;
+      const T* wp = reinterpret_cast<const T*>(a.Wt) + cb * K * CH + po;
 #pragma unroll
       for (int q = 0; q < NGT; ++q) {
-        qf[B][j][q] = *reinterpret_cast<const uint4*>(qp + KG * q);
-        wf[B][j][q] = *reinterpret_cast<const uint4*>(wp + KG * q);
+        qf[B][j][q] = *reinterpret_cast<const uint4*>(qp + q * 64 * VE);
+        wf[B][j][q] = *reinterpret_cast<const uint4*>(wp + q * 64 * VE);
       }
       lam[B][j] = *reinterpret_cast<const f32x4*>(a.glast + cb * K + kr + 4 * g);
     }
@@ -398,21 +399,15 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
     }
     lds_barrier();
     tile_out<T, K, BV, NTH>(reinterpret_cast<T*>(a.dhbuf) + cb * K * V + vt * BV, V, sD, PS, K, tid);
-    // Rbar = F dS+ + Cq^T dO for token tile w (F rows past the end are zero)
-    const bool fok = SUB * w + r16 < len;
-    uint4 fv[NGK];
-#pragma unroll
-    for (int q = 0; q < NGK; ++q) {
-      const uint4 x = ff[B][q];
-      fv[q] = uint4{fok ? x.x : 0u, fok ? x.y : 0u, fok ? x.z : 0u, fok ? x.w : 0u};
-    }
+    // Rbar = F dS+ + Cq^T dO for token tile w (rows past the end are zero: F
+    // and Cq vanish there)
 #pragma unroll
     for (int m = 0; m < CT; ++m) {
       f32x4 acc = zero4();
       const T* db = sDt + (SUB * m + r16) * PK + VE * g;
       const T* ob = sOt[B] + (SUB * m + r16) * PA + VE * g;
 #pragma unroll
-      for (int q = 0; q < NGK; ++q) mma16B<T>(acc, fv[q], *reinterpret_cast<const uint4*>(db + KG * q));
+      for (int q = 0; q < NGK; ++q) mma16B<T>(acc, ff[B][q], *reinterpret_cast<const uint4*>(db + KG * q));
 #pragma unroll
       for (int q = 0; q < NGT; ++q) mma16B<T>(acc, cf[B][q], *reinterpret_cast<const uint4*>(ob + KG * q));
       st_tile_T<T>(acc, sRbt + (SUB * m) * PA + SUB * w, PA);

@@ -52,7 +52,9 @@ struct Args {
   //   W  piece ((tw * K/KG + q) * 64 + l) holds W[16 tw + (l & 15)][KG q + VE (l >> 4) + e]
   //   Ft piece ((tk * 64/KG + q) * 64 + l) holds F[KG q + VE (l >> 4) + e][16 tk + (l & 15)]
   //   U  piece ((tv * 4 + tw) * 64 + l) holds U[16 tw + 4 (l >> 4) + i][16 tv + (l & 15)], i < 4
-  // (U in the C-fragment layout of the R tile it is subtracted from).
+  // (U in the C-fragment layout of the R tile it is subtracted from).  The
+  // reverse scan's operands F, Wt, Qgt and Cqt are stored the same way (F
+  // like W, the "t" tiles like Ft).
   int prep_mode;  // PREP_* bits: which of the sets below k_fwd_prep writes
   void* W;       // A E                 [nc,H,64,K] fragment order   forward scan (R = U - W S)
   void* Ft;      // F^T, F = K exp2(Gn - G) [nc,H,K,64] fragment order   forward scan (S += F^T R)
@@ -60,10 +62,10 @@ struct Args {
   float* glast;  // G2 at the last row  [nc,H,K]     both scans
   void* Qg;      // s Q exp2(G)         [BT,H,K]     output
   void* Cq;      // tril_incl(Qg Y^T)   [nc,H,64,64] output
-  void* F;       // F                   [BT,H,K]     reverse scan (Rbar = F dS+)
-  void* Wt;      // W^T                 [nc,H,K,64]  reverse scan (dS -= W^T Rbar)
-  void* Qgt;     // Qg^T                [nc,H,K,64]  reverse scan (dS += Qg^T dO)
-  void* Cqt;     // Cq^T                [nc,H,64,64] reverse scan (Rbar += Cq^T dO)
+  void* F;       // F                   [nc,H,64,K] fragment order   reverse scan (Rbar = F dS+)
+  void* Wt;      // W^T                 [nc,H,K,64] fragment order   reverse scan (dS -= W^T Rbar)
+  void* Qgt;     // Qg^T                [nc,H,K,64] fragment order   reverse scan (dS += Qg^T dO)
+  void* Cqt;     // Cq^T                [nc,H,64,64] fragment order  reverse scan (Rbar += Cq^T dO)
   void* hbuf;    // state entering each chunk [nc,H,K,V] dtype
   void* R;       // corrections U - W S [BT,H,V] dtype
   void* hbufT;   // the same states transposed [nc,H,V,K] (output kernel)
