@@ -332,6 +332,53 @@ __device__ __forceinline__ void st_frag_T(const f32x4& acc, T* tile, int I, int 
   }
 }
 
+// acc += A B over one 16-byte lane group: lane l supplies 16 bytes of row
+// (l & 15) of A and of column (l & 15) of B, at contraction slots
+// VE (l >> 4) + e of the group (VE = 16 / sizeof(T)).  bf16: one 16x16x32
+// MFMA; fp32: four 16x16x4 MFMAs, step e taking element e of every lane.
+template <typename T>
+__device__ __forceinline__ void mma16B(f32x4& acc, uint4 a, uint4 b) {
+  if constexpr (std::is_same_v<T, bf16>) {
+    union {
+      uint4 u;
+      bf16x8 v;
+    } x, y;
+    x.u = a;
+    y.u = b;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.v, y.v, acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+}
+
+// Copy a [ROWS x COLS] LDS tile (pitch lp; ROWS a multiple of 16, rows are
+// operand rows, columns the contraction) to global memory in operand-fragment
+// order (see st_frag_T), every thread storing the same number of equal
+// pieces (16 or 8 bytes; an 8-byte piece is half a fragment piece).
+template <typename T, int ROWS, int COLS, int NTH>
+__device__ __forceinline__ void frag_out(T* g, const T* s, int lp, int tid) {
+  constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE, NG = COLS / KG;
+  constexpr int BYTES = ROWS * COLS * (int)sizeof(T);
+  constexpr int PB = BYTES / NTH >= 16 ? 16 : BYTES / NTH;
+  static_assert(PB == 16 || PB == 8, "piece size");
+  static_assert(ROWS % SUB == 0 && COLS % KG == 0 && BYTES % (PB * NTH) == 0, "tile split");
+  constexpr int HE = PB / (int)sizeof(T), NP = BYTES / (PB * NTH);
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int idx = tid + j * NTH;                  // piece (16-byte) or half piece (8-byte)
+    const int pc = PB == 16 ? idx : idx >> 1, hf = PB == 16 ? 0 : idx & 1;
+    const int ln = pc % 64, blk = pc / 64, rb = blk / NG, q = blk - rb * NG;
+    const T* src = s + (SUB * rb + (ln & 15)) * lp + KG * q + VE * (ln >> 4) + hf * HE;
+    if constexpr (PB == 16)
+      *reinterpret_cast<uint4*>(g + idx * HE) = *reinterpret_cast<const uint4*>(src);
+    else
+      *reinterpret_cast<uint2*>(g + idx * HE) = *reinterpret_cast<const uint2*>(src);
+  }
+}
+
 // ---- bounds-checked global access ------------------------------------------
 // A buffer resource over [base, base + bytes): the hardware range check makes
 // an access at an offset >= bytes read zeros and drops a store there, so an

@@ -8,48 +8,61 @@ namespace rewy {
 template <typename T, int K, int V>
 __global__ __launch_bounds__(256) void k_fwd_out(Args a) {
   constexpr int PK = pitch<T>(K), PA = pitch<T>(CH);
+  constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE, NGK = K / KG, NGT = CH / KG;
+  constexpr int NVB = V / SUB, VPW = (NVB + 3) / 4;  // value blocks, per wave
   __shared__ __align__(16) T sQg[CH * PK];
-  __shared__ __align__(16) T sHt[V * PK];  // state S_c as operand, [v][k]
   __shared__ __align__(16) T sCq[CH * PA];
-  __shared__ __align__(16) T sRt[V * PA];  // R as operand, [v][i]
 
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const ChunkInfo ci = load_chunk(a.chunks, c);
   const int len = ci.len;
   if (len == 0) return;
-  const int H = a.H;
+  const int H = a.H, w = wave_id(), l = lane_id();
   const int64_t t0 = ci.bos, cb = (int64_t)c * H + h;
   const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
-  // all four tiles are read before the first LDS write waits; Qg rows past
-  // the chunk's end read as zero.  S_c^T and R^T were written transposed by
-  // the forward scan.
+  // Qg and Cq are shared by the waves and go through LDS (Qg rows past the
+  // chunk's end read as zero); the state S_c and R_c were written by the
+  // forward scan in operand-fragment order, and each wave reads the pieces of
+  // its own value blocks straight into registers.
   TileRegs<T, CH, K, 256> pq;
-  TileRegs<T, V, K, 256> ph;
   TileRegs<T, CH, CH, 256> pc;
-  TileRegs<T, V, CH, 256> pr;
   pq.load(gbuf(reinterpret_cast<const T*>(a.Qg) + (t0 * H + h) * K, tile_bytes<T>(len, gsK, K)), gsK, tid);
-  ph.load(gbuf(reinterpret_cast<const T*>(a.hbufT) + cb * V * K, V * K * sizeof(T)), K, tid);
   pc.load(gbuf(reinterpret_cast<const T*>(a.Cq) + cb * CH * CH, CH * CH * sizeof(T)), CH, tid);
-  pr.load(gbuf(reinterpret_cast<const T*>(a.RT) + cb * V * CH, V * CH * sizeof(T)), CH, tid);
+  uint4 sf[VPW][NGK], rf[VPW][NGT];
+  static_for<0, VPW>([&](auto jj) {
+    constexpr int j = decltype(jj)::value;
+    const int vb = min(w + 4 * j, NVB - 1);  // a wave without a block reads one again, unused
+    const T* sp = reinterpret_cast<const T*>(a.hbufT) + ((cb * NVB + vb) * NGK * 64 + l) * VE;
+    const T* rp = reinterpret_cast<const T*>(a.RT) + ((cb * NVB + vb) * NGT * 64 + l) * VE;
+#pragma unroll
+    for (int q = 0; q < NGK; ++q) sf[j][q] = *reinterpret_cast<const uint4*>(sp + q * 64 * VE);
+#pragma unroll
+    for (int q = 0; q < NGT; ++q) rf[j][q] = *reinterpret_cast<const uint4*>(rp + q * 64 * VE);
+  });
   pq.store(sQg, PK, tid);
-  ph.store(sHt, PK, tid);
   pc.store(sCq, PA, tid);
-  pr.store(sRt, PA, tid);
   lds_barrier();
   T* og = reinterpret_cast<T*>(a.o) + (t0 * H + h) * V;
-  const int w = wave_id();
-  for (int vb = w; vb < V / SUB; vb += 4) {
+  const int r16 = l & 15, g = l >> 4;
+  static_for<0, VPW>([&](auto jj) {
+    constexpr int j = decltype(jj)::value;
+    const int vb = w + 4 * j;
+    if (vb >= NVB) return;
     static_for<0, NSUB>([&](auto II) {
       constexpr int I = decltype(II)::value;
       if (I * SUB >= len) return;
       f32x4 acc = zero4();
-      mma_tile<T, true, true>(acc, sQg + I * SUB * PK, PK, 1, sHt + vb * SUB * PK, PK, 1, K);
+      const T* qa = sQg + (I * SUB + r16) * PK + VE * g;
+#pragma unroll
+      for (int q = 0; q < NGK; ++q) mma16B<T>(acc, *reinterpret_cast<const uint4*>(qa + KG * q), sf[j][q]);
       // Cq is lower triangular: row block I needs tokens < 16 (I + 1) only
-      constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
-      mma_tile<T, true, true>(acc, sCq + I * SUB * PA, PA, 1, sRt + vb * SUB * PA, PA, 1, kd);
+      constexpr int nq = (SUB * (I + 1) + KG - 1) / KG;
+      const T* ca = sCq + (I * SUB + r16) * PA + VE * g;
+#pragma unroll
+      for (int q = 0; q < nq; ++q) mma16B<T>(acc, *reinterpret_cast<const uint4*>(ca + KG * q), rf[j][q]);
       st_tile<T>(acc, og + (I * SUB) * gsV + vb * SUB, (int)gsV, 1, len - I * SUB);
     });
-  }
+  });
 }
 
 template <typename T>

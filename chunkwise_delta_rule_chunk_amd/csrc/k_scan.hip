@@ -30,28 +30,6 @@ namespace rewy {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-// acc += A B over one 16-byte lane group: lane l supplies 16 bytes of row
-// (l & 15) of A and of column (l & 15) of B, at contraction slots
-// VE (l >> 4) + e of the group (VE = 16 / sizeof(T)).  bf16: one 16x16x32
-// MFMA; fp32: four 16x16x4 MFMAs, step e taking element e of every lane.
-template <typename T>
-__device__ __forceinline__ void mma16B(f32x4& acc, uint4 a, uint4 b) {
-  if constexpr (std::is_same_v<T, bf16>) {
-    union {
-      uint4 u;
-      bf16x8 v;
-    } x, y;
-    x.u = a;
-    y.u = b;
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.v, y.v, acc, 0, 0, 0);
-  } else {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
-  }
-}
-
 // Copy a [ROWS x COLS] tile from LDS (pitch lp) to global memory (row stride
 // gs elements) with every thread storing the same number of equal pieces, so
 // the store count per thread is a compile-time constant.  Rows >= nvalid are
@@ -196,7 +174,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
     lds_barrier();
     const int64_t cb = (int64_t)c * H + h;
     if constexpr (TRN)
-      tile_out<T, BV, K, NTH>(reinterpret_cast<T*>(a.hbufT) + (cb * V + vt * BV) * K, K, sHt, PK, BV, tid);
+      frag_out<T, BV, K, NTH>(reinterpret_cast<T*>(a.hbufT) + (cb * V + vt * BV) * K, sHt, PK, tid);
     if constexpr (NAT)
       tile_out<T, K, BV, NTH>(reinterpret_cast<T*>(a.hbuf) + cb * K * V + vt * BV, V, sS, PU, K, tid);
     // R = U - W S for token tile w (rows past the chunk's end are zero: W and
@@ -219,7 +197,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
     fetch_wu(ic<B>{}, c + DEPTH);
     lds_barrier();
     if constexpr (TRN)
-      tile_out<T, BV, CH, NTH>(reinterpret_cast<T*>(a.RT) + (cb * V + vt * BV) * CH, CH, sRt, PA, BV, tid);
+      frag_out<T, BV, CH, NTH>(reinterpret_cast<T*>(a.RT) + (cb * V + vt * BV) * CH, sRt, PA, tid);
     if constexpr (NAT)
       tile_out<T, CH, BV, NTH>(reinterpret_cast<T*>(a.R) + ((int64_t)bos * H + h) * V + vt * BV, gsV, sR,
                                PU, len, tid);

@@ -68,8 +68,8 @@ struct Args {
   void* Cqt;     // Cq^T                [nc,H,64,64] fragment order  reverse scan (Rbar += Cq^T dO)
   void* hbuf;    // state entering each chunk [nc,H,K,V] dtype
   void* R;       // corrections U - W S [BT,H,V] dtype
-  void* hbufT;   // the same states transposed [nc,H,V,K] (output kernel)
-  void* RT;      // R^T tiles [nc,H,V,64] (output kernel)
+  void* hbufT;   // the same states transposed [nc,H,V,K], fragment order (output kernel)
+  void* RT;      // R^T tiles [nc,H,V,64], fragment order (output kernel)
   int scan_out;  // SCAN_* bits: which of hbuf/R and hbufT/RT the forward scan writes
   void* At;      // A^T                 [nc,H,64,64] chunk backward (P = A^T Rbar)
   void* Kt;      // K^T                 [nc,H,K,64]  chunk backward
