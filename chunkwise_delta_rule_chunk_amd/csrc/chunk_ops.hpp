@@ -40,23 +40,19 @@ struct GateCols {
     c = tid % KC;
     seg = (tid / KC) % NSUB;
   }
-  // raw natural-log gates, features [k0, k0 + KC), of the chunk's n >= 1 rows.
-  // Every load is unconditional: rows past the end read row n - 1 and are
-  // zeroed by prefix_local(), so the loads' wait falls at that first use.
+  // raw natural-log gates, features [k0, k0 + KC), of the chunk's n >= 1 rows,
+  // through a bounds-checked buffer: rows past the end (and every row without
+  // a gate) read as zero.  One unconditional load per row, so the loads' wait
+  // falls at their first use.
   __device__ __forceinline__ void load(const Args& a, int64_t t0, int h, int n, int K, int k0) {
     const int H = a.H, r0 = seg * RS;
-    if (a.gate == 2) {
-      const float* gp = a.g + (t0 * H + h) * K + k0 + c;
+    const bool vec = a.gate == 2;
+    const int64_t rs = vec ? (int64_t)H * K : H;  // row stride, elements
+    const float* gb = vec ? a.g + (t0 * H + h) * K + k0 : a.g + t0 * H + h;
+    const GBuf b = gbuf(gb, a.gate == 0 ? 0u : tile_bytes<float>(n, rs, vec ? KC : 1));
+    const uint32_t rb = (uint32_t)(rs * 4), base = (uint32_t)r0 * rb + (vec ? c : 0) * 4;
 #pragma unroll
-      for (int r = 0; r < RS; ++r) G[r] = gp[(int64_t)min(r0 + r, n - 1) * H * K];
-    } else if (a.gate == 1) {
-      const float* gp = a.g + t0 * H + h;
-#pragma unroll
-      for (int r = 0; r < RS; ++r) G[r] = gp[(int64_t)min(r0 + r, n - 1) * H];
-    } else {
-#pragma unroll
-      for (int r = 0; r < RS; ++r) G[r] = 0.f;
-    }
+    for (int r = 0; r < RS; ++r) G[r] = __uint_as_float(gld4(b, base + r * rb));
   }
   // G2 = log2(e) * inclusive prefix over the chunk's n rows (rows past the end
   // add zero), in two halves around a barrier the caller places:

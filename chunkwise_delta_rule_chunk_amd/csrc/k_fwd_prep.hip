@@ -57,62 +57,86 @@ hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One persistent workgroup processes chunk-heads item = blockIdx.x + i*gridDim.x
-// (item = chunk * H + head).  The next item's k, q, v, g and beta are read into
-// registers while the current item computes, so HBM latency overlaps compute.
+// Persistent workgroups of four waves, two per compute unit, process
+// chunk-heads item = blockIdx.x + i*gridDim.x (item = chunk * H + head); while
+// one workgroup waits on memory, a barrier or the serial part of the solve,
+// the other computes.  LDS is two regions reused phase by phase (X: the raw,
+// then centred key and query operands, then A, then E^T and Z^T; Y: the
+// prefix totals, then L, then A in the operand type), which keeps a
+// workgroup within half of the compute unit's LDS.  The next item's k, q,
+// beta and gates are read into registers while the current item computes
+// (issued after the solve); the item's own v is read before it.
+//
 // MODE: the PREP_* sets this launch writes (a compile-time constant, so the
 // loop body holds no flag tests and no pointers of unused outputs).
 template <typename T, int K, int V, int MODE>
-__global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
-  constexpr int NTH = 512, NW = NTH / 64;
+__global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
+  constexpr int NTH = 256, NW = NTH / 64;
   constexpr bool BF = std::is_same_v<T, bf16>;
   constexpr int PK = pitch<T>(K);   // T rows of K
   constexpr int PL = CH + 4;        // fp32 rows of 64
   constexpr int PA = pitch<T>(CH);  // T rows of 64
   using GC = GateCols<K>;
   constexpr int RS = GC::RS;
+  constexpr int NSL = (GC::NG + NTH - 1) / NTH;  // gate slots (column, segment) per thread
+  constexpr int VE = 16 / (int)sizeof(T);
 
-  __shared__ __align__(16) T sK[CH * PK];   // raw k, then Kc in place
-  __shared__ __align__(16) T sQ[CH * PK];   // raw q, then Qa in place
-  __shared__ __align__(16) T sKa[CH * PK];
-  __shared__ __align__(16) float sL[CH * PL];
-  __shared__ __align__(16) float sA[CH * PL];
-  __shared__ __align__(16) T sAb[BF ? CH * PA : 8];
-  __shared__ __align__(16) T sEt[K * PA];   // E^T, [k][j]
-  __shared__ __align__(16) T sZt[V * PA];   // Z^T, [v][j]
+  constexpr int SZ_K = CH * PK * (int)sizeof(T), SZ_L = CH * PL * 4;
+  constexpr int SZ_ET = K * PA * (int)sizeof(T), SZ_ZT = V * PA * (int)sizeof(T);
+  // bf16: A (fp32) leaves X for Y, as the operand copy, before E^T and Z^T
+  // are written over it; fp32: A is the operand itself and stays beside them
+  constexpr int SZ_X = cmax(3 * SZ_K, BF ? cmax(SZ_L, SZ_ET + SZ_ZT) : SZ_L + SZ_ET + SZ_ZT);
+  constexpr int SZ_Y = cmax(SZ_L, NSUB * K * 4);
+  __shared__ __align__(16) char sX[SZ_X];
+  __shared__ __align__(16) char sY[SZ_Y];
   __shared__ __align__(16) float sFac[10 * K];
-  __shared__ float sTot[NSUB * K];
   __shared__ float sMid[NSUB * K], sGf[NSUB * K], sGl[NSUB * K], sGn[K];
   __shared__ float sBeta[CH];
   __shared__ int sFlag[NSUB];
+  T* const sK = reinterpret_cast<T*>(sX);  // S0-S3: raw k, then Kc in place
+  T* const sQ = sK + CH * PK;              //        raw q, then Qa in place
+  T* const sKa = sQ + CH * PK;             //        Ka
+  float* const sA = reinterpret_cast<float*>(sX);                      // S4-S5
+  T* const sEt = reinterpret_cast<T*>(sX + (BF ? 0 : SZ_L));           // S5: E^T [k][j]
+  T* const sZt = sEt + K * PA;                                         //     Z^T [v][j]
+  float* const sTot = reinterpret_cast<float*>(sY);                    // S0-S1
+  float* const sL = reinterpret_cast<float*>(sY);                      // S2-S4
+  T* const sAb = reinterpret_cast<T*>(sY);                             // S5 (bf16)
 
   const int H = a.H;
   const int total = a.nc_max * H;
   const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
 
-  GC gc, gnx;
-  gc.init(threadIdx.x);
-  gnx.init(threadIdx.x);
-  Staged<T, CH, K, NTH> pk, pq;
-  // v for Z^T: bf16 threads take rows (2p, 2p + 1), p = tid % 32, and the
-  // eight columns from 8 (tid / 32), so each Z^T write is one 4-byte pair of
+  // gate slots; their G registers hold the next item's raw gates from the end
+  // of the elementwise phase (their last use) to the next item's prefix
+  GC gc[NSL];
+#pragma unroll
+  for (int s = 0; s < NSL; ++s) gc[s].init(threadIdx.x + s * NTH);
+  TileRegs<T, CH, K, NTH> pk, pq;
+  // v for Z^T: bf16 threads take rows (2p, 2p + 1), p = slot % 32, and the
+  // eight columns from 8 (slot / 32), so each Z^T write is one 4-byte pair of
   // tokens (conflict-free across the wave); fp32 keeps the row-piece mapping
-  static constexpr int VSL = (CH / 2) * (V / 8);         // (row pair, column piece) slots
+  static constexpr int VSL = (CH / 2) * (V / 8);              // (row pair, column piece) slots
   static constexpr int VPT = BF ? (VSL + NTH - 1) / NTH : 1;  // slots per thread
   Staged<T, CH, V, NTH> pv;
   uint4 pv2[2 * VPT];
-  uint32_t pbeta = 0u;  // raw bits of the next item's beta for row tid
-  // the next item's inputs: k, q, v and beta as soon as the current ones are in
-  // LDS, the gates once the current gates are consumed
-  auto fetch_kqv = [&](int item, int tid) {
+  uint4 etr[NSL][RS / VE];  // E^T of this thread's rows, from the elementwise phase to S5
+  uint32_t pbeta = 0u;      // raw bits of the next item's beta for row tid
+  auto fetch_kq = [&](int item, int tid) {
     const int c = item / H, h = item - c * H;
     const ChunkInfo ci = load_chunk(a.chunks, c);
     if (ci.len == 0) return;
     const int64_t t0 = ci.bos;
-    pk.load(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, gsK, ci.len, tid);
-    pq.load(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, gsK, ci.len, tid);
+    pk.load(gbuf(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
+    pq.load(gbuf(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
+    pbeta = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, ci.len - 1)) * H + h);
+  };
+  auto fetch_v = [&](int item, int tid) {
+    const int c = item / H, h = item - c * H;
+    const ChunkInfo ci = load_chunk(a.chunks, c);
+    if (ci.len == 0) return;
+    const int64_t t0 = ci.bos;
     if constexpr (BF) {
-      // pair slot s = tid + j NTH: p = s % 32, column piece s / 32
       const GBuf bv = gbuf(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, tile_bytes<T>(ci.len, gsV, V));
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
@@ -124,27 +148,33 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     } else {
       pv.load(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, gsV, ci.len, tid);
     }
-    pbeta = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, ci.len - 1)) * H + h);
   };
   auto fetch_g = [&](int item) {
     const int c = item / H, h = item - c * H;
     const ChunkInfo ci = load_chunk(a.chunks, c);
     if (ci.len == 0) return;
-    gnx.load(a, (int64_t)ci.bos, h, ci.len, K, 0);
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) gc[s].load(a, (int64_t)ci.bos, h, ci.len, K, 0);
   };
 
   if (blockIdx.x < total) {
-    fetch_kqv(blockIdx.x, threadIdx.x);
+    fetch_kq(blockIdx.x, threadIdx.x);
     fetch_g(blockIdx.x);
   }
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int tid = opaque_tid(), w = wave_id();
+    // slot indices opaque per item: addresses derived from them are recomputed
+    // rather than hoisted out of the item loop (where they would stay live and
+    // spill)
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) asm volatile("" : "+v"(gc[s].c), "+v"(gc[s].seg));
     const int c = item / H, h = item - c * H;
     const ChunkInfo ci = load_chunk(a.chunks, c);
     const int n = ci.len;
+    const bool more = item + (int)gridDim.x < total;
     if (n == 0) {  // uniform: nothing was fetched for this slot
-      if (item + (int)gridDim.x < total) {
-        fetch_kqv(item + gridDim.x, tid);
+      if (more) {
+        fetch_kq(item + gridDim.x, tid);
         fetch_g(item + gridDim.x);
       }
       continue;
@@ -156,84 +186,46 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     pq.store(sQ, PK, tid);
     if (tid < CH) sBeta[tid] = tid < n ? beta_val(pbeta, a.beta_f32) : 0.f;
     if (tid < NSUB) sFlag[tid] = 0;
-    for (int idx = tid; idx < CH * PL / 4; idx += NTH) {
-      reinterpret_cast<f32x4*>(sL)[idx] = zero4();
-      reinterpret_cast<f32x4*>(sA)[idx] = zero4();
-    }
 #pragma unroll
-    for (int r = 0; r < RS; ++r) gc.G[r] = gnx.G[r];
-    gc.prefix_local(sTot, n);
+    for (int s = 0; s < NSL; ++s) gc[s].prefix_local(sTot, n);
     lds_barrier();
 
-    // ---- S1: finish the prefix, Z^T from the staged v, statistics ------------
-    gc.prefix_finish(sTot);
-    if constexpr (BF) {
-      // Z^T[v][j] = beta_j v[j][v], two tokens per 4-byte write
+    // ---- S1: finish the prefix, statistics ----------------------------------
 #pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        const int sl = tid + j * NTH, p = sl % 32, c0 = (sl / 32) * 8;
-        if (sl >= VSL) continue;
-        union {
-          uint4 u;
-          T e[8];
-        } v0, v1;
-        v0.u = pv2[2 * j];
-        v1.u = pv2[2 * j + 1];
-        const float b0 = sBeta[2 * p], b1 = sBeta[2 * p + 1];
+    for (int s = 0; s < NSL; ++s) gc[s].prefix_finish(sTot);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          union {
-            uint32_t u;
-            T h[2];
-          } z;
-          z.h[0] = fromf<T>(b0 * tof(v0.e[e]));
-          z.h[1] = fromf<T>(b1 * tof(v1.e[e]));
-          *reinterpret_cast<uint32_t*>(sZt + (c0 + e) * PA + 2 * p) = z.u;
-        }
-      }
-    } else {
-      constexpr int VEC = 4, PER = V / VEC;
-#pragma unroll
-      for (int j = 0; j < decltype(pv)::N; ++j) {
-        const int idx = tid + j * NTH;
-        const int r = idx / PER, c0 = (idx - r * PER) * VEC;
-        if (idx < CH * PER) {
-          union {
-            uint4 u;
-            T e[VEC];
-          } val;
-          val.u = pv.r[j];
-          const float b = sBeta[r];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) sZt[(c0 + e) * PA + r] = fromf<T>(b * tof(val.e[e]));
-        }
-      }
-    }
-    // the staged registers are free: read the next item while this one computes
-    const bool more = item + (int)gridDim.x < total;
-    if (more) fetch_kqv(item + gridDim.x, tid);
-    subchunk_stats_regs(gc, n, sMid, sGf, sGl, sGn, sFlag,
-                        (MODE & PREP_BWD_CHUNK) ? reinterpret_cast<f32x4*>(a.Gst) + cb * NSUB * K
-                                                : nullptr);
+    for (int s = 0; s < NSL; ++s)
+      subchunk_stats_regs(gc[s], n, sMid, sGf, sGl, sGn, sFlag,
+                          (MODE & PREP_BWD_CHUNK) ? reinterpret_cast<f32x4*>(a.Gst) + cb * NSUB * K
+                                                  : nullptr);
     lds_barrier();
 
     // ---- S2: pair factors; element-wise outputs and centred operands --------
+    // the prefix totals are dead: L starts from zeros (strict upper parts and
+    // the blocks past the chunk's end are never written)
+    for (int idx = tid; idx < CH * PL / 4; idx += NTH) reinterpret_cast<f32x4*>(sL)[idx] = zero4();
     pair_factors<K>(sMid, sGf, sGl, sFlag, sFac, n, tid, NTH);
-    if (gc.on) {
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) {
+      // one slot at a time: interleaving the slots' element-wise work would
+      // double the registers it holds live
+      __builtin_amdgcn_sched_barrier(0);
+      GC& g = gc[s];
+      if (!g.on) continue;
       // opaque per item: keeps the compiler from hoisting these addresses out of
       // the item loop (they would have to stay live, and spill, across items)
-      int col = gc.c;
+      int col = g.c;
       asm volatile("" : "+v"(col));
       // the thread's 16 rows lie in sub-chunk seg, the same for the whole wave
       // when a wave spans one segment (K >= 64)
-      const int r0 = K >= 64 ? __builtin_amdgcn_readfirstlane(gc.seg * RS) : gc.seg * RS;
+      const int r0 = K >= 64 ? __builtin_amdgcn_readfirstlane(g.seg * RS) : g.seg * RS;
       const float gn = sGn[col];
       // a segment wholly past the chunk's end has no statistics; its rows hold
       // G2 = gn exactly (the prefix adds zeros there), so gn as both references
       // makes both factors 1
       const bool seg_live = r0 < n;
-      const float rA = seg_live ? ref_recv(sMid, sGf, sFlag, gc.seg, K, col) : gn;
-      const float rB = seg_live ? ref_send(sMid, sGl, sFlag, gc.seg, K, col) : gn;
+      const float rA = seg_live ? ref_recv(sMid, sGf, sFlag, g.seg, K, col) : gn;
+      const float rB = seg_live ? ref_send(sMid, sGl, sFlag, g.seg, K, col) : gn;
       // two exponentials per row: ea = exp2(G - rA), eb = exp2(rB - G); then
       // gamma = exp2(G) = ea exp2(rA) and exp2(gn - G) = eb exp2(gn - rB), with
       // exp2(rA) <= 1 and exp2(gn - rB) <= 1.  Values that flush to zero this
@@ -241,10 +233,10 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       // hold k = q = beta = 0 and come out as zeros.
       const float cA = fexp2(rA), cB = fexp2(gn - rB);
       const float bs = a.scale;
-      constexpr int VE = 16 / (int)sizeof(T);
-      // F^T in operand-fragment order (see kernels.hpp): 16 k rows x KG tokens
-      // per fragment, this thread's VE-token groups are single 16-byte pieces
-      constexpr int KGF = 4 * (16 / (int)sizeof(T)), NGTF = CH / KGF;
+      // F^T and Qg^T in operand-fragment order (see kernels.hpp): 16 k rows x
+      // KG tokens per fragment, this thread's VE-token groups are single
+      // 16-byte pieces
+      constexpr int KGF = 4 * VE, NGTF = CH / KGF;
       T* Ftd = reinterpret_cast<T*>(a.Ft) + cb * K * CH;
       T* Qgtd = reinterpret_cast<T*>(a.Qgt) + cb * K * CH;
       T* Ktd = reinterpret_cast<T*>(a.Kt) + (cb * K + col) * CH + r0;
@@ -257,7 +249,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
       // thread's 16 rows are elements VE apart in one column of pieces
       constexpr int NGKF = K / KGF;
       T* Fd = reinterpret_cast<T*>(a.F) + cb * CH * K +
-              ((gc.seg * NGKF + col / KGF) * 64 + ((col % KGF) / VE) * 16) * VE + col % VE;
+              ((g.seg * NGKF + col / KGF) * 64 + ((col % KGF) / VE) * 16) * VE + col % VE;
       const uint32_t rowb = (uint32_t)(gsK * (int64_t)sizeof(T)), colb = col * (int)sizeof(T);
 #pragma unroll
       for (int r8 = 0; r8 < RS; r8 += VE) {
@@ -271,7 +263,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
           const T kraw = sK[row * PK + col], qraw = sQ[row * PK + col];
           kt.e[e] = kraw;  // raw k and q (zero past the chunk's end)
           qq.e[e] = qraw;
-          const float G = gc.G[r];
+          const float G = g.G[r];
           const float kr = tof(kraw), qr = tof(qraw);
           const float ea = fexp2(G - rA), eb = fexp2(rB - G);
           const float vKa = sBeta[row] * kr * ea, vQa = bs * qr * ea, vKc = kr * eb;
@@ -289,15 +281,14 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
           ft.e[e] = fromf<T>(vF);
           qt.e[e] = fromf<T>(vQg);
         }
-        // token-contiguous tiles: this thread holds consecutive tokens of column col
-        *reinterpret_cast<uint4*>(sEt + col * PA + r0 + r8) = et.u;
+        etr[s][r8 / VE] = et.u;  // E^T reaches LDS in S5
         if constexpr (MODE & PREP_FWD_SCAN) {
-          const int tk = r0 + r8, q = tk / KGF, g = (tk % KGF) / VE;
-          *reinterpret_cast<uint4*>(Ftd + (((col / SUB) * NGTF + q) * 64 + g * 16 + col % SUB) * VE) = ft.u;
+          const int tk = r0 + r8, q = tk / KGF, gq = (tk % KGF) / VE;
+          *reinterpret_cast<uint4*>(Ftd + (((col / SUB) * NGTF + q) * 64 + gq * 16 + col % SUB) * VE) = ft.u;
         }
         if constexpr (MODE & PREP_BWD_SCAN) {
-          const int tk = r0 + r8, q = tk / KGF, g = (tk % KGF) / VE;
-          *reinterpret_cast<uint4*>(Qgtd + (((col / SUB) * NGTF + q) * 64 + g * 16 + col % SUB) * VE) = qt.u;
+          const int tk = r0 + r8, q = tk / KGF, gq = (tk % KGF) / VE;
+          *reinterpret_cast<uint4*>(Qgtd + (((col / SUB) * NGTF + q) * 64 + gq * 16 + col % SUB) * VE) = qt.u;
         }
         if constexpr (MODE & PREP_BWD_CHUNK) {
           *reinterpret_cast<uint4*>(Ktd + r8) = kt.u;
@@ -311,14 +302,11 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         if (G2d)
 #pragma unroll
           for (int r4 = 0; r4 < RS; r4 += 4)
-            *reinterpret_cast<f32x4*>(G2d + r4) =
-                f32x4{gc.G[r4], gc.G[r4 + 1], gc.G[r4 + 2], gc.G[r4 + 3]};
+            *reinterpret_cast<f32x4*>(G2d + r4) = f32x4{g.G[r4], g.G[r4 + 1], g.G[r4 + 2], g.G[r4 + 3]};
       }
       if constexpr ((MODE & (PREP_FWD_SCAN | PREP_BWD_SCAN)) != 0)
-        if (gc.seg == 0) a.glast[cb * K + col] = gn;
+        if (g.seg == 0) a.glast[cb * K + col] = gn;
     }
-    // the gate registers are free: read the next item's gates
-    if (more) fetch_g(item + gridDim.x);
     lds_barrier();
 
     // ---- S3: score tiles L (strict, fp32 in LDS) and Cq (inclusive, global) --
@@ -355,7 +343,22 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     lds_barrier();
 
     // ---- S4: A = (I + L)^-1 in fp32 ------------------------------------------
+
+    // A takes X (the score operands are dead); its off-diagonal blocks start
+    // at zero, written here while wave 0 forms the diagonal blocks
+    for (int idx = tid; idx < NSUB * NSUB * SUB * 4; idx += NTH) {
+      const int blk = idx / (SUB * 4), I = blk / NSUB, J = blk - I * NSUB;
+      const int rem = idx - blk * SUB * 4, rr = rem >> 2, c4 = (rem & 3) * 4;
+      if (I != J) *reinterpret_cast<f32x4*>(sA + (I * SUB + rr) * PL + J * SUB + c4) = zero4();
+    }
     solve_unit_lower(sL, sA, PL, n);
+    // this item's v; the next item's k, q, beta and gates (the gate registers
+    // are free since the elementwise phase), covered by S5
+    fetch_v(item, tid);
+    if (more) {
+      fetch_kq(item + gridDim.x, tid);
+      fetch_g(item + gridDim.x);
+    }
     if constexpr (MODE & PREP_BWD_CHUNK) {  // A^T for the chunk backward, 16-byte rows
       constexpr int VA = 16 / (int)sizeof(T), PER = CH / VA;
       T* Ato = reinterpret_cast<T*>(a.At) + cb * CH * CH;
@@ -372,13 +375,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
     }
 
     // ---- S5: W = A E, U = A Z --------------------------------------------------
-    // W and U in operand-fragment order (see kernels.hpp), all 64 rows (rows
-    // past the chunk's end are exact zeros)
-    T* Wfo = reinterpret_cast<T*>(a.W) + cb * CH * K;
-    T* Ufo = reinterpret_cast<T*>(a.U) + cb * CH * V;
-    T* Wto = reinterpret_cast<T*>(a.Wt) + cb * K * CH;
-    constexpr bool wantW = MODE & PREP_FWD_SCAN, wantWt = MODE & PREP_BWD_SCAN, wantU = wantW;
-    if constexpr (BF) {
+    if constexpr (BF) {  // A to the operand type, into Y (L is dead)
       for (int idx = tid; idx < CH * CH / 4; idx += NTH) {
         const int i = idx / (CH / 4), j = (idx - i * (CH / 4)) * 4;
         const f32x4 x = *reinterpret_cast<const f32x4*>(sA + i * PL + j);
@@ -387,44 +384,104 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
         for (int e = 0; e < 4; ++e) y[e] = (bf16)x[e];
         *reinterpret_cast<bf16x4*>(sAb + i * PA + j) = y;
       }
-      lds_barrier();
+      lds_barrier();  // A in fp32 is dead: E^T and Z^T go over it
     }
-    // staging of W: the score operands in sKa are dead once A is formed
-    T* sWs = sKa;
+    // E^T from the registers of the elementwise phase
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) {
+      if (!gc[s].on) continue;
+      const int col = gc[s].c, r0 = gc[s].seg * RS;
+#pragma unroll
+      for (int r8 = 0; r8 < RS; r8 += VE)
+        *reinterpret_cast<uint4*>(sEt + col * PA + r0 + r8) = etr[s][r8 / VE];
+    }
+    // Z^T = (beta v)^T from the staged v
+    if constexpr (BF) {
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int sl = tid + j * NTH, p = sl % 32, c0 = (sl / 32) * 8;
+        if (sl >= VSL) continue;
+        union {
+          uint4 u;
+          T e[8];
+        } v0, v1;
+        v0.u = pv2[2 * j];
+        v1.u = pv2[2 * j + 1];
+        const float b0 = sBeta[2 * p], b1 = sBeta[2 * p + 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          union {
+            uint32_t u;
+            T hh[2];
+          } z;
+          z.hh[0] = fromf<T>(b0 * tof(v0.e[e]));
+          z.hh[1] = fromf<T>(b1 * tof(v1.e[e]));
+          *reinterpret_cast<uint32_t*>(sZt + (c0 + e) * PA + 2 * p) = z.u;
+        }
+      }
+    } else {
+      constexpr int VEC = 4, PER = V / VEC;
+#pragma unroll
+      for (int j = 0; j < decltype(pv)::N; ++j) {
+        const int idx = tid + j * NTH;
+        const int r = idx / PER, c0 = (idx - r * PER) * VEC;
+        if (idx < CH * PER) {
+          union {
+            uint4 u;
+            T e[VEC];
+          } val;
+          val.u = pv.r[j];
+          const float b = sBeta[r];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) sZt[(c0 + e) * PA + r] = fromf<T>(b * tof(val.e[e]));
+        }
+      }
+    }
+    lds_barrier();
+
+    // W, U in operand-fragment order (see kernels.hpp), all 64 rows (rows past
+    // the chunk's end are exact zeros).  W for the forward scan comes from
+    // W^T tiles, whose C fragments are the 16-long A fragments of W.
+    T* Wfo = reinterpret_cast<T*>(a.W) + cb * CH * K;
+    T* Ufo = reinterpret_cast<T*>(a.U) + cb * CH * V;
+    T* Wto = reinterpret_cast<T*>(a.Wt) + cb * K * CH;
+    constexpr bool wantW = MODE & PREP_FWD_SCAN, wantWt = MODE & PREP_BWD_SCAN, wantU = wantW;
     const T* Aop = BF ? (const T*)sAb : (const T*)sA;
     constexpr int PAo = BF ? PA : PL;
-    const int NCB = (K + (wantU ? V : 0)) / SUB;
-    for (int cbk = w; cbk < NCB; cbk += NW) {
-      const bool isW = cbk < K / SUB;
-      if (isW && !wantW && !wantWt) continue;
-      const int col = isW ? cbk * SUB : (cbk - K / SUB) * SUB;
-      const T* Bop = (isW ? sEt : sZt) + col * PA;
-      static_for<0, NSUB>([&](auto II) {
-        constexpr int I = decltype(II)::value;
-        f32x4 acc = zero4();
-        // A is lower triangular: row block I needs tokens < 16 (I + 1) only
-        constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
-        mma_tile<T, true, true>(acc, Aop + (I * SUB) * PAo, PAo, 1, Bop, PA, 1, kd);
-        if (isW) {
-          if (wantW) st_tile<T>(acc, sWs + (I * SUB) * PK + col, PK, 1);
-          if (wantWt) st_frag_T<T>(acc, Wto, I, col / SUB);
-        } else {
-          // the C tile is the fragment piece: lane l holds rows 16 I + 4 (l >> 4) + i
-          // of column col + (l & 15)
-          using FR = typename Frag4<T>::type;
+    constexpr int NKB = K / SUB, GPP = 16 / (4 * (int)sizeof(T));  // 16-long groups per piece
+    constexpr int NJ0 = wantW ? NKB : 0, NJ1 = wantWt ? NKB : 0, NJ2 = wantU ? V / SUB : 0;
+    using FR = typename Frag4<T>::type;
+    for (int job = w; job < NJ0 + NJ1 + NJ2; job += NW) {
+      if (job < NJ0) {  // W^T, key block kb: C tile rows 16 kb + 4 (l >> 4) + i, token 16 I + (l & 15)
+        const int kb = job;
+        const T* Ea = sEt + (kb * SUB) * PA;
+        static_for<0, NSUB>([&](auto II) {
+          constexpr int I = decltype(II)::value;
+          f32x4 acc = zero4();
+          // A is lower triangular: token block I needs tokens < 16 (I + 1) only
+          constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
+          mma_tile<T, true, true>(acc, Ea, PA, 1, Aop + (I * SUB) * PAo, PAo, 1, kd);
+          *reinterpret_cast<FR*>(Wfo + (((I * (NKB / GPP) + kb / GPP) * 64 + lane_id()) * GPP + kb % GPP) * 4) =
+              to_frag<T>(acc);
+        });
+      } else if (job < NJ0 + NJ1) {  // W, key block kb, for W^T in fragment order
+        const int col = (job - NJ0) * SUB;
+        static_for<0, NSUB>([&](auto II) {
+          constexpr int I = decltype(II)::value;
+          f32x4 acc = zero4();
+          constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
+          mma_tile<T, true, true>(acc, Aop + (I * SUB) * PAo, PAo, 1, sEt + col * PA, PA, 1, kd);
+          st_frag_T<T>(acc, Wto, I, col / SUB);
+        });
+      } else {  // U, value block: the C tile is the fragment piece
+        const int col = (job - NJ0 - NJ1) * SUB;
+        static_for<0, NSUB>([&](auto II) {
+          constexpr int I = decltype(II)::value;
+          f32x4 acc = zero4();
+          constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
+          mma_tile<T, true, true>(acc, Aop + (I * SUB) * PAo, PAo, 1, sZt + col * PA, PA, 1, kd);
           *reinterpret_cast<FR*>(Ufo + (((col / SUB) * NSUB + I) * 64 + lane_id()) * 4) = to_frag<T>(acc);
-        }
-      });
-    }
-    // W leaves through LDS: fragment piece p = (16-row block, key group, lane)
-    // is row 16 tw + (lane & 15), keys KG q + VE (lane >> 4) .. + VE - 1
-    if constexpr (wantW) {
-      lds_barrier();
-      constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE, NGK = K / KG;
-      for (int idx = tid; idx < CH * K / VE; idx += NTH) {
-        const int ln = idx % 64, blk = idx / 64, tw = blk / NGK, q = blk - tw * NGK;
-        const int row = SUB * tw + (ln & 15), k0 = KG * q + VE * (ln >> 4);
-        *reinterpret_cast<uint4*>(Wfo + idx * VE) = *reinterpret_cast<const uint4*>(sWs + row * PK + k0);
+        });
       }
     }
     lds_barrier();  // LDS is rewritten by the next item
@@ -434,7 +491,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep(Args a) {
 template <typename T, int MODE>
 static hipError_t prep_m(const Args& a, hipStream_t s) {
   const int items = a.nc_max * a.H;
-  const dim3 grid(std::min(items, persistent_grid()), 1), block(512);
+  const dim3 grid(std::min(items, 2 * persistent_grid()), 1), block(256);
   REWY_KV_SWITCH_X(k_fwd_prep, MODE)
 }
 

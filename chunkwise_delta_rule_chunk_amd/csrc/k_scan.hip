@@ -96,7 +96,9 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
   // W, F^T and U are stored in operand-fragment order (kernels.hpp), rows past
   // a chunk's end as exact zeros: every read below is one contiguous piece.
   using FR = typename Frag4<T>::type;
-  uint4 wf[DEPTH][NGK];      // W rows 16 w + r16, lane piece of every key group
+  constexpr int GPP = 16 / (int)sizeof(FR);  // 16-long key groups per W piece
+  static_assert(NGK * GPP == K / SUB, "W pieces");
+  uint4 wf[DEPTH][NGK];      // W rows 16 w + r16, GPP 16-long key groups per piece
   FR uf[DEPTH][CT];          // U in the C layout of R's tiles
   uint4 ff[DEPTH][KW][NGT];  // F^T rows 16 ktile + r16, lane piece of every token group
   f32x4 lam[DEPTH][KW];      // G2_last of the state rows this lane holds
@@ -178,13 +180,26 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
     if constexpr (NAT)
       tile_out<T, K, BV, NTH>(reinterpret_cast<T*>(a.hbuf) + cb * K * V + vt * BV, V, sS, PU, K, tid);
     // R = U - W S for token tile w (rows past the chunk's end are zero: W and
-    // U are zero there)
+    // U are zero there).  A W piece holds, for lane l (row l & 15), the keys
+    // 16 kb + 4 (l >> 4) + e of GPP consecutive 16-key groups kb.  bf16 takes
+    // both groups as one 32-slot fragment (slot 8 (l >> 4) + 4 hh + e is key
+    // 32 q + 16 hh + 4 (l >> 4) + e) and reads S^T with the same assignment;
+    // fp32 runs each group as four 16x16x4 steps.
 #pragma unroll
     for (int m = 0; m < CT; ++m) {
       f32x4 p = zero4();
-      const T* hb = sHt + (SUB * m + r16) * PK + VE * g;
+      const T* hb = sHt + (SUB * m + r16) * PK + 4 * g;
 #pragma unroll
-      for (int q = 0; q < NGK; ++q) mma16B<T>(p, wf[B][q], *reinterpret_cast<const uint4*>(hb + KG * q));
+      for (int q = 0; q < NGK; ++q) {
+        if constexpr (std::is_same_v<T, bf16>) {
+          const bf16x4 s0 = *reinterpret_cast<const bf16x4*>(hb + 32 * q);
+          const bf16x4 s1 = *reinterpret_cast<const bf16x4*>(hb + 32 * q + SUB);
+          const bf16x8 sb = __builtin_shufflevector(s0, s1, 0, 1, 2, 3, 4, 5, 6, 7);
+          p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[B][q]), sb, p, 0, 0, 0);
+        } else {
+          mm16(p, __builtin_bit_cast(f32x4, wf[B][q]), *reinterpret_cast<const f32x4*>(hb + SUB * q));
+        }
+      }
       f32x4 rv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

@@ -49,7 +49,9 @@ struct Args {
   // [64 x K] or [64 x V] tile per (chunk, head), so that each MFMA operand a
   // wave needs is one contiguous load of 16 bytes per lane (VE = 16 / sizeof
   // element, KG = 4 VE contraction slots per fragment, lane l, e < VE):
-  //   W  piece ((tw * K/KG + q) * 64 + l) holds W[16 tw + (l & 15)][KG q + VE (l >> 4) + e]
+  //   W  piece ((tw * K/(16 GPP) + q) * 64 + l) holds, GPP = 16 / (4 sizeof element) groups
+  //      of four, W[16 tw + (l & 15)][16 (GPP q + hh) + 4 (l >> 4) + e], hh < GPP, e < 4
+  //      (the C fragments of W^T tiles, which are the 16-long A fragments of W)
   //   Ft piece ((tk * 64/KG + q) * 64 + l) holds F[KG q + VE (l >> 4) + e][16 tk + (l & 15)]
   //   U  piece ((tv * 4 + tw) * 64 + l) holds U[16 tw + 4 (l >> 4) + i][16 tv + (l & 15)], i < 4
   // (U in the C-fragment layout of the R tile it is subtracted from).  The
