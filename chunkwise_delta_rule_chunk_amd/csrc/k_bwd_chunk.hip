@@ -229,7 +229,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   const f32x4 bI = *reinterpret_cast<const f32x4*>(sBeta + I * SUB + 4 * q4);
   f32x4 sufs = zero4();  // scalar gate: Gbar summed over features, this lane's rows
   float dbe[4] = {0.f, 0.f, 0.f, 0.f};
-  float pdq[4] = {0.f, 0.f, 0.f, 0.f}, pdk[4] = {0.f, 0.f, 0.f, 0.f};
+  // dq, dk of the previous (even) feature block, transposed (see below)
+  FR pdq = to_frag<T>(zero4()), pdk = to_frag<T>(zero4());
+  // identity as the B operand of a 16-long product: C = X^T I turns this
+  // lane's C-tile values (rows 4 q4 + e, feature f) into the transposed
+  // layout (row f, features 4 q4 .. + 3), exactly (one term per output)
+  f32x4 idf;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) idf[e] = (4 * q4 + e == f) ? 1.f : 0.f;
+  const FR idt = to_frag<T>(idf);
   float lam0s = 0.f, lamws = 0.f;
 
   // registers of the next block's operands (loaded during this block's
@@ -452,30 +460,35 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       lamw += __shfl_xor(lamw, 16);
       lamw += __shfl_xor(lamw, 32);
     }
-    // dq, dk of an even feature block wait for the next block, so that both
+    // dq, dk of this block, transposed by one product with the identity: lane
+    // (q4, f) then holds row 16 I + f, features 16 fb + 4 q4 .. + 3, one 8-byte
+    // piece (16 bytes in fp32).  An even block waits for the next one, so both
     // halves of each 64-byte row segment are written together; the stores are
     // issued in every block (even blocks and rows past the end fall outside
     // the buffers and are dropped), which keeps the loop's memory operations
-    // the same on every path
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = lrow + e;
+    // the same on every path.
+    {
+      f32x4 tq = zero4(), tk = zero4();
+      mm16(tq, to_frag<T>(f32x4{oq[0], oq[1], oq[2], oq[3]}), idt);
+      mm16(tk, to_frag<T>(f32x4{ok_[0], ok_[1], ok_[2], ok_[3]}), idt);
+      const FR yq = to_frag<T>(tq), yk = to_frag<T>(tk);
       const bool odd = fb & 1;
-      const uint32_t o1 = odd ? (uint32_t)(((int64_t)row * gsK + kc - SUB) * (int64_t)sizeof(T)) : OOB;
-      const uint32_t o2 = odd ? (uint32_t)(((int64_t)row * gsK + kc) * (int64_t)sizeof(T)) : OOB;
+      const int64_t tb = (int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4;
+      const uint32_t o1 = odd ? (uint32_t)((tb - SUB) * (int64_t)sizeof(T)) : OOB;
+      const uint32_t o2 = odd ? (uint32_t)(tb * (int64_t)sizeof(T)) : OOB;
       if constexpr (std::is_same_v<T, bf16>) {
-        gst2(bdq, o1, __builtin_bit_cast(uint16_t, fromf<T>(pdq[e])));
-        gst2(bdq, o2, __builtin_bit_cast(uint16_t, fromf<T>(oq[e])));
-        gst2(bdk, o1, __builtin_bit_cast(uint16_t, fromf<T>(pdk[e])));
-        gst2(bdk, o2, __builtin_bit_cast(uint16_t, fromf<T>(ok_[e])));
+        gst8(bdq, o1, __builtin_bit_cast(uint2, pdq));
+        gst8(bdq, o2, __builtin_bit_cast(uint2, yq));
+        gst8(bdk, o1, __builtin_bit_cast(uint2, pdk));
+        gst8(bdk, o2, __builtin_bit_cast(uint2, yk));
       } else {
-        gst4(bdq, o1, __float_as_uint(pdq[e]));
-        gst4(bdq, o2, __float_as_uint(oq[e]));
-        gst4(bdk, o1, __float_as_uint(pdk[e]));
-        gst4(bdk, o2, __float_as_uint(ok_[e]));
+        gst16(bdq, o1, __builtin_bit_cast(uint4, pdq));
+        gst16(bdq, o2, __builtin_bit_cast(uint4, yq));
+        gst16(bdk, o1, __builtin_bit_cast(uint4, pdk));
+        gst16(bdk, o2, __builtin_bit_cast(uint4, yk));
       }
-      pdq[e] = oq[e];
-      pdk[e] = ok_[e];
+      pdq = yq;
+      pdk = yk;
     }
     if (a.gate == 2) {
       // in-block reverse sum: own rows, then the lane groups after this one
@@ -502,10 +515,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         add += sLam[buf][J * SUB + f];
         if (J > I) add += sTot[buf][J * SUB + f];
       }
+      // transposed like dq (in fp32, exactly): one 16-byte piece per lane;
       // rows past the end (all rows of a wave past the end) are dropped
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        gst4(bdg, (uint32_t)(((int64_t)(lrow + e) * gsK + kc) * 4), __float_as_uint(suf[e] + add));
+      f32x4 tg = zero4();
+      mm16(tg, f32x4{suf[0] + add, suf[1] + add, suf[2] + add, suf[3] + add}, idf);
+      gst16(bdg, (uint32_t)(((int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4) * 4), __builtin_bit_cast(uint4, tg));
     } else if (a.gate == 1 && live) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
