@@ -42,8 +42,16 @@ __global__ __launch_bounds__(256) void k_fwd_out(Args a) {
   pq.store(sQg, PK, tid);
   pc.store(sCq, PA, tid);
   lds_barrier();
-  T* og = reinterpret_cast<T*>(a.o) + (t0 * H + h) * V;
+  // o through a bounds-checked buffer (rows past the chunk's end are dropped)
+  const GBuf bo = gbuf(reinterpret_cast<T*>(a.o) + (t0 * H + h) * V, tile_bytes<T>(len, gsV, V));
   const int r16 = l & 15, g = l >> 4;
+  using FR = typename Frag4<T>::type;
+  // identity as the B operand of a 16-long product: C = X^T I turns the C
+  // tile (rows 4 g + e, column r16) into row r16, columns 4 g .. + 3, exactly
+  f32x4 idf;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) idf[e] = (4 * g + e == r16) ? 1.f : 0.f;
+  const FR idt = to_frag<T>(idf);
   static_for<0, VPW>([&](auto jj) {
     constexpr int j = decltype(jj)::value;
     const int vb = w + 4 * j;
@@ -60,7 +68,11 @@ __global__ __launch_bounds__(256) void k_fwd_out(Args a) {
       const T* ca = sCq + (I * SUB + r16) * PA + VE * g;
 #pragma unroll
       for (int q = 0; q < nq; ++q) mma16B<T>(acc, *reinterpret_cast<const uint4*>(ca + KG * q), rf[j][q]);
-      st_tile<T>(acc, og + (I * SUB) * gsV + vb * SUB, (int)gsV, 1, len - I * SUB);
+      f32x4 tr = zero4();
+      mm16(tr, to_frag<T>(acc), idt);
+      const uint32_t off = (uint32_t)(((int64_t)(I * SUB + r16) * gsV + vb * SUB + 4 * g) * (int64_t)sizeof(T));
+      if constexpr (std::is_same_v<T, bf16>) gst8(bo, off, __builtin_bit_cast(uint2, to_frag<T>(tr)));
+      else gst16(bo, off, __builtin_bit_cast(uint4, tr));
     });
   });
 }
