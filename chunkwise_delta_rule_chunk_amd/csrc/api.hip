@@ -109,7 +109,7 @@ struct Layout {
 Layout layout(const Plan& p) {
   Layout L{};
   const size_t nc = p.nc_max, H = p.H, K = p.K, V = p.V, BT = p.BT, e = p.esz;
-  const size_t tokK = BT * H * K * e, tokV = BT * H * V * e;
+  const size_t tokK = BT * H * K * e;
   const size_t tileK = nc * H * K * CH * e, tileV = nc * H * V * CH * e;
   const size_t tile64 = nc * H * CH * CH * e;
   const size_t g2 = p.gate == REWY_GATE_VECTOR ? nc * H * K * CH * 4
@@ -134,7 +134,7 @@ Layout layout(const Plan& p) {
   size_t s = save ? 0 : off;
   L.glast = take(s, nc * H * K * 4);
   L.hbuf = take(s, nc * H * K * V * e);
-  L.R = take(s, tokV);
+  L.R = take(s, tileV);
   if (save) {
     take_reverse(s);
     L.saved = s;

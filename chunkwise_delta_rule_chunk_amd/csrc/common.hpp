@@ -457,6 +457,29 @@ struct TileRegs {
       if (idx < TOTAL) *reinterpret_cast<uint4*>(s + row * ls + c) = r[j];
     }
   }
+  // The same tile from a column-blocked matrix [COLS/16][rt rows][16] (each
+  // 16-column block row-major): rows row0 .. row0 + ROWS - 1.  Consecutive
+  // threads take consecutive pieces of one block, so a wave reads contiguous
+  // memory; store_cb() puts each piece at its row and column in LDS.
+  static constexpr int SP = 16 / VEC;  // pieces per row of a block
+  static_assert(COLS % 16 == 0, "column blocks of 16");
+  __device__ __forceinline__ void load_cb(const GBuf& b, int rt, int row0, int tid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = tid + j * NTH;
+      const int sub = idx % SP, rr = (idx / SP) % ROWS, blk = idx / (SP * ROWS);
+      r[j] = gld16(b, idx < TOTAL ? (uint32_t)((((int64_t)blk * rt + row0 + rr) * 16 + sub * VEC) * (int64_t)sizeof(T))
+                                  : OOB);
+    }
+  }
+  __device__ __forceinline__ void store_cb(T* s, int ls, int tid) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = tid + j * NTH;
+      const int sub = idx % SP, rr = (idx / SP) % ROWS, blk = idx / (SP * ROWS);
+      if (idx < TOTAL) *reinterpret_cast<uint4*>(s + rr * ls + blk * 16 + sub * VEC) = r[j];
+    }
+  }
 };
 
 // beta may be stored as bf16 or fp32 independently of the feature dtype.

@@ -91,11 +91,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
     TileRegs<T, CH, V, NTH> pO, pR;
     TileRegs<T, CH, CH, NTH> pA;
     pO.load(gbuf(reinterpret_cast<const T*>(a.dO) + (t0 * H + h) * V, tile_bytes<T>(n, gsV, V)), gsV, tid);
-    pR.load(gbuf(reinterpret_cast<const T*>(a.R) + (t0 * H + h) * V, tile_bytes<T>(n, gsV, V)), gsV, tid);
+    // R per chunk-head, column-blocked [V/16][64][16], zero past the chunk's end
+    pR.load_cb(gbuf(reinterpret_cast<const T*>(a.R) + cb * V * CH, V * CH * sizeof(T)), CH, 0, tid);
     pA.load(gbuf(reinterpret_cast<const T*>(a.At) + cb * CH * CH, CH * CH * sizeof(T)), CH, tid);
     const uint32_t braw = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, n - 1)) * H + h);
     pO.store(sO, PV, tid);
-    pR.store(sR, PV, tid);
+    pR.store_cb(sR, PV, tid);
     pA.store(sAt, PA, tid);
     if (tid < CH) sBeta[tid] = tid < n ? beta_val(braw, a.beta_f32) : 0.f;
   }
@@ -118,35 +119,51 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       if constexpr (std::is_same_v<T, bf16>) vr[vb] = gld8(bv, off);
       else vr[vb] = gld16(bv, off);
     });
+    // Rbar is stored in the C-fragment order of its 16 x 16 tiles [token block
+    // T][v block]: lane l's piece of tile (vb, T) holds Rbar[16 T + 4 (l >> 4) + e]
+    // [16 vb + (l & 15)], e < 4, which is the 16-long A fragment of Rbar^T.
+    const GBuf brb = gbuf(Rbt, V * CH * sizeof(T));
+    auto rb_off = [&](int vb, int tb, bool use) {
+      return use ? (uint32_t)((((vb * NSUB + tb) * 64 + l) * 4) * (int)sizeof(T)) : OOB;
+    };
     f32x4 acc[NVB];
     if constexpr (std::is_same_v<T, bf16>) {
-      // bf16: at most two 32-token steps; every Rbar fragment is requested up
-      // front (unused steps read as zero)
-      const GBuf brb = gbuf(Rbt, V * CH * sizeof(T));
+      // bf16: at most two 32-token steps, every Rbar fragment requested up
+      // front (unused steps read as zero).  A step joins token blocks 2 st and
+      // 2 st + 1: slots 8 q4 + e take token 32 st + 4 q4 + e and slots
+      // 8 q4 + 4 + e token 32 st + 16 + 4 q4 + e, in both operands.
       bf16x8 rb[NVB][2];
       static_for<0, NVB>([&](auto vb) {
         static_for<0, 2>([&](auto st) {
-          const uint32_t off = (live && st * 32 >= k0)
-                                   ? (uint32_t)(((vb * SUB + f) * CH + st * 32 + 8 * q4) * sizeof(T))
-                                   : OOB;
-          const uint4 x = gld16(brb, off);
-          rb[vb][st] = __builtin_bit_cast(bf16x8, x);
+          const bool use = live && st * 32 >= k0;
+          const uint2 x0 = gld8(brb, rb_off(vb, 2 * st, use)), x1 = gld8(brb, rb_off(vb, 2 * st + 1, use));
+          rb[vb][st] = __builtin_bit_cast(bf16x8, uint4{x0.x, x0.y, x1.x, x1.y});
         });
       });
       lds_barrier();
-      const bf16x8 at0 = ldfrag<T, true>(sAt + I * SUB * PA, PA, 1, 0);
-      const bf16x8 at1 = ldfrag<T, true>(sAt + I * SUB * PA, PA, 1, 32);
+      auto atf = [&](int st) {
+        const T* p = sAt + (I * SUB + f) * PA + 32 * st + 4 * q4;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p), hi = *reinterpret_cast<const bf16x4*>(p + SUB);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      const bf16x8 at0 = atf(0), at1 = atf(1);
       static_for<0, NVB>([&](auto vb) {
         acc[vb] = mma(rb[vb][1], at1, zero4());
         if (k0 == 0) acc[vb] = mma(rb[vb][0], at0, acc[vb]);
       });
     } else {
+      // fp32: one 16-token product per token block T >= I (A^T is upper
+      // triangular), the others read as zero
       lds_barrier();
       static_for<0, NVB>([&](auto vb) {
+        f32x4 rb[NSUB];
+        static_for<0, NSUB>([&](auto tb) {
+          rb[tb] = __builtin_bit_cast(f32x4, gld16(brb, rb_off(vb, tb, live && tb >= I)));
+        });
         acc[vb] = zero4();
-        if (live)
-          mma_tile<T, true, true>(acc[vb], Rbt + vb * SUB * CH + k0, CH, 1,
-                                  sAt + I * SUB * PA + k0, PA, 1, CH - k0);
+        static_for<0, NSUB>([&](auto tb) {
+          mm16(acc[vb], rb[tb], *reinterpret_cast<const f32x4*>(sAt + (I * SUB + f) * PA + SUB * tb + 4 * q4));
+        });
       });
     }
     const float b = sBeta[i];
@@ -255,8 +272,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
     pK.load(gbuf(Ktg + (int64_t)fb * SUB * CH, SUB * CH * sizeof(T)), CH, tid);
     pQ.load(gbuf(Qtg + (int64_t)fb * SUB * CH, SUB * CH * sizeof(T)), CH, tid);
     pX.load(gbuf(Gstg + fb * SUB * 4, tile_bytes<float>(NSUB, K * 4, SUB * 4)), K * 4, tid);
-    pS.load(gbuf(hb + (int64_t)fb * SUB * V, SUB * V * sizeof(T)), V, tid);
-    pD.load(gbuf(dhb + (int64_t)fb * SUB * V, SUB * V * sizeof(T)), V, tid);
+    pS.load_cb(gbuf(hb, K * V * sizeof(T)), K, fb * SUB, tid);
+    pD.load_cb(gbuf(dhb, K * V * sizeof(T)), K, fb * SUB, tid);
     pN.load(gbuf(a.glast + cb * K + fb * SUB, SUB * sizeof(float)), SUB, tid);
   };
   auto put_fb = [&]() {
@@ -264,8 +281,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
     pK.store(sKs, PKS, tid);
     pQ.store(sQs, PKS, tid);
     pX.store(sSt, SUB * 4, tid);
-    pS.store(sSs, PSS, tid);
-    pD.store(sDs, PSS, tid);
+    pS.store_cb(sSs, PSS, tid);
+    pD.store_cb(sDs, PSS, tid);
     pN.store(sGn, SUB, tid);
   };
   fetch_fb(0);

@@ -30,29 +30,6 @@ namespace rewy {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-// Copy a [ROWS x COLS] tile from LDS (pitch lp) to global memory (row stride
-// gs elements) with every thread storing the same number of equal pieces, so
-// the store count per thread is a compile-time constant.  Rows >= nvalid are
-// redirected to row nvalid - 1 (the same bytes written twice), which keeps
-// the stores unconditional.
-template <typename T, int ROWS, int COLS, int NTH>
-__device__ __forceinline__ void tile_out(T* g, int64_t gs, const T* s, int lp, int nvalid, int tid) {
-  constexpr int BYTES = ROWS * COLS * (int)sizeof(T);
-  constexpr int PB = BYTES / NTH >= 16 ? 16 : BYTES / NTH;  // bytes per piece
-  static_assert(PB == 16 || PB == 8, "piece size");
-  constexpr int E = PB / (int)sizeof(T), PER = COLS / E, NP = BYTES / (PB * NTH);
-  static_assert(COLS % E == 0 && BYTES % (PB * NTH) == 0, "tile split");
-#pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    const int idx = tid + j * NTH;
-    const int r = min(idx / PER, nvalid - 1), c = (idx % PER) * E;
-    if constexpr (PB == 16)
-      *reinterpret_cast<uint4*>(g + (int64_t)r * gs + c) = *reinterpret_cast<const uint4*>(s + r * lp + c);
-    else
-      *reinterpret_cast<uint2*>(g + (int64_t)r * gs + c) = *reinterpret_cast<const uint2*>(s + r * lp + c);
-  }
-}
-
 // Forward scan.  Wave w owns token tile w of R (all value columns of the
 // workgroup) and a set of key tiles of the state; it reads the W rows and F^T
 // rows it contracts straight from global memory into MFMA operand registers
@@ -72,20 +49,16 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
   constexpr bool WIDE = NKT >= 4;
   constexpr int KW = WIDE ? NKT / 4 : 1, CW = WIDE ? CT : CT * NKT / 4;
   static_assert(WIDE || (NKT == 2 && CT == 2), "state tile split");
-  constexpr int PK = pitch<T>(K), PA = pitch<T>(CH), PU = pitch<T>(BV);
+  constexpr int PK = pitch<T>(K), PA = pitch<T>(CH);
   __shared__ __align__(16) T sHt[BV * PK];        // S_c as operand, [v][k]
   __shared__ __align__(16) T sRt[BV * PA];        // R_c as operand, [v][i]
-  __shared__ __align__(16) T sS[NAT ? K * PU : 8];   // S_c, natural layout
-  __shared__ __align__(16) T sR[NAT ? CH * PU : 8];  // R_c, natural layout
 
   const int H = a.H;
   const int u = blockIdx.x, vt = blockIdx.y;
   const int n = u / H, h = u - n * H;
   const int w = wave_id(), tid = threadIdx.x, l = lane_id();
   const int r16 = l & 15, g = l >> 4;
-  const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
   const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
-  const int seq_bos = a.cu ? a.cu[n] : n * a.T, seq_eos = a.cu ? a.cu[n + 1] : (n + 1) * a.T;
   const T* Wg = reinterpret_cast<const T*>(a.W);
   const T* Ftg = reinterpret_cast<const T*>(a.Ft);
   const T* Ug = reinterpret_cast<const T*>(a.U);
@@ -97,13 +70,20 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
   // a chunk's end as exact zeros: every read below is one contiguous piece.
   using FR = typename Frag4<T>::type;
   constexpr int GPP = 16 / (int)sizeof(FR);  // 16-long key groups per W piece
+  // identity as the B operand of a 16-long product: C = X^T I turns a C tile
+  // (rows 4 g + e, column r16) into row r16, columns 4 g .. + 3, exactly; the
+  // natural-layout S_c and R_c leave the registers that way, 8 (bf16) or 16
+  // (fp32) bytes of one row per lane
+  f32x4 idf;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) idf[e] = (4 * g + e == r16) ? 1.f : 0.f;
+  const FR idt = to_frag<T>(idf);
   static_assert(NGK * GPP == K / SUB, "W pieces");
   uint4 wf[DEPTH][NGK];      // W rows 16 w + r16, GPP 16-long key groups per piece
   FR uf[DEPTH][CT];          // U in the C layout of R's tiles
   uint4 ff[DEPTH][KW][NGT];  // F^T rows 16 ktile + r16, lane piece of every token group
   f32x4 lam[DEPTH][KW];      // G2_last of the state rows this lane holds
   // past the last chunk the last one is read again (valid memory, never used)
-  auto chunk_bos = [&](int c) { return seq_bos + (min(c, c1 - 1) - c0) * CH; };
   auto fetch_wu = [&](auto set, int c) {
     constexpr int B = decltype(set)::value;
     const int64_t cb = (int64_t)min(c, c1 - 1) * H + h;
@@ -157,8 +137,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
 
   auto step = [&](auto buf, int c) {
     constexpr int B = decltype(buf)::value;
-    const int bos = chunk_bos(c), len = min(CH, seq_eos - bos);
-    // S_c: operand [v][k] and, for global memory, natural [k][v]
+    const int64_t cb = (int64_t)c * H + h;
+    // S_c: operand [v][k] in LDS and, for global memory, natural [k][v]
 #pragma unroll
     for (int j = 0; j < KW; ++j)
 #pragma unroll
@@ -166,19 +146,18 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
         const int kr = SUB * ktile(j), vc = SUB * vtile(m);
         f32x4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const T y = fromf<T>(st[j][m][i]);
-          x[i] = tof(y);
-          if constexpr (NAT) sS[(kr + 4 * g + i) * PU + vc + r16] = y;
-        }
+        for (int i = 0; i < 4; ++i) x[i] = tof(fromf<T>(st[j][m][i]));
         st_tile_T<T>(x, sHt + vc * PK + kr, PK);
+        if constexpr (NAT) {  // column-blocked [V/16][K][16]: a wave writes 16 whole block rows
+          f32x4 tr = zero4();
+          mm16(tr, to_frag<T>(x), idt);
+          *reinterpret_cast<FR*>(reinterpret_cast<T*>(a.hbuf) + cb * K * V +
+                                 ((int64_t)(vt * CT + vtile(m)) * K + kr + r16) * SUB + 4 * g) = to_frag<T>(tr);
+        }
       }
     lds_barrier();
-    const int64_t cb = (int64_t)c * H + h;
     if constexpr (TRN)
       frag_out<T, BV, K, NTH>(reinterpret_cast<T*>(a.hbufT) + (cb * V + vt * BV) * K, sHt, PK, tid);
-    if constexpr (NAT)
-      tile_out<T, K, BV, NTH>(reinterpret_cast<T*>(a.hbuf) + cb * K * V + vt * BV, V, sS, PU, K, tid);
     // R = U - W S for token tile w (rows past the chunk's end are zero: W and
     // U are zero there).  A W piece holds, for lane l (row l & 15), the keys
     // 16 kb + 4 (l >> 4) + e of GPP consecutive 16-key groups kb.  bf16 takes
@@ -202,20 +181,19 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
       }
       f32x4 rv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const T x = fromf<T>(tof(uf[B][m][i]) - p[i]);
-        if constexpr (NAT) sR[(SUB * w + 4 * g + i) * PU + SUB * m + r16] = x;
-        rv[i] = tof(x);
-      }
+      for (int i = 0; i < 4; ++i) rv[i] = tof(fromf<T>(tof(uf[B][m][i]) - p[i]));
       st_tile_T<T>(rv, sRt + (SUB * m) * PA + SUB * w, PA);
+      if constexpr (NAT) {  // column-blocked [V/16][64][16], all 64 rows (zero past the end)
+        f32x4 tr = zero4();
+        mm16(tr, to_frag<T>(rv), idt);
+        *reinterpret_cast<FR*>(reinterpret_cast<T*>(a.R) + cb * V * CH +
+                               ((int64_t)(vt * CT + m) * CH + SUB * w + r16) * SUB + 4 * g) = to_frag<T>(tr);
+      }
     }
     fetch_wu(ic<B>{}, c + DEPTH);
     lds_barrier();
     if constexpr (TRN)
       frag_out<T, BV, CH, NTH>(reinterpret_cast<T*>(a.RT) + (cb * V + vt * BV) * CH, sRt, PA, tid);
-    if constexpr (NAT)
-      tile_out<T, CH, BV, NTH>(reinterpret_cast<T*>(a.R) + ((int64_t)bos * H + h) * V + vt * BV, gsV, sR,
-                               PU, len, tid);
     // S = diag(exp2 G2_last) S + F^T R
 #pragma unroll
     for (int j = 0; j < KW; ++j) {
@@ -267,13 +245,12 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
   constexpr bool WIDE = NKT >= 4;
   constexpr int KW = WIDE ? NKT / 4 : 1, CW = WIDE ? CT : CT * NKT / 4;
   static_assert(WIDE || (NKT == 2 && CT == 2), "state tile split");
-  constexpr int PK = pitch<T>(K), PA = pitch<T>(CH), PS = pitch<T>(BV);
+  constexpr int PK = pitch<T>(K), PA = pitch<T>(CH);
   // dO rows as staged by the threads: 8-byte pieces (4 elements)
   constexpr int OE = 8 / (int)sizeof(T), OPER = BV / OE;
   constexpr int ON = CH * BV * (int)sizeof(T) / (NTH * 8);  // dO pieces per thread
   static_assert(ON >= 1 && CH * BV * (int)sizeof(T) == NTH * 8 * ON, "dO staging split");
   __shared__ __align__(16) T sDt[BV * PK];      // dS_{c+1} as operand, [v][k]
-  __shared__ __align__(16) T sD[K * PS];        // dS_{c+1}, natural layout
   __shared__ __align__(16) T sOt[2][BV * PA];   // dO_c as operand, [v][j]
   __shared__ __align__(16) T sRbt[BV * PA];     // Rbar_c as operand, [v][i]
 
@@ -282,9 +259,9 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
   const int n = u / H, h = u - n * H;
   const int w = wave_id(), tid = threadIdx.x, l = lane_id();
   const int r16 = l & 15, g = l >> 4;
-  const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
   const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
   const int seq_bos = a.cu ? a.cu[n] : n * a.T, seq_eos = a.cu ? a.cu[n + 1] : (n + 1) * a.T;
+  const int64_t gsV = (int64_t)H * V;
   auto ktile = [&](int j) { return WIDE ? w + 4 * j : w % NKT; };
   auto vtile = [&](int m) { return WIDE ? m : (w / NKT) * CW + m; };
 
@@ -294,6 +271,13 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
   uint4 wf[DEPTH][KW][NGT];  // W^T row 16 ktile + r16 (tokens)
   f32x4 lam[DEPTH][KW];
   uint2 of[DEPTH][ON];       // dO pieces
+  using FR = typename Frag4<T>::type;
+  // identity as the B operand of a 16-long product (C = X^T I, exact): the
+  // natural-layout dS_{c+1} leaves the registers as pieces of one row
+  f32x4 idf;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) idf[e] = (4 * g + e == r16) ? 1.f : 0.f;
+  const FR idt = to_frag<T>(idf);
   // chunks are walked from the last; before the first one the first is read
   // again (valid memory, never used)
   auto chunk_of = [&](int c) { return max(c, c0); };
@@ -372,12 +356,12 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
         const int kr = SUB * ktile(j), vc = SUB * vtile(m);
         f32x4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const T y = fromf<T>(st[j][m][i]);
-          x[i] = tof(y);
-          sD[(kr + 4 * g + i) * PS + vc + r16] = y;
-        }
+        for (int i = 0; i < 4; ++i) x[i] = tof(fromf<T>(st[j][m][i]));
         st_tile_T<T>(x, sDt + vc * PK + kr, PK);
+        f32x4 tr = zero4();  // column-blocked [V/16][K][16]
+        mm16(tr, to_frag<T>(x), idt);
+        *reinterpret_cast<FR*>(reinterpret_cast<T*>(a.dhbuf) + cb * K * V +
+                               ((int64_t)(vt * CT + vtile(m)) * K + kr + r16) * SUB + 4 * g) = to_frag<T>(tr);
       }
 #pragma unroll
     for (int e = 0; e < ON; ++e) {
@@ -391,7 +375,6 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
       for (int k = 0; k < OE; ++k) sOt[B][(c8 + k) * PA + r] = r < len ? x.v[k] : fromf<T>(0.f);
     }
     lds_barrier();
-    tile_out<T, K, BV, NTH>(reinterpret_cast<T*>(a.dhbuf) + cb * K * V + vt * BV, V, sD, PS, K, tid);
     // Rbar = F dS+ + Cq^T dO for token tile w (rows past the end are zero: F
     // and Cq vanish there)
 #pragma unroll
@@ -404,9 +387,12 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
 #pragma unroll
       for (int q = 0; q < NGT; ++q) mma16B<T>(acc, cf[B][q], *reinterpret_cast<const uint4*>(ob + KG * q));
       st_tile_T<T>(acc, sRbt + (SUB * m) * PA + SUB * w, PA);
+      // Rbar in the C-fragment order of its 16 x 16 tiles: a wave writes one
+      // contiguous tile
+      *reinterpret_cast<FR*>(reinterpret_cast<T*>(a.Rbt) + cb * V * CH +
+                             (((int64_t)(vt * CT + m) * NSUB + w) * 64 + l) * 4) = to_frag<T>(acc);
     }
     lds_barrier();
-    tile_out<T, BV, CH, NTH>(reinterpret_cast<T*>(a.Rbt) + (cb * V + vt * BV) * CH, CH, sRbt, PA, BV, tid);
     // dS = diag(exp2 G2_last) dS+ + Qg^T dO - W^T Rbar (W^T negated by its sign bits)
 #pragma unroll
     for (int j = 0; j < KW; ++j) {

@@ -68,8 +68,8 @@ struct Args {
   void* Wt;      // W^T                 [nc,H,K,64] fragment order   reverse scan (dS -= W^T Rbar)
   void* Qgt;     // Qg^T                [nc,H,K,64] fragment order   reverse scan (dS += Qg^T dO)
   void* Cqt;     // Cq^T                [nc,H,64,64] fragment order  reverse scan (Rbar += Cq^T dO)
-  void* hbuf;    // state entering each chunk [nc,H,K,V] dtype
-  void* R;       // corrections U - W S [BT,H,V] dtype
+  void* hbuf;    // state entering each chunk [nc,H,V/16,K,16] dtype (column-blocked)
+  void* R;       // corrections U - W S [nc,H,V/16,64,16] dtype (column-blocked, zero past the end)
   void* hbufT;   // the same states transposed [nc,H,V,K], fragment order (output kernel)
   void* RT;      // R^T tiles [nc,H,V,64], fragment order (output kernel)
   int scan_out;  // SCAN_* bits: which of hbuf/R and hbufT/RT the forward scan writes
@@ -80,8 +80,8 @@ struct Args {
   float* Gst;    // sub-chunk gate statistics [nc,H,4,K] of float4 {G2 at the first row,
                  // G2 at the last valid row, midpoint (max+min)/2, range max-min}
   // backward intermediates
-  void* Rbt;     // correction adjoint Rbar^T [nc,H,V,64] dtype
-  void* dhbuf;   // adjoint of the state leaving each chunk [nc,H,K,V] dtype
+  void* Rbt;     // correction adjoint Rbar [nc,H,V/16,4,64 lanes,4] dtype, C-fragment order of its 16x16 tiles
+  void* dhbuf;   // adjoint of the state leaving each chunk [nc,H,V/16,K,16] dtype (column-blocked)
 };
 
 constexpr int SCAN_NATURAL = 1;     // hbuf, R (read by the chunk backward)

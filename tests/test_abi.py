@@ -82,7 +82,8 @@ def test_workspace_sizes_follow_the_layout(lib):
     tokK, tokV = up(BT * H * K * e), up(BT * H * V * e)
     tileK, tile64 = up(nc * H * K * 64 * e), up(nc * H * 64 * 64 * e)
     head = up(nc * 16) + up(2 * 4)
-    shared = up(nc * H * K * 4) + up(nc * H * K * V * e) + tokV        # glast, hbuf, R
+    tileV = up(nc * H * V * 64 * e)
+    shared = up(nc * H * K * 4) + up(nc * H * K * V * e) + tileV       # glast, hbuf, R
     scan = tokK + tileK + tokV                                          # W, Ft, U
     out = tokK + tile64 + up(nc * H * K * V * e) + up(nc * H * V * 64 * e)  # Qg, Cq, hbufT, RT
     rscan = tokK + 2 * tileK + tile64                                   # F, Wt, Qgt, Cqt
