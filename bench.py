@@ -57,11 +57,15 @@ def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy
         "k_bwd_chunk": n * 3 * tv + tile64 + tileV + 2 * st + 2 * tileK + g2t + gst + n * besz
                        + n * (2 * tk + tv + gb + besz),
     }
+    # the backward's forward scan and reverse scan in one launch
+    per_head["k_scans"] = per_head["k_fwd_scan"] + per_head["k_bwd_scan"]
     for name, b in per_head.items():
         if f"{len(name)}{name}I" in kernel:
             extra = 0
             if name in ("k_fwd_scan", "k_bwd_scan"):
                 extra = nseq * 2 * 4 * K * V  # initial / final state (fp32) per sequence
+            elif name == "k_scans":
+                extra = nseq * 4 * 4 * K * V
             return b * H + extra * H
     return None
 
@@ -214,7 +218,7 @@ def main():
     gate = {"none": 0, "scalar": 1, "vector": 2}[inp.gate]
     dbytes = kernel_bytes(dom, chunk_lens, H, K, V, esz, besz, gate, len(seq_lens), args.policy)
     achieved = dbytes / (dom_avg * 1e-3) / 1e9 if dbytes else None
-    short = next((k for k in ("k_fwd_prep", "k_fwd_scan", "k_fwd_out", "k_bwd_scan", "k_bwd_chunk")
+    short = next((k for k in ("k_fwd_prep", "k_fwd_scan", "k_fwd_out", "k_bwd_scan", "k_bwd_chunk", "k_scans")
                   if f"{len(k)}{k}I" in dom), dom)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": None if achieved is None else achieved / PEAK_HBM_GBS,

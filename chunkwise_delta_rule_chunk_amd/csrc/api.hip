@@ -246,7 +246,7 @@ hipError_t traced(const char* stage, int variant, hipStream_t s, F&& launch) {
 int variant_of(const Args& a, bool f32) { return (f32 ? 1000000 : 0) + a.K * 1000 + a.V; }
 
 // Forward chunk stages shared by rewy_fwd and the recompute in rewy_bwd.
-int run_forward_stages(const Args& a, bool f32, bool with_output, hipStream_t s) {
+int run_forward_stages(const Args& a, bool f32, bool with_scan, bool with_output, hipStream_t s) {
   int rc;
   const int vr = variant_of(a, f32);
   if ((rc = hip_check(traced("k_chunk_table", -1, s, [&] { return launch_chunk_table(a, s); }),
@@ -255,7 +255,8 @@ int run_forward_stages(const Args& a, bool f32, bool with_output, hipStream_t s)
   if ((rc = hip_check(traced("k_fwd_prep", vr, s, [&] { return launch_fwd_prep(a, f32, s); }),
                       "forward prep")))
     return rc;
-  if ((rc = hip_check(traced("k_fwd_scan", vr, s, [&] { return launch_fwd_scan(a, f32, s); }),
+  if (with_scan &&
+      (rc = hip_check(traced("k_fwd_scan", vr, s, [&] { return launch_fwd_scan(a, f32, s); }),
                       "forward scan")))
     return rc;
   if (with_output &&
@@ -313,7 +314,7 @@ REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const vo
   a.prep_mode = PREP_FWD_SCAN | PREP_FWD_OUT |
                 (p.policy == REWY_SAVE ? PREP_BWD_SCAN | PREP_BWD_CHUNK : 0);
   a.scan_out = SCAN_TRANSPOSED | (p.policy == REWY_SAVE ? SCAN_NATURAL : 0);
-  return run_forward_stages(a, p.f32, true, s);
+  return run_forward_stages(a, p.f32, true, true, s);
 }
 
 REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const void* v,
@@ -355,15 +356,19 @@ REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const vo
   const bool f32 = p.f32;
   const int vr = variant_of(a, f32);
   if (p.policy == REWY_RECOMPUTE) {
-    if ((rc = run_forward_stages(a, f32, false, s))) return rc;
-  } else if ((rc = hip_check(traced("k_chunk_table", -1, s,
-                                    [&] { return launch_chunk_table(a, s); }),
-                             "chunk table"))) {
-    return rc;
+    // prep again, then the forward scan and the reverse scan side by side
+    if ((rc = run_forward_stages(a, f32, false, false, s))) return rc;
+    if ((rc = hip_check(traced("k_scans", vr, s, [&] { return launch_scans(a, f32, s); }),
+                        "forward and reverse scans")))
+      return rc;
+  } else {
+    if ((rc = hip_check(traced("k_chunk_table", -1, s, [&] { return launch_chunk_table(a, s); }),
+                        "chunk table")))
+      return rc;
+    if ((rc = hip_check(traced("k_bwd_scan", vr, s, [&] { return launch_bwd_scan(a, f32, s); }),
+                        "reverse scan")))
+      return rc;
   }
-  if ((rc = hip_check(traced("k_bwd_scan", vr, s, [&] { return launch_bwd_scan(a, f32, s); }),
-                      "reverse scan")))
-    return rc;
   if ((rc = hip_check(traced("k_bwd_chunk", vr, s, [&] { return launch_bwd_chunk(a, f32, s); }),
                       "chunk backward")))
     return rc;

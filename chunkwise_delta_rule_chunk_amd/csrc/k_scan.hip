@@ -38,7 +38,7 @@ using ic = std::integral_constant<int, V>;
 // (clamped indices, selects): the compiler then counts exactly which loads a
 // use has to wait for, and the prefetches stay in flight across steps.
 template <typename T, int K, int V, int BV, int OUT>
-__global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
+__device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const int vt) {
   constexpr int NTH = 256, DEPTH = 2;
   constexpr bool NAT = OUT & SCAN_NATURAL, TRN = OUT & SCAN_TRANSPOSED;
   constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE;  // elements per lane piece, per group
@@ -54,7 +54,6 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
   __shared__ __align__(16) T sRt[BV * PA];        // R_c as operand, [v][i]
 
   const int H = a.H;
-  const int u = blockIdx.x, vt = blockIdx.y;
   const int n = u / H, h = u - n * H;
   const int w = wave_id(), tid = threadIdx.x, l = lane_id();
   const int r16 = l & 15, g = l >> 4;
@@ -237,7 +236,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
 // go straight from global memory into operand registers; dS_{c+1}, dO_c
 // (transposed) and Rbar_c pass through LDS.
 template <typename T, int K, int V, int BV>
-__global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
+__device__ __forceinline__ void bwd_scan_wg(const Args& a, const int u, const int vt) {
   constexpr int NTH = 256, DEPTH = 2;
   constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE;
   constexpr int CT = BV / SUB, NKT = K / SUB;
@@ -255,7 +254,6 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
   __shared__ __align__(16) T sRbt[BV * PA];     // Rbar_c as operand, [v][i]
 
   const int H = a.H;
-  const int u = blockIdx.x, vt = blockIdx.y;
   const int n = u / H, h = u - n * H;
   const int w = wave_id(), tid = threadIdx.x, l = lane_id();
   const int r16 = l & 15, g = l >> 4;
@@ -429,6 +427,26 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
   final_out();
 }
 
+template <typename T, int K, int V, int BV, int OUT>
+__global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
+  fwd_scan_wg<T, K, V, BV, OUT>(a, blockIdx.x, blockIdx.y);
+}
+template <typename T, int K, int V, int BV>
+__global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
+  bwd_scan_wg<T, K, V, BV>(a, blockIdx.x, blockIdx.y);
+}
+// Both scans of the backward under recompute in one launch: they read
+// disjoint operands and write disjoint outputs, so the forward recompute scan
+// (grid z = 0) and the reverse scan (z = 1) run side by side, each on its own
+// share of the CUs.  Wider value tiles halve the operand reads of each scan.
+template <typename T, int K, int V, int BV>
+__global__ __launch_bounds__(256) void k_scans(Args a) {
+  if (blockIdx.z == 0)
+    fwd_scan_wg<T, K, V, BV, SCAN_NATURAL>(a, blockIdx.x, blockIdx.y);
+  else
+    bwd_scan_wg<T, K, V, BV>(a, blockIdx.x, blockIdx.y);
+}
+
 int scan_bv(const Args& a, int f32) {
   if (a.K == 32) return 32;  // four waves need K * BV >= 1024
   if (f32) return 16;        // keeps the fp32 double buffers within LDS
@@ -492,6 +510,33 @@ hipError_t launch_bwd_scan(const Args& a, int f32, hipStream_t s) {
   const bool w32 = scan_bv(a, f32) == 32;
   if (f32) return w32 ? bwd_scan_bv<float, 32>(a, s) : bwd_scan_bv<float, 16>(a, s);
   return w32 ? bwd_scan_bv<bf16, 32>(a, s) : bwd_scan_bv<bf16, 16>(a, s);
+}
+
+template <typename T, int BV>
+static hipError_t scans_bv(const Args& a, hipStream_t s) {
+  const dim3 grid(a.N * a.H, a.V / BV, 2), block(256);
+#define REWY_SCAN_CASE(K_, V_)                                                  \
+  case K_ * 1000 + V_:                                                          \
+    if constexpr (kv_ok<T, K_, V_>() && V_ >= BV && K_ * BV >= 1024 &&          \
+                  (sizeof(T) == 2 || K_ == 32 || BV == 16)) {                   \
+      hipLaunchKernelGGL((k_scans<T, K_, V_, BV>), grid, block, 0, s, a);       \
+      return hipGetLastError();                                                 \
+    } else {                                                                    \
+      return hipErrorInvalidValue;                                              \
+    }
+  switch (a.K * 1000 + a.V) {
+    REWY_SCAN_CASE(32, 32) REWY_SCAN_CASE(32, 64) REWY_SCAN_CASE(32, 128)
+    REWY_SCAN_CASE(64, 32) REWY_SCAN_CASE(64, 64) REWY_SCAN_CASE(64, 128)
+    REWY_SCAN_CASE(128, 32) REWY_SCAN_CASE(128, 64) REWY_SCAN_CASE(128, 128)
+    default: return hipErrorInvalidValue;
+  }
+#undef REWY_SCAN_CASE
+}
+// 32-wide value tiles wherever the kernels allow them (fp32 keeps 16 for LDS)
+hipError_t launch_scans(const Args& a, int f32, hipStream_t s) {
+  if (a.scan_out != SCAN_NATURAL) return hipErrorInvalidValue;
+  if (f32) return a.K == 32 ? scans_bv<float, 32>(a, s) : scans_bv<float, 16>(a, s);
+  return scans_bv<bf16, 32>(a, s);
 }
 
 }  // namespace rewy
