@@ -265,21 +265,24 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   TileRegs<float, NSUB, SUB * 4, NTH> pX;
   TileRegs<T, SUB, V, NTH> pS, pD;
   TileRegs<float, 1, SUB, NTH> pN;
+  // G2^T, K^T and Q^T are column-blocked [64/16][K][16] (a scalar gate: one
+  // row, [64]; rows 1 .. 15 of its tile are not used)
+  const float* gp = a.gate == 2 ? a.G2t + cb * K * CH : a.G2t + cb * CH;
+  const int grt = a.gate == 2 ? K : 1;
+  const uint32_t gbytes = a.gate == 2 ? K * CH * 4 : a.gate == 1 ? CH * 4 : 0;
   auto fetch_fb = [&](int fb) {
-    const float* gp = a.gate == 2 ? a.G2t + (cb * K + fb * SUB) * CH : a.G2t + cb * CH;
-    const int grows = a.gate == 2 ? SUB : a.gate == 1 ? 1 : 0;
-    pG.load(gbuf(gp, tile_bytes<float>(grows, CH, CH)), CH, tid);
-    pK.load(gbuf(Ktg + (int64_t)fb * SUB * CH, SUB * CH * sizeof(T)), CH, tid);
-    pQ.load(gbuf(Qtg + (int64_t)fb * SUB * CH, SUB * CH * sizeof(T)), CH, tid);
+    pG.load_cb(gbuf(gp, gbytes), grt, a.gate == 2 ? fb * SUB : 0, tid);
+    pK.load_cb(gbuf(Ktg, K * CH * sizeof(T)), K, fb * SUB, tid);
+    pQ.load_cb(gbuf(Qtg, K * CH * sizeof(T)), K, fb * SUB, tid);
     pX.load(gbuf(Gstg + fb * SUB * 4, tile_bytes<float>(NSUB, K * 4, SUB * 4)), K * 4, tid);
     pS.load_cb(gbuf(hb, K * V * sizeof(T)), K, fb * SUB, tid);
     pD.load_cb(gbuf(dhb, K * V * sizeof(T)), K, fb * SUB, tid);
     pN.load(gbuf(a.glast + cb * K + fb * SUB, SUB * sizeof(float)), SUB, tid);
   };
   auto put_fb = [&]() {
-    if (a.gate != 0) pG.store(sG2, PGS, tid);
-    pK.store(sKs, PKS, tid);
-    pQ.store(sQs, PKS, tid);
+    if (a.gate != 0) pG.store_cb(sG2, PGS, tid);
+    pK.store_cb(sKs, PKS, tid);
+    pQ.store_cb(sQs, PKS, tid);
     pX.store(sSt, SUB * 4, tid);
     pS.store_cb(sSs, PSS, tid);
     pD.store_cb(sDs, PSS, tid);

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void k_fwd_out(Args a) {
   TileRegs<T, CH, K, 256> pq;
   TileRegs<T, CH, CH, 256> pc;
   pq.load(gbuf(reinterpret_cast<const T*>(a.Qg) + (t0 * H + h) * K, tile_bytes<T>(len, gsK, K)), gsK, tid);
-  pc.load(gbuf(reinterpret_cast<const T*>(a.Cq) + cb * CH * CH, CH * CH * sizeof(T)), CH, tid);
+  pc.load_cb(gbuf(reinterpret_cast<const T*>(a.Cq) + cb * CH * CH, CH * CH * sizeof(T)), CH, 0, tid);
   uint4 sf[VPW][NGK], rf[VPW][NGT];
   static_for<0, VPW>([&](auto jj) {
     constexpr int j = decltype(jj)::value;
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void k_fwd_out(Args a) {
     for (int q = 0; q < NGT; ++q) rf[j][q] = *reinterpret_cast<const uint4*>(rp + q * 64 * VE);
   });
   pq.store(sQg, PK, tid);
-  pc.store(sCq, PA, tid);
+  pc.store_cb(sCq, PA, tid);
   lds_barrier();
   // o through a bounds-checked buffer (rows past the chunk's end are dropped)
   const GBuf bo = gbuf(reinterpret_cast<T*>(a.o) + (t0 * H + h) * V, tile_bytes<T>(len, gsV, V));

@@ -239,8 +239,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
       constexpr int KGF = 4 * VE, NGTF = CH / KGF;
       T* Ftd = reinterpret_cast<T*>(a.Ft) + cb * K * CH;
       T* Qgtd = reinterpret_cast<T*>(a.Qgt) + cb * K * CH;
-      T* Ktd = reinterpret_cast<T*>(a.Kt) + (cb * K + col) * CH + r0;
-      T* Qtd = reinterpret_cast<T*>(a.Qt) + (cb * K + col) * CH + r0;
+      // K^T, Q^T, G2^T column-blocked [64/16][K][16]: this thread's 16 rows are
+      // one block row, and a wave's consecutive columns are contiguous
+      T* Ktd = reinterpret_cast<T*>(a.Kt) + cb * K * CH + ((int64_t)g.seg * K + col) * SUB;
+      T* Qtd = reinterpret_cast<T*>(a.Qt) + cb * K * CH + ((int64_t)g.seg * K + col) * SUB;
       // natural-layout rows of Qg through a bounds-checked buffer: rows past
       // the chunk's end are dropped by the range check
       const uint32_t natb = tile_bytes<T>(n, gsK, K);
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
       }
       // G2 token-contiguous (rows past the end hold G2 of the last row)
       if constexpr (MODE & PREP_BWD_CHUNK) {
-        float* G2d = a.gate == 2 ? a.G2t + (cb * K + col) * CH + r0
+        float* G2d = a.gate == 2 ? a.G2t + cb * K * CH + ((int64_t)g.seg * K + col) * SUB
                                  : (a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr);
         if (G2d)
 #pragma unroll
@@ -312,6 +314,14 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
     // ---- S3: score tiles L (strict, fp32 in LDS) and Cq (inclusive, global) --
     {
       T* Cqo = reinterpret_cast<T*>(a.Cq) + cb * CH * CH;
+      using FR = typename Frag4<T>::type;
+      // identity as the B operand of a 16-long product: C = X^T I turns a C
+      // tile (rows 4 (l >> 4) + e, column l & 15) into row l & 15, columns
+      // 4 (l >> 4) .. + 3, exactly
+      f32x4 idf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) idf[e] = (crow(e) == ccol()) ? 1.f : 0.f;
+      const FR idt = to_frag<T>(idf);
       T* Cqto = reinterpret_cast<T*>(a.Cqt) + cb * CH * CH;
       auto store = [&](int I, int J, const f32x4& accL, const f32x4& accC) {
         f32x4 cq;
@@ -321,7 +331,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
           if (row > col) sL[row * PL + col] = accL[i];
           cq[i] = row >= col ? accC[i] : 0.f;
         }
-        if constexpr (MODE & PREP_FWD_OUT) st_tile<T>(cq, Cqo + (I * SUB) * CH + J * SUB, CH, 1);
+        if constexpr (MODE & PREP_FWD_OUT) {  // column-blocked [J][64][16], rows via an exact transpose
+          f32x4 tr = zero4();
+          mm16(tr, to_frag<T>(cq), idt);
+          *reinterpret_cast<FR*>(Cqo + ((J * CH + I * SUB + ccol()) * SUB + crow(0))) = to_frag<T>(tr);
+        }
         if constexpr (MODE & PREP_BWD_SCAN) st_frag_T<T>(cq, Cqto, I, J);
       };
       score_tiles_pre<T, K, true, NW>(sKa, sQ, sK, PK, sFac, sFlag, n, store);
@@ -336,7 +350,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
       for (int t = w; t < NSUB * NSUB; t += NW) {
         const int I = t / NSUB, J = t - I * NSUB;
         if (J <= I && I * SUB < n) continue;
-        if constexpr (MODE & PREP_FWD_OUT) st_tile<T>(zero4(), Cqo + (I * SUB) * CH + J * SUB, CH, 1);
+        if constexpr (MODE & PREP_FWD_OUT)
+          *reinterpret_cast<FR*>(Cqo + ((J * CH + I * SUB + ccol()) * SUB + crow(0))) = to_frag<T>(zero4());
         if constexpr (MODE & PREP_BWD_SCAN) st_frag_T<T>(zero4(), Cqto, I, J);
       }
     }
@@ -449,20 +464,26 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
     const T* Aop = BF ? (const T*)sAb : (const T*)sA;
     constexpr int PAo = BF ? PA : PL;
     constexpr int NKB = K / SUB, GPP = 16 / (4 * (int)sizeof(T));  // 16-long groups per piece
-    constexpr int NJ0 = wantW ? NKB : 0, NJ1 = wantWt ? NKB : 0, NJ2 = wantU ? V / SUB : 0;
+    constexpr int NJ0 = wantW ? NKB / GPP : 0, NJ1 = wantWt ? NKB : 0, NJ2 = wantU ? V / SUB : 0;
     using FR = typename Frag4<T>::type;
     for (int job = w; job < NJ0 + NJ1 + NJ2; job += NW) {
-      if (job < NJ0) {  // W^T, key block kb: C tile rows 16 kb + 4 (l >> 4) + i, token 16 I + (l & 15)
-        const int kb = job;
-        const T* Ea = sEt + (kb * SUB) * PA;
+      if (job < NJ0) {  // W^T, key blocks GPP job .. + GPP - 1: C tile rows 16 kb + 4 (l >> 4) + i,
+                        // token 16 I + (l & 15); one job fills whole W pieces
         static_for<0, NSUB>([&](auto II) {
           constexpr int I = decltype(II)::value;
-          f32x4 acc = zero4();
           // A is lower triangular: token block I needs tokens < 16 (I + 1) only
           constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
-          mma_tile<T, true, true>(acc, Ea, PA, 1, Aop + (I * SUB) * PAo, PAo, 1, kd);
-          *reinterpret_cast<FR*>(Wfo + (((I * (NKB / GPP) + kb / GPP) * 64 + lane_id()) * GPP + kb % GPP) * 4) =
-              to_frag<T>(acc);
+          union {
+            uint4 u;
+            FR f[GPP];
+          } piece;
+          static_for<0, GPP>([&](auto hh) {
+            const int kb = job * GPP + hh;
+            f32x4 acc = zero4();
+            mma_tile<T, true, true>(acc, sEt + (kb * SUB) * PA, PA, 1, Aop + (I * SUB) * PAo, PAo, 1, kd);
+            piece.f[hh] = to_frag<T>(acc);
+          });
+          *reinterpret_cast<uint4*>(Wfo + ((I * (NKB / GPP) + job) * 64 + lane_id()) * GPP * 4) = piece.u;
         });
       } else if (job < NJ0 + NJ1) {  // W, key block kb, for W^T in fragment order
         const int col = (job - NJ0) * SUB;

@@ -63,7 +63,7 @@ struct Args {
   void* U;       // A Z                 [nc,H,64,V] fragment order   forward scan
   float* glast;  // G2 at the last row  [nc,H,K]     both scans
   void* Qg;      // s Q exp2(G)         [BT,H,K]     output
-  void* Cq;      // tril_incl(Qg Y^T)   [nc,H,64,64] output
+  void* Cq;      // tril_incl(Qg Y^T)   [nc,H,64/16,64,16] column-blocked  output
   void* F;       // F                   [nc,H,64,K] fragment order   reverse scan (Rbar = F dS+)
   void* Wt;      // W^T                 [nc,H,K,64] fragment order   reverse scan (dS -= W^T Rbar)
   void* Qgt;     // Qg^T                [nc,H,K,64] fragment order   reverse scan (dS += Qg^T dO)
@@ -74,9 +74,9 @@ struct Args {
   void* RT;      // R^T tiles [nc,H,V,64], fragment order (output kernel)
   int scan_out;  // SCAN_* bits: which of hbuf/R and hbufT/RT the forward scan writes
   void* At;      // A^T                 [nc,H,64,64] chunk backward (P = A^T Rbar)
-  void* Kt;      // K^T                 [nc,H,K,64]  chunk backward
-  void* Qt;      // Q^T                 [nc,H,K,64]  chunk backward
-  float* G2t;    // G2^T  [nc,H,K,64] (vector gate) or [nc,H,64] (scalar gate)
+  void* Kt;      // K^T                 [nc,H,64/16,K,16] column-blocked  chunk backward
+  void* Qt;      // Q^T                 [nc,H,64/16,K,16] column-blocked  chunk backward
+  float* G2t;    // G2^T  [nc,H,64/16,K,16] column-blocked (vector gate) or [nc,H,64] (scalar gate)
   float* Gst;    // sub-chunk gate statistics [nc,H,4,K] of float4 {G2 at the first row,
                  // G2 at the last valid row, midpoint (max+min)/2, range max-min}
   // backward intermediates
