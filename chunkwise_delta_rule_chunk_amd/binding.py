@@ -18,7 +18,8 @@ REWY_BF16, REWY_F32 = 0, 1
 REWY_RECOMPUTE, REWY_SAVE = 0, 1
 
 EXPORTS = ("rewy_workspace_bytes", "rewy_saved_bytes", "rewy_fwd", "rewy_bwd",
-           "rewy_trace_begin", "rewy_trace_end", "rewy_status_string", "rewy_last_error")
+           "rewy_trace_begin", "rewy_trace_end", "rewy_trace_select", "rewy_status_string",
+           "rewy_last_error")
 
 
 class RewyDesc(ctypes.Structure):
@@ -69,6 +70,8 @@ def load():
         lib.rewy_trace_begin.restype = ctypes.c_int
         lib.rewy_trace_end.argtypes = [ctypes.POINTER(RewyTraceEntry), ctypes.c_int]
         lib.rewy_trace_end.restype = ctypes.c_int
+        lib.rewy_trace_select.argtypes = [ctypes.c_char_p]
+        lib.rewy_trace_select.restype = ctypes.c_int
         lib.rewy_status_string.argtypes = [ctypes.c_int]
         lib.rewy_status_string.restype = ctypes.c_char_p
         lib.rewy_last_error.argtypes = []
@@ -98,6 +101,14 @@ def rewy_bwd(desc, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, 
 
 def rewy_trace_begin() -> int:
     return load().rewy_trace_begin()
+
+
+def rewy_trace_select(stage=None) -> int:
+    """Trace only the launches of kernel `stage` (e.g. "k_fwd_prep"); None: all."""
+    rc = load().rewy_trace_select(None if stage is None else stage.encode())
+    if rc < 0:
+        raise RewyError(rc, "rewy_trace_select")
+    return rc
 
 
 def rewy_trace_end(cap: int = 32):

@@ -218,6 +218,7 @@ struct TraceRec {
 };
 struct Tracer {
   bool on = false;
+  char only[64] = {0};  // empty: every launch
   std::vector<TraceRec> recs;
   std::vector<hipEvent_t> pool;
   size_t used = 0;
@@ -234,7 +235,7 @@ thread_local Tracer g_tr;
 
 template <typename F>
 hipError_t traced(const char* stage, int variant, hipStream_t s, F&& launch) {
-  if (!g_tr.on) return launch();
+  if (!g_tr.on || (g_tr.only[0] && strcmp(g_tr.only, stage) != 0)) return launch();
   TraceRec r{stage, variant, g_tr.ev(), g_tr.ev()};
   if (r.e0) hipEventRecord(r.e0, s);
   const hipError_t e = launch();
@@ -379,6 +380,12 @@ REWY_API int rewy_trace_begin(void) {
   g_tr.recs.clear();
   g_tr.used = 0;
   g_tr.on = true;
+  return REWY_OK;
+}
+
+REWY_API int rewy_trace_select(const char* stage) {
+  if (stage && strlen(stage) >= sizeof(g_tr.only)) return fail(REWY_EINVAL, "trace stage name too long");
+  snprintf(g_tr.only, sizeof(g_tr.only), "%s", stage ? stage : "");
   return REWY_OK;
 }
 

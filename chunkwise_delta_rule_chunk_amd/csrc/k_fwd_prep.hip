@@ -122,18 +122,18 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
   uint4 pv2[2 * VPT];
   uint4 etr[NSL][RS / VE];  // E^T of this thread's rows, from the elementwise phase to S5
   uint32_t pbeta = 0u;      // raw bits of the next item's beta for row tid
-  auto fetch_kq = [&](int item, int tid) {
-    const int c = item / H, h = item - c * H;
-    const ChunkInfo ci = load_chunk(a.chunks, c);
+  // the fetches take the item's chunk record, read one item ahead (its
+  // scalar load completes during the previous item instead of stalling here)
+  auto fetch_kq = [&](int item, const ChunkInfo& ci, int tid) {
+    const int h = item % H;
     if (ci.len == 0) return;
     const int64_t t0 = ci.bos;
     pk.load(gbuf(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
     pq.load(gbuf(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
     pbeta = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, ci.len - 1)) * H + h);
   };
-  auto fetch_v = [&](int item, int tid) {
-    const int c = item / H, h = item - c * H;
-    const ChunkInfo ci = load_chunk(a.chunks, c);
+  auto fetch_v = [&](int item, const ChunkInfo& ci, int tid) {
+    const int h = item % H;
     if (ci.len == 0) return;
     const int64_t t0 = ci.bos;
     if constexpr (BF) {
@@ -149,17 +149,17 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
       pv.load(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, gsV, ci.len, tid);
     }
   };
-  auto fetch_g = [&](int item) {
-    const int c = item / H, h = item - c * H;
-    const ChunkInfo ci = load_chunk(a.chunks, c);
+  auto fetch_g = [&](int item, const ChunkInfo& ci) {
+    const int h = item % H;
     if (ci.len == 0) return;
 #pragma unroll
     for (int s = 0; s < NSL; ++s) gc[s].load(a, (int64_t)ci.bos, h, ci.len, K, 0);
   };
 
+  ChunkInfo cnext = load_chunk(a.chunks, min((int)blockIdx.x, total - 1) / H);
   if (blockIdx.x < total) {
-    fetch_kq(blockIdx.x, threadIdx.x);
-    fetch_g(blockIdx.x);
+    fetch_kq(blockIdx.x, cnext, threadIdx.x);
+    fetch_g(blockIdx.x, cnext);
   }
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int tid = opaque_tid(), w = wave_id();
@@ -169,13 +169,15 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
 #pragma unroll
     for (int s = 0; s < NSL; ++s) asm volatile("" : "+v"(gc[s].c), "+v"(gc[s].seg));
     const int c = item / H, h = item - c * H;
-    const ChunkInfo ci = load_chunk(a.chunks, c);
+    const ChunkInfo ci = cnext;
     const int n = ci.len;
     const bool more = item + (int)gridDim.x < total;
+    // the next item's record (the last one again past the end: never used)
+    cnext = load_chunk(a.chunks, min(item + (int)gridDim.x, total - 1) / H);
     if (n == 0) {  // uniform: nothing was fetched for this slot
       if (more) {
-        fetch_kq(item + gridDim.x, tid);
-        fetch_g(item + gridDim.x);
+        fetch_kq(item + gridDim.x, cnext, tid);
+        fetch_g(item + gridDim.x, cnext);
       }
       continue;
     }
@@ -369,10 +371,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
     solve_unit_lower(sL, sA, PL, n);
     // this item's v; the next item's k, q, beta and gates (the gate registers
     // are free since the elementwise phase), covered by S5
-    fetch_v(item, tid);
+    fetch_v(item, ci, tid);
     if (more) {
-      fetch_kq(item + gridDim.x, tid);
-      fetch_g(item + gridDim.x);
+      fetch_kq(item + gridDim.x, cnext, tid);
+      fetch_g(item + gridDim.x, cnext);
     }
     if constexpr (MODE & PREP_BWD_CHUNK) {  // A^T for the chunk backward, 16-byte rows
       constexpr int VA = 16 / (int)sizeof(T), PER = CH / VA;

@@ -126,6 +126,13 @@ typedef struct {
 int rewy_trace_begin(void);
 int rewy_trace_end(rewy_trace_entry *out, int cap);
 
+/* Restricts this thread's trace to the launches of one kernel, named by its
+ * template name ("k_fwd_prep", "k_scans", ...), so that a timed run pays for
+ * one event pair per launch of that kernel only.  NULL (the default) traces
+ * every launch.  Applies from the next call; the name is copied.  Returns
+ * REWY_OK, or REWY_EINVAL for a name longer than 63 characters. */
+int rewy_trace_select(const char *stage);
+
 /* Name of a rewy_status value. */
 const char *rewy_status_string(int status);
 
