@@ -43,7 +43,7 @@ def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy
     gst = nc * 4 * K * 16               # sub-chunk gate statistics, float4 per (block, feature)
     prep_in = n * (2 * tk + tv + gb + besz)
     w_fscan = n * (tk + tv) + tileK + glast              # W, U, Ft, glast
-    w_fout = n * tk + tile64                              # Qg, Cq
+    w_fout = tileK + tile64                               # Qg, Cq
     w_bscan = n * tk + 2 * tileK + tile64                 # F, Wt, Qgt, Cqt
     w_bchunk = tile64 + 2 * tileK + g2t + gst             # At, Kt, Qt, G2t, Gst
     if policy == "save":
@@ -52,14 +52,16 @@ def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy
         prep = prep_in + (w_fscan + w_fout + (w_fscan + w_bscan + w_bchunk)) / 2
     per_head = {
         "k_fwd_prep": prep,
-        "k_fwd_scan": n * (tk + tv) + tileK + glast + st + n * tv,
-        "k_fwd_out": n * (tk + tv) + st + tile64 + n * tv,
+        # forward pass: reads W, U, Ft, glast, Qg, Cq; writes o (and, saving,
+        # the states and R for the backward)
+        "k_fwd_scan": n * (tk + tv) + tileK + glast + tileK + tile64 + n * tv
+                      + (st + tileV if policy == "save" else 0),
         "k_bwd_scan": n * (tk + tv) + 2 * tileK + tile64 + glast + st + tileV,
         "k_bwd_chunk": n * 3 * tv + tile64 + tileV + 2 * st + 2 * tileK + g2t + gst + n * besz
                        + n * (2 * tk + tv + gb + besz),
     }
     # the backward's forward scan and reverse scan in one launch
-    per_head["k_scans"] = per_head["k_fwd_scan"] + per_head["k_bwd_scan"]
+    per_head["k_scans"] = n * (tk + tv) + tileK + glast + st + tileV + per_head["k_bwd_scan"]
     for name, b in per_head.items():
         if f"{len(name)}{name}I" in kernel:
             extra = 0
@@ -230,7 +232,7 @@ def main():
     gate = {"none": 0, "scalar": 1, "vector": 2}[inp.gate]
     dbytes = kernel_bytes(dom, chunk_lens, H, K, V, esz, besz, gate, len(seq_lens), args.policy)
     achieved = dbytes / (dom_avg * 1e-3) / 1e9 if dbytes else None
-    short = next((k for k in ("k_fwd_prep", "k_fwd_scan", "k_fwd_out", "k_bwd_scan", "k_bwd_chunk", "k_scans")
+    short = next((k for k in ("k_fwd_prep", "k_fwd_scan", "k_bwd_scan", "k_bwd_chunk", "k_scans")
                   if f"{len(k)}{k}I" in dom), dom)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": None if achieved is None else achieved / PEAK_HBM_GBS,

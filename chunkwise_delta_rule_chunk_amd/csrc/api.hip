@@ -92,14 +92,14 @@ int make_plan(const rewy_desc* d, Plan& p) {
 // the save-all policy; everything else is scratch in the workspace.  The
 // reverse set is what the reverse scan and the chunk backward read:
 // F Wt Qgt Cqt (reverse scan) and At Kt Qt G2t Gst (chunk backward).
-//   recompute: ws = [index | glast hbuf R | W Ft U | (fwd) Qg Cq hbufT RT / (bwd) reverse set | Rbt dhbuf]
+//   recompute: ws = [index | glast hbuf R | W Ft U | (fwd) Qg Cq / (bwd) reverse set | Rbt dhbuf]
 //   save-all:  saved = [glast hbuf R | reverse set]
-//              ws (fwd) = [index | W Ft U Qg Cq hbufT RT],  ws (bwd) = [index | Rbt dhbuf]
+//              ws (fwd) = [index | W Ft U Qg Cq],  ws (bwd) = [index | Rbt dhbuf]
 struct Layout {
   size_t chunks, seqoff;
   size_t glast, hbuf, R;             // read by output and backward
   size_t W, Ft, U;                   // forward scan operands
-  size_t Qg, Cq, hbufT, RT;          // output operands
+  size_t Qg, Cq;                     // output-product operands
   size_t F, Wt, Qgt, Cqt;            // reverse scan operands
   size_t At, Kt, Qt, G2t, Gst;       // chunk backward operands
   size_t Rbt, dhbuf;                 // written by the reverse scan
@@ -109,7 +109,6 @@ struct Layout {
 Layout layout(const Plan& p) {
   Layout L{};
   const size_t nc = p.nc_max, H = p.H, K = p.K, V = p.V, BT = p.BT, e = p.esz;
-  const size_t tokK = BT * H * K * e;
   const size_t tileK = nc * H * K * CH * e, tileV = nc * H * V * CH * e;
   const size_t tile64 = nc * H * CH * CH * e;
   const size_t g2 = p.gate == REWY_GATE_VECTOR ? nc * H * K * CH * 4
@@ -146,10 +145,8 @@ Layout layout(const Plan& p) {
   L.Ft = take(off, tileK);
   L.U = take(off, tileV);
   const size_t after_scan = off;
-  L.Qg = take(off, tokK);
+  L.Qg = take(off, tileK);
   L.Cq = take(off, tile64);
-  L.hbufT = take(off, nc * H * K * V * e);
-  L.RT = take(off, tileV);
   L.ws_fwd = off;
   if (save) {
     off = head;
@@ -195,7 +192,6 @@ void fill_common(Args& a, const Plan& p, const rewy_desc* d, char* ws, char* sv,
   a.hbuf = fs + L.hbuf; a.R = fs + L.R;
   a.F = fs + L.F; a.Wt = fs + L.Wt; a.Qgt = fs + L.Qgt; a.Cqt = fs + L.Cqt;
   a.W = ws + L.W; a.Ft = ws + L.Ft; a.U = ws + L.U; a.Qg = ws + L.Qg; a.Cq = ws + L.Cq;
-  a.hbufT = ws + L.hbufT; a.RT = ws + L.RT;
   a.At = fs + L.At; a.Kt = fs + L.Kt; a.Qt = fs + L.Qt;
   a.G2t = reinterpret_cast<float*>(fs + L.G2t);
   a.Gst = reinterpret_cast<float*>(fs + L.Gst);
@@ -247,7 +243,7 @@ hipError_t traced(const char* stage, int variant, hipStream_t s, F&& launch) {
 int variant_of(const Args& a, bool f32) { return (f32 ? 1000000 : 0) + a.K * 1000 + a.V; }
 
 // Forward chunk stages shared by rewy_fwd and the recompute in rewy_bwd.
-int run_forward_stages(const Args& a, bool f32, bool with_scan, bool with_output, hipStream_t s) {
+int run_forward_stages(const Args& a, bool f32, bool with_scan, hipStream_t s) {
   int rc;
   const int vr = variant_of(a, f32);
   if ((rc = hip_check(traced("k_chunk_table", -1, s, [&] { return launch_chunk_table(a, s); }),
@@ -259,10 +255,6 @@ int run_forward_stages(const Args& a, bool f32, bool with_scan, bool with_output
   if (with_scan &&
       (rc = hip_check(traced("k_fwd_scan", vr, s, [&] { return launch_fwd_scan(a, f32, s); }),
                       "forward scan")))
-    return rc;
-  if (with_output &&
-      (rc = hip_check(traced("k_fwd_out", vr, s, [&] { return launch_fwd_out(a, f32, s); }),
-                      "forward output")))
     return rc;
   return REWY_OK;
 }
@@ -314,8 +306,8 @@ REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const vo
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
   a.prep_mode = PREP_FWD_SCAN | PREP_FWD_OUT |
                 (p.policy == REWY_SAVE ? PREP_BWD_SCAN | PREP_BWD_CHUNK : 0);
-  a.scan_out = SCAN_TRANSPOSED | (p.policy == REWY_SAVE ? SCAN_NATURAL : 0);
-  return run_forward_stages(a, p.f32, true, true, s);
+  a.scan_out = SCAN_OUTPUT | (p.policy == REWY_SAVE ? SCAN_NATURAL : 0);
+  return run_forward_stages(a, p.f32, true, s);
 }
 
 REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const void* v,
@@ -358,7 +350,7 @@ REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const vo
   const int vr = variant_of(a, f32);
   if (p.policy == REWY_RECOMPUTE) {
     // prep again, then the forward scan and the reverse scan side by side
-    if ((rc = run_forward_stages(a, f32, false, false, s))) return rc;
+    if ((rc = run_forward_stages(a, f32, false, s))) return rc;
     if ((rc = hip_check(traced("k_scans", vr, s, [&] { return launch_scans(a, f32, s); }),
                         "forward and reverse scans")))
       return rc;

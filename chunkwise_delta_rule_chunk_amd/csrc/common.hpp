@@ -354,28 +354,35 @@ __device__ __forceinline__ void mma16B(f32x4& acc, uint4 a, uint4 b) {
   }
 }
 
-// Copy a [ROWS x COLS] LDS tile (pitch lp; ROWS a multiple of 16, rows are
-// operand rows, columns the contraction) to global memory in operand-fragment
-// order (see st_frag_T), every thread storing the same number of equal
-// pieces (16 or 8 bytes; an 8-byte piece is half a fragment piece).
-template <typename T, int ROWS, int COLS, int NTH>
-__device__ __forceinline__ void frag_out(T* g, const T* s, int lp, int tid) {
-  constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE, NG = COLS / KG;
-  constexpr int BYTES = ROWS * COLS * (int)sizeof(T);
-  constexpr int PB = BYTES / NTH >= 16 ? 16 : BYTES / NTH;
-  static_assert(PB == 16 || PB == 8, "piece size");
-  static_assert(ROWS % SUB == 0 && COLS % KG == 0 && BYTES % (PB * NTH) == 0, "tile split");
-  constexpr int HE = PB / (int)sizeof(T), NP = BYTES / (PB * NTH);
-#pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    const int idx = tid + j * NTH;                  // piece (16-byte) or half piece (8-byte)
-    const int pc = PB == 16 ? idx : idx >> 1, hf = PB == 16 ? 0 : idx & 1;
-    const int ln = pc % 64, blk = pc / 64, rb = blk / NG, q = blk - rb * NG;
-    const T* src = s + (SUB * rb + (ln & 15)) * lp + KG * q + VE * (ln >> 4) + hf * HE;
-    if constexpr (PB == 16)
-      *reinterpret_cast<uint4*>(g + idx * HE) = *reinterpret_cast<const uint4*>(src);
-    else
-      *reinterpret_cast<uint2*>(g + idx * HE) = *reinterpret_cast<const uint2*>(src);
+// C-fragment order: a matrix stored as the C fragments of its 16 x 16 blocks,
+// block (rb, cb) at piece (rb * ncb + cb) * 64 + l, four elements per lane,
+// M[16 rb + 4 (l >> 4) + i][16 cb + (l & 15)] for i < 4.  That piece is the
+// 16-long B fragment of M (and A fragment of M^T) for a contraction over M's
+// row index.  cfrag_op() reads the operand of one lane group of a contraction
+// over rows 32 q .. 32 q + 31 (bf16, blocks 2 q and 2 q + 1 joined: slot
+// 8 (l >> 4) + e is row 32 q + 4 (l >> 4) + e, slot 8 (l >> 4) + 4 + e is row
+// 32 q + 16 + 4 (l >> 4) + e) or 16 q .. 16 q + 15 (fp32, block q);
+// perm_row() reads the other operand's row with the same slot assignment.
+// p points at the lane's piece of block cb = 0 (base + l * 4 elements).
+template <typename T>
+__device__ __forceinline__ uint4 cfrag_op(const T* p, int q) {
+  if constexpr (std::is_same_v<T, bf16>) {
+    const uint2 x0 = *reinterpret_cast<const uint2*>(p + (2 * q) * 256);
+    const uint2 x1 = *reinterpret_cast<const uint2*>(p + (2 * q + 1) * 256);
+    return uint4{x0.x, x0.y, x1.x, x1.y};
+  } else {
+    return *reinterpret_cast<const uint4*>(p + q * 256);
+  }
+}
+// row points at element 4 (l >> 4) of the row (LDS)
+template <typename T>
+__device__ __forceinline__ uint4 perm_row(const T* row, int q) {
+  if constexpr (std::is_same_v<T, bf16>) {
+    const uint2 x0 = *reinterpret_cast<const uint2*>(row + 32 * q);
+    const uint2 x1 = *reinterpret_cast<const uint2*>(row + 32 * q + 16);
+    return uint4{x0.x, x0.y, x1.x, x1.y};
+  } else {
+    return *reinterpret_cast<const uint4*>(row + 16 * q);
   }
 }
 

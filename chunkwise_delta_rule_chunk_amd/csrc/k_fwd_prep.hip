@@ -245,16 +245,19 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
       // one block row, and a wave's consecutive columns are contiguous
       T* Ktd = reinterpret_cast<T*>(a.Kt) + cb * K * CH + ((int64_t)g.seg * K + col) * SUB;
       T* Qtd = reinterpret_cast<T*>(a.Qt) + cb * K * CH + ((int64_t)g.seg * K + col) * SUB;
-      // natural-layout rows of Qg through a bounds-checked buffer: rows past
-      // the chunk's end are dropped by the range check
-      const uint32_t natb = tile_bytes<T>(n, gsK, K);
-      const GBuf bQg = gbuf(reinterpret_cast<T*>(a.Qg) + (t0 * H + h) * K, (MODE & PREP_FWD_OUT) ? natb : 0u);
-      // F in operand-fragment order (row block seg, key group col / KGF): this
-      // thread's 16 rows are elements VE apart in one column of pieces
+      // F and Qg in operand-fragment order (row block seg, key group
+      // col / KGF): this thread's 16 rows are elements VE apart in one column
+      // of pieces (rows past the chunk's end are zeros)
       constexpr int NGKF = K / KGF;
       T* Fd = reinterpret_cast<T*>(a.F) + cb * CH * K +
               ((g.seg * NGKF + col / KGF) * 64 + ((col % KGF) / VE) * 16) * VE + col % VE;
-      const uint32_t rowb = (uint32_t)(gsK * (int64_t)sizeof(T)), colb = col * (int)sizeof(T);
+      // Qg in the order of W (pieces of GPQ 16-key groups, kernels.hpp), so the
+      // forward scan contracts it with the same S operand as W: this thread's
+      // 16 rows are 4 GPQ elements apart
+      constexpr int NKBQ = K / SUB, GPQ = 16 / (4 * (int)sizeof(T));
+      T* Qgd = reinterpret_cast<T*>(a.Qg) + cb * CH * K +
+               ((((int64_t)g.seg * (NKBQ / GPQ) + (col / SUB) / GPQ) * 64 + 16 * ((col % SUB) / 4)) * GPQ +
+                (col / SUB) % GPQ) * 4 + col % 4;
 #pragma unroll
       for (int r8 = 0; r8 < RS; r8 += VE) {
         union {
@@ -272,11 +275,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
           const float ea = fexp2(G - rA), eb = fexp2(rB - G);
           const float vKa = sBeta[row] * kr * ea, vQa = bs * qr * ea, vKc = kr * eb;
           const float vE = vKa * cA, vQg = vQa * cA, vF = vKc * cB;
-          const uint32_t off = colb + (uint32_t)row * rowb;
-          if constexpr (MODE & PREP_FWD_OUT) {
-            if constexpr (sizeof(T) == 2) gst2(bQg, off, __builtin_bit_cast(uint16_t, fromf<T>(vQg)));
-            else gst4(bQg, off, __float_as_uint(vQg));
-          }
+          if constexpr (MODE & PREP_FWD_OUT) Qgd[r * GPQ * 4] = fromf<T>(vQg);
           if constexpr (MODE & PREP_BWD_SCAN) Fd[r * VE] = fromf<T>(vF);
           sKa[row * PK + col] = fromf<T>(vKa);
           sQ[row * PK + col] = fromf<T>(vQa);
@@ -333,10 +332,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
           if (row > col) sL[row * PL + col] = accL[i];
           cq[i] = row >= col ? accC[i] : 0.f;
         }
-        if constexpr (MODE & PREP_FWD_OUT) {  // column-blocked [J][64][16], rows via an exact transpose
+        if constexpr (MODE & PREP_FWD_OUT) {  // C fragments of the transposed blocks (exact transpose)
           f32x4 tr = zero4();
           mm16(tr, to_frag<T>(cq), idt);
-          *reinterpret_cast<FR*>(Cqo + ((J * CH + I * SUB + ccol()) * SUB + crow(0))) = to_frag<T>(tr);
+          *reinterpret_cast<FR*>(Cqo + ((I * NSUB + J) * 64 + lane_id()) * 4) = to_frag<T>(tr);
         }
         if constexpr (MODE & PREP_BWD_SCAN) st_frag_T<T>(cq, Cqto, I, J);
       };
@@ -353,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
         const int I = t / NSUB, J = t - I * NSUB;
         if (J <= I && I * SUB < n) continue;
         if constexpr (MODE & PREP_FWD_OUT)
-          *reinterpret_cast<FR*>(Cqo + ((J * CH + I * SUB + ccol()) * SUB + crow(0))) = to_frag<T>(zero4());
+          *reinterpret_cast<FR*>(Cqo + ((I * NSUB + J) * 64 + lane_id()) * 4) = to_frag<T>(zero4());
         if constexpr (MODE & PREP_BWD_SCAN) st_frag_T<T>(zero4(), Cqto, I, J);
       }
     }

@@ -15,9 +15,12 @@
 // compiler's memory counters let each use wait for exactly its own load and
 // the prefetches stay in flight across steps.
 //
-// Forward (ReWY paper, "The chunk system": R = U - W S, S' = Lambda S + F^T R;
-// KDA blog section 6.4 state fast-forward):
-//   for each chunk c:  write S_c;  R_c = U_c - W_c S_c;  S_{c+1} = diag(exp2 G2_last) S_c + F_c^T R_c
+// Forward (ReWY paper, "The chunk system": R = U - W S, S' = Lambda S + F^T R,
+// O = Qg S + Cq R; KDA blog sections 6.4-6.5, state fast-forward and output):
+//   for each chunk c:  [write S_c];  R_c = U_c - W_c S_c;  [write R_c];
+//                      S_{c+1} = diag(exp2 G2_last) S_c + F_c^T R_c;
+//                      o_c = Qg_c S_c + Cq_c R_c   (the forward pass; the
+//                      recompute in the backward writes S_c and R_c instead)
 // Reverse (ReWY paper Appendix 7.2 / Algorithm 1; the scan supplies the
 // incoming-state term -E^T P = -W^T Rbar once):
 //   for each chunk c from the last:  write dS_{c+1};
@@ -40,7 +43,7 @@ using ic = std::integral_constant<int, V>;
 template <typename T, int K, int V, int BV, int OUT>
 __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const int vt) {
   constexpr int NTH = 256, DEPTH = 2;
-  constexpr bool NAT = OUT & SCAN_NATURAL, TRN = OUT & SCAN_TRANSPOSED;
+  constexpr bool NAT = OUT & SCAN_NATURAL, OUTP = OUT & SCAN_OUTPUT;
   constexpr int VE = 16 / (int)sizeof(T), KG = 4 * VE;  // elements per lane piece, per group
   constexpr int CT = BV / SUB, NKT = K / SUB;
   constexpr int NGK = K / KG, NGT = CH / KG;
@@ -58,6 +61,8 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
   const int w = wave_id(), tid = threadIdx.x, l = lane_id();
   const int r16 = l & 15, g = l >> 4;
   const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
+  const int seq_bos = a.cu ? a.cu[n] : n * a.T, seq_eos = a.cu ? a.cu[n + 1] : (n + 1) * a.T;
+  const int64_t gsV = (int64_t)H * V;
   const T* Wg = reinterpret_cast<const T*>(a.W);
   const T* Ftg = reinterpret_cast<const T*>(a.Ft);
   const T* Ug = reinterpret_cast<const T*>(a.U);
@@ -80,6 +85,10 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
   static_assert(NGK * GPP == K / SUB, "W pieces");
   uint4 wf[DEPTH][NGK];      // W rows 16 w + r16, GPP 16-long key groups per piece
   FR uf[DEPTH][CT];          // U in the C layout of R's tiles
+  // output product O = Qg S + Cq R for token tile w: Qg rows in the order of
+  // W (contracted with the same S operand), Cq row block w in C-fragment
+  // order (two 16-token blocks joined per lane group, R read to match)
+  uint4 qf[DEPTH][OUTP ? NGK : 1], cqf[DEPTH][OUTP ? NGT : 1];
   uint4 ff[DEPTH][KW][NGT];  // F^T rows 16 ktile + r16, lane piece of every token group
   f32x4 lam[DEPTH][KW];      // G2_last of the state rows this lane holds
   // past the last chunk the last one is read again (valid memory, never used)
@@ -92,6 +101,11 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
     const T* up = Ug + cb * CH * V + (int64_t)((vt * CT * NSUB + w) * 64 + l) * 4;
 #pragma unroll
     for (int m = 0; m < CT; ++m) uf[B][m] = *reinterpret_cast<const FR*>(up + m * NSUB * 64 * 4);
+    if constexpr (OUTP) {  // used with W, before this set is refilled
+      const T* qp = reinterpret_cast<const T*>(a.Qg) + cb * CH * K + (int64_t)(w * NGK * 64 + l) * VE;
+#pragma unroll
+      for (int q = 0; q < NGK; ++q) qf[B][q] = *reinterpret_cast<const uint4*>(qp + q * 64 * VE);
+    }
   };
   auto fetch_fl = [&](auto set, int c) {
     constexpr int B = decltype(set)::value;
@@ -103,6 +117,11 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
 #pragma unroll
       for (int q = 0; q < NGT; ++q) ff[B][j][q] = *reinterpret_cast<const uint4*>(fp + q * 64 * VE);
       lam[B][j] = *reinterpret_cast<const f32x4*>(a.glast + cb * K + kr + 4 * g);
+    }
+    if constexpr (OUTP) {  // used after the state update, with F^T's set
+      const T* cp = reinterpret_cast<const T*>(a.Cq) + cb * CH * CH + (int64_t)(w * NSUB * 64 + l) * 4;
+#pragma unroll
+      for (int q = 0; q < NGT; ++q) cqf[B][q] = cfrag_op<T>(cp, q);
     }
   };
 
@@ -137,6 +156,7 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
   auto step = [&](auto buf, int c) {
     constexpr int B = decltype(buf)::value;
     const int64_t cb = (int64_t)c * H + h;
+    const int bos = seq_bos + (c - c0) * CH, len = min(CH, seq_eos - bos);
     // S_c: operand [v][k] in LDS and, for global memory, natural [k][v]
 #pragma unroll
     for (int j = 0; j < KW; ++j)
@@ -155,17 +175,19 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
         }
       }
     lds_barrier();
-    if constexpr (TRN)
-      frag_out<T, BV, K, NTH>(reinterpret_cast<T*>(a.hbufT) + (cb * V + vt * BV) * K, sHt, PK, tid);
     // R = U - W S for token tile w (rows past the chunk's end are zero: W and
     // U are zero there).  A W piece holds, for lane l (row l & 15), the keys
     // 16 kb + 4 (l >> 4) + e of GPP consecutive 16-key groups kb.  bf16 takes
     // both groups as one 32-slot fragment (slot 8 (l >> 4) + 4 hh + e is key
     // 32 q + 16 hh + 4 (l >> 4) + e) and reads S^T with the same assignment;
     // fp32 runs each group as four 16x16x4 steps.
+    // (Qg S for the output goes with it, on the same S operand; its Cq R
+    // part follows the state update, when R_c is in LDS.)
+    f32x4 po[OUTP ? CT : 1];
 #pragma unroll
     for (int m = 0; m < CT; ++m) {
       f32x4 p = zero4();
+      if constexpr (OUTP) po[m] = zero4();
       const T* hb = sHt + (SUB * m + r16) * PK + 4 * g;
 #pragma unroll
       for (int q = 0; q < NGK; ++q) {
@@ -174,8 +196,12 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
           const bf16x4 s1 = *reinterpret_cast<const bf16x4*>(hb + 32 * q + SUB);
           const bf16x8 sb = __builtin_shufflevector(s0, s1, 0, 1, 2, 3, 4, 5, 6, 7);
           p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[B][q]), sb, p, 0, 0, 0);
+          if constexpr (OUTP)
+            po[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[B][q]), sb, po[m], 0, 0, 0);
         } else {
-          mm16(p, __builtin_bit_cast(f32x4, wf[B][q]), *reinterpret_cast<const f32x4*>(hb + SUB * q));
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(hb + SUB * q);
+          mm16(p, __builtin_bit_cast(f32x4, wf[B][q]), sv);
+          if constexpr (OUTP) mm16(po[m], __builtin_bit_cast(f32x4, qf[B][q]), sv);
         }
       }
       f32x4 rv;
@@ -191,8 +217,6 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
     }
     fetch_wu(ic<B>{}, c + DEPTH);
     lds_barrier();
-    if constexpr (TRN)
-      frag_out<T, BV, CH, NTH>(reinterpret_cast<T*>(a.RT) + (cb * V + vt * BV) * CH, sRt, PA, tid);
     // S = diag(exp2 G2_last) S + F^T R
 #pragma unroll
     for (int j = 0; j < KW; ++j) {
@@ -206,6 +230,23 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
         for (int i = 0; i < 4; ++i) st[j][m][i] *= d[i];
 #pragma unroll
         for (int q = 0; q < NGT; ++q) mma16B<T>(st[j][m], ff[B][j][q], *reinterpret_cast<const uint4*>(rb + KG * q));
+      }
+    }
+    // o rows of token tile w: O += Cq R, transposed by the identity product
+    // into 8-byte (16-byte fp32) row pieces; rows past the chunk's end fall
+    // outside the buffer and are dropped
+    if constexpr (OUTP) {
+      const GBuf bo = gbuf(reinterpret_cast<T*>(a.o) + ((int64_t)bos * H + h) * V, tile_bytes<T>(len, gsV, V));
+#pragma unroll
+      for (int m = 0; m < CT; ++m) {
+        const T* rb = sRt + (SUB * m + r16) * PA + 4 * g;
+#pragma unroll
+        for (int q = 0; q < NGT; ++q) mma16B<T>(po[m], cqf[B][q], perm_row<T>(rb, q));
+        f32x4 tr = zero4();
+        mm16(tr, to_frag<T>(po[m]), idt);
+        const uint32_t off = (uint32_t)(((int64_t)(SUB * w + r16) * gsV + vt * BV + SUB * m + 4 * g) * (int64_t)sizeof(T));
+        if constexpr (std::is_same_v<T, bf16>) gst8(bo, off, __builtin_bit_cast(uint2, to_frag<T>(tr)));
+        else gst16(bo, off, __builtin_bit_cast(uint4, tr));
       }
     }
     fetch_fl(ic<B>{}, c + DEPTH);
@@ -461,12 +502,12 @@ static hipError_t fwd_scan_bv(const Args& a, hipStream_t s) {
   case K_ * 1000 + V_:                                                          \
     if constexpr (kv_ok<T, K_, V_>() && V_ >= BV && K_ * BV >= 1024 && \
                   (sizeof(T) == 2 || K_ == 32 || BV == 16)) {                             \
-      if (a.scan_out == SCAN_NATURAL)                                           \
-        hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV, SCAN_NATURAL>), grid, block, 0, s, a); \
-      else if (a.scan_out == SCAN_TRANSPOSED)                                   \
-        hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV, SCAN_TRANSPOSED>), grid, block, 0, s, a); \
+      if (a.scan_out == SCAN_OUTPUT)                                            \
+        hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV, SCAN_OUTPUT>), grid, block, 0, s, a); \
+      else if (a.scan_out == (SCAN_NATURAL | SCAN_OUTPUT))                      \
+        hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV, SCAN_NATURAL | SCAN_OUTPUT>), grid, block, 0, s, a); \
       else                                                                      \
-        hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV, SCAN_NATURAL | SCAN_TRANSPOSED>), grid, block, 0, s, a); \
+        return hipErrorInvalidValue;                                            \
       return hipGetLastError();                                                 \
     } else {                                                                    \
       return hipErrorInvalidValue;                                              \

@@ -62,17 +62,16 @@ struct Args {
   void* Ft;      // F^T, F = K exp2(Gn - G) [nc,H,K,64] fragment order   forward scan (S += F^T R)
   void* U;       // A Z                 [nc,H,64,V] fragment order   forward scan
   float* glast;  // G2 at the last row  [nc,H,K]     both scans
-  void* Qg;      // s Q exp2(G)         [BT,H,K]     output
-  void* Cq;      // tril_incl(Qg Y^T)   [nc,H,64/16,64,16] column-blocked  output
+  void* Qg;      // s Q exp2(G)         [nc,H,64,K] in the order of W   forward scan output product
+  void* Cq;      // tril_incl(Qg Y^T)   [nc,H,4,4,64 lanes,4]: block (I, J) holds the C fragment of
+                 // (Cq_IJ)^T, i.e. Cq[16 I + (l & 15)][16 J + 4 (l >> 4) + e]   forward scan output product
   void* F;       // F                   [nc,H,64,K] fragment order   reverse scan (Rbar = F dS+)
   void* Wt;      // W^T                 [nc,H,K,64] fragment order   reverse scan (dS -= W^T Rbar)
   void* Qgt;     // Qg^T                [nc,H,K,64] fragment order   reverse scan (dS += Qg^T dO)
   void* Cqt;     // Cq^T                [nc,H,64,64] fragment order  reverse scan (Rbar += Cq^T dO)
   void* hbuf;    // state entering each chunk [nc,H,V/16,K,16] dtype (column-blocked)
   void* R;       // corrections U - W S [nc,H,V/16,64,16] dtype (column-blocked, zero past the end)
-  void* hbufT;   // the same states transposed [nc,H,V,K], fragment order (output kernel)
-  void* RT;      // R^T tiles [nc,H,V,64], fragment order (output kernel)
-  int scan_out;  // SCAN_* bits: which of hbuf/R and hbufT/RT the forward scan writes
+  int scan_out;  // SCAN_* bits: whether the forward scan writes hbuf/R and whether it forms o
   void* At;      // A^T                 [nc,H,64,64] chunk backward (P = A^T Rbar)
   void* Kt;      // K^T                 [nc,H,64/16,K,16] column-blocked  chunk backward
   void* Qt;      // Q^T                 [nc,H,64/16,K,16] column-blocked  chunk backward
@@ -84,8 +83,8 @@ struct Args {
   void* dhbuf;   // adjoint of the state leaving each chunk [nc,H,V/16,K,16] dtype (column-blocked)
 };
 
-constexpr int SCAN_NATURAL = 1;     // hbuf, R (read by the chunk backward)
-constexpr int SCAN_TRANSPOSED = 2;  // hbufT, RT (read by the output kernel)
+constexpr int SCAN_NATURAL = 1;  // hbuf, R (read by the chunk backward)
+constexpr int SCAN_OUTPUT = 2;   // o = Qg S + Cq R, formed by the forward scan
 
 constexpr int PREP_FWD_SCAN = 1;  // W, Ft, U, glast
 constexpr int PREP_FWD_OUT = 2;   // Qg, Cq
@@ -99,7 +98,6 @@ hipError_t launch_fwd_prep(const Args& a, int dtype_f32, hipStream_t s);
 // that the number of workgroups covers the chip.
 int scan_bv(const Args& a, int dtype_f32);
 hipError_t launch_fwd_scan(const Args& a, int dtype_f32, hipStream_t s);
-hipError_t launch_fwd_out(const Args& a, int dtype_f32, hipStream_t s);
 hipError_t launch_bwd_scan(const Args& a, int dtype_f32, hipStream_t s);
 // the forward scan (natural outputs) and the reverse scan in one launch
 hipError_t launch_scans(const Args& a, int dtype_f32, hipStream_t s);

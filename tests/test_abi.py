@@ -85,7 +85,7 @@ def test_workspace_sizes_follow_the_layout(lib):
     tileV = up(nc * H * V * 64 * e)
     shared = up(nc * H * K * 4) + up(nc * H * K * V * e) + tileV       # glast, hbuf, R
     scan = tokK + tileK + tokV                                          # W, Ft, U
-    out = tokK + tile64 + up(nc * H * K * V * e) + up(nc * H * V * 64 * e)  # Qg, Cq, hbufT, RT
+    out = tileK + tile64                                                # Qg, Cq
     rscan = tokK + 2 * tileK + tile64                                   # F, Wt, Qgt, Cqt
     rscan += tile64 + 2 * tileK + up(nc * H * K * 64 * 4)               # At, Kt, Qt, G2t
     rscan += up(nc * H * 4 * K * 16)                                    # Gst
