@@ -37,7 +37,9 @@
 
 namespace rewy {
 
-template <typename T, int K, int V>
+// GATE: 0 none, 1 scalar, 2 vector (a template parameter: no gate tests in
+// the loops).
+template <typename T, int K, int V, int GATE>
 __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   constexpr int NTH = 256;
   constexpr int PV = pitch<T>(V), PA = pitch<T>(CH);
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   // outputs through bounds-checked buffers: rows past the chunk's end are dropped
   const GBuf bdq = gbuf(reinterpret_cast<T*>(a.dq) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
   const GBuf bdk = gbuf(reinterpret_cast<T*>(a.dk) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
-  const GBuf bdg = gbuf(a.dg + (t0 * H + h) * K, a.gate == 2 ? tile_bytes<float>(n, gsK, K) : 0u);
+  const GBuf bdg = gbuf(a.dg + (t0 * H + h) * K, GATE == 2 ? tile_bytes<float>(n, gsK, K) : 0u);
   const int jl = n - 1;  // last valid row
   const FR DmI = pick(Dm, I), HmI = pick(Hm, I), DtmI = pick(Dtm, I), HtmI = pick(Htm, I);
   const f32x4 bI = *reinterpret_cast<const f32x4*>(sBeta + I * SUB + 4 * q4);
@@ -267,11 +269,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   TileRegs<float, 1, SUB, NTH> pN;
   // G2^T, K^T and Q^T are column-blocked [64/16][K][16] (a scalar gate: one
   // row, [64]; rows 1 .. 15 of its tile are not used)
-  const float* gp = a.gate == 2 ? a.G2t + cb * K * CH : a.G2t + cb * CH;
-  const int grt = a.gate == 2 ? K : 1;
-  const uint32_t gbytes = a.gate == 2 ? K * CH * 4 : a.gate == 1 ? CH * 4 : 0;
+  const float* gp = GATE == 2 ? a.G2t + cb * K * CH : a.G2t + cb * CH;
+  const int grt = GATE == 2 ? K : 1;
+  const uint32_t gbytes = GATE == 2 ? K * CH * 4 : GATE == 1 ? CH * 4 : 0;
   auto fetch_fb = [&](int fb) {
-    pG.load_cb(gbuf(gp, gbytes), grt, a.gate == 2 ? fb * SUB : 0, tid);
+    pG.load_cb(gbuf(gp, gbytes), grt, GATE == 2 ? fb * SUB : 0, tid);
     pK.load_cb(gbuf(Ktg, K * CH * sizeof(T)), K, fb * SUB, tid);
     pQ.load_cb(gbuf(Qtg, K * CH * sizeof(T)), K, fb * SUB, tid);
     pX.load(gbuf(Gstg + fb * SUB * 4, tile_bytes<float>(NSUB, K * 4, SUB * 4)), K * 4, tid);
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
     pN.load(gbuf(a.glast + cb * K + fb * SUB, SUB * sizeof(float)), SUB, tid);
   };
   auto put_fb = [&]() {
-    if (a.gate != 0) pG.store_cb(sG2, PGS, tid);
+    if constexpr (GATE != 0) pG.store_cb(sG2, PGS, tid);
     pK.store_cb(sKs, PKS, tid);
     pQ.store_cb(sQs, PKS, tid);
     pX.store(sSt, SUB * 4, tid);
@@ -311,9 +313,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       FR kp[NSUB], qp[NSUB];
       static_for<0, NSUB>([&](auto J) {
         const int r0 = J * SUB + 4 * q4;
-        if (a.gate == 2)
+        if constexpr (GATE == 2)
           G[J] = *reinterpret_cast<const f32x4*>(sG2 + f * PGS + r0);
-        else if (a.gate == 1)
+        else if constexpr (GATE == 1)
           G[J] = *reinterpret_cast<const f32x4*>(sG2 + r0);
         else
           G[J] = zero4();
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       pdq = yq;
       pdk = yk;
     }
-    if (a.gate == 2) {
+    if constexpr (GATE == 2) {
       // in-block reverse sum: own rows, then the lane groups after this one
       const float s = gbar[0] + gbar[1] + gbar[2] + gbar[3];
       float x = s;
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       f32x4 tg = zero4();
       mm16(tg, f32x4{suf[0] + add, suf[1] + add, suf[2] + add, suf[3] + add}, idf);
       gst16(bdg, (uint32_t)(((int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4) * 4), __builtin_bit_cast(uint4, tg));
-    } else if (a.gate == 1 && live) {
+    } else if (GATE == 1 && live) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = gbar[e];
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       lamws += x;
       lam0s += y;
     }
-    if (a.gate != 2) lds_barrier();  // this block's operands are no longer read
+    if constexpr (GATE != 2) lds_barrier();  // this block's operands are no longer read
     put_fb();                        // after the last block: unused
     lds_barrier();                   // the next block's operands are visible
   }
@@ -581,7 +583,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   }
 
   // ---- scalar gate: reverse sum over the chunk's rows ---------------------------
-  if (a.gate == 1) {
+  if constexpr (GATE == 1) {
     const float s = sufs[0] + sufs[1] + sufs[2] + sufs[3];
     float x = s;
     float y = __shfl_down(x, 16);
@@ -614,10 +616,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   }
 }
 
+template <typename T, int GATE>
+static hipError_t bwd_chunk_g(const Args& a, hipStream_t s) {
+  const dim3 grid(a.nc_max * a.H), block(256);
+  REWY_KV_SWITCH_X(k_bwd_chunk, GATE)
+}
+
 template <typename T>
 static hipError_t bwd_chunk_t(const Args& a, hipStream_t s) {
-  const dim3 grid(a.nc_max * a.H), block(256);
-  REWY_KV_SWITCH(k_bwd_chunk)
+  switch (a.gate) {
+    case 0: return bwd_chunk_g<T, 0>(a, s);
+    case 1: return bwd_chunk_g<T, 1>(a, s);
+    case 2: return bwd_chunk_g<T, 2>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_bwd_chunk(const Args& a, int f32, hipStream_t s) {
