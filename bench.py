@@ -45,7 +45,7 @@ def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy
     w_fscan = n * (tk + tv) + tileK + glast              # W, U, Ft, glast
     w_fout = tileK + tile64                               # Qg, Cq
     w_bscan = n * tk + 2 * tileK + tile64                 # F, Wt, Qgt, Cqt
-    w_bchunk = tile64 + 2 * tileK + g2t + gst             # At, Kt, Qt, G2t, Gst
+    w_bchunk = tile64 + g2t + gst                         # At, G2t, Gst
     if policy == "save":
         prep = prep_in + w_fscan + w_fout + w_bscan + w_bchunk
     else:
@@ -57,8 +57,10 @@ def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy
         "k_fwd_scan": n * (tk + tv) + tileK + glast + tileK + tile64 + n * tv
                       + (st + tileV if policy == "save" else 0),
         "k_bwd_scan": n * (tk + tv) + 2 * tileK + tile64 + glast + st + tileV,
-        "k_bwd_chunk": n * 3 * tv + tile64 + tileV + 2 * st + 2 * tileK + g2t + gst + n * besz
-                       + n * (2 * tk + tv + gb + besz),
+        # reads dO, R, v, A^T, Rbar, S, dS+, k, q, G2^T, statistics, glast, beta;
+        # writes dq, dk, dv, dg, dbeta
+        "k_bwd_chunk": n * 3 * tv + tile64 + tileV + 2 * st + n * 2 * tk + g2t + gst + glast
+                       + n * besz + n * (2 * tk + tv + gb + besz),
     }
     # the backward's forward scan and reverse scan in one launch
     per_head["k_scans"] = n * (tk + tv) + tileK + glast + st + tileV + per_head["k_bwd_scan"]

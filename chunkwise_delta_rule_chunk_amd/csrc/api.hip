@@ -91,7 +91,7 @@ int make_plan(const rewy_desc* d, Plan& p) {
 // Buffer layout.  `saved` holds what the backward reads from the forward under
 // the save-all policy; everything else is scratch in the workspace.  The
 // reverse set is what the reverse scan and the chunk backward read:
-// F Wt Qgt Cqt (reverse scan) and At Kt Qt G2t Gst (chunk backward).
+// F Wt Qgt Cqt (reverse scan) and At G2t Gst (chunk backward).
 //   recompute: ws = [index | glast hbuf R | W Ft U | (fwd) Qg Cq / (bwd) reverse set | Rbt dhbuf]
 //   save-all:  saved = [glast hbuf R | reverse set]
 //              ws (fwd) = [index | W Ft U Qg Cq],  ws (bwd) = [index | Rbt dhbuf]
@@ -101,7 +101,7 @@ struct Layout {
   size_t W, Ft, U;                   // forward scan operands
   size_t Qg, Cq;                     // output-product operands
   size_t F, Wt, Qgt, Cqt;            // reverse scan operands
-  size_t At, Kt, Qt, G2t, Gst;       // chunk backward operands
+  size_t At, G2t, Gst;               // chunk backward operands
   size_t Rbt, dhbuf;                 // written by the reverse scan
   size_t ws_fwd, ws_bwd, saved;
 };
@@ -121,8 +121,6 @@ Layout layout(const Plan& p) {
     L.Qgt = take(o, tileK);
     L.Cqt = take(o, tile64);
     L.At = take(o, tile64);
-    L.Kt = take(o, tileK);
-    L.Qt = take(o, tileK);
     L.G2t = take(o, g2);
     L.Gst = take(o, nc * H * NSUB * K * 16);
   };
@@ -192,7 +190,7 @@ void fill_common(Args& a, const Plan& p, const rewy_desc* d, char* ws, char* sv,
   a.hbuf = fs + L.hbuf; a.R = fs + L.R;
   a.F = fs + L.F; a.Wt = fs + L.Wt; a.Qgt = fs + L.Qgt; a.Cqt = fs + L.Cqt;
   a.W = ws + L.W; a.Ft = ws + L.Ft; a.U = ws + L.U; a.Qg = ws + L.Qg; a.Cq = ws + L.Cq;
-  a.At = fs + L.At; a.Kt = fs + L.Kt; a.Qt = fs + L.Qt;
+  a.At = fs + L.At;
   a.G2t = reinterpret_cast<float*>(fs + L.G2t);
   a.Gst = reinterpret_cast<float*>(fs + L.Gst);
   a.Rbt = ws + L.Rbt; a.dhbuf = ws + L.dhbuf;

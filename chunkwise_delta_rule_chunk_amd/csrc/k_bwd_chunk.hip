@@ -236,8 +236,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   // are exchanged through LDS once per feature block (all waves take part).
   const T* hb = reinterpret_cast<const T*>(a.hbuf) + cb * K * V;
   const T* dhb = reinterpret_cast<const T*>(a.dhbuf) + cb * K * V;
-  const T* Ktg = reinterpret_cast<const T*>(a.Kt) + cb * K * CH;
-  const T* Qtg = reinterpret_cast<const T*>(a.Qt) + cb * K * CH;
+  // raw k and q rows of the chunk (rows past the end read as zero)
+  const GBuf bk = gbuf(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
+  const GBuf bq = gbuf(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
   const float* Gstg = a.Gst + cb * NSUB * K * 4;  // float4 records, [J][K]
   // outputs through bounds-checked buffers: rows past the chunk's end are dropped
   const GBuf bdq = gbuf(reinterpret_cast<T*>(a.dq) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
@@ -263,7 +264,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   // products).  Every load is unconditional: a scalar gate has one G2 row
   // (the others read as zero) and no gate reads none.
   TileRegs<float, SUB, CH, NTH> pG;
-  TileRegs<T, SUB, CH, NTH> pK, pQ;
+  // k and q of a feature block from their natural rows: a piece is KQV
+  // features of one token; the first half of the pieces is k, the second q
+  // (uniform per wave), transposed into [feature][token] when stored
+  constexpr int KQV = 16 / (int)sizeof(T), KQR = SUB / KQV;  // features per piece, pieces per row
+  constexpr int KQP = 2 * CH * KQR, KQN = KQP / NTH;         // pieces, per thread
+  static_assert(KQP % NTH == 0 && (CH * KQR) % 64 == 0, "k/q pieces");
+  uint4 pkq[KQN];
   TileRegs<float, NSUB, SUB * 4, NTH> pX;
   TileRegs<T, SUB, V, NTH> pS, pD;
   TileRegs<float, 1, SUB, NTH> pN;
@@ -274,8 +281,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   const uint32_t gbytes = GATE == 2 ? K * CH * 4 : GATE == 1 ? CH * 4 : 0;
   auto fetch_fb = [&](int fb) {
     pG.load_cb(gbuf(gp, gbytes), grt, GATE == 2 ? fb * SUB : 0, tid);
-    pK.load_cb(gbuf(Ktg, K * CH * sizeof(T)), K, fb * SUB, tid);
-    pQ.load_cb(gbuf(Qtg, K * CH * sizeof(T)), K, fb * SUB, tid);
+#pragma unroll
+    for (int j = 0; j < KQN; ++j) {
+      const int pc = tid + j * NTH, rem = pc % (CH * KQR);
+      const int t = rem / KQR, f0 = (rem % KQR) * KQV;
+      const uint32_t off = (uint32_t)(((int64_t)t * gsK + fb * SUB + f0) * (int64_t)sizeof(T));
+      // k or q is the same for the whole wave (64 consecutive pieces)
+      const bool isk = __builtin_amdgcn_readfirstlane(pc) < CH * KQR;
+      pkq[j] = gld16(isk ? bk : bq, off);
+    }
     pX.load(gbuf(Gstg + fb * SUB * 4, tile_bytes<float>(NSUB, K * 4, SUB * 4)), K * 4, tid);
     pS.load_cb(gbuf(hb, K * V * sizeof(T)), K, fb * SUB, tid);
     pD.load_cb(gbuf(dhb, K * V * sizeof(T)), K, fb * SUB, tid);
@@ -283,8 +297,19 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   };
   auto put_fb = [&]() {
     if constexpr (GATE != 0) pG.store_cb(sG2, PGS, tid);
-    pK.store_cb(sKs, PKS, tid);
-    pQ.store_cb(sQs, PKS, tid);
+#pragma unroll
+    for (int j = 0; j < KQN; ++j) {
+      const int pc = tid + j * NTH, rem = pc % (CH * KQR);
+      const int t = rem / KQR, f0 = (rem % KQR) * KQV;
+      union {
+        uint4 u;
+        T e[KQV];
+      } x;
+      x.u = pkq[j];
+      T* dst = (pc < CH * KQR ? sKs : sQs) + f0 * PKS + t;
+#pragma unroll
+      for (int e = 0; e < KQV; ++e) dst[e * PKS] = x.e[e];
+    }
     pX.store(sSt, SUB * 4, tid);
     pS.store_cb(sSs, PSS, tid);
     pD.store_cb(sDs, PSS, tid);

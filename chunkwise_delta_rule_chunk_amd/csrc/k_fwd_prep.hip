@@ -241,10 +241,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
       constexpr int KGF = 4 * VE, NGTF = CH / KGF;
       T* Ftd = reinterpret_cast<T*>(a.Ft) + cb * K * CH;
       T* Qgtd = reinterpret_cast<T*>(a.Qgt) + cb * K * CH;
-      // K^T, Q^T, G2^T column-blocked [64/16][K][16]: this thread's 16 rows are
-      // one block row, and a wave's consecutive columns are contiguous
-      T* Ktd = reinterpret_cast<T*>(a.Kt) + cb * K * CH + ((int64_t)g.seg * K + col) * SUB;
-      T* Qtd = reinterpret_cast<T*>(a.Qt) + cb * K * CH + ((int64_t)g.seg * K + col) * SUB;
       // F and Qg in operand-fragment order (row block seg, key group
       // col / KGF): this thread's 16 rows are elements VE apart in one column
       // of pieces (rows past the chunk's end are zeros)
@@ -263,13 +259,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
         union {
           uint4 u;
           T e[VE];
-        } ft, qt, kt, qq, et;
+        } ft, qt, et;
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
           const int r = r8 + e, row = r0 + r;
           const T kraw = sK[row * PK + col], qraw = sQ[row * PK + col];
-          kt.e[e] = kraw;  // raw k and q (zero past the chunk's end)
-          qq.e[e] = qraw;
           const float G = g.G[r];
           const float kr = tof(kraw), qr = tof(qraw);
           const float ea = fexp2(G - rA), eb = fexp2(rB - G);
@@ -293,12 +287,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
           const int tk = r0 + r8, q = tk / KGF, gq = (tk % KGF) / VE;
           *reinterpret_cast<uint4*>(Qgtd + (((col / SUB) * NGTF + q) * 64 + gq * 16 + col % SUB) * VE) = qt.u;
         }
-        if constexpr (MODE & PREP_BWD_CHUNK) {
-          *reinterpret_cast<uint4*>(Ktd + r8) = kt.u;
-          *reinterpret_cast<uint4*>(Qtd + r8) = qq.u;
-        }
       }
-      // G2 token-contiguous (rows past the end hold G2 of the last row)
+      // G2^T column-blocked [64/16][K][16]: this thread's 16 rows are one block
+      // row, and a wave's consecutive columns are contiguous (rows past the end
+      // hold G2 of the last row)
       if constexpr (MODE & PREP_BWD_CHUNK) {
         float* G2d = a.gate == 2 ? a.G2t + cb * K * CH + ((int64_t)g.seg * K + col) * SUB
                                  : (a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr);

@@ -73,8 +73,6 @@ struct Args {
   void* R;       // corrections U - W S [nc,H,V/16,64,16] dtype (column-blocked, zero past the end)
   int scan_out;  // SCAN_* bits: whether the forward scan writes hbuf/R and whether it forms o
   void* At;      // A^T                 [nc,H,64,64] chunk backward (P = A^T Rbar)
-  void* Kt;      // K^T                 [nc,H,64/16,K,16] column-blocked  chunk backward
-  void* Qt;      // Q^T                 [nc,H,64/16,K,16] column-blocked  chunk backward
   float* G2t;    // G2^T  [nc,H,64/16,K,16] column-blocked (vector gate) or [nc,H,64] (scalar gate)
   float* Gst;    // sub-chunk gate statistics [nc,H,4,K] of float4 {G2 at the first row,
                  // G2 at the last valid row, midpoint (max+min)/2, range max-min}
@@ -89,7 +87,7 @@ constexpr int SCAN_OUTPUT = 2;   // o = Qg S + Cq R, formed by the forward scan
 constexpr int PREP_FWD_SCAN = 1;  // W, Ft, U, glast
 constexpr int PREP_FWD_OUT = 2;   // Qg, Cq
 constexpr int PREP_BWD_SCAN = 4;  // F, Wt, Qgt, Cqt, glast
-constexpr int PREP_BWD_CHUNK = 8; // At, Kt, Qt, G2t, Gst
+constexpr int PREP_BWD_CHUNK = 8; // At, G2t, Gst
 
 // Launchers: enqueue on `stream`; return the hipError_t of the launch.
 hipError_t launch_chunk_table(const Args& a, hipStream_t s);
