@@ -24,14 +24,15 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy):
+def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy, prep_mode=None):
     """Algorithmic HBM bytes of one launch of `kernel` in this design: its
     compulsory reads and writes, each counted once.  Token-level rows count per
     valid token; chunk tiles count their full 64 rows per chunk-head.  The
     forward prep runs in two modes under the recompute policy (forward pass,
     and the recompute in the backward pass that also writes the reverse-scan
     and chunk-backward operands); its figure is the mean of the launches of
-    one step, matching the pooled average duration."""
+    one step, matching the pooled average duration (prep_mode "forward" or
+    "recompute" gives one launch's figure instead)."""
     n = sum(chunk_lens)                 # valid tokens per head
     nc = len(chunk_lens)                # chunks per head
     gb = {0: 0, 1: 4, 2: 4 * K}[gate]   # gate bytes per token
@@ -48,6 +49,10 @@ def kernel_bytes(kernel: str, chunk_lens, H, K, V, esz, besz, gate, nseq, policy
     w_bchunk = tile64 + g2t + gst                         # At, G2t, Gst
     if policy == "save":
         prep = prep_in + w_fscan + w_fout + w_bscan + w_bchunk
+    elif prep_mode == "forward":
+        prep = prep_in + w_fscan + w_fout
+    elif prep_mode == "recompute":
+        prep = prep_in + w_fscan + w_bscan + w_bchunk
     else:
         prep = prep_in + (w_fscan + w_fout + (w_fscan + w_bscan + w_bchunk)) / 2
     per_head = {
