@@ -101,6 +101,48 @@ def measured_traffic(kernel: str, workload: str, policy: str):
     return None
 
 
+def _time_decode(result, args, ops, binding, torch):
+    """The token-serial forward (rewy_recurrent_fwd) at a decode shape: 64
+    sequences with an fp32 state each, one new token per sequence and call,
+    H=32, K=V=128, bf16, vector gate.  The kernel reads and writes every state
+    once per call, so it is HBM-bound on the state bytes."""
+    import workloads
+    Bd, H, K, V = 64, 32, 128, 128
+    dev = torch.device("cuda:0")
+    inp = workloads.make_inputs(Bd, 1, H, K, V, gate="vector", dtype="bf16", h0="normal", seed=11)
+    x = inp.to(dev)
+
+    def call():
+        return ops.recurrent_forward(x.q, x.k, x.v, x.g, x.beta, scale=inp.scale, h0=x.h0)
+
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    n = max(args.steps, 20)
+    binding.rewy_trace_select("k_recurrent")
+    binding.rewy_trace_begin()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    tr = binding.rewy_trace_end()
+    binding.rewy_trace_select(None)
+    kern_ms = sum(t for _, t, _ in tr) / max(1, sum(c for _, _, c in tr))
+    state = Bd * H * K * V * 4
+    nbytes = 2 * state + Bd * H * ((2 * K + 2 * V) * 2 + K * 4 + 2)  # states in/out; q k v o, g, beta
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    result["decode"] = {
+        "workload": "kda_decode_b64_h32_d128: 64 sequences, one new token each, fp32 state carried",
+        "tokens_per_s": Bd / (ms * 1e-3), "ms_per_call": ms, "kernel_ms": kern_ms,
+        "roofline": {"kernel": "k_recurrent", "bound": "hbm", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    print(f"[bench] decode: {ms:.3f} ms per call, kernel {kern_ms * 1e3:.1f} us, "
+          f"{achieved:.0f} GB/s", file=sys.stderr, flush=True)
+
+
 def _time_other(result, other, prob2, x, inp, B, T, args, ops, torch):
     """Time K steps under the other saving policy and record them in result."""
     w20, w21 = ops.workspace(prob2, 0), ops.workspace(prob2, 1)
@@ -137,6 +179,8 @@ def main():
                     help="warm-up lasts at least this long (profiler runs pass 0)")
     ap.add_argument("--no-other-policy", action="store_true",
                     help="skip timing the other saving policy (profiler runs)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip timing the token-serial forward at a decode shape")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB once (a plain "
                          "copy kernel of known size, to calibrate HBM byte counters)")
@@ -279,6 +323,8 @@ def main():
                                                          cu_seqlens=inp.cu_seqlens, policy=other)
     if other is not None:
         _time_other(result, other, prob2, x, inp, B, T, args, ops, torch)
+    if not args.no_decode:
+        _time_decode(result, args, ops, binding, torch)
 
     if not args.no_cpu_baseline:
         import oracle

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(HERE, "librewy.so")
 ARCH = "gfx950"
-SOURCES = ["api.hip", "k_fwd_prep.hip", "k_scan.hip", "k_bwd_chunk.hip"]
+SOURCES = ["api.hip", "k_fwd_prep.hip", "k_scan.hip", "k_bwd_chunk.hip", "k_recurrent.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 CFLAGS = [

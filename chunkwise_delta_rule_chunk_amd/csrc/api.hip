@@ -308,6 +308,33 @@ REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const vo
   return run_forward_stages(a, p.f32, true, s);
 }
 
+REWY_API int rewy_recurrent_fwd(const rewy_desc* d, const void* q, const void* k, const void* v,
+                                const float* g, const void* beta, const float* h0, void* o,
+                                float* ht, void* stream) {
+  Plan p;
+  int rc = make_plan(d, p);
+  if (rc) return rc;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t state_n = (int64_t)p.N * p.H * p.K * p.V;
+  if (p.BT == 0) return copy_state(ht, h0, state_n, s);
+  {
+    const void* ps[] = {q, k, v, beta, o};
+    const char* nm[] = {"q", "k", "v", "beta", "o"};
+    if ((rc = check_tensor_ptrs(ps, nm, 5))) return rc;
+  }
+  if ((p.gate != REWY_GATE_NONE) != (g != nullptr))
+    return fail(REWY_EINVAL, "g must be given exactly when gate != NONE");
+  if (g && !aligned(g, 16)) return fail(REWY_EINVAL, "g is not 16-byte aligned");
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.B = p.B; a.T = p.T; a.H = p.H; a.K = p.K; a.V = p.V; a.N = p.N;
+  a.gate = p.gate; a.beta_f32 = p.beta_f32; a.scale = d->scale; a.cu = d->cu_seqlens;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+  return hip_check(traced("k_recurrent", variant_of(a, p.f32), s,
+                          [&] { return launch_recurrent(a, p.f32, s); }),
+                   "recurrent forward");
+}
+
 REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const void* v,
                       const float* g, const void* beta, const float* h0, const void* dO,
                       const float* dht, const void* saved, void* dq, void* dk, void* dv,

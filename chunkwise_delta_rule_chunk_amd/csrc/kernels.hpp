@@ -100,5 +100,7 @@ hipError_t launch_bwd_scan(const Args& a, int dtype_f32, hipStream_t s);
 // the forward scan (natural outputs) and the reverse scan in one launch
 hipError_t launch_scans(const Args& a, int dtype_f32, hipStream_t s);
 hipError_t launch_bwd_chunk(const Args& a, int dtype_f32, hipStream_t s);
+// the token-serial forward (decode)
+hipError_t launch_recurrent(const Args& a, int dtype_f32, hipStream_t s);
 
 }  // namespace rewy

@@ -105,6 +105,19 @@ def forward(q, k, v, g, beta, *, scale=None, h0=None, cu_seqlens=None, policy="r
     return o, ht, ctx
 
 
+def recurrent_forward(q, k, v, g, beta, *, scale=None, h0=None, cu_seqlens=None,
+                      output_final_state=True, stream=None):
+    """Run rewy_recurrent_fwd (token-serial, for decoding).  Returns (o, ht or None)."""
+    prob = make_problem(q, v, g, beta, scale=scale, cu_seqlens=cu_seqlens)
+    o = torch.empty_like(v)
+    ht = torch.empty(prob.state_shape, dtype=torch.float32, device=q.device) \
+        if output_final_state else None
+    rc = B.rewy_recurrent_fwd(prob.desc, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0), _p(o),
+                              _p(ht), _stream(q.device, stream))
+    _check(rc, "rewy_recurrent_fwd")
+    return o, ht
+
+
 def backward(ctx, dO, dht=None, *, stream=None, ws=None, want_dh0=None):
     """Run rewy_bwd.  Returns dict dq, dk, dv, dg, dbeta, dh0."""
     prob = ctx["prob"]

@@ -109,6 +109,20 @@ int rewy_bwd(const rewy_desc *d, const void *q, const void *k, const void *v,
              void *dq, void *dk, void *dv, float *dg, void *dbeta, float *dh0,
              void *workspace, size_t ws_bytes, void *stream);
 
+/* Token-serial forward for decoding (the pages' fused recurrent form of the
+ * same recurrence: ReWY paper, Background / Delta-rule operators; KDA blog
+ * section 4): o_t = S_t^T (s q_t) with the state updated one token at a time,
+ * decay -> predict -> correct -> write -> read.  Same descriptor and tensors as
+ * rewy_fwd (the policy is ignored) and no workspace or saved buffer: the
+ * fp32 state of each (sequence, head) stays on chip from h0 to ht.  h0 and ht
+ * may be NULL (zero initial state; final state not returned).  Meant for short
+ * continuations, e.g. one new token per sequence with h0/ht carried between
+ * calls; long prompts are faster through rewy_fwd.  Argument errors return a
+ * negative status before anything is enqueued. */
+int rewy_recurrent_fwd(const rewy_desc *d, const void *q, const void *k, const void *v,
+                       const float *g, const void *beta, const float *h0,
+                       void *o, float *ht, void *stream);
+
 /* Per-kernel timing (a tracing aid: device events, as in the ReWY paper's timing
  * protocol).  After rewy_trace_begin(), calls made by this thread
  * record a HIP event pair on the call's stream around every kernel they

@@ -133,6 +133,13 @@ def test_calls_reject_bad_pointers_without_launching(lib):
     rc = B.rewy_fwd(dsv, P(256), P(256), P(256), P(256), P(256), None, P(256), None, None,
                     P(256), 1 << 40, None)
     assert rc == B.REWY_EWORKSPACE
+    # token-serial forward: the same host-side checks
+    rc = B.rewy_recurrent_fwd(d, None, P(256), P(256), P(256), P(256), None, P(256), None, None)
+    assert rc == B.REWY_EINVAL and "q is NULL" in B.rewy_last_error()
+    rc = B.rewy_recurrent_fwd(d, P(256), P(256), P(256), None, P(256), None, P(256), None, None)
+    assert rc == B.REWY_EINVAL and "g must be given" in B.rewy_last_error()
+    rc = B.rewy_recurrent_fwd(d, P(256), P(256), P(264), P(256), P(256), None, P(256), None, None)
+    assert rc == B.REWY_EINVAL and "aligned" in B.rewy_last_error()
     del ws
 
 
