@@ -143,6 +143,31 @@ def _time_decode(result, args, ops, binding, torch):
           f"{achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
 
+def _time_gdn2(result, x, inp, B, T, args, ops, torch):
+    """The erase/write form (independent erase gate b [B,T,H,K] and write gate
+    w [B,T,H,V]) on the same inputs: one forward + backward step."""
+    gen = torch.Generator().manual_seed(13)
+    b = torch.sigmoid(torch.randn(*inp.k.shape, generator=gen)).to(inp.q.dtype).to(x.q.device)
+    w = torch.sigmoid(torch.randn(*inp.v.shape, generator=gen)).to(inp.q.dtype).to(x.q.device)
+
+    def step2():
+        o, ht, ctx = ops.forward_gdn2(x.q, x.k, x.v, x.g, b, w, scale=inp.scale, h0=x.h0,
+                                      cu_seqlens=inp.cu_seqlens, policy=args.policy)
+        return ops.backward(ctx, x.dO, x.dht)
+
+    for _ in range(max(3, args.warmup // 4)):
+        step2()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step2()
+    torch.cuda.synchronize()
+    ms2 = (time.perf_counter() - t2) * 1e3 / args.steps
+    result["gdn2"] = {"form": "erase/write gates (b, w) in place of beta", "policy": args.policy,
+                      "ms_per_step": ms2, "value": B * T / (ms2 * 1e-3), "unit": "tokens/s"}
+    print(f"[bench] erase/write form: {ms2:.3f} ms/step", file=sys.stderr, flush=True)
+
+
 def _time_other(result, other, prob2, x, inp, B, T, args, ops, torch):
     """Time K steps under the other saving policy and record them in result."""
     w20, w21 = ops.workspace(prob2, 0), ops.workspace(prob2, 1)
@@ -181,6 +206,8 @@ def main():
                     help="skip timing the other saving policy (profiler runs)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip timing the token-serial forward at a decode shape")
+    ap.add_argument("--no-gdn2", action="store_true",
+                    help="skip timing the erase/write form")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB once (a plain "
                          "copy kernel of known size, to calibrate HBM byte counters)")
@@ -325,6 +352,8 @@ def main():
         _time_other(result, other, prob2, x, inp, B, T, args, ops, torch)
     if not args.no_decode:
         _time_decode(result, args, ops, binding, torch)
+    if not args.no_gdn2:
+        _time_gdn2(result, x, inp, B, T, args, ops, torch)
 
     if not args.no_cpu_baseline:
         import oracle

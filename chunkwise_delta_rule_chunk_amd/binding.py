@@ -17,7 +17,8 @@ REWY_GATE_NONE, REWY_GATE_SCALAR, REWY_GATE_VECTOR = 0, 1, 2
 REWY_BF16, REWY_F32 = 0, 1
 REWY_RECOMPUTE, REWY_SAVE = 0, 1
 
-EXPORTS = ("rewy_workspace_bytes", "rewy_saved_bytes", "rewy_fwd", "rewy_bwd", "rewy_recurrent_fwd",
+EXPORTS = ("rewy_workspace_bytes", "rewy_saved_bytes", "rewy_fwd", "rewy_bwd", "rewy_fwd_gdn2",
+           "rewy_bwd_gdn2", "rewy_recurrent_fwd",
            "rewy_trace_begin", "rewy_trace_end", "rewy_trace_select", "rewy_status_string",
            "rewy_last_error")
 
@@ -66,6 +67,10 @@ def load():
         lib.rewy_fwd.restype = ctypes.c_int
         lib.rewy_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
         lib.rewy_bwd.restype = ctypes.c_int
+        lib.rewy_fwd_gdn2.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        lib.rewy_fwd_gdn2.restype = ctypes.c_int
+        lib.rewy_bwd_gdn2.argtypes = [D] + [P] * 18 + [S, P]
+        lib.rewy_bwd_gdn2.restype = ctypes.c_int
         lib.rewy_recurrent_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P]
         lib.rewy_recurrent_fwd.restype = ctypes.c_int
         lib.rewy_trace_begin.argtypes = []
@@ -99,6 +104,17 @@ def rewy_bwd(desc, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, 
              ws_bytes, stream) -> int:
     return load().rewy_bwd(ctypes.byref(desc), q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv,
                            dg, dbeta, dh0, workspace, ws_bytes, stream)
+
+
+def rewy_fwd_gdn2(desc, q, k, v, g, b, w, h0, o, ht, saved, workspace, ws_bytes, stream) -> int:
+    return load().rewy_fwd_gdn2(ctypes.byref(desc), q, k, v, g, b, w, h0, o, ht, saved, workspace,
+                                ws_bytes, stream)
+
+
+def rewy_bwd_gdn2(desc, q, k, v, g, b, w, h0, dO, dht, saved, dq, dk, dv, dg, db, dw, dh0,
+                  workspace, ws_bytes, stream) -> int:
+    return load().rewy_bwd_gdn2(ctypes.byref(desc), q, k, v, g, b, w, h0, dO, dht, saved, dq, dk,
+                                dv, dg, db, dw, dh0, workspace, ws_bytes, stream)
 
 
 def rewy_recurrent_fwd(desc, q, k, v, g, beta, h0, o, ht, stream) -> int:

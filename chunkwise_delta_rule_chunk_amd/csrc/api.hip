@@ -275,12 +275,20 @@ REWY_API size_t rewy_saved_bytes(const rewy_desc* d) {
   return layout(p).saved;
 }
 
-REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const void* v,
-                      const float* g, const void* beta, const float* h0, void* o, float* ht,
-                      void* saved, void* workspace, size_t ws_bytes, void* stream) {
+namespace rewy {
+namespace {
+// The forward of both forms: beta [BT,H] (shared erase/write factor), or
+// with wg non-null the erase gate b [BT,H,K] in `beta` and the write gate w
+// [BT,H,V] in `wg`, both in the feature dtype.
+int forward_impl(const rewy_desc* d, const void* q, const void* k, const void* v, const float* g,
+                 const void* beta, const void* wg, const float* h0, void* o, float* ht, void* saved,
+                 void* workspace, size_t ws_bytes, void* stream) {
   Plan p;
   int rc = make_plan(d, p);
   if (rc) return rc;
+  const bool ew = wg != nullptr;
+  if (ew && d->beta_dtype != d->dtype)
+    return fail(REWY_EUNSUPPORTED, "the erase/write gates must have the feature dtype");
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t state_n = (int64_t)p.N * p.H * p.K * p.V;
   if (p.BT == 0) return copy_state(ht, h0, state_n, s);
@@ -302,10 +310,27 @@ REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const vo
   Args a;
   fill_common(a, p, d, static_cast<char*>(workspace), static_cast<char*>(saved), L);
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+  a.wg = wg; a.ew = ew;
+  if (ew && !aligned(wg, 16)) return fail(REWY_EINVAL, "w is not 16-byte aligned");
   a.prep_mode = PREP_FWD_SCAN | PREP_FWD_OUT |
                 (p.policy == REWY_SAVE ? PREP_BWD_SCAN | PREP_BWD_CHUNK : 0);
   a.scan_out = SCAN_OUTPUT | (p.policy == REWY_SAVE ? SCAN_NATURAL : 0);
   return run_forward_stages(a, p.f32, true, s);
+}
+}  // namespace
+}  // namespace rewy
+
+REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const void* v,
+                      const float* g, const void* beta, const float* h0, void* o, float* ht,
+                      void* saved, void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(d, q, k, v, g, beta, nullptr, h0, o, ht, saved, workspace, ws_bytes, stream);
+}
+
+REWY_API int rewy_fwd_gdn2(const rewy_desc* d, const void* q, const void* k, const void* v,
+                           const float* g, const void* b, const void* w, const float* h0, void* o,
+                           float* ht, void* saved, void* workspace, size_t ws_bytes, void* stream) {
+  if (!b || !w) return fail(REWY_EINVAL, "b and w must be given");
+  return forward_impl(d, q, k, v, g, b, w, h0, o, ht, saved, workspace, ws_bytes, stream);
 }
 
 REWY_API int rewy_recurrent_fwd(const rewy_desc* d, const void* q, const void* k, const void* v,
@@ -335,14 +360,23 @@ REWY_API int rewy_recurrent_fwd(const rewy_desc* d, const void* q, const void* k
                    "recurrent forward");
 }
 
-REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const void* v,
-                      const float* g, const void* beta, const float* h0, const void* dO,
-                      const float* dht, const void* saved, void* dq, void* dk, void* dv,
-                      float* dg, void* dbeta, float* dh0, void* workspace, size_t ws_bytes,
-                      void* stream) {
+namespace rewy {
+namespace {
+// The backward of both forms; with wg non-null, `dbeta` receives db [BT,H,K]
+// and `dw` receives dw [BT,H,V] (feature dtype).
+int backward_impl(const rewy_desc* d, const void* q, const void* k, const void* v, const float* g,
+                  const void* beta, const void* wg, const float* h0, const void* dO,
+                  const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
+                  void* dbeta, void* dw, float* dh0, void* workspace, size_t ws_bytes,
+                  void* stream) {
   Plan p;
   int rc = make_plan(d, p);
   if (rc) return rc;
+  const bool ew = wg != nullptr;
+  if (ew && d->beta_dtype != d->dtype)
+    return fail(REWY_EUNSUPPORTED, "the erase/write gates must have the feature dtype");
+  if (ew && (!dw || !aligned(wg, 16) || !aligned(dw, 16)))
+    return fail(REWY_EINVAL, "w and dw must be given, 16-byte aligned");
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (h0 && !dh0) return fail(REWY_EINVAL, "dh0 must be given when h0 is given");
   const int64_t state_n = (int64_t)p.N * p.H * p.K * p.V;
@@ -371,6 +405,7 @@ REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const vo
   a.scan_out = SCAN_NATURAL;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = dO; a.dht = dht;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+  a.wg = wg; a.ew = ew; a.dw = dw;
   const bool f32 = p.f32;
   const int vr = variant_of(a, f32);
   if (p.policy == REWY_RECOMPUTE) {
@@ -391,6 +426,27 @@ REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const vo
                       "chunk backward")))
     return rc;
   return REWY_OK;
+}
+}  // namespace
+}  // namespace rewy
+
+REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const void* v,
+                      const float* g, const void* beta, const float* h0, const void* dO,
+                      const float* dht, const void* saved, void* dq, void* dk, void* dv,
+                      float* dg, void* dbeta, float* dh0, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  return backward_impl(d, q, k, v, g, beta, nullptr, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
+                       nullptr, dh0, workspace, ws_bytes, stream);
+}
+
+REWY_API int rewy_bwd_gdn2(const rewy_desc* d, const void* q, const void* k, const void* v,
+                           const float* g, const void* b, const void* w, const float* h0,
+                           const void* dO, const float* dht, const void* saved, void* dq, void* dk,
+                           void* dv, float* dg, void* db, void* dw, float* dh0, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  if (!b || !w) return fail(REWY_EINVAL, "b and w must be given");
+  return backward_impl(d, q, k, v, g, b, w, h0, dO, dht, saved, dq, dk, dv, dg, db, dw, dh0,
+                       workspace, ws_bytes, stream);
 }
 
 REWY_API int rewy_trace_begin(void) {

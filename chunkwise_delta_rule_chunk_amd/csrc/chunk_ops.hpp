@@ -196,7 +196,9 @@ __device__ __forceinline__ void score_tiles_pre(const T* sKa, const T* sQa, cons
 // with G_i - G_j summed from the raw gates between the two rows, so no factor
 // exceeds 1.  Reads q, k, g from global.  Lane l takes column j = l & 15 and
 // the feature quarter l >> 4; results come back in the C-fragment layout.
-template <typename T, int K, bool WITH_CQ>
+// EW: the erase gate is a vector b (a.beta, [.., K], element type T), taken
+// inside the sum over features instead of beta_i outside it.
+template <typename T, int K, bool WITH_CQ, bool EW = false>
 __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, int n, int I,
                                               const float* sBeta, f32x4& accL, f32x4& accC) {
   const int l = lane_id(), j = l & 15, qk = l >> 4, H = a.H;
@@ -221,7 +223,9 @@ __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, 
             run += gi * LOG2E;
           }
           const float f = fexp2(run) * kj;
-          pL[i] += tof(kg[((t0 + ri) * H + h) * K + k]) * f;
+          float ki = tof(kg[((t0 + ri) * H + h) * K + k]);
+          if constexpr (EW) ki *= tof(reinterpret_cast<const T*>(a.beta)[((t0 + ri) * H + h) * K + k]);
+          pL[i] += ki * f;
           if constexpr (WITH_CQ) pC[i] += tof(qg[((t0 + ri) * H + h) * K + k]) * f;
         }
       }
@@ -243,7 +247,7 @@ __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, 
     if (qk == g4)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        accL[r] = sBeta[I * SUB + 4 * g4 + r] * pL[4 * g4 + r];
+        accL[r] = EW ? pL[4 * g4 + r] : sBeta[I * SUB + 4 * g4 + r] * pL[4 * g4 + r];
         accC[r] = a.scale * pC[4 * g4 + r];
       }
 }

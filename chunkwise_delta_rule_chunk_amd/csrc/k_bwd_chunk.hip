@@ -37,10 +37,15 @@
 
 namespace rewy {
 
-// GATE: 0 none, 1 scalar, 2 vector (a template parameter: no gate tests in
-// the loops).
-template <typename T, int K, int V, int GATE>
-__global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
+// GX = GATE + 4 EW.  GATE: 0 none, 1 scalar, 2 vector (a template parameter:
+// no gate tests in the loops).  EW: the erase/write form, with an erase gate b
+// per (token, feature) in place of beta in E = b gamma K and a write gate w per
+// (token, value) in Z = w V; it returns db = (gamma K) Ebar and dw = V P per
+// element (ReWY paper Table 1, GDN2 row) and runs one workgroup per CU.
+template <typename T, int K, int V, int GX>
+__global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
+  constexpr int GATE = GX & 3;
+  constexpr bool EW = GX & 4;
   constexpr int NTH = 256;
   constexpr int PV = pitch<T>(V), PA = pitch<T>(CH);
   constexpr int NFB = K / SUB, NVB = V / SUB;
@@ -54,6 +59,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   __shared__ __align__(16) T sP[CH * PV];  // P
   __shared__ __align__(16) T sR[CH * PV];  // R
   __shared__ __align__(16) char sX[cmax(SZ_AT, SZ_DG)];  // A^T, then the diagonal blocks
+  __shared__ __align__(16) T sBs[EW ? SUB * pitch<T>(CH) : 8];  // erase gate, [feature][token]
   __shared__ __align__(16) float sBeta[CH];
   __shared__ float sDbw[CH];
   __shared__ float sTot[2][NSUB * SUB], sLam[2][NSUB * SUB];  // per feature block, two buffers
@@ -96,11 +102,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
     // R per chunk-head, column-blocked [V/16][64][16], zero past the chunk's end
     pR.load_cb(gbuf(reinterpret_cast<const T*>(a.R) + cb * V * CH, V * CH * sizeof(T)), CH, 0, tid);
     pA.load(gbuf(reinterpret_cast<const T*>(a.At) + cb * CH * CH, CH * CH * sizeof(T)), CH, tid);
-    const uint32_t braw = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, n - 1)) * H + h);
+    const uint32_t braw = EW ? 0u : ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, n - 1)) * H + h);
     pO.store(sO, PV, tid);
     pR.store_cb(sR, PV, tid);
     pA.store(sAt, PA, tid);
-    if (tid < CH) sBeta[tid] = tid < n ? beta_val(braw, a.beta_f32) : 0.f;
+    if (tid < CH) sBeta[tid] = (tid < n && !EW) ? beta_val(braw, a.beta_f32) : 0.f;
   }
 
   // ---- P = A^T Rbar, rows of block I; dv and the write part of dbeta --------
@@ -115,11 +121,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
     const int i = I * SUB + f;
     // this lane's four values of v in each value block (zero past the end)
     using VR = std::conditional_t<std::is_same_v<T, bf16>, uint2, uint4>;
-    VR vr[NVB];
+    VR vr[NVB], wr[EW ? NVB : 1];  // v and (erase/write form) the write gate
+    const GBuf bw = gbuf(reinterpret_cast<const T*>(a.wg) + (t0 * H + h) * V, EW ? tile_bytes<T>(n, gsV, V) : 0u);
     static_for<0, NVB>([&](auto vb) {
       const uint32_t off = (uint32_t)(((int64_t)i * gsV + vb * SUB + 4 * q4) * (int64_t)sizeof(T));
       if constexpr (std::is_same_v<T, bf16>) vr[vb] = gld8(bv, off);
       else vr[vb] = gld16(bv, off);
+      if constexpr (EW) {
+        if constexpr (std::is_same_v<T, bf16>) wr[vb] = gld8(bw, off);
+        else wr[vb] = gld16(bw, off);
+      }
     });
     // Rbar is stored in the C-fragment order of its 16 x 16 tiles [token block
     // T][v block]: lane l's piece of tile (vb, T) holds Rbar[16 T + 4 (l >> 4) + e]
@@ -177,12 +188,28 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) dbw += tof(x[e]) * acc[vb][e];
     });
-    // rows past the chunk's end fall outside the buffer and are dropped
+    // rows past the chunk's end fall outside the buffer and are dropped.
+    // Erase/write form: dv = w P and dw = v P, element by element.
+    const GBuf bdw = gbuf(reinterpret_cast<T*>(a.dw) + (t0 * H + h) * V, EW ? tile_bytes<T>(n, gsV, V) : 0u);
     static_for<0, NVB>([&](auto vb) {
       const uint32_t off = (uint32_t)(((int64_t)i * gsV + vb * SUB + 4 * q4) * (int64_t)sizeof(T));
-      const FR y = to_frag<T>(b * acc[vb]);
+      f32x4 dvv = b * acc[vb], dww = zero4();
+      if constexpr (EW) {
+        const FR wx = __builtin_bit_cast(FR, wr[vb]), vx = __builtin_bit_cast(FR, vr[vb]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dvv[e] = tof(wx[e]) * acc[vb][e];
+          dww[e] = tof(vx[e]) * acc[vb][e];
+        }
+      }
+      const FR y = to_frag<T>(dvv);
       if constexpr (std::is_same_v<T, bf16>) gst8(bdv, off, __builtin_bit_cast(uint2, y));
       else gst16(bdv, off, __builtin_bit_cast(uint4, y));
+      if constexpr (EW) {
+        const FR z = to_frag<T>(dww);
+        if constexpr (std::is_same_v<T, bf16>) gst8(bdw, off, __builtin_bit_cast(uint2, z));
+        else gst16(bdw, off, __builtin_bit_cast(uint4, z));
+      }
     });
     dbw += __shfl_xor(dbw, 16);
     dbw += __shfl_xor(dbw, 32);
@@ -246,11 +273,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   const GBuf bdg = gbuf(a.dg + (t0 * H + h) * K, GATE == 2 ? tile_bytes<float>(n, gsK, K) : 0u);
   const int jl = n - 1;  // last valid row
   const FR DmI = pick(Dm, I), HmI = pick(Hm, I), DtmI = pick(Dtm, I), HtmI = pick(Htm, I);
-  const f32x4 bI = *reinterpret_cast<const f32x4*>(sBeta + I * SUB + 4 * q4);
+  const f32x4 bIb = *reinterpret_cast<const f32x4*>(sBeta + I * SUB + 4 * q4);  // beta, rows of block I
   f32x4 sufs = zero4();  // scalar gate: Gbar summed over features, this lane's rows
   float dbe[4] = {0.f, 0.f, 0.f, 0.f};
   // dq, dk of the previous (even) feature block, transposed (see below)
-  FR pdq = to_frag<T>(zero4()), pdk = to_frag<T>(zero4());
+  FR pdq = to_frag<T>(zero4()), pdk = to_frag<T>(zero4()), pdb = to_frag<T>(zero4());
+  // erase/write form: db of this lane's rows, stored like dk
+  const GBuf bdb = gbuf(reinterpret_cast<T*>(a.dbeta) + (t0 * H + h) * K, EW ? tile_bytes<T>(n, gsK, K) : 0u);
   // identity as the B operand of a 16-long product: C = X^T I turns this
   // lane's C-tile values (rows 4 q4 + e, feature f) into the transposed
   // layout (row f, features 4 q4 .. + 3), exactly (one term per output)
@@ -271,6 +300,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   constexpr int KQP = 2 * CH * KQR, KQN = KQP / NTH;         // pieces, per thread
   static_assert(KQP % NTH == 0 && (CH * KQR) % 64 == 0, "k/q pieces");
   uint4 pkq[KQN];
+  // erase/write form: the erase gate of the feature block, like k (a piece
+  // is KQV features of one token; only the first CH KQR pieces exist)
+  constexpr int BQN = EW ? (CH * KQR + NTH - 1) / NTH : 1;
+  static_assert((CH * KQR) % 64 == 0, "erase-gate pieces");
+  uint4 pbq[BQN];
+  const GBuf bbk = gbuf(reinterpret_cast<const T*>(a.beta) + (t0 * H + h) * K, EW ? tile_bytes<T>(n, gsK, K) : 0u);
   TileRegs<float, NSUB, SUB * 4, NTH> pX;
   TileRegs<T, SUB, V, NTH> pS, pD;
   TileRegs<float, 1, SUB, NTH> pN;
@@ -289,6 +324,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       // k or q is the same for the whole wave (64 consecutive pieces)
       const bool isk = __builtin_amdgcn_readfirstlane(pc) < CH * KQR;
       pkq[j] = gld16(isk ? bk : bq, off);
+    }
+    if constexpr (EW) {
+#pragma unroll
+      for (int j = 0; j < BQN; ++j) {
+        const int pc = tid + j * NTH, t = pc / KQR, f0 = (pc % KQR) * KQV;
+        pbq[j] = gld16(bbk, pc < CH * KQR ? (uint32_t)(((int64_t)t * gsK + fb * SUB + f0) * (int64_t)sizeof(T)) : OOB);
+      }
     }
     pX.load(gbuf(Gstg + fb * SUB * 4, tile_bytes<float>(NSUB, K * 4, SUB * 4)), K * 4, tid);
     pS.load_cb(gbuf(hb, K * V * sizeof(T)), K, fb * SUB, tid);
@@ -309,6 +351,21 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       T* dst = (pc < CH * KQR ? sKs : sQs) + f0 * PKS + t;
 #pragma unroll
       for (int e = 0; e < KQV; ++e) dst[e * PKS] = x.e[e];
+    }
+    if constexpr (EW) {
+#pragma unroll
+      for (int j = 0; j < BQN; ++j) {
+        const int pc = tid + j * NTH, t = pc / KQR, f0 = (pc % KQR) * KQV;
+        if (pc < CH * KQR) {  // whole waves
+          union {
+            uint4 u;
+            T e[KQV];
+          } x;
+          x.u = pbq[j];
+#pragma unroll
+          for (int e = 0; e < KQV; ++e) sBs[(f0 + e) * PKS + t] = x.e[e];
+        }
+      }
     }
     pX.store(sSt, SUB * 4, tid);
     pS.store_cb(sSs, PSS, tid);
@@ -331,11 +388,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
     f32x4 gbar = zero4();
     float lamw = 0.f, l0 = 0.f;
     float oq[4] = {0.f, 0.f, 0.f, 0.f}, ok_[4] = {0.f, 0.f, 0.f, 0.f};  // dq, dk of this block
+    float ob[4] = {0.f, 0.f, 0.f, 0.f};  // erase/write form: db of this block
     if (live) {
       // gated operands of all four blocks at this lane's rows 16 J + 4 q4 + e
       // (k and q stay packed in their storage type until used)
       f32x4 G[NSUB];
-      FR kp[NSUB], qp[NSUB];
+      FR kp[NSUB], qp[NSUB], bp[NSUB];
       static_for<0, NSUB>([&](auto J) {
         const int r0 = J * SUB + 4 * q4;
         if constexpr (GATE == 2)
@@ -346,6 +404,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
           G[J] = zero4();
         kp[J] = *reinterpret_cast<const FR*>(sKs + f * PKS + r0);
         qp[J] = *reinterpret_cast<const FR*>(sQs + f * PKS + r0);
+        if constexpr (EW) bp[J] = *reinterpret_cast<const FR*>(sBs + f * PKS + r0);
       });
       auto unpack = [](const FR& x) {
         f32x4 r;
@@ -368,6 +427,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       });
       const float Gn = sGn[f];
       const f32x4 GI = pick(G, I), kI = unpack(pick(kp, I)), qI = unpack(pick(qp, I));
+      // erase factor of this lane's rows: beta per row, or b per (row, feature)
+      f32x4 bI = bIb;
+      if constexpr (EW) bI = unpack(pick(bp, I));
       const float GfI = pick(Gf, I), GlI = pick(Gl, I), MdI = pick(Md, I);
       const bool wideI = pick(wide, I);
       // Row factors of block I.  Centred block: xp = exp2(G - Md), xm = exp2(Md - G)
@@ -430,7 +492,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         if (J <= I || J * SUB >= n) return;
         f32x4 es, qs;
         const f32x4 kJ = unpack(kp[J]), qJ = unpack(qp[J]);
-        const f32x4 bJ = *reinterpret_cast<const f32x4*>(sBeta + J * SUB + 4 * q4);
+        f32x4 bJ;
+        if constexpr (EW) bJ = unpack(bp[J]);
+        else bJ = *reinterpret_cast<const f32x4*>(sBeta + J * SUB + 4 * q4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = fexp2(G[J][e] - Gf[J]);
@@ -470,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
           const float Gj = __shfl(GI[j & 3], src);
           const float kj = __shfl(kI[j & 3], src);
           const float qj = __shfl(qI[j & 3], src);
-          const float bj = sBeta[I * SUB + j];
+          const float bj = EW ? tof(sBs[f * PKS + I * SUB + j]) : sBeta[I * SUB + j];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * q4 + e;
@@ -501,6 +565,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
           ok_[e] = b * XE + XY;
           gbar[e] = scale * qv * XQ + b * kv * XE - kv * XY;
           dbe[e] += kv * XE;
+          ob[e] = kv * XE;
           lamw += kv * SF[e] * tail[e];
         }
       }
@@ -519,6 +584,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
       mm16(tq, to_frag<T>(f32x4{oq[0], oq[1], oq[2], oq[3]}), idt);
       mm16(tk, to_frag<T>(f32x4{ok_[0], ok_[1], ok_[2], ok_[3]}), idt);
       const FR yq = to_frag<T>(tq), yk = to_frag<T>(tk);
+      FR yb = to_frag<T>(zero4());
+      if constexpr (EW) {
+        f32x4 tbb = zero4();
+        mm16(tbb, to_frag<T>(f32x4{ob[0], ob[1], ob[2], ob[3]}), idt);
+        yb = to_frag<T>(tbb);
+      }
       const bool odd = fb & 1;
       const int64_t tb = (int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4;
       const uint32_t o1 = odd ? (uint32_t)((tb - SUB) * (int64_t)sizeof(T)) : OOB;
@@ -528,14 +599,23 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
         gst8(bdq, o2, __builtin_bit_cast(uint2, yq));
         gst8(bdk, o1, __builtin_bit_cast(uint2, pdk));
         gst8(bdk, o2, __builtin_bit_cast(uint2, yk));
+        if constexpr (EW) {
+          gst8(bdb, o1, __builtin_bit_cast(uint2, pdb));
+          gst8(bdb, o2, __builtin_bit_cast(uint2, yb));
+        }
       } else {
         gst16(bdq, o1, __builtin_bit_cast(uint4, pdq));
         gst16(bdq, o2, __builtin_bit_cast(uint4, yq));
         gst16(bdk, o1, __builtin_bit_cast(uint4, pdk));
         gst16(bdk, o2, __builtin_bit_cast(uint4, yk));
+        if constexpr (EW) {
+          gst16(bdb, o1, __builtin_bit_cast(uint4, pdb));
+          gst16(bdb, o2, __builtin_bit_cast(uint4, yb));
+        }
       }
       pdq = yq;
       pdk = yk;
+      pdb = yb;
     }
     if constexpr (GATE == 2) {
       // in-block reverse sum: own rows, then the lane groups after this one
@@ -595,8 +675,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   }
 
   // ---- dbeta = write part + erase part (rows of block I) ---------------------
+  // (the erase/write form wrote db and dw element by element instead)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
+    if constexpr (EW) break;
     float x = dbe[e];
     x += __shfl_xor(x, 1);
     x += __shfl_xor(x, 2);
@@ -641,18 +723,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(Args a) {
   }
 }
 
-template <typename T, int GATE>
+template <typename T, int GX>
 static hipError_t bwd_chunk_g(const Args& a, hipStream_t s) {
   const dim3 grid(a.nc_max * a.H), block(256);
-  REWY_KV_SWITCH_X(k_bwd_chunk, GATE)
+  REWY_KV_SWITCH_X(k_bwd_chunk, GX)
 }
 
 template <typename T>
 static hipError_t bwd_chunk_t(const Args& a, hipStream_t s) {
   switch (a.gate) {
-    case 0: return bwd_chunk_g<T, 0>(a, s);
-    case 1: return bwd_chunk_g<T, 1>(a, s);
-    case 2: return bwd_chunk_g<T, 2>(a, s);
+    case 0: return a.ew ? bwd_chunk_g<T, 4>(a, s) : bwd_chunk_g<T, 0>(a, s);
+    case 1: return a.ew ? bwd_chunk_g<T, 5>(a, s) : bwd_chunk_g<T, 1>(a, s);
+    case 2: return a.ew ? bwd_chunk_g<T, 6>(a, s) : bwd_chunk_g<T, 2>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

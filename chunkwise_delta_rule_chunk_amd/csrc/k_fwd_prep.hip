@@ -70,7 +70,10 @@ hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
 // MODE: the PREP_* sets this launch writes (a compile-time constant, so the
 // loop body holds no flag tests and no pointers of unused outputs).
 template <typename T, int K, int V, int MODE>
-__global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
+__global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args a) {
+  // the erase/write form runs one workgroup per CU: the erase gate of the
+  // thread's rows and the write gate's v pieces need registers
+  constexpr bool EW = MODE & PREP_EW;
   constexpr int NTH = 256, NW = NTH / 64;
   constexpr bool BF = std::is_same_v<T, bf16>;
   constexpr int PK = pitch<T>(K);   // T rows of K
@@ -122,6 +125,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
   uint4 pv2[2 * VPT];
   uint4 etr[NSL][RS / VE];  // E^T of this thread's rows, from the elementwise phase to S5
   uint32_t pbeta = 0u;      // raw bits of the next item's beta for row tid
+  // erase/write form: raw bits of the next item's erase gate at this thread's
+  // rows and columns, and the write gate in the layout of the staged v
+  uint32_t bwr[EW ? NSL : 1][EW ? RS : 1];
+  uint4 pw2[EW && BF ? 2 * VPT : 1];
+  Staged<T, CH, V, NTH> pw;
   // the fetches take the item's chunk record, read one item ahead (its
   // scalar load completes during the previous item instead of stalling here)
   auto fetch_kq = [&](int item, const ChunkInfo& ci, int tid) {
@@ -130,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
     const int64_t t0 = ci.bos;
     pk.load(gbuf(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
     pq.load(gbuf(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
-    pbeta = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, ci.len - 1)) * H + h);
+    if constexpr (!EW) pbeta = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, ci.len - 1)) * H + h);
   };
   auto fetch_v = [&](int item, const ChunkInfo& ci, int tid) {
     const int h = item % H;
@@ -144,9 +152,15 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
         const bool ok = sl < VSL;
         pv2[2 * j] = gld16(bv, ok ? (uint32_t)(((int64_t)(2 * p) * gsV + c0) * 2) : OOB);
         pv2[2 * j + 1] = gld16(bv, ok ? (uint32_t)(((int64_t)(2 * p + 1) * gsV + c0) * 2) : OOB);
+        if constexpr (EW) {
+          const GBuf bw = gbuf(reinterpret_cast<const T*>(a.wg) + (t0 * H + h) * V, tile_bytes<T>(ci.len, gsV, V));
+          pw2[2 * j] = gld16(bw, ok ? (uint32_t)(((int64_t)(2 * p) * gsV + c0) * 2) : OOB);
+          pw2[2 * j + 1] = gld16(bw, ok ? (uint32_t)(((int64_t)(2 * p + 1) * gsV + c0) * 2) : OOB);
+        }
       }
     } else {
       pv.load(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, gsV, ci.len, tid);
+      if constexpr (EW) pw.load(reinterpret_cast<const T*>(a.wg) + (t0 * H + h) * V, gsV, ci.len, tid);
     }
   };
   auto fetch_g = [&](int item, const ChunkInfo& ci) {
@@ -154,6 +168,18 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
     if (ci.len == 0) return;
 #pragma unroll
     for (int s = 0; s < NSL; ++s) gc[s].load(a, (int64_t)ci.bos, h, ci.len, K, 0);
+    if constexpr (EW) {  // erase gate rows past the end read as zero
+      const GBuf bb = gbuf(reinterpret_cast<const T*>(a.beta) + ((int64_t)ci.bos * H + h) * K,
+                           tile_bytes<T>(ci.len, gsK, K));
+#pragma unroll
+      for (int s = 0; s < NSL; ++s)
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+          const uint32_t off = (uint32_t)((((int64_t)gc[s].seg * RS + r) * gsK + gc[s].c) * (int64_t)sizeof(T));
+          if constexpr (sizeof(T) == 2) bwr[s][r] = gld2(bb, off);
+          else bwr[s][r] = gld4(bb, off);
+        }
+    }
   };
 
   ChunkInfo cnext = load_chunk(a.chunks, min((int)blockIdx.x, total - 1) / H);
@@ -267,7 +293,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
           const float G = g.G[r];
           const float kr = tof(kraw), qr = tof(qraw);
           const float ea = fexp2(G - rA), eb = fexp2(rB - G);
-          const float vKa = sBeta[row] * kr * ea, vQa = bs * qr * ea, vKc = kr * eb;
+          float bk = 0.f;  // erase factor of this row (and feature)
+          if constexpr (EW) bk = sizeof(T) == 2 ? __uint_as_float(bwr[s][r] << 16) : __uint_as_float(bwr[s][r]);
+          else bk = sBeta[row];
+          const float vKa = bk * kr * ea, vQa = bs * qr * ea, vKc = kr * eb;
           const float vE = vKa * cA, vQg = vQa * cA, vF = vKc * cB;
           if constexpr (MODE & PREP_FWD_OUT) Qgd[r * GPQ * 4] = fromf<T>(vQg);
           if constexpr (MODE & PREP_BWD_SCAN) Fd[r * VE] = fromf<T>(vF);
@@ -336,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
       for (int J = w; J < NSUB; J += NW)
         if (J * SUB < n && sFlag[J]) {
           f32x4 accL, accC;
-          pairwise_diag<T, K, true>(a, t0, h, n, J, sBeta, accL, accC);
+          pairwise_diag<T, K, true, EW>(a, t0, h, n, J, sBeta, accL, accC);
           store(J, J, accL, accC);
         }
       // tiles nobody computed: zeros (the upper triangle and rows past the end)
@@ -415,15 +444,23 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
         } v0, v1;
         v0.u = pv2[2 * j];
         v1.u = pv2[2 * j + 1];
-        const float b0 = sBeta[2 * p], b1 = sBeta[2 * p + 1];
+        union {
+          uint4 u;
+          T e[8];
+        } w0, w1;  // write gate (erase/write form)
+        if constexpr (EW) {
+          w0.u = pw2[2 * j];
+          w1.u = pw2[2 * j + 1];
+        }
+        const float b0 = EW ? 0.f : sBeta[2 * p], b1 = EW ? 0.f : sBeta[2 * p + 1];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           union {
             uint32_t u;
             T hh[2];
           } z;
-          z.hh[0] = fromf<T>(b0 * tof(v0.e[e]));
-          z.hh[1] = fromf<T>(b1 * tof(v1.e[e]));
+          z.hh[0] = fromf<T>((EW ? tof(w0.e[e]) : b0) * tof(v0.e[e]));
+          z.hh[1] = fromf<T>((EW ? tof(w1.e[e]) : b1) * tof(v1.e[e]));
           *reinterpret_cast<uint32_t*>(sZt + (c0 + e) * PA + 2 * p) = z.u;
         }
       }
@@ -439,9 +476,15 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
             T e[VEC];
           } val;
           val.u = pv.r[j];
-          const float b = sBeta[r];
+          union {
+            uint4 u;
+            T e[VEC];
+          } wv;
+          if constexpr (EW) wv.u = pw.r[j];
+          const float b = EW ? 0.f : sBeta[r];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) sZt[(c0 + e) * PA + r] = fromf<T>(b * tof(val.e[e]));
+          for (int e = 0; e < VEC; ++e)
+            sZt[(c0 + e) * PA + r] = fromf<T>((EW ? tof(wv.e[e]) : b) * tof(val.e[e]));
         }
       }
     }
@@ -505,21 +548,26 @@ __global__ __launch_bounds__(256, 2) void k_fwd_prep(Args a) {
 template <typename T, int MODE>
 static hipError_t prep_m(const Args& a, hipStream_t s) {
   const int items = a.nc_max * a.H;
-  const dim3 grid(std::min(items, 2 * persistent_grid()), 1), block(256);
+  const dim3 grid(std::min(items, ((MODE & PREP_EW) ? 1 : 2) * persistent_grid()), 1), block(256);
   REWY_KV_SWITCH_X(k_fwd_prep, MODE)
 }
 
 // The three output sets in use: the forward (recompute policy), the forward
-// that also saves the backward's operands, and the recomputation in the backward.
+// that also saves the backward's operands, and the recomputation in the
+// backward; each with a shared beta or in the erase/write form.
 template <typename T>
 static hipError_t prep_t(const Args& a, hipStream_t s) {
   constexpr int FWD = PREP_FWD_SCAN | PREP_FWD_OUT;
   constexpr int ALL = FWD | PREP_BWD_SCAN | PREP_BWD_CHUNK;
   constexpr int BWD = PREP_FWD_SCAN | PREP_BWD_SCAN | PREP_BWD_CHUNK;
-  switch (a.prep_mode) {
+  constexpr int E = PREP_EW;
+  switch (a.prep_mode | (a.ew ? E : 0)) {
     case FWD: return prep_m<T, FWD>(a, s);
     case ALL: return prep_m<T, ALL>(a, s);
     case BWD: return prep_m<T, BWD>(a, s);
+    case FWD | E: return prep_m<T, FWD | E>(a, s);
+    case ALL | E: return prep_m<T, ALL | E>(a, s);
+    case BWD | E: return prep_m<T, BWD | E>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

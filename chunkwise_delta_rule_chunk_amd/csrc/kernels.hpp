@@ -26,7 +26,9 @@ struct Args {
   const void* k;
   const void* v;
   const float* g;
-  const void* beta;
+  const void* beta;         // beta [BT,H]; in the erase/write form the erase gate b [BT,H,K]
+  const void* wg;           // erase/write form: the write gate w [BT,H,V], else nullptr
+  int ew;                   // 1 for the erase/write form
   const float* h0;
   const void* dO;
   const float* dht;
@@ -37,7 +39,8 @@ struct Args {
   void* dk;
   void* dv;
   float* dg;
-  void* dbeta;
+  void* dbeta;              // dbeta [BT,H]; in the erase/write form db [BT,H,K]
+  void* dw;                 // erase/write form: dw [BT,H,V]
   float* dh0;
   // Forward intermediates.  Token-major tensors are [BT,H,*]; chunk tiles are
   // [nc_max,H,rows,64] with all 64 token columns written (zeros past the
@@ -88,6 +91,9 @@ constexpr int PREP_FWD_SCAN = 1;  // W, Ft, U, glast
 constexpr int PREP_FWD_OUT = 2;   // Qg, Cq
 constexpr int PREP_BWD_SCAN = 4;  // F, Wt, Qgt, Cqt, glast
 constexpr int PREP_BWD_CHUNK = 8; // At, G2t, Gst
+// The erase/write form: beta holds the erase gate b [.., K] and wg the write
+// gate w [.., V] (both in the feature dtype); E = b gamma K and Z = w V.
+constexpr int PREP_EW = 16;
 
 // Launchers: enqueue on `stream`; return the hipError_t of the launch.
 hipError_t launch_chunk_table(const Args& a, hipStream_t s);

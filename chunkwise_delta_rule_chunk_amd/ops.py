@@ -118,9 +118,33 @@ def recurrent_forward(q, k, v, g, beta, *, scale=None, h0=None, cu_seqlens=None,
     return o, ht
 
 
+def forward_gdn2(q, k, v, g, b, w, *, scale=None, h0=None, cu_seqlens=None, policy="recompute",
+                 output_final_state=True, stream=None, ws=None):
+    """Run rewy_fwd_gdn2: independent erase gate b [B,T,H,K] and write gate w
+    [B,T,H,V] (feature dtype).  Returns (o, ht or None, ctx) for ``backward``."""
+    prob = make_problem(q, v, g, b, scale=scale, cu_seqlens=cu_seqlens, policy=policy)
+    o = torch.empty_like(v)
+    ht = torch.empty(prob.state_shape, dtype=torch.float32, device=q.device) \
+        if output_final_state else None
+    saved = None
+    if policy == "save":
+        saved = torch.empty(B.rewy_saved_bytes(prob.desc), dtype=torch.uint8, device=q.device)
+    if ws is None:
+        ws = workspace(prob, 0)
+    rc = B.rewy_fwd_gdn2(prob.desc, _p(q), _p(k), _p(v), _p(g), _p(b), _p(w), _p(h0), _p(o),
+                         _p(ht), _p(saved), _p(ws), ws.numel(), _stream(q.device, stream))
+    _check(rc, "rewy_fwd_gdn2")
+    ctx = dict(prob=prob, q=q, k=k, v=v, g=g, beta=b, w=w, h0=h0, saved=saved)
+    return o, ht, ctx
+
+
 def backward(ctx, dO, dht=None, *, stream=None, ws=None, want_dh0=None):
-    """Run rewy_bwd.  Returns dict dq, dk, dv, dg, dbeta, dh0."""
+    """Run rewy_bwd (or rewy_bwd_gdn2 for a ``forward_gdn2`` context).  Returns
+    dict dq, dk, dv, dg, dbeta, dh0 (and, for the erase/write form, db and dw
+    in place of dbeta)."""
     prob = ctx["prob"]
+    if ctx.get("w") is not None:
+        return _backward_gdn2(ctx, dO, dht, stream=stream, ws=ws, want_dh0=want_dh0)
     q, k, v, g, beta, h0 = (ctx[x] for x in ("q", "k", "v", "g", "beta", "h0"))
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -137,6 +161,24 @@ def backward(ctx, dO, dht=None, *, stream=None, ws=None, want_dh0=None):
                     _p(ws), ws.numel(), _stream(q.device, stream))
     _check(rc, "rewy_bwd")
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0)
+
+
+def _backward_gdn2(ctx, dO, dht=None, *, stream=None, ws=None, want_dh0=None):
+    prob = ctx["prob"]
+    q, k, v, g, b, w, h0 = (ctx[x] for x in ("q", "k", "v", "g", "beta", "w", "h0"))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = None if g is None else torch.empty_like(g)
+    db, dw = torch.empty_like(k), torch.empty_like(v)
+    if want_dh0 is None:
+        want_dh0 = h0 is not None
+    dh0 = torch.empty(prob.state_shape, dtype=torch.float32, device=q.device) if want_dh0 else None
+    if ws is None:
+        ws = workspace(prob, 1)
+    rc = B.rewy_bwd_gdn2(prob.desc, _p(q), _p(k), _p(v), _p(g), _p(b), _p(w), _p(h0), _p(dO),
+                         _p(dht), _p(ctx["saved"]), _p(dq), _p(dk), _p(dv), _p(dg), _p(db),
+                         _p(dw), _p(dh0), _p(ws), ws.numel(), _stream(q.device, stream))
+    _check(rc, "rewy_bwd_gdn2")
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, db=db, dw=dw, dh0=dh0)
 
 
 class ChunkDeltaRule(torch.autograd.Function):

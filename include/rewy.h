@@ -109,6 +109,25 @@ int rewy_bwd(const rewy_desc *d, const void *q, const void *k, const void *v,
              void *dq, void *dk, void *dv, float *dg, void *dbeta, float *dh0,
              void *workspace, size_t ws_bytes, void *stream);
 
+/* The erase/write form (ReWY paper Table 1, GDN2 row; GDN2 spec section 2):
+ * independent erase and write vector gates in place of the shared beta,
+ *     r_t = w_t * v_t - S~^T (b_t * k_t),   S = S~ + k_t r_t^T,
+ * so that E = b gamma K and Z = w V in the chunk form.  b is [B,T,H,K] and w
+ * [B,T,H,V], both in the feature dtype (beta_dtype must equal dtype, else
+ * REWY_EUNSUPPORTED); with b = w = beta the result is rewy_fwd's.  Everything
+ * else (descriptor, workspace and saved sizes, ownership, errors) is as for
+ * rewy_fwd / rewy_bwd; the backward returns db [B,T,H,K] and dw [B,T,H,V] in
+ * the feature dtype, element by element, in place of dbeta. */
+int rewy_fwd_gdn2(const rewy_desc *d, const void *q, const void *k, const void *v,
+                  const float *g, const void *b, const void *w, const float *h0,
+                  void *o, float *ht, void *saved,
+                  void *workspace, size_t ws_bytes, void *stream);
+int rewy_bwd_gdn2(const rewy_desc *d, const void *q, const void *k, const void *v,
+                  const float *g, const void *b, const void *w, const float *h0,
+                  const void *dO, const float *dht, const void *saved,
+                  void *dq, void *dk, void *dv, float *dg, void *db, void *dw, float *dh0,
+                  void *workspace, size_t ws_bytes, void *stream);
+
 /* Token-serial forward for decoding (the pages' fused recurrent form of the
  * same recurrence: ReWY paper, Background / Delta-rule operators; KDA blog
  * section 4): o_t = S_t^T (s q_t) with the state updated one token at a time,

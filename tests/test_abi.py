@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "rewy.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(rewy_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(rewy_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     for name in decl:
         assert hasattr(lib, name), name
     out = os.popen(f"nm -D --defined-only {B.LIB_PATH}").read()
-    exported = sorted(set(re.findall(r"\bT (rewy_[a-z_]+)\b", out)))
+    exported = sorted(set(re.findall(r"\bT (rewy_[a-z0-9_]+)\b", out)))
     assert exported == decl  # nothing else of ours is exported
 
 
