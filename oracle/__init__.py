@@ -145,6 +145,26 @@ def forward(q, k, v, g, beta, *, scale, h0=None, cu_seqlens=None, erase=None, wr
     return o.reshape(p.B, p.T, p.H, p.V), ht
 
 
+def kda_gate(x, a_log, dt_bias):
+    """Channel-wise log-decay from its pre-activation (GDN2 spec section 4.4,
+    the layer's gate; computed inside the kernels in section 2.1 and section 3):
+        g = -exp(A_log[h]) * softplus(x + dt_bias[h, k])
+    x [B,T,H,K], A_log [H], dt_bias [H,K]; FP64, natural log."""
+    z = _f64(x) + _f64(dt_bias)[None, None]
+    return -np.exp(_f64(a_log))[None, None, :, None] * np.logaddexp(0.0, z)
+
+
+def kda_gate_backward(x, a_log, dt_bias, dg):
+    """Reverse mode of ``kda_gate`` for a given dg: returns (dx, dA_log,
+    ddt_bias).  d softplus(z)/dz = sigmoid(z); dg/dA_log = g."""
+    z = _f64(x) + _f64(dt_bias)[None, None]
+    ea = np.exp(_f64(a_log))[None, None, :, None]
+    dg = _f64(dg)
+    dx = -ea * dg / (1.0 + np.exp(-z))
+    g = -ea * np.logaddexp(0.0, z)
+    return dx, (dg * g).sum(axis=(0, 1, 3)), dx.sum(axis=(0, 1))
+
+
 def backward(q, k, v, g, beta, dO, *, scale, h0=None, dht=None, cu_seqlens=None, erase=None,
              write=None, threads=None):
     """Exact reverse mode of ``forward`` for l = <dO, o> + <dht, ht>.

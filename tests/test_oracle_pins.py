@@ -395,3 +395,30 @@ def test_flop_closed_form_matches_paper():
     assert round(rw / 1e6, 2) == fx["rewy_millions_printed"]
     assert round(100 * (ex - rw) / ex, 1) == fx["removed_percent_printed"]
     assert ex - rw == 4 * n * n * dk + 4 * n ** 3
+
+
+def test_kda_gate_formula_and_reverse_mode():
+    """GDN2 spec section 4.4: g = -exp(A_log) softplus(x + dt_bias).  At
+    x = -dt_bias softplus is ln 2; far on the positive side it is the identity;
+    the reverse mode (dx, dA_log, ddt_bias) matches central differences."""
+    rng = np.random.default_rng(3)
+    B, T, H, K = 2, 5, 3, 4
+    x = rng.normal(size=(B, T, H, K))
+    a = rng.uniform(-2.0, 0.0, H)
+    d = rng.normal(size=(H, K)) * 0.5
+    at_zero = oracle.kda_gate(np.broadcast_to(-d, (B, T, H, K)), a, d)
+    assert np.allclose(at_zero, -np.exp(a)[None, None, :, None] * np.log(2.0), rtol=1e-14, atol=0)
+    far = oracle.kda_gate(np.broadcast_to(40.0 - d, (B, T, H, K)), a, d)
+    assert np.allclose(far, -np.exp(a)[None, None, :, None] * 40.0, rtol=1e-12, atol=0)
+    R = rng.normal(size=(B, T, H, K))
+    dx, da, dd = oracle.kda_gate_backward(x, a, d, R)
+    loss = lambda xx, aa, db: float((R * oracle.kda_gate(xx, aa, db)).sum())
+    eps = 1e-6
+    for grad, arg in ((dx, 0), (da, 1), (dd, 2)):
+        base = [x, a, d]
+        u = rng.normal(size=base[arg].shape)
+        plus, minus = list(base), list(base)
+        plus[arg] = base[arg] + eps * u
+        minus[arg] = base[arg] - eps * u
+        fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+        assert abs(fd - float((grad * u).sum())) <= 1e-7 * max(1.0, abs(fd)), (arg, fd)

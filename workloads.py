@@ -54,6 +54,11 @@ class Inputs:
     cu_seqlens: Optional[torch.Tensor]  # int32, host
     scale: float
     gate: str  # "none" | "scalar" | "vector"
+    # vector gate: the pre-activation x [B,T,H,K] (fp32 draw), A_log [H] and
+    # dt_bias [H,K] that g was formed from (g = -exp(A_log) softplus(x + dt_bias))
+    gate_x: Optional[torch.Tensor] = None
+    a_log: Optional[torch.Tensor] = None
+    dt_bias: Optional[torch.Tensor] = None
 
     @property
     def shape(self):
@@ -68,7 +73,8 @@ class Inputs:
         f = lambda x: None if x is None else x.to(device)
         return dataclasses.replace(self, q=f(self.q), k=f(self.k), v=f(self.v), g=f(self.g),
                                    beta=f(self.beta), h0=f(self.h0), dO=f(self.dO),
-                                   dht=f(self.dht))
+                                   dht=f(self.dht), gate_x=f(self.gate_x), a_log=f(self.a_log),
+                                   dt_bias=f(self.dt_bias))
 
 
 def _dt(name):
@@ -114,11 +120,13 @@ def make_inputs(B, T, H, K, V, *, gate="vector", dtype="bf16", seed=0, h0="zero"
     v = rn(B, T, H, V).to(dt)
     shift = (1.0 if strong else 0.0) if beta_shift is None else beta_shift
     beta = torch.sigmoid(rn(B, T, H) + shift).to(dt)
+    gx = a_log = dt_bias = None
     if gate == "vector":
         a_log = ru(0.0, 1.0, H) if strong else ru(-2.0, 0.0, H)
         x = rn(B, T, H, K)
         dt_bias = rn(H, K) * 0.5
         g = -torch.exp(a_log)[:, None] * torch.nn.functional.softplus(x + dt_bias)
+        gx = x
     elif gate == "scalar":
         n = rn(B, T, H)
         u = ru(-3.0, 0.0, B, T, H)
@@ -138,7 +146,8 @@ def make_inputs(B, T, H, K, V, *, gate="vector", dtype="bf16", seed=0, h0="zero"
     dO = rn(B, T, H, V).to(dt)
     dht_t = rn(N, H, K, V) * 0.1 if dht else None
     cu = None if cu_seqlens is None else torch.tensor(cu_seqlens, dtype=torch.int32)
-    return Inputs(name, q, k, v, g, beta, h0_t, dO, dht_t, cu, float(K) ** -0.5, gate)
+    return Inputs(name, q, k, v, g, beta, h0_t, dO, dht_t, cu, float(K) ** -0.5, gate,
+                  gx, a_log, dt_bias)
 
 
 def workload(name, device="cpu"):
