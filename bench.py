@@ -168,6 +168,42 @@ def _time_gdn2(result, x, inp, B, T, args, ops, torch):
     print(f"[bench] erase/write form: {ms2:.3f} ms/step", file=sys.stderr, flush=True)
 
 
+def _time_kda_gate(result, x, inp, B, T, args, ops, binding, torch):
+    """The same step with the vector gate formed inside the kernels from its
+    pre-activation (g = -exp(A_log) softplus(x + dt_bias)); x in the feature
+    dtype, dx, dA_log and ddt_bias returned in place of dg."""
+    if inp.gate_x is None:
+        return
+    dev = x.q.device
+    gx = inp.gate_x.to(inp.q.dtype).to(dev)
+    al, db = inp.a_log.to(dev).contiguous(), inp.dt_bias.to(dev).contiguous()
+
+    def step3():
+        o, ht, ctx = ops.forward_kda_gate(x.q, x.k, x.v, gx, al, db, x.beta, scale=inp.scale,
+                                          h0=x.h0, cu_seqlens=inp.cu_seqlens, policy=args.policy)
+        return ops.backward(ctx, x.dO, x.dht)
+
+    for _ in range(max(3, args.warmup // 4)):
+        step3()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step3()
+    torch.cuda.synchronize()
+    ms3 = (time.perf_counter() - t2) * 1e3 / args.steps
+    binding.rewy_trace_begin()  # per-kernel durations from a separate, untimed pass
+    for _ in range(args.steps):
+        step3()
+    tr = binding.rewy_trace_end()
+    torch.cuda.synchronize()
+    result["kda_gate_in_kernel"] = {
+        "form": "g = -exp(A_log) softplus(x + dt_bias) formed in the kernels; dx, dA_log, ddt_bias out",
+        "policy": args.policy, "ms_per_step": ms3, "value": B * T / (ms3 * 1e-3), "unit": "tokens/s",
+        "kernels_ms": {name: {"avg_ms": tot / cnt, "launches_per_step": cnt / args.steps}
+                       for name, tot, cnt in tr}}
+    print(f"[bench] gate formed in the kernels: {ms3:.3f} ms/step", file=sys.stderr, flush=True)
+
+
 def _time_other(result, other, prob2, x, inp, B, T, args, ops, torch):
     """Time K steps under the other saving policy and record them in result."""
     w20, w21 = ops.workspace(prob2, 0), ops.workspace(prob2, 1)
@@ -206,6 +242,8 @@ def main():
                     help="skip timing the other saving policy (profiler runs)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip timing the token-serial forward at a decode shape")
+    ap.add_argument("--no-kda-gate", action="store_true",
+                    help="skip timing the step with the gate formed in the kernels")
     ap.add_argument("--no-gdn2", action="store_true",
                     help="skip timing the erase/write form")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -354,6 +392,8 @@ def main():
         _time_decode(result, args, ops, binding, torch)
     if not args.no_gdn2:
         _time_gdn2(result, x, inp, B, T, args, ops, torch)
+    if not args.no_kda_gate:
+        _time_kda_gate(result, x, inp, B, T, args, ops, binding, torch)
 
     if not args.no_cpu_baseline:
         import oracle

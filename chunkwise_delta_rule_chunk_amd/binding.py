@@ -18,7 +18,7 @@ REWY_BF16, REWY_F32 = 0, 1
 REWY_RECOMPUTE, REWY_SAVE = 0, 1
 
 EXPORTS = ("rewy_workspace_bytes", "rewy_saved_bytes", "rewy_fwd", "rewy_bwd", "rewy_fwd_gdn2",
-           "rewy_bwd_gdn2", "rewy_recurrent_fwd",
+           "rewy_bwd_gdn2", "rewy_fwd_kda_gate", "rewy_bwd_kda_gate", "rewy_recurrent_fwd",
            "rewy_trace_begin", "rewy_trace_end", "rewy_trace_select", "rewy_status_string",
            "rewy_last_error")
 
@@ -71,6 +71,10 @@ def load():
         lib.rewy_fwd_gdn2.restype = ctypes.c_int
         lib.rewy_bwd_gdn2.argtypes = [D] + [P] * 18 + [S, P]
         lib.rewy_bwd_gdn2.restype = ctypes.c_int
+        lib.rewy_fwd_kda_gate.argtypes = [D] + [P] * 12 + [S, P]
+        lib.rewy_fwd_kda_gate.restype = ctypes.c_int
+        lib.rewy_bwd_kda_gate.argtypes = [D] + [P] * 20 + [S, P]
+        lib.rewy_bwd_kda_gate.restype = ctypes.c_int
         lib.rewy_recurrent_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P]
         lib.rewy_recurrent_fwd.restype = ctypes.c_int
         lib.rewy_trace_begin.argtypes = []
@@ -115,6 +119,19 @@ def rewy_bwd_gdn2(desc, q, k, v, g, b, w, h0, dO, dht, saved, dq, dk, dv, dg, db
                   workspace, ws_bytes, stream) -> int:
     return load().rewy_bwd_gdn2(ctypes.byref(desc), q, k, v, g, b, w, h0, dO, dht, saved, dq, dk,
                                 dv, dg, db, dw, dh0, workspace, ws_bytes, stream)
+
+
+def rewy_fwd_kda_gate(desc, q, k, v, x, a_log, dt_bias, beta, h0, o, ht, saved, workspace, ws_bytes,
+                      stream) -> int:
+    return load().rewy_fwd_kda_gate(ctypes.byref(desc), q, k, v, x, a_log, dt_bias, beta, h0, o, ht,
+                                    saved, workspace, ws_bytes, stream)
+
+
+def rewy_bwd_kda_gate(desc, q, k, v, x, a_log, dt_bias, beta, h0, dO, dht, saved, dq, dk, dv, dx,
+                      da_log, ddt_bias, dbeta, dh0, workspace, ws_bytes, stream) -> int:
+    return load().rewy_bwd_kda_gate(ctypes.byref(desc), q, k, v, x, a_log, dt_bias, beta, h0, dO,
+                                    dht, saved, dq, dk, dv, dx, da_log, ddt_bias, dbeta, dh0,
+                                    workspace, ws_bytes, stream)
 
 
 def rewy_recurrent_fwd(desc, q, k, v, g, beta, h0, o, ht, stream) -> int:

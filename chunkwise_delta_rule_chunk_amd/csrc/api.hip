@@ -95,6 +95,8 @@ int make_plan(const rewy_desc* d, Plan& p) {
 //   recompute: ws = [index | glast hbuf R | W Ft U | (fwd) Qg Cq / (bwd) reverse set | Rbt dhbuf]
 //   save-all:  saved = [glast hbuf R | reverse set]
 //              ws (fwd) = [index | W Ft U Qg Cq],  ws (bwd) = [index | Rbt dhbuf]
+// The backward with the gate formed in the kernel appends the per-wave partial
+// sums of the gate parameters' gradients to its workspace (phase 2).
 struct Layout {
   size_t chunks, seqoff;
   size_t glast, hbuf, R;             // read by output and backward
@@ -103,7 +105,8 @@ struct Layout {
   size_t F, Wt, Qgt, Cqt;            // reverse scan operands
   size_t At, G2t, Gst;               // chunk backward operands
   size_t Rbt, dhbuf;                 // written by the reverse scan
-  size_t ws_fwd, ws_bwd, saved;
+  size_t gpart;                      // gate in the kernel: [nc,H,NSUB,K] then [nc,H,NSUB] fp32
+  size_t ws_fwd, ws_bwd, ws_gin, saved;
 };
 
 Layout layout(const Plan& p) {
@@ -155,6 +158,8 @@ Layout layout(const Plan& p) {
   L.Rbt = take(off, tileV);
   L.dhbuf = take(off, nc * H * K * V * e);
   L.ws_bwd = off;
+  L.gpart = take(off, nc * H * NSUB * (K + 1) * 4);
+  L.ws_gin = off;
   return L;
 }
 
@@ -266,7 +271,15 @@ REWY_API size_t rewy_workspace_bytes(const rewy_desc* d, int phase) {
   Plan p;
   if (make_plan(d, p) != REWY_OK) return 0;
   const Layout L = layout(p);
-  return phase == 0 ? L.ws_fwd : L.ws_bwd;
+  if (phase == 2 && p.gate != REWY_GATE_VECTOR) {
+    fail(REWY_EINVAL, "phase 2 (the gate formed in the kernel) needs gate == VECTOR");
+    return 0;
+  }
+  if (phase < 0 || phase > 2) {
+    fail(REWY_EINVAL, "bad phase %d", phase);
+    return 0;
+  }
+  return phase == 0 ? L.ws_fwd : phase == 1 ? L.ws_bwd : L.ws_gin;
 }
 
 REWY_API size_t rewy_saved_bytes(const rewy_desc* d) {
@@ -277,12 +290,29 @@ REWY_API size_t rewy_saved_bytes(const rewy_desc* d) {
 
 namespace rewy {
 namespace {
-// The forward of both forms: beta [BT,H] (shared erase/write factor), or
+// The gate formed in the kernel: pre-activation x [BT,H,K] (feature dtype),
+// A_log [H] and dt_bias [H,K] (fp32).
+struct GateIn {
+  const void* x;
+  const float* a_log;
+  const float* dt_bias;
+};
+
+int check_gate_in(const Plan& p, const GateIn* gi) {
+  if (p.gate != REWY_GATE_VECTOR) return fail(REWY_EINVAL, "the gate formed in the kernel needs gate == VECTOR");
+  if (!gi->x || !gi->a_log || !gi->dt_bias) return fail(REWY_EINVAL, "x, A_log and dt_bias must be given");
+  if (!aligned(gi->x, 16) || !aligned(gi->dt_bias, 16) || !aligned(gi->a_log, 4))
+    return fail(REWY_EINVAL, "x and dt_bias must be 16-byte aligned, A_log 4-byte aligned");
+  return REWY_OK;
+}
+
+// The forward of every form: beta [BT,H] (shared erase/write factor), or
 // with wg non-null the erase gate b [BT,H,K] in `beta` and the write gate w
-// [BT,H,V] in `wg`, both in the feature dtype.
+// [BT,H,V] in `wg`, both in the feature dtype; with gi non-null the vector
+// gate is formed in the kernel from gi (and g is not given).
 int forward_impl(const rewy_desc* d, const void* q, const void* k, const void* v, const float* g,
-                 const void* beta, const void* wg, const float* h0, void* o, float* ht, void* saved,
-                 void* workspace, size_t ws_bytes, void* stream) {
+                 const void* beta, const void* wg, const GateIn* gi, const float* h0, void* o,
+                 float* ht, void* saved, void* workspace, size_t ws_bytes, void* stream) {
   Plan p;
   int rc = make_plan(d, p);
   if (rc) return rc;
@@ -297,8 +327,11 @@ int forward_impl(const rewy_desc* d, const void* q, const void* k, const void* v
     const char* nm[] = {"q", "k", "v", "beta", "o"};
     if ((rc = check_tensor_ptrs(ps, nm, 5))) return rc;
   }
-  if ((p.gate != REWY_GATE_NONE) != (g != nullptr))
+  if (gi) {
+    if ((rc = check_gate_in(p, gi))) return rc;
+  } else if ((p.gate != REWY_GATE_NONE) != (g != nullptr)) {
     return fail(REWY_EINVAL, "g must be given exactly when gate != NONE");
+  }
   if (g && !aligned(g, 16)) return fail(REWY_EINVAL, "g is not 16-byte aligned");
   const Layout L = layout(p);
   if (!workspace || !aligned(workspace, ALIGN) || ws_bytes < L.ws_fwd)
@@ -311,6 +344,9 @@ int forward_impl(const rewy_desc* d, const void* q, const void* k, const void* v
   fill_common(a, p, d, static_cast<char*>(workspace), static_cast<char*>(saved), L);
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
   a.wg = wg; a.ew = ew;
+  if (gi) {
+    a.g = nullptr; a.gx = gi->x; a.a_log = gi->a_log; a.dt_bias = gi->dt_bias; a.gin = 1;
+  }
   if (ew && !aligned(wg, 16)) return fail(REWY_EINVAL, "w is not 16-byte aligned");
   a.prep_mode = PREP_FWD_SCAN | PREP_FWD_OUT |
                 (p.policy == REWY_SAVE ? PREP_BWD_SCAN | PREP_BWD_CHUNK : 0);
@@ -323,14 +359,24 @@ int forward_impl(const rewy_desc* d, const void* q, const void* k, const void* v
 REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const void* v,
                       const float* g, const void* beta, const float* h0, void* o, float* ht,
                       void* saved, void* workspace, size_t ws_bytes, void* stream) {
-  return forward_impl(d, q, k, v, g, beta, nullptr, h0, o, ht, saved, workspace, ws_bytes, stream);
+  return forward_impl(d, q, k, v, g, beta, nullptr, nullptr, h0, o, ht, saved, workspace, ws_bytes,
+                      stream);
+}
+
+REWY_API int rewy_fwd_kda_gate(const rewy_desc* d, const void* q, const void* k, const void* v,
+                               const void* x, const float* a_log, const float* dt_bias,
+                               const void* beta, const float* h0, void* o, float* ht, void* saved,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  const GateIn gi{x, a_log, dt_bias};
+  return forward_impl(d, q, k, v, nullptr, beta, nullptr, &gi, h0, o, ht, saved, workspace,
+                      ws_bytes, stream);
 }
 
 REWY_API int rewy_fwd_gdn2(const rewy_desc* d, const void* q, const void* k, const void* v,
                            const float* g, const void* b, const void* w, const float* h0, void* o,
                            float* ht, void* saved, void* workspace, size_t ws_bytes, void* stream) {
   if (!b || !w) return fail(REWY_EINVAL, "b and w must be given");
-  return forward_impl(d, q, k, v, g, b, w, h0, o, ht, saved, workspace, ws_bytes, stream);
+  return forward_impl(d, q, k, v, g, b, w, nullptr, h0, o, ht, saved, workspace, ws_bytes, stream);
 }
 
 REWY_API int rewy_recurrent_fwd(const rewy_desc* d, const void* q, const void* k, const void* v,
@@ -362,13 +408,22 @@ REWY_API int rewy_recurrent_fwd(const rewy_desc* d, const void* q, const void* k
 
 namespace rewy {
 namespace {
-// The backward of both forms; with wg non-null, `dbeta` receives db [BT,H,K]
-// and `dw` receives dw [BT,H,V] (feature dtype).
+// Gradients of the gate formed in the kernel: dx [BT,H,K] (feature dtype),
+// dA_log [H] and ddt_bias [H,K] (fp32, overwritten).
+struct GateInGrad {
+  void* dx;
+  float* da_log;
+  float* ddt_bias;
+};
+
+// The backward of every form; with wg non-null, `dbeta` receives db [BT,H,K]
+// and `dw` receives dw [BT,H,V] (feature dtype); with gi non-null the gate is
+// formed in the kernel and gg receives its gradients in place of dg.
 int backward_impl(const rewy_desc* d, const void* q, const void* k, const void* v, const float* g,
-                  const void* beta, const void* wg, const float* h0, const void* dO,
-                  const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
-                  void* dbeta, void* dw, float* dh0, void* workspace, size_t ws_bytes,
-                  void* stream) {
+                  const void* beta, const void* wg, const GateIn* gi, const float* h0,
+                  const void* dO, const float* dht, const void* saved, void* dq, void* dk, void* dv,
+                  float* dg, void* dbeta, void* dw, const GateInGrad* gg, float* dh0,
+                  void* workspace, size_t ws_bytes, void* stream) {
   Plan p;
   int rc = make_plan(d, p);
   if (rc) return rc;
@@ -386,15 +441,23 @@ int backward_impl(const rewy_desc* d, const void* q, const void* k, const void* 
     const char* nm[] = {"q", "k", "v", "beta", "dO", "dq", "dk", "dv", "dbeta"};
     if ((rc = check_tensor_ptrs(ps, nm, 9))) return rc;
   }
-  if ((p.gate != REWY_GATE_NONE) != (g != nullptr))
-    return fail(REWY_EINVAL, "g must be given exactly when gate != NONE");
-  if ((p.gate != REWY_GATE_NONE) != (dg != nullptr))
-    return fail(REWY_EINVAL, "dg must be given exactly when gate != NONE");
-  if ((g && !aligned(g, 16)) || (dg && !aligned(dg, 16)))
-    return fail(REWY_EINVAL, "g / dg must be 16-byte aligned");
+  if (gi) {
+    if ((rc = check_gate_in(p, gi))) return rc;
+    if (!gg->dx || !gg->da_log || !gg->ddt_bias)
+      return fail(REWY_EINVAL, "dx, dA_log and ddt_bias must be given");
+    if (!aligned(gg->dx, 16)) return fail(REWY_EINVAL, "dx is not 16-byte aligned");
+  } else {
+    if ((p.gate != REWY_GATE_NONE) != (g != nullptr))
+      return fail(REWY_EINVAL, "g must be given exactly when gate != NONE");
+    if ((p.gate != REWY_GATE_NONE) != (dg != nullptr))
+      return fail(REWY_EINVAL, "dg must be given exactly when gate != NONE");
+    if ((g && !aligned(g, 16)) || (dg && !aligned(dg, 16)))
+      return fail(REWY_EINVAL, "g / dg must be 16-byte aligned");
+  }
   const Layout L = layout(p);
-  if (!workspace || !aligned(workspace, ALIGN) || ws_bytes < L.ws_bwd)
-    return fail(REWY_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.ws_bwd,
+  const size_t need = gi ? L.ws_gin : L.ws_bwd;
+  if (!workspace || !aligned(workspace, ALIGN) || ws_bytes < need)
+    return fail(REWY_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                 ws_bytes);
   if (p.policy == REWY_SAVE && (!saved || !aligned(saved, ALIGN)))
     return fail(REWY_EWORKSPACE, "policy SAVE needs the saved buffer written by rewy_fwd");
@@ -406,6 +469,12 @@ int backward_impl(const rewy_desc* d, const void* q, const void* k, const void* 
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = dO; a.dht = dht;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
   a.wg = wg; a.ew = ew; a.dw = dw;
+  if (gi) {
+    a.g = nullptr; a.dg = nullptr;
+    a.gx = gi->x; a.a_log = gi->a_log; a.dt_bias = gi->dt_bias; a.gin = 1;
+    a.dgx = gg->dx; a.da_log = gg->da_log; a.ddt_bias = gg->ddt_bias;
+    a.gpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.gpart);
+  }
   const bool f32 = p.f32;
   const int vr = variant_of(a, f32);
   if (p.policy == REWY_RECOMPUTE) {
@@ -425,6 +494,9 @@ int backward_impl(const rewy_desc* d, const void* q, const void* k, const void* 
   if ((rc = hip_check(traced("k_bwd_chunk", vr, s, [&] { return launch_bwd_chunk(a, f32, s); }),
                       "chunk backward")))
     return rc;
+  if (gi && (rc = hip_check(traced("k_gate_reduce", -1, s, [&] { return launch_gate_reduce(a, s); }),
+                            "gate parameter gradients")))
+    return rc;
   return REWY_OK;
 }
 }  // namespace
@@ -435,8 +507,20 @@ REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const vo
                       const float* dht, const void* saved, void* dq, void* dk, void* dv,
                       float* dg, void* dbeta, float* dh0, void* workspace, size_t ws_bytes,
                       void* stream) {
-  return backward_impl(d, q, k, v, g, beta, nullptr, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
-                       nullptr, dh0, workspace, ws_bytes, stream);
+  return backward_impl(d, q, k, v, g, beta, nullptr, nullptr, h0, dO, dht, saved, dq, dk, dv, dg,
+                       dbeta, nullptr, nullptr, dh0, workspace, ws_bytes, stream);
+}
+
+REWY_API int rewy_bwd_kda_gate(const rewy_desc* d, const void* q, const void* k, const void* v,
+                               const void* x, const float* a_log, const float* dt_bias,
+                               const void* beta, const float* h0, const void* dO, const float* dht,
+                               const void* saved, void* dq, void* dk, void* dv, void* dx,
+                               float* da_log, float* ddt_bias, void* dbeta, float* dh0,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  const GateIn gi{x, a_log, dt_bias};
+  const GateInGrad gg{dx, da_log, ddt_bias};
+  return backward_impl(d, q, k, v, nullptr, beta, nullptr, &gi, h0, dO, dht, saved, dq, dk, dv,
+                       nullptr, dbeta, nullptr, &gg, dh0, workspace, ws_bytes, stream);
 }
 
 REWY_API int rewy_bwd_gdn2(const rewy_desc* d, const void* q, const void* k, const void* v,
@@ -445,8 +529,8 @@ REWY_API int rewy_bwd_gdn2(const rewy_desc* d, const void* q, const void* k, con
                            void* dv, float* dg, void* db, void* dw, float* dh0, void* workspace,
                            size_t ws_bytes, void* stream) {
   if (!b || !w) return fail(REWY_EINVAL, "b and w must be given");
-  return backward_impl(d, q, k, v, g, b, w, h0, dO, dht, saved, dq, dk, dv, dg, db, dw, dh0,
-                       workspace, ws_bytes, stream);
+  return backward_impl(d, q, k, v, g, b, w, nullptr, h0, dO, dht, saved, dq, dk, dv, dg, db, dw,
+                       nullptr, dh0, workspace, ws_bytes, stream);
 }
 
 REWY_API int rewy_trace_begin(void) {

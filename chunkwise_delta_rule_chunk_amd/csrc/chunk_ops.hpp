@@ -54,6 +54,30 @@ struct GateCols {
 #pragma unroll
     for (int r = 0; r < RS; ++r) G[r] = __uint_as_float(gld4(b, base + r * rb));
   }
+  // The gate formed in the kernel: the pre-activation x [.., K] (type X) of
+  // this thread's column (features [0, KC), KC = K) and rows, raw bits kept
+  // in G until kda_gate(); rows past the end read as zero.
+  template <typename X>
+  __device__ __forceinline__ void load_x(const Args& a, int64_t t0, int h, int n, int K) {
+    const int H = a.H, r0 = seg * RS;
+    const int64_t rs = (int64_t)H * K;
+    const GBuf b = gbuf(reinterpret_cast<const X*>(a.gx) + (t0 * H + h) * K, tile_bytes<X>(n, rs, KC));
+    const uint32_t rb = (uint32_t)(rs * (int64_t)sizeof(X)), base = (uint32_t)r0 * rb + c * (uint32_t)sizeof(X);
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+      G[r] = __uint_as_float(sizeof(X) == 2 ? gld2(b, base + r * rb) : gld4(b, base + r * rb));
+  }
+  // g = -ea softplus(x + dtb), ea = exp(A_log) of the head, dtb = dt_bias of
+  // this column (GDN2 spec section 4.4); rows past the end are masked later
+  template <typename X>
+  __device__ __forceinline__ void kda_gate(float ea, float dtb) {
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const uint32_t u = __float_as_uint(G[r]);
+      const float x = sizeof(X) == 2 ? __uint_as_float(u << 16) : __uint_as_float(u);
+      G[r] = -ea * softplus(x + dtb);
+    }
+  }
   // G2 = log2(e) * inclusive prefix over the chunk's n rows (rows past the end
   // add zero), in two halves around a barrier the caller places:
   // prefix_local() publishes the segment totals in sTot [NSUB][KC],
@@ -197,8 +221,9 @@ __device__ __forceinline__ void score_tiles_pre(const T* sKa, const T* sQa, cons
 // exceeds 1.  Reads q, k, g from global.  Lane l takes column j = l & 15 and
 // the feature quarter l >> 4; results come back in the C-fragment layout.
 // EW: the erase gate is a vector b (a.beta, [.., K], element type T), taken
-// inside the sum over features instead of beta_i outside it.
-template <typename T, int K, bool WITH_CQ, bool EW = false>
+// inside the sum over features instead of beta_i outside it.  GIN: the gate
+// is formed from its pre-activation, g = -exp(A_log) softplus(x + dt_bias).
+template <typename T, int K, bool WITH_CQ, bool EW = false, bool GIN = false>
 __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, int n, int I,
                                               const float* sBeta, f32x4& accL, f32x4& accC) {
   const int l = lane_id(), j = l & 15, qk = l >> 4, H = a.H;
@@ -207,6 +232,7 @@ __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, 
   float pL[SUB], pC[SUB];
 #pragma unroll
   for (int i = 0; i < SUB; ++i) pL[i] = pC[i] = 0.f;
+  const float ea = GIN ? fexp2(a.a_log[h] * LOG2E) : 0.f;
   const int rj = I * SUB + j;
   if (rj < n) {
     for (int k = qk * (K / 4); k < (qk + 1) * (K / 4); ++k) {
@@ -218,7 +244,10 @@ __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, 
         if (i >= j && ri < n) {
           if (i > j) {
             float gi = 0.f;
-            if (a.gate == 2) gi = a.g[((t0 + ri) * H + h) * K + k];
+            if constexpr (GIN)
+              gi = -ea * softplus(tof(reinterpret_cast<const T*>(a.gx)[((t0 + ri) * H + h) * K + k]) +
+                                  a.dt_bias[(int64_t)h * K + k]);
+            else if (a.gate == 2) gi = a.g[((t0 + ri) * H + h) * K + k];
             else if (a.gate == 1) gi = a.g[(t0 + ri) * H + h];
             run += gi * LOG2E;
           }

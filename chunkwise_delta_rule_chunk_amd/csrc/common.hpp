@@ -82,6 +82,38 @@ __device__ __forceinline__ void lds_barrier() {
 // the normal range flush to zero.  Every use is a gate factor or decay whose
 // values that small are negligible against the terms they scale.
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float LN2 = 0.6931471805599453f;
+// softplus(z) = log(1 + exp(z)) = max(z, 0) + log(1 + exp(-|z|)), by the
+// hardware exp2 and log2 (no overflow for large |z|; below z ~ -17 the
+// result is 0 where the exact value is below 4e-8)
+__device__ __forceinline__ float softplus(float z) {
+  return fmaxf(z, 0.f) + LN2 * __builtin_amdgcn_logf(1.f + fexp2(-fabsf(z) * LOG2E));
+}
+// softplus(z) and its derivative, the logistic sigmoid 1 / (1 + exp(-z)),
+// from one exponential e = exp(-|z|): sigmoid = (z >= 0 ? 1 : e) / (1 + e)
+__device__ __forceinline__ void softplus_sigmoid(float z, float& sp, float& sg) {
+  const float e = fexp2(-fabsf(z) * LOG2E);
+  sp = fmaxf(z, 0.f) + LN2 * __builtin_amdgcn_logf(1.f + e);
+  sg = (z >= 0.f ? 1.f : e) * __builtin_amdgcn_rcpf(1.f + e);
+}
+
+// Sum over the 16 lanes of each row of the wave (lanes 16 r .. 16 r + 15),
+// returned to every lane of the row, by DPP lane moves: the two quad
+// permutations [1,0,3,2] and [2,3,0,1], then the half-row mirror (lane i of
+// 8 reads lane 7 - i, in the other quad) and the row mirror (lane i reads
+// 15 - i, in the other half).  Each step pairs lanes whose partial sums cover
+// disjoint lanes, and runs on the VALU (no LDS traffic, no wait).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
 
 template <typename T>
 __device__ __forceinline__ float tof(T x) { return (float)x; }

@@ -37,15 +37,23 @@
 
 namespace rewy {
 
-// GX = GATE + 4 EW.  GATE: 0 none, 1 scalar, 2 vector (a template parameter:
-// no gate tests in the loops).  EW: the erase/write form, with an erase gate b
-// per (token, feature) in place of beta in E = b gamma K and a write gate w per
-// (token, value) in Z = w V; it returns db = (gamma K) Ebar and dw = V P per
-// element (ReWY paper Table 1, GDN2 row) and runs one workgroup per CU.
+// GX = GATE + 4 EW + 8 GIN.  GATE: 0 none, 1 scalar, 2 vector (a template
+// parameter: no gate tests in the loops).  EW: the erase/write form, with an
+// erase gate b per (token, feature) in place of beta in E = b gamma K and a
+// write gate w per (token, value) in Z = w V; it returns db = (gamma K) Ebar
+// and dw = V P per element (ReWY paper Table 1, GDN2 row) and runs one
+// workgroup per CU.  GIN (vector gate only): the gate was formed from its
+// pre-activation, g = -exp(A_log) softplus(x + dt_bias) (GDN2 spec section
+// 4.4), and the chain rule is taken here: dx = -exp(A_log) sigmoid(x + dt_bias)
+// dg is written in place of dg, and each wave writes its partial sums of
+// dA_log = sum dg g and ddt_bias = sum over tokens of dx for a later
+// reduction over chunks.
 template <typename T, int K, int V, int GX>
 __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   constexpr int GATE = GX & 3;
   constexpr bool EW = GX & 4;
+  constexpr bool GIN = GX & 8;
+  static_assert(!GIN || (GATE == 2 && !EW), "the gate is formed in the kernel for the vector gate");
   constexpr int NTH = 256;
   constexpr int PV = pitch<T>(V), PA = pitch<T>(CH);
   constexpr int NFB = K / SUB, NVB = V / SUB;
@@ -80,7 +88,15 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   const int c = blockIdx.x / H, h = blockIdx.x - c * H;
   const ChunkInfo ci = load_chunk(a.chunks, c);
   const int n = ci.len;
-  if (n == 0) return;
+  if (n == 0) {
+    // gate in the kernel: an empty slot adds zero to the parameter gradients
+    if constexpr (GIN) {
+      float* gp = a.gpart + ((int64_t)c * H + h) * NSUB * K;
+      for (int i = threadIdx.x; i < NSUB * K; i += 256) gp[i] = 0.f;
+      if (threadIdx.x < NSUB) a.gpart[(int64_t)a.nc_max * H * NSUB * K + ((int64_t)c * H + h) * NSUB + threadIdx.x] = 0.f;
+    }
+    return;
+  }
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   const int q4 = l >> 4, f = l & 15;
   const int I = w;  // row block of this wave
@@ -270,7 +286,16 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   // outputs through bounds-checked buffers: rows past the chunk's end are dropped
   const GBuf bdq = gbuf(reinterpret_cast<T*>(a.dq) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
   const GBuf bdk = gbuf(reinterpret_cast<T*>(a.dk) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
-  const GBuf bdg = gbuf(a.dg + (t0 * H + h) * K, GATE == 2 ? tile_bytes<float>(n, gsK, K) : 0u);
+  const GBuf bdg = gbuf(a.dg + (t0 * H + h) * K, GATE == 2 && !GIN ? tile_bytes<float>(n, gsK, K) : 0u);
+  // gate in the kernel: dx (like dq), the pre-activation and dt_bias of this
+  // lane's row and four features, the wave's partial sums
+  const GBuf bdx = gbuf(reinterpret_cast<T*>(a.dgx) + (t0 * H + h) * K, GIN ? tile_bytes<T>(n, gsK, K) : 0u);
+  const GBuf bgx = gbuf(reinterpret_cast<const T*>(a.gx) + (t0 * H + h) * K, GIN ? tile_bytes<T>(n, gsK, K) : 0u);
+  const GBuf bdt = gbuf(a.dt_bias + (int64_t)h * K, GIN ? K * 4 : 0u);
+  const GBuf bgp = gbuf(a.gpart + cb * NSUB * K, GIN ? NSUB * K * 4 : 0u);
+  const float nea = GIN ? -fexp2(__uint_as_float(gld4(gbuf(a.a_log, H * 4), h * 4)) * LOG2E) : 0.f;
+  float dal = 0.f;                 // gate in the kernel: this lane's part of sum dg softplus(z)
+  FR pdx = to_frag<T>(zero4());    // dx of the previous (even) feature block
   const int jl = n - 1;  // last valid row
   const FR DmI = pick(Dm, I), HmI = pick(Hm, I), DtmI = pick(Dtm, I), HtmI = pick(Htm, I);
   const f32x4 bIb = *reinterpret_cast<const f32x4*>(sBeta + I * SUB + 4 * q4);  // beta, rows of block I
@@ -381,6 +406,20 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
     const int kc = fb * SUB + f;  // this lane's feature
     const int buf = fb & 1;
     fetch_fb(min(fb + 1, NFB - 1));  // the last block reads itself again, unused
+    // gate in the kernel: x at (row 16 I + f, features 16 fb + 4 q4 .. + 3)
+    // and dt_bias of those features, used after the block's reverse sum
+    uint4 xr = {0u, 0u, 0u, 0u}, dtr = {0u, 0u, 0u, 0u};
+    if constexpr (GIN) {
+      const uint32_t xo = (uint32_t)(((int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4) * (int64_t)sizeof(T));
+      if constexpr (sizeof(T) == 2) {
+        const uint2 x2 = gld8(bgx, xo);
+        xr.x = x2.x;
+        xr.y = x2.y;
+      } else {
+        xr = gld16(bgx, xo);
+      }
+      dtr = gld16(bdt, (uint32_t)((fb * SUB + 4 * q4) * 4));
+    }
     // first row of this lane, opaque per iteration: the output addresses derived
     // from it are recomputed rather than kept live (and spilled) across blocks
     int lrow = I * SUB + 4 * q4;
@@ -646,32 +685,67 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
       // rows past the end (all rows of a wave past the end) are dropped
       f32x4 tg = zero4();
       mm16(tg, f32x4{suf[0] + add, suf[1] + add, suf[2] + add, suf[3] + add}, idf);
-      gst16(bdg, (uint32_t)(((int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4) * 4), __builtin_bit_cast(uint4, tg));
+      if constexpr (GIN) {
+        // dx = -ea sigmoid(z) dg, z = x + dt_bias; the wave's sums over its
+        // valid rows of dg softplus(z) (times -ea at the end: dg g) and, per
+        // feature, of dx.  dg is zeroed on rows past the end (their dx is
+        // not stored), so no other mask is needed.
+        const float rm = I * SUB + f < n ? 1.f : 0.f;
+        f32x4 xv, dx, px;
+        if constexpr (sizeof(T) == 2) {
+          xv[0] = __uint_as_float(xr.x << 16);
+          xv[1] = __uint_as_float(xr.x & 0xffff0000u);
+          xv[2] = __uint_as_float(xr.y << 16);
+          xv[3] = __uint_as_float(xr.y & 0xffff0000u);
+        } else {
+          xv = __builtin_bit_cast(f32x4, xr);
+        }
+        const f32x4 dt = __builtin_bit_cast(f32x4, dtr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float sp, sg;
+          softplus_sigmoid(xv[e] + dt[e], sp, sg);
+          const float dgm = tg[e] * rm;
+          dx[e] = nea * sg * dgm;
+          px[e] = row16_sum(dx[e]);  // over the wave's 16 rows
+          dal += dgm * sp;
+        }
+        gst16(bgp, f == 0 ? (uint32_t)((I * K + fb * SUB + 4 * q4) * 4) : OOB, __builtin_bit_cast(uint4, px));
+        // stored in pairs of feature blocks, like dq
+        const FR yx = to_frag<T>(dx);
+        const bool odd = fb & 1;
+        const int64_t tb = (int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4;
+        const uint32_t o1 = odd ? (uint32_t)((tb - SUB) * (int64_t)sizeof(T)) : OOB;
+        const uint32_t o2 = odd ? (uint32_t)(tb * (int64_t)sizeof(T)) : OOB;
+        if constexpr (std::is_same_v<T, bf16>) {
+          gst8(bdx, o1, __builtin_bit_cast(uint2, pdx));
+          gst8(bdx, o2, __builtin_bit_cast(uint2, yx));
+        } else {
+          gst16(bdx, o1, __builtin_bit_cast(uint4, pdx));
+          gst16(bdx, o2, __builtin_bit_cast(uint4, yx));
+        }
+        pdx = yx;
+      } else {
+        gst16(bdg, (uint32_t)(((int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4) * 4), __builtin_bit_cast(uint4, tg));
+      }
     } else if (GATE == 1 && live) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = gbar[e];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        x += __shfl_xor(x, 8);
-        sufs[e] += x;
-      }
-      float x = lamw, y = l0;
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
-      x += __shfl_xor(x, 4);
-      x += __shfl_xor(x, 8);
-      y += __shfl_xor(y, 1);
-      y += __shfl_xor(y, 2);
-      y += __shfl_xor(y, 4);
-      y += __shfl_xor(y, 8);
-      lamws += x;
-      lam0s += y;
+      for (int e = 0; e < 4; ++e) sufs[e] += row16_sum(gbar[e]);  // over the block's 16 features
+      lamws += row16_sum(lamw);
+      lam0s += row16_sum(l0);
     }
     if constexpr (GATE != 2) lds_barrier();  // this block's operands are no longer read
     put_fb();                        // after the last block: unused
     lds_barrier();                   // the next block's operands are visible
+  }
+
+  // ---- gate in the kernel: the wave's partial sum of dg g ---------------------
+  if constexpr (GIN) {
+    float x = row16_sum(dal) * nea;
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    const GBuf bga = gbuf(a.gpart + (int64_t)a.nc_max * H * NSUB * K + cb * NSUB, NSUB * 4);
+    gst4(bga, l == 0 ? (uint32_t)(I * 4) : OOB, __float_as_uint(x));
   }
 
   // ---- dbeta = write part + erase part (rows of block I) ---------------------
@@ -679,11 +753,7 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if constexpr (EW) break;
-    float x = dbe[e];
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+    const float x = row16_sum(dbe[e]);
     const int row = I * SUB + 4 * q4 + e;
     if (f == 0 && row < n)
       st_beta(a.dbeta, a.beta_f32, (t0 + row) * H + h, sDbw[row] + x);
@@ -734,13 +804,68 @@ static hipError_t bwd_chunk_t(const Args& a, hipStream_t s) {
   switch (a.gate) {
     case 0: return a.ew ? bwd_chunk_g<T, 4>(a, s) : bwd_chunk_g<T, 0>(a, s);
     case 1: return a.ew ? bwd_chunk_g<T, 5>(a, s) : bwd_chunk_g<T, 1>(a, s);
-    case 2: return a.ew ? bwd_chunk_g<T, 6>(a, s) : bwd_chunk_g<T, 2>(a, s);
+    case 2: return a.ew ? bwd_chunk_g<T, 6>(a, s) : a.gin ? bwd_chunk_g<T, 10>(a, s) : bwd_chunk_g<T, 2>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_bwd_chunk(const Args& a, int f32, hipStream_t s) {
   return f32 ? bwd_chunk_t<float>(a, s) : bwd_chunk_t<bf16>(a, s);
+}
+
+// Parameter gradients of the gate formed in the kernel, from the chunk
+// backward's per-wave partial sums (GDN2 spec section 4.4: dA_log = sum of
+// dg g over tokens and features, ddt_bias = sum of dx over tokens).  Block
+// (h, y): y < ceil(K/64) sums ddt_bias of 64 features, sixteen slices of the
+// chunk slots per feature; the last y sums dA_log of the head.  Every chunk
+// slot holds partials (zeros for a slot without tokens), so the loads are
+// independent of each other.  A fixed order of summation: the result does not
+// depend on timing.
+__global__ __launch_bounds__(1024) void k_gate_reduce(Args a) {
+  constexpr int NS = 16;
+  __shared__ float sp[NS][64];
+  const int h = blockIdx.x, H = a.H, K = a.K;
+  const int tid = threadIdx.x, tx = tid & 63, sl = tid >> 6;
+  const int nkb = (K + 63) / 64;
+  float acc = 0.f;
+  if ((int)blockIdx.y == nkb) {
+    const float* p = a.gpart + (int64_t)a.nc_max * H * NSUB * K;
+#pragma unroll 4
+    for (int i = tid; i < a.nc_max * NSUB; i += 1024) {
+      const int c = i / NSUB;
+      acc += p[((int64_t)c * H + h) * NSUB + (i - c * NSUB)];
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) acc += __shfl_xor(acc, m);
+    if (tx == 0) sp[sl][0] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.f;
+      for (int j = 0; j < NS; ++j) t += sp[j][0];
+      a.da_log[h] = t;
+    }
+    return;
+  }
+  const int k = blockIdx.y * 64 + tx;
+  if (k < K) {
+#pragma unroll 4
+    for (int c = sl; c < a.nc_max; c += NS) {
+      const float* p = a.gpart + ((int64_t)c * H + h) * NSUB * K + k;
+      acc += (p[0] + p[K]) + (p[2 * K] + p[3 * K]);
+    }
+  }
+  sp[sl][tx] = acc;
+  __syncthreads();
+  if (sl == 0 && k < K) {
+    float t = 0.f;
+    for (int j = 0; j < NS; ++j) t += sp[j][tx];
+    a.ddt_bias[(int64_t)h * K + k] = t;
+  }
+}
+
+hipError_t launch_gate_reduce(const Args& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_gate_reduce, dim3(a.H, (a.K + 63) / 64 + 1), dim3(1024), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace rewy

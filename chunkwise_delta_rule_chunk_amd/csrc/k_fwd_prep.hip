@@ -74,6 +74,8 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   // the erase/write form runs one workgroup per CU: the erase gate of the
   // thread's rows and the write gate's v pieces need registers
   constexpr bool EW = MODE & PREP_EW;
+  // the gate formed from its pre-activation: g = -exp(A_log) softplus(x + dt_bias)
+  constexpr bool GIN = MODE & PREP_GIN;
   constexpr int NTH = 256, NW = NTH / 64;
   constexpr bool BF = std::is_same_v<T, bf16>;
   constexpr int PK = pitch<T>(K);   // T rows of K
@@ -128,6 +130,9 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   // erase/write form: raw bits of the next item's erase gate at this thread's
   // rows and columns, and the write gate in the layout of the staged v
   uint32_t bwr[EW ? NSL : 1][EW ? RS : 1];
+  // gate in the kernel: A_log of the next item's head and dt_bias of each
+  // slot's column (raw bits)
+  uint32_t gal = 0u, gdtb[GIN ? NSL : 1];
   uint4 pw2[EW && BF ? 2 * VPT : 1];
   Staged<T, CH, V, NTH> pw;
   // the fetches take the item's chunk record, read one item ahead (its
@@ -166,8 +171,18 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   auto fetch_g = [&](int item, const ChunkInfo& ci) {
     const int h = item % H;
     if (ci.len == 0) return;
+    if constexpr (GIN) {
+      const GBuf bd = gbuf(a.dt_bias + (int64_t)h * K, K * 4);
 #pragma unroll
-    for (int s = 0; s < NSL; ++s) gc[s].load(a, (int64_t)ci.bos, h, ci.len, K, 0);
+      for (int s = 0; s < NSL; ++s) {
+        gc[s].template load_x<T>(a, (int64_t)ci.bos, h, ci.len, K);
+        gdtb[s] = gld4(bd, gc[s].c * 4);
+      }
+      gal = gld4(gbuf(a.a_log, a.H * 4), h * 4);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NSL; ++s) gc[s].load(a, (int64_t)ci.bos, h, ci.len, K, 0);
+    }
     if constexpr (EW) {  // erase gate rows past the end read as zero
       const GBuf bb = gbuf(reinterpret_cast<const T*>(a.beta) + ((int64_t)ci.bos * H + h) * K,
                            tile_bytes<T>(ci.len, gsK, K));
@@ -214,6 +229,11 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     pq.store(sQ, PK, tid);
     if (tid < CH) sBeta[tid] = tid < n ? beta_val(pbeta, a.beta_f32) : 0.f;
     if (tid < NSUB) sFlag[tid] = 0;
+    if constexpr (GIN) {
+      const float ea = fexp2(__uint_as_float(gal) * LOG2E);
+#pragma unroll
+      for (int s = 0; s < NSL; ++s) gc[s].template kda_gate<T>(ea, __uint_as_float(gdtb[s]));
+    }
 #pragma unroll
     for (int s = 0; s < NSL; ++s) gc[s].prefix_local(sTot, n);
     lds_barrier();
@@ -365,7 +385,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       for (int J = w; J < NSUB; J += NW)
         if (J * SUB < n && sFlag[J]) {
           f32x4 accL, accC;
-          pairwise_diag<T, K, true, EW>(a, t0, h, n, J, sBeta, accL, accC);
+          pairwise_diag<T, K, true, EW, GIN>(a, t0, h, n, J, sBeta, accL, accC);
           store(J, J, accL, accC);
         }
       // tiles nobody computed: zeros (the upper triangle and rows past the end)
@@ -560,14 +580,17 @@ static hipError_t prep_t(const Args& a, hipStream_t s) {
   constexpr int FWD = PREP_FWD_SCAN | PREP_FWD_OUT;
   constexpr int ALL = FWD | PREP_BWD_SCAN | PREP_BWD_CHUNK;
   constexpr int BWD = PREP_FWD_SCAN | PREP_BWD_SCAN | PREP_BWD_CHUNK;
-  constexpr int E = PREP_EW;
-  switch (a.prep_mode | (a.ew ? E : 0)) {
+  constexpr int E = PREP_EW, GI = PREP_GIN;
+  switch (a.prep_mode | (a.ew ? E : 0) | (a.gin ? GI : 0)) {
     case FWD: return prep_m<T, FWD>(a, s);
     case ALL: return prep_m<T, ALL>(a, s);
     case BWD: return prep_m<T, BWD>(a, s);
     case FWD | E: return prep_m<T, FWD | E>(a, s);
     case ALL | E: return prep_m<T, ALL | E>(a, s);
     case BWD | E: return prep_m<T, BWD | E>(a, s);
+    case FWD | GI: return prep_m<T, FWD | GI>(a, s);
+    case ALL | GI: return prep_m<T, ALL | GI>(a, s);
+    case BWD | GI: return prep_m<T, BWD | GI>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

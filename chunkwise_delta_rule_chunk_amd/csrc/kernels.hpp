@@ -29,6 +29,12 @@ struct Args {
   const void* beta;         // beta [BT,H]; in the erase/write form the erase gate b [BT,H,K]
   const void* wg;           // erase/write form: the write gate w [BT,H,V], else nullptr
   int ew;                   // 1 for the erase/write form
+  // gate in the kernel: g = -exp(A_log[h]) softplus(x + dt_bias[h, k]) from
+  // the pre-activation x [BT,H,K] (feature dtype), A_log [H], dt_bias [H,K]
+  const void* gx;
+  const float* a_log;
+  const float* dt_bias;
+  int gin;                  // 1 when the gate is formed in the kernels
   const float* h0;
   const void* dO;
   const float* dht;
@@ -41,6 +47,10 @@ struct Args {
   float* dg;
   void* dbeta;              // dbeta [BT,H]; in the erase/write form db [BT,H,K]
   void* dw;                 // erase/write form: dw [BT,H,V]
+  void* dgx;                // gate in the kernel: dx [BT,H,K] (feature dtype)
+  float* da_log;            // gate in the kernel: dA_log [H]
+  float* ddt_bias;          // gate in the kernel: ddt_bias [H,K]
+  float* gpart;             // gate in the kernel: per (chunk, head, wave) partial sums
   float* dh0;
   // Forward intermediates.  Token-major tensors are [BT,H,*]; chunk tiles are
   // [nc_max,H,rows,64] with all 64 token columns written (zeros past the
@@ -94,6 +104,8 @@ constexpr int PREP_BWD_CHUNK = 8; // At, G2t, Gst
 // The erase/write form: beta holds the erase gate b [.., K] and wg the write
 // gate w [.., V] (both in the feature dtype); E = b gamma K and Z = w V.
 constexpr int PREP_EW = 16;
+// The gate formed in the kernel from its pre-activation (Args::gx).
+constexpr int PREP_GIN = 32;
 
 // Launchers: enqueue on `stream`; return the hipError_t of the launch.
 hipError_t launch_chunk_table(const Args& a, hipStream_t s);
@@ -106,6 +118,8 @@ hipError_t launch_bwd_scan(const Args& a, int dtype_f32, hipStream_t s);
 // the forward scan (natural outputs) and the reverse scan in one launch
 hipError_t launch_scans(const Args& a, int dtype_f32, hipStream_t s);
 hipError_t launch_bwd_chunk(const Args& a, int dtype_f32, hipStream_t s);
+// the gate-in-kernel parameter gradients from the chunk backward's partials
+hipError_t launch_gate_reduce(const Args& a, hipStream_t s);
 // the token-serial forward (decode)
 hipError_t launch_recurrent(const Args& a, int dtype_f32, hipStream_t s);
 

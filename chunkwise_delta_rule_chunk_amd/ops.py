@@ -43,14 +43,17 @@ class Problem:
         return (self.N, d.H, d.K, d.V)
 
 
-def make_problem(q, v, g, beta, *, scale=None, cu_seqlens=None, policy="recompute") -> Problem:
+def make_problem(q, v, g, beta, *, scale=None, cu_seqlens=None, policy="recompute",
+                 vector_gate=False) -> Problem:
     if q.dtype not in _DT or v.dtype != q.dtype:
         raise TypeError("q, k, v must share dtype bf16 or fp32")
     if beta.dtype not in _DT:
         raise TypeError("beta must be bf16 or fp32")
     Bsz, T, H, K = q.shape
     V = v.shape[-1]
-    if g is None:
+    if vector_gate:  # the gate is formed in the kernels from its pre-activation
+        gate = B.REWY_GATE_VECTOR
+    elif g is None:
         gate = B.REWY_GATE_NONE
     elif g.dim() == 3:
         gate = B.REWY_GATE_SCALAR
@@ -138,13 +141,44 @@ def forward_gdn2(q, k, v, g, b, w, *, scale=None, h0=None, cu_seqlens=None, poli
     return o, ht, ctx
 
 
+def forward_kda_gate(q, k, v, x, a_log, dt_bias, beta, *, scale=None, h0=None, cu_seqlens=None,
+                     policy="recompute", output_final_state=True, stream=None, ws=None):
+    """Run rewy_fwd_kda_gate: the vector gate g = -exp(A_log) softplus(x + dt_bias)
+    is formed in the kernels from x [B,T,H,K] (feature dtype), A_log [H] and
+    dt_bias [H,K] (fp32).  Returns (o, ht or None, ctx) for ``backward``."""
+    if a_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+        raise TypeError("A_log and dt_bias must be fp32")
+    if x.dtype != q.dtype:
+        raise TypeError("x must have the feature dtype")
+    prob = make_problem(q, v, None, beta, scale=scale, cu_seqlens=cu_seqlens, policy=policy,
+                        vector_gate=True)
+    o = torch.empty_like(v)
+    ht = torch.empty(prob.state_shape, dtype=torch.float32, device=q.device) \
+        if output_final_state else None
+    saved = None
+    if policy == "save":
+        saved = torch.empty(B.rewy_saved_bytes(prob.desc), dtype=torch.uint8, device=q.device)
+    if ws is None:
+        ws = workspace(prob, 0)
+    rc = B.rewy_fwd_kda_gate(prob.desc, _p(q), _p(k), _p(v), _p(x), _p(a_log), _p(dt_bias),
+                             _p(beta), _p(h0), _p(o), _p(ht), _p(saved), _p(ws), ws.numel(),
+                             _stream(q.device, stream))
+    _check(rc, "rewy_fwd_kda_gate")
+    ctx = dict(prob=prob, q=q, k=k, v=v, g=None, x=x, a_log=a_log, dt_bias=dt_bias, beta=beta,
+               h0=h0, saved=saved)
+    return o, ht, ctx
+
+
 def backward(ctx, dO, dht=None, *, stream=None, ws=None, want_dh0=None):
-    """Run rewy_bwd (or rewy_bwd_gdn2 for a ``forward_gdn2`` context).  Returns
-    dict dq, dk, dv, dg, dbeta, dh0 (and, for the erase/write form, db and dw
-    in place of dbeta)."""
+    """Run rewy_bwd (rewy_bwd_gdn2 for a ``forward_gdn2`` context,
+    rewy_bwd_kda_gate for a ``forward_kda_gate`` one).  Returns dict dq, dk, dv,
+    dg, dbeta, dh0 (for the erase/write form db and dw in place of dbeta; for
+    the gate formed in the kernels dx, dA_log and ddt_bias in place of dg)."""
     prob = ctx["prob"]
     if ctx.get("w") is not None:
         return _backward_gdn2(ctx, dO, dht, stream=stream, ws=ws, want_dh0=want_dh0)
+    if ctx.get("x") is not None:
+        return _backward_kda_gate(ctx, dO, dht, stream=stream, ws=ws, want_dh0=want_dh0)
     q, k, v, g, beta, h0 = (ctx[x] for x in ("q", "k", "v", "g", "beta", "h0"))
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -179,6 +213,25 @@ def _backward_gdn2(ctx, dO, dht=None, *, stream=None, ws=None, want_dh0=None):
                          _p(dw), _p(dh0), _p(ws), ws.numel(), _stream(q.device, stream))
     _check(rc, "rewy_bwd_gdn2")
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, db=db, dw=dw, dh0=dh0)
+
+
+def _backward_kda_gate(ctx, dO, dht=None, *, stream=None, ws=None, want_dh0=None):
+    prob = ctx["prob"]
+    q, k, v, x, a_log, dt_bias, beta, h0 = (ctx[n] for n in ("q", "k", "v", "x", "a_log", "dt_bias",
+                                                          "beta", "h0"))
+    dq, dk, dv, dx = (torch.empty_like(t) for t in (q, k, v, x))
+    da_log, ddt_bias, dbeta = torch.empty_like(a_log), torch.empty_like(dt_bias), torch.empty_like(beta)
+    if want_dh0 is None:
+        want_dh0 = h0 is not None
+    dh0 = torch.empty(prob.state_shape, dtype=torch.float32, device=q.device) if want_dh0 else None
+    if ws is None:
+        ws = workspace(prob, 2)
+    rc = B.rewy_bwd_kda_gate(prob.desc, _p(q), _p(k), _p(v), _p(x), _p(a_log), _p(dt_bias), _p(beta),
+                             _p(h0), _p(dO), _p(dht), _p(ctx["saved"]), _p(dq), _p(dk), _p(dv),
+                             _p(dx), _p(da_log), _p(ddt_bias), _p(dbeta), _p(dh0), _p(ws),
+                             ws.numel(), _stream(q.device, stream))
+    _check(rc, "rewy_bwd_kda_gate")
+    return dict(dq=dq, dk=dk, dv=dv, dx=dx, da_log=da_log, ddt_bias=ddt_bias, dbeta=dbeta, dh0=dh0)
 
 
 class ChunkDeltaRule(torch.autograd.Function):

@@ -83,8 +83,11 @@ typedef struct {
     float scale;                    /* query scale, usually K^-1/2 */
 } rewy_desc;
 
-/* Bytes of device workspace a call needs: phase 0 = rewy_fwd, 1 = rewy_bwd.
- * Returns 0 for an invalid descriptor (see rewy_last_error). */
+/* Bytes of device workspace a call needs: phase 0 = rewy_fwd (and the other
+ * forwards), 1 = rewy_bwd and rewy_bwd_gdn2, 2 = rewy_bwd_kda_gate (phase 1
+ * plus the per-chunk partial sums of the gate parameters' gradients; needs
+ * gate == VECTOR).  Returns 0 for an invalid descriptor or phase (see
+ * rewy_last_error). */
 size_t rewy_workspace_bytes(const rewy_desc *d, int phase);
 
 /* Bytes of the `saved` buffer for policy SAVE (0 for RECOMPUTE). */
@@ -127,6 +130,32 @@ int rewy_bwd_gdn2(const rewy_desc *d, const void *q, const void *k, const void *
                   const void *dO, const float *dht, const void *saved,
                   void *dq, void *dk, void *dv, float *dg, void *db, void *dw, float *dh0,
                   void *workspace, size_t ws_bytes, void *stream);
+
+/* The vector gate formed inside the kernels from its pre-activation (GDN2
+ * spec section 4.4, the KDA gate; KDA blog section 6 for the operator):
+ *     g[t,h,k] = -exp(A_log[h]) * softplus(x[t,h,k] + dt_bias[h,k]),
+ * so the fp32 log-decay g [B,T,H,K] is never read from or written to memory.
+ * gate must be VECTOR.  x is [B,T,H,K] in the feature dtype, 16-byte aligned;
+ * A_log is fp32 [H]; dt_bias is fp32 [H,K], 16-byte aligned.  The result is
+ * rewy_fwd's / rewy_bwd's with g formed by the formula above in fp32.  The
+ * backward returns, in place of dg, dx [B,T,H,K] (feature dtype) and the fp32
+ * parameter gradients dA_log [H] and ddt_bias [H,K], summed over every token
+ * of every sequence and overwritten (not accumulated into); its workspace is
+ * rewy_workspace_bytes(d, 2).  The sums over chunks are taken in a fixed
+ * order, so repeated calls give identical results.  Everything else
+ * (descriptor, saved buffer, ownership, errors) is as for rewy_fwd / rewy_bwd;
+ * the saved buffer of rewy_fwd_kda_gate serves rewy_bwd_kda_gate only. */
+int rewy_fwd_kda_gate(const rewy_desc *d, const void *q, const void *k, const void *v,
+                      const void *x, const float *a_log, const float *dt_bias,
+                      const void *beta, const float *h0, void *o, float *ht, void *saved,
+                      void *workspace, size_t ws_bytes, void *stream);
+int rewy_bwd_kda_gate(const rewy_desc *d, const void *q, const void *k, const void *v,
+                      const void *x, const float *a_log, const float *dt_bias,
+                      const void *beta, const float *h0,
+                      const void *dO, const float *dht, const void *saved,
+                      void *dq, void *dk, void *dv, void *dx, float *da_log, float *ddt_bias,
+                      void *dbeta, float *dh0,
+                      void *workspace, size_t ws_bytes, void *stream);
 
 /* Token-serial forward for decoding (the pages' fused recurrent form of the
  * same recurrence: ReWY paper, Background / Delta-rule operators; KDA blog

@@ -93,6 +93,12 @@ def test_workspace_sizes_follow_the_layout(lib):
     assert B.rewy_workspace_bytes(d, 0) == head + shared + scan + out
     # the reverse-scan set of the backward reuses the output operands' space
     assert B.rewy_workspace_bytes(d, 1) == head + shared + scan + rscan + bwd
+    # the gate formed in the kernels: per (chunk, head, wave) partial sums of
+    # ddt_bias [K] and dA_log [1] follow the backward's buffers
+    assert B.rewy_workspace_bytes(d, 2) == head + shared + scan + rscan + bwd + up(nc * H * 4 * (K + 1) * 4)
+    assert B.rewy_workspace_bytes(_desc(gate=B.REWY_GATE_SCALAR), 2) == 0
+    assert "VECTOR" in B.rewy_last_error()
+    assert B.rewy_workspace_bytes(d, 3) == 0 and "bad phase" in B.rewy_last_error()
     assert B.rewy_saved_bytes(d) == 0
     ds = _desc(policy=B.REWY_SAVE)
     assert B.rewy_saved_bytes(ds) == shared + rscan
@@ -140,6 +146,26 @@ def test_calls_reject_bad_pointers_without_launching(lib):
     assert rc == B.REWY_EINVAL and "g must be given" in B.rewy_last_error()
     rc = B.rewy_recurrent_fwd(d, P(256), P(256), P(264), P(256), P(256), None, P(256), None, None)
     assert rc == B.REWY_EINVAL and "aligned" in B.rewy_last_error()
+    # gate formed in the kernels: vector gate only, every gate tensor given, aligned
+    rc = B.rewy_fwd_kda_gate(_desc(gate=B.REWY_GATE_SCALAR), P(256), P(256), P(256), P(256), P(256),
+                             P(256), P(256), None, P(256), None, None, P(256), 1 << 40, None)
+    assert rc == B.REWY_EINVAL and "VECTOR" in B.rewy_last_error()
+    rc = B.rewy_fwd_kda_gate(d, P(256), P(256), P(256), P(256), None, P(256), P(256), None, P(256),
+                             None, None, P(256), 1 << 40, None)
+    assert rc == B.REWY_EINVAL and "A_log" in B.rewy_last_error()
+    rc = B.rewy_fwd_kda_gate(d, P(256), P(256), P(256), P(256), P(256), P(264), P(256), None, P(256),
+                             None, None, P(256), 1 << 40, None)
+    assert rc == B.REWY_EINVAL and "aligned" in B.rewy_last_error()
+    rc = B.rewy_bwd_kda_gate(d, P(256), P(256), P(256), P(256), P(256), P(256), P(256), None, P(256),
+                             None, None, P(256), P(256), P(256), P(256), None, P(256), P(256), None,
+                             P(256), 1 << 40, None)
+    assert rc == B.REWY_EINVAL and "dA_log" in B.rewy_last_error()
+    # the phase-1 size is too small for the backward with the gate in the kernels
+    n1 = B.rewy_workspace_bytes(d, 1)
+    rc = B.rewy_bwd_kda_gate(d, P(256), P(256), P(256), P(256), P(256), P(256), P(256), None, P(256),
+                             None, None, P(256), P(256), P(256), P(256), P(256), P(256), P(256), None,
+                             P(256), n1, None)
+    assert rc == B.REWY_EWORKSPACE
     del ws
 
 
