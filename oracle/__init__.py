@@ -145,24 +145,36 @@ def forward(q, k, v, g, beta, *, scale, h0=None, cu_seqlens=None, erase=None, wr
     return o.reshape(p.B, p.T, p.H, p.V), ht
 
 
-def kda_gate(x, a_log, dt_bias):
+def kda_gate(x, a_log, dt_bias, lower_bound=0.0):
     """Channel-wise log-decay from its pre-activation (GDN2 spec section 4.4,
     the layer's gate; computed inside the kernels in section 2.1 and section 3):
-        g = -exp(A_log[h]) * softplus(x + dt_bias[h, k])
+        g = -exp(A_log[h]) * softplus(x + dt_bias[h, k])            (lower_bound = 0)
+        g = lower_bound * sigmoid(exp(A_log[h]) * (x + dt_bias[h, k]))  (lower_bound < 0)
+    The second, bounded form keeps g inside (lower_bound, 0) (GDN2 spec
+    section 3, the recurrent kernel's gate, and section 4.3 for the bound).
     x [B,T,H,K], A_log [H], dt_bias [H,K]; FP64, natural log."""
     z = _f64(x) + _f64(dt_bias)[None, None]
-    return -np.exp(_f64(a_log))[None, None, :, None] * np.logaddexp(0.0, z)
+    ea = np.exp(_f64(a_log))[None, None, :, None]
+    if lower_bound == 0.0:
+        return -ea * np.logaddexp(0.0, z)
+    return float(lower_bound) / (1.0 + np.exp(-ea * z))
 
 
-def kda_gate_backward(x, a_log, dt_bias, dg):
+def kda_gate_backward(x, a_log, dt_bias, dg, lower_bound=0.0):
     """Reverse mode of ``kda_gate`` for a given dg: returns (dx, dA_log,
-    ddt_bias).  d softplus(z)/dz = sigmoid(z); dg/dA_log = g."""
+    ddt_bias).  Softplus form: d softplus(z)/dz = sigmoid(z), dg/dA_log = g.
+    Bounded form, u = exp(A_log) z: dg/dz = lower_bound s (1 - s) exp(A_log)
+    with s = sigmoid(u), and dg/dA_log = (dg/dz) z."""
     z = _f64(x) + _f64(dt_bias)[None, None]
     ea = np.exp(_f64(a_log))[None, None, :, None]
     dg = _f64(dg)
-    dx = -ea * dg / (1.0 + np.exp(-z))
-    g = -ea * np.logaddexp(0.0, z)
-    return dx, (dg * g).sum(axis=(0, 1, 3)), dx.sum(axis=(0, 1))
+    if lower_bound == 0.0:
+        dx = -ea * dg / (1.0 + np.exp(-z))
+        g = -ea * np.logaddexp(0.0, z)
+        return dx, (dg * g).sum(axis=(0, 1, 3)), dx.sum(axis=(0, 1))
+    s = 1.0 / (1.0 + np.exp(-ea * z))
+    dx = dg * float(lower_bound) * s * (1.0 - s) * ea
+    return dx, (dx * z).sum(axis=(0, 1, 3)), dx.sum(axis=(0, 1))
 
 
 def backward(q, k, v, g, beta, dO, *, scale, h0=None, dht=None, cu_seqlens=None, erase=None,

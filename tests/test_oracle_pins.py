@@ -422,3 +422,38 @@ def test_kda_gate_formula_and_reverse_mode():
         minus[arg] = base[arg] - eps * u
         fd = (loss(*plus) - loss(*minus)) / (2 * eps)
         assert abs(fd - float((grad * u).sum())) <= 1e-7 * max(1.0, abs(fd)), (arg, fd)
+
+
+def test_kda_gate_bounded_form_and_reverse_mode():
+    """GDN2 spec section 3 (the recurrent kernel's gate) with the bound of
+    section 4.3: g = lower_bound * sigmoid(exp(A_log) (x + dt_bias)).  At
+    x = -dt_bias it is lower_bound / 2; far on either side it reaches 0 and
+    lower_bound; it stays inside (lower_bound, 0); the reverse mode matches
+    central differences."""
+    rng = np.random.default_rng(5)
+    B, T, H, K = 2, 5, 3, 4
+    lb = -3.5
+    x = rng.normal(size=(B, T, H, K))
+    a = rng.uniform(-2.0, 0.0, H)
+    d = rng.normal(size=(H, K)) * 0.5
+    mid = oracle.kda_gate(np.broadcast_to(-d, (B, T, H, K)), a, d, lb)
+    assert np.allclose(mid, lb / 2, rtol=1e-15, atol=0)
+    lo = oracle.kda_gate(np.broadcast_to(-2000.0 - d, (B, T, H, K)), a, d, lb)
+    hi = oracle.kda_gate(np.broadcast_to(2000.0 - d, (B, T, H, K)), a, d, lb)
+    assert np.abs(lo).max() < 1e-20 and np.allclose(hi, lb, rtol=1e-15, atol=0)
+    g = oracle.kda_gate(x, a, d, lb)
+    assert (g < 0).all() and (g > lb).all()
+    # the two forms differ: the bounded one is not the softplus one
+    assert not np.allclose(g, oracle.kda_gate(x, a, d))
+    R = rng.normal(size=(B, T, H, K))
+    dx, da, dd = oracle.kda_gate_backward(x, a, d, R, lb)
+    loss = lambda xx, aa, db: float((R * oracle.kda_gate(xx, aa, db, lb)).sum())
+    eps = 1e-6
+    for grad, arg in ((dx, 0), (da, 1), (dd, 2)):
+        base = [x, a, d]
+        u = rng.normal(size=base[arg].shape)
+        plus, minus = list(base), list(base)
+        plus[arg] = base[arg] + eps * u
+        minus[arg] = base[arg] - eps * u
+        fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+        assert abs(fd - float((grad * u).sum())) <= 1e-7 * max(1.0, abs(fd)), (arg, fd)
