@@ -157,7 +157,7 @@ def kda_gate(x, a_log, dt_bias, lower_bound=0.0):
     ea = np.exp(_f64(a_log))[None, None, :, None]
     if lower_bound == 0.0:
         return -ea * np.logaddexp(0.0, z)
-    return float(lower_bound) / (1.0 + np.exp(-ea * z))
+    return float(lower_bound) * np.exp(-np.logaddexp(0.0, -ea * z))  # sigmoid without overflow
 
 
 def kda_gate_backward(x, a_log, dt_bias, dg, lower_bound=0.0):
@@ -172,7 +172,7 @@ def kda_gate_backward(x, a_log, dt_bias, dg, lower_bound=0.0):
         dx = -ea * dg / (1.0 + np.exp(-z))
         g = -ea * np.logaddexp(0.0, z)
         return dx, (dg * g).sum(axis=(0, 1, 3)), dx.sum(axis=(0, 1))
-    s = 1.0 / (1.0 + np.exp(-ea * z))
+    s = np.exp(-np.logaddexp(0.0, -ea * z))
     dx = dg * float(lower_bound) * s * (1.0 - s) * ea
     return dx, (dx * z).sum(axis=(0, 1, 3)), dx.sum(axis=(0, 1))
 
