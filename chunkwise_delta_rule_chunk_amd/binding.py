@@ -71,9 +71,10 @@ def load():
         lib.rewy_fwd_gdn2.restype = ctypes.c_int
         lib.rewy_bwd_gdn2.argtypes = [D] + [P] * 18 + [S, P]
         lib.rewy_bwd_gdn2.restype = ctypes.c_int
-        lib.rewy_fwd_kda_gate.argtypes = [D] + [P] * 12 + [S, P]
+        F = ctypes.c_float
+        lib.rewy_fwd_kda_gate.argtypes = [D] + [P] * 6 + [F] + [P] * 6 + [S, P]
         lib.rewy_fwd_kda_gate.restype = ctypes.c_int
-        lib.rewy_bwd_kda_gate.argtypes = [D] + [P] * 20 + [S, P]
+        lib.rewy_bwd_kda_gate.argtypes = [D] + [P] * 6 + [F] + [P] * 14 + [S, P]
         lib.rewy_bwd_kda_gate.restype = ctypes.c_int
         lib.rewy_recurrent_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P]
         lib.rewy_recurrent_fwd.restype = ctypes.c_int
@@ -121,17 +122,17 @@ def rewy_bwd_gdn2(desc, q, k, v, g, b, w, h0, dO, dht, saved, dq, dk, dv, dg, db
                                 dv, dg, db, dw, dh0, workspace, ws_bytes, stream)
 
 
-def rewy_fwd_kda_gate(desc, q, k, v, x, a_log, dt_bias, beta, h0, o, ht, saved, workspace, ws_bytes,
-                      stream) -> int:
-    return load().rewy_fwd_kda_gate(ctypes.byref(desc), q, k, v, x, a_log, dt_bias, beta, h0, o, ht,
-                                    saved, workspace, ws_bytes, stream)
+def rewy_fwd_kda_gate(desc, q, k, v, x, a_log, dt_bias, lower_bound, beta, h0, o, ht, saved,
+                      workspace, ws_bytes, stream) -> int:
+    return load().rewy_fwd_kda_gate(ctypes.byref(desc), q, k, v, x, a_log, dt_bias, lower_bound,
+                                    beta, h0, o, ht, saved, workspace, ws_bytes, stream)
 
 
-def rewy_bwd_kda_gate(desc, q, k, v, x, a_log, dt_bias, beta, h0, dO, dht, saved, dq, dk, dv, dx,
-                      da_log, ddt_bias, dbeta, dh0, workspace, ws_bytes, stream) -> int:
-    return load().rewy_bwd_kda_gate(ctypes.byref(desc), q, k, v, x, a_log, dt_bias, beta, h0, dO,
-                                    dht, saved, dq, dk, dv, dx, da_log, ddt_bias, dbeta, dh0,
-                                    workspace, ws_bytes, stream)
+def rewy_bwd_kda_gate(desc, q, k, v, x, a_log, dt_bias, lower_bound, beta, h0, dO, dht, saved, dq,
+                      dk, dv, dx, da_log, ddt_bias, dbeta, dh0, workspace, ws_bytes, stream) -> int:
+    return load().rewy_bwd_kda_gate(ctypes.byref(desc), q, k, v, x, a_log, dt_bias, lower_bound,
+                                    beta, h0, dO, dht, saved, dq, dk, dv, dx, da_log, ddt_bias,
+                                    dbeta, dh0, workspace, ws_bytes, stream)
 
 
 def rewy_recurrent_fwd(desc, q, k, v, g, beta, h0, o, ht, stream) -> int:

@@ -296,6 +296,7 @@ struct GateIn {
   const void* x;
   const float* a_log;
   const float* dt_bias;
+  float lower_bound;  // 0: softplus form; [-5, 0): bounded form
 };
 
 int check_gate_in(const Plan& p, const GateIn* gi) {
@@ -303,6 +304,9 @@ int check_gate_in(const Plan& p, const GateIn* gi) {
   if (!gi->x || !gi->a_log || !gi->dt_bias) return fail(REWY_EINVAL, "x, A_log and dt_bias must be given");
   if (!aligned(gi->x, 16) || !aligned(gi->dt_bias, 16) || !aligned(gi->a_log, 4))
     return fail(REWY_EINVAL, "x and dt_bias must be 16-byte aligned, A_log 4-byte aligned");
+  const float lb = gi->lower_bound;
+  if (!(lb == 0.f || (lb >= -5.f && lb < 0.f)))
+    return fail(REWY_EINVAL, "lower_bound must be 0 (softplus form) or in [-5, 0) (got %g)", (double)lb);
   return REWY_OK;
 }
 
@@ -346,6 +350,7 @@ int forward_impl(const rewy_desc* d, const void* q, const void* k, const void* v
   a.wg = wg; a.ew = ew;
   if (gi) {
     a.g = nullptr; a.gx = gi->x; a.a_log = gi->a_log; a.dt_bias = gi->dt_bias; a.gin = 1;
+    a.gate_lb = gi->lower_bound;
   }
   if (ew && !aligned(wg, 16)) return fail(REWY_EINVAL, "w is not 16-byte aligned");
   a.prep_mode = PREP_FWD_SCAN | PREP_FWD_OUT |
@@ -365,9 +370,10 @@ REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const vo
 
 REWY_API int rewy_fwd_kda_gate(const rewy_desc* d, const void* q, const void* k, const void* v,
                                const void* x, const float* a_log, const float* dt_bias,
-                               const void* beta, const float* h0, void* o, float* ht, void* saved,
-                               void* workspace, size_t ws_bytes, void* stream) {
-  const GateIn gi{x, a_log, dt_bias};
+                               float lower_bound, const void* beta, const float* h0, void* o,
+                               float* ht, void* saved, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  const GateIn gi{x, a_log, dt_bias, lower_bound};
   return forward_impl(d, q, k, v, nullptr, beta, nullptr, &gi, h0, o, ht, saved, workspace,
                       ws_bytes, stream);
 }
@@ -472,6 +478,7 @@ int backward_impl(const rewy_desc* d, const void* q, const void* k, const void* 
   if (gi) {
     a.g = nullptr; a.dg = nullptr;
     a.gx = gi->x; a.a_log = gi->a_log; a.dt_bias = gi->dt_bias; a.gin = 1;
+    a.gate_lb = gi->lower_bound;
     a.dgx = gg->dx; a.da_log = gg->da_log; a.ddt_bias = gg->ddt_bias;
     a.gpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.gpart);
   }
@@ -513,11 +520,12 @@ REWY_API int rewy_bwd(const rewy_desc* d, const void* q, const void* k, const vo
 
 REWY_API int rewy_bwd_kda_gate(const rewy_desc* d, const void* q, const void* k, const void* v,
                                const void* x, const float* a_log, const float* dt_bias,
-                               const void* beta, const float* h0, const void* dO, const float* dht,
-                               const void* saved, void* dq, void* dk, void* dv, void* dx,
-                               float* da_log, float* ddt_bias, void* dbeta, float* dh0,
-                               void* workspace, size_t ws_bytes, void* stream) {
-  const GateIn gi{x, a_log, dt_bias};
+                               float lower_bound, const void* beta, const float* h0,
+                               const void* dO, const float* dht, const void* saved, void* dq,
+                               void* dk, void* dv, void* dx, float* da_log, float* ddt_bias,
+                               void* dbeta, float* dh0, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  const GateIn gi{x, a_log, dt_bias, lower_bound};
   const GateInGrad gg{dx, da_log, ddt_bias};
   return backward_impl(d, q, k, v, nullptr, beta, nullptr, &gi, h0, dO, dht, saved, dq, dk, dv,
                        nullptr, dbeta, nullptr, &gg, dh0, workspace, ws_bytes, stream);

@@ -67,15 +67,22 @@ struct GateCols {
     for (int r = 0; r < RS; ++r)
       G[r] = __uint_as_float(sizeof(X) == 2 ? gld2(b, base + r * rb) : gld4(b, base + r * rb));
   }
-  // g = -ea softplus(x + dtb), ea = exp(A_log) of the head, dtb = dt_bias of
-  // this column (GDN2 spec section 4.4); rows past the end are masked later
+  // g = -ea softplus(x + dtb) (lb = 0; GDN2 spec section 4.4) or the
+  // bounded form g = lb sigmoid(ea (x + dtb)) (lb < 0; GDN2 spec section 3),
+  // ea = exp(A_log) of the head, dtb = dt_bias of this column; rows past the
+  // end are masked later
   template <typename X>
-  __device__ __forceinline__ void kda_gate(float ea, float dtb) {
-#pragma unroll
-    for (int r = 0; r < RS; ++r) {
+  __device__ __forceinline__ void kda_gate(float ea, float dtb, float lb) {
+    auto zr = [&](int r) {
       const uint32_t u = __float_as_uint(G[r]);
-      const float x = sizeof(X) == 2 ? __uint_as_float(u << 16) : __uint_as_float(u);
-      G[r] = -ea * softplus(x + dtb);
+      return (sizeof(X) == 2 ? __uint_as_float(u << 16) : __uint_as_float(u)) + dtb;
+    };
+    if (lb == 0.f) {  // uniform: one form per launch
+#pragma unroll
+      for (int r = 0; r < RS; ++r) G[r] = -ea * softplus(zr(r));
+    } else {
+#pragma unroll
+      for (int r = 0; r < RS; ++r) G[r] = lb * sigmoid_f(ea * zr(r));
     }
   }
   // G2 = log2(e) * inclusive prefix over the chunk's n rows (rows past the end
@@ -222,7 +229,7 @@ __device__ __forceinline__ void score_tiles_pre(const T* sKa, const T* sQa, cons
 // the feature quarter l >> 4; results come back in the C-fragment layout.
 // EW: the erase gate is a vector b (a.beta, [.., K], element type T), taken
 // inside the sum over features instead of beta_i outside it.  GIN: the gate
-// is formed from its pre-activation, g = -exp(A_log) softplus(x + dt_bias).
+// is formed from its pre-activation (softplus or bounded form, Args::gate_lb).
 template <typename T, int K, bool WITH_CQ, bool EW = false, bool GIN = false>
 __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, int n, int I,
                                               const float* sBeta, f32x4& accL, f32x4& accC) {
@@ -244,9 +251,11 @@ __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, 
         if (i >= j && ri < n) {
           if (i > j) {
             float gi = 0.f;
-            if constexpr (GIN)
-              gi = -ea * softplus(tof(reinterpret_cast<const T*>(a.gx)[((t0 + ri) * H + h) * K + k]) +
-                                  a.dt_bias[(int64_t)h * K + k]);
+            if constexpr (GIN) {
+              const float z = tof(reinterpret_cast<const T*>(a.gx)[((t0 + ri) * H + h) * K + k]) +
+                              a.dt_bias[(int64_t)h * K + k];
+              gi = a.gate_lb == 0.f ? -ea * softplus(z) : a.gate_lb * sigmoid_f(ea * z);
+            }
             else if (a.gate == 2) gi = a.g[((t0 + ri) * H + h) * K + k];
             else if (a.gate == 1) gi = a.g[(t0 + ri) * H + h];
             run += gi * LOG2E;

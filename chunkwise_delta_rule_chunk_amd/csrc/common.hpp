@@ -97,6 +97,12 @@ __device__ __forceinline__ void softplus_sigmoid(float z, float& sp, float& sg) 
   sg = (z >= 0.f ? 1.f : e) * __builtin_amdgcn_rcpf(1.f + e);
 }
 
+// logistic sigmoid 1 / (1 + exp(-u)): 0 and 1 in the limits (the reciprocal
+// of infinity is zero)
+__device__ __forceinline__ float sigmoid_f(float u) {
+  return __builtin_amdgcn_rcpf(1.f + fexp2(-u * LOG2E));
+}
+
 // Sum over the 16 lanes of each row of the wave (lanes 16 r .. 16 r + 15),
 // returned to every lane of the row, by DPP lane moves: the two quad
 // permutations [1,0,3,2] and [2,3,0,1], then the half-row mirror (lane i of

@@ -43,11 +43,12 @@ namespace rewy {
 // write gate w per (token, value) in Z = w V; it returns db = (gamma K) Ebar
 // and dw = V P per element (ReWY paper Table 1, GDN2 row) and runs one
 // workgroup per CU.  GIN (vector gate only): the gate was formed from its
-// pre-activation, g = -exp(A_log) softplus(x + dt_bias) (GDN2 spec section
-// 4.4), and the chain rule is taken here: dx = -exp(A_log) sigmoid(x + dt_bias)
-// dg is written in place of dg, and each wave writes its partial sums of
-// dA_log = sum dg g and ddt_bias = sum over tokens of dx for a later
-// reduction over chunks.
+// pre-activation, z = x + dt_bias, as g = -exp(A_log) softplus(z) (GDN2 spec
+// section 4.4) or as the bounded g = lb sigmoid(exp(A_log) z) (section 3), and
+// the chain rule is taken here: dx = (dg/dz) dg is written in place of dg, and
+// each wave writes its partial sums of dA_log (sum of dg g for the softplus
+// form, of dx z for the bounded form) and of ddt_bias = sum over tokens of dx,
+// for a later reduction over chunks.
 template <typename T, int K, int V, int GX>
 __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   constexpr int GATE = GX & 3;
@@ -294,7 +295,8 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   const GBuf bdt = gbuf(a.dt_bias + (int64_t)h * K, GIN ? K * 4 : 0u);
   const GBuf bgp = gbuf(a.gpart + cb * NSUB * K, GIN ? NSUB * K * 4 : 0u);
   const float nea = GIN ? -fexp2(__uint_as_float(gld4(gbuf(a.a_log, H * 4), h * 4)) * LOG2E) : 0.f;
-  float dal = 0.f;                 // gate in the kernel: this lane's part of sum dg softplus(z)
+  const float lb = GIN ? a.gate_lb : 0.f, lbea = -lb * nea;  // bounded form: lb exp(A_log)
+  float dal = 0.f;                 // gate in the kernel: this lane's part of the dA_log sum
   FR pdx = to_frag<T>(zero4());    // dx of the previous (even) feature block
   const int jl = n - 1;  // last valid row
   const FR DmI = pick(Dm, I), HmI = pick(Hm, I), DtmI = pick(Dtm, I), HtmI = pick(Htm, I);
@@ -686,10 +688,11 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
       f32x4 tg = zero4();
       mm16(tg, f32x4{suf[0] + add, suf[1] + add, suf[2] + add, suf[3] + add}, idf);
       if constexpr (GIN) {
-        // dx = -ea sigmoid(z) dg, z = x + dt_bias; the wave's sums over its
-        // valid rows of dg softplus(z) (times -ea at the end: dg g) and, per
-        // feature, of dx.  dg is zeroed on rows past the end (their dx is
-        // not stored), so no other mask is needed.
+        // dx = (dg/dz) dg, z = x + dt_bias: softplus form -ea sigmoid(z),
+        // bounded form lb s (1 - s) ea with s = sigmoid(ea z).  The wave's sums
+        // over its valid rows of dg softplus(z) (times -ea at the end: dg g)
+        // or of dx z, and, per feature, of dx.  dg is zeroed on rows past the
+        // end (their dx is not stored), so no other mask is needed.
         const float rm = I * SUB + f < n ? 1.f : 0.f;
         f32x4 xv, dx, px;
         if constexpr (sizeof(T) == 2) {
@@ -701,15 +704,28 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
           xv = __builtin_bit_cast(f32x4, xr);
         }
         const f32x4 dt = __builtin_bit_cast(f32x4, dtr);
+        if (lb == 0.f) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float sp, sg;
-          softplus_sigmoid(xv[e] + dt[e], sp, sg);
-          const float dgm = tg[e] * rm;
-          dx[e] = nea * sg * dgm;
-          px[e] = row16_sum(dx[e]);  // over the wave's 16 rows
-          dal += dgm * sp;
+          for (int e = 0; e < 4; ++e) {
+            float sp, sg;
+            softplus_sigmoid(xv[e] + dt[e], sp, sg);
+            const float dgm = tg[e] * rm;
+            dx[e] = nea * sg * dgm;
+            dal += dgm * sp;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // s (1 - s) = e / (1 + e)^2 with e = exp(-|u|), u = ea z: no
+            // cancellation where s is close to 1
+            const float z = xv[e] + dt[e];
+            const float ex = fexp2(nea * fabsf(z) * LOG2E), rr = __builtin_amdgcn_rcpf(1.f + ex);
+            dx[e] = lbea * (ex * rr * rr) * (tg[e] * rm);
+            dal += dx[e] * z;
+          }
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) px[e] = row16_sum(dx[e]);  // over the wave's 16 rows
         gst16(bgp, f == 0 ? (uint32_t)((I * K + fb * SUB + 4 * q4) * 4) : OOB, __builtin_bit_cast(uint4, px));
         // stored in pairs of feature blocks, like dq
         const FR yx = to_frag<T>(dx);
@@ -741,7 +757,7 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
 
   // ---- gate in the kernel: the wave's partial sum of dg g ---------------------
   if constexpr (GIN) {
-    float x = row16_sum(dal) * nea;
+    float x = row16_sum(dal) * (lb == 0.f ? nea : 1.f);
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
     const GBuf bga = gbuf(a.gpart + (int64_t)a.nc_max * H * NSUB * K + cb * NSUB, NSUB * 4);

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   // the erase/write form runs one workgroup per CU: the erase gate of the
   // thread's rows and the write gate's v pieces need registers
   constexpr bool EW = MODE & PREP_EW;
-  // the gate formed from its pre-activation: g = -exp(A_log) softplus(x + dt_bias)
+  // the gate formed from its pre-activation x, A_log and dt_bias (Args::gate_lb
+  // selects the softplus or the bounded form)
   constexpr bool GIN = MODE & PREP_GIN;
   constexpr int NTH = 256, NW = NTH / 64;
   constexpr bool BF = std::is_same_v<T, bf16>;
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     if constexpr (GIN) {
       const float ea = fexp2(__uint_as_float(gal) * LOG2E);
 #pragma unroll
-      for (int s = 0; s < NSL; ++s) gc[s].template kda_gate<T>(ea, __uint_as_float(gdtb[s]));
+      for (int s = 0; s < NSL; ++s) gc[s].template kda_gate<T>(ea, __uint_as_float(gdtb[s]), a.gate_lb);
     }
 #pragma unroll
     for (int s = 0; s < NSL; ++s) gc[s].prefix_local(sTot, n);

@@ -29,11 +29,14 @@ struct Args {
   const void* beta;         // beta [BT,H]; in the erase/write form the erase gate b [BT,H,K]
   const void* wg;           // erase/write form: the write gate w [BT,H,V], else nullptr
   int ew;                   // 1 for the erase/write form
-  // gate in the kernel: g = -exp(A_log[h]) softplus(x + dt_bias[h, k]) from
-  // the pre-activation x [BT,H,K] (feature dtype), A_log [H], dt_bias [H,K]
+  // gate in the kernel, from the pre-activation x [BT,H,K] (feature dtype),
+  // A_log [H], dt_bias [H,K], z = x + dt_bias[h, k]:
+  //   gate_lb == 0:  g = -exp(A_log[h]) softplus(z)
+  //   gate_lb < 0:   g = gate_lb sigmoid(exp(A_log[h]) z)   (bounded form)
   const void* gx;
   const float* a_log;
   const float* dt_bias;
+  float gate_lb;
   int gin;                  // 1 when the gate is formed in the kernels
   const float* h0;
   const void* dO;

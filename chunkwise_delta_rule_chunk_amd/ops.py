@@ -141,11 +141,14 @@ def forward_gdn2(q, k, v, g, b, w, *, scale=None, h0=None, cu_seqlens=None, poli
     return o, ht, ctx
 
 
-def forward_kda_gate(q, k, v, x, a_log, dt_bias, beta, *, scale=None, h0=None, cu_seqlens=None,
-                     policy="recompute", output_final_state=True, stream=None, ws=None):
-    """Run rewy_fwd_kda_gate: the vector gate g = -exp(A_log) softplus(x + dt_bias)
-    is formed in the kernels from x [B,T,H,K] (feature dtype), A_log [H] and
-    dt_bias [H,K] (fp32).  Returns (o, ht or None, ctx) for ``backward``."""
+def forward_kda_gate(q, k, v, x, a_log, dt_bias, beta, *, lower_bound=0.0, scale=None, h0=None,
+                     cu_seqlens=None, policy="recompute", output_final_state=True, stream=None,
+                     ws=None):
+    """Run rewy_fwd_kda_gate: the vector gate is formed in the kernels from
+    x [B,T,H,K] (feature dtype), A_log [H] and dt_bias [H,K] (fp32), as
+    g = -exp(A_log) softplus(x + dt_bias) (lower_bound = 0) or
+    g = lower_bound sigmoid(exp(A_log) (x + dt_bias)) (-5 <= lower_bound < 0).
+    Returns (o, ht or None, ctx) for ``backward``."""
     if a_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
         raise TypeError("A_log and dt_bias must be fp32")
     if x.dtype != q.dtype:
@@ -161,11 +164,11 @@ def forward_kda_gate(q, k, v, x, a_log, dt_bias, beta, *, scale=None, h0=None, c
     if ws is None:
         ws = workspace(prob, 0)
     rc = B.rewy_fwd_kda_gate(prob.desc, _p(q), _p(k), _p(v), _p(x), _p(a_log), _p(dt_bias),
-                             _p(beta), _p(h0), _p(o), _p(ht), _p(saved), _p(ws), ws.numel(),
-                             _stream(q.device, stream))
+                             float(lower_bound), _p(beta), _p(h0), _p(o), _p(ht), _p(saved),
+                             _p(ws), ws.numel(), _stream(q.device, stream))
     _check(rc, "rewy_fwd_kda_gate")
-    ctx = dict(prob=prob, q=q, k=k, v=v, g=None, x=x, a_log=a_log, dt_bias=dt_bias, beta=beta,
-               h0=h0, saved=saved)
+    ctx = dict(prob=prob, q=q, k=k, v=v, g=None, x=x, a_log=a_log, dt_bias=dt_bias,
+               lower_bound=float(lower_bound), beta=beta, h0=h0, saved=saved)
     return o, ht, ctx
 
 
@@ -226,8 +229,8 @@ def _backward_kda_gate(ctx, dO, dht=None, *, stream=None, ws=None, want_dh0=None
     dh0 = torch.empty(prob.state_shape, dtype=torch.float32, device=q.device) if want_dh0 else None
     if ws is None:
         ws = workspace(prob, 2)
-    rc = B.rewy_bwd_kda_gate(prob.desc, _p(q), _p(k), _p(v), _p(x), _p(a_log), _p(dt_bias), _p(beta),
-                             _p(h0), _p(dO), _p(dht), _p(ctx["saved"]), _p(dq), _p(dk), _p(dv),
+    rc = B.rewy_bwd_kda_gate(prob.desc, _p(q), _p(k), _p(v), _p(x), _p(a_log), _p(dt_bias),
+                             ctx["lower_bound"], _p(beta), _p(h0), _p(dO), _p(dht), _p(ctx["saved"]), _p(dq), _p(dk), _p(dv),
                              _p(dx), _p(da_log), _p(ddt_bias), _p(dbeta), _p(dh0), _p(ws),
                              ws.numel(), _stream(q.device, stream))
     _check(rc, "rewy_bwd_kda_gate")

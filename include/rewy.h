@@ -132,9 +132,12 @@ int rewy_bwd_gdn2(const rewy_desc *d, const void *q, const void *k, const void *
                   void *workspace, size_t ws_bytes, void *stream);
 
 /* The vector gate formed inside the kernels from its pre-activation (GDN2
- * spec section 4.4, the KDA gate; KDA blog section 6 for the operator):
- *     g[t,h,k] = -exp(A_log[h]) * softplus(x[t,h,k] + dt_bias[h,k]),
- * so the fp32 log-decay g [B,T,H,K] is never read from or written to memory.
+ * spec section 4.4, the KDA gate, and section 3 for the bounded form; KDA
+ * blog section 6 for the operator).  With z = x[t,h,k] + dt_bias[h,k]:
+ *     lower_bound == 0:          g = -exp(A_log[h]) * softplus(z)
+ *     -5 <= lower_bound < 0:     g = lower_bound * sigmoid(exp(A_log[h]) * z)
+ * (any other lower_bound, NaN included, returns REWY_EINVAL), so the fp32
+ * log-decay g [B,T,H,K] is never read from or written to memory.
  * gate must be VECTOR.  x is [B,T,H,K] in the feature dtype, 16-byte aligned;
  * A_log is fp32 [H]; dt_bias is fp32 [H,K], 16-byte aligned.  The result is
  * rewy_fwd's / rewy_bwd's with g formed by the formula above in fp32.  The
@@ -146,11 +149,11 @@ int rewy_bwd_gdn2(const rewy_desc *d, const void *q, const void *k, const void *
  * (descriptor, saved buffer, ownership, errors) is as for rewy_fwd / rewy_bwd;
  * the saved buffer of rewy_fwd_kda_gate serves rewy_bwd_kda_gate only. */
 int rewy_fwd_kda_gate(const rewy_desc *d, const void *q, const void *k, const void *v,
-                      const void *x, const float *a_log, const float *dt_bias,
+                      const void *x, const float *a_log, const float *dt_bias, float lower_bound,
                       const void *beta, const float *h0, void *o, float *ht, void *saved,
                       void *workspace, size_t ws_bytes, void *stream);
 int rewy_bwd_kda_gate(const rewy_desc *d, const void *q, const void *k, const void *v,
-                      const void *x, const float *a_log, const float *dt_bias,
+                      const void *x, const float *a_log, const float *dt_bias, float lower_bound,
                       const void *beta, const float *h0,
                       const void *dO, const float *dht, const void *saved,
                       void *dq, void *dk, void *dv, void *dx, float *da_log, float *ddt_bias,

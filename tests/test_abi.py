@@ -148,23 +148,28 @@ def test_calls_reject_bad_pointers_without_launching(lib):
     assert rc == B.REWY_EINVAL and "aligned" in B.rewy_last_error()
     # gate formed in the kernels: vector gate only, every gate tensor given, aligned
     rc = B.rewy_fwd_kda_gate(_desc(gate=B.REWY_GATE_SCALAR), P(256), P(256), P(256), P(256), P(256),
-                             P(256), P(256), None, P(256), None, None, P(256), 1 << 40, None)
+                             P(256), 0.0, P(256), None, P(256), None, None, P(256), 1 << 40, None)
     assert rc == B.REWY_EINVAL and "VECTOR" in B.rewy_last_error()
-    rc = B.rewy_fwd_kda_gate(d, P(256), P(256), P(256), P(256), None, P(256), P(256), None, P(256),
+    rc = B.rewy_fwd_kda_gate(d, P(256), P(256), P(256), P(256), None, P(256), 0.0, P(256), None, P(256),
                              None, None, P(256), 1 << 40, None)
     assert rc == B.REWY_EINVAL and "A_log" in B.rewy_last_error()
-    rc = B.rewy_fwd_kda_gate(d, P(256), P(256), P(256), P(256), P(256), P(264), P(256), None, P(256),
+    rc = B.rewy_fwd_kda_gate(d, P(256), P(256), P(256), P(256), P(256), P(264), 0.0, P(256), None, P(256),
                              None, None, P(256), 1 << 40, None)
     assert rc == B.REWY_EINVAL and "aligned" in B.rewy_last_error()
-    rc = B.rewy_bwd_kda_gate(d, P(256), P(256), P(256), P(256), P(256), P(256), P(256), None, P(256),
-                             None, None, P(256), P(256), P(256), P(256), None, P(256), P(256), None,
-                             P(256), 1 << 40, None)
+    # the bounded form's lower bound lies in [-5, 0); 0 selects the softplus form
+    for lb in (-5.5, 0.5, float("nan")):
+        rc = B.rewy_fwd_kda_gate(d, P(256), P(256), P(256), P(256), P(256), P(256), lb, P(256), None,
+                                 P(256), None, None, P(256), 1 << 40, None)
+        assert rc == B.REWY_EINVAL and "lower_bound" in B.rewy_last_error(), lb
+    rc = B.rewy_bwd_kda_gate(d, P(256), P(256), P(256), P(256), P(256), P(256), 0.0, P(256), None,
+                             P(256), None, None, P(256), P(256), P(256), P(256), None, P(256), P(256),
+                             None, P(256), 1 << 40, None)
     assert rc == B.REWY_EINVAL and "dA_log" in B.rewy_last_error()
     # the phase-1 size is too small for the backward with the gate in the kernels
     n1 = B.rewy_workspace_bytes(d, 1)
-    rc = B.rewy_bwd_kda_gate(d, P(256), P(256), P(256), P(256), P(256), P(256), P(256), None, P(256),
-                             None, None, P(256), P(256), P(256), P(256), P(256), P(256), P(256), None,
-                             P(256), n1, None)
+    rc = B.rewy_bwd_kda_gate(d, P(256), P(256), P(256), P(256), P(256), P(256), -1.0, P(256), None,
+                             P(256), None, None, P(256), P(256), P(256), P(256), P(256), P(256),
+                             P(256), None, P(256), n1, None)
     assert rc == B.REWY_EWORKSPACE
     del ws
 

@@ -1,6 +1,7 @@
 """GPU parity of the gate formed inside the kernels (rewy_fwd_kda_gate /
 rewy_bwd_kda_gate: g = -exp(A_log) softplus(x + dt_bias), GDN2 spec section
-4.4) against the FP64 oracle: the oracle forms g from the same pre-activation
+4.4, or the bounded g = lower_bound sigmoid(exp(A_log)(x + dt_bias)), section
+3) against the FP64 oracle: the oracle forms g from the same pre-activation
 (rounded to the feature dtype, as the kernels read it), runs its token
 recurrence and reverse mode, and takes dg back to dx, dA_log and ddt_bias with
 its own chain rule.  Every output and gradient within the stated tolerances,
@@ -30,6 +31,16 @@ CASES = [
     ("kdag_bf16_varlen", 1, 330, 2, 64, 64, "bf16", "normal", [0, 1, 64, 128, 193, 330]),
 ]
 
+# the bounded form: name, B, T, H, K, V, dtype, h0, cu, lower_bound, A_log shift
+BOUNDED = [
+    ("kdagb_bf16_k128_lb1", 2, 200, 2, 128, 128, "bf16", "normal", None, -1.0, 0.0),
+    ("kdagb_fp32_k64_lb3", 1, 140, 2, 64, 64, "fp32", "normal", None, -3.0, 0.0),
+    # exp(A_log) ~ 30: most gates sit near the bound -5, sub-chunk ranges near
+    # 16 * 5 / ln 2 = 115 log2 units (the widest the bound allows)
+    ("kdagb_bf16_lb5_strong", 1, 256, 2, 64, 64, "bf16", "normal", None, -5.0, 3.4),
+    ("kdagb_bf16_varlen_lb2", 1, 330, 2, 64, 64, "bf16", "normal", [0, 1, 64, 128, 193, 330], -2.0, 0.0),
+]
+
 
 def _inputs(name, B, T, H, K, V, dt, h0, cu, a_shift=0.0):
     seed = zlib.crc32(name.encode()) % 1000
@@ -40,25 +51,26 @@ def _inputs(name, B, T, H, K, V, dt, h0, cu, a_shift=0.0):
     return inp, x, a_log, inp.dt_bias
 
 
-def _oracle(inp, x, a_log, dt_bias):
+def _oracle(inp, x, a_log, dt_bias, lb=0.0):
     cu = None if inp.cu_seqlens is None else list(inp.cu_seqlens)
-    g = oracle.kda_gate(x, a_log, dt_bias)
+    g = oracle.kda_gate(x, a_log, dt_bias, lb)
     o, ht = oracle.forward(inp.q, inp.k, inp.v, g, inp.beta, scale=inp.scale, h0=inp.h0,
                            cu_seqlens=cu)
     gr = oracle.backward(inp.q, inp.k, inp.v, g, inp.beta, inp.dO, scale=inp.scale, h0=inp.h0,
                          dht=inp.dht, cu_seqlens=cu)
-    dx, da, ddt = oracle.kda_gate_backward(x, a_log, dt_bias, gr["dg"])
+    dx, da, ddt = oracle.kda_gate_backward(x, a_log, dt_bias, gr["dg"], lb)
     return dict(o=o, ht=ht, dq=gr["dq"], dk=gr["dk"], dv=gr["dv"], dx=dx, da_log=da, ddt_bias=ddt,
                 dbeta=gr["dbeta"], dh0=gr["dh0"])
 
 
-def _hip_torch(inp, x, a_log, dt_bias, policy):
+def _hip_torch(inp, x, a_log, dt_bias, policy, lb=0.0):
     from chunkwise_delta_rule_chunk_amd import ops
     dev = torch.device("cuda:0")
     t = inp.to(dev)
     xd, ad, dd = x.to(dev), a_log.to(dev).contiguous(), dt_bias.to(dev).contiguous()
-    o, ht, ctx = ops.forward_kda_gate(t.q, t.k, t.v, xd, ad, dd, t.beta, scale=inp.scale, h0=t.h0,
-                                      cu_seqlens=inp.cu_seqlens, policy=policy)
+    o, ht, ctx = ops.forward_kda_gate(t.q, t.k, t.v, xd, ad, dd, t.beta, lower_bound=lb,
+                                      scale=inp.scale, h0=t.h0, cu_seqlens=inp.cu_seqlens,
+                                      policy=policy)
     gr = ops.backward(ctx, t.dO, t.dht, want_dh0=True)
     torch.cuda.synchronize()
     return dict(o=o, ht=ht, **gr)
@@ -75,6 +87,16 @@ def test_kda_gate_matches_oracle(case, policy):
     say(f"[case] {name} policy={policy}")
     inp, x, a_log, dt_bias = _inputs(*case)
     compare(_np(_hip_torch(inp, x, a_log, dt_bias, policy)), _oracle(inp, x, a_log, dt_bias),
+            TOL[inp.q.dtype], names=NAMES, label=f"{name}/{policy}")
+
+
+@pytest.mark.parametrize("case", BOUNDED, ids=[c[0] for c in BOUNDED])
+@pytest.mark.parametrize("policy", ["recompute", "save"])
+def test_kda_gate_bounded_form_matches_oracle(case, policy):
+    name, lb, shift = case[0], case[9], case[10]
+    say(f"[case] {name} policy={policy} lower_bound={lb}")
+    inp, x, a_log, dt_bias = _inputs(*case[:9], a_shift=shift)
+    compare(_np(_hip_torch(inp, x, a_log, dt_bias, policy, lb)), _oracle(inp, x, a_log, dt_bias, lb),
             TOL[inp.q.dtype], names=NAMES, label=f"{name}/{policy}")
 
 
@@ -117,7 +139,7 @@ def test_kda_gate_strong_decay_takes_pairwise_path():
             TOL[inp.q.dtype], names=NAMES, label="kda-gate-strong-decay")
 
 
-def _hip_no_host_cu(inp, x, a_log, dt_bias):
+def _hip_no_host_cu(inp, x, a_log, dt_bias, lb=0.0):
     """Forward + backward through the C ABI with cu_seqlens on the device only:
     the chunk slots are then an upper bound and some hold no tokens."""
     from chunkwise_delta_rule_chunk_amd import binding as B
@@ -133,13 +155,14 @@ def _hip_no_host_cu(inp, x, a_log, dt_bias):
     o, ht = torch.empty_like(t.v), torch.empty(prob.state_shape, device=dev)
     ws0, ws2 = ops.workspace(prob, 0), ops.workspace(prob, 2)
     assert ws2.numel() > B.rewy_workspace_bytes(prob.desc, 1)
-    ops._check(B.rewy_fwd_kda_gate(prob.desc, p(t.q), p(t.k), p(t.v), p(xd), p(ad), p(dd), p(t.beta),
-                                   p(t.h0), p(o), p(ht), None, p(ws0), ws0.numel(), s), "fwd")
+    ops._check(B.rewy_fwd_kda_gate(prob.desc, p(t.q), p(t.k), p(t.v), p(xd), p(ad), p(dd), lb,
+                                   p(t.beta), p(t.h0), p(o), p(ht), None, p(ws0), ws0.numel(), s),
+               "fwd")
     dq, dk, dv, dx = (torch.empty_like(a) for a in (t.q, t.k, t.v, xd))
     da, ddt, dbeta = torch.empty_like(ad), torch.empty_like(dd), torch.empty_like(t.beta)
     dh0 = torch.empty(prob.state_shape, device=dev)
-    ops._check(B.rewy_bwd_kda_gate(prob.desc, p(t.q), p(t.k), p(t.v), p(xd), p(ad), p(dd), p(t.beta),
-                                   p(t.h0), p(t.dO), p(t.dht), None, p(dq), p(dk), p(dv), p(dx),
+    ops._check(B.rewy_bwd_kda_gate(prob.desc, p(t.q), p(t.k), p(t.v), p(xd), p(ad), p(dd), lb,
+                                   p(t.beta), p(t.h0), p(t.dO), p(t.dht), None, p(dq), p(dk), p(dv), p(dx),
                                    p(da), p(ddt), p(dbeta), p(dh0), p(ws2), ws2.numel(), s), "bwd")
     torch.cuda.synchronize()
     return dict(o=o, ht=ht, dq=dq, dk=dk, dv=dv, dx=dx, da_log=da, ddt_bias=ddt, dbeta=dbeta,
@@ -162,3 +185,18 @@ def test_kda_gate_parameter_gradients_are_deterministic():
     ref = _oracle(inp, x, a_log, dt_bias)
     compare(_np(c), ref, TOL[inp.q.dtype], names=NAMES, label="kda-gate-device-cu")
     compare(_np(a), ref, TOL[inp.q.dtype], names=NAMES, label="kda-gate-host-cu")
+
+
+def test_kda_gate_bounded_form_empty_slots_and_repeatability():
+    """The bounded form with cu_seqlens on the device only (chunk slots without
+    tokens) matches the oracle, and repeated calls give identical parameter
+    gradients."""
+    say("[case] kda gate bounded form, device-only cu_seqlens")
+    cu = [0, 7, 70, 200, 333]
+    inp, x, a_log, dt_bias = _inputs("kdagb_det", 1, 333, 2, 128, 128, "bf16", "normal", cu)
+    a = _hip_no_host_cu(inp, x, a_log, dt_bias, -4.0)
+    b = _hip_no_host_cu(inp, x, a_log, dt_bias, -4.0)
+    for n in ("da_log", "ddt_bias", "dx"):
+        assert torch.equal(a[n], b[n]), n
+    compare(_np(a), _oracle(inp, x, a_log, dt_bias, -4.0), TOL[inp.q.dtype], names=NAMES,
+            label="kda-gate-bounded-device-cu")
