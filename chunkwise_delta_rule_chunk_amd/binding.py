@@ -19,6 +19,7 @@ REWY_RECOMPUTE, REWY_SAVE = 0, 1
 
 EXPORTS = ("rewy_workspace_bytes", "rewy_saved_bytes", "rewy_fwd", "rewy_bwd", "rewy_fwd_gdn2",
            "rewy_bwd_gdn2", "rewy_fwd_kda_gate", "rewy_bwd_kda_gate", "rewy_recurrent_fwd",
+           "rewy_recurrent_fwd_gdn2",
            "rewy_trace_begin", "rewy_trace_end", "rewy_trace_select", "rewy_status_string",
            "rewy_last_error")
 
@@ -78,6 +79,8 @@ def load():
         lib.rewy_bwd_kda_gate.restype = ctypes.c_int
         lib.rewy_recurrent_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P]
         lib.rewy_recurrent_fwd.restype = ctypes.c_int
+        lib.rewy_recurrent_fwd_gdn2.argtypes = [D] + [P] * 10
+        lib.rewy_recurrent_fwd_gdn2.restype = ctypes.c_int
         lib.rewy_trace_begin.argtypes = []
         lib.rewy_trace_begin.restype = ctypes.c_int
         lib.rewy_trace_end.argtypes = [ctypes.POINTER(RewyTraceEntry), ctypes.c_int]
@@ -137,6 +140,10 @@ def rewy_bwd_kda_gate(desc, q, k, v, x, a_log, dt_bias, lower_bound, beta, h0, d
 
 def rewy_recurrent_fwd(desc, q, k, v, g, beta, h0, o, ht, stream) -> int:
     return load().rewy_recurrent_fwd(ctypes.byref(desc), q, k, v, g, beta, h0, o, ht, stream)
+
+
+def rewy_recurrent_fwd_gdn2(desc, q, k, v, g, b, w, h0, o, ht, stream) -> int:
+    return load().rewy_recurrent_fwd_gdn2(ctypes.byref(desc), q, k, v, g, b, w, h0, o, ht, stream)
 
 
 def rewy_trace_begin() -> int:

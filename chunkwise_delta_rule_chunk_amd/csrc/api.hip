@@ -385,12 +385,20 @@ REWY_API int rewy_fwd_gdn2(const rewy_desc* d, const void* q, const void* k, con
   return forward_impl(d, q, k, v, g, b, w, nullptr, h0, o, ht, saved, workspace, ws_bytes, stream);
 }
 
-REWY_API int rewy_recurrent_fwd(const rewy_desc* d, const void* q, const void* k, const void* v,
-                                const float* g, const void* beta, const float* h0, void* o,
-                                float* ht, void* stream) {
+namespace rewy {
+namespace {
+// The token-serial forward; with wg non-null the erase/write form (b in
+// `beta`, w in `wg`, both in the feature dtype).
+int recurrent_impl(const rewy_desc* d, const void* q, const void* k, const void* v,
+                   const float* g, const void* beta, const void* wg, const float* h0, void* o,
+                   float* ht, void* stream) {
   Plan p;
   int rc = make_plan(d, p);
   if (rc) return rc;
+  const bool ew = wg != nullptr;
+  if (ew && d->beta_dtype != d->dtype)
+    return fail(REWY_EUNSUPPORTED, "the erase/write gates must have the feature dtype");
+  if (ew && !aligned(wg, 16)) return fail(REWY_EINVAL, "w is not 16-byte aligned");
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t state_n = (int64_t)p.N * p.H * p.K * p.V;
   if (p.BT == 0) return copy_state(ht, h0, state_n, s);
@@ -407,9 +415,25 @@ REWY_API int rewy_recurrent_fwd(const rewy_desc* d, const void* q, const void* k
   a.B = p.B; a.T = p.T; a.H = p.H; a.K = p.K; a.V = p.V; a.N = p.N;
   a.gate = p.gate; a.beta_f32 = p.beta_f32; a.scale = d->scale; a.cu = d->cu_seqlens;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+  a.wg = wg; a.ew = ew;
   return hip_check(traced("k_recurrent", variant_of(a, p.f32), s,
                           [&] { return launch_recurrent(a, p.f32, s); }),
                    "recurrent forward");
+}
+}  // namespace
+}  // namespace rewy
+
+REWY_API int rewy_recurrent_fwd(const rewy_desc* d, const void* q, const void* k, const void* v,
+                                const float* g, const void* beta, const float* h0, void* o,
+                                float* ht, void* stream) {
+  return recurrent_impl(d, q, k, v, g, beta, nullptr, h0, o, ht, stream);
+}
+
+REWY_API int rewy_recurrent_fwd_gdn2(const rewy_desc* d, const void* q, const void* k,
+                                     const void* v, const float* g, const void* b, const void* w,
+                                     const float* h0, void* o, float* ht, void* stream) {
+  if (!b || !w) return fail(REWY_EINVAL, "b and w must be given");
+  return recurrent_impl(d, q, k, v, g, b, w, h0, o, ht, stream);
 }
 
 namespace rewy {

@@ -103,6 +103,26 @@ __device__ __forceinline__ float sigmoid_f(float u) {
   return __builtin_amdgcn_rcpf(1.f + fexp2(-u * LOG2E));
 }
 
+// Sums across the wave's four 16-lane rows (the same lane of each row), by
+// the row swaps of gfx950 (VALU, no LDS).  v_permlane16_swap on two copies of
+// x returns, in every lane, x of the even and of the odd row of its row pair
+// (0, 1) or (2, 3); v_permlane32_swap returns x of rows (0 or 1) and (2 or
+// 3) with the lane's own parity.
+// x summed over the four rows
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float p = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // pair sum
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// x summed over the rows q >= q4 (the lane's own row q4 and the later ones)
+__device__ __forceinline__ float rows_suffix_sum(float x, int q4) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float p = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // pair sum
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  return ((q4 & 1) ? x : p) + (q4 < 2 ? __uint_as_float(s[1]) : 0.f);
+}
+
 // Sum over the 16 lanes of each row of the wave (lanes 16 r .. 16 r + 15),
 // returned to every lane of the row, by DPP lane moves: the two quad
 // permutations [1,0,3,2] and [2,3,0,1], then the half-row mirror (lane i of

@@ -228,8 +228,7 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
         else gst16(bdw, off, __builtin_bit_cast(uint4, z));
       }
     });
-    dbw += __shfl_xor(dbw, 16);
-    dbw += __shfl_xor(dbw, 32);
+    dbw = rows_sum(dbw);
     if (q4 == 0) sDbw[i] = dbw;
   }
   lds_barrier();  // P complete; A^T is dead
@@ -610,8 +609,7 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
           lamw += kv * SF[e] * tail[e];
         }
       }
-      lamw += __shfl_xor(lamw, 16);
-      lamw += __shfl_xor(lamw, 32);
+      lamw = rows_sum(lamw);
     }
     // dq, dk of this block, transposed by one product with the identity: lane
     // (q4, f) then holds row 16 I + f, features 16 fb + 4 q4 .. + 3, one 8-byte
@@ -661,11 +659,7 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
     if constexpr (GATE == 2) {
       // in-block reverse sum: own rows, then the lane groups after this one
       const float s = gbar[0] + gbar[1] + gbar[2] + gbar[3];
-      float x = s;
-      float y = __shfl_down(x, 16);
-      x += q4 < 3 ? y : 0.f;
-      y = __shfl_down(x, 32);
-      x += q4 < 2 ? y : 0.f;  // sum over lane groups >= q4
+      const float x = rows_suffix_sum(s, q4);  // sum over lane groups >= q4
       float run = x - s;
       f32x4 suf;
       suf[3] = run += gbar[3];
@@ -757,9 +751,7 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
 
   // ---- gate in the kernel: the wave's partial sum of dg g ---------------------
   if constexpr (GIN) {
-    float x = row16_sum(dal) * (lb == 0.f ? nea : 1.f);
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
+    const float x = rows_sum(row16_sum(dal) * (lb == 0.f ? nea : 1.f));
     const GBuf bga = gbuf(a.gpart + (int64_t)a.nc_max * H * NSUB * K + cb * NSUB, NSUB * 4);
     gst4(bga, l == 0 ? (uint32_t)(I * 4) : OOB, __float_as_uint(x));
   }
@@ -778,11 +770,7 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   // ---- scalar gate: reverse sum over the chunk's rows ---------------------------
   if constexpr (GATE == 1) {
     const float s = sufs[0] + sufs[1] + sufs[2] + sufs[3];
-    float x = s;
-    float y = __shfl_down(x, 16);
-    x += q4 < 3 ? y : 0.f;
-    y = __shfl_down(x, 32);
-    x += q4 < 2 ? y : 0.f;
+    const float x = rows_suffix_sum(s, q4);
     float run = x - s;
     sufs[3] = run += sufs[3];
     sufs[2] = run += sufs[2];

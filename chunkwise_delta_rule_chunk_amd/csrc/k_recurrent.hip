@@ -9,15 +9,20 @@
 // then reads them as broadcasts; predict, correct, write and read are lane-
 // local sums over K (four partial sums each for instruction-level
 // parallelism).  Lanes past V work on a valid column and store nothing.
+//
+// EW: the erase/write form (ReWY paper Table 1, GDN2 row; GDN2 spec section 3,
+// the recurrent kernel): r_t = w_t * v_t - S~^T (b_t * k_t) with an erase gate
+// b per key feature (staged as b * k) and a write gate w per value column.
 #include "chunk_common.hpp"
 
 namespace rewy {
 
-template <typename T, int K, int GATE>
+template <typename T, int K, int GATE, bool EW>
 __global__ __launch_bounds__(64) void k_recurrent(Args a) {
   __shared__ __align__(16) float sk[K];  // k_t
   __shared__ __align__(16) float sq[K];  // s q_t
   __shared__ __align__(16) float sa[K];  // exp(g_t) per key row (vector gate)
+  __shared__ __align__(16) float se[EW ? K : 4];  // erase/write form: b_t * k_t
   const int H = a.H, V = a.V;
   const int u = blockIdx.x, n = u / H, h = u - n * H;
   const int l = threadIdx.x, v = blockIdx.y * 64 + l;
@@ -28,6 +33,8 @@ __global__ __launch_bounds__(64) void k_recurrent(Args a) {
   const T* qg = reinterpret_cast<const T*>(a.q);
   const T* kg = reinterpret_cast<const T*>(a.k);
   const T* vg = reinterpret_cast<const T*>(a.v);
+  const T* bg = reinterpret_cast<const T*>(a.beta);  // erase/write form: b [.., K]
+  const T* wg = reinterpret_cast<const T*>(a.wg);    // erase/write form: w [.., V]
   T* og = reinterpret_cast<T*>(a.o);
 
   float S[K];
@@ -40,21 +47,24 @@ __global__ __launch_bounds__(64) void k_recurrent(Args a) {
     for (int r0 = 0; r0 < K; r0 += 64) {
       const int r = r0 + l;
       if (r < K) {
-        sk[r] = tof(kg[th * K + r]);
+        const float kr = tof(kg[th * K + r]);
+        sk[r] = kr;
+        if constexpr (EW) se[r] = tof(bg[th * K + r]) * kr;
         sq[r] = a.scale * tof(qg[th * K + r]);
         if constexpr (GATE == 2) sa[r] = fexp2(a.g[th * K + r] * LOG2E);
       }
     }
     float decay = 1.f;
     if constexpr (GATE == 1) decay = fexp2(a.g[th] * LOG2E);
-    const float b = ld_beta(a.beta, a.beta_f32, th);
+    const float b = EW ? 0.f : ld_beta(a.beta, a.beta_f32, th);
+    const float wv = EW ? tof(wg[th * V + vc]) : 0.f;
     const float vt = tof(vg[th * V + vc]);
     __syncthreads();  // k, s q, exp(g) staged
-    // decay and predict: p = (diag(exp g) S)^T k
+    // decay and predict: p = (diag(exp g) S)^T k  (erase/write form: b * k)
     float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < K; k += 4) {
-      const f32x4 kk = *reinterpret_cast<const f32x4*>(sk + k);
+      const f32x4 kk = *reinterpret_cast<const f32x4*>((EW ? se : sk) + k);
       f32x4 dd;
       if constexpr (GATE == 2) dd = *reinterpret_cast<const f32x4*>(sa + k);
 #pragma unroll
@@ -65,7 +75,8 @@ __global__ __launch_bounds__(64) void k_recurrent(Args a) {
       }
     }
     // correct, write, read
-    const float r = b * (vt - ((p[0] + p[1]) + (p[2] + p[3])));
+    const float pr = (p[0] + p[1]) + (p[2] + p[3]);
+    const float r = EW ? wv * vt - pr : b * (vt - pr);
     float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < K; k += 4) {
@@ -86,16 +97,20 @@ __global__ __launch_bounds__(64) void k_recurrent(Args a) {
   }
 }
 
-template <typename T, int K>
-static hipError_t recurrent_k(const Args& a, hipStream_t s) {
+template <typename T, int K, bool EW>
+static hipError_t recurrent_e(const Args& a, hipStream_t s) {
   const dim3 grid(a.N * a.H, (a.V + 63) / 64), block(64);
   switch (a.gate) {
-    case 0: hipLaunchKernelGGL((k_recurrent<T, K, 0>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((k_recurrent<T, K, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_recurrent<T, K, 2>), grid, block, 0, s, a); break;
+    case 0: hipLaunchKernelGGL((k_recurrent<T, K, 0, EW>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_recurrent<T, K, 1, EW>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_recurrent<T, K, 2, EW>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+template <typename T, int K>
+static hipError_t recurrent_k(const Args& a, hipStream_t s) {
+  return a.ew ? recurrent_e<T, K, true>(a, s) : recurrent_e<T, K, false>(a, s);
 }
 
 template <typename T>

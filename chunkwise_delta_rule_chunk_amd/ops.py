@@ -121,6 +121,20 @@ def recurrent_forward(q, k, v, g, beta, *, scale=None, h0=None, cu_seqlens=None,
     return o, ht
 
 
+def recurrent_forward_gdn2(q, k, v, g, b, w, *, scale=None, h0=None, cu_seqlens=None,
+                           output_final_state=True, stream=None):
+    """Run rewy_recurrent_fwd_gdn2 (token-serial, erase gate b [B,T,H,K] and
+    write gate w [B,T,H,V] in the feature dtype).  Returns (o, ht or None)."""
+    prob = make_problem(q, v, g, b, scale=scale, cu_seqlens=cu_seqlens)
+    o = torch.empty_like(v)
+    ht = torch.empty(prob.state_shape, dtype=torch.float32, device=q.device) \
+        if output_final_state else None
+    rc = B.rewy_recurrent_fwd_gdn2(prob.desc, _p(q), _p(k), _p(v), _p(g), _p(b), _p(w), _p(h0),
+                                   _p(o), _p(ht), _stream(q.device, stream))
+    _check(rc, "rewy_recurrent_fwd_gdn2")
+    return o, ht
+
+
 def forward_gdn2(q, k, v, g, b, w, *, scale=None, h0=None, cu_seqlens=None, policy="recompute",
                  output_final_state=True, stream=None, ws=None):
     """Run rewy_fwd_gdn2: independent erase gate b [B,T,H,K] and write gate w

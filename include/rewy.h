@@ -174,6 +174,15 @@ int rewy_recurrent_fwd(const rewy_desc *d, const void *q, const void *k, const v
                        const float *g, const void *beta, const float *h0,
                        void *o, float *ht, void *stream);
 
+/* Token-serial forward of the erase/write form (GDN2 spec section 3, the
+ * recurrent kernel; ReWY paper Table 1, GDN2 row): r_t = w_t * v_t -
+ * S~^T (b_t * k_t), S = S~ + k_t r_t^T, with b [B,T,H,K] and w [B,T,H,V] in the
+ * feature dtype (beta_dtype must equal dtype, else REWY_EUNSUPPORTED).  All
+ * else as rewy_recurrent_fwd; with b = w = beta it computes the same as it. */
+int rewy_recurrent_fwd_gdn2(const rewy_desc *d, const void *q, const void *k, const void *v,
+                            const float *g, const void *b, const void *w, const float *h0,
+                            void *o, float *ht, void *stream);
+
 /* Per-kernel timing (a tracing aid: device events, as in the ReWY paper's timing
  * protocol).  After rewy_trace_begin(), calls made by this thread
  * record a HIP event pair on the call's stream around every kernel they

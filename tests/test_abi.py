@@ -146,6 +146,12 @@ def test_calls_reject_bad_pointers_without_launching(lib):
     assert rc == B.REWY_EINVAL and "g must be given" in B.rewy_last_error()
     rc = B.rewy_recurrent_fwd(d, P(256), P(256), P(264), P(256), P(256), None, P(256), None, None)
     assert rc == B.REWY_EINVAL and "aligned" in B.rewy_last_error()
+    rc = B.rewy_recurrent_fwd_gdn2(d, P(256), P(256), P(256), P(256), None, P(256), None, P(256),
+                                   None, None)
+    assert rc == B.REWY_EINVAL and "b and w" in B.rewy_last_error()
+    rc = B.rewy_recurrent_fwd_gdn2(_desc(beta_dtype=B.REWY_F32), P(256), P(256), P(256), P(256),
+                                   P(256), P(256), None, P(256), None, None)
+    assert rc == B.REWY_EUNSUPPORTED
     # gate formed in the kernels: vector gate only, every gate tensor given, aligned
     rc = B.rewy_fwd_kda_gate(_desc(gate=B.REWY_GATE_SCALAR), P(256), P(256), P(256), P(256), P(256),
                              P(256), 0.0, P(256), None, P(256), None, None, P(256), 1 << 40, None)

@@ -87,3 +87,67 @@ def test_recurrent_agrees_with_the_chunked_forward():
     err_h = (torch.linalg.norm((ht_r - ht_c).double()) / torch.linalg.norm(ht_c.double())).item()
     say(f"[parity] recurrent-vs-chunked o={err_o:.2e} ht={err_h:.2e}")
     assert err_o < TOL[inp.q.dtype] and err_h < TOL[inp.q.dtype]
+
+
+EW_CASES = [
+    # name, B, T, H, K, V, gate, dtype, h0, cu
+    ("recew_bf16_vector_k128", 2, 37, 2, 128, 128, "vector", "bf16", "normal", None),
+    ("recew_bf16_scalar_k64_v32", 3, 20, 2, 64, 32, "scalar", "bf16", "zero", None),
+    ("recew_fp32_none_k32_v64", 1, 30, 2, 32, 64, "none", "fp32", "normal", None),
+    ("recew_bf16_varlen", 1, 100, 2, 64, 64, "vector", "bf16", "normal", [0, 1, 1, 40, 100]),
+]
+
+
+def _ew_gates(inp, seed):
+    gen = torch.Generator().manual_seed(seed)
+    b = torch.sigmoid(torch.randn(*inp.k.shape, generator=gen)).to(inp.q.dtype)
+    w = torch.sigmoid(torch.randn(*inp.v.shape, generator=gen)).to(inp.q.dtype)
+    return b, w
+
+
+@pytest.mark.parametrize("case", EW_CASES, ids=[c[0] for c in EW_CASES])
+def test_recurrent_erase_write_matches_oracle(case):
+    """rewy_recurrent_fwd_gdn2: erase gate b per key feature and write gate w
+    per value column (GDN2 spec section 3) against the oracle's recurrence
+    with the same separate gates."""
+    from chunkwise_delta_rule_chunk_amd import ops
+    name, B, T, H, K, V, gate, dt, h0, cu = case
+    say(f"[case] {name}")
+    seed = zlib.crc32(name.encode()) % 1000
+    inp = workloads.make_inputs(B, T, H, K, V, gate=gate, dtype=dt, h0=h0, cu_seqlens=cu, seed=seed)
+    b, w = _ew_gates(inp, seed + 1)
+    dev = torch.device("cuda:0")
+    x = inp.to(dev)
+    o, ht = ops.recurrent_forward_gdn2(x.q, x.k, x.v, x.g, b.to(dev), w.to(dev), scale=inp.scale,
+                                       h0=x.h0, cu_seqlens=inp.cu_seqlens)
+    torch.cuda.synchronize()
+    cuv = None if cu is None else list(cu)
+    ro, rht = oracle.forward(inp.q, inp.k, inp.v, inp.g, None, scale=inp.scale, h0=inp.h0,
+                             cu_seqlens=cuv, erase=b, write=w)
+    compare(dict(o=o.double().cpu().numpy(), ht=ht.double().cpu().numpy()), dict(o=ro, ht=rht),
+            TOL[inp.q.dtype], names=("o", "ht"), label=name)
+
+
+def test_recurrent_erase_write_agrees_with_chunked_and_shared_beta():
+    """The token-serial erase/write forward agrees with the chunked one
+    (rewy_fwd_gdn2) on the same inputs, and with b = w = beta it reproduces
+    the shared-beta token-serial forward."""
+    from chunkwise_delta_rule_chunk_amd import ops
+    say("[case] recurrent erase/write vs chunked and vs shared beta")
+    inp = workloads.make_inputs(2, 150, 2, 64, 64, gate="vector", dtype="fp32", h0="normal", seed=21)
+    b, w = _ew_gates(inp, 22)
+    dev = torch.device("cuda:0")
+    x = inp.to(dev)
+    bd, wd = b.to(dev), w.to(dev)
+    o1, ht1 = ops.recurrent_forward_gdn2(x.q, x.k, x.v, x.g, bd, wd, scale=inp.scale, h0=x.h0)
+    o2, ht2, _ = ops.forward_gdn2(x.q, x.k, x.v, x.g, bd, wd, scale=inp.scale, h0=x.h0)
+    bb = x.beta[..., None].expand(*x.k.shape).contiguous()
+    wb = x.beta[..., None].expand(*x.v.shape).contiguous()
+    o3, ht3 = ops.recurrent_forward_gdn2(x.q, x.k, x.v, x.g, bb, wb, scale=inp.scale, h0=x.h0)
+    o4, ht4 = ops.recurrent_forward(x.q, x.k, x.v, x.g, x.beta, scale=inp.scale, h0=x.h0)
+    torch.cuda.synchronize()
+    rel = lambda a, r: (torch.linalg.norm((a - r).double()) / torch.linalg.norm(r.double())).item()
+    errs = dict(o_chunk=rel(o1, o2), ht_chunk=rel(ht1, ht2), o_beta=rel(o3, o4), ht_beta=rel(ht3, ht4))
+    say("[parity] recurrent-ew " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert errs["o_chunk"] < 1e-4 and errs["ht_chunk"] < 1e-4, errs
+    assert errs["o_beta"] < 1e-6 and errs["ht_beta"] < 1e-6, errs
