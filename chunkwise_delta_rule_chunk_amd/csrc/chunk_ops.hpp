@@ -40,6 +40,14 @@ struct GateCols {
     c = tid % KC;
     seg = (tid / KC) % NSUB;
   }
+  // Column pairs: slot s (0 or 1) of thread tid < 2 KC takes column
+  // 2 (tid % (KC/2)) + s of sub-chunk tid / (KC/2), so a thread's two slots are
+  // adjacent columns of the same 16 rows (element pairs are contiguous).
+  __device__ __forceinline__ void init_pair(int tid, int s) {
+    on = tid < 2 * KC;
+    c = 2 * (tid % (KC / 2)) + s;
+    seg = (tid / (KC / 2)) % NSUB;
+  }
   // raw natural-log gates, features [k0, k0 + KC), of the chunk's n >= 1 rows,
   // through a bounds-checked buffer: rows past the end (and every row without
   // a gate) read as zero.  One unconditional load per row, so the loads' wait

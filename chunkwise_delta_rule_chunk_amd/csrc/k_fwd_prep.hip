@@ -85,6 +85,10 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   using GC = GateCols<K>;
   constexpr int RS = GC::RS;
   constexpr int NSL = (GC::NG + NTH - 1) / NTH;  // gate slots (column, segment) per thread
+  // bf16 with two slots per thread: the slots are adjacent columns of the same
+  // rows, so the element-wise phase moves bf16 pairs (4-byte LDS and global
+  // accesses, one conversion per pair)
+  constexpr bool PAIR = BF && NSL == 2;
   constexpr int VE = 16 / (int)sizeof(T);
 
   constexpr int SZ_K = CH * PK * (int)sizeof(T), SZ_L = CH * PL * 4;
@@ -117,7 +121,10 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   // of the elementwise phase (their last use) to the next item's prefix
   GC gc[NSL];
 #pragma unroll
-  for (int s = 0; s < NSL; ++s) gc[s].init(threadIdx.x + s * NTH);
+  for (int s = 0; s < NSL; ++s) {
+    if constexpr (PAIR) gc[s].init_pair(threadIdx.x, s);
+    else gc[s].init(threadIdx.x + s * NTH);
+  }
   TileRegs<T, CH, K, NTH> pk, pq;
   // v for Z^T: bf16 threads take rows (2p, 2p + 1), p = slot % 32, and the
   // eight columns from 8 (slot / 32), so each Z^T write is one 4-byte pair of
@@ -249,13 +256,108 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
                                                   : nullptr);
     lds_barrier();
 
+    // Element-wise phase of a column pair (PAIR): the thread's two slots are
+    // columns c0 = gc[0].c (even) and c0 + 1 of the same 16 rows, so every
+    // LDS access, conversion and 2-byte output store of the one-column phase
+    // below becomes one access of a bf16 pair.  Same arithmetic, same outputs.
+    auto elementwise_pairs = [&]() {
+      if (!gc[0].on) return;
+      int c0 = gc[0].c;
+      asm volatile("" : "+v"(c0));
+      const int sg = gc[0].seg;
+      const int r0 = __builtin_amdgcn_readfirstlane(sg * RS);
+      const bool seg_live = r0 < n;
+      float rA[2], rB[2], cA[2], cB[2], gn[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        gn[j] = sGn[c0 + j];
+        rA[j] = seg_live ? ref_recv(sMid, sGf, sFlag, sg, K, c0 + j) : gn[j];
+        rB[j] = seg_live ? ref_send(sMid, sGl, sFlag, sg, K, c0 + j) : gn[j];
+        cA[j] = fexp2(rA[j]);
+        cB[j] = fexp2(gn[j] - rB[j]);
+      }
+      const float bs = a.scale;
+      constexpr int KGF = 4 * VE, NGTF = CH / KGF, NGKF = K / KGF;
+      constexpr int NKBQ = K / SUB, GPQ = 16 / (4 * (int)sizeof(T));
+      T* Ftd = reinterpret_cast<T*>(a.Ft) + cb * K * CH;
+      T* Qgtd = reinterpret_cast<T*>(a.Qgt) + cb * K * CH;
+      T* Fd = reinterpret_cast<T*>(a.F) + cb * CH * K +
+              ((sg * NGKF + c0 / KGF) * 64 + ((c0 % KGF) / VE) * 16) * VE + c0 % VE;
+      T* Qgd = reinterpret_cast<T*>(a.Qg) + cb * CH * K +
+               ((((int64_t)sg * (NKBQ / GPQ) + (c0 / SUB) / GPQ) * 64 + 16 * ((c0 % SUB) / 4)) * GPQ +
+                (c0 / SUB) % GPQ) * 4 + c0 % 4;
+      auto pk2 = [](float x, float y) { return __builtin_bit_cast(uint32_t, bf16x2{(bf16)x, (bf16)y}); };
+#pragma unroll
+      for (int r8 = 0; r8 < RS; r8 += VE) {
+        union {
+          uint4 u;
+          T e[VE];
+        } ft[2], qt[2], et[2];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const int r = r8 + e, row = r0 + r;
+          const uint32_t k2 = *reinterpret_cast<const uint32_t*>(sK + row * PK + c0);
+          const uint32_t q2 = *reinterpret_cast<const uint32_t*>(sQ + row * PK + c0);
+          const float kr[2] = {__uint_as_float(k2 << 16), __uint_as_float(k2 & 0xffff0000u)};
+          const float qr[2] = {__uint_as_float(q2 << 16), __uint_as_float(q2 & 0xffff0000u)};
+          float vKa[2], vQa[2], vKc[2], vQg[2], vF[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float G = gc[j].G[r];
+            const float ea = fexp2(G - rA[j]), eb = fexp2(rB[j] - G);
+            float bk;  // erase factor of this row (and feature)
+            if constexpr (EW) bk = __uint_as_float(bwr[j][r] << 16);
+            else bk = sBeta[row];
+            vKa[j] = bk * kr[j] * ea;
+            vQa[j] = bs * qr[j] * ea;
+            vKc[j] = kr[j] * eb;
+            vQg[j] = vQa[j] * cA[j];
+            vF[j] = vKc[j] * cB[j];
+            et[j].e[e] = fromf<T>(vKa[j] * cA[j]);
+            ft[j].e[e] = fromf<T>(vF[j]);
+            qt[j].e[e] = fromf<T>(vQg[j]);
+          }
+          if constexpr (MODE & PREP_FWD_OUT) *reinterpret_cast<uint32_t*>(Qgd + r * GPQ * 4) = pk2(vQg[0], vQg[1]);
+          if constexpr (MODE & PREP_BWD_SCAN) *reinterpret_cast<uint32_t*>(Fd + r * VE) = pk2(vF[0], vF[1]);
+          *reinterpret_cast<uint32_t*>(sKa + row * PK + c0) = pk2(vKa[0], vKa[1]);
+          *reinterpret_cast<uint32_t*>(sQ + row * PK + c0) = pk2(vQa[0], vQa[1]);
+          *reinterpret_cast<uint32_t*>(sK + row * PK + c0) = pk2(vKc[0], vKc[1]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = c0 + j;
+          etr[j][r8 / VE] = et[j].u;  // E^T reaches LDS in S5
+          const int tk = r0 + r8, q = tk / KGF, gq = (tk % KGF) / VE;
+          if constexpr (MODE & PREP_FWD_SCAN)
+            *reinterpret_cast<uint4*>(Ftd + (((col / SUB) * NGTF + q) * 64 + gq * 16 + col % SUB) * VE) = ft[j].u;
+          if constexpr (MODE & PREP_BWD_SCAN)
+            *reinterpret_cast<uint4*>(Qgtd + (((col / SUB) * NGTF + q) * 64 + gq * 16 + col % SUB) * VE) = qt[j].u;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = c0 + j;
+        if constexpr (MODE & PREP_BWD_CHUNK) {
+          float* G2d = a.gate == 2 ? a.G2t + cb * K * CH + ((int64_t)sg * K + col) * SUB
+                                   : (a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr);
+          if (G2d)
+#pragma unroll
+            for (int r4 = 0; r4 < RS; r4 += 4)
+              *reinterpret_cast<f32x4*>(G2d + r4) = f32x4{gc[j].G[r4], gc[j].G[r4 + 1], gc[j].G[r4 + 2], gc[j].G[r4 + 3]};
+        }
+        if constexpr ((MODE & (PREP_FWD_SCAN | PREP_BWD_SCAN)) != 0)
+          if (sg == 0) a.glast[cb * K + col] = gn[j];
+      }
+    };
+
     // ---- S2: pair factors; element-wise outputs and centred operands --------
     // the prefix totals are dead: L starts from zeros (strict upper parts and
     // the blocks past the chunk's end are never written)
     for (int idx = tid; idx < CH * PL / 4; idx += NTH) reinterpret_cast<f32x4*>(sL)[idx] = zero4();
     pair_factors<K>(sMid, sGf, sGl, sFlag, sFac, n, tid, NTH);
+    if constexpr (PAIR) elementwise_pairs();
 #pragma unroll
-    for (int s = 0; s < NSL; ++s) {
+    for (int s = 0; s < (PAIR ? 0 : NSL); ++s) {
       // one slot at a time: interleaving the slots' element-wise work would
       // double the registers it holds live
       __builtin_amdgcn_sched_barrier(0);
