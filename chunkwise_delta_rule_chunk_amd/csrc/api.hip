@@ -98,7 +98,7 @@ int make_plan(const rewy_desc* d, Plan& p) {
 // The backward with the gate formed in the kernel appends the per-wave partial
 // sums of the gate parameters' gradients to its workspace (phase 2).
 struct Layout {
-  size_t chunks, seqoff;
+  size_t chunks, seqoff, seqord;
   size_t glast, hbuf, R;             // read by output and backward
   size_t W, Ft, U;                   // forward scan operands
   size_t Qg, Cq;                     // output-product operands
@@ -129,6 +129,7 @@ Layout layout(const Plan& p) {
   };
   L.chunks = take(off, nc * sizeof(ChunkInfo));
   L.seqoff = take(off, (size_t)(p.N + 1) * 4);
+  L.seqord = take(off, (size_t)p.N * 4);
   const size_t head = off;
   const bool save = p.policy == REWY_SAVE;
   size_t s = save ? 0 : off;
@@ -190,6 +191,7 @@ void fill_common(Args& a, const Plan& p, const rewy_desc* d, char* ws, char* sv,
   a.gate = p.gate; a.beta_f32 = p.beta_f32; a.scale = d->scale; a.cu = d->cu_seqlens;
   a.chunks = reinterpret_cast<ChunkInfo*>(ws + L.chunks);
   a.seqoff = reinterpret_cast<int*>(ws + L.seqoff);
+  a.seqord = reinterpret_cast<int*>(ws + L.seqord);
   char* fs = p.policy == REWY_SAVE ? sv : ws;  // where the saved set lives
   a.glast = reinterpret_cast<float*>(fs + L.glast);
   a.hbuf = fs + L.hbuf; a.R = fs + L.R;

@@ -30,6 +30,25 @@ __global__ void k_chunk_table(Args a) {
   }
   __syncthreads();  // full fence: the other threads read seqoff from global memory
   const int total = s_total;
+  // Scan order: sequences by chunk count, longest first (ties by index), so
+  // that the scans dispatch their longest serial chains first.  Identity
+  // without cu_seqlens (equal lengths) and beyond 1024 sequences.
+  {
+    __shared__ int s_cnt[1024];
+    const bool sort = a.cu && a.N <= 1024;
+    if (sort)
+      for (int i = threadIdx.x; i < a.N; i += blockDim.x) s_cnt[i] = a.seqoff[i + 1] - a.seqoff[i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.N; i += blockDim.x) {
+      int rank = i;
+      if (sort) {
+        const int ni = s_cnt[i];
+        rank = 0;
+        for (int j = 0; j < a.N; ++j) rank += (s_cnt[j] > ni) || (s_cnt[j] == ni && j < i);
+      }
+      a.seqord[rank] = i;
+    }
+  }
   for (int c = threadIdx.x; c < a.nc_max; c += blockDim.x) {
     ChunkInfo ci = {0, 0, 0, 0};
     if (c < total) {

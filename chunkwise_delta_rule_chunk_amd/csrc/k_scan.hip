@@ -57,7 +57,8 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
   __shared__ __align__(16) T sRt[BV * PA];        // R_c as operand, [v][i]
 
   const int H = a.H;
-  const int n = u / H, h = u - n * H;
+  const int rk = u / H, h = u - rk * H;
+  const int n = a.seqord[rk];  // the rk-th longest sequence
   const int w = wave_id(), tid = threadIdx.x, l = lane_id();
   const int r16 = l & 15, g = l >> 4;
   const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
@@ -295,7 +296,8 @@ __device__ __forceinline__ void bwd_scan_wg(const Args& a, const int u, const in
   __shared__ __align__(16) T sRbt[BV * PA];     // Rbar_c as operand, [v][i]
 
   const int H = a.H;
-  const int n = u / H, h = u - n * H;
+  const int rk = u / H, h = u - rk * H;
+  const int n = a.seqord[rk];  // the rk-th longest sequence
   const int w = wave_id(), tid = threadIdx.x, l = lane_id();
   const int r16 = l & 15, g = l >> 4;
   const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
@@ -468,24 +470,47 @@ __device__ __forceinline__ void bwd_scan_wg(const Args& a, const int u, const in
   final_out();
 }
 
+// Workgroup id -> (unit, value tile), units u = rank * H + head in the scan
+// order (longest sequences first, Args::seqord).  Eight consecutive units form
+// a group whose NSC scans x NT value tiles are dispatched together, and unit u
+// runs on XCD u % 8 (workgroup ids go round-robin over the eight XCDs), so the
+// tiles of one (sequence, head) share that XCD's L2.  Ids past the last unit
+// exit at once.
+template <int NT, int NSC>
+__device__ __forceinline__ bool scan_unit(const Args& a, int& u, int& vt, int& sc) {
+  const int id = blockIdx.x, grp = id / (8 * NT * NSC), rem = id - grp * 8 * NT * NSC;
+  sc = rem / (8 * NT);
+  vt = (rem / 8) % NT;
+  u = grp * 8 + (rem & 7);
+  return u < a.N * a.H;
+}
+inline dim3 scan_grid(const Args& a, int nt, int nsc) {
+  return dim3(((a.N * a.H + 7) / 8) * 8 * nt * nsc);
+}
+
 template <typename T, int K, int V, int BV, int OUT>
 __global__ __launch_bounds__(256) void k_fwd_scan(Args a) {
-  fwd_scan_wg<T, K, V, BV, OUT>(a, blockIdx.x, blockIdx.y);
+  int u, vt, sc;
+  if (scan_unit<V / BV, 1>(a, u, vt, sc)) fwd_scan_wg<T, K, V, BV, OUT>(a, u, vt);
 }
 template <typename T, int K, int V, int BV>
 __global__ __launch_bounds__(256) void k_bwd_scan(Args a) {
-  bwd_scan_wg<T, K, V, BV>(a, blockIdx.x, blockIdx.y);
+  int u, vt, sc;
+  if (scan_unit<V / BV, 1>(a, u, vt, sc)) bwd_scan_wg<T, K, V, BV>(a, u, vt);
 }
 // Both scans of the backward under recompute in one launch: they read
-// disjoint operands and write disjoint outputs, so the forward recompute scan
-// (grid z = 0) and the reverse scan (z = 1) run side by side, each on its own
-// share of the CUs.  Wider value tiles halve the operand reads of each scan.
+// disjoint operands and write disjoint outputs, so the reverse scan (the
+// longer one, dispatched first within each group of units) and the forward
+// recompute scan run side by side, each on its own share of the CUs.  Wider
+// value tiles halve the operand reads of each scan.
 template <typename T, int K, int V, int BV>
 __global__ __launch_bounds__(256) void k_scans(Args a) {
-  if (blockIdx.z == 0)
-    fwd_scan_wg<T, K, V, BV, SCAN_NATURAL>(a, blockIdx.x, blockIdx.y);
+  int u, vt, sc;
+  if (!scan_unit<V / BV, 2>(a, u, vt, sc)) return;
+  if (sc == 0)
+    bwd_scan_wg<T, K, V, BV>(a, u, vt);
   else
-    bwd_scan_wg<T, K, V, BV>(a, blockIdx.x, blockIdx.y);
+    fwd_scan_wg<T, K, V, BV, SCAN_NATURAL>(a, u, vt);
 }
 
 int scan_bv(const Args& a, int f32) {
@@ -497,7 +522,7 @@ int scan_bv(const Args& a, int f32) {
 
 template <typename T, int BV>
 static hipError_t fwd_scan_bv(const Args& a, hipStream_t s) {
-  const dim3 grid(a.N * a.H, a.V / BV), block(256);
+  const dim3 grid = scan_grid(a, a.V / BV, 1), block(256);
 #define REWY_SCAN_CASE(K_, V_)                                                  \
   case K_ * 1000 + V_:                                                          \
     if constexpr (kv_ok<T, K_, V_>() && V_ >= BV && K_ * BV >= 1024 && \
@@ -523,7 +548,7 @@ static hipError_t fwd_scan_bv(const Args& a, hipStream_t s) {
 
 template <typename T, int BV>
 static hipError_t bwd_scan_bv(const Args& a, hipStream_t s) {
-  const dim3 grid(a.N * a.H, a.V / BV), block(256);
+  const dim3 grid = scan_grid(a, a.V / BV, 1), block(256);
 #define REWY_SCAN_CASE(K_, V_)                                                  \
   case K_ * 1000 + V_:                                                          \
     if constexpr (kv_ok<T, K_, V_>() && V_ >= BV && K_ * BV >= 1024 && \
@@ -555,7 +580,7 @@ hipError_t launch_bwd_scan(const Args& a, int f32, hipStream_t s) {
 
 template <typename T, int BV>
 static hipError_t scans_bv(const Args& a, hipStream_t s) {
-  const dim3 grid(a.N * a.H, a.V / BV, 2), block(256);
+  const dim3 grid = scan_grid(a, a.V / BV, 2), block(256);
 #define REWY_SCAN_CASE(K_, V_)                                                  \
   case K_ * 1000 + V_:                                                          \
     if constexpr (kv_ok<T, K_, V_>() && V_ >= BV && K_ * BV >= 1024 &&          \

@@ -21,6 +21,7 @@ struct Args {
   // chunk index (workspace)
   ChunkInfo* chunks;        // [nc_max]
   int* seqoff;              // [N+1] first chunk slot of each sequence
+  int* seqord;              // [N] scan order: sequences by chunk count, longest first
   // inputs
   const void* q;
   const void* k;

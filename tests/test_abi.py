@@ -81,7 +81,7 @@ def test_workspace_sizes_follow_the_layout(lib):
     up = lambda x: (x + 255) // 256 * 256
     tokK, tokV = up(BT * H * K * e), up(BT * H * V * e)
     tileK, tile64 = up(nc * H * K * 64 * e), up(nc * H * 64 * 64 * e)
-    head = up(nc * 16) + up(2 * 4)
+    head = up(nc * 16) + up(2 * 4) + up(1 * 4)  # chunk records, seqoff [N+1], scan order [N]
     tileV = up(nc * H * V * 64 * e)
     shared = up(nc * H * K * 4) + up(nc * H * K * V * e) + tileV       # glast, hbuf, R
     scan = tokK + tileK + tokV                                          # W, Ft, U
