@@ -320,17 +320,24 @@ def main():
     # events (recorded on their launch stream), so its average duration is
     # measured over exactly the timed launches while the other kernels run
     # without event overhead.
+    # One device event at every step boundary (on the stream the kernels run
+    # on) gives the distribution of single-step times as well.
     torch.cuda.synchronize()
     binding.rewy_trace_select(dom_stage)
     binding.rewy_trace_begin()
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    bounds[0].record()
+    for i in range(args.steps):
         step()
+        bounds[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     tr = binding.rewy_trace_end()
     binding.rewy_trace_select(None)
     ms = elapsed * 1e3 / args.steps
+    step_ms = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps))
+    pct = lambda p: step_ms[min(len(step_ms) - 1, int(round(p * (len(step_ms) - 1))))]
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
     timed = {name: (tot / cnt, cnt / args.steps) for name, tot, cnt in tr}
     dom_avg, dom_per = timed[dom]
@@ -366,6 +373,8 @@ def main():
                    "parallelism": "single-gpu"},
         "tflops": tflops, "pct_bf16_peak": 100 * tflops / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "step_ms_p10": pct(0.1), "step_ms_median": pct(0.5), "step_ms_p90": pct(0.9),
+        "step_ms_source": "device events at every step boundary of the timed region",
         "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
         "bwd_pct_bf16_peak": 100 * f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "flops_per_step": {"forward": f_fwd, "backward": f_bwd, "recompute_executed": f_rc},
