@@ -115,8 +115,9 @@ struct GateCols {
 
 // Sub-chunk statistics from the register-resident prefix sums: midpoint, first
 // row and last valid row per (J, feature) into sMid/sGf/sGl [NSUB][KC], G2 at
-// the chunk's last valid row into sGn [KC], and sFlag[J] set when a feature's
-// range exceeds CENTRE_MAX_RANGE (sFlag zero on entry).  With gst non-null the
+// the chunk's last valid row into sGn [KC], and sFlag[J][fb] (16-feature
+// block fb, [NSUB][KC/16]) set when a feature of the block ranges over more
+// than CENTRE_MAX_RANGE (sFlag zero on entry).  With gst non-null the
 // record {first, last, midpoint, range} of every non-empty (J, feature) is also
 // written to gst[J * KC + feature].  No barrier inside.
 template <int KC>
@@ -143,22 +144,31 @@ __device__ __forceinline__ void subchunk_stats_regs(const GateCols<KC>& gc, int 
   sGf[idx] = gc.G[0];
   sGl[idx] = gl;
   if (last == n - 1) sGn[gc.c] = gl;
-  if (mx - mn > CENTRE_MAX_RANGE) sFlag[J] = 1;  // benign race: same value
+  if (mx - mn > CENTRE_MAX_RANGE) sFlag[J * (KC / SUB) + gc.c / SUB] = 1;  // benign race: same value
   if (gst) gst[idx] = f32x4{gc.G[0], gl, 0.5f * (mx + mn), mx - mn};
 }
 
 // References of sub-chunk J for feature k (after the statistics are visible).
 __device__ __forceinline__ float ref_recv(const float* sMid, const float* sGf, const int* sFlag,
                                           int J, int KC, int k) {
-  return sFlag[J] ? sGf[J * KC + k] : sMid[J * KC + k];
+  return sFlag[J * (KC / SUB) + k / SUB] ? sGf[J * KC + k] : sMid[J * KC + k];
 }
 __device__ __forceinline__ float ref_send(const float* sMid, const float* sGl, const int* sFlag,
                                           int J, int KC, int k) {
-  return sFlag[J] ? sGl[J * KC + k] : sMid[J * KC + k];
+  return sFlag[J * (KC / SUB) + k / SUB] ? sGl[J * KC + k] : sMid[J * KC + k];
+}
+
+// Sub-chunk J has a wide feature block (some feature ranges over more than
+// CENTRE_MAX_RANGE).
+__device__ __forceinline__ bool flagged(const int* sFlag, int J, int nfb) {
+  int any = 0;
+  for (int b = 0; b < nfb; ++b) any |= sFlag[J * nfb + b];
+  return any != 0;
 }
 
 // Pair factors fac[p][KC] = exp2(rA_I - rB_J) for the 10 pairs I >= J (pair_ij
-// order); 1 on a centred diagonal, and unused on a wide diagonal.
+// order).  On a diagonal pair: 1 for a feature of a centred block and 0 for a
+// feature of a wide block, whose terms the pairwise sum supplies instead.
 template <int KC>
 __device__ __forceinline__ void pair_factors(const float* sMid, const float* sGf,
                                              const float* sGl, const int* sFlag, float* fac,
@@ -169,31 +179,27 @@ __device__ __forceinline__ void pair_factors(const float* sMid, const float* sGf
     pair_ij(p, I, J);
     float f = 0.f;
     if (I * SUB < n)
-      f = (I == J) ? 1.f
+      f = (I == J) ? (sFlag[J * (KC / SUB) + k / SUB] ? 0.f : 1.f)
                    : fexp2(ref_recv(sMid, sGf, sFlag, I, KC, k) -
                            ref_send(sMid, sGl, sFlag, J, KC, k));
     fac[idx] = f;
   }
 }
 
-// Score tiles from pre-scaled operands (natural [token][feature] layout, pitch
-// PK, bf16 or fp32): L_IJ = (Ka_I * f_IJ) Kc_J^T (strict), and with WITH_CQ
-// Cq_IJ = (Qa_I * f_IJ) Kc_J^T (inclusive), for the pairs I >= J with rows < n.
-// Flagged diagonal pairs are skipped here (see pairwise_diag).  The callback
-// st(I, J, accL, accC) receives each finished tile.  Called by all NW waves.
-template <typename T, int K, bool WITH_CQ, int NW, typename Store>
-__device__ __forceinline__ void score_tiles_pre(const T* sKa, const T* sQa, const T* sKc, int PK,
-                                                const float* fac, const int* sFlag, int n,
-                                                Store&& st) {
+// One score tile from pre-scaled operands (natural [token][feature] layout,
+// pitch PK, bf16 or fp32), accumulated into accL / accC:
+// L_IJ += (Ka_I * f_IJ) Kc_J^T and, with WITH_CQ, Cq_IJ += (Qa_I * f_IJ) Kc_J^T
+// (the triangles are cut by the caller).  A diagonal tile skips the factors
+// unless `masked` (a flagged diagonal: f is 1 or 0 per feature).  One wave.
+template <typename T, int K, bool WITH_CQ>
+__device__ __forceinline__ void score_tile(const T* sKa, const T* sQa, const T* sKc, int PK,
+                                           const float* f, int I, int J, bool masked,
+                                           f32x4& accL, f32x4& accC) {
   constexpr bool BF = std::is_same_v<T, bf16>;
-  const int w = wave_id(), l = lane_id();
-  for (int p = w; p < 10; p += NW) {
-    int I, J;
-    pair_ij(p, I, J);
-    if (I * SUB >= n || (I == J && sFlag[J])) continue;
+  const int l = lane_id();
+  const bool plain = I == J && !masked;
+  {
     const int ri = I * SUB + (l & 15), rj = J * SUB + (l & 15);
-    const float* f = fac + p * K;
-    f32x4 accL = zero4(), accC = zero4();
     for (int k0 = 0; k0 < K; k0 += MM<T>::KS) {
       typename MM<T>::frag ak, aq, bk;
       if constexpr (BF) {
@@ -202,7 +208,7 @@ __device__ __forceinline__ void score_tiles_pre(const T* sKa, const T* sQa, cons
         bk = *reinterpret_cast<const bf16x8*>(sKc + rj * PK + kb);
         bf16x8 qa;
         if constexpr (WITH_CQ) qa = *reinterpret_cast<const bf16x8*>(sQa + ri * PK + kb);
-        if (I == J) {
+        if (plain) {
           ak = ka;
           if constexpr (WITH_CQ) aq = qa;
         } else {
@@ -217,7 +223,7 @@ __device__ __forceinline__ void score_tiles_pre(const T* sKa, const T* sQa, cons
         }
       } else {
         const int kk = k0 + (l >> 4);
-        const float fe = (I == J) ? 1.f : f[kk];
+        const float fe = plain ? 1.f : f[kk];
         ak = tof(sKa[ri * PK + kk]) * fe;
         if constexpr (WITH_CQ) aq = tof(sQa[ri * PK + kk]) * fe;
         bk = sKc[rj * PK + kk];
@@ -225,22 +231,42 @@ __device__ __forceinline__ void score_tiles_pre(const T* sKa, const T* sQa, cons
       accL = mma(ak, bk, accL);
       if constexpr (WITH_CQ) accC = mma(aq, bk, accC);
     }
+  }
+}
+
+// All score tiles of the pairs I >= J with rows < n, except the flagged
+// diagonals (see pairwise_diag).  The callback st(I, J, accL, accC) receives
+// each finished tile.  Called by all NW waves.
+template <typename T, int K, bool WITH_CQ, int NW, typename Store>
+__device__ __forceinline__ void score_tiles_pre(const T* sKa, const T* sQa, const T* sKc, int PK,
+                                                const float* fac, const int* sFlag, int n,
+                                                Store&& st) {
+  const int w = wave_id();
+  for (int p = w; p < 10; p += NW) {
+    int I, J;
+    pair_ij(p, I, J);
+    if (I * SUB >= n || (I == J && flagged(sFlag, J, K / SUB))) continue;
+    f32x4 accL = zero4(), accC = zero4();
+    score_tile<T, K, WITH_CQ>(sKa, sQa, sKc, PK, fac + p * K, I, J, false, accL, accC);
     st(I, J, accL, accC);
   }
 }
 
-// Pairwise diagonal tile of a wide sub-chunk I (one wave): entries
-//   L[i][j]  = beta_i sum_k k_ik k_jk exp2(G_ik - G_jk)      (j < i)
-//   Cq[i][j] = s sum_k q_ik k_jk exp2(G_ik - G_jk)            (j <= i)
+// Pairwise part of the diagonal tile of sub-chunk I (one wave): the terms of
+// the features in wide 16-feature blocks (wide[fb] != 0),
+//   L[i][j]  += beta_i sum_k k_ik k_jk exp2(G_ik - G_jk)      (j < i)
+//   Cq[i][j] += s sum_k q_ik k_jk exp2(G_ik - G_jk)            (j <= i)
 // with G_i - G_j summed from the raw gates between the two rows, so no factor
-// exceeds 1.  Reads q, k, g from global.  Lane l takes column j = l & 15 and
-// the feature quarter l >> 4; results come back in the C-fragment layout.
+// exceeds 1, added to the centred blocks' terms already in accL / accC.  Reads
+// q, k, g from global.  Lane l takes column j = l & 15 and the feature quarter
+// l >> 4; results come back in the C-fragment layout.
 // EW: the erase gate is a vector b (a.beta, [.., K], element type T), taken
 // inside the sum over features instead of beta_i outside it.  GIN: the gate
 // is formed from its pre-activation (softplus or bounded form, Args::gate_lb).
 template <typename T, int K, bool WITH_CQ, bool EW = false, bool GIN = false>
 __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, int n, int I,
-                                              const float* sBeta, f32x4& accL, f32x4& accC) {
+                                              const float* sBeta, const int* wide, f32x4& accL,
+                                              f32x4& accC) {
   const int l = lane_id(), j = l & 15, qk = l >> 4, H = a.H;
   const T* kg = reinterpret_cast<const T*>(a.k);
   const T* qg = reinterpret_cast<const T*>(a.q);
@@ -251,6 +277,7 @@ __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, 
   const int rj = I * SUB + j;
   if (rj < n) {
     for (int k = qk * (K / 4); k < (qk + 1) * (K / 4); ++k) {
+      if (!wide[k / SUB]) continue;  // a centred block: its terms came from the MFMA tile
       const float kj = tof(kg[((t0 + rj) * H + h) * K + k]);
       float run = 0.f;
 #pragma unroll
@@ -286,15 +313,13 @@ __device__ __forceinline__ void pairwise_diag(const Args& a, int64_t t0, int h, 
       pC[i] += __shfl_xor(pC[i], 32);
     }
   }
-  accL = zero4();
-  accC = zero4();
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4)
     if (qk == g4)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        accL[r] = EW ? pL[4 * g4 + r] : sBeta[I * SUB + 4 * g4 + r] * pL[4 * g4 + r];
-        accC[r] = a.scale * pC[4 * g4 + r];
+        accL[r] += EW ? pL[4 * g4 + r] : sBeta[I * SUB + 4 * g4 + r] * pL[4 * g4 + r];
+        accC[r] += a.scale * pC[4 * g4 + r];
       }
 }
 

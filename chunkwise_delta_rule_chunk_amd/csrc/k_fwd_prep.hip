@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   __shared__ __align__(16) float sFac[10 * K];
   __shared__ float sMid[NSUB * K], sGf[NSUB * K], sGl[NSUB * K], sGn[K];
   __shared__ float sBeta[CH];
-  __shared__ int sFlag[NSUB];
+  __shared__ int sFlag[NSUB * (K / SUB)];  // wide (sub-chunk, 16-feature block)
   T* const sK = reinterpret_cast<T*>(sX);  // S0-S3: raw k, then Kc in place
   T* const sQ = sK + CH * PK;              //        raw q, then Qa in place
   T* const sKa = sQ + CH * PK;             //        Ka
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     pk.store(sK, PK, tid);
     pq.store(sQ, PK, tid);
     if (tid < CH) sBeta[tid] = tid < n ? beta_val(pbeta, a.beta_f32) : 0.f;
-    if (tid < NSUB) sFlag[tid] = 0;
+    if (tid < NSUB * (K / SUB)) sFlag[tid] = 0;
     if constexpr (GIN) {
       const float ea = fexp2(__uint_as_float(gal) * LOG2E);
 #pragma unroll
@@ -503,11 +503,14 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
         if constexpr (MODE & PREP_BWD_SCAN) st_frag_T<T>(cq, Cqto, I, J);
       };
       score_tiles_pre<T, K, true, NW>(sKa, sQ, sK, PK, sFac, sFlag, n, store);
-      // wide diagonal sub-chunks: pairwise, one wave each
+      // diagonal sub-chunks with a wide feature block, one wave each: the
+      // centred blocks by MFMA (the wide ones masked by a zero pair factor),
+      // then the wide blocks pairwise
       for (int J = w; J < NSUB; J += NW)
-        if (J * SUB < n && sFlag[J]) {
-          f32x4 accL, accC;
-          pairwise_diag<T, K, true, EW, GIN>(a, t0, h, n, J, sBeta, accL, accC);
+        if (J * SUB < n && flagged(sFlag, J, K / SUB)) {
+          f32x4 accL = zero4(), accC = zero4();
+          score_tile<T, K, true>(sKa, sQ, sK, PK, sFac + (J * (J + 1) / 2 + J) * K, J, J, true, accL, accC);
+          pairwise_diag<T, K, true, EW, GIN>(a, t0, h, n, J, sBeta, sFlag + J * (K / SUB), accL, accC);
           store(J, J, accL, accC);
         }
       // tiles nobody computed: zeros (the upper triangle and rows past the end)
