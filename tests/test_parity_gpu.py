@@ -146,7 +146,8 @@ def test_deterministic_and_policies_bitwise_equal():
 
 def test_chunk_index_bit_exact():
     """The device chunk table equals the integer reference: chunks restart at
-    every sequence, the last one of a sequence is partial, none is empty."""
+    every sequence, the last one of a sequence is partial, none is empty; and
+    the scan order ranks the sequences by chunk count."""
     say("[case] chunk index")
     from chunkwise_delta_rule_chunk_amd import ops
     cu = [0, 5, 5, 69, 200, 201, 320]
@@ -162,6 +163,15 @@ def test_chunk_index_bit_exact():
             ref.append((n, start, min(64, cu[n + 1] - start), p))
     got = ws[: 16 * len(ref)].view(torch.int32).view(-1, 4).cpu().tolist()
     assert [tuple(x) for x in got] == ref
+    # the scan order that follows the chunk records and the sequence offsets
+    # (256-byte aligned regions): sequences by chunk count, longest first, ties
+    # by index
+    up = lambda x: (x + 255) // 256 * 256
+    N = len(cu) - 1
+    off = up(16 * len(ref)) + up(4 * (N + 1))
+    order = ws[off: off + 4 * N].view(torch.int32).cpu().tolist()
+    counts = [len(range(cu[n], cu[n + 1], 64)) for n in range(N)]
+    assert order == sorted(range(N), key=lambda n: (-counts[n], n)), (order, counts)
 
 
 def test_graph_replay_with_changing_inputs():
