@@ -143,7 +143,7 @@ def _time_decode(result, args, ops, binding, torch):
           f"{achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
 
-def _time_gdn2(result, x, inp, B, T, args, ops, torch):
+def _time_gdn2(result, x, inp, B, T, args, ops, binding, torch):
     """The erase/write form (independent erase gate b [B,T,H,K] and write gate
     w [B,T,H,V]) on the same inputs: one forward + backward step."""
     gen = torch.Generator().manual_seed(13)
@@ -163,8 +163,15 @@ def _time_gdn2(result, x, inp, B, T, args, ops, torch):
         step2()
     torch.cuda.synchronize()
     ms2 = (time.perf_counter() - t2) * 1e3 / args.steps
+    binding.rewy_trace_begin()  # per-kernel durations from a separate, untimed pass
+    for _ in range(args.steps):
+        step2()
+    tr = binding.rewy_trace_end()
+    torch.cuda.synchronize()
     result["gdn2"] = {"form": "erase/write gates (b, w) in place of beta", "policy": args.policy,
-                      "ms_per_step": ms2, "value": B * T / (ms2 * 1e-3), "unit": "tokens/s"}
+                      "ms_per_step": ms2, "value": B * T / (ms2 * 1e-3), "unit": "tokens/s",
+                      "kernels_ms": {name: {"avg_ms": tot / cnt, "launches_per_step": cnt / args.steps}
+                                     for name, tot, cnt in tr}}
     print(f"[bench] erase/write form: {ms2:.3f} ms/step", file=sys.stderr, flush=True)
 
 
@@ -400,7 +407,7 @@ def main():
     if not args.no_decode:
         _time_decode(result, args, ops, binding, torch)
     if not args.no_gdn2:
-        _time_gdn2(result, x, inp, B, T, args, ops, torch)
+        _time_gdn2(result, x, inp, B, T, args, ops, binding, torch)
     if not args.no_kda_gate:
         _time_kda_gate(result, x, inp, B, T, args, ops, binding, torch)
 
