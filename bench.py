@@ -258,7 +258,7 @@ def main():
                          "copy kernel of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(heads shard across GPUs with no communication, so per-GPU throughput is the "
               "N=1 figure)", file=sys.stderr)
         sys.exit(2)

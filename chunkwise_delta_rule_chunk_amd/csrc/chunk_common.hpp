@@ -85,7 +85,7 @@ inline int persistent_grid() {
   return cached[dev];
 }
 
-// Launch helper: the (T, K, V) instantiations this build provides.  fp32 keeps
+// Launch helper: the (T, K, V) instantiations the library provides.  fp32 keeps
 // K, V <= 64 so that every kernel's LDS stays within one CU's 160 KB.
 template <typename T, int K, int V>
 constexpr bool kv_ok() {

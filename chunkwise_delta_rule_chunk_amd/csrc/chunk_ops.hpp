@@ -9,9 +9,10 @@
 //
 // Centring (ReWY paper section 3.3, "Centered factors", and Appendix 8): every
 // sub-chunk J of 16 rows gets, per feature, a receiving reference rA_J and a
-// sending reference rB_J: both its gate midpoint (max + min) / 2, or, when the
-// sub-chunk's gate range exceeds CENTRE_MAX_RANGE, its first row (rA) and its
-// last valid row (rB).  Operands are stored pre-scaled,
+// sending reference rB_J: both its gate midpoint (max + min) / 2, or, for the
+// features of a 16-feature block in which some feature's gate range over the
+// sub-chunk exceeds CENTRE_MAX_RANGE, its first row (rA) and its last valid
+// row (rB).  Operands are stored pre-scaled,
 //   Ka[i] = beta_i k_i exp2(G_i - rA),  Qa[i] = s q_i exp2(G_i - rA),
 //   Kc[j] = k_j exp2(rB - G_j),
 // and a pair of sub-chunks I > J contributes through the per-feature factor
@@ -19,7 +20,8 @@
 //                                    last row of J <= rB_J for a decaying gate),
 // so exp2(G_i - G_j) = exp2(G_i - rA_I) f_IJ exp2(rB_J - G_j) is never formed as
 // a product of unbounded factors.  Midpoint-centred factors are bounded by
-// 2^(range/2) <= 2^64.  A diagonal pair of a wide sub-chunk is summed pairwise.
+// 2^(range/2) <= 2^64.  On a diagonal pair the terms of a wide feature block are
+// summed pairwise instead.
 #pragma once
 #include "chunk_common.hpp"
 

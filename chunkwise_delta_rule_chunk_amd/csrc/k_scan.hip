@@ -1,9 +1,10 @@
 // The two serial inter-chunk scans.  One workgroup of four waves per
 // (sequence, head, value tile of BV columns) walks the sequence's chunks in
 // order; the fp32 state tile [K x BV] stays in MFMA accumulator registers for
-// the whole walk.  Grid = (N*H, V/BV): consecutive workgroup ids, which the
-// dispatcher spreads round-robin over the 8 XCDs, give the value tiles of one
-// (sequence, head) the same XCD and L2 whenever N*H is a multiple of 8.
+// the whole walk.  A 1D grid dispatches eight (sequence, head) units at a
+// time with all their value tiles, longest sequences first, and keeps each
+// unit on one XCD (workgroup ids go round-robin over the eight XCDs), so the
+// tiles of a unit share that XCD's L2 (scan_unit below).
 //
 // Wave w owns token tile w of the per-chunk product (R or Rbar) and a set of
 // key tiles of the state.  The chunk operands it contracts (rows of W, F^T,

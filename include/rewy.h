@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
     REWY_OK = 0,
     REWY_EINVAL = -1,       /* malformed argument (null pointer, bad shape, bad cu_seqlens) */
-    REWY_EUNSUPPORTED = -2, /* valid request this build does not implement (K, V not in {32,64,128}) */
+    REWY_EUNSUPPORTED = -2, /* valid request the library does not implement (K, V not in {32,64,128}) */
     REWY_EWORKSPACE = -3,   /* workspace or saved buffer too small or misaligned */
     REWY_EHIP = -4          /* a HIP launch or copy reported an error */
 } rewy_status;
