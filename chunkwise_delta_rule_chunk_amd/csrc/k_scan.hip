@@ -155,10 +155,43 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
     fetch_fl(B, c0 + B);
   });
 
+  // The output of a chunk is stored one step late: its C_q R product is issued
+  // at the end of the chunk's step, and its transpose and store come in the
+  // next step, so their latency overlaps that step's work instead of holding
+  // the wave (instructions issue in order).  pbos / plen are the rows of the
+  // pending chunk; plen = 0 drops the stores (nothing pending yet).
+  f32x4 pend[OUTP ? CT : 1], ptr[OUTP ? CT : 1];
+  int pbos = 0, plen = 0;
+  auto out_transpose = [&]() {
+    if constexpr (OUTP) {
+#pragma unroll
+      for (int m = 0; m < CT; ++m) {
+        ptr[m] = zero4();
+        mm16(ptr[m], to_frag<T>(pend[m]), idt);
+      }
+    }
+  };
+  auto out_store = [&]() {
+    if constexpr (OUTP) {
+      const GBuf bo = gbuf(reinterpret_cast<T*>(a.o) + ((int64_t)pbos * H + h) * V, tile_bytes<T>(plen, gsV, V));
+#pragma unroll
+      for (int m = 0; m < CT; ++m) {
+        const uint32_t off = (uint32_t)(((int64_t)(SUB * w + r16) * gsV + vt * BV + SUB * m + 4 * g) * (int64_t)sizeof(T));
+        if constexpr (std::is_same_v<T, bf16>) gst8(bo, off, __builtin_bit_cast(uint2, to_frag<T>(ptr[m])));
+        else gst16(bo, off, __builtin_bit_cast(uint4, ptr[m]));
+      }
+    }
+  };
+  if constexpr (OUTP) {
+#pragma unroll
+    for (int m = 0; m < CT; ++m) pend[m] = zero4();
+  }
+
   auto step = [&](auto buf, int c) {
     constexpr int B = decltype(buf)::value;
     const int64_t cb = (int64_t)c * H + h;
     const int bos = seq_bos + (c - c0) * CH, len = min(CH, seq_eos - bos);
+    out_transpose();  // the previous chunk's output rows
     // S_c: operand [v][k] in LDS and, for global memory, natural [k][v]
 #pragma unroll
     for (int j = 0; j < KW; ++j)
@@ -217,6 +250,7 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
                                ((int64_t)(vt * CT + m) * CH + SUB * w + r16) * SUB + 4 * g) = to_frag<T>(tr);
       }
     }
+    out_store();
     fetch_wu(ic<B>{}, c + DEPTH);
     lds_barrier();
     // S = diag(exp2 G2_last) S + F^T R
@@ -234,22 +268,20 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
         for (int q = 0; q < NGT; ++q) mma16B<T>(st[j][m], ff[B][j][q], *reinterpret_cast<const uint4*>(rb + KG * q));
       }
     }
-    // o rows of token tile w: O += Cq R, transposed by the identity product
-    // into 8-byte (16-byte fp32) row pieces; rows past the chunk's end fall
-    // outside the buffer and are dropped
+    // o rows of token tile w: O += Cq R, left pending; the next step (or the
+    // end of the walk) transposes it by the identity product into 8-byte
+    // (16-byte fp32) row pieces and stores them; rows past the chunk's end
+    // fall outside the buffer and are dropped
     if constexpr (OUTP) {
-      const GBuf bo = gbuf(reinterpret_cast<T*>(a.o) + ((int64_t)bos * H + h) * V, tile_bytes<T>(len, gsV, V));
 #pragma unroll
       for (int m = 0; m < CT; ++m) {
         const T* rb = sRt + (SUB * m + r16) * PA + 4 * g;
 #pragma unroll
         for (int q = 0; q < NGT; ++q) mma16B<T>(po[m], cqf[B][q], perm_row<T>(rb, q));
-        f32x4 tr = zero4();
-        mm16(tr, to_frag<T>(po[m]), idt);
-        const uint32_t off = (uint32_t)(((int64_t)(SUB * w + r16) * gsV + vt * BV + SUB * m + 4 * g) * (int64_t)sizeof(T));
-        if constexpr (std::is_same_v<T, bf16>) gst8(bo, off, __builtin_bit_cast(uint2, to_frag<T>(tr)));
-        else gst16(bo, off, __builtin_bit_cast(uint4, tr));
+        pend[m] = po[m];
       }
+      pbos = bos;
+      plen = len;
     }
     fetch_fl(ic<B>{}, c + DEPTH);
   };
@@ -261,6 +293,8 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
     step(ic<1>{}, c);
     if (++c >= c1) break;
   }
+  out_transpose();  // the last chunk's output rows
+  out_store();
   if (a.ht) {
 #pragma unroll
     for (int j = 0; j < KW; ++j)
