@@ -192,7 +192,10 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
     const int64_t cb = (int64_t)c * H + h;
     const int bos = seq_bos + (c - c0) * CH, len = min(CH, seq_eos - bos);
     out_transpose();  // the previous chunk's output rows
-    // S_c: operand [v][k] in LDS and, for global memory, natural [k][v]
+    // S_c: operand [v][k] in LDS and, for global memory, natural [k][v] (its
+    // transposes are issued here and stored after the barrier, whose wait
+    // covers their latency)
+    f32x4 trh[NAT ? KW : 1][NAT ? CW : 1];
 #pragma unroll
     for (int j = 0; j < KW; ++j)
 #pragma unroll
@@ -203,13 +206,19 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
         for (int i = 0; i < 4; ++i) x[i] = tof(fromf<T>(st[j][m][i]));
         st_tile_T<T>(x, sHt + vc * PK + kr, PK);
         if constexpr (NAT) {  // column-blocked [V/16][K][16]: a wave writes 16 whole block rows
-          f32x4 tr = zero4();
-          mm16(tr, to_frag<T>(x), idt);
-          *reinterpret_cast<FR*>(reinterpret_cast<T*>(a.hbuf) + cb * K * V +
-                                 ((int64_t)(vt * CT + vtile(m)) * K + kr + r16) * SUB + 4 * g) = to_frag<T>(tr);
+          trh[j][m] = zero4();
+          mm16(trh[j][m], to_frag<T>(x), idt);
         }
       }
     lds_barrier();
+    if constexpr (NAT)
+#pragma unroll
+      for (int j = 0; j < KW; ++j)
+#pragma unroll
+        for (int m = 0; m < CW; ++m)
+          *reinterpret_cast<FR*>(reinterpret_cast<T*>(a.hbuf) + cb * K * V +
+                                 ((int64_t)(vt * CT + vtile(m)) * K + SUB * ktile(j) + r16) * SUB + 4 * g) =
+              to_frag<T>(trh[j][m]);
     // R = U - W S for token tile w (rows past the chunk's end are zero: W and
     // U are zero there).  A W piece holds, for lane l (row l & 15), the keys
     // 16 kb + 4 (l >> 4) + e of GPP consecutive 16-key groups kb.  bf16 takes
@@ -219,6 +228,7 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
     // (Qg S for the output goes with it, on the same S operand; its Cq R
     // part follows the state update, when R_c is in LDS.)
     f32x4 po[OUTP ? CT : 1];
+    f32x4 trr[NAT ? CT : 1];
 #pragma unroll
     for (int m = 0; m < CT; ++m) {
       f32x4 p = zero4();
@@ -243,16 +253,19 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
 #pragma unroll
       for (int i = 0; i < 4; ++i) rv[i] = tof(fromf<T>(tof(uf[B][m][i]) - p[i]));
       st_tile_T<T>(rv, sRt + (SUB * m) * PA + SUB * w, PA);
-      if constexpr (NAT) {  // column-blocked [V/16][64][16], all 64 rows (zero past the end)
-        f32x4 tr = zero4();
-        mm16(tr, to_frag<T>(rv), idt);
-        *reinterpret_cast<FR*>(reinterpret_cast<T*>(a.R) + cb * V * CH +
-                               ((int64_t)(vt * CT + m) * CH + SUB * w + r16) * SUB + 4 * g) = to_frag<T>(tr);
+      if constexpr (NAT) {  // column-blocked [V/16][64][16], all 64 rows (zero past the end); stored after the barrier
+        trr[m] = zero4();
+        mm16(trr[m], to_frag<T>(rv), idt);
       }
     }
     out_store();
     fetch_wu(ic<B>{}, c + DEPTH);
     lds_barrier();
+    if constexpr (NAT)
+#pragma unroll
+      for (int m = 0; m < CT; ++m)
+        *reinterpret_cast<FR*>(reinterpret_cast<T*>(a.R) + cb * V * CH +
+                               ((int64_t)(vt * CT + m) * CH + SUB * w + r16) * SUB + 4 * g) = to_frag<T>(trr[m]);
     // S = diag(exp2 G2_last) S + F^T R
 #pragma unroll
     for (int j = 0; j < KW; ++j) {
@@ -424,7 +437,9 @@ __device__ __forceinline__ void bwd_scan_wg(const Args& a, const int u, const in
     const int bos = seq_bos + (c - c0) * CH, len = min(CH, seq_eos - bos);
     const int64_t cb = (int64_t)c * H + h;
     // dS_{c+1}: operand [v][k] and natural [k][v]; dO_c transposed (rows past
-    // the chunk's end zero)
+    // the chunk's end zero).  The natural copy's transposes are issued here and
+    // stored after the barrier, whose wait covers their latency.
+    f32x4 trd[KW][CW];
 #pragma unroll
     for (int j = 0; j < KW; ++j)
 #pragma unroll
@@ -434,10 +449,8 @@ __device__ __forceinline__ void bwd_scan_wg(const Args& a, const int u, const in
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = tof(fromf<T>(st[j][m][i]));
         st_tile_T<T>(x, sDt + vc * PK + kr, PK);
-        f32x4 tr = zero4();  // column-blocked [V/16][K][16]
-        mm16(tr, to_frag<T>(x), idt);
-        *reinterpret_cast<FR*>(reinterpret_cast<T*>(a.dhbuf) + cb * K * V +
-                               ((int64_t)(vt * CT + vtile(m)) * K + kr + r16) * SUB + 4 * g) = to_frag<T>(tr);
+        trd[j][m] = zero4();  // column-blocked [V/16][K][16]
+        mm16(trd[j][m], to_frag<T>(x), idt);
       }
 #pragma unroll
     for (int e = 0; e < ON; ++e) {
@@ -451,6 +464,13 @@ __device__ __forceinline__ void bwd_scan_wg(const Args& a, const int u, const in
       for (int k = 0; k < OE; ++k) sOt[B][(c8 + k) * PA + r] = r < len ? x.v[k] : fromf<T>(0.f);
     }
     lds_barrier();
+#pragma unroll
+    for (int j = 0; j < KW; ++j)
+#pragma unroll
+      for (int m = 0; m < CW; ++m)
+        *reinterpret_cast<FR*>(reinterpret_cast<T*>(a.dhbuf) + cb * K * V +
+                               ((int64_t)(vt * CT + vtile(m)) * K + SUB * ktile(j) + r16) * SUB + 4 * g) =
+            to_frag<T>(trd[j][m]);
     // Rbar = F dS+ + Cq^T dO for token tile w (rows past the end are zero: F
     // and Cq vanish there)
 #pragma unroll
