@@ -1,11 +1,14 @@
 // Host side of the C ABI declared in include/rewy.h: argument validation,
 // workspace planning and the launch sequence of each pass.  Nothing here
 // allocates device memory or waits for the device.
+#include <cxxabi.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <string>
 #include <vector>
 
 #include "kernels.hpp"
@@ -14,6 +17,12 @@
 #define REWY_API extern "C" __attribute__((visibility("default")))
 
 namespace rewy {
+
+const void*& last_kernel() {
+  static thread_local const void* k = nullptr;
+  return k;
+}
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -71,15 +80,13 @@ int make_plan(const rewy_desc* d, Plan& p) {
       const int32_t* cu = d->cu_seqlens_host;
       if (cu[0] != 0 || cu[p.N] != d->T)
         return fail(REWY_EINVAL, "cu_seqlens must start at 0 and end at T=%d", d->T);
-      int64_t nc = 0;
-      for (int i = 0; i < p.N; ++i) {
+      for (int i = 0; i < p.N; ++i)
         if (cu[i + 1] < cu[i]) return fail(REWY_EINVAL, "cu_seqlens not ascending at %d", i);
-        nc += (cu[i + 1] - cu[i] + CH - 1) / CH;
-      }
-      p.nc_max = (int)nc;
-    } else {
-      p.nc_max = (d->T + CH - 1) / CH + p.N;
     }
+    // Chunk slots: sum over sequences of ceil(len / 64) <= ceil(T / 64) + N.
+    // The bound, not the exact count, so that every buffer layout (workspace
+    // and saved) is the same whether or not the host copy is passed.
+    p.nc_max = (int)std::min<int64_t>((int64_t)(d->T + CH - 1) / CH + p.N, INT32_MAX);
   } else {
     if (d->N != 0 && d->N != d->B) return fail(REWY_EINVAL, "N=%d must equal B=%d without cu_seqlens", d->N, d->B);
     p.N = d->B;
@@ -92,10 +99,13 @@ int make_plan(const rewy_desc* d, Plan& p) {
 // the save-all policy; everything else is scratch in the workspace.  The
 // reverse set is what the reverse scan and the chunk backward read:
 // F Wt Qgt Cqt (reverse scan) and At G2t Gst (chunk backward).
-//   recompute: ws = [index | glast hbuf R | W Ft U | (fwd) Qg Cq / (bwd) reverse set | Rbt dhbuf]
+//   recompute: ws = [index | glast | W Ft U | (fwd) Qg Cq
+//                                           | (bwd) hbuf R reverse set Rbt dhbuf]
 //   save-all:  saved = [glast hbuf R | reverse set]
 //              ws (fwd) = [index | W Ft U Qg Cq],  ws (bwd) = [index | Rbt dhbuf]
-// The backward with the gate formed in the kernel appends the per-wave partial
+// The forward of the recompute policy writes neither hbuf nor R, so they share
+// the output operands' space with the rest of the backward's buffers.  The
+// backward with the gate formed in the kernel appends the per-wave partial
 // sums of the gate parameters' gradients to its workspace (phase 2).
 struct Layout {
   size_t chunks, seqoff, seqord;
@@ -111,9 +121,9 @@ struct Layout {
 
 Layout layout(const Plan& p) {
   Layout L{};
-  const size_t nc = p.nc_max, H = p.H, K = p.K, V = p.V, BT = p.BT, e = p.esz;
+  const size_t nc = p.nc_max, H = p.H, K = p.K, V = p.V, e = p.esz;
   const size_t tileK = nc * H * K * CH * e, tileV = nc * H * V * CH * e;
-  const size_t tile64 = nc * H * CH * CH * e;
+  const size_t tile64 = nc * H * CH * CH * e, states = nc * H * K * V * e;
   const size_t g2 = p.gate == REWY_GATE_VECTOR ? nc * H * K * CH * 4
                     : p.gate == REWY_GATE_SCALAR ? nc * H * CH * 4 : 0;
   size_t off = 0;
@@ -134,9 +144,9 @@ Layout layout(const Plan& p) {
   const bool save = p.policy == REWY_SAVE;
   size_t s = save ? 0 : off;
   L.glast = take(s, nc * H * K * 4);
-  L.hbuf = take(s, nc * H * K * V * e);
-  L.R = take(s, tileV);
   if (save) {
+    L.hbuf = take(s, states);
+    L.R = take(s, tileV);
     take_reverse(s);
     L.saved = s;
     off = head;
@@ -153,11 +163,13 @@ Layout layout(const Plan& p) {
   if (save) {
     off = head;
   } else {
-    off = after_scan;  // the reverse set shares the output operands' space
+    off = after_scan;  // the backward's buffers share the output operands' space
+    L.hbuf = take(off, states);
+    L.R = take(off, tileV);
     take_reverse(off);
   }
   L.Rbt = take(off, tileV);
-  L.dhbuf = take(off, nc * H * K * V * e);
+  L.dhbuf = take(off, states);
   L.ws_bwd = off;
   L.gpart = take(off, nc * H * NSUB * (K + 1) * 4);
   L.ws_gin = off;
@@ -178,7 +190,7 @@ int hip_check(hipError_t e, const char* what) {
 int copy_state(float* dst, const float* src, int64_t n, hipStream_t s) {
   if (!dst || n == 0) return REWY_OK;
   const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
-  hipLaunchKernelGGL(k_copy_or_zero, dim3(blocks), dim3(256), 0, s, dst, src, n);
+  REWY_LAUNCH(k_copy_or_zero, dim3(blocks), dim3(256), s, dst, src, n);
   return hip_check(hipGetLastError(), "state copy");
 }
 
@@ -213,8 +225,8 @@ int check_tensor_ptrs(const void* const* ps, const char* const* names, int n) {
 
 // ---- tracing: event pairs around every launch, per thread ------------------
 struct TraceRec {
-  const char* stage;  // kernel template name
-  int variant;        // instantiation key (dtype, K, V)
+  const void* fn;  // host stub of the launched kernel
+  hipStream_t s;
   hipEvent_t e0, e1;
 };
 struct Tracer {
@@ -234,31 +246,46 @@ struct Tracer {
 };
 thread_local Tracer g_tr;
 
+// `stage` is the kernel's template name, which rewy_trace_select matches
 template <typename F>
-hipError_t traced(const char* stage, int variant, hipStream_t s, F&& launch) {
+hipError_t traced(const char* stage, hipStream_t s, F&& launch) {
   if (!g_tr.on || (g_tr.only[0] && strcmp(g_tr.only, stage) != 0)) return launch();
-  TraceRec r{stage, variant, g_tr.ev(), g_tr.ev()};
+  TraceRec r{nullptr, s, g_tr.ev(), g_tr.ev()};
   if (r.e0) hipEventRecord(r.e0, s);
+  last_kernel() = nullptr;
   const hipError_t e = launch();
   if (r.e1) hipEventRecord(r.e1, s);
-  if (r.e0 && r.e1) g_tr.recs.push_back(r);
+  r.fn = last_kernel();
+  if (r.e0 && r.e1 && r.fn) g_tr.recs.push_back(r);
   return e;
 }
 
-int variant_of(const Args& a, bool f32) { return (f32 ? 1000000 : 0) + a.K * 1000 + a.V; }
+// The kernel's name as the profiler reports it: the symbol of the launched
+// instantiation (every template argument included), demangled where the
+// host's demangler can.
+std::string kernel_name(const TraceRec& r) {
+  const char* m = hipKernelNameRefByPtr(r.fn, r.s);
+  if (!m) return "unknown";
+  int st = 0;
+  char* d = abi::__cxa_demangle(m, nullptr, nullptr, &st);
+  // the mangled symbol where the demangler cannot read it (the bfloat16 type
+  // code DF16b), as rocprofv3 prints it then
+  std::string out = (st == 0 && d) ? std::string(d) : std::string(m);
+  free(d);
+  return out;
+}
 
 // Forward chunk stages shared by rewy_fwd and the recompute in rewy_bwd.
 int run_forward_stages(const Args& a, bool f32, bool with_scan, hipStream_t s) {
   int rc;
-  const int vr = variant_of(a, f32);
-  if ((rc = hip_check(traced("k_chunk_table", -1, s, [&] { return launch_chunk_table(a, s); }),
+  if ((rc = hip_check(traced("k_chunk_table", s, [&] { return launch_chunk_table(a, s); }),
                       "chunk table")))
     return rc;
-  if ((rc = hip_check(traced("k_fwd_prep", vr, s, [&] { return launch_fwd_prep(a, f32, s); }),
+  if ((rc = hip_check(traced("k_fwd_prep", s, [&] { return launch_fwd_prep(a, f32, s); }),
                       "forward prep")))
     return rc;
   if (with_scan &&
-      (rc = hip_check(traced("k_fwd_scan", vr, s, [&] { return launch_fwd_scan(a, f32, s); }),
+      (rc = hip_check(traced("k_fwd_scan", s, [&] { return launch_fwd_scan(a, f32, s); }),
                       "forward scan")))
     return rc;
   return REWY_OK;
@@ -418,7 +445,7 @@ int recurrent_impl(const rewy_desc* d, const void* q, const void* k, const void*
   a.gate = p.gate; a.beta_f32 = p.beta_f32; a.scale = d->scale; a.cu = d->cu_seqlens;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
   a.wg = wg; a.ew = ew;
-  return hip_check(traced("k_recurrent", variant_of(a, p.f32), s,
+  return hip_check(traced("k_recurrent", s,
                           [&] { return launch_recurrent(a, p.f32, s); }),
                    "recurrent forward");
 }
@@ -509,25 +536,24 @@ int backward_impl(const rewy_desc* d, const void* q, const void* k, const void* 
     a.gpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.gpart);
   }
   const bool f32 = p.f32;
-  const int vr = variant_of(a, f32);
   if (p.policy == REWY_RECOMPUTE) {
     // prep again, then the forward scan and the reverse scan side by side
     if ((rc = run_forward_stages(a, f32, false, s))) return rc;
-    if ((rc = hip_check(traced("k_scans", vr, s, [&] { return launch_scans(a, f32, s); }),
+    if ((rc = hip_check(traced("k_scans", s, [&] { return launch_scans(a, f32, s); }),
                         "forward and reverse scans")))
       return rc;
   } else {
-    if ((rc = hip_check(traced("k_chunk_table", -1, s, [&] { return launch_chunk_table(a, s); }),
+    if ((rc = hip_check(traced("k_chunk_table", s, [&] { return launch_chunk_table(a, s); }),
                         "chunk table")))
       return rc;
-    if ((rc = hip_check(traced("k_bwd_scan", vr, s, [&] { return launch_bwd_scan(a, f32, s); }),
+    if ((rc = hip_check(traced("k_bwd_scan", s, [&] { return launch_bwd_scan(a, f32, s); }),
                         "reverse scan")))
       return rc;
   }
-  if ((rc = hip_check(traced("k_bwd_chunk", vr, s, [&] { return launch_bwd_chunk(a, f32, s); }),
+  if ((rc = hip_check(traced("k_bwd_chunk", s, [&] { return launch_bwd_chunk(a, f32, s); }),
                       "chunk backward")))
     return rc;
-  if (gi && (rc = hip_check(traced("k_gate_reduce", -1, s, [&] { return launch_gate_reduce(a, s); }),
+  if (gi && (rc = hip_check(traced("k_gate_reduce", s, [&] { return launch_gate_reduce(a, s); }),
                             "gate parameter gradients")))
     return rc;
   return REWY_OK;
@@ -588,21 +614,12 @@ REWY_API int rewy_trace_end(rewy_trace_entry* out, int cap) {
     if (hipEventSynchronize(r.e1) != hipSuccess) return fail(REWY_EHIP, "trace synchronise");
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) return fail(REWY_EHIP, "trace elapsed");
-    // the names rocprofv3 reports: the plain kernel demangled, the templates mangled
-    char name[96];
-    if (r.variant < 0) {
-      snprintf(name, sizeof(name), "rewy::%s(rewy::Args)", r.stage);
-    } else {
-      const bool f32 = r.variant >= 1000000;
-      const int kv = r.variant % 1000000;
-      snprintf(name, sizeof(name), "_ZN4rewy%zu%sI%sLi%dELi%dEEEvNS_4ArgsE", strlen(r.stage),
-               r.stage, f32 ? "f" : "DF16b", kv / 1000, kv % 1000);
-    }
+    const std::string name = kernel_name(r);
     size_t i = 0;
-    while (i < agg.size() && strcmp(agg[i].kernel, name) != 0) ++i;
+    while (i < agg.size() && strcmp(agg[i].kernel, name.c_str()) != 0) ++i;
     if (i == agg.size()) {
       rewy_trace_entry e{};
-      snprintf(e.kernel, sizeof(e.kernel), "%s", name);
+      snprintf(e.kernel, sizeof(e.kernel), "%s", name.c_str());
       agg.push_back(e);
     }
     agg[i].total_ms += ms;

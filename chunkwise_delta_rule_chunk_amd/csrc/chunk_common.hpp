@@ -95,7 +95,7 @@ constexpr bool kv_ok() {
 #define REWY_KV_CASE(KERNEL, K_, V_)                                              \
   case K_ * 1000 + V_:                                                            \
     if constexpr (kv_ok<T, K_, V_>()) {                                           \
-      hipLaunchKernelGGL((KERNEL<T, K_, V_>), grid, block, 0, s, a);              \
+      REWY_LAUNCH((KERNEL<T, K_, V_>), grid, block, s, a);              \
       return hipGetLastError();                                                   \
     } else {                                                                      \
       return hipErrorInvalidValue;                                                \
@@ -105,7 +105,7 @@ constexpr bool kv_ok() {
 #define REWY_KV_CASE_X(KERNEL, X, K_, V_)                                         \
   case K_ * 1000 + V_:                                                            \
     if constexpr (kv_ok<T, K_, V_>()) {                                           \
-      hipLaunchKernelGGL((KERNEL<T, K_, V_, X>), grid, block, 0, s, a);           \
+      REWY_LAUNCH((KERNEL<T, K_, V_, X>), grid, block, s, a);           \
       return hipGetLastError();                                                   \
     } else {                                                                      \
       return hipErrorInvalidValue;                                                \

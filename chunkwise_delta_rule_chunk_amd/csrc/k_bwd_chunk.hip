@@ -868,7 +868,7 @@ __global__ __launch_bounds__(1024) void k_gate_reduce(Args a) {
 }
 
 hipError_t launch_gate_reduce(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_gate_reduce, dim3(a.H, (a.K + 63) / 64 + 1), dim3(1024), 0, s, a);
+  REWY_LAUNCH(k_gate_reduce, dim3(a.H, (a.K + 63) / 64 + 1), dim3(1024), s, a);
   return hipGetLastError();
 }
 

@@ -15,17 +15,32 @@
 
 namespace rewy {
 
+// Token range of sequence n.  Device cu_seqlens are clamped to the packed
+// token axis [0, B T) and made non-decreasing, so a malformed array (checked
+// only when a host copy is given) yields empty or overlapping sequences but
+// never a chunk outside the inputs, and never more than nc_max chunk slots.
+__device__ __forceinline__ void seq_range(const Args& a, int n, int& bos, int& eos) {
+  if (a.cu) {
+    const int BT = a.B * a.T;
+    bos = min(max(a.cu[n], 0), BT);
+    eos = min(max(a.cu[n + 1], bos), BT);
+  } else {
+    bos = n * a.T;
+    eos = bos + a.T;
+  }
+}
+
 __global__ void k_chunk_table(Args a) {
   __shared__ int s_total;
   if (threadIdx.x == 0) {
     int off = 0;
     for (int n = 0; n < a.N; ++n) {
-      const int bos = a.cu ? a.cu[n] : n * a.T;
-      const int eos = a.cu ? a.cu[n + 1] : (n + 1) * a.T;
-      a.seqoff[n] = off;
-      off += max(0, eos - bos + CH - 1) / CH;
+      int bos, eos;
+      seq_range(a, n, bos, eos);
+      a.seqoff[n] = min(off, a.nc_max);
+      off += (eos - bos + CH - 1) / CH;
     }
-    a.seqoff[a.N] = off;
+    a.seqoff[a.N] = min(off, a.nc_max);
     s_total = min(off, a.nc_max);
   }
   __syncthreads();  // full fence: the other threads read seqoff from global memory
@@ -59,8 +74,8 @@ __global__ void k_chunk_table(Args a) {
         if (a.seqoff[mid] <= c) lo = mid;
         else hi = mid - 1;
       }
-      const int bos = a.cu ? a.cu[lo] : lo * a.T;
-      const int eos = a.cu ? a.cu[lo + 1] : (lo + 1) * a.T;
+      int bos, eos;
+      seq_range(a, lo, bos, eos);
       const int pos = c - a.seqoff[lo];
       ci.seq = lo;
       ci.pos = pos;
@@ -72,7 +87,7 @@ __global__ void k_chunk_table(Args a) {
 }
 
 hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, a);
+  REWY_LAUNCH(k_chunk_table, dim3(1), dim3(256), s, a);
   return hipGetLastError();
 }
 

@@ -28,7 +28,10 @@ __global__ __launch_bounds__(64) void k_recurrent(Args a) {
   const int l = threadIdx.x, v = blockIdx.y * 64 + l;
   const bool on = v < V;
   const int vc = min(v, V - 1);
-  const int bos = a.cu ? a.cu[n] : n * a.T, eos = a.cu ? a.cu[n + 1] : (n + 1) * a.T;
+  // device cu_seqlens clamped to the packed token axis (never a token outside the inputs)
+  const int BT = a.B * a.T;
+  const int bos = a.cu ? min(max(a.cu[n], 0), BT) : n * a.T;
+  const int eos = a.cu ? min(max(a.cu[n + 1], bos), BT) : (n + 1) * a.T;
   const int64_t sb = ((int64_t)n * H + h) * K * V + vc;  // state element (0, vc)
   const T* qg = reinterpret_cast<const T*>(a.q);
   const T* kg = reinterpret_cast<const T*>(a.k);
@@ -101,9 +104,9 @@ template <typename T, int K, bool EW>
 static hipError_t recurrent_e(const Args& a, hipStream_t s) {
   const dim3 grid(a.N * a.H, (a.V + 63) / 64), block(64);
   switch (a.gate) {
-    case 0: hipLaunchKernelGGL((k_recurrent<T, K, 0, EW>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((k_recurrent<T, K, 1, EW>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_recurrent<T, K, 2, EW>), grid, block, 0, s, a); break;
+    case 0: REWY_LAUNCH((k_recurrent<T, K, 0, EW>), grid, block, s, a); break;
+    case 1: REWY_LAUNCH((k_recurrent<T, K, 1, EW>), grid, block, s, a); break;
+    case 2: REWY_LAUNCH((k_recurrent<T, K, 2, EW>), grid, block, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

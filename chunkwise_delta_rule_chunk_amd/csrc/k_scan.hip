@@ -63,7 +63,10 @@ __device__ __forceinline__ void fwd_scan_wg(const Args& a, const int u, const in
   const int w = wave_id(), tid = threadIdx.x, l = lane_id();
   const int r16 = l & 15, g = l >> 4;
   const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
-  const int seq_bos = a.cu ? a.cu[n] : n * a.T, seq_eos = a.cu ? a.cu[n + 1] : (n + 1) * a.T;
+  // token range of the sequence from its chunk records (clamped to the inputs)
+  const ChunkInfo cfirst = load_chunk(a.chunks, c0 < c1 ? c0 : 0);
+  const ChunkInfo clast = load_chunk(a.chunks, c0 < c1 ? c1 - 1 : 0);
+  const int seq_bos = cfirst.bos, seq_eos = clast.bos + clast.len;
   const int64_t gsV = (int64_t)H * V;
   const T* Wg = reinterpret_cast<const T*>(a.W);
   const T* Ftg = reinterpret_cast<const T*>(a.Ft);
@@ -349,7 +352,10 @@ __device__ __forceinline__ void bwd_scan_wg(const Args& a, const int u, const in
   const int w = wave_id(), tid = threadIdx.x, l = lane_id();
   const int r16 = l & 15, g = l >> 4;
   const int c0 = a.seqoff[n], c1 = a.seqoff[n + 1];
-  const int seq_bos = a.cu ? a.cu[n] : n * a.T, seq_eos = a.cu ? a.cu[n + 1] : (n + 1) * a.T;
+  // token range of the sequence from its chunk records (clamped to the inputs)
+  const ChunkInfo cfirst = load_chunk(a.chunks, c0 < c1 ? c0 : 0);
+  const ChunkInfo clast = load_chunk(a.chunks, c0 < c1 ? c1 - 1 : 0);
+  const int seq_bos = cfirst.bos, seq_eos = clast.bos + clast.len;
   const int64_t gsV = (int64_t)H * V;
   auto ktile = [&](int j) { return WIDE ? w + 4 * j : w % NKT; };
   auto vtile = [&](int m) { return WIDE ? m : (w / NKT) * CW + m; };
@@ -583,9 +589,9 @@ static hipError_t fwd_scan_bv(const Args& a, hipStream_t s) {
     if constexpr (kv_ok<T, K_, V_>() && V_ >= BV && K_ * BV >= 1024 && \
                   (sizeof(T) == 2 || K_ == 32 || BV == 16)) {                             \
       if (a.scan_out == SCAN_OUTPUT)                                            \
-        hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV, SCAN_OUTPUT>), grid, block, 0, s, a); \
+        REWY_LAUNCH((k_fwd_scan<T, K_, V_, BV, SCAN_OUTPUT>), grid, block, s, a); \
       else if (a.scan_out == (SCAN_NATURAL | SCAN_OUTPUT))                      \
-        hipLaunchKernelGGL((k_fwd_scan<T, K_, V_, BV, SCAN_NATURAL | SCAN_OUTPUT>), grid, block, 0, s, a); \
+        REWY_LAUNCH((k_fwd_scan<T, K_, V_, BV, SCAN_NATURAL | SCAN_OUTPUT>), grid, block, s, a); \
       else                                                                      \
         return hipErrorInvalidValue;                                            \
       return hipGetLastError();                                                 \
@@ -608,7 +614,7 @@ static hipError_t bwd_scan_bv(const Args& a, hipStream_t s) {
   case K_ * 1000 + V_:                                                          \
     if constexpr (kv_ok<T, K_, V_>() && V_ >= BV && K_ * BV >= 1024 && \
                   (sizeof(T) == 2 || K_ == 32 || BV == 16)) {                             \
-      hipLaunchKernelGGL((k_bwd_scan<T, K_, V_, BV>), grid, block, 0, s, a);    \
+      REWY_LAUNCH((k_bwd_scan<T, K_, V_, BV>), grid, block, s, a);    \
       return hipGetLastError();                                                 \
     } else {                                                                    \
       return hipErrorInvalidValue;                                              \
@@ -640,7 +646,7 @@ static hipError_t scans_bv(const Args& a, hipStream_t s) {
   case K_ * 1000 + V_:                                                          \
     if constexpr (kv_ok<T, K_, V_>() && V_ >= BV && K_ * BV >= 1024 &&          \
                   (sizeof(T) == 2 || K_ == 32 || BV == 16)) {                   \
-      hipLaunchKernelGGL((k_scans<T, K_, V_, BV>), grid, block, 0, s, a);       \
+      REWY_LAUNCH((k_scans<T, K_, V_, BV>), grid, block, s, a);       \
       return hipGetLastError();                                                 \
     } else {                                                                    \
       return hipErrorInvalidValue;                                              \

@@ -111,6 +111,17 @@ constexpr int PREP_EW = 16;
 // The gate formed in the kernel from its pre-activation (Args::gx).
 constexpr int PREP_GIN = 32;
 
+// The kernel this thread enqueued last (its host-side stub), so that the
+// tracing hook can name each launch exactly as the profiler does.
+const void*& last_kernel();
+// Every launch goes through this macro: one launch of KERNEL (a possibly
+// parenthesised template-id) with no dynamic LDS, recorded in last_kernel().
+#define REWY_LAUNCH(KERNEL, GRID, BLOCK, STREAM, ...)                             \
+  do {                                                                          \
+    ::rewy::last_kernel() = reinterpret_cast<const void*>(&KERNEL);             \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);            \
+  } while (0)
+
 // Launchers: enqueue on `stream`; return the hipError_t of the launch.
 hipError_t launch_chunk_table(const Args& a, hipStream_t s);
 hipError_t launch_fwd_prep(const Args& a, int dtype_f32, hipStream_t s);

@@ -71,3 +71,42 @@ def workload_flops(seq_lengths, H, K, V, C=64):
     bw = sum(backward_chunk(n, K, V) for n in ns) * H
     rc = sum(recompute_chunk(n, K, V) for n in ns) * H
     return fw, bw, rc
+
+
+# ---- the same products split by the kernel that executes them --------------
+# (prep: F2-F4; forward scan: F5-F6; reverse scan: B1; chunk backward: B2-B4)
+
+def prep_chunk(n, K, V):
+    """Scores, solve and WY form (the chunk-parallel forward preparation)."""
+    f = 2 * K * _tri(n, True) + 2 * K * _tri(n, False)   # L, Cq
+    f += n ** 3 // 3                                     # (I + L)^-1
+    f += 2 * K * _tri(n, False) + 2 * V * _tri(n, False)  # W = A E, U = A Z
+    return f
+
+
+def fwd_scan_chunk(n, K, V):
+    """State scan and output: R, S update, Qg S, Cq R."""
+    return 2 * n * K * V * 3 + 2 * V * _tri(n, False)
+
+
+def bwd_scan_chunk(n, K, V):
+    """Reverse scan: Cq^T dO, F dh+, Qg^T dO, W^T Rbar."""
+    return 2 * V * _tri(n, False) + 2 * n * K * V * 3
+
+
+def bwd_chunk_chunk(n, K, V):
+    """ReWY producer and consumers: P, D, Hq, the three state products and the
+    four matrix-intra contractions."""
+    return backward_chunk(n, K, V) - bwd_scan_chunk(n, K, V)
+
+
+def kernel_flops(stage, seq_lengths, H, K, V, C=64):
+    """Algorithmic FLOPs one launch of `stage` performs for the method (work
+    re-executed under the recompute policy is not counted: a recompute prep
+    counts zero, the fused backward scans count the reverse scan only)."""
+    ns = chunk_lengths(seq_lengths, C)
+    per = {"prep_forward": prep_chunk, "fwd_scan": fwd_scan_chunk,
+           "bwd_scan": bwd_scan_chunk, "bwd_chunk": bwd_chunk_chunk}.get(stage)
+    if per is None:
+        return 0
+    return sum(per(n, K, V) for n in ns) * H

@@ -29,6 +29,11 @@
  * batch must be B = 1 and the N sequences are packed along T; chunks of 64
  * tokens restart at every sequence start and the last chunk of a sequence may
  * be partial.  Without it, N = B and every batch row is one sequence.
+ * cu_seqlens is validated on the host only when its host copy is given; the
+ * kernels clamp the device array to [0, T] and to non-decreasing offsets, so
+ * a malformed array gives wrong results but never an access outside the
+ * caller's buffers.  Workspace and saved layouts are sized by the bound
+ * ceil(T / 64) + N chunk slots and do not depend on the host copy.
  *
  * Ownership and execution.  Every pointer except desc and cu_seqlens_host is a
  * device pointer owned by the caller.  The library never allocates device
@@ -187,10 +192,14 @@ int rewy_recurrent_fwd_gdn2(const rewy_desc *d, const void *q, const void *k, co
  * protocol).  After rewy_trace_begin(), calls made by this thread
  * record a HIP event pair on the call's stream around every kernel they
  * enqueue.  rewy_trace_end() waits for the recorded events, stops recording and
- * fills at most `cap` entries, one per kernel name (the name rocprofv3 shows),
- * with the summed elapsed milliseconds and the launch count; it returns the
- * number of entries, or a negative rewy_status.  Not for use under graph
- * capture.  Events are created once per thread and reused. */
+ * fills at most `cap` entries, one per launched instantiation, named by its
+ * symbol with every template argument exactly as rocprofv3 reports it
+ * (demangled where the host's demangler can, e.g. "rewy::k_chunk_table(rewy::Args)",
+ * else mangled, e.g. "_ZN4rewy10k_fwd_prepIDF16bLi128ELi128ELi13EEEvNS_4ArgsE"
+ * for the bfloat16 instantiations), with the summed
+ * elapsed milliseconds and the launch count; it returns the number of
+ * entries, or a negative rewy_status.  Not for use under graph capture.
+ * Events are created once per thread and reused. */
 typedef struct {
     char kernel[96];
     double total_ms;
@@ -201,7 +210,8 @@ int rewy_trace_begin(void);
 int rewy_trace_end(rewy_trace_entry *out, int cap);
 
 /* Restricts this thread's trace to the launches of one kernel, named by its
- * template name ("k_fwd_prep", "k_scans", ...), so that a timed run pays for
+ * template name without arguments ("k_fwd_prep", "k_scans", ...; every
+ * instantiation of it), so that a timed run pays for
  * one event pair per launch of that kernel only.  NULL (the default) traces
  * every launch.  Applies from the next call; the name is copied.  Returns
  * REWY_OK, or REWY_EINVAL for a name longer than 63 characters. */

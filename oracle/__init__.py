@@ -76,11 +76,18 @@ def _ptr(a):
 
 
 def default_threads() -> int:
+    """Host threads for a call: the CPUs this process may run on, or
+    OMP_NUM_THREADS when that is set lower.  The oracle hands one
+    (sequence, head) unit to a thread at a time, so a call uses at most
+    min(this, units) of them."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
 
 
 class _Prob:

@@ -82,9 +82,45 @@ def normwise(x, ref):
     return float(np.linalg.norm(x - ref) / np.linalg.norm(ref))
 
 
-def compare(hip, ref, tol, names=OUT_NAMES, label=""):
-    """Assert every output is within ``tol``; returns the error table."""
-    errs = {}
+# outputs that hold one [K, V] state per (sequence, head): [N, H, K, V]
+STATE_NAMES = ("ht", "dh0")
+# parameter gradients summed over every token of every sequence: one tensor,
+# no (sequence, head) units
+WHOLE_NAMES = ("da_log", "ddt_bias")
+
+
+def unit_slices(name, shape, cu=None):
+    """The (sequence, head) units of output ``name``: yields (label, index)
+    pairs, index selecting the unit's elements.  Token tensors are
+    [B, T, H, ...] (one unit per batch row and head, or per packed sequence
+    and head with ``cu``); state tensors are [N, H, K, V]."""
+    if name in WHOLE_NAMES:
+        return
+    if name in STATE_NAMES:
+        for n in range(shape[0]):
+            for h in range(shape[1]):
+                yield (n, h), (n, h)
+        return
+    B, T, H = shape[:3]
+    if cu is None:
+        for b in range(B):
+            for h in range(H):
+                yield (b, h), (b, slice(None), h)
+    else:
+        cu = [int(x) for x in cu]
+        for n in range(len(cu) - 1):
+            for h in range(H):
+                yield (n, h), (0, slice(cu[n], cu[n + 1]), h)
+
+
+def compare(hip, ref, tol, names=OUT_NAMES, label="", cu=None, units=True, worst_out=None):
+    """Assert every output is within ``tol``, as one tensor and, with
+    ``units``, on every (sequence, head) unit on its own (a wrong sequence or
+    head cannot hide inside a large tensor's norm).  Prints the whole-tensor
+    error and the worst unit of each output; returns the whole-tensor table.
+    ``worst_out`` (a dict), if given, keeps the largest unit error per output
+    over several calls, with the label of the call and the unit."""
+    errs, worst = {}, {}
     for n in names:
         a, r = hip.get(n), ref.get(n)
         if r is None:
@@ -93,8 +129,25 @@ def compare(hip, ref, tol, names=OUT_NAMES, label=""):
         if a is None:
             continue
         errs[n] = normwise(a, r)
+        if units:
+            a_np, r_np = np.asarray(a), np.asarray(r)
+            w = (0.0, None)
+            for lab, idx in unit_slices(n, r_np.shape, cu):
+                e = normwise(a_np[idx], r_np[idx])
+                if w[1] is None or not e <= w[0]:  # a non-finite error always wins
+                    w = (e, lab)
+            if w[1] is not None:
+                worst[n] = w
     say(f"[parity] {label} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    if worst:
+        say(f"[parity] {label} worst unit " +
+            " ".join(f"{k}={e:.2e}@{lab}" for k, (e, lab) in worst.items()))
+    if worst_out is not None:
+        for k, (e, lab) in worst.items():
+            if k not in worst_out or not e <= worst_out[k][0]:
+                worst_out[k] = (e, f"{label}{lab}")
     bad = {k: v for k, v in errs.items() if not v <= tol}
+    bad.update({f"{k}{lab}": e for k, (e, lab) in worst.items() if not e <= tol})
     assert not bad, f"{label}: outside tolerance {tol}: {bad}"
     return errs
 

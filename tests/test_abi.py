@@ -74,6 +74,25 @@ def test_cu_seqlens_validation(lib):
     assert B.rewy_workspace_bytes(d, 0) == 0 and "B == 1" in B.rewy_last_error()
 
 
+def test_layout_does_not_depend_on_the_host_copy_of_cu_seqlens(lib):
+    """Workspace and saved sizes (and so every buffer offset) are the same
+    with and without the optional host copy of cu_seqlens, so a caller may pass
+    it to one call and not to another; the layout is sized by the bound
+    ceil(T / 64) + N chunk slots."""
+    cu = (ctypes.c_int32 * 4)(0, 5, 69, 256)
+    for policy in (B.REWY_RECOMPUTE, B.REWY_SAVE):
+        with_host = _desc(N=3, cu_seqlens=8, cu_seqlens_host=ctypes.addressof(cu), policy=policy)
+        without = _desc(N=3, cu_seqlens=8, policy=policy)
+        for phase in (0, 1, 2):
+            assert B.rewy_workspace_bytes(with_host, phase) == B.rewy_workspace_bytes(without, phase) > 0
+        assert B.rewy_saved_bytes(with_host) == B.rewy_saved_bytes(without)
+    # sized by the bound: 256 / 64 + 3 = 7 chunk slots, as many as an unpacked
+    # 448-token sequence has (every buffer is sized by the chunk slots)
+    for phase in (0, 1):
+        assert B.rewy_workspace_bytes(_desc(N=3, cu_seqlens=8), phase) == \
+            B.rewy_workspace_bytes(_desc(T=7 * 64), phase)
+
+
 def test_workspace_sizes_follow_the_layout(lib):
     d = _desc()
     nc = 4  # 256 tokens / 64
@@ -83,19 +102,22 @@ def test_workspace_sizes_follow_the_layout(lib):
     tileK, tile64 = up(nc * H * K * 64 * e), up(nc * H * 64 * 64 * e)
     head = up(nc * 16) + up(2 * 4) + up(1 * 4)  # chunk records, seqoff [N+1], scan order [N]
     tileV = up(nc * H * V * 64 * e)
-    shared = up(nc * H * K * 4) + up(nc * H * K * V * e) + tileV       # glast, hbuf, R
+    glast = up(nc * H * K * 4)
+    states = up(nc * H * K * V * e) + tileV                             # hbuf, R
     scan = tokK + tileK + tokV                                          # W, Ft, U
     out = tileK + tile64                                                # Qg, Cq
     rscan = tokK + 2 * tileK + tile64                                   # F, Wt, Qgt, Cqt
     rscan += tile64 + up(nc * H * K * 64 * 4)                           # At, G2t
     rscan += up(nc * H * 4 * K * 16)                                    # Gst
     bwd = up(nc * H * V * 64 * e) + up(nc * H * K * V * e)              # Rbt, dhbuf
-    assert B.rewy_workspace_bytes(d, 0) == head + shared + scan + out
-    # the reverse-scan set of the backward reuses the output operands' space
-    assert B.rewy_workspace_bytes(d, 1) == head + shared + scan + rscan + bwd
+    shared = glast + states
+    # the forward of the recompute policy needs no per-chunk states or corrections
+    assert B.rewy_workspace_bytes(d, 0) == head + glast + scan + out
+    # the backward's buffers reuse the output operands' space
+    assert B.rewy_workspace_bytes(d, 1) == head + glast + scan + states + rscan + bwd
     # the gate formed in the kernels: per (chunk, head, wave) partial sums of
     # ddt_bias [K] and dA_log [1] follow the backward's buffers
-    assert B.rewy_workspace_bytes(d, 2) == head + shared + scan + rscan + bwd + up(nc * H * 4 * (K + 1) * 4)
+    assert B.rewy_workspace_bytes(d, 2) == head + glast + scan + states + rscan + bwd + up(nc * H * 4 * (K + 1) * 4)
     assert B.rewy_workspace_bytes(_desc(gate=B.REWY_GATE_SCALAR), 2) == 0
     assert "VECTOR" in B.rewy_last_error()
     assert B.rewy_workspace_bytes(d, 3) == 0 and "bad phase" in B.rewy_last_error()

@@ -62,7 +62,7 @@ def test_kda_gate_full_workload_sampled():
     dx, da, dd = oracle.kda_gate_backward(xs, al, db, rg["dg"])
     ref = dict(o=ro, ht=rht, dq=rg["dq"], dk=rg["dk"], dv=rg["dv"], dx=dx, da_log=da, ddt_bias=dd,
                dbeta=rg["dbeta"], dh0=rg["dh0"])
-    compare(hip, ref, TOL[inp.q.dtype], names=tuple(ref), label=f"{WORKLOAD}/kda-gate")
+    compare(hip, ref, TOL[inp.q.dtype], cu=inp.cu_seqlens, names=tuple(ref), label=f"{WORKLOAD}/kda-gate")
 
 
 def test_erase_write_full_workload_sampled():
@@ -86,7 +86,7 @@ def test_erase_write_full_workload_sampled():
     rg = oracle.backward(q, k, v, g, None, dO, scale=inp.scale, erase=bs, write=ws)
     ref = dict(o=ro, ht=rht, dq=rg["dq"], dk=rg["dk"], dv=rg["dv"], dg=rg["dg"], db=rg["derase"],
                dw=rg["dwrite"], dh0=rg["dh0"])
-    compare(hip, ref, TOL[inp.q.dtype], names=tuple(ref), label=f"{WORKLOAD}/erase-write")
+    compare(hip, ref, TOL[inp.q.dtype], cu=inp.cu_seqlens, names=tuple(ref), label=f"{WORKLOAD}/erase-write")
 
 
 def test_decode_bench_config():
@@ -100,4 +100,4 @@ def test_decode_bench_config():
     torch.cuda.synchronize()
     ro, rht = oracle.forward(inp.q, inp.k, inp.v, inp.g, inp.beta, scale=inp.scale, h0=inp.h0)
     compare(dict(o=o.double().cpu().numpy(), ht=ht.double().cpu().numpy()), dict(o=ro, ht=rht),
-            TOL[inp.q.dtype], names=("o", "ht"), label="decode-bench-config")
+            TOL[inp.q.dtype], cu=inp.cu_seqlens, names=("o", "ht"), label="decode-bench-config")

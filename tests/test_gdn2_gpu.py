@@ -73,7 +73,7 @@ def test_gdn2_matches_oracle(case, policy):
     inp = workloads.make_inputs(B, T, H, K, V, gate=gate, dtype=dt, seed=seed, h0=h0, dht=True,
                                 cu_seqlens=cu)
     b, w = _gates(inp, seed + 1)
-    compare(_hip(inp, b, w, policy), _oracle(inp, b, w), TOL[inp.q.dtype], names=NAMES,
+    compare(_hip(inp, b, w, policy), _oracle(inp, b, w), TOL[inp.q.dtype], cu=inp.cu_seqlens, names=NAMES,
             label=f"{name}/{policy}")
 
 
@@ -112,5 +112,5 @@ def test_gdn2_strong_decay_takes_pairwise_path():
     sub = G.reshape(1, 4, 4, 16, 2, 64)
     assert (sub.max(3) - sub.min(3)).max() > 128  # the fallback is really exercised
     b, w = _gates(inp, 41)
-    compare(_hip(inp, b, w, "recompute"), _oracle(inp, b, w), TOL[inp.q.dtype], names=NAMES,
+    compare(_hip(inp, b, w, "recompute"), _oracle(inp, b, w), TOL[inp.q.dtype], cu=inp.cu_seqlens, names=NAMES,
             label="gdn2-strong-decay")

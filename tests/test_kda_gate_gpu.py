@@ -87,7 +87,7 @@ def test_kda_gate_matches_oracle(case, policy):
     say(f"[case] {name} policy={policy}")
     inp, x, a_log, dt_bias = _inputs(*case)
     compare(_np(_hip_torch(inp, x, a_log, dt_bias, policy)), _oracle(inp, x, a_log, dt_bias),
-            TOL[inp.q.dtype], names=NAMES, label=f"{name}/{policy}")
+            TOL[inp.q.dtype], cu=inp.cu_seqlens, names=NAMES, label=f"{name}/{policy}")
 
 
 @pytest.mark.parametrize("case", BOUNDED, ids=[c[0] for c in BOUNDED])
@@ -97,7 +97,7 @@ def test_kda_gate_bounded_form_matches_oracle(case, policy):
     say(f"[case] {name} policy={policy} lower_bound={lb}")
     inp, x, a_log, dt_bias = _inputs(*case[:9], a_shift=shift)
     compare(_np(_hip_torch(inp, x, a_log, dt_bias, policy, lb)), _oracle(inp, x, a_log, dt_bias, lb),
-            TOL[inp.q.dtype], names=NAMES, label=f"{name}/{policy}")
+            TOL[inp.q.dtype], cu=inp.cu_seqlens, names=NAMES, label=f"{name}/{policy}")
 
 
 def test_kda_gate_agrees_with_the_explicit_gate():
@@ -136,7 +136,7 @@ def test_kda_gate_strong_decay_takes_pairwise_path():
     sub = G.reshape(1, 4, 4, 16, 2, 64)
     assert (sub.max(3) - sub.min(3)).max() > 128  # the fallback is really exercised
     compare(_np(_hip_torch(inp, x, a_log, dt_bias, "recompute")), _oracle(inp, x, a_log, dt_bias),
-            TOL[inp.q.dtype], names=NAMES, label="kda-gate-strong-decay")
+            TOL[inp.q.dtype], cu=inp.cu_seqlens, names=NAMES, label="kda-gate-strong-decay")
 
 
 def _hip_no_host_cu(inp, x, a_log, dt_bias, lb=0.0):
@@ -183,8 +183,8 @@ def test_kda_gate_parameter_gradients_are_deterministic():
         assert torch.equal(a[n], b[n]), n
     c = _hip_no_host_cu(inp, x, a_log, dt_bias)
     ref = _oracle(inp, x, a_log, dt_bias)
-    compare(_np(c), ref, TOL[inp.q.dtype], names=NAMES, label="kda-gate-device-cu")
-    compare(_np(a), ref, TOL[inp.q.dtype], names=NAMES, label="kda-gate-host-cu")
+    compare(_np(c), ref, TOL[inp.q.dtype], cu=inp.cu_seqlens, names=NAMES, label="kda-gate-device-cu")
+    compare(_np(a), ref, TOL[inp.q.dtype], cu=inp.cu_seqlens, names=NAMES, label="kda-gate-host-cu")
 
 
 def test_kda_gate_bounded_form_empty_slots_and_repeatability():
@@ -198,5 +198,36 @@ def test_kda_gate_bounded_form_empty_slots_and_repeatability():
     b = _hip_no_host_cu(inp, x, a_log, dt_bias, -4.0)
     for n in ("da_log", "ddt_bias", "dx"):
         assert torch.equal(a[n], b[n]), n
-    compare(_np(a), _oracle(inp, x, a_log, dt_bias, -4.0), TOL[inp.q.dtype], names=NAMES,
+    compare(_np(a), _oracle(inp, x, a_log, dt_bias, -4.0), TOL[inp.q.dtype], cu=inp.cu_seqlens, names=NAMES,
             label="kda-gate-bounded-device-cu")
+
+
+@pytest.mark.timeout(600)
+def test_kda_gate_long_strong_decay_two_heads_all_rows():
+    """The gate formed in the kernels on the long-context strong-decay workload
+    (B=4, T=32768, H=32, d=128, bf16, A_log ~ U(0, 1)) at full size.  The oracle
+    computes two heads over all four batch rows, so its dA_log and ddt_bias of
+    those heads sum every token of every sequence, as the kernels' do (about
+    sixteen times the terms of the KDA workload, with cancellation)."""
+    name = "kda_b4_t32768_h32_strong"
+    say(f"[case] {name} gate formed in the kernels: GPU")
+    inp = workloads.workload(name, device="cuda")
+    x = inp.gate_x.to(inp.q.dtype)
+    out = _hip_torch(inp, x, inp.a_log, inp.dt_bias, "recompute")
+    heads = [5, 30]
+
+    def pick(k, v):
+        if k in ("ht", "dh0"):
+            return v[:, heads]
+        if k in ("da_log", "ddt_bias"):
+            return v[heads]
+        return v[:, :, heads]
+
+    hip = {k: (None if v is None else pick(k, v).double().cpu().numpy()) for k, v in out.items()}
+    del out
+    cut = lambda t: t[:, :, heads].cpu()
+    sub = workloads.Inputs(name, cut(inp.q), cut(inp.k), cut(inp.v), None, cut(inp.beta), None,
+                           cut(inp.dO), None, None, inp.scale, inp.gate)
+    say(f"[case] {name} gate formed in the kernels: oracle heads {heads}, all rows")
+    ref = _oracle(sub, cut(x), inp.a_log[heads].cpu(), inp.dt_bias[heads].cpu())
+    compare(hip, ref, TOL[inp.q.dtype], names=NAMES, label=f"{name}/kda-gate")

@@ -46,7 +46,7 @@ def test_recurrent_matches_oracle(case):
                                   cu_seqlens=inp.cu_seqlens)
     torch.cuda.synchronize()
     hip = dict(o=o.double().cpu().numpy(), ht=ht.double().cpu().numpy())
-    compare(hip, _oracle_fwd(inp), TOL[inp.q.dtype], names=("o", "ht"), label=name)
+    compare(hip, _oracle_fwd(inp), TOL[inp.q.dtype], cu=inp.cu_seqlens, names=("o", "ht"), label=name)
 
 
 def test_recurrent_decode_steps_carry_the_state():
@@ -70,7 +70,7 @@ def test_recurrent_decode_steps_carry_the_state():
     # the same arithmetic in the same order: identical results
     assert torch.equal(torch.cat(outs, 1), o_all) and torch.equal(h, ht_all)
     hip = dict(o=o_all.double().cpu().numpy(), ht=ht_all.double().cpu().numpy())
-    compare(hip, _oracle_fwd(inp), TOL[inp.q.dtype], names=("o", "ht"), label="decode-steps")
+    compare(hip, _oracle_fwd(inp), TOL[inp.q.dtype], cu=inp.cu_seqlens, names=("o", "ht"), label="decode-steps")
 
 
 def test_recurrent_agrees_with_the_chunked_forward():
@@ -125,7 +125,7 @@ def test_recurrent_erase_write_matches_oracle(case):
     ro, rht = oracle.forward(inp.q, inp.k, inp.v, inp.g, None, scale=inp.scale, h0=inp.h0,
                              cu_seqlens=cuv, erase=b, write=w)
     compare(dict(o=o.double().cpu().numpy(), ht=ht.double().cpu().numpy()), dict(o=ro, ht=rht),
-            TOL[inp.q.dtype], names=("o", "ht"), label=name)
+            TOL[inp.q.dtype], cu=inp.cu_seqlens, names=("o", "ht"), label=name)
 
 
 def test_recurrent_erase_write_agrees_with_chunked_and_shared_beta():

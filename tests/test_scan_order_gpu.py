@@ -45,5 +45,5 @@ def test_varlen_scan_order_matches_oracle(case, policy):
     say(f"[case] {name} policy={policy} sequences={len(lens)} tokens={cu[-1]}")
     inp = workloads.make_inputs(1, cu[-1], H, K, V, gate=gate, dtype=dt, seed=17, h0="normal",
                                 dht=True, cu_seqlens=cu)
-    compare(hip_run(inp, policy=policy, want_dh0=True), oracle_run(inp), TOL[inp.q.dtype],
+    compare(hip_run(inp, policy=policy, want_dh0=True), oracle_run(inp), TOL[inp.q.dtype], cu=inp.cu_seqlens,
             label=f"{name}/{policy}")
