@@ -91,7 +91,7 @@ def kernel_role(name):
             "k_bwd_chunk": "bwd_chunk"}.get(stage, "other")
 
 
-# ---- the method's compulsory bytes per launch (SURVEY 8(d) convention) ----------
+# ---- the method's compulsory bytes per launch ----------------------------------
 
 def method_bytes(role, n_tokens, H, K, V, esz, besz, gate, nseq, has_h0, has_dht):
     """Compulsory HBM bytes of the method that one launch of `role` moves: the
@@ -569,7 +569,7 @@ def main():
     ddesign = design_bytes(drole, chunk_lens, H, K, V, esz, besz, gate, nseq, args.policy)
     achieved = dbytes / (dom_avg * 1e-3) / 1e9
     traffic = measured_traffic(dlabel, args.workload, args.policy)
-    # whole step: the pass floors of SURVEY 8(d), forward 1,538 B and backward
+    # whole step: the pass floors, forward 1,538 B and backward
     # 2,820 B per token-head (+ states), over the whole step's time
     step_floor = (mb("prep_forward") + mb("fwd_scan")) + mb("bwd_chunk")
     roofline = {
