@@ -17,7 +17,10 @@ REWY_GATE_NONE, REWY_GATE_SCALAR, REWY_GATE_VECTOR = 0, 1, 2
 REWY_BF16, REWY_F32 = 0, 1
 REWY_RECOMPUTE, REWY_SAVE = 0, 1
 
-EXPORTS = ("rewy_workspace_bytes", "rewy_saved_bytes", "rewy_fwd", "rewy_bwd", "rewy_fwd_gdn2",
+NOALLOC_SCRATCH_BYTES = 128 << 20  # REWY_NOALLOC_SCRATCH_BYTES
+
+EXPORTS = ("rewy_workspace_bytes", "rewy_saved_bytes", "rewy_fwd", "rewy_bwd", "rewy_fwd_noalloc",
+           "rewy_fwd_gdn2",
            "rewy_bwd_gdn2", "rewy_fwd_kda_gate", "rewy_bwd_kda_gate", "rewy_recurrent_fwd",
            "rewy_recurrent_fwd_gdn2",
            "rewy_trace_begin", "rewy_trace_end", "rewy_trace_select", "rewy_status_string",
@@ -68,6 +71,8 @@ def load():
         lib.rewy_fwd.restype = ctypes.c_int
         lib.rewy_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
         lib.rewy_bwd.restype = ctypes.c_int
+        lib.rewy_fwd_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+        lib.rewy_fwd_noalloc.restype = ctypes.c_int
         lib.rewy_fwd_gdn2.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
         lib.rewy_fwd_gdn2.restype = ctypes.c_int
         lib.rewy_bwd_gdn2.argtypes = [D] + [P] * 18 + [S, P]
@@ -106,6 +111,10 @@ def rewy_saved_bytes(desc: RewyDesc) -> int:
 def rewy_fwd(desc, q, k, v, g, beta, h0, o, ht, saved, workspace, ws_bytes, stream) -> int:
     return load().rewy_fwd(ctypes.byref(desc), q, k, v, g, beta, h0, o, ht, saved, workspace,
                            ws_bytes, stream)
+
+
+def rewy_fwd_noalloc(desc, q, k, v, g, beta, h0, o, ht, saved, stream) -> int:
+    return load().rewy_fwd_noalloc(ctypes.byref(desc), q, k, v, g, beta, h0, o, ht, saved, stream)
 
 
 def rewy_bwd(desc, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0, workspace,

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -395,6 +396,71 @@ REWY_API int rewy_fwd(const rewy_desc* d, const void* q, const void* k, const vo
                       void* saved, void* workspace, size_t ws_bytes, void* stream) {
   return forward_impl(d, q, k, v, g, beta, nullptr, nullptr, h0, o, ht, saved, workspace, ws_bytes,
                       stream);
+}
+
+// ---- the allocation-free forward ---------------------------------------------
+// Its workspace is this file-scope device array, one copy per GPU (the loader
+// places it in each device's memory when the library's code is loaded there,
+// and it stays until the process ends).  In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, once per device,
+// and only that address is ever handed to kernels.
+namespace rewy {
+static __device__ __align__(256) unsigned char scratch[REWY_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device (resolved on the first
+// call there), or nullptr with the error recorded.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+    fail(REWY_EHIP, "allocation-free forward: no current device (or more than %d)", MAX_DEVICES);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(REWY_EHIP, "allocation-free forward: hipGetSymbolAddress: %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+}  // namespace
+}  // namespace rewy
+
+REWY_API int rewy_fwd_noalloc(const rewy_desc* d, const void* q, const void* k, const void* v,
+                              const float* g, const void* beta, const float* h0, void* o,
+                              float* ht, void* saved, void* stream) {
+  // the size check comes first and touches no device
+  Plan p;
+  const int rc = make_plan(d, p);
+  if (rc) return rc;
+  const size_t need = layout(p).ws_fwd;
+  if (need > (size_t)REWY_NOALLOC_SCRATCH_BYTES)
+    return fail(REWY_EWORKSPACE,
+                "rewy_fwd_noalloc: this problem needs %zu bytes of workspace, above the %zu-byte "
+                "device scratch of the allocation-free forward (use rewy_fwd with a workspace)",
+                need, (size_t)REWY_NOALLOC_SCRATCH_BYTES);
+  if (stream) {  // kernels and the scratch address must belong to the stream's device
+    int sdev = -1, cur = -1;
+    if (hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev) != hipSuccess ||
+        hipGetDevice(&cur) != hipSuccess)
+      return fail(REWY_EHIP, "rewy_fwd_noalloc: cannot query the stream's device");
+    if (sdev != cur)
+      return fail(REWY_EINVAL, "rewy_fwd_noalloc: the stream belongs to device %d, the current "
+                  "device is %d", sdev, cur);
+  }
+  void* ws = scratch_on_current_device();
+  if (!ws) return REWY_EHIP;
+  return forward_impl(d, q, k, v, g, beta, nullptr, nullptr, h0, o, ht, saved, ws,
+                      (size_t)REWY_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 REWY_API int rewy_fwd_kda_gate(const rewy_desc* d, const void* q, const void* k, const void* v,

@@ -117,6 +117,26 @@ int rewy_bwd(const rewy_desc *d, const void *q, const void *k, const void *v,
              void *dq, void *dk, void *dv, float *dg, void *dbeta, float *dh0,
              void *workspace, size_t ws_bytes, void *stream);
 
+/* Forward without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Computes exactly what rewy_fwd computes (the same kernels
+ * in the same order: bitwise the same o, ht and saved buffer), with the
+ * workspace taken from a device array of REWY_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  The caller
+ * still passes every input and output (and, for policy SAVE, the saved
+ * buffer).  A problem whose rewy_workspace_bytes(d, 0) exceeds that size
+ * returns REWY_EWORKSPACE before anything is enqueued; at K = V = 128 in bf16
+ * the forward needs about 1.2 KB per token and head, so the scratch serves up
+ * to about 110 k token-heads (e.g. T = 3.5 k at H = 32).  The stream must
+ * belong to the current device.  Every call on one GPU uses the same scratch:
+ * calls that overlap in time on one GPU (different streams, or threads)
+ * race and must be serialised by the caller.  Nothing in the scratch needs
+ * clearing between calls: every element a call reads, it has written first. */
+#define REWY_NOALLOC_SCRATCH_BYTES (128u << 20)
+int rewy_fwd_noalloc(const rewy_desc *d, const void *q, const void *k, const void *v,
+                     const float *g, const void *beta, const float *h0,
+                     void *o, float *ht, void *saved, void *stream);
+
 /* The erase/write form (ReWY paper Table 1, GDN2 row; GDN2 spec section 2):
  * independent erase and write vector gates in place of the shared beta,
  *     r_t = w_t * v_t - S~^T (b_t * k_t),   S = S~ + k_t r_t^T,

@@ -202,6 +202,22 @@ def test_calls_reject_bad_pointers_without_launching(lib):
     del ws
 
 
+def test_noalloc_forward_rejects_problems_beyond_its_scratch(lib):
+    """rewy_fwd_noalloc refuses, on the host and before touching any device, a
+    problem whose forward workspace exceeds the fixed device scratch."""
+    P = ctypes.c_void_p
+    big = _desc(B=1, T=65536, H=32)  # about 4.7 GB of workspace
+    assert B.rewy_workspace_bytes(big, 0) > B.NOALLOC_SCRATCH_BYTES
+    rc = B.rewy_fwd_noalloc(big, P(256), P(256), P(256), P(256), P(256), None, P(256), None, None,
+                            None)
+    assert rc == B.REWY_EWORKSPACE
+    assert "rewy_fwd_noalloc" in B.rewy_last_error() and "scratch" in B.rewy_last_error()
+    # argument errors come first, as for rewy_fwd
+    rc = B.rewy_fwd_noalloc(_desc(K=48), P(256), P(256), P(256), P(256), P(256), None, P(256),
+                            None, None, None)
+    assert rc == B.REWY_EUNSUPPORTED
+
+
 def test_product_path_has_no_fallback():
     """The package never imports the oracle and raises when the library is missing."""
     import chunkwise_delta_rule_chunk_amd as pkg
