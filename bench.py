@@ -75,8 +75,11 @@ def kernel_label(name):
         return f"{stage} (BV={args[3]})"
     if stage == "k_bwd_chunk" and len(args) >= 4:
         gx = int(args[3])
+        if gx & 16:
+            return "k_bwd_chunk (producer)"
         kind = {0: "no gate", 1: "scalar gate", 2: "vector gate"}[gx & 3]
-        return f"k_bwd_chunk ({kind}{', erase/write' if gx & 4 else ''}{', gate in kernel' if gx & 8 else ''})"
+        return (f"k_bwd_chunk ({'consumers, ' if gx & 32 else ''}{kind}"
+                f"{', erase/write' if gx & 4 else ''}{', gate in kernel' if gx & 8 else ''})")
     return stage
 
 
@@ -87,6 +90,9 @@ def kernel_role(name):
     stage, args = parse_kernel(name)
     if stage == "k_fwd_prep":
         return "prep_recompute" if len(args) >= 4 and (int(args[3]) & 2) == 0 else "prep_forward"
+    if stage == "k_bwd_chunk" and len(args) >= 4:
+        gx = int(args[3])
+        return "bwd_producer" if gx & 16 else "bwd_consumers" if gx & 32 else "bwd_chunk"
     return {"k_fwd_scan": "fwd_scan", "k_bwd_scan": "bwd_scan", "k_scans": "scans",
             "k_bwd_chunk": "bwd_chunk"}.get(stage, "other")
 
@@ -112,6 +118,10 @@ def method_bytes(role, n_tokens, H, K, V, esz, besz, gate, nseq, has_h0, has_dht
         "bwd_scan": tv,
         "scans": tv,
         "bwd_chunk": 2 * (2 * tk + tv + gb + besz) + tv,
+        # the separate schedule splits that floor: v, beta in and dv out for
+        # the producer; the rest for the consumers
+        "bwd_producer": 2 * tv + besz,
+        "bwd_consumers": 2 * (2 * tk + gb) + tv + 2 * besz,
     }.get(role)
     if per is None:
         return None
@@ -125,7 +135,8 @@ def method_bytes(role, n_tokens, H, K, V, esz, besz, gate, nseq, has_h0, has_dht
 
 def method_flops(role, seq_lens, H, K, V, flops):
     key = {"prep_forward": "prep_forward", "fwd_scan": "fwd_scan", "bwd_scan": "bwd_scan",
-           "scans": "bwd_scan", "bwd_chunk": "bwd_chunk"}.get(role)
+           "scans": "bwd_scan", "bwd_chunk": "bwd_chunk", "bwd_producer": "bwd_producer",
+           "bwd_consumers": "bwd_consumers"}.get(role)
     return 0 if key is None else flops.kernel_flops(key, seq_lens, H, K, V)
 
 
@@ -452,6 +463,10 @@ def main():
                     help="skip timing the step with the gate formed in the kernels")
     ap.add_argument("--no-gdn2", action="store_true",
                     help="skip timing the erase/write form")
+    ap.add_argument("--no-schedules", action="store_true",
+                    help="skip timing the separate producer-consumer schedule of the backward")
+    ap.add_argument("--schedule", default="joint", choices=["joint", "separate"],
+                    help="the chunk backward's schedule for the headline run (profiler runs)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replayed 60-observation protocol (profiler runs)")
     ap.add_argument("--no-peaks", action="store_true",
@@ -471,6 +486,8 @@ def main():
     from chunkwise_delta_rule_chunk_amd import binding, flops, ops
 
     dev = torch.device("cuda:0")
+    if args.schedule == "separate":
+        binding.rewy_bwd_schedule(binding.REWY_SCHEDULE_SEPARATE)
     inp = workloads.workload(args.workload)  # CPU generator, then resident in HBM
     x = inp.to(dev)
     B, T, H, K, V = inp.shape
@@ -640,6 +657,25 @@ def main():
         print(f"[bench] {other} policy: {ms2:.3f} ms/step", file=sys.stderr, flush=True)
         del step2
     result["memory_bytes"] = mem
+
+    # The other schedule of the chunk backward (ReWY paper, "Execution and
+    # numerical precision": joint or separate consumers), same policy and
+    # inputs: the producer hands P, D and the write part of dbeta to the
+    # consumers through the workspace.
+    if not args.no_schedules and args.schedule == "joint":
+        prev = binding.rewy_bwd_schedule(binding.REWY_SCHEDULE_SEPARATE)
+        try:
+            step3 = Step(x, inp, args.policy, torch, ops, binding)
+            ms3, kern3 = _timed(step3, args.steps, max(3, args.warmup // 4), torch, binding)
+            sep = {"policy": args.policy, "ms_per_step": ms3, "value": n_tokens / (ms3 * 1e-3),
+                   "unit": "tokens/s", "workspace_bwd": step3.ws1.numel(), "kernels_ms": kern3}
+            if not args.no_graph:
+                sep["graph_protocol"] = graph_protocol(step3, torch)
+            result["separate_schedule"] = sep
+            del step3
+        finally:
+            binding.rewy_bwd_schedule(prev)
+        print(f"[bench] separate schedule: {ms3:.3f} ms/step", file=sys.stderr, flush=True)
     if not args.no_decode:
         _time_decode(result, args, ops, binding, torch)
     if not args.no_gdn2:

@@ -16,6 +16,7 @@ REWY_OK, REWY_EINVAL, REWY_EUNSUPPORTED, REWY_EWORKSPACE, REWY_EHIP = 0, -1, -2,
 REWY_GATE_NONE, REWY_GATE_SCALAR, REWY_GATE_VECTOR = 0, 1, 2
 REWY_BF16, REWY_F32 = 0, 1
 REWY_RECOMPUTE, REWY_SAVE = 0, 1
+REWY_SCHEDULE_JOINT, REWY_SCHEDULE_SEPARATE = 0, 1
 
 NOALLOC_SCRATCH_BYTES = 128 << 20  # REWY_NOALLOC_SCRATCH_BYTES
 
@@ -23,7 +24,8 @@ EXPORTS = ("rewy_workspace_bytes", "rewy_saved_bytes", "rewy_fwd", "rewy_bwd", "
            "rewy_fwd_gdn2",
            "rewy_bwd_gdn2", "rewy_fwd_kda_gate", "rewy_bwd_kda_gate", "rewy_recurrent_fwd",
            "rewy_recurrent_fwd_gdn2",
-           "rewy_trace_begin", "rewy_trace_end", "rewy_trace_select", "rewy_status_string",
+           "rewy_bwd_schedule", "rewy_trace_begin", "rewy_trace_end", "rewy_trace_select",
+           "rewy_status_string",
            "rewy_last_error")
 
 
@@ -86,6 +88,8 @@ def load():
         lib.rewy_recurrent_fwd.restype = ctypes.c_int
         lib.rewy_recurrent_fwd_gdn2.argtypes = [D] + [P] * 10
         lib.rewy_recurrent_fwd_gdn2.restype = ctypes.c_int
+        lib.rewy_bwd_schedule.argtypes = [ctypes.c_int]
+        lib.rewy_bwd_schedule.restype = ctypes.c_int
         lib.rewy_trace_begin.argtypes = []
         lib.rewy_trace_begin.restype = ctypes.c_int
         lib.rewy_trace_end.argtypes = [ctypes.POINTER(RewyTraceEntry), ctypes.c_int]
@@ -153,6 +157,16 @@ def rewy_recurrent_fwd(desc, q, k, v, g, beta, h0, o, ht, stream) -> int:
 
 def rewy_recurrent_fwd_gdn2(desc, q, k, v, g, b, w, h0, o, ht, stream) -> int:
     return load().rewy_recurrent_fwd_gdn2(ctypes.byref(desc), q, k, v, g, b, w, h0, o, ht, stream)
+
+
+def rewy_bwd_schedule(schedule: int) -> int:
+    """Set the chunk backward's schedule for later calls (REWY_SCHEDULE_JOINT or
+    REWY_SCHEDULE_SEPARATE); returns the previous one (a negative argument only
+    queries)."""
+    rc = load().rewy_bwd_schedule(schedule)
+    if rc < 0 and schedule >= 0:
+        raise RewyError(rc, "rewy_bwd_schedule")
+    return rc
 
 
 def rewy_trace_begin() -> int:

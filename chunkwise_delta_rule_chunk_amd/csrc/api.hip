@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -44,8 +45,12 @@ struct Plan {
   int64_t BT;  // packed tokens
   bool f32, beta_f32;
   int gate, policy;
+  int sched;   // REWY_SCHEDULE_* of the chunk backward
   size_t esz;
 };
+
+// Schedule of the chunk backward for later calls (rewy_bwd_schedule).
+std::atomic<int> g_schedule{REWY_SCHEDULE_JOINT};
 
 int kv_supported(int K, int V, bool f32) {
   auto ok = [](int x) { return x == 32 || x == 64 || x == 128; };
@@ -69,6 +74,7 @@ int make_plan(const rewy_desc* d, Plan& p) {
     return fail(REWY_EUNSUPPORTED, "K=%d V=%d not supported for %s (K, V in {32,64,128}; fp32 <= 64)",
                 d->K, d->V, f32 ? "fp32" : "bf16");
   p.B = d->B; p.T = d->T; p.H = d->H; p.K = d->K; p.V = d->V;
+  p.sched = g_schedule.load();
   p.f32 = f32; p.beta_f32 = d->beta_dtype == REWY_F32; p.gate = d->gate; p.policy = d->policy;
   p.esz = f32 ? 4 : 2;
   p.BT = (int64_t)d->B * d->T;
@@ -116,6 +122,7 @@ struct Layout {
   size_t F, Wt, Qgt, Cqt;            // reverse scan operands
   size_t At, G2t, Gst;               // chunk backward operands
   size_t Rbt, dhbuf;                 // written by the reverse scan
+  size_t Pbuf, Dfrag, Ddiag, dbw;    // separate schedule: producer to consumers
   size_t gpart;                      // gate in the kernel: [nc,H,NSUB,K] then [nc,H,NSUB] fp32
   size_t ws_fwd, ws_bwd, ws_gin, saved;
 };
@@ -171,6 +178,12 @@ Layout layout(const Plan& p) {
   }
   L.Rbt = take(off, tileV);
   L.dhbuf = take(off, states);
+  if (p.sched == REWY_SCHEDULE_SEPARATE) {
+    L.Pbuf = take(off, tileV);
+    L.Dfrag = take(off, nc * H * NSUB * NSUB * 2 * 64 * 4 * e);
+    L.Ddiag = take(off, nc * H * NSUB * SUB * SUB * 4);
+    L.dbw = take(off, nc * H * CH * 4);
+  }
   L.ws_bwd = off;
   L.gpart = take(off, nc * H * NSUB * (K + 1) * 4);
   L.ws_gin = off;
@@ -214,6 +227,12 @@ void fill_common(Args& a, const Plan& p, const rewy_desc* d, char* ws, char* sv,
   a.G2t = reinterpret_cast<float*>(fs + L.G2t);
   a.Gst = reinterpret_cast<float*>(fs + L.Gst);
   a.Rbt = ws + L.Rbt; a.dhbuf = ws + L.dhbuf;
+  if (p.sched == REWY_SCHEDULE_SEPARATE) {
+    a.Pbuf = ws + L.Pbuf;
+    a.Dfrag = ws + L.Dfrag;
+    a.Ddiag = reinterpret_cast<float*>(ws + L.Ddiag);
+    a.dbw = reinterpret_cast<float*>(ws + L.dbw);
+  }
 }
 
 int check_tensor_ptrs(const void* const* ps, const char* const* names, int n) {
@@ -616,9 +635,18 @@ int backward_impl(const rewy_desc* d, const void* q, const void* k, const void* 
                         "reverse scan")))
       return rc;
   }
-  if ((rc = hip_check(traced("k_bwd_chunk", s, [&] { return launch_bwd_chunk(a, f32, s); }),
-                      "chunk backward")))
+  // the separate schedule serves the shared-beta forms; the others run joint
+  if (p.sched == REWY_SCHEDULE_SEPARATE && !ew && !gi) {
+    if ((rc = hip_check(traced("k_bwd_chunk", s, [&] { return launch_bwd_producer(a, f32, s); }),
+                        "chunk backward producer")))
+      return rc;
+    if ((rc = hip_check(traced("k_bwd_chunk", s, [&] { return launch_bwd_consumers(a, f32, s); }),
+                        "chunk backward consumers")))
+      return rc;
+  } else if ((rc = hip_check(traced("k_bwd_chunk", s, [&] { return launch_bwd_chunk(a, f32, s); }),
+                             "chunk backward"))) {
     return rc;
+  }
   if (gi && (rc = hip_check(traced("k_gate_reduce", s, [&] { return launch_gate_reduce(a, s); }),
                             "gate parameter gradients")))
     return rc;
@@ -657,6 +685,13 @@ REWY_API int rewy_bwd_gdn2(const rewy_desc* d, const void* q, const void* k, con
   if (!b || !w) return fail(REWY_EINVAL, "b and w must be given");
   return backward_impl(d, q, k, v, g, b, w, nullptr, h0, dO, dht, saved, dq, dk, dv, dg, db, dw,
                        nullptr, dh0, workspace, ws_bytes, stream);
+}
+
+REWY_API int rewy_bwd_schedule(int schedule) {
+  if (schedule < 0) return g_schedule.load();
+  if (schedule != REWY_SCHEDULE_JOINT && schedule != REWY_SCHEDULE_SEPARATE)
+    return fail(REWY_EINVAL, "bad schedule %d", schedule);
+  return g_schedule.exchange(schedule);
 }
 
 REWY_API int rewy_trace_begin(void) {

@@ -49,12 +49,24 @@ namespace rewy {
 // each wave writes its partial sums of dA_log (sum of dg g for the softplus
 // form, of dx z for the bounded form) and of ddt_bias = sum over tokens of dx,
 // for a later reduction over chunks.
+//
+// GX & 16 (PROD) and GX & 32 (CONS) split the kernel for the separate
+// schedule of the ReWY paper ("Execution and numerical precision", joint and
+// separate consumers): PROD runs the producer only (P, dv, the write part of
+// dbeta and D, written to the workspace; it needs no gate), CONS the
+// consumers only (P, D and the write part of dbeta read back, Hq formed as
+// in the joint kernel).  Every value is rounded at the same point in both
+// schedules, so their results are bitwise equal.
 template <typename T, int K, int V, int GX>
 __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   constexpr int GATE = GX & 3;
   constexpr bool EW = GX & 4;
   constexpr bool GIN = GX & 8;
+  constexpr bool PROD = GX & 16, CONS = GX & 32;
   static_assert(!GIN || (GATE == 2 && !EW), "the gate is formed in the kernel for the vector gate");
+  static_assert(!(PROD && CONS) && (!(PROD || CONS) || (!EW && !GIN)),
+                "the separate schedule serves the shared-beta forms");
+  static_assert(!PROD || GATE == 0, "the producer does not depend on the gate");
   constexpr int NTH = 256;
   constexpr int PV = pitch<T>(V), PA = pitch<T>(CH);
   constexpr int NFB = K / SUB, NVB = V / SUB;
@@ -113,17 +125,26 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   const GBuf bv = gbuf(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, tile_bytes<T>(n, gsV, V));
   const int k0a = (I * SUB / KS) * KS;  // A^T is upper triangular: tokens j >= 16 I
   {
-    TileRegs<T, CH, V, NTH> pO, pR;
+    // the producer reads no dO; the consumers read P (and the write part of
+    // dbeta) in place of A^T and Rbar
+    TileRegs<T, CH, V, NTH> pO, pR, pP;
     TileRegs<T, CH, CH, NTH> pA;
-    pO.load(gbuf(reinterpret_cast<const T*>(a.dO) + (t0 * H + h) * V, tile_bytes<T>(n, gsV, V)), gsV, tid);
+    if constexpr (!PROD)
+      pO.load(gbuf(reinterpret_cast<const T*>(a.dO) + (t0 * H + h) * V, tile_bytes<T>(n, gsV, V)), gsV, tid);
     // R per chunk-head, column-blocked [V/16][64][16], zero past the chunk's end
     pR.load_cb(gbuf(reinterpret_cast<const T*>(a.R) + cb * V * CH, V * CH * sizeof(T)), CH, 0, tid);
-    pA.load(gbuf(reinterpret_cast<const T*>(a.At) + cb * CH * CH, CH * CH * sizeof(T)), CH, tid);
+    if constexpr (!CONS)
+      pA.load(gbuf(reinterpret_cast<const T*>(a.At) + cb * CH * CH, CH * CH * sizeof(T)), CH, tid);
+    else
+      pP.load(gbuf(reinterpret_cast<const T*>(a.Pbuf) + cb * CH * V, CH * V * sizeof(T)), V, tid);
     const uint32_t braw = EW ? 0u : ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, n - 1)) * H + h);
-    pO.store(sO, PV, tid);
+    const float dbwr = CONS ? a.dbw[cb * CH + (tid & (CH - 1))] : 0.f;
+    if constexpr (!PROD) pO.store(sO, PV, tid);
     pR.store_cb(sR, PV, tid);
-    pA.store(sAt, PA, tid);
+    if constexpr (!CONS) pA.store(sAt, PA, tid);
+    else pP.store(sP, PV, tid);
     if (tid < CH) sBeta[tid] = (tid < n && !EW) ? beta_val(braw, a.beta_f32) : 0.f;
+    if (CONS && tid < CH) sDbw[tid] = dbwr;
   }
 
   // ---- P = A^T Rbar, rows of block I; dv and the write part of dbeta --------
@@ -131,7 +152,9 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   // row i = 16 I + (l & 15) and the four columns v0 .. v0 + 3, v0 = 16 vb + 4 (l >> 4).
   // All value blocks are computed first, then each row of dv is written in one
   // sweep (whole rows reach the cache together and leave it as full lines).
-  {
+  // The producer of the separate schedule also writes P (rounded as the
+  // consumers read it) and the write part of dbeta to the workspace.
+  if constexpr (!CONS) {
     const T* Rbt = reinterpret_cast<const T*>(a.Rbt) + cb * V * CH;
     const GBuf bdv = gbuf(reinterpret_cast<T*>(a.dv) + (t0 * H + h) * V, tile_bytes<T>(n, gsV, V));
     const int k0 = k0a;
@@ -198,9 +221,15 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
     }
     const float b = sBeta[i];
     float dbw = 0.f;
+    const GBuf bpo = gbuf(reinterpret_cast<T*>(a.Pbuf) + cb * CH * V, PROD ? CH * V * sizeof(T) : 0u);
     static_for<0, NVB>([&](auto vb) {
       const int v0 = vb * SUB + 4 * q4;
       *reinterpret_cast<FR*>(sP + i * PV + v0) = to_frag<T>(acc[vb]);
+      if constexpr (PROD) {
+        const uint32_t off = (uint32_t)((i * V + v0) * (int)sizeof(T));
+        if constexpr (std::is_same_v<T, bf16>) gst8(bpo, off, __builtin_bit_cast(uint2, to_frag<T>(acc[vb])));
+        else gst16(bpo, off, __builtin_bit_cast(uint4, acc[vb]));
+      }
       const FR x = __builtin_bit_cast(FR, vr[vb]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) dbw += tof(x[e]) * acc[vb][e];
@@ -229,30 +258,34 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
       }
     });
     dbw = rows_sum(dbw);
-    if (q4 == 0) sDbw[i] = dbw;
+    if (q4 == 0) {
+      if constexpr (PROD) a.dbw[cb * CH + i] = dbw;
+      else sDbw[i] = dbw;
+    }
   }
-  lds_barrier();  // P complete; A^T is dead
+  lds_barrier();  // P complete (loaded, for the consumers); A^T is dead
 
   // ---- left operands of block I, straight into fragments ---------------------
   //   Dm[J]  = D[I, J]      (J <= I)    Hm[J]  = Hq[I, J]      (J <= I)
   //   Dtm[J] = D[J, I]^T    (J >= I)    Htm[J] = Hq[J, I]^T    (J >= I)
   // The fragment of M is the C tile of M^T; lane l holds M(l & 15, 4 (l >> 4) + e).
   FR Dm[NSUB], Hm[NSUB], Dtm[NSUB], Htm[NSUB];
+  f32x4 ddiag = zero4();  // this lane's four values of the diagonal block D_II (fp32)
   static_for<0, NSUB>([&](auto J) {
     Dm[J] = Hm[J] = Dtm[J] = Htm[J] = to_frag<T>(zero4());
     if (!live || J * SUB >= n) return;
     if (J <= I) {
       f32x4 yd = zero4(), yh = zero4();
-      mma_tile<T, true, true>(yd, sR + J * SUB * PV, PV, 1, sP + I * SUB * PV, PV, 1, V);
-      mma_tile<T, true, true>(yh, sR + J * SUB * PV, PV, 1, sO + I * SUB * PV, PV, 1, V);
+      if constexpr (!CONS) mma_tile<T, true, true>(yd, sR + J * SUB * PV, PV, 1, sP + I * SUB * PV, PV, 1, V);
+      if constexpr (!PROD) mma_tile<T, true, true>(yh, sR + J * SUB * PV, PV, 1, sO + I * SUB * PV, PV, 1, V);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int jj = 4 * q4 + e;  // column of M inside block J; row is f
         yd[e] = (J < I || jj < f) ? -yd[e] : 0.f;
         yh[e] = (J < I || jj <= f) ? yh[e] : 0.f;
         if (J == I) {
-          sDiag[f * PD + jj] = yd[e];
-          sDiag[SUB * PD + f * PD + jj] = yh[e];
+          if constexpr (!CONS) sDiag[f * PD + jj] = ddiag[e] = yd[e];
+          if constexpr (!PROD) sDiag[SUB * PD + f * PD + jj] = yh[e];
         }
       }
       Dm[J] = to_frag<T>(yd);
@@ -260,8 +293,8 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
     }
     if (J >= I) {
       f32x4 yd = zero4(), yh = zero4();
-      mma_tile<T, true, true>(yd, sP + J * SUB * PV, PV, 1, sR + I * SUB * PV, PV, 1, V);
-      mma_tile<T, true, true>(yh, sO + J * SUB * PV, PV, 1, sR + I * SUB * PV, PV, 1, V);
+      if constexpr (!CONS) mma_tile<T, true, true>(yd, sP + J * SUB * PV, PV, 1, sR + I * SUB * PV, PV, 1, V);
+      if constexpr (!PROD) mma_tile<T, true, true>(yh, sO + J * SUB * PV, PV, 1, sR + I * SUB * PV, PV, 1, V);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int jj = 4 * q4 + e;
@@ -272,6 +305,44 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
       Htm[J] = to_frag<T>(yh);
     }
   });
+  // Separate schedule: D leaves the producer as the operand fragments the
+  // consumers use, [wave I][J][D[I, J] | D[J, I]^T][lane][4] in the feature
+  // dtype, and its diagonal blocks in fp32, [I][16 rows][16]; the consumers
+  // read them back in place of computing D.
+  if constexpr (PROD || CONS) {
+    constexpr int FB = 4 * (int)sizeof(T);  // bytes of one lane's fragment
+    const GBuf bdf = gbuf(reinterpret_cast<T*>(a.Dfrag) + cb * NSUB * NSUB * 2 * 64 * 4,
+                          NSUB * NSUB * 2 * 64 * FB);
+    const GBuf bdd = gbuf(a.Ddiag + cb * NSUB * SUB * SUB, NSUB * SUB * SUB * 4);
+    auto foff = [&](int J, int kind) { return (uint32_t)((((I * NSUB + J) * 2 + kind) * 64 + l) * FB); };
+    const uint32_t doff = (uint32_t)((I * SUB * SUB + f * SUB + 4 * q4) * 4);
+    if constexpr (PROD) {
+      static_for<0, NSUB>([&](auto J) {
+        if constexpr (std::is_same_v<T, bf16>) {
+          gst8(bdf, foff(J, 0), __builtin_bit_cast(uint2, Dm[J]));
+          gst8(bdf, foff(J, 1), __builtin_bit_cast(uint2, Dtm[J]));
+        } else {
+          gst16(bdf, foff(J, 0), __builtin_bit_cast(uint4, Dm[J]));
+          gst16(bdf, foff(J, 1), __builtin_bit_cast(uint4, Dtm[J]));
+        }
+      });
+      gst16(bdd, doff, __builtin_bit_cast(uint4, ddiag));
+      return;  // every wave of the producer ends here
+    } else {
+      static_for<0, NSUB>([&](auto J) {
+        if constexpr (std::is_same_v<T, bf16>) {
+          Dm[J] = __builtin_bit_cast(FR, gld8(bdf, foff(J, 0)));
+          Dtm[J] = __builtin_bit_cast(FR, gld8(bdf, foff(J, 1)));
+        } else {
+          Dm[J] = __builtin_bit_cast(FR, gld16(bdf, foff(J, 0)));
+          Dtm[J] = __builtin_bit_cast(FR, gld16(bdf, foff(J, 1)));
+        }
+      });
+      ddiag = __builtin_bit_cast(f32x4, gld16(bdd, doff));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sDiag[f * PD + 4 * q4 + e] = ddiag[e];
+    }
+  }
   lds_barrier();  // diagonal blocks in sDiag visible to every lane of the wave
 
   // ---- per 16-feature block: state products, matrix intra, chain rules -------
@@ -812,9 +883,26 @@ static hipError_t bwd_chunk_t(const Args& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 }
+template <typename T>
+static hipError_t bwd_consumers_t(const Args& a, hipStream_t s) {
+  switch (a.gate) {
+    case 0: return bwd_chunk_g<T, 32>(a, s);
+    case 1: return bwd_chunk_g<T, 33>(a, s);
+    case 2: return bwd_chunk_g<T, 34>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_bwd_chunk(const Args& a, int f32, hipStream_t s) {
   return f32 ? bwd_chunk_t<float>(a, s) : bwd_chunk_t<bf16>(a, s);
+}
+hipError_t launch_bwd_producer(const Args& a, int f32, hipStream_t s) {
+  if (a.ew || a.gin) return hipErrorInvalidValue;
+  return f32 ? bwd_chunk_g<float, 16>(a, s) : bwd_chunk_g<bf16, 16>(a, s);
+}
+hipError_t launch_bwd_consumers(const Args& a, int f32, hipStream_t s) {
+  if (a.ew || a.gin) return hipErrorInvalidValue;
+  return f32 ? bwd_consumers_t<float>(a, s) : bwd_consumers_t<bf16>(a, s);
 }
 
 // Parameter gradients of the gate formed in the kernel, from the chunk

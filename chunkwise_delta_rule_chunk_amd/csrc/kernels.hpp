@@ -96,6 +96,11 @@ struct Args {
   // backward intermediates
   void* Rbt;     // correction adjoint Rbar [nc,H,V/16,4,64 lanes,4] dtype, C-fragment order of its 16x16 tiles
   void* dhbuf;   // adjoint of the state leaving each chunk [nc,H,V/16,K,16] dtype (column-blocked)
+  // separate producer-consumer schedule: what the producer hands over
+  void* Pbuf;    // P = A^T Rbar [nc,H,64,V] dtype (rounded as the consumers read it)
+  void* Dfrag;   // D as operand fragments [nc,H,4 waves,4 blocks,2,64 lanes,4] dtype
+  float* Ddiag;  // diagonal blocks of D [nc,H,4,16,16] fp32
+  float* dbw;    // write part of dbeta [nc,H,64] fp32
 };
 
 constexpr int SCAN_NATURAL = 1;  // hbuf, R (read by the chunk backward)
@@ -133,6 +138,9 @@ hipError_t launch_bwd_scan(const Args& a, int dtype_f32, hipStream_t s);
 // the forward scan (natural outputs) and the reverse scan in one launch
 hipError_t launch_scans(const Args& a, int dtype_f32, hipStream_t s);
 hipError_t launch_bwd_chunk(const Args& a, int dtype_f32, hipStream_t s);
+// the separate schedule of the chunk backward: producer, then consumers
+hipError_t launch_bwd_producer(const Args& a, int dtype_f32, hipStream_t s);
+hipError_t launch_bwd_consumers(const Args& a, int dtype_f32, hipStream_t s);
 // the gate-in-kernel parameter gradients from the chunk backward's partials
 hipError_t launch_gate_reduce(const Args& a, hipStream_t s);
 // the token-serial forward (decode)

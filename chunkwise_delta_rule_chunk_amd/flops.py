@@ -100,13 +100,24 @@ def bwd_chunk_chunk(n, K, V):
     return backward_chunk(n, K, V) - bwd_scan_chunk(n, K, V)
 
 
+def bwd_producer_chunk(n, K, V):
+    """The ReWY producer alone: P = A^T Rbar and D = -tril_strict(P R^T)."""
+    return 2 * V * _tri(n, False) + 2 * V * _tri(n, True)
+
+
+def bwd_consumers_chunk(n, K, V):
+    """The consumers alone: Hq, the three state products, matrix intra."""
+    return bwd_chunk_chunk(n, K, V) - bwd_producer_chunk(n, K, V)
+
+
 def kernel_flops(stage, seq_lengths, H, K, V, C=64):
     """Algorithmic FLOPs one launch of `stage` performs for the method (work
     re-executed under the recompute policy is not counted: a recompute prep
     counts zero, the fused backward scans count the reverse scan only)."""
     ns = chunk_lengths(seq_lengths, C)
     per = {"prep_forward": prep_chunk, "fwd_scan": fwd_scan_chunk,
-           "bwd_scan": bwd_scan_chunk, "bwd_chunk": bwd_chunk_chunk}.get(stage)
+           "bwd_scan": bwd_scan_chunk, "bwd_chunk": bwd_chunk_chunk,
+           "bwd_producer": bwd_producer_chunk, "bwd_consumers": bwd_consumers_chunk}.get(stage)
     if per is None:
         return 0
     return sum(per(n, K, V) for n in ns) * H

@@ -208,6 +208,22 @@ int rewy_recurrent_fwd_gdn2(const rewy_desc *d, const void *q, const void *k, co
                             const float *g, const void *b, const void *w, const float *h0,
                             void *o, float *ht, void *stream);
 
+/* Schedule of the chunk backward (ReWY paper, "Execution and numerical
+ * precision", joint and separate consumers).  JOINT (the default): one kernel
+ * per chunk-head forms the shared sensitivity P = A^T Rbar and D =
+ * -tril_strict(P R^T) and consumes them on chip.  SEPARATE: a producer kernel
+ * writes P, D and the write part of dbeta to the workspace and a consumer
+ * kernel reads them back; the results are bitwise those of JOINT, the
+ * workspace (rewy_workspace_bytes phase 1) grows by about 580 B per token and
+ * head at K = V = 128 in bf16.  Applies to later rewy_bwd calls from every
+ * thread (the erase/write form and the gate formed in the kernels always run
+ * JOINT); workspace sizes follow the schedule in force when they are queried,
+ * so query them after setting it.  Returns the previous schedule; a negative
+ * argument only returns the current one; an unknown schedule returns
+ * REWY_EINVAL and changes nothing. */
+typedef enum { REWY_SCHEDULE_JOINT = 0, REWY_SCHEDULE_SEPARATE = 1 } rewy_schedule;
+int rewy_bwd_schedule(int schedule);
+
 /* Per-kernel timing (a tracing aid: device events, as in the ReWY paper's timing
  * protocol).  After rewy_trace_begin(), calls made by this thread
  * record a HIP event pair on the call's stream around every kernel they

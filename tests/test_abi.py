@@ -218,6 +218,31 @@ def test_noalloc_forward_rejects_problems_beyond_its_scratch(lib):
     assert rc == B.REWY_EUNSUPPORTED
 
 
+def test_backward_schedule_knob(lib):
+    """rewy_bwd_schedule sets the chunk backward's schedule; the separate one
+    needs a larger backward workspace (P, D and the write part of dbeta handed
+    from the producer to the consumers) and no other buffer changes."""
+    d = _desc()
+    joint = B.rewy_workspace_bytes(d, 1)
+    fwd = B.rewy_workspace_bytes(d, 0)
+    prev = B.rewy_bwd_schedule(B.REWY_SCHEDULE_SEPARATE)
+    try:
+        assert prev == B.REWY_SCHEDULE_JOINT
+        assert B.rewy_bwd_schedule(-1) == B.REWY_SCHEDULE_SEPARATE
+        nc, H, K, V, e = 4, 2, 128, 128, 2
+        up = lambda x: (x + 255) // 256 * 256
+        extra = up(nc * H * 64 * V * e) + up(nc * H * 4 * 4 * 2 * 64 * 4 * e) \
+            + up(nc * H * 4 * 16 * 16 * 4) + up(nc * H * 64 * 4)
+        assert B.rewy_workspace_bytes(d, 1) == joint + extra
+        assert B.rewy_workspace_bytes(d, 0) == fwd
+        with pytest.raises(B.RewyError):
+            B.rewy_bwd_schedule(7)
+        assert B.rewy_bwd_schedule(-1) == B.REWY_SCHEDULE_SEPARATE
+    finally:
+        B.rewy_bwd_schedule(prev)
+    assert B.rewy_workspace_bytes(d, 1) == joint
+
+
 def test_product_path_has_no_fallback():
     """The package never imports the oracle and raises when the library is missing."""
     import chunkwise_delta_rule_chunk_amd as pkg
