@@ -69,6 +69,7 @@ __device__ __forceinline__ void solve_unit_lower(const float* sL, float* sA, int
 }
 
 constexpr int cmax(int x, int y) { return x > y ? x : y; }
+constexpr int cmin(int x, int y) { return x < y ? x : y; }
 
 // Workgroups of a persistent chunk kernel: one per compute unit of the
 // current device (queried once per device).

@@ -373,8 +373,16 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   const f32x4 bIb = *reinterpret_cast<const f32x4*>(sBeta + I * SUB + 4 * q4);  // beta, rows of block I
   f32x4 sufs = zero4();  // scalar gate: Gbar summed over features, this lane's rows
   float dbe[4] = {0.f, 0.f, 0.f, 0.f};
-  // dq, dk of the previous (even) feature block, transposed (see below)
-  FR pdq = to_frag<T>(zero4()), pdk = to_frag<T>(zero4()), pdb = to_frag<T>(zero4());
+  // dq, dk of the previous feature blocks of this group, transposed (see
+  // below): a group is the blocks that fill whole 128-byte lines of a row,
+  // four in bf16 and two in fp32
+  constexpr int QG = cmin(128 / (SUB * (int)sizeof(T)), NFB);
+  static_assert(NFB % QG == 0, "whole groups of feature blocks");
+  FR pdq[QG - 1], pdk[QG - 1];
+#pragma unroll
+  for (int j = 0; j < QG - 1; ++j) pdq[j] = pdk[j] = to_frag<T>(zero4());
+  FR pdb = to_frag<T>(zero4());
+  f32x4 pdg = zero4();  // dg of the previous (even) feature block
   // erase/write form: db of this lane's rows, stored like dk
   const GBuf bdb = gbuf(reinterpret_cast<T*>(a.dbeta) + (t0 * H + h) * K, EW ? tile_bytes<T>(n, gsK, K) : 0u);
   // identity as the B operand of a 16-long product: C = X^T I turns this
@@ -684,11 +692,12 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
     }
     // dq, dk of this block, transposed by one product with the identity: lane
     // (q4, f) then holds row 16 I + f, features 16 fb + 4 q4 .. + 3, one 8-byte
-    // piece (16 bytes in fp32).  An even block waits for the next one, so both
-    // halves of each 64-byte row segment are written together; the stores are
-    // issued in every block (even blocks and rows past the end fall outside
-    // the buffers and are dropped), which keeps the loop's memory operations
-    // the same on every path.
+    // piece (16 bytes in fp32).  The blocks of a group wait for its last one,
+    // so each 128-byte line of a row is written whole in one burst (a line
+    // completed across iterations can leave the cache half written and cost
+    // a second write); the stores are issued in every block (other blocks and
+    // rows past the end fall outside the buffers and are dropped), which
+    // keeps the loop's memory operations the same on every path.
     {
       f32x4 tq = zero4(), tk = zero4();
       mm16(tq, to_frag<T>(f32x4{oq[0], oq[1], oq[2], oq[3]}), idt);
@@ -700,32 +709,36 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
         mm16(tbb, to_frag<T>(f32x4{ob[0], ob[1], ob[2], ob[3]}), idt);
         yb = to_frag<T>(tbb);
       }
-      const bool odd = fb & 1;
       const int64_t tb = (int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4;
-      const uint32_t o1 = odd ? (uint32_t)((tb - SUB) * (int64_t)sizeof(T)) : OOB;
-      const uint32_t o2 = odd ? (uint32_t)(tb * (int64_t)sizeof(T)) : OOB;
-      if constexpr (std::is_same_v<T, bf16>) {
-        gst8(bdq, o1, __builtin_bit_cast(uint2, pdq));
-        gst8(bdq, o2, __builtin_bit_cast(uint2, yq));
-        gst8(bdk, o1, __builtin_bit_cast(uint2, pdk));
-        gst8(bdk, o2, __builtin_bit_cast(uint2, yk));
-        if constexpr (EW) {
-          gst8(bdb, o1, __builtin_bit_cast(uint2, pdb));
-          gst8(bdb, o2, __builtin_bit_cast(uint2, yb));
-        }
-      } else {
-        gst16(bdq, o1, __builtin_bit_cast(uint4, pdq));
-        gst16(bdq, o2, __builtin_bit_cast(uint4, yq));
-        gst16(bdk, o1, __builtin_bit_cast(uint4, pdk));
-        gst16(bdk, o2, __builtin_bit_cast(uint4, yk));
-        if constexpr (EW) {
-          gst16(bdb, o1, __builtin_bit_cast(uint4, pdb));
-          gst16(bdb, o2, __builtin_bit_cast(uint4, yb));
-        }
+      const bool last = (fb % QG) == QG - 1;
+      // block fb - d of the group, d = QG - 1 .. 0 (d = 0: this block)
+      auto qoff = [&](int d) { return last ? (uint32_t)((tb - d * SUB) * (int64_t)sizeof(T)) : OOB; };
+      auto st = [&](const GBuf& b, uint32_t off, const FR& x) {
+        if constexpr (std::is_same_v<T, bf16>) gst8(b, off, __builtin_bit_cast(uint2, x));
+        else gst16(b, off, __builtin_bit_cast(uint4, x));
+      };
+#pragma unroll
+      for (int j = QG - 2; j >= 0; --j) {  // pdq[j] is block fb - 1 - j
+        st(bdq, qoff(j + 1), pdq[j]);
+        st(bdk, qoff(j + 1), pdk[j]);
       }
-      pdq = yq;
-      pdk = yk;
-      pdb = yb;
+      st(bdq, qoff(0), yq);
+      st(bdk, qoff(0), yk);
+#pragma unroll
+      for (int j = QG - 2; j > 0; --j) {
+        pdq[j] = pdq[j - 1];
+        pdk[j] = pdk[j - 1];
+      }
+      pdq[0] = yq;
+      pdk[0] = yk;
+      if constexpr (EW) {  // db in pairs of blocks
+        const bool odd = fb & 1;
+        const uint32_t o1 = odd ? (uint32_t)((tb - SUB) * (int64_t)sizeof(T)) : OOB;
+        const uint32_t o2 = odd ? (uint32_t)(tb * (int64_t)sizeof(T)) : OOB;
+        st(bdb, o1, pdb);
+        st(bdb, o2, yb);
+        pdb = yb;
+      }
     }
     if constexpr (GATE == 2) {
       // in-block reverse sum: own rows, then the lane groups after this one
@@ -806,8 +819,12 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
           gst16(bdx, o2, __builtin_bit_cast(uint4, yx));
         }
         pdx = yx;
-      } else {
-        gst16(bdg, (uint32_t)(((int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4) * 4), __builtin_bit_cast(uint4, tg));
+      } else {  // in pairs of blocks: each 128-byte line of a row in one burst
+        const bool odd = fb & 1;
+        const int64_t tb = (int64_t)(I * SUB + f) * gsK + fb * SUB + 4 * q4;
+        gst16(bdg, odd ? (uint32_t)((tb - SUB) * 4) : OOB, __builtin_bit_cast(uint4, pdg));
+        gst16(bdg, odd ? (uint32_t)(tb * 4) : OOB, __builtin_bit_cast(uint4, tg));
+        pdg = tg;
       }
     } else if (GATE == 1 && live) {
 #pragma unroll
