@@ -77,7 +77,7 @@ def _chunk_fwd(Q, K, V, G, beta, S, scale):
     return O, S_next, ctx
 
 
-def _chunk_bwd(ctx, Q, K, V, beta, dO, Splus, scale, scalar_gate, route):
+def _chunk_bwd(ctx, Q, K, V, beta, dO, Splus, scale, scalar_gate, route, round_DH=None):
     gam, E, Y, Qg, Cq, A, R, lam, F, S, W, Z = (ctx[x] for x in
                                                 ("gam", "E", "Y", "Qg", "Cq", "A", "R", "lam",
                                                  "F", "S", "W", "Z"))
@@ -95,6 +95,8 @@ def _chunk_bwd(ctx, Q, K, V, beta, dO, Splus, scale, scalar_gate, route):
         D = -_tril(P @ R.T, True)
         Edir = -P @ S.T
     Hq = _tril(dO @ R.T, False)
+    if round_DH is not None:  # operand-format experiment: D and Hq enter their products rounded
+        D, Hq = round_DH(D), round_DH(Hq)
     Fbar = R @ Splus.T
     Qgbar = dO @ S.T + Hq @ Y
     Ebar = Edir + D @ Y
@@ -140,13 +142,18 @@ def _seq_iter(B, T, cu_seqlens):
 
 
 def forward_backward(q, k, v, g, beta, dO=None, *, scale, h0=None, dht=None, cu_seqlens=None,
-                     chunk=64, route="rewy"):
+                     chunk=64, route="rewy", round_DH=None):
     """Chunked evaluation of forward (and backward when dO is given).
 
     ``chunk`` is a chunk size or, for a single sequence, an explicit list of
     chunk lengths (a nonuniform partition).  ``route`` selects the backward
     graph: "rewy" (Algorithm 1), "expanded" (the seven-product WY graph),
     "gram_eliminated" or "gram_matrix" (scalar-gate log-gate reductions).
+    ``round_DH`` (default None: exact) is applied to D and Hq of every chunk
+    before they enter their products; it lets a test measure what a lower
+    operand format for these two coefficient matrices does to the gradients
+    (the paper's precision contract, section "Execution and numerical
+    precision" and the precision-eligibility appendix).
     Returns a dict with o, ht and, with dO, dq, dk, dv, dg, dbeta, dh0.
     """
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
@@ -194,7 +201,8 @@ def forward_backward(q, k, v, g, beta, dO=None, *, scale, h0=None, dht=None, cu_
             for c in range(len(lens) - 1, -1, -1):
                 a, e = starts[c], starts[c + 1]
                 r = _chunk_bwd(ctxs[c], q[b, a:e, h], k[b, a:e, h], v[b, a:e, h],
-                               beta[b, a:e, h], dO[b, a:e, h], Splus, scale, scalar, route)
+                               beta[b, a:e, h], dO[b, a:e, h], Splus, scale, scalar, route,
+                               round_DH)
                 dq[b, a:e, h], dk[b, a:e, h], dv[b, a:e, h], dbeta[b, a:e, h] = r[:4]
                 if dg is not None:
                     dg[b, a:e, h] = r[4]

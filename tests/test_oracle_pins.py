@@ -457,3 +457,65 @@ def test_kda_gate_bounded_form_and_reverse_mode():
         minus[arg] = base[arg] - eps * u
         fd = (loss(*plus) - loss(*minus)) / (2 * eps)
         assert abs(fd - float((grad * u).sum())) <= 1e-7 * max(1.0, abs(fd)), (arg, fd)
+
+
+# ------------------------------------------------------ operand-format experiment
+
+def _round_bf16(x):
+    """Round to the nearest bfloat16 (ties to even) through the float32 bit
+    pattern: keep the top 16 bits after adding half an ulp of the kept part."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def test_bf16_rounding_helper():
+    """bfloat16 keeps 8 significant bits (spacing 2^-7 above 1): 1 + 2^-8 is a
+    tie that rounds to 1 (even), 1 + 3 * 2^-8 a tie that rounds up to
+    1 + 2^-6, and the relative error of any normal value is at most the unit
+    roundoff 2^-8."""
+    one = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5])
+    r = _round_bf16(one)
+    assert r[0] == 1.0 and r[1] == 1.0 and r[2] == 1.0 + 2.0 ** -6 and r[3] == -2.5
+    x = np.random.default_rng(3).standard_normal(100000) * 10.0 ** np.random.default_rng(4).uniform(-20, 20, 100000)
+    rel = np.abs(_round_bf16(x) - x) / np.abs(x)
+    assert rel.max() <= 2.0 ** -8 * (1 + 1e-12) and rel.max() > 2.0 ** -8 * 0.9
+
+
+@pytest.mark.parametrize("strong", [False, True], ids=["kda", "strong_decay"])
+def test_precision_of_bf16_D_and_Hq_operands(strong):
+    """What bfloat16 operands for the two coefficient matrices D and Hq do to
+    the gradients (ReWY paper, "Execution and numerical precision" and the
+    precision-eligibility appendix: existing FP32 L/D working matrices keep
+    their format there).  The GPU chunk backward forms D and Hq in FP32
+    accumulators and feeds them to its products as bfloat16 MFMA operands;
+    this measures that rounding alone in the FP64 chunked evaluation at the
+    KDA gates (A_log ~ U(-2, 0)) and the strong-decay gates (A_log ~ U(0, 1),
+    in-chunk log decay down to about -220), K = V = 128, four chunks.
+
+    Structural pins: dv and dh0 do not depend on D or Hq, so they are
+    unchanged bit for bit.  Measured: dq 1.7e-3, dk 1.4e-3, dg 1.3e-3,
+    dbeta 8e-5 relative (normwise) in both regimes -- below the bfloat16
+    unit roundoff 2^-8 and below the 3.5e-3 the whole bfloat16 GPU path
+    shows on dv, which involves neither matrix."""
+    import workloads
+
+    inp = workloads.make_inputs(1, 256, 2, 128, 128, gate="vector", dtype="bf16", seed=7,
+                                strong=strong, dht=True)
+    f64 = lambda t: None if t is None else t.double().numpy()
+    args = [f64(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.dO)]
+    kw = dict(scale=inp.scale, h0=f64(inp.h0), dht=f64(inp.dht))
+    exact = chunked.forward_backward(*args, **kw)
+    rounded = chunked.forward_backward(*args, **kw, round_DH=_round_bf16)
+    err = {n: np.linalg.norm(rounded[n] - exact[n]) / np.linalg.norm(exact[n])
+           for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0")}
+    assert err["dv"] == 0.0 and err["dh0"] == 0.0, err
+    for n in ("dq", "dk", "dg"):
+        assert 5e-4 < err[n] < 2.5e-3, (n, err)
+    assert err["dbeta"] < 2e-4, err
+    # the gates of the strong regime really are strong: some in-chunk log
+    # decay falls below -100 there, none does at the KDA gates
+    g = args[3][0]
+    low = min(np.cumsum(g[c:c + 64], axis=0).min() for c in range(0, 256, 64))
+    assert (low < -100.0) == strong, low
