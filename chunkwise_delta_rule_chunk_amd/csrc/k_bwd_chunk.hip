@@ -534,23 +534,38 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
       // sub-chunk statistics of this feature (written by the forward prep):
       // G2 at the first and last valid row, midpoint, range; only blocks with
       // valid rows are used
-      float Gf[NSUB], Gl[NSUB], Md[NSUB];
-      bool wide[NSUB];
+      float Gf[NSUB], Gl[NSUB];
+      f32x4 stJ[NSUB];
       static_for<0, NSUB>([&](auto J) {
-        f32x4 st = zero4();
-        if (J * SUB < n) st = *reinterpret_cast<const f32x4*>(sSt + (J * SUB + f) * 4);
-        Gf[J] = st[0];
-        Gl[J] = st[1];
-        Md[J] = st[2];
-        wide[J] = __any(st[3] > CENTRE_MAX_RANGE);
+        stJ[J] = zero4();
+        if (J * SUB < n) stJ[J] = *reinterpret_cast<const f32x4*>(sSt + (J * SUB + f) * 4);
+        Gf[J] = stJ[J][0];
+        Gl[J] = stJ[J][1];
       });
       const float Gn = sGn[f];
-      const f32x4 GI = pick(G, I), kI = unpack(pick(kp, I)), qI = unpack(pick(qp, I));
-      // erase factor of this lane's rows: beta per row, or b per (row, feature)
-      f32x4 bI = bIb;
-      if constexpr (EW) bI = unpack(pick(bp, I));
-      const float GfI = pick(Gf, I), GlI = pick(Gl, I), MdI = pick(Md, I);
-      const bool wideI = pick(wide, I);
+      // Block I's own operands and statistics.  Read again at the wave's own
+      // (uniform) offsets, which costs fewer instructions than selecting them
+      // from the arrays above; the gate formed in the kernel keeps the
+      // selection (its extra registers would not fit beside the re-reads).
+      const int rI = I * SUB + 4 * q4;
+      f32x4 GI, kI, qI, stI, bI = bIb;
+      if constexpr (GIN) {
+        GI = pick(G, I);
+        kI = unpack(pick(kp, I));
+        qI = unpack(pick(qp, I));
+        stI = pick(stJ, I);
+      } else {
+        GI = zero4();
+        if constexpr (GATE == 2) GI = *reinterpret_cast<const f32x4*>(sG2 + f * PGS + rI);
+        else if constexpr (GATE == 1) GI = *reinterpret_cast<const f32x4*>(sG2 + rI);
+        kI = unpack(*reinterpret_cast<const FR*>(sKs + f * PKS + rI));
+        qI = unpack(*reinterpret_cast<const FR*>(sQs + f * PKS + rI));
+        // erase factor of this lane's rows: beta per row, or b per (row, feature)
+        if constexpr (EW) bI = unpack(*reinterpret_cast<const FR*>(sBs + f * PKS + rI));
+        stI = *reinterpret_cast<const f32x4*>(sSt + (I * SUB + f) * 4);  // live: I * SUB < n
+      }
+      const float GfI = stI[0], GlI = stI[1], MdI = stI[2];
+      const bool wideI = __any(stI[3] > CENTRE_MAX_RANGE);
       // Row factors of block I.  Centred block: xp = exp2(G - Md), xm = exp2(Md - G)
       // (each at most 2^(range/2)), and the receiving factors follow by per-lane
       // constants, fr = exp2(G - Gf) = xp exp2(Md - Gf), fc = exp2(Gl - G) =
