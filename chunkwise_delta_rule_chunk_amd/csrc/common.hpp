@@ -607,16 +607,30 @@ __device__ __forceinline__ typename Frag4<T>::type to_frag(const f32x4& x) {
   }
 }
 
+// x ~ hi + lo in bf16: hi = x rounded to nearest, lo = (x - hi) rounded.  One
+// pair conversion gives both hi values; their fp32 values are the lower and
+// upper halves of its bits moved into place.  The packed word passes an empty
+// asm statement, so the compiler keeps the pair conversion instead of
+// converting each element again on its own.
+__device__ __forceinline__ void split_bf16(const f32x4& x, bf16x4& hi, bf16x4& lo) {
+  uint32_t hb[2], lb[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    hb[p] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)x[2 * p], (bf16)x[2 * p + 1]});
+    asm("" : "+v"(hb[p]));
+    const float h0 = __uint_as_float(hb[p] << 16), h1 = __uint_as_float(hb[p] & 0xffff0000u);
+    lb[p] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)(x[2 * p] - h0), (bf16)(x[2 * p + 1] - h1)});
+  }
+  hi = __builtin_bit_cast(bf16x4, u32x2{hb[0], hb[1]});
+  lo = __builtin_bit_cast(bf16x4, u32x2{lb[0], lb[1]});
+}
+
 // acc += M x (hi + lo) for a sending operand x given in fp32 (bf16: two MFMAs).
 template <typename T>
 __device__ __forceinline__ void mm16_split(f32x4& acc, typename Frag4<T>::type m, const f32x4& x) {
   if constexpr (std::is_same_v<T, bf16>) {
     bf16x4 hi, lo;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      hi[e] = (bf16)x[e];
-      lo[e] = (bf16)(x[e] - (float)hi[e]);
-    }
+    split_bf16(x, hi, lo);
     mm16(acc, m, hi);
     mm16(acc, m, lo);
   } else {
