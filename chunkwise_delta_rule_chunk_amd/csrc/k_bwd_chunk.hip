@@ -607,21 +607,22 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
         l0 = __shfl(comp(SS, f & 3), ((f >> 2) << 4) | f) * fexp2(Gn);
       }
       // -- sources before I: gamma (Hq Y), gamma (D Y) ----------------------------
+      // The sending factor of an earlier block J carries the column factor as
+      // well, exp2(Gf_I - G) = exp2(Gf_I - Gl_J) exp2(Gl_J - G) <= 1, so the
+      // products of every J accumulate in the MFMA accumulators directly.  XHQ
+      // is formed without the query scale, applied once in the chain rules.
       f32x4 XHY = zero4(), XDY = zero4(), XDE = zero4(), XHQ = zero4();
       static_for<0, NSUB - 1>([&](auto J) {
         if (J >= I) return;
         f32x4 ks;
         const f32x4 kJ = unpack(kp[J]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ks[e] = kJ[e] * fexp2(Gl[J] - G[J][e]);
-        f32x4 tH = zero4(), tD = zero4();
-        mm16_split<T>(tH, Hm[J], ks);
-        mm16_split<T>(tD, Dm[J], ks);
-        const float cf = fexp2(GfI - Gl[J]);
-        XHY += cf * tH;
-        XDY += cf * tD;
+        for (int e = 0; e < 4; ++e) ks[e] = kJ[e] * fexp2(GfI - G[J][e]);
+        mm16_split<T>(XHY, Hm[J], ks);
+        mm16_split<T>(XDY, Dm[J], ks);
       });
       // -- sources after I: (D^T E) / gamma, (Hq^T Qg) / gamma -------------------
+      // (the mirror: exp2(G - Gl_I) = exp2(Gf_J - Gl_I) exp2(G - Gf_J) <= 1)
       static_for<1, NSUB>([&](auto J) {
         if (J <= I || J * SUB >= n) return;
         f32x4 es, qs;
@@ -631,16 +632,12 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
         else bJ = *reinterpret_cast<const f32x4*>(sBeta + J * SUB + 4 * q4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x = fexp2(G[J][e] - Gf[J]);
+          const float x = fexp2(G[J][e] - GlI);
           es[e] = bJ[e] * kJ[e] * x;
-          qs[e] = scale * qJ[e] * x;
+          qs[e] = qJ[e] * x;
         }
-        f32x4 tE = zero4(), tQ = zero4();
-        mm16_split<T>(tE, Dtm[J], es);
-        mm16_split<T>(tQ, Htm[J], qs);
-        const float cf = fexp2(Gf[J] - GlI);
-        XDE += cf * tE;
-        XHQ += cf * tQ;
+        mm16_split<T>(XDE, Dtm[J], es);
+        mm16_split<T>(XHQ, Htm[J], qs);
       });
       XHY *= fr;
       XDY *= fr;
@@ -648,7 +645,7 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
       XHQ *= fc;
       // -- diagonal block ------------------------------------------------------------
       if (!wideI) {
-        const f32x4 ks = kI * xm, es = bI * kI * xp, qs = scale * qI * xp;
+        const f32x4 ks = kI * xm, es = bI * kI * xp, qs = qI * xp;
         f32x4 tH = zero4(), tD = zero4(), tE = zero4(), tQ = zero4();
         mm16_split<T>(tH, HmI, ks);
         mm16_split<T>(tD, DmI, ks);
@@ -680,7 +677,7 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
             if (j >= r) {
               const float x = fexp2(Gj - GI[e]);
               XDE[e] += Dd[j * PD + r] * bj * kj * x;
-              XHQ[e] += Hd[j * PD + r] * scale * qj * x;
+              XHQ[e] += Hd[j * PD + r] * qj * x;
             }
           }
         }
@@ -693,7 +690,7 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
           const float gam = fexp2(GI[e]);
           const float XQ = gam * SQ[e] + XHY[e];
           const float XE = -gam * SE[e] + XDY[e];
-          const float XY = XDE[e] + XHQ[e] + SF[e] * tail[e];
+          const float XY = XDE[e] + scale * XHQ[e] + SF[e] * tail[e];
           const float kv = kI[e], qv = qI[e], b = bI[e];
           oq[e] = scale * XQ;
           ok_[e] = b * XE + XY;
