@@ -22,13 +22,17 @@ __device__ __forceinline__ void pair_ij(int p, int& I, int& J) {
 
 // A = (I + L)^-1 for the strictly lower fp32 L (pitch PL); A must be zero on
 // entry (its upper blocks stay zero).  Diagonal 16x16 blocks are inverted by
-// forward substitution (one lane per column), then the off-diagonal blocks are
-// merged in order of distance from the diagonal,
-//   A_IJ = -A_II * sum_{m=J}^{I-1} L_Im A_mJ,
-// with fp32 MFMA.  Called by every wave of the workgroup (waves 0 .. 2 do the
-// merges).
+// forward substitution (one lane per column), then the 32x32 halves and the
+// whole 64x64 inverse follow from the 2 x 2 block formula
+//   [M11 0; M21 M22]^-1 = [A11 0; -A22 M21 A11  A22]
+// with fp32 MFMA: first A_10 and A_32 (two waves), then the four blocks of
+// the lower-left 32x32 quarter (one wave each, forming the products
+// T_kj = sum_m L_{2+k,m} A_mj it needs itself).  Every operand of a product is
+// read from LDS before its MFMAs; a C fragment is used directly as the B
+// operand of the next product.  Three barriers.  Called by every wave of the
+// workgroup.
 __device__ __forceinline__ void solve_unit_lower(const float* sL, float* sA, int PL, int n) {
-  const int w = wave_id(), l = lane_id();
+  const int w = wave_id(), l = lane_id(), g = l >> 4, r16 = l & 15;
   if (w == 0) {
     const int b = l >> 4, cc = l & 15;
     const float* Lb = sL + (b * SUB) * PL + b * SUB;
@@ -46,26 +50,46 @@ __device__ __forceinline__ void solve_unit_lower(const float* sL, float* sA, int
     for (int i = 0; i < SUB; ++i) Ab[i * PL + cc] = x[i];
   }
   lds_barrier();
-  // distance d is a compile-time constant, so each product's operand reads
-  // are issued together ahead of its MFMA chain.  The inner sum stays in
-  // registers: its C fragment (lane l: rows 4 (l >> 4) .. +3 of column l & 15)
-  // is the B operand of the outer product with A_II.
-  static_for<1, NSUB>([&](auto dd) {
-    constexpr int d = decltype(dd)::value;
-    const int I = w + d, J = w;
-    if ((w < NSUB - d) && (I * SUB < n)) {
-      f32x4 t = zero4();
-      mma_tile<float, false, false>(t, sL + (I * SUB) * PL + J * SUB, PL, 1,
-                                    sA + (J * SUB) * PL + J * SUB, 1, PL, SUB * d);
-      const int l = lane_id();
-      const f32x4 aII =
-          *reinterpret_cast<const f32x4*>(sA + (I * SUB + (l & 15)) * PL + I * SUB + 4 * (l >> 4));
-      f32x4 r = zero4();
-      mm16(r, aII, t);
-      st_tile<float>(-r, sA + (I * SUB) * PL + J * SUB, PL, 1);
+  // operands of a 16-long fp32 contraction: the A operand is four consecutive
+  // columns of row r16, the B operand four consecutive rows of column r16
+  auto arow = [&](const float* m, int I, int J) {
+    return *reinterpret_cast<const f32x4*>(m + (I * SUB + r16) * PL + J * SUB + 4 * g);
+  };
+  auto bcol = [&](const float* m, int I, int J) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = m[(I * SUB + 4 * g + e) * PL + J * SUB + r16];
+    return v;
+  };
+  // A_{b+1,b} = -A_{b+1,b+1} L_{b+1,b} A_{b,b}, b = 0 (wave 0) and b = 2 (wave 1)
+  if (w < 2 && (2 * w + 1) * SUB < n) {
+    const int b = 2 * w;
+    const f32x4 la = arow(sL, b + 1, b), ab = bcol(sA, b, b), aa = arow(sA, b + 1, b + 1);
+    f32x4 t = zero4(), r = zero4();
+    mm16(t, la, ab);
+    mm16(r, aa, t);
+    st_tile<float>(-r, sA + ((b + 1) * SUB) * PL + b * SUB, PL, 1);
+  }
+  lds_barrier();
+  // block (2 + i, j) of A, wave 2 i + j: -sum_{k <= i} A_{2+i,2+k} T_kj
+  {
+    const int i = w >> 1, j = w & 1;
+    if ((2 + i) * SUB < n) {
+      f32x4 R = zero4();
+      static_for<0, 2>([&](auto kk) {
+        constexpr int k = decltype(kk)::value;
+        if (k > i) return;
+        const f32x4 l0 = arow(sL, 2 + k, 0), l1 = arow(sL, 2 + k, 1), a2 = arow(sA, 2 + i, 2 + k);
+        const f32x4 b0 = bcol(sA, 0, j), b1 = bcol(sA, 1, j);
+        f32x4 T = zero4();
+        if (j == 0) mm16(T, l0, b0);  // m = 0 (A_0j is zero for j = 1)
+        mm16(T, l1, b1);              // m = 1
+        mm16(R, a2, T);
+      });
+      st_tile<float>(-R, sA + ((2 + i) * SUB) * PL + j * SUB, PL, 1);
     }
-    lds_barrier();
-  });
+  }
+  lds_barrier();
 }
 
 constexpr int cmax(int x, int y) { return x > y ? x : y; }
