@@ -177,15 +177,19 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   uint32_t gal = 0u, gdtb[GIN ? NSL : 1];
   uint4 pw2[EW && BF ? 2 * VPT : 1];
   Staged<T, CH, V, NTH> pw;
-  // the fetches take the item's chunk record, read one item ahead (its
-  // scalar load completes during the previous item instead of stalling here)
+  // The fetches take the item's chunk record, read one item ahead (its
+  // scalar load completes during the previous item instead of stalling here).
+  // The next item's fetches are issued on every path, also for an empty chunk
+  // slot or past the last item (bounds-checked loads read zeros there; beta's
+  // row is clamped to a valid one): a fetch under a condition leaves its
+  // registers with two possible sources at the loop head, and the copies that
+  // merge them wait for the loads at once.
   auto fetch_kq = [&](int item, const ChunkInfo& ci, int tid) {
     const int h = item % H;
-    if (ci.len == 0) return;
     const int64_t t0 = ci.bos;
     pk.load(gbuf(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
     pq.load(gbuf(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
-    if constexpr (!EW) pbeta = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, ci.len - 1)) * H + h);
+    if constexpr (!EW) pbeta = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, max(ci.len - 1, 0))) * H + h);
   };
   auto fetch_v = [&](int item, const ChunkInfo& ci, int tid) {
     const int h = item % H;
@@ -212,7 +216,6 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   };
   auto fetch_g = [&](int item, const ChunkInfo& ci) {
     const int h = item % H;
-    if (ci.len == 0) return;
     if constexpr (GIN) {
       const GBuf bd = gbuf(a.dt_bias + (int64_t)h * K, K * 4);
 #pragma unroll
@@ -239,11 +242,10 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     }
   };
 
+  // (the grid never exceeds the item count, so blockIdx.x < total)
   ChunkInfo cnext = load_chunk(a.chunks, min((int)blockIdx.x, total - 1) / H);
-  if (blockIdx.x < total) {
-    fetch_kq(blockIdx.x, cnext, threadIdx.x);
-    fetch_g(blockIdx.x, cnext);
-  }
+  fetch_kq(blockIdx.x, cnext, threadIdx.x);
+  fetch_g(blockIdx.x, cnext);
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int tid = opaque_tid(), w = wave_id();
     // slot indices opaque per item: addresses derived from them are recomputed
@@ -254,14 +256,11 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     const int c = item / H, h = item - c * H;
     const ChunkInfo ci = cnext;
     const int n = ci.len;
-    const bool more = item + (int)gridDim.x < total;
     // the next item's record (the last one again past the end: never used)
     cnext = load_chunk(a.chunks, min(item + (int)gridDim.x, total - 1) / H);
-    if (n == 0) {  // uniform: nothing was fetched for this slot
-      if (more) {
-        fetch_kq(item + gridDim.x, cnext, tid);
-        fetch_g(item + gridDim.x, cnext);
-      }
+    if (n == 0) {  // uniform: an empty chunk slot
+      fetch_kq(item + gridDim.x, cnext, tid);
+      fetch_g(item + gridDim.x, cnext);
       continue;
     }
     const int64_t t0 = ci.bos, cb = (int64_t)c * H + h;
@@ -541,6 +540,12 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
 
     // ---- S4: A = (I + L)^-1 in fp32 ------------------------------------------
 
+    // this item's v and the next item's k, q, beta and gates (the gate
+    // registers are free since the elementwise phase), issued before the
+    // solve so that it covers their latency
+    fetch_v(item, ci, tid);
+    fetch_kq(item + gridDim.x, cnext, tid);
+    fetch_g(item + gridDim.x, cnext);
     // A takes X (the score operands are dead); its off-diagonal blocks start
     // at zero, written here while wave 0 forms the diagonal blocks
     for (int idx = tid; idx < NSUB * NSUB * SUB * 4; idx += NTH) {
@@ -549,13 +554,6 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       if (I != J) *reinterpret_cast<f32x4*>(sA + (I * SUB + rr) * PL + J * SUB + c4) = zero4();
     }
     solve_unit_lower(sL, sA, PL, n);
-    // this item's v; the next item's k, q, beta and gates (the gate registers
-    // are free since the elementwise phase), covered by S5
-    fetch_v(item, ci, tid);
-    if (more) {
-      fetch_kq(item + gridDim.x, cnext, tid);
-      fetch_g(item + gridDim.x, cnext);
-    }
     if constexpr (MODE & PREP_BWD_CHUNK) {  // A^T for the chunk backward, 16-byte rows
       constexpr int VA = 16 / (int)sizeof(T), PER = CH / VA;
       T* Ato = reinterpret_cast<T*>(a.At) + cb * CH * CH;
