@@ -123,6 +123,13 @@ __device__ __forceinline__ float rows_suffix_sum(float x, int q4) {
   const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
   return ((q4 & 1) ? x : p) + (q4 < 2 ? __uint_as_float(s[1]) : 0.f);
 }
+// x summed over the rows q < q4 (zero in row 0)
+__device__ __forceinline__ float rows_prefix_excl(float x, int q4) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float p = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // pair sum
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  return ((q4 & 1) ? __uint_as_float(r[0]) : 0.f) + (q4 >= 2 ? __uint_as_float(s[0]) : 0.f);
+}
 
 // Sum over the 16 lanes of each row of the wave (lanes 16 r .. 16 r + 15),
 // returned to every lane of the row, by DPP lane moves: the two quad

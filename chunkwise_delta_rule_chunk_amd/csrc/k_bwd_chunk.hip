@@ -398,6 +398,16 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   // products).  Every load is unconditional: a scalar gate has one G2 row
   // (the others read as zero) and no gate reads none.
   TileRegs<float, SUB, CH, NTH> pG;
+  // A vector gate given as g: G2 of the feature block is rebuilt here from g
+  // (the prep keeps only its sub-chunk statistics).  Wave w takes rows
+  // [16 w, 16 w + 16): lane (q4, f) reads g at rows 16 w + 4 q4 + e of feature
+  // 16 fb + f and G2 at the block's first row (its statistics record; zero for
+  // a block past the chunk's end, whose G2 is never used).  The gate formed in
+  // the kernels and the scalar gate read the prep's G2 tile.
+  constexpr bool GRAW = GATE == 2 && !GIN;
+  uint32_t graw[GRAW ? 4 : 1], gfw = 0u;
+  const GBuf bgr = gbuf(a.g + (t0 * H + h) * K, GRAW ? tile_bytes<float>(n, gsK, K) : 0u);
+  const GBuf bgf = gbuf(Gstg, GRAW ? (uint32_t)(((n + SUB - 1) / SUB) * K * 16) : 0u);
   // k and q of a feature block from their natural rows: a piece is KQV
   // features of one token; the first half of the pieces is k, the second q
   // (uniform per wave), transposed into [feature][token] when stored
@@ -420,7 +430,14 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
   const int grt = GATE == 2 ? K : 1;
   const uint32_t gbytes = GATE == 2 ? K * CH * 4 : GATE == 1 ? CH * 4 : 0;
   auto fetch_fb = [&](int fb) {
-    pG.load_cb(gbuf(gp, gbytes), grt, GATE == 2 ? fb * SUB : 0, tid);
+    if constexpr (GRAW) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        graw[e] = gld4(bgr, (uint32_t)(((int64_t)(w * SUB + 4 * q4 + e) * gsK + fb * SUB + f) * 4));
+      gfw = gld4(bgf, (uint32_t)(((w * K + fb * SUB + f) * 4) * 4));
+    } else {
+      pG.load_cb(gbuf(gp, gbytes), grt, GATE == 2 ? fb * SUB : 0, tid);
+    }
 #pragma unroll
     for (int j = 0; j < KQN; ++j) {
       const int pc = tid + j * NTH, rem = pc % (CH * KQR);
@@ -443,7 +460,20 @@ __global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
     pN.load(gbuf(a.glast + cb * K + fb * SUB, SUB * sizeof(float)), SUB, tid);
   };
   auto put_fb = [&]() {
-    if constexpr (GATE != 0) pG.store_cb(sG2, PGS, tid);
+    if constexpr (GRAW) {
+      // G2 = G2 at the first row + log2(e) times the sum of g over the later
+      // rows up to this one (in-lane over four rows, then the lane rows before)
+      f32x4 x;
+      x[0] = q4 == 0 ? 0.f : __uint_as_float(graw[0]);
+#pragma unroll
+      for (int e = 1; e < 4; ++e) x[e] = x[e - 1] + __uint_as_float(graw[e]);
+      const float off = rows_prefix_excl(x[3], q4), gf = __uint_as_float(gfw);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = gf + LOG2E * (off + x[e]);
+      *reinterpret_cast<f32x4*>(sG2 + f * PGS + w * SUB + 4 * q4) = x;
+    } else if constexpr (GATE != 0) {
+      pG.store_cb(sG2, PGS, tid);
+    }
 #pragma unroll
     for (int j = 0; j < KQN; ++j) {
       const int pc = tid + j * NTH, rem = pc % (CH * KQR);
