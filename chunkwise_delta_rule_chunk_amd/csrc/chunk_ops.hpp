@@ -64,6 +64,25 @@ struct GateCols {
 #pragma unroll
     for (int r = 0; r < RS; ++r) G[r] = __uint_as_float(gld4(b, base + r * rb));
   }
+  // Both slots of a column pair (init_pair: this slot's column c and the
+  // column c + 1 of slot `odd`, the same rows), one 8-byte load per row.  The
+  // range check of a buffer load is made per 4-byte word, so a scalar gate
+  // (one word per row; the second word of each load is not used) reads its
+  // last row like the others.
+  __device__ __forceinline__ void load_pair(GateCols& odd, const Args& a, int64_t t0, int h, int n, int K) {
+    const int H = a.H, r0 = seg * RS;
+    const bool vec = a.gate == 2;
+    const int64_t rs = vec ? (int64_t)H * K : H;  // row stride, elements
+    const float* gb = vec ? a.g + (t0 * H + h) * K : a.g + t0 * H + h;
+    const GBuf b = gbuf(gb, a.gate == 0 ? 0u : tile_bytes<float>(n, rs, vec ? KC : 1));
+    const uint32_t rb = (uint32_t)(rs * 4), base = (uint32_t)r0 * rb + (vec ? c : 0) * 4;
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const uint2 x = gld8(b, base + r * rb);
+      G[r] = __uint_as_float(x.x);
+      odd.G[r] = __uint_as_float(vec ? x.y : x.x);
+    }
+  }
   // The gate formed in the kernel: the pre-activation x [.., K] (type X) of
   // this thread's column (features [0, KC), KC = K) and rows, raw bits kept
   // in G until kda_gate(); rows past the end read as zero.
@@ -76,6 +95,27 @@ struct GateCols {
 #pragma unroll
     for (int r = 0; r < RS; ++r)
       G[r] = __uint_as_float(sizeof(X) == 2 ? gld2(b, base + r * rb) : gld4(b, base + r * rb));
+  }
+  // x of a column pair (as load_pair), one 4-byte (bf16) or 8-byte (fp32)
+  // load per row; raw bits kept in G until kda_gate()
+  template <typename X>
+  __device__ __forceinline__ void load_x_pair(GateCols& odd, const Args& a, int64_t t0, int h, int n, int K) {
+    const int H = a.H, r0 = seg * RS;
+    const int64_t rs = (int64_t)H * K;
+    const GBuf b = gbuf(reinterpret_cast<const X*>(a.gx) + (t0 * H + h) * K, tile_bytes<X>(n, rs, KC));
+    const uint32_t rb = (uint32_t)(rs * (int64_t)sizeof(X)), base = (uint32_t)r0 * rb + c * (uint32_t)sizeof(X);
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      if constexpr (sizeof(X) == 2) {
+        const uint32_t x = gld4(b, base + r * rb);
+        G[r] = __uint_as_float(x & 0xffffu);
+        odd.G[r] = __uint_as_float(x >> 16);
+      } else {
+        const uint2 x = gld8(b, base + r * rb);
+        G[r] = __uint_as_float(x.x);
+        odd.G[r] = __uint_as_float(x.y);
+      }
+    }
   }
   // g = -ea softplus(x + dtb) (lb = 0; GDN2 spec section 4.4) or the
   // bounded form g = lb sigmoid(ea (x + dtb)) (lb < 0; GDN2 spec section 3),

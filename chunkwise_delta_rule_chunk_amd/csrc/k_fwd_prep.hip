@@ -218,12 +218,21 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     const int h = item % H;
     if constexpr (GIN) {
       const GBuf bd = gbuf(a.dt_bias + (int64_t)h * K, K * 4);
+      if constexpr (PAIR) {
+        gc[0].template load_x_pair<T>(gc[1], a, (int64_t)ci.bos, h, ci.len, K);
+        const uint2 d2 = gld8(bd, gc[0].c * 4);
+        gdtb[0] = d2.x;
+        gdtb[1] = d2.y;
+      } else {
 #pragma unroll
-      for (int s = 0; s < NSL; ++s) {
-        gc[s].template load_x<T>(a, (int64_t)ci.bos, h, ci.len, K);
-        gdtb[s] = gld4(bd, gc[s].c * 4);
+        for (int s = 0; s < NSL; ++s) {
+          gc[s].template load_x<T>(a, (int64_t)ci.bos, h, ci.len, K);
+          gdtb[s] = gld4(bd, gc[s].c * 4);
+        }
       }
       gal = gld4(gbuf(a.a_log, a.H * 4), h * 4);
+    } else if constexpr (PAIR) {
+      gc[0].load_pair(gc[1], a, (int64_t)ci.bos, h, ci.len, K);
     } else {
 #pragma unroll
       for (int s = 0; s < NSL; ++s) gc[s].load(a, (int64_t)ci.bos, h, ci.len, K, 0);
