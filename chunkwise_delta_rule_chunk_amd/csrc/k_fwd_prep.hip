@@ -663,8 +663,10 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     lds_barrier();
 
     // W, U in operand-fragment order (see kernels.hpp), all 64 rows (rows past
-    // the chunk's end are exact zeros).  W for the forward scan comes from
-    // W^T tiles, whose C fragments are the 16-long A fragments of W.
+    // the chunk's end are exact zeros).  Each tile of W^T is formed once: its C
+    // fragments are the 16-long A fragments of W, the pieces of the forward
+    // scan, and one product with the identity turns them exactly into the C
+    // fragments of the W tile, from which W^T is stored for the reverse scan.
     T* Wfo = reinterpret_cast<T*>(a.W) + cb * CH * K;
     T* Ufo = reinterpret_cast<T*>(a.U) + cb * CH * V;
     T* Wto = reinterpret_cast<T*>(a.Wt) + cb * K * CH;
@@ -672,11 +674,14 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     const T* Aop = BF ? (const T*)sAb : (const T*)sA;
     constexpr int PAo = BF ? PA : PL;
     constexpr int NKB = K / SUB, GPP = 16 / (4 * (int)sizeof(T));  // 16-long groups per piece
-    constexpr int NJ0 = wantW ? NKB / GPP : 0, NJ1 = wantWt ? NKB : 0, NJ2 = wantU ? V / SUB : 0;
+    constexpr int NJW = (wantW || wantWt) ? NKB / GPP : 0, NJU = wantU ? V / SUB : 0;
     using FR = typename Frag4<T>::type;
-    for (int job = w; job < NJ0 + NJ1 + NJ2; job += NW) {
-      if (job < NJ0) {  // W^T, key blocks GPP job .. + GPP - 1: C tile rows 16 kb + 4 (l >> 4) + i,
-                        // token 16 I + (l & 15); one job fills whole W pieces
+    f32x4 idf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) idf[e] = (crow(e) == ccol()) ? 1.f : 0.f;
+    const FR idt = to_frag<T>(idf);
+    for (int job = w; job < NJW + NJU; job += NW) {
+      if (job < NJW) {  // W, key blocks GPP job .. + GPP - 1, every token block
         static_for<0, NSUB>([&](auto II) {
           constexpr int I = decltype(II)::value;
           // A is lower triangular: token block I needs tokens < 16 (I + 1) only
@@ -687,23 +692,23 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
           } piece;
           static_for<0, GPP>([&](auto hh) {
             const int kb = job * GPP + hh;
+            // C tile of W^T: lane l holds keys 16 kb + 4 (l >> 4) .. + 3 of
+            // token 16 I + (l & 15)
             f32x4 acc = zero4();
             mma_tile<T, true, true>(acc, sEt + (kb * SUB) * PA, PA, 1, Aop + (I * SUB) * PAo, PAo, 1, kd);
-            piece.f[hh] = to_frag<T>(acc);
+            const FR wt = to_frag<T>(acc);
+            if constexpr (wantW) piece.f[hh] = wt;
+            if constexpr (wantWt) {
+              f32x4 tr = zero4();
+              mm16(tr, wt, idt);
+              st_frag_T<T>(tr, Wto, I, kb);
+            }
           });
-          *reinterpret_cast<uint4*>(Wfo + ((I * (NKB / GPP) + job) * 64 + lane_id()) * GPP * 4) = piece.u;
-        });
-      } else if (job < NJ0 + NJ1) {  // W, key block kb, for W^T in fragment order
-        const int col = (job - NJ0) * SUB;
-        static_for<0, NSUB>([&](auto II) {
-          constexpr int I = decltype(II)::value;
-          f32x4 acc = zero4();
-          constexpr int kd = ((SUB * (I + 1) + MM<T>::KS - 1) / MM<T>::KS) * MM<T>::KS;
-          mma_tile<T, true, true>(acc, Aop + (I * SUB) * PAo, PAo, 1, sEt + col * PA, PA, 1, kd);
-          st_frag_T<T>(acc, Wto, I, col / SUB);
+          if constexpr (wantW)
+            *reinterpret_cast<uint4*>(Wfo + ((I * (NKB / GPP) + job) * 64 + lane_id()) * GPP * 4) = piece.u;
         });
       } else {  // U, value block: the C tile is the fragment piece
-        const int col = (job - NJ0 - NJ1) * SUB;
+        const int col = (job - NJW) * SUB;
         static_for<0, NSUB>([&](auto II) {
           constexpr int I = decltype(II)::value;
           f32x4 acc = zero4();
