@@ -152,7 +152,9 @@ def design_bytes(role, chunk_lens, H, K, V, esz, besz, gate, nseq, policy):
     tileK, tileV, tile64 = nc * 64 * K * esz, nc * 64 * V * esz, nc * 64 * 64 * esz
     st = nc * K * V * esz
     glast = nc * K * 4
-    g2t = {0: 0, 1: nc * 64 * 4, 2: nc * 64 * K * 4}[gate]
+    # G2 tile of the chunk backward: written for a scalar gate only (the chunk
+    # backward rebuilds G2 of a vector gate from g and the statistics)
+    g2t = {0: 0, 1: nc * 64 * 4, 2: 0}[gate]
     gst = nc * 4 * K * 16
     prep_in = n * (2 * tk + tv + gb + besz)
     w_fscan = 2 * tileK + tileV + glast                   # W, Ft, U, glast
@@ -165,8 +167,10 @@ def design_bytes(role, chunk_lens, H, K, V, esz, besz, gate, nseq, policy):
         "prep_recompute": prep_in + w_fscan + w_bscan + w_bchunk,
         "fwd_scan": fscan_in + w_fout + n * tv + ((st + tileV) if policy == "save" else 0),
         "bwd_scan": w_bscan + glast + n * tv + st + tileV,
-        "bwd_chunk": n * 3 * tv + tile64 + tileV + 2 * st + n * 2 * tk + g2t + gst + glast
-                     + n * besz + n * (2 * tk + tv + gb + besz),
+        # reads dO, v, q, k, beta, A^T, R, Rbar, S, dS+, statistics, glast and
+        # g (vector gate) or the G2 tile (scalar gate); writes dq, dk, dv, dg, dbeta
+        "bwd_chunk": n * (3 * tv + 4 * tk + 2 * besz) + tile64 + 2 * tileV + 2 * st + gst + glast
+                     + (n * gb if gate == 2 else g2t) + n * gb,
     }
     per_head["scans"] = fscan_in + st + tileV + per_head["bwd_scan"]
     b = per_head.get(role)
