@@ -149,6 +149,33 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// 4 x 4 exchange of 4-byte words among the lanes L, L ^ 1, L ^ M and
+// L ^ M ^ 1 (M = 2 or 8: one 16-lane row).  The lane of role
+// j = (L & 1) + 2 [L & M] enters with w[k], its word for item k, and leaves
+// with w[k] = the item-j word of the lane of role k.  Two butterfly stages of
+// DPP lane moves (partner L ^ 1, then L ^ M); no LDS.
+template <int M>
+__device__ __forceinline__ void xpose4_words(uint32_t (&w)[4]) {
+  static_assert(M == 2 || M == 8, "partner lanes within a 16-lane row");
+  constexpr int C2 = M == 2 ? 0x4E : 0x128;  // quad_perm [2,3,0,1] / row_ror:8
+  const int l = lane_id();
+  const bool p1 = l & 1, p2 = l & M;
+#pragma unroll
+  for (int k0 = 0; k0 < 4; k0 += 2) {  // items k0, k0 + 1 with the partner L ^ 1
+    const uint32_t x = p1 ? w[k0] : w[k0 + 1];
+    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+    if (p1) w[k0] = y;
+    else w[k0 + 1] = y;
+  }
+#pragma unroll
+  for (int k0 = 0; k0 < 2; ++k0) {  // items k0, k0 + 2 with the partner L ^ M
+    const uint32_t x = p2 ? w[k0] : w[k0 + 2];
+    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, C2, 0xF, 0xF, false);
+    if (p2) w[k0] = y;
+    else w[k0 + 2] = y;
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ float tof(T x) { return (float)x; }
 template <typename T>

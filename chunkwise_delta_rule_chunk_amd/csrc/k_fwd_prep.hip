@@ -329,11 +329,16 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       constexpr int NKBQ = K / SUB, GPQ = 16 / (4 * (int)sizeof(T));
       T* Ftd = reinterpret_cast<T*>(a.Ft) + cb * K * CH;
       T* Qgtd = reinterpret_cast<T*>(a.Qgt) + cb * K * CH;
-      T* Fd = reinterpret_cast<T*>(a.F) + cb * CH * K +
-              ((sg * NGKF + c0 / KGF) * 64 + ((c0 % KGF) / VE) * 16) * VE + c0 % VE;
-      T* Qgd = reinterpret_cast<T*>(a.Qg) + cb * CH * K +
-               ((((int64_t)sg * (NKBQ / GPQ) + (c0 / SUB) / GPQ) * 64 + 16 * ((c0 % SUB) / 4)) * GPQ +
-                (c0 / SUB) % GPQ) * 4 + c0 % 4;
+      // F and Qg (orders as in the one-column phase below) in whole 16-byte
+      // pieces: the four 4-byte words of a piece row come from four lanes (F:
+      // a lane quad; Qg: lanes L, L ^ 1, L ^ 8, L ^ 9), which exchange their
+      // words for each group of four rows (xpose4_words), so that the lane of
+      // role j stores the piece of row 4 i + j of group i
+      const int tl = c0 >> 1;  // the lane: column pairs run along the wave
+      const int frole = tl & 3, qrole = (tl & 1) + ((tl >> 2) & 2);
+      T* Fp = reinterpret_cast<T*>(a.F) + cb * CH * K + ((sg * NGKF + c0 / KGF) * 64 + ((c0 % KGF) / VE) * 16) * VE;
+      T* Qgp = reinterpret_cast<T*>(a.Qg) + cb * CH * K +
+               (((int64_t)sg * (NKBQ / GPQ) + (c0 / SUB) / GPQ) * 64 + 16 * ((c0 % SUB) / 4)) * GPQ * 4;
       auto pk2 = [](float x, float y) { return __builtin_bit_cast(uint32_t, bf16x2{(bf16)x, (bf16)y}); };
 #pragma unroll
       for (int r8 = 0; r8 < RS; r8 += VE) {
@@ -341,6 +346,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
           uint4 u;
           T e[VE];
         } ft[2], qt[2], et[2];
+        uint32_t qw[4], fw[4];  // words of the current group of four rows
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
           const int r = r8 + e, row = r0 + r;
@@ -365,11 +371,22 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
             ft[j].e[e] = fromf<T>(vF[j]);
             qt[j].e[e] = fromf<T>(vQg[j]);
           }
-          if constexpr (MODE & PREP_FWD_OUT) *reinterpret_cast<uint32_t*>(Qgd + r * GPQ * 4) = pk2(vQg[0], vQg[1]);
-          if constexpr (MODE & PREP_BWD_SCAN) *reinterpret_cast<uint32_t*>(Fd + r * VE) = pk2(vF[0], vF[1]);
+          qw[e & 3] = pk2(vQg[0], vQg[1]);
+          fw[e & 3] = pk2(vF[0], vF[1]);
           *reinterpret_cast<uint32_t*>(sKa + row * PK + c0) = pk2(vKa[0], vKa[1]);
           *reinterpret_cast<uint32_t*>(sQ + row * PK + c0) = pk2(vQa[0], vQa[1]);
           *reinterpret_cast<uint32_t*>(sK + row * PK + c0) = pk2(vKc[0], vKc[1]);
+          if ((e & 3) == 3) {  // group of rows r8 + e - 3 .. r8 + e complete
+            const int rg = r8 + e - 3;
+            if constexpr (MODE & PREP_FWD_OUT) {
+              xpose4_words<8>(qw);
+              *reinterpret_cast<uint4*>(Qgp + (rg + qrole) * GPQ * 4) = uint4{qw[0], qw[1], qw[2], qw[3]};
+            }
+            if constexpr (MODE & PREP_BWD_SCAN) {
+              xpose4_words<2>(fw);
+              *reinterpret_cast<uint4*>(Fp + (rg + frole) * VE) = uint4{fw[0], fw[1], fw[2], fw[3]};
+            }
+          }
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
