@@ -100,7 +100,8 @@ hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
 // workgroup within half of the compute unit's LDS.  The next item's k, q,
 // beta and gates are read into registers while the current item computes
 // (k, q, beta and this item's v once k and q are staged, the gates after the
-// elementwise phase).
+// elementwise phase; the one-column layouts issue all of them before the
+// solve).
 //
 // MODE: the PREP_* sets this launch writes (a compile-time constant, so the
 // loop body holds no flag tests and no pointers of unused outputs).
@@ -292,9 +293,12 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     // ---- S1: finish the prefix, statistics ----------------------------------
     // this item's v and the next item's k, q and beta (the k and q registers
     // are free once staged), issued here so that the rest of the item covers
-    // their latency
-    fetch_v(item, ci, tid);
-    fetch_kq(item + gridDim.x, cnext, tid);
+    // their latency; the one-column layouts issue them with the gates before
+    // the solve (below), where their registers fit without spilling
+    if constexpr (PAIR) {
+      fetch_v(item, ci, tid);
+      fetch_kq(item + gridDim.x, cnext, tid);
+    }
 #pragma unroll
     for (int s = 0; s < NSL; ++s) gc[s].prefix_finish(sTot);
 #pragma unroll
@@ -526,7 +530,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     // ---- S3: score tiles L (strict, fp32 in LDS) and Cq (inclusive, global) --
     // the next item's gates: their registers are free since the elementwise
     // phase
-    fetch_g(item + gridDim.x, cnext);
+    if constexpr (PAIR) fetch_g(item + gridDim.x, cnext);
     {
       T* Cqo = reinterpret_cast<T*>(a.Cq) + cb * CH * CH;
       using FR = typename Frag4<T>::type;
@@ -576,6 +580,11 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     lds_barrier();
 
     // ---- S4: A = (I + L)^-1 in fp32 ------------------------------------------
+    if constexpr (!PAIR) {  // the one-column layouts: all fetches here, before the solve
+      fetch_v(item, ci, tid);
+      fetch_kq(item + gridDim.x, cnext, tid);
+      fetch_g(item + gridDim.x, cnext);
+    }
 
     // A takes X (the score operands are dead); its off-diagonal blocks start
     // at zero, written here while wave 0 forms the diagonal blocks
