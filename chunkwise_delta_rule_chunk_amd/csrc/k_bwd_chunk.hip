@@ -57,8 +57,14 @@ namespace rewy {
 // consumers only (P, D and the write part of dbeta read back, Hq formed as
 // in the joint kernel).  Every value is rounded at the same point in both
 // schedules, so their results are bitwise equal.
+// One workgroup per CU for the erase/write form and for fp32 at V = 32 (both
+// need more than half of a SIMD's registers), two otherwise.
+template <typename T, int V, int GX>
+constexpr int bwd_chunk_wgs() {
+  return ((GX & 4) || (std::is_same_v<T, float> && V == 32)) ? 1 : 2;
+}
 template <typename T, int K, int V, int GX>
-__global__ __launch_bounds__(256, (GX & 4) ? 1 : 2) void k_bwd_chunk(Args a) {
+__global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(Args a) {
   constexpr int GATE = GX & 3;
   constexpr bool EW = GX & 4;
   constexpr bool GIN = GX & 8;

@@ -98,10 +98,10 @@ hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
 // then centred key and query operands, then A, then E^T and Z^T; Y: the
 // prefix totals, then L, then A in the operand type), which keeps a
 // workgroup within half of the compute unit's LDS.  The next item's k, q,
-// beta and gates are read into registers while the current item computes
-// (k, q, beta and this item's v once k and q are staged, the gates after the
-// elementwise phase; the one-column layouts issue all of them before the
-// solve).
+// beta, gates and v are read into registers while the current item computes
+// (k, q and beta once k and q are staged, the gates after the elementwise
+// phase, v once this item's v is in Z^T; the one-column layouts issue them
+// before the solve, v for the item itself).
 //
 // MODE: the PREP_* sets this launch writes (a compile-time constant, so the
 // loop body holds no flag tests and no pointers of unused outputs).
@@ -195,7 +195,6 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   };
   auto fetch_v = [&](int item, const ChunkInfo& ci, int tid) {
     const int h = item % H;
-    if (ci.len == 0) return;
     const int64_t t0 = ci.bos;
     if constexpr (BF) {
       const GBuf bv = gbuf(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, tile_bytes<T>(ci.len, gsV, V));
@@ -257,6 +256,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   ChunkInfo cnext = load_chunk(a.chunks, min((int)blockIdx.x, total - 1) / H);
   fetch_kq(blockIdx.x, cnext, threadIdx.x);
   fetch_g(blockIdx.x, cnext);
+  if constexpr (PAIR) fetch_v(blockIdx.x, cnext, threadIdx.x);
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int tid = opaque_tid(), w = wave_id();
     // slot indices opaque per item: addresses derived from them are recomputed
@@ -272,6 +272,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     if (n == 0) {  // uniform: an empty chunk slot
       fetch_kq(item + gridDim.x, cnext, tid);
       fetch_g(item + gridDim.x, cnext);
+      if constexpr (PAIR) fetch_v(item + gridDim.x, cnext, tid);
       continue;
     }
     const int64_t t0 = ci.bos, cb = (int64_t)c * H + h;
@@ -291,14 +292,11 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     lds_barrier();
 
     // ---- S1: finish the prefix, statistics ----------------------------------
-    // this item's v and the next item's k, q and beta (the k and q registers
-    // are free once staged), issued here so that the rest of the item covers
-    // their latency; the one-column layouts issue them with the gates before
+    // the next item's k, q and beta (their registers are free once staged),
+    // issued here so that the rest of the item covers their latency; the
+    // one-column layouts issue them with this item's v and the gates before
     // the solve (below), where their registers fit without spilling
-    if constexpr (PAIR) {
-      fetch_v(item, ci, tid);
-      fetch_kq(item + gridDim.x, cnext, tid);
-    }
+    if constexpr (PAIR) fetch_kq(item + gridDim.x, cnext, tid);
 #pragma unroll
     for (int s = 0; s < NSL; ++s) gc[s].prefix_finish(sTot);
 #pragma unroll
@@ -687,6 +685,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       }
     }
     lds_barrier();
+    if constexpr (PAIR) fetch_v(item + gridDim.x, cnext, tid);  // the staged v is in Z^T
 
     // W, U in operand-fragment order (see kernels.hpp), all 64 rows (rows past
     // the chunk's end are exact zeros).  Each tile of W^T is formed once: its C
