@@ -314,9 +314,20 @@ __device__ __forceinline__ void fwd_scan_output(const Args& a, const int u, cons
   auto fetch_cq = [&](auto set, int c) {
     constexpr int B = decltype(set)::value;
     const int64_t cb = (int64_t)min(c, c1 - 1) * H + h;
-    const T* cp = reinterpret_cast<const T*>(a.Cq) + cb * CH * CH + (int64_t)(w * NSUB * 64 + l) * 4;
+    // Cq is lower triangular: its blocks right of the diagonal (J > w) are
+    // zero and are not read (an offset past the buffer's range returns
+    // zeros); otherwise as cfrag_op, blocks 2 q and 2 q + 1 joined (bf16)
+    const GBuf bc = gbuf(reinterpret_cast<const T*>(a.Cq) + cb * CH * CH, CH * CH * sizeof(T));
+    auto off = [&](int J) { return J > w ? OOB : (uint32_t)(((w * NSUB + J) * 64 + l) * 4 * (int)sizeof(T)); };
 #pragma unroll
-    for (int q = 0; q < NGT; ++q) cqf[B][q] = cfrag_op<T>(cp, q);
+    for (int q = 0; q < NGT; ++q) {
+      if constexpr (std::is_same_v<T, bf16>) {
+        const uint2 x0 = gld8(bc, off(2 * q)), x1 = gld8(bc, off(2 * q + 1));
+        cqf[B][q] = uint4{x0.x, x0.y, x1.x, x1.y};
+      } else {
+        cqf[B][q] = gld16(bc, off(q));
+      }
+    }
   };
   static_for<0, DEPTH>([&](auto B) {
     fetch_q(B, c0 + B);
@@ -602,9 +613,13 @@ __device__ __forceinline__ void bwd_scan_side(const Args& a, const int u, const 
     const int cc = chunk_of(c);
     const int bos = sr.seq_bos + (cc - c0) * CH, len = min(CH, sr.seq_eos - bos);
     const int64_t cb = (int64_t)cc * H + h;
-    const T* cp = reinterpret_cast<const T*>(a.Cqt) + cb * CH * CH + (int64_t)(w * NGT * 64 + l) * VE;
+    // Cq^T is upper triangular: a piece whose columns (tokens i) all lie
+    // before the wave's rows is zero and is not read (an offset past the
+    // buffer's range returns zeros)
+    const GBuf bcq = gbuf(reinterpret_cast<const T*>(a.Cqt) + cb * CH * CH, CH * CH * sizeof(T));
 #pragma unroll
-    for (int q = 0; q < NGT; ++q) cf[B][q] = *reinterpret_cast<const uint4*>(cp + q * 64 * VE);
+    for (int q = 0; q < NGT; ++q)
+      cf[B][q] = gld16(bcq, KG * (q + 1) <= SUB * w ? OOB : (uint32_t)(((w * NGT + q) * 64 + l) * VE * (int)sizeof(T)));
 #pragma unroll
     for (int j = 0; j < KW; ++j) {
       const T* qp = reinterpret_cast<const T*>(a.Qgt) + cb * K * CH + (int64_t)(ktile(j) * NGT * 64 + l) * VE;
