@@ -105,7 +105,8 @@ int make_plan(const rewy_desc* d, Plan& p) {
 // Buffer layout.  `saved` holds what the backward reads from the forward under
 // the save-all policy; everything else is scratch in the workspace.  The
 // reverse set is what the reverse scan and the chunk backward read:
-// F Wt Qgt Cqt (reverse scan) and At G2t Gst (chunk backward).
+// F Wt Qgt Cqt (reverse scan) and At G2t Gst (chunk backward; G2t only for a
+// scalar gate).
 //   recompute: ws = [index | glast | W Ft U | (fwd) Qg Cq
 //                                           | (bwd) hbuf R reverse set Rbt dhbuf]
 //   save-all:  saved = [glast hbuf R | reverse set]
@@ -132,8 +133,7 @@ Layout layout(const Plan& p) {
   const size_t nc = p.nc_max, H = p.H, K = p.K, V = p.V, e = p.esz;
   const size_t tileK = nc * H * K * CH * e, tileV = nc * H * V * CH * e;
   const size_t tile64 = nc * H * CH * CH * e, states = nc * H * K * V * e;
-  const size_t g2 = p.gate == REWY_GATE_VECTOR ? nc * H * K * CH * 4
-                    : p.gate == REWY_GATE_SCALAR ? nc * H * CH * 4 : 0;
+  const size_t g2 = p.gate == REWY_GATE_SCALAR ? nc * H * CH * 4 : 0;  // G2 row of a scalar gate
   size_t off = 0;
   auto take = [&](size_t& o, size_t bytes) { const size_t r = o; o += up(bytes); return r; };
   auto take_reverse = [&](size_t& o) {

@@ -404,15 +404,16 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
   // products).  Every load is unconditional: a scalar gate has one G2 row
   // (the others read as zero) and no gate reads none.
   TileRegs<float, SUB, CH, NTH> pG;
-  // A vector gate given as g: G2 of the feature block is rebuilt here from g
-  // (the prep keeps only its sub-chunk statistics).  Wave w takes rows
-  // [16 w, 16 w + 16): lane (q4, f) reads g at rows 16 w + 4 q4 + e of feature
-  // 16 fb + f and G2 at the block's first row (its statistics record; zero for
-  // a block past the chunk's end, whose G2 is never used).  The gate formed in
-  // the kernels and the scalar gate read the prep's G2 tile.
-  constexpr bool GRAW = GATE == 2 && !GIN;
-  uint32_t graw[GRAW ? 4 : 1], gfw = 0u;
-  const GBuf bgr = gbuf(a.g + (t0 * H + h) * K, GRAW ? tile_bytes<float>(n, gsK, K) : 0u);
+  // A vector gate: G2 of the feature block is rebuilt here (the prep keeps
+  // only its sub-chunk statistics).  Wave w takes rows [16 w, 16 w + 16):
+  // lane (q4, f) reads g at rows 16 w + 4 q4 + e of feature 16 fb + f (the
+  // gate formed in the kernels: x there and dt_bias of the feature, g formed
+  // as in the prep) and G2 at the block's first row (its statistics record;
+  // zero for a block past the chunk's end, whose G2 is never used).  The
+  // scalar gate reads the prep's G2 row.
+  constexpr bool GRAW = GATE == 2;
+  uint32_t graw[GRAW ? 4 : 1], gfw = 0u, gdw = 0u;
+  const GBuf bgr = gbuf(a.g + (t0 * H + h) * K, GRAW && !GIN ? tile_bytes<float>(n, gsK, K) : 0u);
   const GBuf bgf = gbuf(Gstg, GRAW ? (uint32_t)(((n + SUB - 1) / SUB) * K * 16) : 0u);
   // k and q of a feature block from their natural rows: a piece is KQV
   // features of one token; the first half of the pieces is k, the second q
@@ -430,19 +431,23 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
   TileRegs<float, NSUB, SUB * 4, NTH> pX;
   TileRegs<T, SUB, V, NTH> pS, pD;
   TileRegs<float, 1, SUB, NTH> pN;
-  // G2^T, K^T and Q^T are column-blocked [64/16][K][16] (a scalar gate: one
-  // row, [64]; rows 1 .. 15 of its tile are not used)
-  const float* gp = GATE == 2 ? a.G2t + cb * K * CH : a.G2t + cb * CH;
-  const int grt = GATE == 2 ? K : 1;
-  const uint32_t gbytes = GATE == 2 ? K * CH * 4 : GATE == 1 ? CH * 4 : 0;
+  // the scalar gate's G2 row [64] (rows 1 .. 15 of the tile read as zero and
+  // are not used)
+  const float* gp = a.G2t + cb * CH;
+  const uint32_t gbytes = GATE == 1 ? CH * 4 : 0;
   auto fetch_fb = [&](int fb) {
     if constexpr (GRAW) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        graw[e] = gld4(bgr, (uint32_t)(((int64_t)(w * SUB + 4 * q4 + e) * gsK + fb * SUB + f) * 4));
+      for (int e = 0; e < 4; ++e) {
+        const int64_t el = (int64_t)(w * SUB + 4 * q4 + e) * gsK + fb * SUB + f;
+        if constexpr (!GIN) graw[e] = gld4(bgr, (uint32_t)(el * 4));
+        else if constexpr (sizeof(T) == 2) graw[e] = gld2(bgx, (uint32_t)(el * 2));
+        else graw[e] = gld4(bgx, (uint32_t)(el * 4));
+      }
+      if constexpr (GIN) gdw = gld4(bdt, (uint32_t)((fb * SUB + f) * 4));
       gfw = gld4(bgf, (uint32_t)(((w * K + fb * SUB + f) * 4) * 4));
     } else {
-      pG.load_cb(gbuf(gp, gbytes), grt, GATE == 2 ? fb * SUB : 0, tid);
+      pG.load_cb(gbuf(gp, gbytes), 1, 0, tid);
     }
 #pragma unroll
     for (int j = 0; j < KQN; ++j) {
@@ -469,10 +474,22 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
     if constexpr (GRAW) {
       // G2 = G2 at the first row + log2(e) times the sum of g over the later
       // rows up to this one (in-lane over four rows, then the lane rows before)
-      f32x4 x;
-      x[0] = q4 == 0 ? 0.f : __uint_as_float(graw[0]);
+      f32x4 gv;
 #pragma unroll
-      for (int e = 1; e < 4; ++e) x[e] = x[e - 1] + __uint_as_float(graw[e]);
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (GIN) {  // g = -ea softplus(z) or lb sigmoid(ea z), z = x + dt_bias; zero past the end
+          const float z = (sizeof(T) == 2 ? __uint_as_float(graw[e] << 16) : __uint_as_float(graw[e])) +
+                          __uint_as_float(gdw);
+          const float gg = lb == 0.f ? nea * softplus(z) : lb * sigmoid_f(-nea * z);
+          gv[e] = w * SUB + 4 * q4 + e < n ? gg : 0.f;
+        } else {
+          gv[e] = __uint_as_float(graw[e]);
+        }
+      }
+      f32x4 x;
+      x[0] = q4 == 0 ? 0.f : gv[0];
+#pragma unroll
+      for (int e = 1; e < 4; ++e) x[e] = x[e - 1] + gv[e];
       const float off = rows_prefix_excl(x[3], q4), gf = __uint_as_float(gfw);
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = gf + LOG2E * (off + x[e]);

@@ -405,8 +405,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       for (int j = 0; j < 2; ++j) {
         const int col = c0 + j;
         if constexpr (MODE & PREP_BWD_CHUNK) {
-          float* G2d = a.gate == 2 ? (GIN ? a.G2t + cb * K * CH + ((int64_t)sg * K + col) * SUB : nullptr)
-                                   : (a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr);
+          float* G2d = a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr;
           if (G2d)
 #pragma unroll
             for (int r4 = 0; r4 < RS; r4 += 4)
@@ -507,14 +506,11 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
           *reinterpret_cast<uint4*>(Qgtd + (((col / SUB) * NGTF + q) * 64 + gq * 16 + col % SUB) * VE) = qt.u;
         }
       }
-      // G2^T column-blocked [64/16][K][16]: this thread's 16 rows are one block
-      // row, and a wave's consecutive columns are contiguous (rows past the end
-      // hold G2 of the last row).  Written for a scalar gate and for the gate
-      // formed in the kernels; the chunk backward rebuilds G2 of a given
-      // vector gate from g and the statistics.
+      // the scalar gate's G2 row (rows past the end hold G2 of the last row);
+      // the chunk backward rebuilds G2 of a vector gate from g (or x) and the
+      // statistics
       if constexpr (MODE & PREP_BWD_CHUNK) {
-        float* G2d = a.gate == 2 ? (GIN ? a.G2t + cb * K * CH + ((int64_t)g.seg * K + col) * SUB : nullptr)
-                                 : (a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr);
+        float* G2d = a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr;
         if (G2d)
 #pragma unroll
           for (int r4 = 0; r4 < RS; r4 += 4)

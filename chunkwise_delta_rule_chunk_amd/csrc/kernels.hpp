@@ -90,9 +90,8 @@ struct Args {
   void* R;       // corrections U - W S [nc,H,V/16,64,16] dtype (column-blocked, zero past the end)
   int scan_out;  // SCAN_* bits: whether the forward scan writes hbuf/R and whether it forms o
   void* At;      // A^T                 [nc,H,64,64] chunk backward (P = A^T Rbar)
-  float* G2t;    // G2^T  [nc,H,64/16,K,16] column-blocked (vector gate formed in the kernels) or
-                 // [nc,H,64] (scalar gate); not written for a given vector gate, whose G2 the
-                 // chunk backward rebuilds from g and Gst
+  float* G2t;    // G2 of a scalar gate [nc,H,64] (rows past the end: G2 of the last row); the
+                 // chunk backward rebuilds G2 of a vector gate from g (or x) and Gst
   float* Gst;    // sub-chunk gate statistics [nc,H,4,K] of float4 {G2 at the first row,
                  // G2 at the last valid row, midpoint (max+min)/2, range max-min}
   // backward intermediates
@@ -111,7 +110,7 @@ constexpr int SCAN_OUTPUT = 2;   // o = Qg S + Cq R, formed by the forward scan
 constexpr int PREP_FWD_SCAN = 1;  // W, Ft, U, glast
 constexpr int PREP_FWD_OUT = 2;   // Qg, Cq
 constexpr int PREP_BWD_SCAN = 4;  // F, Wt, Qgt, Cqt, glast
-constexpr int PREP_BWD_CHUNK = 8; // At, Gst, G2t (scalar gate or gate formed in the kernels)
+constexpr int PREP_BWD_CHUNK = 8; // At, Gst, G2t (scalar gate)
 // The erase/write form: beta holds the erase gate b [.., K] and wg the write
 // gate w [.., V] (both in the feature dtype); E = b gamma K and Z = w V.
 constexpr int PREP_EW = 16;

@@ -107,7 +107,7 @@ def test_workspace_sizes_follow_the_layout(lib):
     scan = tokK + tileK + tokV                                          # W, Ft, U
     out = tileK + tile64                                                # Qg, Cq
     rscan = tokK + 2 * tileK + tile64                                   # F, Wt, Qgt, Cqt
-    rscan += tile64 + up(nc * H * K * 64 * 4)                           # At, G2t
+    rscan += tile64                                                     # At (no G2 tile: vector gate)
     rscan += up(nc * H * 4 * K * 16)                                    # Gst
     bwd = up(nc * H * V * 64 * e) + up(nc * H * K * V * e)              # Rbt, dhbuf
     shared = glast + states
