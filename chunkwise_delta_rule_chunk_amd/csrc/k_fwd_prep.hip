@@ -562,13 +562,18 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
           pairwise_diag<T, K, true, EW, GIN>(a, t0, h, n, J, sBeta, sFlag + J * (K / SUB), accL, accC);
           store(J, J, accL, accC);
         }
-      // tiles nobody computed: zeros (the upper triangle and rows past the end)
+      // tiles nobody computed: zeros (rows past the end; of the upper
+      // triangle only what the scans read: the forward scan reads blocks
+      // J <= I only, the reverse scan skips the 16-byte pieces of C_q^T whose
+      // tokens i all lie before its rows j)
+      constexpr int KGQ = 4 * (16 / (int)sizeof(T));  // tokens per piece of C_q^T
       for (int t = w; t < NSUB * NSUB; t += NW) {
         const int I = t / NSUB, J = t - I * NSUB;
         if (J <= I && I * SUB < n) continue;
         if constexpr (MODE & PREP_FWD_OUT)
-          *reinterpret_cast<FR*>(Cqo + ((I * NSUB + J) * 64 + lane_id()) * 4) = to_frag<T>(zero4());
-        if constexpr (MODE & PREP_BWD_SCAN) st_frag_T<T>(zero4(), Cqto, I, J);
+          if (J <= I) *reinterpret_cast<FR*>(Cqo + ((I * NSUB + J) * 64 + lane_id()) * 4) = to_frag<T>(zero4());
+        if constexpr (MODE & PREP_BWD_SCAN)
+          if (KGQ * ((I * SUB) / KGQ + 1) > SUB * J) st_frag_T<T>(zero4(), Cqto, I, J);
       }
     }
     lds_barrier();
