@@ -451,22 +451,11 @@ __device__ __forceinline__ void mma16B(f32x4& acc, uint4 a, uint4 b) {
 // block (rb, cb) at piece (rb * ncb + cb) * 64 + l, four elements per lane,
 // M[16 rb + 4 (l >> 4) + i][16 cb + (l & 15)] for i < 4.  That piece is the
 // 16-long B fragment of M (and A fragment of M^T) for a contraction over M's
-// row index.  cfrag_op() reads the operand of one lane group of a contraction
-// over rows 32 q .. 32 q + 31 (bf16, blocks 2 q and 2 q + 1 joined: slot
-// 8 (l >> 4) + e is row 32 q + 4 (l >> 4) + e, slot 8 (l >> 4) + 4 + e is row
-// 32 q + 16 + 4 (l >> 4) + e) or 16 q .. 16 q + 15 (fp32, block q);
+// row index.  The operand of one lane group of a contraction over rows
+// 32 q .. 32 q + 31 joins blocks 2 q and 2 q + 1 (bf16: slot 8 (l >> 4) + e
+// is row 32 q + 4 (l >> 4) + e, slot 8 (l >> 4) + 4 + e is row
+// 32 q + 16 + 4 (l >> 4) + e; fp32 takes rows 16 q .. 16 q + 15 from block q);
 // perm_row() reads the other operand's row with the same slot assignment.
-// p points at the lane's piece of block cb = 0 (base + l * 4 elements).
-template <typename T>
-__device__ __forceinline__ uint4 cfrag_op(const T* p, int q) {
-  if constexpr (std::is_same_v<T, bf16>) {
-    const uint2 x0 = *reinterpret_cast<const uint2*>(p + (2 * q) * 256);
-    const uint2 x1 = *reinterpret_cast<const uint2*>(p + (2 * q + 1) * 256);
-    return uint4{x0.x, x0.y, x1.x, x1.y};
-  } else {
-    return *reinterpret_cast<const uint4*>(p + q * 256);
-  }
-}
 // row points at element 4 (l >> 4) of the row (LDS)
 template <typename T>
 __device__ __forceinline__ uint4 perm_row(const T* row, int q) {

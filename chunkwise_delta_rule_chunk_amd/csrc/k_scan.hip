@@ -316,7 +316,8 @@ __device__ __forceinline__ void fwd_scan_output(const Args& a, const int u, cons
     const int64_t cb = (int64_t)min(c, c1 - 1) * H + h;
     // Cq is lower triangular: its blocks right of the diagonal (J > w) are
     // zero and are not read (an offset past the buffer's range returns
-    // zeros); otherwise as cfrag_op, blocks 2 q and 2 q + 1 joined (bf16)
+    // zeros); blocks 2 q and 2 q + 1 joined into one operand (bf16, the slot
+    // assignment of C-fragment order in common.hpp)
     const GBuf bc = gbuf(reinterpret_cast<const T*>(a.Cq) + cb * CH * CH, CH * CH * sizeof(T));
     auto off = [&](int J) { return J > w ? OOB : (uint32_t)(((w * NSUB + J) * 64 + l) * 4 * (int)sizeof(T)); };
 #pragma unroll
