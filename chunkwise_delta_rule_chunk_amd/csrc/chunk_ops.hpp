@@ -230,7 +230,8 @@ __device__ __forceinline__ void pair_factors(const float* sMid, const float* sGf
 
 // One score tile from pre-scaled operands (natural [token][feature] layout,
 // pitch PK, bf16 or fp32), accumulated into accL / accC:
-// L_IJ += (Ka_I * f_IJ) Kc_J^T and, with WITH_CQ, Cq_IJ += (Qa_I * f_IJ) Kc_J^T
+// L_IJ += Ka_I (Kc_J * f_IJ)^T and, with WITH_CQ, Cq_IJ += Qa_I (Kc_J * f_IJ)^T,
+// the per-feature pair factor on the sending operand both products share
 // (the triangles are cut by the caller).  A diagonal tile skips the factors
 // unless `masked` (a flagged diagonal: f is 1 or 0 per feature).  One wave.
 template <typename T, int K, bool WITH_CQ>
@@ -246,29 +247,23 @@ __device__ __forceinline__ void score_tile(const T* sKa, const T* sQa, const T* 
       typename MM<T>::frag ak, aq, bk;
       if constexpr (BF) {
         const int kb = k0 + (l >> 4) * 8;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sKa + ri * PK + kb);
-        bk = *reinterpret_cast<const bf16x8*>(sKc + rj * PK + kb);
-        bf16x8 qa;
-        if constexpr (WITH_CQ) qa = *reinterpret_cast<const bf16x8*>(sQa + ri * PK + kb);
+        ak = *reinterpret_cast<const bf16x8*>(sKa + ri * PK + kb);
+        if constexpr (WITH_CQ) aq = *reinterpret_cast<const bf16x8*>(sQa + ri * PK + kb);
+        const bf16x8 kc = *reinterpret_cast<const bf16x8*>(sKc + rj * PK + kb);
         if (plain) {
-          ak = ka;
-          if constexpr (WITH_CQ) aq = qa;
-        } else {
+          bk = kc;
+        } else {  // the pair factor on the sending operand, which both products share
           const f32x4 f0 = *reinterpret_cast<const f32x4*>(f + kb);
           const f32x4 f1 = *reinterpret_cast<const f32x4*>(f + kb + 4);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float fe = e < 4 ? f0[e] : f1[e - 4];
-            ak[e] = (bf16)((float)ka[e] * fe);
-            if constexpr (WITH_CQ) aq[e] = (bf16)((float)qa[e] * fe);
-          }
+          for (int e = 0; e < 8; ++e) bk[e] = (bf16)((float)kc[e] * (e < 4 ? f0[e] : f1[e - 4]));
         }
       } else {
         const int kk = k0 + (l >> 4);
         const float fe = plain ? 1.f : f[kk];
-        ak = tof(sKa[ri * PK + kk]) * fe;
-        if constexpr (WITH_CQ) aq = tof(sQa[ri * PK + kk]) * fe;
-        bk = sKc[rj * PK + kk];
+        ak = tof(sKa[ri * PK + kk]);
+        if constexpr (WITH_CQ) aq = tof(sQa[ri * PK + kk]);
+        bk = tof(sKc[rj * PK + kk]) * fe;
       }
       accL = mma(ak, bk, accL);
       if constexpr (WITH_CQ) accC = mma(aq, bk, accC);
