@@ -44,6 +44,18 @@ namespace rewy {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+// Value i of the lane's quad (lane 4 (l >> 2) + i): with x = glast of row
+// kr + 4 (l >> 4) + (l & 3) in every lane, that is row kr + 4 (l >> 4) + i
+// (DPP quad broadcast, VALU only).
+__device__ __forceinline__ float glast_rows(float x, int i) {
+  switch (i) {
+    case 0: return dpp_mov<0x00>(x);
+    case 1: return dpp_mov<0x55>(x);
+    case 2: return dpp_mov<0xAA>(x);
+    default: return dpp_mov<0xFF>(x);
+  }
+}
+
 // Scan workgroup: the chain waves, then the side waves.
 constexpr int SCAN_THREADS = 512;
 constexpr int CHAIN_WAVES = 4;
@@ -123,7 +135,12 @@ __device__ __forceinline__ void fwd_scan_chain(const Args& a, const int u, const
   uint4 wf[DEPTH][NGK];      // W rows 16 w + r16, GPP 16-long key groups per piece
   FR uf[DEPTH][CT];          // U in the C layout of R's tiles
   uint4 ff[DEPTH][KW][NGT];  // F^T rows 16 ktile + r16, lane piece of every token group
-  f32x4 lam[DEPTH][KW];      // G2_last of the state rows this lane holds
+  // G2_last of the state rows: lane l holds row kr + 4 (l >> 4) + (l & 3), and
+  // each lane takes the four rows 4 (l >> 4) + i it needs from its quad
+  // (glast_rows): one 4-byte load per lane instead of a 16-byte load of four
+  // values that every lane of a row shares, which spent the address unit's
+  // cycles on repeats
+  float lam[DEPTH][KW];
   // past the last chunk the last one is read again (valid memory, never used)
   auto fetch_wu = [&](auto set, int c) {
     constexpr int B = decltype(set)::value;
@@ -144,7 +161,7 @@ __device__ __forceinline__ void fwd_scan_chain(const Args& a, const int u, const
       const T* fp = Ftg + cb * K * CH + (int64_t)(ktile(j) * NGT * 64 + l) * VE;
 #pragma unroll
       for (int q = 0; q < NGT; ++q) ff[B][j][q] = *reinterpret_cast<const uint4*>(fp + q * 64 * VE);
-      lam[B][j] = *reinterpret_cast<const f32x4*>(a.glast + cb * K + kr + 4 * g);
+      lam[B][j] = a.glast[cb * K + kr + 4 * g + (l & 3)];
     }
   };
 
@@ -253,7 +270,7 @@ __device__ __forceinline__ void fwd_scan_chain(const Args& a, const int u, const
     for (int j = 0; j < KW; ++j) {
       f32x4 d;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = fexp2(lam[B][j][i]);
+      for (int i = 0; i < 4; ++i) d[i] = fexp2(glast_rows(lam[B][j], i));
 #pragma unroll
       for (int m = 0; m < CW; ++m) {
         const T* rb = sRt + (SUB * vtile(m) + r16) * PA + VE * g;
@@ -445,7 +462,7 @@ __device__ __forceinline__ void bwd_scan_chain(const Args& a, const int u, const
 
   uint4 ff[DEPTH][NGK];      // F row 16 w + r16 (keys)
   uint4 wf[DEPTH][KW][NGT];  // W^T row 16 ktile + r16 (tokens)
-  f32x4 lam[DEPTH][KW];
+  float lam[DEPTH][KW];  // G2_last, one row per lane (as in the forward chain)
   using FR = typename Frag4<T>::type;
   // identity as the B operand of a 16-long product (C = X^T I, exact): the
   // natural-layout dS_{c+1} leaves the registers as pieces of one row
@@ -467,7 +484,7 @@ __device__ __forceinline__ void bwd_scan_chain(const Args& a, const int u, const
       const T* wp = reinterpret_cast<const T*>(a.Wt) + cb * K * CH + (int64_t)(ktile(j) * NGT * 64 + l) * VE;
 #pragma unroll
       for (int q = 0; q < NGT; ++q) wf[B][j][q] = *reinterpret_cast<const uint4*>(wp + q * 64 * VE);
-      lam[B][j] = *reinterpret_cast<const f32x4*>(a.glast + cb * K + kr + 4 * g);
+      lam[B][j] = a.glast[cb * K + kr + 4 * g + (l & 3)];
     }
   };
 
@@ -549,7 +566,7 @@ __device__ __forceinline__ void bwd_scan_chain(const Args& a, const int u, const
     for (int j = 0; j < KW; ++j) {
       f32x4 d;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = fexp2(lam[B][j][i]);
+      for (int i = 0; i < 4; ++i) d[i] = fexp2(glast_rows(lam[B][j], i));
       uint4 wn[NGT];
       constexpr unsigned SGN = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
 #pragma unroll
