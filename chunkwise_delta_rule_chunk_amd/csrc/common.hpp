@@ -402,6 +402,21 @@ __device__ __forceinline__ ChunkInfo load_chunk(const ChunkInfo* p, int c) {
   return r;
 }
 
+// A view of the kernel's arguments in the kernarg segment (the kernel's only
+// argument is the Args record at its start).  Reading a field through it is a
+// scalar load that hits the scalar cache.  After renew(), the compiler can no
+// longer reuse values loaded or addresses derived before it, so they need not
+// stay in scalar registers across a long kernel: a persistent kernel whose
+// argument pointers and per-item addresses all stayed live spilled them to
+// vector-register lanes and reloaded them one lane read at a time.
+struct KernArgs {
+  const __attribute__((address_space(4))) char* p;
+  __device__ __forceinline__ KernArgs() : p((const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr()) {}
+  template <typename A>
+  __device__ __forceinline__ const A& get() const { return *(const A*)(const char*)p; }
+  __device__ __forceinline__ void renew() { asm volatile("" : "+s"(p)); }
+};
+
 // ---- operand-fragment order ---------------------------------------------------
 // A tile with 64-long rows stored so that the MFMA operand fragments of a row
 // block are contiguous: with VE = 16 / sizeof(T) and KG = 4 VE, piece

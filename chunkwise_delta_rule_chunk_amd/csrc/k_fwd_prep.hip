@@ -106,7 +106,7 @@ hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
 // MODE: the PREP_* sets this launch writes (a compile-time constant, so the
 // loop body holds no flag tests and no pointers of unused outputs).
 template <typename T, int K, int V, int MODE>
-__global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args a) {
+__global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args) {
   // the erase/write form runs one workgroup per CU: the erase gate of the
   // thread's rows and the write gate's v pieces need registers
   constexpr bool EW = MODE & PREP_EW;
@@ -149,8 +149,13 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   float* const sL = reinterpret_cast<float*>(sY);                      // S2-S4
   T* const sAb = reinterpret_cast<T*>(sY);                             // S5 (bf16)
 
-  const int H = a.H;
-  const int total = a.nc_max * H;
+  // the arguments are read through a kernarg view renewed at every phase, so
+  // that pointers and per-item output addresses are re-read where used
+  // instead of living (and spilling) across the item loop
+  KernArgs kargs;
+  auto ka = [&]() -> const Args& { return kargs.template get<Args>(); };
+  const int H = ka().H;
+  const int total = ka().nc_max * H;
   const int64_t gsK = (int64_t)H * K, gsV = (int64_t)H * V;
 
   // gate slots; their G registers hold the next item's raw gates from the end
@@ -189,15 +194,15 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   auto fetch_kq = [&](int item, const ChunkInfo& ci, int tid) {
     const int h = item % H;
     const int64_t t0 = ci.bos;
-    pk.load(gbuf(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
-    pq.load(gbuf(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
-    if constexpr (!EW) pbeta = ld_beta_raw(a.beta, a.beta_f32, (t0 + min(tid, max(ci.len - 1, 0))) * H + h);
+    pk.load(gbuf(reinterpret_cast<const T*>(ka().k) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
+    pq.load(gbuf(reinterpret_cast<const T*>(ka().q) + (t0 * H + h) * K, tile_bytes<T>(ci.len, gsK, K)), gsK, tid);
+    if constexpr (!EW) pbeta = ld_beta_raw(ka().beta, ka().beta_f32, (t0 + min(tid, max(ci.len - 1, 0))) * H + h);
   };
   auto fetch_v = [&](int item, const ChunkInfo& ci, int tid) {
     const int h = item % H;
     const int64_t t0 = ci.bos;
     if constexpr (BF) {
-      const GBuf bv = gbuf(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, tile_bytes<T>(ci.len, gsV, V));
+      const GBuf bv = gbuf(reinterpret_cast<const T*>(ka().v) + (t0 * H + h) * V, tile_bytes<T>(ci.len, gsV, V));
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         const int sl = tid + j * NTH, p = sl % 32, c0 = (sl / 32) * 8;
@@ -205,41 +210,41 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
         pv2[2 * j] = gld16(bv, ok ? (uint32_t)(((int64_t)(2 * p) * gsV + c0) * 2) : OOB);
         pv2[2 * j + 1] = gld16(bv, ok ? (uint32_t)(((int64_t)(2 * p + 1) * gsV + c0) * 2) : OOB);
         if constexpr (EW) {
-          const GBuf bw = gbuf(reinterpret_cast<const T*>(a.wg) + (t0 * H + h) * V, tile_bytes<T>(ci.len, gsV, V));
+          const GBuf bw = gbuf(reinterpret_cast<const T*>(ka().wg) + (t0 * H + h) * V, tile_bytes<T>(ci.len, gsV, V));
           pw2[2 * j] = gld16(bw, ok ? (uint32_t)(((int64_t)(2 * p) * gsV + c0) * 2) : OOB);
           pw2[2 * j + 1] = gld16(bw, ok ? (uint32_t)(((int64_t)(2 * p + 1) * gsV + c0) * 2) : OOB);
         }
       }
     } else {
-      pv.load(reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, gsV, ci.len, tid);
-      if constexpr (EW) pw.load(reinterpret_cast<const T*>(a.wg) + (t0 * H + h) * V, gsV, ci.len, tid);
+      pv.load(reinterpret_cast<const T*>(ka().v) + (t0 * H + h) * V, gsV, ci.len, tid);
+      if constexpr (EW) pw.load(reinterpret_cast<const T*>(ka().wg) + (t0 * H + h) * V, gsV, ci.len, tid);
     }
   };
   auto fetch_g = [&](int item, const ChunkInfo& ci) {
     const int h = item % H;
     if constexpr (GIN) {
-      const GBuf bd = gbuf(a.dt_bias + (int64_t)h * K, K * 4);
+      const GBuf bd = gbuf(ka().dt_bias + (int64_t)h * K, K * 4);
       if constexpr (PAIR) {
-        gc[0].template load_x_pair<T>(gc[1], a, (int64_t)ci.bos, h, ci.len, K);
+        gc[0].template load_x_pair<T>(gc[1], ka(), (int64_t)ci.bos, h, ci.len, K);
         const uint2 d2 = gld8(bd, gc[0].c * 4);
         gdtb[0] = d2.x;
         gdtb[1] = d2.y;
       } else {
 #pragma unroll
         for (int s = 0; s < NSL; ++s) {
-          gc[s].template load_x<T>(a, (int64_t)ci.bos, h, ci.len, K);
+          gc[s].template load_x<T>(ka(), (int64_t)ci.bos, h, ci.len, K);
           gdtb[s] = gld4(bd, gc[s].c * 4);
         }
       }
-      gal = gld4(gbuf(a.a_log, a.H * 4), h * 4);
+      gal = gld4(gbuf(ka().a_log, ka().H * 4), h * 4);
     } else if constexpr (PAIR) {
-      gc[0].load_pair(gc[1], a, (int64_t)ci.bos, h, ci.len, K);
+      gc[0].load_pair(gc[1], ka(), (int64_t)ci.bos, h, ci.len, K);
     } else {
 #pragma unroll
-      for (int s = 0; s < NSL; ++s) gc[s].load(a, (int64_t)ci.bos, h, ci.len, K, 0);
+      for (int s = 0; s < NSL; ++s) gc[s].load(ka(), (int64_t)ci.bos, h, ci.len, K, 0);
     }
     if constexpr (EW) {  // erase gate rows past the end read as zero
-      const GBuf bb = gbuf(reinterpret_cast<const T*>(a.beta) + ((int64_t)ci.bos * H + h) * K,
+      const GBuf bb = gbuf(reinterpret_cast<const T*>(ka().beta) + ((int64_t)ci.bos * H + h) * K,
                            tile_bytes<T>(ci.len, gsK, K));
 #pragma unroll
       for (int s = 0; s < NSL; ++s)
@@ -253,11 +258,12 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   };
 
   // (the grid never exceeds the item count, so blockIdx.x < total)
-  ChunkInfo cnext = load_chunk(a.chunks, min((int)blockIdx.x, total - 1) / H);
+  ChunkInfo cnext = load_chunk(ka().chunks, min((int)blockIdx.x, total - 1) / H);
   fetch_kq(blockIdx.x, cnext, threadIdx.x);
   fetch_g(blockIdx.x, cnext);
   if constexpr (PAIR) fetch_v(blockIdx.x, cnext, threadIdx.x);
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    kargs.renew();
     const int tid = opaque_tid(), w = wave_id();
     // slot indices opaque per item: addresses derived from them are recomputed
     // rather than hoisted out of the item loop (where they would stay live and
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     const ChunkInfo ci = cnext;
     const int n = ci.len;
     // the next item's record (the last one again past the end: never used)
-    cnext = load_chunk(a.chunks, min(item + (int)gridDim.x, total - 1) / H);
+    cnext = load_chunk(ka().chunks, min(item + (int)gridDim.x, total - 1) / H);
     if (n == 0) {  // uniform: an empty chunk slot
       fetch_kq(item + gridDim.x, cnext, tid);
       fetch_g(item + gridDim.x, cnext);
@@ -280,16 +286,17 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     // ---- S0: staged inputs into LDS, local gate prefix ----------------------
     pk.store(sK, PK, tid);
     pq.store(sQ, PK, tid);
-    if (tid < CH) sBeta[tid] = tid < n ? beta_val(pbeta, a.beta_f32) : 0.f;
+    if (tid < CH) sBeta[tid] = tid < n ? beta_val(pbeta, ka().beta_f32) : 0.f;
     if (tid < NSUB * (K / SUB)) sFlag[tid] = 0;
     if constexpr (GIN) {
       const float ea = fexp2(__uint_as_float(gal) * LOG2E);
 #pragma unroll
-      for (int s = 0; s < NSL; ++s) gc[s].template kda_gate<T>(ea, __uint_as_float(gdtb[s]), a.gate_lb);
+      for (int s = 0; s < NSL; ++s) gc[s].template kda_gate<T>(ea, __uint_as_float(gdtb[s]), ka().gate_lb);
     }
 #pragma unroll
     for (int s = 0; s < NSL; ++s) gc[s].prefix_local(sTot, n);
     lds_barrier();
+    kargs.renew();
 
     // ---- S1: finish the prefix, statistics ----------------------------------
     // the next item's k, q and beta (their registers are free once staged),
@@ -302,9 +309,10 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
 #pragma unroll
     for (int s = 0; s < NSL; ++s)
       subchunk_stats_regs(gc[s], n, sMid, sGf, sGl, sGn, sFlag,
-                          (MODE & PREP_BWD_CHUNK) ? reinterpret_cast<f32x4*>(a.Gst) + cb * NSUB * K
+                          (MODE & PREP_BWD_CHUNK) ? reinterpret_cast<f32x4*>(ka().Gst) + cb * NSUB * K
                                                   : nullptr);
     lds_barrier();
+    kargs.renew();
 
     // Element-wise phase of a column pair (PAIR): the thread's two slots are
     // columns c0 = gc[0].c (even) and c0 + 1 of the same 16 rows, so every
@@ -326,11 +334,11 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
         cA[j] = fexp2(rA[j]);
         cB[j] = fexp2(gn[j] - rB[j]);
       }
-      const float bs = a.scale;
+      const float bs = ka().scale;
       constexpr int KGF = 4 * VE, NGTF = CH / KGF, NGKF = K / KGF;
       constexpr int NKBQ = K / SUB, GPQ = 16 / (4 * (int)sizeof(T));
-      T* Ftd = reinterpret_cast<T*>(a.Ft) + cb * K * CH;
-      T* Qgtd = reinterpret_cast<T*>(a.Qgt) + cb * K * CH;
+      T* Ftd = reinterpret_cast<T*>(ka().Ft) + cb * K * CH;
+      T* Qgtd = reinterpret_cast<T*>(ka().Qgt) + cb * K * CH;
       // F and Qg (orders as in the one-column phase below) in whole 16-byte
       // pieces: the four 4-byte words of a piece row come from four lanes (F:
       // a lane quad; Qg: lanes L, L ^ 1, L ^ 8, L ^ 9), which exchange their
@@ -338,8 +346,8 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       // role j stores the piece of row 4 i + j of group i
       const int tl = c0 >> 1;  // the lane: column pairs run along the wave
       const int frole = tl & 3, qrole = (tl & 1) + ((tl >> 2) & 2);
-      T* Fp = reinterpret_cast<T*>(a.F) + cb * CH * K + ((sg * NGKF + c0 / KGF) * 64 + ((c0 % KGF) / VE) * 16) * VE;
-      T* Qgp = reinterpret_cast<T*>(a.Qg) + cb * CH * K +
+      T* Fp = reinterpret_cast<T*>(ka().F) + cb * CH * K + ((sg * NGKF + c0 / KGF) * 64 + ((c0 % KGF) / VE) * 16) * VE;
+      T* Qgp = reinterpret_cast<T*>(ka().Qg) + cb * CH * K +
                (((int64_t)sg * (NKBQ / GPQ) + (c0 / SUB) / GPQ) * 64 + 16 * ((c0 % SUB) / 4)) * GPQ * 4;
       auto pk2 = [](float x, float y) { return __builtin_bit_cast(uint32_t, bf16x2{(bf16)x, (bf16)y}); };
 #pragma unroll
@@ -405,14 +413,14 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       for (int j = 0; j < 2; ++j) {
         const int col = c0 + j;
         if constexpr (MODE & PREP_BWD_CHUNK) {
-          float* G2d = a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr;
+          float* G2d = ka().gate == 1 && col == 0 ? ka().G2t + cb * CH + r0 : nullptr;
           if (G2d)
 #pragma unroll
             for (int r4 = 0; r4 < RS; r4 += 4)
               *reinterpret_cast<f32x4*>(G2d + r4) = f32x4{gc[j].G[r4], gc[j].G[r4 + 1], gc[j].G[r4 + 2], gc[j].G[r4 + 3]};
         }
         if constexpr ((MODE & (PREP_FWD_SCAN | PREP_BWD_SCAN)) != 0)
-          if (sg == 0) a.glast[cb * K + col] = gn[j];
+          if (sg == 0) ka().glast[cb * K + col] = gn[j];
       }
     };
 
@@ -449,24 +457,24 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       // way are below 2^-62 and multiply O(1) terms.  Rows past the chunk's end
       // hold k = q = beta = 0 and come out as zeros.
       const float cA = fexp2(rA), cB = fexp2(gn - rB);
-      const float bs = a.scale;
+      const float bs = ka().scale;
       // F^T and Qg^T in operand-fragment order (see kernels.hpp): 16 k rows x
       // KG tokens per fragment, this thread's VE-token groups are single
       // 16-byte pieces
       constexpr int KGF = 4 * VE, NGTF = CH / KGF;
-      T* Ftd = reinterpret_cast<T*>(a.Ft) + cb * K * CH;
-      T* Qgtd = reinterpret_cast<T*>(a.Qgt) + cb * K * CH;
+      T* Ftd = reinterpret_cast<T*>(ka().Ft) + cb * K * CH;
+      T* Qgtd = reinterpret_cast<T*>(ka().Qgt) + cb * K * CH;
       // F and Qg in operand-fragment order (row block seg, key group
       // col / KGF): this thread's 16 rows are elements VE apart in one column
       // of pieces (rows past the chunk's end are zeros)
       constexpr int NGKF = K / KGF;
-      T* Fd = reinterpret_cast<T*>(a.F) + cb * CH * K +
+      T* Fd = reinterpret_cast<T*>(ka().F) + cb * CH * K +
               ((g.seg * NGKF + col / KGF) * 64 + ((col % KGF) / VE) * 16) * VE + col % VE;
       // Qg in the order of W (pieces of GPQ 16-key groups, kernels.hpp), so the
       // forward scan contracts it with the same S operand as W: this thread's
       // 16 rows are 4 GPQ elements apart
       constexpr int NKBQ = K / SUB, GPQ = 16 / (4 * (int)sizeof(T));
-      T* Qgd = reinterpret_cast<T*>(a.Qg) + cb * CH * K +
+      T* Qgd = reinterpret_cast<T*>(ka().Qg) + cb * CH * K +
                ((((int64_t)g.seg * (NKBQ / GPQ) + (col / SUB) / GPQ) * 64 + 16 * ((col % SUB) / 4)) * GPQ +
                 (col / SUB) % GPQ) * 4 + col % 4;
 #pragma unroll
@@ -510,23 +518,24 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       // the chunk backward rebuilds G2 of a vector gate from g (or x) and the
       // statistics
       if constexpr (MODE & PREP_BWD_CHUNK) {
-        float* G2d = a.gate == 1 && col == 0 ? a.G2t + cb * CH + r0 : nullptr;
+        float* G2d = ka().gate == 1 && col == 0 ? ka().G2t + cb * CH + r0 : nullptr;
         if (G2d)
 #pragma unroll
           for (int r4 = 0; r4 < RS; r4 += 4)
             *reinterpret_cast<f32x4*>(G2d + r4) = f32x4{g.G[r4], g.G[r4 + 1], g.G[r4 + 2], g.G[r4 + 3]};
       }
       if constexpr ((MODE & (PREP_FWD_SCAN | PREP_BWD_SCAN)) != 0)
-        if (g.seg == 0) a.glast[cb * K + col] = gn;
+        if (g.seg == 0) ka().glast[cb * K + col] = gn;
     }
     lds_barrier();
+    kargs.renew();
 
     // ---- S3: score tiles L (strict, fp32 in LDS) and Cq (inclusive, global) --
     // the next item's gates: their registers are free since the elementwise
     // phase
     if constexpr (PAIR) fetch_g(item + gridDim.x, cnext);
     {
-      T* Cqo = reinterpret_cast<T*>(a.Cq) + cb * CH * CH;
+      T* Cqo = reinterpret_cast<T*>(ka().Cq) + cb * CH * CH;
       using FR = typename Frag4<T>::type;
       // identity as the B operand of a 16-long product: C = X^T I turns a C
       // tile (rows 4 (l >> 4) + e, column l & 15) into row l & 15, columns
@@ -535,7 +544,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
 #pragma unroll
       for (int e = 0; e < 4; ++e) idf[e] = (crow(e) == ccol()) ? 1.f : 0.f;
       const FR idt = to_frag<T>(idf);
-      T* Cqto = reinterpret_cast<T*>(a.Cqt) + cb * CH * CH;
+      T* Cqto = reinterpret_cast<T*>(ka().Cqt) + cb * CH * CH;
       auto store = [&](int I, int J, const f32x4& accL, const f32x4& accC) {
         f32x4 cq;
 #pragma unroll
@@ -559,7 +568,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
         if (J * SUB < n && flagged(sFlag, J, K / SUB)) {
           f32x4 accL = zero4(), accC = zero4();
           score_tile<T, K, true>(sKa, sQ, sK, PK, sFac + (J * (J + 1) / 2 + J) * K, J, J, true, accL, accC);
-          pairwise_diag<T, K, true, EW, GIN>(a, t0, h, n, J, sBeta, sFlag + J * (K / SUB), accL, accC);
+          pairwise_diag<T, K, true, EW, GIN>(ka(), t0, h, n, J, sBeta, sFlag + J * (K / SUB), accL, accC);
           store(J, J, accL, accC);
         }
       // tiles nobody computed: zeros (rows past the end; of the upper
@@ -577,6 +586,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       }
     }
     lds_barrier();
+    kargs.renew();
 
     // ---- S4: A = (I + L)^-1 in fp32 ------------------------------------------
     if constexpr (!PAIR) {  // the one-column layouts: all fetches here, before the solve
@@ -595,7 +605,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     solve_unit_lower(sL, sA, PL, n);
     if constexpr (MODE & PREP_BWD_CHUNK) {  // A^T for the chunk backward, 16-byte rows
       constexpr int VA = 16 / (int)sizeof(T), PER = CH / VA;
-      T* Ato = reinterpret_cast<T*>(a.At) + cb * CH * CH;
+      T* Ato = reinterpret_cast<T*>(ka().At) + cb * CH * CH;
       for (int idx = tid; idx < CH * PER; idx += NTH) {
         const int i = idx / PER, j0 = (idx - i * PER) * VA;
         union {
@@ -619,6 +629,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
         *reinterpret_cast<bf16x4*>(sAb + i * PA + j) = y;
       }
       lds_barrier();  // A in fp32 is dead: E^T and Z^T go over it
+      kargs.renew();
     }
     // E^T from the registers of the elementwise phase
 #pragma unroll
@@ -686,6 +697,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       }
     }
     lds_barrier();
+    kargs.renew();
     if constexpr (PAIR) fetch_v(item + gridDim.x, cnext, tid);  // the staged v is in Z^T
 
     // W, U in operand-fragment order (see kernels.hpp), all 64 rows (rows past
@@ -693,9 +705,9 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     // fragments are the 16-long A fragments of W, the pieces of the forward
     // scan, and one product with the identity turns them exactly into the C
     // fragments of the W tile, from which W^T is stored for the reverse scan.
-    T* Wfo = reinterpret_cast<T*>(a.W) + cb * CH * K;
-    T* Ufo = reinterpret_cast<T*>(a.U) + cb * CH * V;
-    T* Wto = reinterpret_cast<T*>(a.Wt) + cb * K * CH;
+    T* Wfo = reinterpret_cast<T*>(ka().W) + cb * CH * K;
+    T* Ufo = reinterpret_cast<T*>(ka().U) + cb * CH * V;
+    T* Wto = reinterpret_cast<T*>(ka().Wt) + cb * K * CH;
     constexpr bool wantW = MODE & PREP_FWD_SCAN, wantWt = MODE & PREP_BWD_SCAN, wantU = wantW;
     const T* Aop = BF ? (const T*)sAb : (const T*)sA;
     constexpr int PAo = BF ? PA : PL;
@@ -745,6 +757,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       }
     }
     lds_barrier();  // LDS is rewritten by the next item
+    kargs.renew();
   }
 }
 
