@@ -57,11 +57,11 @@ namespace rewy {
 // consumers only (P, D and the write part of dbeta read back, Hq formed as
 // in the joint kernel).  Every value is rounded at the same point in both
 // schedules, so their results are bitwise equal.
-// One workgroup per CU for the erase/write form and for fp32 at V = 32 (both
-// need more than half of a SIMD's registers), two otherwise.
+// One workgroup per CU for the erase/write form and for fp32 (both need more
+// than half of a SIMD's registers), two otherwise.
 template <typename T, int V, int GX>
 constexpr int bwd_chunk_wgs() {
-  return ((GX & 4) || (std::is_same_v<T, float> && V == 32)) ? 1 : 2;
+  return ((GX & 4) || std::is_same_v<T, float>) ? 1 : 2;
 }
 template <typename T, int K, int V, int GX>
 __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(Args a) {
@@ -712,6 +712,12 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
         // pairwise inside the block: exp2(G_r - G_j) formed per pair, never above 1
         const float* Dd = sDiag;
         const float* Hd = sDiag + SUB * PD;
+        // this lane's first row, opaque here (bf16): the row comparisons below
+        // are formed on this (rare) path instead of being hoisted out of the
+        // feature-block loop, where their lane masks stayed live and spilled
+        // (fp32 keeps the hoisted form, which fits its registers better)
+        int r0 = 4 * q4;
+        if constexpr (std::is_same_v<T, bf16>) asm volatile("" : "+v"(r0));
 #pragma unroll
         for (int j = 0; j < SUB; ++j) {
           const int src = ((j >> 2) << 4) | f;
@@ -721,7 +727,7 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
           const float bj = EW ? tof(sBs[f * PKS + I * SUB + j]) : sBeta[I * SUB + j];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 4 * q4 + e;
+            const int r = r0 + e;
             if (j <= r) {
               const float x = fexp2(GI[e] - Gj) * kj;
               XHY[e] += Hd[r * PD + j] * x;
