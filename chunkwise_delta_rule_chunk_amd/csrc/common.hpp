@@ -64,9 +64,13 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // Thread index made opaque to the optimiser.  Persistent item loops take it
 // once per item: otherwise the compiler hoists address arithmetic derived from
 // it out of the loop, and the hoisted values stay live (and spill) across items.
+template <int NTH>
 __device__ __forceinline__ int opaque_tid() {
   int t = threadIdx.x;
   asm volatile("" : "+v"(t));
+  // still a thread of an NTH-thread workgroup: index checks that hold for
+  // every thread (whole tiles) fold away
+  __builtin_assume(t >= 0 && t < NTH);
   return t;
 }
 

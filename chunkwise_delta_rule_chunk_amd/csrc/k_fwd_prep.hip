@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
   if constexpr (PAIR) fetch_v(blockIdx.x, cnext, threadIdx.x);
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     kargs.renew();
-    const int tid = opaque_tid(), w = wave_id();
+    const int tid = opaque_tid<NTH>(), w = wave_id();
     // slot indices opaque per item: addresses derived from them are recomputed
     // rather than hoisted out of the item loop (where they would stay live and
     // spill)
