@@ -269,7 +269,10 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
     // rather than hoisted out of the item loop (where they would stay live and
     // spill)
 #pragma unroll
-    for (int s = 0; s < NSL; ++s) asm volatile("" : "+v"(gc[s].c), "+v"(gc[s].seg));
+    for (int s = 0; s < NSL; ++s) {
+      asm volatile("" : "+v"(gc[s].c), "+v"(gc[s].seg));
+      __builtin_assume(gc[s].c >= 0 && gc[s].c < K && gc[s].seg >= 0 && gc[s].seg < NSUB);
+    }
     const int c = item / H, h = item - c * H;
     const ChunkInfo ci = cnext;
     const int n = ci.len;
@@ -322,6 +325,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       if (!gc[0].on) return;
       int c0 = gc[0].c;
       asm volatile("" : "+v"(c0));
+      __builtin_assume(c0 >= 0 && c0 < K);
       const int sg = gc[0].seg;
       const int r0 = __builtin_amdgcn_readfirstlane(sg * RS);
       const bool seg_live = r0 < n;
@@ -441,6 +445,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       // the item loop (they would have to stay live, and spill, across items)
       int col = g.c;
       asm volatile("" : "+v"(col));
+      __builtin_assume(col >= 0 && col < K);
       // the thread's 16 rows lie in sub-chunk seg, the same for the whole wave
       // when a wave spans one segment (K >= 64)
       const int r0 = K >= 64 ? __builtin_amdgcn_readfirstlane(g.seg * RS) : g.seg * RS;
