@@ -170,17 +170,18 @@ __device__ __forceinline__ void subchunk_stats_regs(const GateCols<KC>& gc, int 
   const int J = gc.seg, r0 = J * SUB;
   if (r0 >= n) return;
   const int last = min(r0 + SUB, n) - 1;
-  float mx = -INFINITY, mn = INFINITY, gl = 0.f;
+  // Rows past the chunk's end repeat the last valid row's G (the prefix adds
+  // zeros there), so the extremes over all 16 rows are those over the valid
+  // rows, and the last row holds the last valid value.  The extremes use
+  // med3 against an infinity: the same max and min of two finite values
+  // without the NaN quieting fmaxf/fminf add to each input.
+  float mx = gc.G[0], mn = gc.G[0];
 #pragma unroll
-  for (int r = 0; r < SUB; ++r) {
-    const int row = r0 + r;
-    const float x = gc.G[r];
-    if (row < n) {
-      mx = fmaxf(mx, x);
-      mn = fminf(mn, x);
-    }
-    if (row == last) gl = x;
+  for (int r = 1; r < SUB; ++r) {
+    mx = __builtin_amdgcn_fmed3f(gc.G[r], mx, INFINITY);
+    mn = __builtin_amdgcn_fmed3f(gc.G[r], mn, -INFINITY);
   }
+  const float gl = gc.G[SUB - 1];
   const int idx = J * KC + gc.c;
   sMid[idx] = 0.5f * (mx + mn);
   sGf[idx] = gc.G[0];
