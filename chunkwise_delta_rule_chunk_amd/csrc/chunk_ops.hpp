@@ -139,9 +139,13 @@ struct GateCols {
   // add zero), in two halves around a barrier the caller places:
   // prefix_local() publishes the segment totals in sTot [NSUB][KC],
   // prefix_finish() adds the totals of earlier segments.
+  // MASK: zero the rows past the end first (a gate formed from x, which is
+  // nonzero there); a loaded g already reads as zero past the end.
+  template <bool MASK>
   __device__ __forceinline__ void prefix_local(float* sTot, int n) {
+    if constexpr (MASK)
 #pragma unroll
-    for (int r = 0; r < RS; ++r) G[r] = seg * RS + r < n ? G[r] : 0.f;
+      for (int r = 0; r < RS; ++r) G[r] = seg * RS + r < n ? G[r] : 0.f;
 #pragma unroll
     for (int r = 1; r < RS; ++r) G[r] += G[r - 1];
     if (on) sTot[seg * KC + c] = G[RS - 1];

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256, (MODE & PREP_EW) ? 1 : 2) void k_fwd_prep(Args
       for (int s = 0; s < NSL; ++s) gc[s].template kda_gate<T>(ea, __uint_as_float(gdtb[s]), ka().gate_lb);
     }
 #pragma unroll
-    for (int s = 0; s < NSL; ++s) gc[s].prefix_local(sTot, n);
+    for (int s = 0; s < NSL; ++s) gc[s].template prefix_local<GIN>(sTot, n);
     lds_barrier();
     kargs.renew();
 
