@@ -271,6 +271,89 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
   }
   lds_barrier();  // P complete (loaded, for the consumers); A^T is dead
 
+  // ---- the first feature block's operands --------------------------------------
+  // requested here in the joint schedule, so that their latency overlaps the
+  // D and H_q products (the consumers of the separate schedule read D first)
+  const T* hb = reinterpret_cast<const T*>(a.hbuf) + cb * K * V;
+  const T* dhb = reinterpret_cast<const T*>(a.dhbuf) + cb * K * V;
+  // raw k and q rows of the chunk (rows past the end read as zero)
+  const GBuf bk = gbuf(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
+  const GBuf bq = gbuf(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
+  const float* Gstg = a.Gst + cb * NSUB * K * 4;  // float4 records, [J][K]
+  const GBuf bgx = gbuf(reinterpret_cast<const T*>(a.gx) + (t0 * H + h) * K, GIN ? tile_bytes<T>(n, gsK, K) : 0u);
+  const GBuf bdt = gbuf(a.dt_bias + (int64_t)h * K, GIN ? K * 4 : 0u);
+  // registers of the next block's operands (loaded during this block's
+  // products).  Every load is unconditional: a scalar gate has one G2 row
+  // (the others read as zero) and no gate reads none.
+  TileRegs<float, SUB, CH, NTH> pG;
+  // A vector gate: G2 of the feature block is rebuilt here (the prep keeps
+  // only its sub-chunk statistics).  Wave w takes rows [16 w, 16 w + 16):
+  // lane (q4, f) reads g at rows 16 w + 4 q4 + e of feature 16 fb + f (the
+  // gate formed in the kernels: x there and dt_bias of the feature, g formed
+  // as in the prep) and G2 at the block's first row (its statistics record;
+  // zero for a block past the chunk's end, whose G2 is never used).  The
+  // scalar gate reads the prep's G2 row.
+  constexpr bool GRAW = GATE == 2;
+  uint32_t graw[GRAW ? 4 : 1], gfw = 0u, gdw = 0u;
+  const GBuf bgr = gbuf(a.g + (t0 * H + h) * K, GRAW && !GIN ? tile_bytes<float>(n, gsK, K) : 0u);
+  const GBuf bgf = gbuf(Gstg, GRAW ? (uint32_t)(((n + SUB - 1) / SUB) * K * 16) : 0u);
+  // k and q of a feature block from their natural rows: a piece is KQV
+  // features of one token; the first half of the pieces is k, the second q
+  // (uniform per wave), transposed into [feature][token] when stored
+  constexpr int KQV = 16 / (int)sizeof(T), KQR = SUB / KQV;  // features per piece, pieces per row
+  constexpr int KQP = 2 * CH * KQR, KQN = KQP / NTH;         // pieces, per thread
+  static_assert(KQP % NTH == 0 && (CH * KQR) % 64 == 0, "k/q pieces");
+  uint4 pkq[KQN];
+  // erase/write form: the erase gate of the feature block, like k (a piece
+  // is KQV features of one token; only the first CH KQR pieces exist)
+  constexpr int BQN = EW ? (CH * KQR + NTH - 1) / NTH : 1;
+  static_assert((CH * KQR) % 64 == 0, "erase-gate pieces");
+  uint4 pbq[BQN];
+  const GBuf bbk = gbuf(reinterpret_cast<const T*>(a.beta) + (t0 * H + h) * K, EW ? tile_bytes<T>(n, gsK, K) : 0u);
+  TileRegs<float, NSUB, SUB * 4, NTH> pX;
+  TileRegs<T, SUB, V, NTH> pS, pD;
+  TileRegs<float, 1, SUB, NTH> pN;
+  // the scalar gate's G2 row [64] (rows 1 .. 15 of the tile read as zero and
+  // are not used)
+  const float* gp = a.G2t + cb * CH;
+  const uint32_t gbytes = GATE == 1 ? CH * 4 : 0;
+  auto fetch_fb = [&](int fb) {
+    if constexpr (GRAW) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t el = (int64_t)(w * SUB + 4 * q4 + e) * gsK + fb * SUB + f;
+        if constexpr (!GIN) graw[e] = gld4(bgr, (uint32_t)(el * 4));
+        else if constexpr (sizeof(T) == 2) graw[e] = gld2(bgx, (uint32_t)(el * 2));
+        else graw[e] = gld4(bgx, (uint32_t)(el * 4));
+      }
+      if constexpr (GIN) gdw = gld4(bdt, (uint32_t)((fb * SUB + f) * 4));
+      gfw = gld4(bgf, (uint32_t)(((w * K + fb * SUB + f) * 4) * 4));
+    } else {
+      pG.load_cb(gbuf(gp, gbytes), 1, 0, tid);
+    }
+#pragma unroll
+    for (int j = 0; j < KQN; ++j) {
+      const int pc = tid + j * NTH, rem = pc % (CH * KQR);
+      const int t = rem / KQR, f0 = (rem % KQR) * KQV;
+      const uint32_t off = (uint32_t)(((int64_t)t * gsK + fb * SUB + f0) * (int64_t)sizeof(T));
+      // k or q is the same for the whole wave (64 consecutive pieces)
+      const bool isk = __builtin_amdgcn_readfirstlane(pc) < CH * KQR;
+      pkq[j] = gld16(isk ? bk : bq, off);
+    }
+    if constexpr (EW) {
+#pragma unroll
+      for (int j = 0; j < BQN; ++j) {
+        const int pc = tid + j * NTH, t = pc / KQR, f0 = (pc % KQR) * KQV;
+        pbq[j] = gld16(bbk, pc < CH * KQR ? (uint32_t)(((int64_t)t * gsK + fb * SUB + f0) * (int64_t)sizeof(T)) : OOB);
+      }
+    }
+    pX.load(gbuf(Gstg + fb * SUB * 4, tile_bytes<float>(NSUB, K * 4, SUB * 4)), K * 4, tid);
+    pS.load_cb(gbuf(hb, K * V * sizeof(T)), K, fb * SUB, tid);
+    pD.load_cb(gbuf(dhb, K * V * sizeof(T)), K, fb * SUB, tid);
+    pN.load(gbuf(a.glast + cb * K + fb * SUB, SUB * sizeof(float)), SUB, tid);
+  };
+  if constexpr (!PROD && !CONS) fetch_fb(0);
+
   // ---- left operands of block I, straight into fragments ---------------------
   //   Dm[J]  = D[I, J]      (J <= I)    Hm[J]  = Hq[I, J]      (J <= I)
   //   Dtm[J] = D[J, I]^T    (J >= I)    Htm[J] = Hq[J, I]^T    (J >= I)
@@ -354,12 +437,6 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
   // ---- per 16-feature block: state products, matrix intra, chain rules -------
   // The gate reverse sum needs the block totals of the later row blocks: they
   // are exchanged through LDS once per feature block (all waves take part).
-  const T* hb = reinterpret_cast<const T*>(a.hbuf) + cb * K * V;
-  const T* dhb = reinterpret_cast<const T*>(a.dhbuf) + cb * K * V;
-  // raw k and q rows of the chunk (rows past the end read as zero)
-  const GBuf bk = gbuf(reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
-  const GBuf bq = gbuf(reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
-  const float* Gstg = a.Gst + cb * NSUB * K * 4;  // float4 records, [J][K]
   // outputs through bounds-checked buffers: rows past the chunk's end are dropped
   const GBuf bdq = gbuf(reinterpret_cast<T*>(a.dq) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
   const GBuf bdk = gbuf(reinterpret_cast<T*>(a.dk) + (t0 * H + h) * K, tile_bytes<T>(n, gsK, K));
@@ -367,8 +444,6 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
   // gate in the kernel: dx (like dq), the pre-activation and dt_bias of this
   // lane's row and four features, the wave's partial sums
   const GBuf bdx = gbuf(reinterpret_cast<T*>(a.dgx) + (t0 * H + h) * K, GIN ? tile_bytes<T>(n, gsK, K) : 0u);
-  const GBuf bgx = gbuf(reinterpret_cast<const T*>(a.gx) + (t0 * H + h) * K, GIN ? tile_bytes<T>(n, gsK, K) : 0u);
-  const GBuf bdt = gbuf(a.dt_bias + (int64_t)h * K, GIN ? K * 4 : 0u);
   const GBuf bgp = gbuf(a.gpart + cb * NSUB * K, GIN ? NSUB * K * 4 : 0u);
   const float nea = GIN ? -fexp2(__uint_as_float(gld4(gbuf(a.a_log, H * 4), h * 4)) * LOG2E) : 0.f;
   const float lb = GIN ? a.gate_lb : 0.f, lbea = -lb * nea;  // bounded form: lb exp(A_log)
@@ -400,76 +475,6 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
   const FR idt = to_frag<T>(idf);
   float lam0s = 0.f, lamws = 0.f;
 
-  // registers of the next block's operands (loaded during this block's
-  // products).  Every load is unconditional: a scalar gate has one G2 row
-  // (the others read as zero) and no gate reads none.
-  TileRegs<float, SUB, CH, NTH> pG;
-  // A vector gate: G2 of the feature block is rebuilt here (the prep keeps
-  // only its sub-chunk statistics).  Wave w takes rows [16 w, 16 w + 16):
-  // lane (q4, f) reads g at rows 16 w + 4 q4 + e of feature 16 fb + f (the
-  // gate formed in the kernels: x there and dt_bias of the feature, g formed
-  // as in the prep) and G2 at the block's first row (its statistics record;
-  // zero for a block past the chunk's end, whose G2 is never used).  The
-  // scalar gate reads the prep's G2 row.
-  constexpr bool GRAW = GATE == 2;
-  uint32_t graw[GRAW ? 4 : 1], gfw = 0u, gdw = 0u;
-  const GBuf bgr = gbuf(a.g + (t0 * H + h) * K, GRAW && !GIN ? tile_bytes<float>(n, gsK, K) : 0u);
-  const GBuf bgf = gbuf(Gstg, GRAW ? (uint32_t)(((n + SUB - 1) / SUB) * K * 16) : 0u);
-  // k and q of a feature block from their natural rows: a piece is KQV
-  // features of one token; the first half of the pieces is k, the second q
-  // (uniform per wave), transposed into [feature][token] when stored
-  constexpr int KQV = 16 / (int)sizeof(T), KQR = SUB / KQV;  // features per piece, pieces per row
-  constexpr int KQP = 2 * CH * KQR, KQN = KQP / NTH;         // pieces, per thread
-  static_assert(KQP % NTH == 0 && (CH * KQR) % 64 == 0, "k/q pieces");
-  uint4 pkq[KQN];
-  // erase/write form: the erase gate of the feature block, like k (a piece
-  // is KQV features of one token; only the first CH KQR pieces exist)
-  constexpr int BQN = EW ? (CH * KQR + NTH - 1) / NTH : 1;
-  static_assert((CH * KQR) % 64 == 0, "erase-gate pieces");
-  uint4 pbq[BQN];
-  const GBuf bbk = gbuf(reinterpret_cast<const T*>(a.beta) + (t0 * H + h) * K, EW ? tile_bytes<T>(n, gsK, K) : 0u);
-  TileRegs<float, NSUB, SUB * 4, NTH> pX;
-  TileRegs<T, SUB, V, NTH> pS, pD;
-  TileRegs<float, 1, SUB, NTH> pN;
-  // the scalar gate's G2 row [64] (rows 1 .. 15 of the tile read as zero and
-  // are not used)
-  const float* gp = a.G2t + cb * CH;
-  const uint32_t gbytes = GATE == 1 ? CH * 4 : 0;
-  auto fetch_fb = [&](int fb) {
-    if constexpr (GRAW) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t el = (int64_t)(w * SUB + 4 * q4 + e) * gsK + fb * SUB + f;
-        if constexpr (!GIN) graw[e] = gld4(bgr, (uint32_t)(el * 4));
-        else if constexpr (sizeof(T) == 2) graw[e] = gld2(bgx, (uint32_t)(el * 2));
-        else graw[e] = gld4(bgx, (uint32_t)(el * 4));
-      }
-      if constexpr (GIN) gdw = gld4(bdt, (uint32_t)((fb * SUB + f) * 4));
-      gfw = gld4(bgf, (uint32_t)(((w * K + fb * SUB + f) * 4) * 4));
-    } else {
-      pG.load_cb(gbuf(gp, gbytes), 1, 0, tid);
-    }
-#pragma unroll
-    for (int j = 0; j < KQN; ++j) {
-      const int pc = tid + j * NTH, rem = pc % (CH * KQR);
-      const int t = rem / KQR, f0 = (rem % KQR) * KQV;
-      const uint32_t off = (uint32_t)(((int64_t)t * gsK + fb * SUB + f0) * (int64_t)sizeof(T));
-      // k or q is the same for the whole wave (64 consecutive pieces)
-      const bool isk = __builtin_amdgcn_readfirstlane(pc) < CH * KQR;
-      pkq[j] = gld16(isk ? bk : bq, off);
-    }
-    if constexpr (EW) {
-#pragma unroll
-      for (int j = 0; j < BQN; ++j) {
-        const int pc = tid + j * NTH, t = pc / KQR, f0 = (pc % KQR) * KQV;
-        pbq[j] = gld16(bbk, pc < CH * KQR ? (uint32_t)(((int64_t)t * gsK + fb * SUB + f0) * (int64_t)sizeof(T)) : OOB);
-      }
-    }
-    pX.load(gbuf(Gstg + fb * SUB * 4, tile_bytes<float>(NSUB, K * 4, SUB * 4)), K * 4, tid);
-    pS.load_cb(gbuf(hb, K * V * sizeof(T)), K, fb * SUB, tid);
-    pD.load_cb(gbuf(dhb, K * V * sizeof(T)), K, fb * SUB, tid);
-    pN.load(gbuf(a.glast + cb * K + fb * SUB, SUB * sizeof(float)), SUB, tid);
-  };
   auto put_fb = [&]() {
     if constexpr (GRAW) {
       // G2 = G2 at the first row + log2(e) times the sum of g over the later
@@ -530,7 +535,7 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
     pD.store_cb(sDs, PSS, tid);
     pN.store(sGn, SUB, tid);
   };
-  fetch_fb(0);
+  if constexpr (PROD || CONS) fetch_fb(0);  // the joint schedule issued it before D and H_q
   put_fb();
   lds_barrier();
 
@@ -715,7 +720,7 @@ __global__ __launch_bounds__(256, (bwd_chunk_wgs<T, V, GX>())) void k_bwd_chunk(
         // this lane's first row, opaque here (bf16): the row comparisons below
         // are formed on this (rare) path instead of being hoisted out of the
         // feature-block loop, where their lane masks stayed live and spilled
-        // (fp32 keeps the hoisted form, which fits its registers better)
+        // (measured on the bf16 kernels; the fp32 ones are left as they were)
         int r0 = 4 * q4;
         if constexpr (std::is_same_v<T, bf16>) asm volatile("" : "+v"(r0));
 #pragma unroll
